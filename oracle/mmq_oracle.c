@@ -1,0 +1,402 @@
+/*
+ * mmq_oracle.c - plain, slow CPU oracle for the prefill MMQ contraction.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path (the HIP library and
+ * its Python binding) may include, link, load or call this file. Only the
+ * tests, the smoke check and the bench's CPU-baseline leg use it.
+ *
+ * It shares no code, header, table or constant with the GPU path. Every
+ * function below is a direct transcription of a definition from the MMQ
+ * pages, restated in this project's own words:
+ *
+ *  - "08 . R1 - int8 MMQ prefill GEMM" (minfer), section 3.2, the CPU
+ *    reference of the parity test: per 32-value block, d = max|x|/127 in f32,
+ *    the stored scale is d rounded to f16, q = round-half-even(x * (1/d))
+ *    clamped to [-128,127], and the block's integer sum is kept. Section 2.2
+ *    gives the rank-1 min term: sum(w*q) = ds*sum(nib*q) - dmin*sum(q).
+ *  - "A Negative Result on int8 Tensor-Core MMQ" (Hanzo), section 2: the
+ *    contraction out[m,n] = sum over 32-blocks of (xs*wd) * sum(xq*wq).
+ *  - llama.cpp PR #304 "CUDA: add IQ1_M to MMQ", description: an IQ1_M value
+ *    is d*(2s+1)*(g+delta); 8(g+delta) = 8g +- 1 and the per-16 scale becomes
+ *    d(2s+1)/8.
+ *  - "INT8 W8A8 GEMM - Prefill" (metainfer), section 1: int8 activations with
+ *    a per-token f32 scale, int8 weights with a per-channel f32 scale, int32
+ *    accumulation, epilogue fragment -> scale -> bf16, no bias.
+ *
+ * The raw weight byte layouts are this project's own (the pages give
+ * semantics, not bytes); they are documented in gen/__init__.py.
+ *
+ * Precision: the quantiser works in f32 because the pages fix it; integer
+ * partial sums are exact (int64, checked to fit int32); the f32 outputs are
+ * accumulated in double; the W8A8 epilogue is the pages' f32 two-multiply
+ * order rounded to bf16 (round-to-nearest-even).
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_Q8_0 0
+#define ORC_Q4_0 1
+#define ORC_Q4_K 2
+#define ORC_IQ1T 3
+
+/* ---------------------------------------------------------------- scalars */
+
+/* IEEE binary16 -> binary32, exact (handles zero, subnormal, inf, nan). */
+float orc_half_to_float(uint16_t h) {
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t expo = (uint32_t)(h >> 10) & 0x1Fu;
+    uint32_t mant = (uint32_t)h & 0x3FFu;
+    float mag;
+    if (expo == 0) {
+        mag = ldexpf((float)mant, -24);                 /* subnormal or zero */
+    } else if (expo == 31) {
+        mag = mant ? NAN : INFINITY;
+    } else {
+        mag = ldexpf((float)(mant | 0x400u), (int)expo - 25);
+    }
+    return sign ? -mag : mag;
+}
+
+/* binary32 -> binary16 with round-to-nearest-even (finite inputs; overflow -> inf). */
+uint16_t orc_float_to_half(float f) {
+    uint32_t sign = signbit(f) ? 0x8000u : 0u;
+    double a = fabs((double)f);
+    if (isnan(f)) return (uint16_t)(sign | 0x7E00u);
+    if (a == 0.0) return (uint16_t)sign;
+    int e;
+    (void)frexp(a, &e);                                /* a = m * 2^e, m in [0.5,1) */
+    int ulp_exp = e - 11;                              /* 11 significant bits */
+    if (ulp_exp < -24) ulp_exp = -24;                  /* subnormal spacing */
+    double units = a / ldexp(1.0, ulp_exp);            /* exact: a has 24 bits */
+    double r = nearbyint(units);                       /* default mode: ties to even */
+    double v = r * ldexp(1.0, ulp_exp);
+    if (v >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    /* re-encode v exactly */
+    if (v < ldexp(1.0, -14)) {                         /* subnormal (or rounds up to min normal) */
+        uint32_t m = (uint32_t)(v / ldexp(1.0, -24));
+        return (uint16_t)(sign | m);                   /* m == 1024 encodes 2^-14 correctly */
+    }
+    int ve;
+    double vm = frexp(v, &ve);                         /* v = vm * 2^ve, vm in [0.5,1) */
+    uint32_t expo = (uint32_t)(ve - 1 + 15);
+    uint32_t mant = (uint32_t)(vm * 2048.0) - 1024u;
+    return (uint16_t)(sign | (expo << 10) | mant);
+}
+
+/* binary32 -> bfloat16 with round-to-nearest-even (finite inputs). */
+uint16_t orc_float_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x40u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ------------------------------------------------------ activation quantiser */
+
+/* q8_1: for every row m and 32-value block b of x (row stride ldx floats):
+ *   amax = max |x|;  d = amax/127 (f32);  di = d != 0 ? 1/d : 0;
+ *   q_i = clamp(rint(x_i*di), -128, 127);  xs = f32(f16_rne(d));  xsum = sum q_i.
+ * Outputs are row-major: xq [M][K], xs [M][K/32], xsum [M][K/32].            */
+void orc_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ldx,
+                       int8_t* xq, float* xs, int32_t* xsum) {
+    const int64_t KB = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const float* blk = x + m * ldx + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(blk[i]);
+                if (a > amax) amax = a;
+            }
+            float d = amax / 127.0f;
+            float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+            int32_t s = 0;
+            for (int i = 0; i < 32; ++i) {
+                float v = blk[i] * di;
+                float r = rintf(v);
+                if (r < -128.0f) r = -128.0f;
+                if (r > 127.0f) r = 127.0f;
+                int q = (int)r;
+                xq[m * K + b * 32 + i] = (int8_t)q;
+                s += q;
+            }
+            xs[m * KB + b] = orc_half_to_float(orc_float_to_half(d));
+            xsum[m * KB + b] = s;
+        }
+    }
+}
+
+/* Per-token int8 (W8A8 activations): the same steps with the block being the
+ * whole row and the scale kept in f32 (not rounded to f16).                  */
+void orc_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_t ldx,
+                           int8_t* a, float* sa) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const float* row = x + m * ldx;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(row[k]);
+            if (v > amax) amax = v;
+        }
+        float d = amax / 127.0f;
+        float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float r = rintf(row[k] * di);
+            if (r < -128.0f) r = -128.0f;
+            if (r > 127.0f) r = 127.0f;
+            a[m * K + k] = (int8_t)(int)r;
+        }
+        sa[m] = d;
+    }
+}
+
+/* ------------------------------------------------------------ weight decode */
+
+/* Decode one weight row into:
+ *   wq[K]      - the integer that enters the int8 dot for each value
+ *                (q8_0: q; q4_0: nib-8; q4_K: nib (unsigned); iq1t: 8g+sigma)
+ *   wd[K/16]   - the f32 scale multiplying each 16-value half of the dot
+ *                (q8_0/q4_0: d; q4_K: d*sc; iq1t: d*(2s+1)/8)
+ *   wm[K/32]   - the f32 coefficient of the activation block sum
+ *                (q4_K: -dmin*m, others 0)
+ * Every scale here is exact in f32 (an f16 times a small integer, or /8).    */
+static void decode_row(int fmt, const uint8_t* row, int64_t K,
+                       int16_t* wq, float* wd, float* wm) {
+    const int64_t KB = K / 32;
+    for (int64_t b = 0; b < KB; ++b) wm[b] = 0.0f;
+    if (fmt == ORC_Q8_0) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const uint8_t* blk = row + b * 34;
+            float d = orc_half_to_float(rd16(blk));
+            for (int i = 0; i < 32; ++i) wq[b * 32 + i] = (int8_t)blk[2 + i];
+            wd[2 * b] = d;
+            wd[2 * b + 1] = d;
+        }
+    } else if (fmt == ORC_Q4_0) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const uint8_t* blk = row + b * 18;
+            float d = orc_half_to_float(rd16(blk));
+            for (int j = 0; j < 16; ++j) {
+                wq[b * 32 + j] = (int16_t)((blk[2 + j] & 0xF) - 8);
+                wq[b * 32 + 16 + j] = (int16_t)((blk[2 + j] >> 4) - 8);
+            }
+            wd[2 * b] = d;
+            wd[2 * b + 1] = d;
+        }
+    } else if (fmt == ORC_Q4_K) {
+        for (int64_t sb = 0; sb < K / 256; ++sb) {
+            const uint8_t* blk = row + sb * 144;
+            float d = orc_half_to_float(rd16(blk));
+            float dmin = orc_half_to_float(rd16(blk + 2));
+            uint64_t scw = 0, mw = 0;
+            for (int i = 0; i < 6; ++i) {
+                scw |= (uint64_t)blk[4 + i] << (8 * i);
+                mw |= (uint64_t)blk[10 + i] << (8 * i);
+            }
+            const uint8_t* qs = blk + 16;
+            for (int j = 0; j < 8; ++j) {
+                int sc = (int)((scw >> (6 * j)) & 63u);
+                int mm = (int)((mw >> (6 * j)) & 63u);
+                int64_t b = sb * 8 + j;
+                for (int i = 0; i < 16; ++i) {
+                    wq[b * 32 + i] = (int16_t)(qs[16 * j + i] & 0xF);
+                    wq[b * 32 + 16 + i] = (int16_t)(qs[16 * j + i] >> 4);
+                }
+                wd[2 * b] = d * (float)sc;
+                wd[2 * b + 1] = d * (float)sc;
+                wm[b] = -(dmin * (float)mm);
+            }
+        }
+    } else { /* ORC_IQ1T */
+        for (int64_t sb = 0; sb < K / 256; ++sb) {
+            const uint8_t* blk = row + sb * 76;
+            float d = orc_half_to_float(rd16(blk + 74));
+            uint64_t sw = 0;
+            for (int i = 0; i < 6; ++i) sw |= (uint64_t)blk[64 + i] << (8 * i);
+            for (int e = 0; e < 256; ++e) {
+                int c = (blk[e / 4] >> (2 * (e % 4))) & 3;
+                int g = c - 1;
+                int sgn = (blk[70 + e / 64] >> ((e / 8) % 8)) & 1;
+                wq[sb * 256 + e] = (int16_t)(8 * g + (sgn ? -1 : 1));
+            }
+            for (int h = 0; h < 16; ++h) {
+                int s = (int)((sw >> (3 * h)) & 7u);
+                wd[sb * 16 + h] = d * (float)(2 * s + 1) / 8.0f;
+            }
+        }
+    }
+}
+
+/* Expose the decoder (one row) for the oracle's own tests. */
+void orc_decode_row(int fmt, const uint8_t* row, int64_t K, int16_t* wq, float* wd, float* wm) {
+    decode_row(fmt, row, K, wq, wd, wm);
+}
+
+static int64_t raw_row_bytes(int fmt, int64_t K) {
+    switch (fmt) {
+        case ORC_Q8_0: return K / 32 * 34;
+        case ORC_Q4_0: return K / 32 * 18;
+        case ORC_Q4_K: return K / 256 * 144;
+        default:       return K / 256 * 76;
+    }
+}
+
+/* ----------------------------------------------------------- integer partials */
+
+/* P[m][n][b] = the exact integer dot of block b:
+ *   q8_0, q4_0: sum xq*wq;  q4_K: sum xq*nib (unsigned nibbles);
+ *   iq1t: the folded per-32 form sum_h (2s_h+1) * sum_{16 in half h} xq*(8g+sigma).
+ * Returns 0, or -1 if any partial falls outside int32.                        */
+int orc_partials(int fmt, const uint8_t* raw, int64_t N, int64_t K,
+                 const int8_t* xq, int64_t M, int32_t* P) {
+    const int64_t KB = K / 32, rb = raw_row_bytes(fmt, K);
+    int bad = 0;
+#pragma omp parallel
+    {
+        int16_t* wq = (int16_t*)malloc(sizeof(int16_t) * K);
+        float* wd = (float*)malloc(sizeof(float) * (K / 16));
+        float* wm = (float*)malloc(sizeof(float) * KB);
+        int16_t* mult = (int16_t*)malloc(sizeof(int16_t) * (K / 16));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            decode_row(fmt, raw + n * rb, K, wq, wd, wm);
+            for (int64_t h = 0; h < K / 16; ++h) mult[h] = 1;
+            if (fmt == ORC_IQ1T) {
+                const uint8_t* row = raw + n * rb;
+                for (int64_t sb = 0; sb < K / 256; ++sb) {
+                    uint64_t sw = 0;
+                    for (int i = 0; i < 6; ++i) sw |= (uint64_t)row[sb * 76 + 64 + i] << (8 * i);
+                    for (int h = 0; h < 16; ++h) mult[sb * 16 + h] = (int16_t)(2 * ((sw >> (3 * h)) & 7u) + 1);
+                }
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                for (int64_t b = 0; b < KB; ++b) {
+                    int64_t total = 0;
+                    for (int half = 0; half < 2; ++half) {
+                        int64_t s16 = 0;
+                        for (int i = 0; i < 16; ++i) {
+                            int64_t k = b * 32 + half * 16 + i;
+                            s16 += (int64_t)xq[m * K + k] * (int64_t)wq[k];
+                        }
+                        total += (int64_t)mult[2 * b + half] * s16;
+                    }
+                    if (total > INT32_MAX || total < INT32_MIN) bad = 1;
+                    P[(m * N + n) * KB + b] = (int32_t)total;
+                }
+            }
+        }
+        free(wq); free(wd); free(wm); free(mult);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Per-16 iq1t partials P16[m][n][h] = sum over the 16 values of half-block h of
+ * xq * (8g+sigma), before the (2s+1) fold.                                    */
+void orc_partials16_iq1t(const uint8_t* raw, int64_t N, int64_t K,
+                         const int8_t* xq, int64_t M, int32_t* P16) {
+    const int64_t KH = K / 16, rb = raw_row_bytes(ORC_IQ1T, K);
+#pragma omp parallel
+    {
+        int16_t* wq = (int16_t*)malloc(sizeof(int16_t) * K);
+        float* wd = (float*)malloc(sizeof(float) * KH);
+        float* wm = (float*)malloc(sizeof(float) * (K / 32));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            decode_row(ORC_IQ1T, raw + n * rb, K, wq, wd, wm);
+            for (int64_t m = 0; m < M; ++m)
+                for (int64_t h = 0; h < KH; ++h) {
+                    int32_t s = 0;
+                    for (int i = 0; i < 16; ++i) s += (int32_t)xq[m * K + h * 16 + i] * wq[h * 16 + i];
+                    P16[(m * N + n) * KH + h] = s;
+                }
+        }
+        free(wq); free(wd); free(wm);
+    }
+}
+
+/* ------------------------------------------------------------ f32 output */
+
+/* out[m*ldo + n] = sum over blocks b of xs[m,b] * ( sum_half wd*P16 + wm*xsum[m,b] ),
+ * accumulated in double and rounded to f32 once. Rows m0 <= m < m1 only (the
+ * bench times a bounded sample of rows with this).                           */
+void orc_gemm_rows(int fmt, const uint8_t* raw, int64_t N, int64_t K,
+                   const int8_t* xq, const float* xs, const int32_t* xsum,
+                   int64_t m0, int64_t m1, float* out, int64_t ldo) {
+    const int64_t KB = K / 32, rb = raw_row_bytes(fmt, K);
+    int16_t* wq_all = (int16_t*)malloc(sizeof(int16_t) * (size_t)(N * K));
+    float* wd_all = (float*)malloc(sizeof(float) * (size_t)(N * (K / 16)));
+    float* wm_all = (float*)malloc(sizeof(float) * (size_t)(N * KB));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        decode_row(fmt, raw + n * rb, K, wq_all + n * K, wd_all + n * (K / 16), wm_all + n * KB);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const int16_t* wq = wq_all + n * K;
+            const float* wd = wd_all + n * (K / 16);
+            const float* wm = wm_all + n * KB;
+            double acc = 0.0;
+            for (int64_t b = 0; b < KB; ++b) {
+                double blockval = 0.0;
+                for (int half = 0; half < 2; ++half) {
+                    int32_t s16 = 0;
+                    for (int i = 0; i < 16; ++i) {
+                        int64_t k = b * 32 + half * 16 + i;
+                        s16 += (int32_t)xq[m * K + k] * (int32_t)wq[k];
+                    }
+                    blockval += (double)wd[2 * b + half] * (double)s16;
+                }
+                blockval += (double)wm[b] * (double)xsum[m * KB + b];
+                acc += (double)xs[m * KB + b] * blockval;
+            }
+            out[(m - m0) * ldo + n] = (float)acc;
+        }
+    }
+    free(wq_all); free(wd_all); free(wm_all);
+}
+
+void orc_gemm(int fmt, const uint8_t* raw, int64_t N, int64_t K,
+              const int8_t* xq, const float* xs, const int32_t* xsum, int64_t M, float* out) {
+    orc_gemm_rows(fmt, raw, N, K, xq, xs, xsum, 0, M, out, N);
+}
+
+/* ---------------------------------------------------------------- W8A8 */
+
+/* acc[m][n] = sum_k a[m,k]*w[n,k] (exact int32); out = bf16_rne((f32(acc)*sa[m])*sw[n]),
+ * two separate f32 multiplies in that order. acc may be NULL. Returns -1 if an
+ * accumulator leaves int32.                                                    */
+int orc_gemm_w8a8(const int8_t* a, const float* sa, int64_t M, const int8_t* w, const float* sw,
+                  int64_t N, int64_t K, int32_t* acc, uint16_t* out, int64_t m0, int64_t m1) {
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k) s += (int64_t)a[m * K + k] * (int64_t)w[n * K + k];
+            if (s > INT32_MAX || s < INT32_MIN) bad = 1;
+            volatile float t = (float)(int32_t)s * sa[m];
+            volatile float u = t * sw[n];
+            if (acc) acc[(m - m0) * N + n] = (int32_t)s;
+            out[(m - m0) * N + n] = orc_float_to_bf16(u);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
