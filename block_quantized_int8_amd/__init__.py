@@ -1,0 +1,218 @@
+"""Python binding for libmmq.so, the MI355X (gfx950) prefill MMQ library.
+
+Argument marshalling only: every step of the path (activation quantisation, weight repack,
+the MMQ contraction, MoE grouping) runs in the library's HIP kernels. PyTorch provides device
+memory and the stream. There is no CPU fallback: if the library is missing, every call raises.
+
+The functions mirror include/mmq.h one to one (same names without the `mmq_` prefix):
+
+    act_bytes, act_region_offsets, quantize_act, packed_bytes, repack_weights, gemm,
+    gemm_id_workspace_bytes, gemm_id, status_string
+
+plus `act_to_host`, a host-side decoder of the documented q8_1 act layout used by tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmmq.so")
+
+# enums (include/mmq.h)
+MMQ_OK, MMQ_EINVAL, MMQ_EUNSUPPORTED, MMQ_EALIGN, MMQ_EWORKSPACE, MMQ_EHIP = range(6)
+WTYPE = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "i8_row": 4}
+ATYPE = {"q8_1": 0, "i8_token": 1}
+OTYPE = {"f32": 0, "bf16": 1, "i32_partials": 2}
+
+
+class MMQError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {status_string(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmmq.so (built in-tree by __graft_entry__.build()); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    e = ctypes.c_int
+    L.mmq_status_string.argtypes = [e]
+    L.mmq_status_string.restype = ctypes.c_char_p
+    L.mmq_act_bytes.argtypes = [e, I, I]
+    L.mmq_act_bytes.restype = S
+    L.mmq_act_region_offsets.argtypes = [e, I, I, ctypes.POINTER(S)]
+    L.mmq_act_region_offsets.restype = e
+    L.mmq_quantize_act.argtypes = [e, P, I, I, I, P, P]
+    L.mmq_quantize_act.restype = e
+    L.mmq_packed_bytes.argtypes = [e, I, I]
+    L.mmq_packed_bytes.restype = S
+    L.mmq_repack_weights.argtypes = [e, P, P, I, I, P, P]
+    L.mmq_repack_weights.restype = e
+    L.mmq_gemm.argtypes = [e, P, P, I, I, I, e, P, I, P]
+    L.mmq_gemm.restype = e
+    L.mmq_gemm_id_workspace_bytes.argtypes = [I, I, I]
+    L.mmq_gemm_id_workspace_bytes.restype = S
+    L.mmq_gemm_id.argtypes = [e, P, I, P, P, I, I, I, I, e, P, P, S, P]
+    L.mmq_gemm_id.restype = e
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return lib().mmq_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int):
+    if code != MMQ_OK:
+        raise MMQError(fn, code)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _wt(w) -> int:
+    return WTYPE[w] if isinstance(w, str) else int(w)
+
+
+def _at(a) -> int:
+    return ATYPE[a] if isinstance(a, str) else int(a)
+
+
+def _ot(o) -> int:
+    return OTYPE[o] if isinstance(o, str) else int(o)
+
+
+# -------------------------------------------------------------------------- sizes
+
+def act_bytes(atype, M: int, K: int) -> int:
+    return int(lib().mmq_act_bytes(_at(atype), M, K))
+
+
+def act_region_offsets(atype, M: int, K: int) -> tuple[int, int, int]:
+    arr = (ctypes.c_size_t * 3)()
+    _check("mmq_act_region_offsets", lib().mmq_act_region_offsets(_at(atype), M, K, arr))
+    return int(arr[0]), int(arr[1]), int(arr[2])
+
+
+def packed_bytes(wtype, N: int, K: int) -> int:
+    return int(lib().mmq_packed_bytes(_wt(wtype), N, K))
+
+
+def gemm_id_workspace_bytes(E: int, T: int, top_k: int) -> int:
+    return int(lib().mmq_gemm_id_workspace_bytes(E, T, top_k))
+
+
+# -------------------------------------------------------------------------- calls
+
+def quantize_act(x, atype="q8_1", out=None, stream=None):
+    """x: CUDA float32 [M, K] (row stride x.stride(0)); returns the act buffer (uint8)."""
+    import torch
+    assert x.is_cuda and x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    nbytes = act_bytes(atype, M, K)
+    if nbytes == 0:
+        raise MMQError("mmq_act_bytes", MMQ_EINVAL)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _check("mmq_quantize_act", lib().mmq_quantize_act(_at(atype), _ptr(x), M, K, x.stride(0),
+                                                       _ptr(out), _stream(stream)))
+    return out
+
+
+def repack_weights(wtype, raw, N: int, K: int, row_scale=None, out=None, stream=None):
+    """raw: CUDA tensor holding the raw rows (uint8 bytes, or int8 [N,K] for i8_row)."""
+    import torch
+    nbytes = packed_bytes(wtype, N, K)
+    if nbytes == 0:
+        raise MMQError("mmq_packed_bytes", MMQ_EINVAL)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=raw.device)
+    _check("mmq_repack_weights", lib().mmq_repack_weights(_wt(wtype), _ptr(raw), _ptr(row_scale), N, K,
+                                                           _ptr(out), _stream(stream)))
+    return out
+
+
+def gemm(wtype, packed, act, M: int, N: int, K: int, otype="f32", out=None, ldo=None, stream=None):
+    import torch
+    o = _ot(otype)
+    if out is None:
+        if o == OTYPE["f32"]:
+            out = torch.empty((M, N), dtype=torch.float32, device=packed.device)
+        elif o == OTYPE["bf16"]:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=packed.device)
+        else:
+            shape = (M, N) if _wt(wtype) == WTYPE["i8_row"] else (M, N, K // 32)
+            out = torch.empty(shape, dtype=torch.int32, device=packed.device)
+    if ldo is None:
+        ldo = out.stride(0) if out.dim() == 2 else N
+    _check("mmq_gemm", lib().mmq_gemm(_wt(wtype), _ptr(packed), _ptr(act), M, N, K, o, _ptr(out), ldo,
+                                       _stream(stream)))
+    return out
+
+
+def gemm_id(wtype, packed, E: int, act, ids, T: int, top_k: int, N: int, K: int, out=None,
+            workspace=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((T, top_k, N), dtype=torch.float32, device=packed.device)
+    ws = gemm_id_workspace_bytes(E, T, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=packed.device)
+    _check("mmq_gemm_id", lib().mmq_gemm_id(_wt(wtype), _ptr(packed), E, _ptr(act), _ptr(ids), T, top_k, N, K,
+                                             OTYPE["f32"], _ptr(out), _ptr(workspace), workspace.numel(),
+                                             _stream(stream)))
+    return out
+
+
+# -------------------------------------------------------------------------- host helpers
+
+def act_to_host(act_bytes_host: np.ndarray, M: int, K: int):
+    """Decode a q8_1 act buffer (copied to host as uint8) into plain row-major
+    (xq int8 [M,K], xs f32 [M,K/32], xsum int32 [M,K/32]) following the documented layout."""
+    o0, o1, o2 = act_region_offsets("q8_1", M, K)
+    Mp = (M + 31) // 32 * 32
+    KB = K // 32
+    KBp = (KB + 7) // 8 * 8
+    MT = Mp // 32
+    buf = np.asarray(act_bytes_host, dtype=np.uint8)
+    t = buf[o0:o0 + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)   # [mt, b, h, r, 16]
+    xq = t.transpose(0, 3, 1, 2, 4).reshape(Mp, KBp * 32)[:M, :K]
+    xs = buf[o1:o1 + MT * KBp * 128].view(np.float32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
+    xsum = buf[o2:o2 + MT * KBp * 128].view(np.int32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
+    return np.ascontiguousarray(xq), np.ascontiguousarray(xs[:M, :KB]), np.ascontiguousarray(xsum[:M, :KB])
+
+
+def act_padding_host(act_bytes_host: np.ndarray, M: int, K: int):
+    """The padded rows (m >= M) and padded blocks (b >= K/32) of a q8_1 act buffer, as three
+    flat arrays that must all be zero."""
+    o0, o1, o2 = act_region_offsets("q8_1", M, K)
+    Mp = (M + 31) // 32 * 32
+    KB = K // 32
+    KBp = (KB + 7) // 8 * 8
+    MT = Mp // 32
+    buf = np.asarray(act_bytes_host, dtype=np.uint8)
+    t = buf[o0:o0 + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)
+    xq = t.transpose(0, 3, 1, 2, 4).reshape(Mp, KBp * 32)
+    xs = buf[o1:o1 + MT * KBp * 128].view(np.float32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
+    xsum = buf[o2:o2 + MT * KBp * 128].view(np.int32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
+    pads = [xq[M:].ravel(), xq[:, K:].ravel(), xs[M:].ravel(), xs[:, KB:].ravel(),
+            xsum[M:].ravel(), xsum[:, KB:].ravel()]
+    return np.concatenate([p.astype(np.float64) for p in pads]) if pads else np.zeros(0)

@@ -1,0 +1,130 @@
+// api.cpp - the extern "C" entry points declared in include/mmq.h: argument validation on the
+// host, then a launch on the caller's stream. Nothing here allocates device memory.
+#include "mmq_internal.h"
+
+using namespace mmq;
+
+namespace {
+
+constexpr int64_t MAX_DIM = int64_t(1) << 24;    // keeps every index of the kernels in int32
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_wtype(int t) { return t >= MMQ_Q8_0 && t <= MMQ_I8_ROW; }
+bool valid_atype(int a) { return a == MMQ_ACT_Q8_1 || a == MMQ_ACT_I8_TOKEN; }
+bool valid_otype(int o) { return o >= MMQ_OUT_F32 && o <= MMQ_OUT_I32_PARTIALS; }
+
+int64_t k_multiple(mmq_wtype t) { return (t == MMQ_Q4_K || t == MMQ_IQ1T) ? 256 : 32; }
+
+bool sizes_ok(int64_t M, int64_t N, int64_t K) {
+    return M >= 1 && N >= 1 && K >= 32 && M <= MAX_DIM && N <= MAX_DIM && K <= MAX_DIM;
+}
+
+mmq_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return MMQ_OK;
+    if (e == hipErrorNotSupported) return MMQ_EUNSUPPORTED;
+    return MMQ_EHIP;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mmq_status_string(mmq_status s) {
+    switch (s) {
+        case MMQ_OK: return "MMQ_OK";
+        case MMQ_EINVAL: return "MMQ_EINVAL: a size, stride or enum is out of range";
+        case MMQ_EUNSUPPORTED: return "MMQ_EUNSUPPORTED: this format/output combination is not implemented";
+        case MMQ_EALIGN: return "MMQ_EALIGN: a pointer or leading dimension is not 16-byte aligned";
+        case MMQ_EWORKSPACE: return "MMQ_EWORKSPACE: workspace missing or too small";
+        case MMQ_EHIP: return "MMQ_EHIP: the HIP runtime reported an error";
+    }
+    return "unknown mmq_status";
+}
+
+size_t mmq_act_bytes(mmq_atype a, int64_t M, int64_t K) {
+    if (!valid_atype(a) || !sizes_ok(M, 1, K) || K % QK) return 0;
+    if (a == MMQ_ACT_Q8_1) return (size_t)act_q8_1_layout(M, K).bytes;
+    return (size_t)act_i8_layout(M, K).bytes;
+}
+
+mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[3]) {
+    if (!offsets || !valid_atype(a) || !sizes_ok(M, 1, K) || K % QK) return MMQ_EINVAL;
+    if (a == MMQ_ACT_Q8_1) {
+        const ActQ81Layout L = act_q8_1_layout(M, K);
+        offsets[0] = (size_t)L.xq_off;
+        offsets[1] = (size_t)L.xs_off;
+        offsets[2] = (size_t)L.xsum_off;
+    } else {
+        const ActI8Layout L = act_i8_layout(M, K);
+        offsets[0] = (size_t)L.a_off;
+        offsets[1] = (size_t)L.sa_off;
+        offsets[2] = 0;
+    }
+    return MMQ_OK;
+}
+
+mmq_status mmq_quantize_act(mmq_atype a, const float* x, int64_t M, int64_t K, int64_t ldx,
+                            void* act, void* stream) {
+    if (!valid_atype(a) || !sizes_ok(M, 1, K) || K % QK || ldx < K) return MMQ_EINVAL;
+    if (!x || !act) return MMQ_EINVAL;
+    if (!aligned16(x) || !aligned16(act) || (ldx & 3)) return MMQ_EALIGN;
+    hipError_t e = (a == MMQ_ACT_Q8_1) ? launch_quantize_q8_1(x, M, K, ldx, act, as_stream(stream))
+                                       : launch_quantize_i8_token(x, M, K, ldx, act, as_stream(stream));
+    return from_hip(e);
+}
+
+size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K) {
+    if (!valid_wtype(t) || !sizes_ok(1, N, K) || K % k_multiple(t)) return 0;
+    return (size_t)packed_layout(t, N, K).bytes;
+}
+
+mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const float* row_scale, int64_t N,
+                              int64_t K, void* packed, void* stream) {
+    if (!valid_wtype(t) || !sizes_ok(1, N, K) || K % k_multiple(t)) return MMQ_EINVAL;
+    if (!raw || !packed) return MMQ_EINVAL;
+    if ((t == MMQ_I8_ROW) != (row_scale != nullptr)) return MMQ_EINVAL;
+    if (!aligned16(raw) || !aligned16(packed) || (row_scale && !aligned16(row_scale))) return MMQ_EALIGN;
+    return from_hip(launch_repack(t, raw, row_scale, N, K, packed, as_stream(stream)));
+}
+
+mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
+                    int64_t K, mmq_otype o, void* out, int64_t ldo, void* stream) {
+    if (!valid_wtype(t) || !valid_otype(o) || !sizes_ok(M, N, K) || K % k_multiple(t)) return MMQ_EINVAL;
+    if (!packed || !act || !out) return MMQ_EINVAL;
+    if (ldo < N) return MMQ_EINVAL;
+    if (o == MMQ_OUT_I32_PARTIALS && ldo != N) return MMQ_EINVAL;
+    if (t == MMQ_I8_ROW) {
+        if (o == MMQ_OUT_F32) return MMQ_EUNSUPPORTED;
+    } else {
+        if (o == MMQ_OUT_BF16) return MMQ_EUNSUPPORTED;
+        if (o == MMQ_OUT_I32_PARTIALS && M * N * (K / QK) > (int64_t(1) << 31)) return MMQ_EINVAL;
+    }
+    if (!aligned16(packed) || !aligned16(act) || !aligned16(out)) return MMQ_EALIGN;
+    return from_hip(launch_gemm(t, packed, act, M, N, K, o, out, ldo, as_stream(stream)));
+}
+
+size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
+    if (E < 1 || T < 1 || top_k < 1 || top_k > E || E > 4096 || T * top_k > MAX_DIM) return 0;
+    return gemm_id_workspace_bytes(E, T, top_k);
+}
+
+mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
+                       const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
+                       mmq_otype o, void* out, void* workspace, size_t ws_bytes, void* stream) {
+    if (!valid_wtype(t) || !valid_otype(o) || !sizes_ok(T, N, K) || K % k_multiple(t)) return MMQ_EINVAL;
+    if (E < 1 || top_k < 1 || top_k > E || E > 4096 || T * top_k > MAX_DIM) return MMQ_EINVAL;
+    if (!packed || !act || !ids || !out) return MMQ_EINVAL;
+    if (t == MMQ_I8_ROW || o != MMQ_OUT_F32) return MMQ_EUNSUPPORTED;
+    const size_t need = gemm_id_workspace_bytes(E, T, top_k);
+    if (!workspace || ws_bytes < need) return MMQ_EWORKSPACE;
+    if (!aligned16(packed) || !aligned16(act) || !aligned16(ids) || !aligned16(out) ||
+        !aligned16(workspace))
+        return MMQ_EALIGN;
+    return from_hip(launch_gemm_id(t, packed, E, act, ids, T, top_k, N, K, out, workspace, ws_bytes,
+                                   as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+/*
+ * mmq.h - C ABI of the MI355X (gfx950) prefill MMQ library, libmmq.so.
+ *
+ * MMQ ("matrix multiplication with quantized weights") computes
+ *
+ *     out[m,n] = sum over 32-value k-blocks b of (xs[m,b] * wd[n,b]) * sum_{k in b} xq[m,k] * wq[n,k]
+ *
+ * with weights kept in their raw block-quantised form, activations quantised once per
+ * call to q8_1 (int8 values, one scale and one integer sum per 32 values), every int8 x
+ * int8 block dot accumulated exactly in int32, and the f32 block scale applied once per
+ * block. Definition: "A Negative Result on int8 Tensor-Core MMQ" (Hanzo paper 07.5),
+ * section 2; minfer "08 . R1 - int8 MMQ prefill GEMM", sections 2.1-2.2 and 3.2.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked (device) are device pointers on the current HIP device; (host) are
+ *    host pointers. The caller allocates and frees every buffer; the library never
+ *    allocates or frees memory and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). All device
+ *    work is enqueued asynchronously on it; nothing synchronises.
+ *  - Arguments are validated on the host before anything is enqueued. On any error the
+ *    call returns a non-zero status and enqueues nothing. A failed kernel launch returns
+ *    MMQ_EHIP. Faults inside kernels surface at the caller's next stream synchronisation.
+ *  - Every device pointer must be 16-byte aligned (MMQ_EALIGN otherwise).
+ *  - Sizes are int64_t; M, N >= 1; K >= 32.
+ */
+#ifndef MMQ_H
+#define MMQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MMQ_OK = 0,
+    MMQ_EINVAL = 1,        /* a size, stride or enum is out of range */
+    MMQ_EUNSUPPORTED = 2,  /* valid enums, but the combination is not implemented */
+    MMQ_EALIGN = 3,        /* a pointer or leading dimension breaks the alignment rule */
+    MMQ_EWORKSPACE = 4,    /* the workspace is missing or too small */
+    MMQ_EHIP = 5           /* the HIP runtime reported an error (launch failure) */
+} mmq_status;
+
+/* Raw weight formats (row-major: row n of W is K consecutive values, stored as blocks).
+ * Byte layouts (little-endian):
+ *  MMQ_Q8_0  34 B per 32 values: f16 d, int8 q[32].                      w = d*q
+ *  MMQ_Q4_0  18 B per 32 values: f16 d, u8 qs[16]; value j = qs[j]&15, value j+16 =
+ *            qs[j]>>4.                                                   w = d*(nib-8)
+ *  MMQ_Q4_K  144 B per 256 values: f16 d, f16 dmin, 6 B of eight 6-bit sub-block scales
+ *            sc (LSB-first), 6 B of eight 6-bit mins m, u8 qs[128]; sub-block j uses
+ *            qs[16j..16j+15], low nibble = value 32j+i, high = value 32j+16+i.
+ *                                                             w = d*sc_j*nib - dmin*m_j
+ *  MMQ_IQ1T  76 B per 256 values (IQ1_M-style ternary): u8 codes[64] (2-bit c = g+1, four
+ *            per byte LSB-first, c = 3 invalid), 6 B of sixteen 3-bit sub-scales s (one per
+ *            16 values, LSB-first), 4 B of 32 sign bits (one per 8 values, 0 -> +1/8,
+ *            1 -> -1/8), f16 d.                                   w = d*(2s+1)*(g+delta)
+ *  MMQ_I8_ROW int8 [N][K] plus one f32 scale per row (per-channel W8A8).  w = sw[n]*q
+ * Value formulas: minfer R1 sections 1-2.2 (q8_0, q4_0, Q4_K); llama.cpp PR #304
+ * description (IQ1_M); metainfer "INT8 W8A8 GEMM - Prefill" section 1 (per-channel). */
+typedef enum { MMQ_Q8_0 = 0, MMQ_Q4_0 = 1, MMQ_Q4_K = 2, MMQ_IQ1T = 3, MMQ_I8_ROW = 4 } mmq_wtype;
+
+/* Activation formats.
+ *  MMQ_ACT_Q8_1     per 32-value block: amax = max|x|; d = amax/127 (f32); q = clamp(
+ *                   round-half-even(x * (1/d)), -128, 127) (q = 0 if d = 0); the stored scale
+ *                   xs = d rounded to f16 (kept as f32); xsum = sum of the 32 q
+ *                   (minfer R1 section 3.2 CPU reference; section 2.2 block sum).
+ *  MMQ_ACT_I8_TOKEN one block per row (the whole of K), scale kept in f32 (metainfer W8A8
+ *                   section 1: int8 activations with a per-token f32 scale). */
+typedef enum { MMQ_ACT_Q8_1 = 0, MMQ_ACT_I8_TOKEN = 1 } mmq_atype;
+
+/* Output types.
+ *  MMQ_OUT_F32          f32 [M][ldo] (block-quantised formats)
+ *  MMQ_OUT_BF16         bf16 [M][ldo]: bf16_rne((f32(acc) * sa[m]) * sw[n]), for MMQ_I8_ROW
+ *                       with MMQ_ACT_I8_TOKEN only (metainfer section 1: fragment -> scale ->
+ *                       bf16, no bias)
+ *  MMQ_OUT_I32_PARTIALS debug: block formats: int32 [M][N][K/32] of the exact per-block
+ *                       integer dots (Q4_K: sum xq*nib with unsigned nibbles; IQ1T: the folded
+ *                       sum_h (2s_h+1) * sum_16 xq*(8g+-1)); MMQ_I8_ROW: int32 [M][N] of the
+ *                       full-K accumulators. ldo must equal N. Same kernels as the scaled
+ *                       outputs, the scale step replaced by a store. */
+typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq_otype;
+
+/* ---------------------------------------------------------------------------------------
+ * Activation buffer ("act"). Opaque to most callers, but its layout is fixed so that other
+ * producers can fill it. Let Mp = M rounded up to 32, KB = K/32, KBp = KB rounded up to 8.
+ *
+ * MMQ_ACT_Q8_1 (three regions, each starting on a 256-byte boundary):
+ *   region 0  xq   int8, Mp*KBp*32 bytes, tiled for the matrix cores: the 32x32 tile
+ *                  (row tile mt = m/32, block b) occupies bytes [(mt*KBp + b)*1024, +1024);
+ *                  inside it, row r = m%32 and k' = k%32 sit at ((k'/16)*32 + r)*16 + k'%16.
+ *   region 1  xs   f32 [Mp/32][KBp][32]: xs of (row mt*32+r, block b) at (mt*KBp + b)*32 + r.
+ *   region 2  xsum int32, same indexing as xs.
+ *   Rows m >= M and blocks b >= KB hold zeros.
+ * MMQ_ACT_I8_TOKEN (two regions):
+ *   region 0  a    int8 [M][K] row-major (row stride K).
+ *   region 1  sa   f32 [M], starting at the first 256-byte boundary after region 0.
+ * --------------------------------------------------------------------------------------- */
+
+/* Total bytes of an act buffer; 0 if the arguments are invalid. (host only) */
+size_t mmq_act_bytes(mmq_atype a, int64_t M, int64_t K);
+
+/* Byte offsets of the act buffer's regions (offsets[2] = 0 for MMQ_ACT_I8_TOKEN).
+ * Returns MMQ_EINVAL for invalid arguments. (host only) */
+mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[3]);
+
+/* Quantise f32 activations x [M][ldx] (device, row stride ldx >= K floats) into `act`
+ * (device, mmq_act_bytes(a, M, K) bytes). Deterministic and bit-exact with the definition
+ * above. K must be a multiple of 32. (minfer R1 section 3.2 for q8_1; W8A8 section 1 for
+ * the per-token form.) */
+mmq_status mmq_quantize_act(mmq_atype a, const float* x, int64_t M, int64_t K, int64_t ldx,
+                            void* act, void* stream);
+
+/* Bytes of the packed (repacked) weight buffer for one N x K matrix; 0 if invalid. */
+size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K);
+
+/* One-time, untimed repack of raw weights into the library's matrix-core panel layout.
+ *  raw       (device) raw rows as described at mmq_wtype; for MMQ_I8_ROW the int8 [N][K]
+ *            values.
+ *  row_scale (device) f32 [N] per-row scales, MMQ_I8_ROW only; must be NULL otherwise.
+ *  packed    (device) mmq_packed_bytes(t, N, K) bytes; written completely (padding rows
+ *            are zero). Immutable afterwards and safe to reuse across graph replays
+ *            (metainfer section 3.2: one-time pack outside the timed region).
+ * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, IQ1T). An invalid IQ1T
+ * code (3) decodes as 0 - the caller must not pass one. */
+mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const float* row_scale,
+                              int64_t N, int64_t K, void* packed, void* stream);
+
+/* The MMQ contraction out = act x packed^T.
+ *  packed (device) from mmq_repack_weights(t, ..., N, K, ...)
+ *  act    (device) from mmq_quantize_act (MMQ_ACT_Q8_1 for the block formats,
+ *         MMQ_ACT_I8_TOKEN for MMQ_I8_ROW) with the same M and K
+ *  out    (device) o = MMQ_OUT_F32: f32 [M][ldo]; MMQ_OUT_BF16: bf16 [M][ldo];
+ *         MMQ_OUT_I32_PARTIALS: see mmq_otype (ldo = N). Columns n >= N of each row are
+ *         left untouched.
+ *  ldo    >= N, in elements.
+ * Supported (t, o): block formats with F32 or I32_PARTIALS; I8_ROW with BF16 or
+ * I32_PARTIALS. */
+mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
+                    int64_t K, mmq_otype o, void* out, int64_t ldo, void* stream);
+
+/* Workspace bytes needed by mmq_gemm_id for E experts, T tokens, top_k slots. */
+size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
+
+/* MUL_MAT_ID (expert-routed MoE, llama.cpp PR #304: MUL_MAT_ID through MMQ):
+ *     out[t][j][:] = act[t] x W_{ids[t][j]}^T      for t < T, j < top_k
+ *  packed    (device) E packed matrices back to back, each mmq_packed_bytes(t, N, K) bytes
+ *  act       (device) MMQ_ACT_Q8_1 act of T rows
+ *  ids       (device) int32 [T][top_k], each in [0, E). Pairs with an id outside [0, E) are
+ *            skipped (their output rows are left untouched).
+ *  out       (device) f32 [T][top_k][N]
+ *  workspace (device) >= mmq_gemm_id_workspace_bytes(E, T, top_k) bytes of scratch; its
+ *            contents need no initialisation and are overwritten.
+ * The expert grouping (count, scan, scatter, tile list) runs on the device with no host
+ * round trip, so the call is stream-ordered and capturable. Block formats only; o must be
+ * MMQ_OUT_F32. */
+mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
+                       const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
+                       mmq_otype o, void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code (host). */
+const char* mmq_status_string(mmq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMQ_H */

@@ -1,0 +1,153 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports every entry point
+include/mmq.h declares, sizes its buffers as documented, and rejects bad arguments on the
+host before touching the device (every call here returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mmq.h")
+
+
+@pytest.fixture(scope="module")
+def mmq():
+    import block_quantized_int8_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from block_quantized_int8_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mmq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = _declared_functions()
+    for fn in ["mmq_quantize_act", "mmq_repack_weights", "mmq_gemm", "mmq_gemm_id"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(mmq):
+    L = mmq.lib()
+    for fn in _declared_functions():
+        assert hasattr(L, fn), fn
+
+
+def test_status_strings(mmq):
+    for code in range(6):
+        assert mmq.status_string(code).startswith("MMQ_")
+    assert "unknown" in mmq.status_string(99)
+
+
+def test_act_bytes_and_offsets(mmq):
+    M, K = 70, 96                      # Mp = 96, KB = 3, KBp = 8
+    o = mmq.act_region_offsets("q8_1", M, K)
+    assert o[0] == 0
+    assert o[1] == 3 * 8 * 1024        # xq region: MT * KBp * 1 KB
+    assert o[2] == o[1] + 3 * 8 * 128
+    assert mmq.act_bytes("q8_1", M, K) == o[2] + 3 * 8 * 128
+    assert all(v % 256 == 0 for v in o)
+    oi = mmq.act_region_offsets("i8_token", 3, 64)
+    assert oi == (0, 256, 0)
+    assert mmq.act_bytes("i8_token", 3, 64) == 512
+    assert mmq.act_bytes("q8_1", 4, 33) == 0         # K not a multiple of 32
+    assert mmq.act_bytes("q8_1", 0, 64) == 0
+    assert mmq.act_bytes(7, 4, 64) == 0
+
+
+def test_packed_bytes(mmq):
+    # q4_0: NT=2, KBp=8 -> 2*8*512 B fragments + 2*8*32*2 B f16 scales
+    assert mmq.packed_bytes("q4_0", 40, 64) == 2 * 8 * 512 + 2 * 8 * 64
+    assert mmq.packed_bytes("q8_0", 32, 256) == 8 * 1024 + 8 * 64
+    assert mmq.packed_bytes("i8_row", 33, 32) == 2 * 8 * 1024 + 256
+    assert mmq.packed_bytes("q4_K", 32, 128) == 0      # Q4_K needs K % 256 == 0
+    assert mmq.packed_bytes("iq1t", 32, 200) == 0
+    assert mmq.packed_bytes(9, 32, 64) == 0
+
+
+def test_validation_rejects_before_any_launch(mmq):
+    L = mmq.lib()
+    BAD = ctypes.c_void_p(0x1001)      # misaligned, never dereferenced
+    GOOD = ctypes.c_void_p(0x10000)    # aligned, never dereferenced (validation fails first)
+    # null pointers
+    assert L.mmq_quantize_act(0, None, 4, 64, 64, GOOD, None) == mmq.MMQ_EINVAL
+    assert L.mmq_gemm(0, None, GOOD, 4, 32, 64, 0, GOOD, 32, None) == mmq.MMQ_EINVAL
+    # sizes / strides / enums
+    assert L.mmq_quantize_act(0, GOOD, 4, 48, 48, GOOD, None) == mmq.MMQ_EINVAL      # K % 32
+    assert L.mmq_quantize_act(0, GOOD, 4, 64, 32, GOOD, None) == mmq.MMQ_EINVAL      # ldx < K
+    assert L.mmq_quantize_act(5, GOOD, 4, 64, 64, GOOD, None) == mmq.MMQ_EINVAL      # atype
+    assert L.mmq_gemm(0, GOOD, GOOD, 4, 32, 64, 0, GOOD, 16, None) == mmq.MMQ_EINVAL   # ldo < N
+    assert L.mmq_gemm(2, GOOD, GOOD, 4, 32, 128, 0, GOOD, 32, None) == mmq.MMQ_EINVAL  # q4_K K
+    assert L.mmq_gemm(0, GOOD, GOOD, 0, 32, 64, 0, GOOD, 32, None) == mmq.MMQ_EINVAL   # M = 0
+    assert L.mmq_gemm(0, GOOD, GOOD, 4, 32, 64, 3, GOOD, 32, None) == mmq.MMQ_EINVAL   # otype
+    assert L.mmq_gemm(0, GOOD, GOOD, 4, 32, 64, 2, GOOD, 40, None) == mmq.MMQ_EINVAL   # partials ldo
+    # unsupported combinations
+    assert L.mmq_gemm(0, GOOD, GOOD, 4, 32, 64, 1, GOOD, 32, None) == mmq.MMQ_EUNSUPPORTED  # q8_0 bf16
+    assert L.mmq_gemm(4, GOOD, GOOD, 4, 32, 64, 0, GOOD, 32, None) == mmq.MMQ_EUNSUPPORTED  # i8 f32
+    # alignment
+    assert L.mmq_quantize_act(0, BAD, 4, 64, 64, GOOD, None) == mmq.MMQ_EALIGN
+    assert L.mmq_quantize_act(0, GOOD, 4, 64, 66, GOOD, None) == mmq.MMQ_EALIGN     # ldx % 4
+    assert L.mmq_gemm(0, GOOD, BAD, 4, 32, 64, 0, GOOD, 32, None) == mmq.MMQ_EALIGN
+    assert L.mmq_repack_weights(1, BAD, None, 32, 64, GOOD, None) == mmq.MMQ_EALIGN
+    # row_scale only with i8_row
+    assert L.mmq_repack_weights(1, GOOD, GOOD, 32, 64, GOOD, None) == mmq.MMQ_EINVAL
+    assert L.mmq_repack_weights(4, GOOD, None, 32, 64, GOOD, None) == mmq.MMQ_EINVAL
+
+
+def test_gemm_id_validation(mmq):
+    L = mmq.lib()
+    GOOD = ctypes.c_void_p(0x10000)
+    ws = mmq.gemm_id_workspace_bytes(64, 512, 8)
+    assert ws > 0 and ws % 256 == 0
+    assert mmq.gemm_id_workspace_bytes(4, 10, 5) == 0           # top_k > E
+    args = lambda wsz, ids=GOOD: (3, GOOD, 64, GOOD, ids, 512, 8, 2048, 4096, 0, GOOD, GOOD, wsz, None)
+    assert L.mmq_gemm_id(*args(ws - 1)) == mmq.MMQ_EWORKSPACE
+    assert L.mmq_gemm_id(*args(ws, None)) == mmq.MMQ_EINVAL
+    assert L.mmq_gemm_id(4, GOOD, 64, GOOD, GOOD, 512, 8, 2048, 4096, 0, GOOD, GOOD, ws, None) == mmq.MMQ_EUNSUPPORTED
+    assert L.mmq_gemm_id(3, GOOD, 64, GOOD, GOOD, 512, 8, 2048, 4096, 1, GOOD, GOOD, ws, None) == mmq.MMQ_EUNSUPPORTED
+
+
+def test_act_to_host_layout_decoder(mmq):
+    # build a q8_1 act image by hand from the header's formula and decode it back
+    M, K = 40, 96
+    o0, o1, o2 = mmq.act_region_offsets("q8_1", M, K)
+    Mp, KB, KBp = 64, 3, 8
+    buf = np.zeros(mmq.act_bytes("q8_1", M, K), np.uint8)
+    r = np.random.default_rng(0)
+    xq = r.integers(-128, 128, (M, K)).astype(np.int8)
+    xs = r.random((M, KB)).astype(np.float32)
+    xsum = r.integers(-4000, 4000, (M, KB)).astype(np.int32)
+    for m in range(M):
+        for k in range(K):
+            mt, b, kk = m // 32, k // 32, k % 32
+            buf[o0 + (mt * KBp + b) * 1024 + ((kk // 16) * 32 + m % 32) * 16 + kk % 16] = xq[m, k].view(np.uint8)
+        for b in range(KB):
+            idx = ((m // 32) * KBp + b) * 32 + m % 32
+            buf[o1 + 4 * idx:o1 + 4 * idx + 4] = np.frombuffer(xs[m, b].tobytes(), np.uint8)
+            buf[o2 + 4 * idx:o2 + 4 * idx + 4] = np.frombuffer(xsum[m, b].tobytes(), np.uint8)
+    a, s, u = mmq.act_to_host(buf, M, K)
+    assert np.array_equal(a, xq) and np.array_equal(s, xs) and np.array_equal(u, xsum)
+    assert np.all(mmq.act_padding_host(buf, M, K) == 0)
+
+
+def test_product_path_does_not_import_oracle():
+    # the HIP path and the oracle share no code: no import of oracle/ from the package
+    pkg = os.path.join(ROOT, "block_quantized_int8_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "mmq_oracle" not in text, f
+    # and the oracle does not import the package
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "block_quantized_int8_amd" not in text, f
