@@ -1,20 +1,25 @@
 """Benchmark of the prefill MMQ hot path on one MI355X.
 
-A step is one pass of the whole hot path over one batch: quantise f32 activations to q8_1
-(a1) and run the MMQ contraction with raw q4_0 weights (a3-a6). The weight repack (a2) is
-one-time and untimed, as on the pages (metainfer section 3.2). Workload: q4_0 weights
-N=4096 x K=4096 from N(0,0.02), activations M=2048 x K=4096 from N(0,1) with 0.1% outliers
-x20, f32 output - the q4_0 prefill shape of the MMQ pages' 7B-class models, synthetic and
-seeded (gen.CONFIGS["cfg2a_q4_0"]).
+A step is one pass of the whole hot path over one batch: quantise the f32 activations to q8_1
+(a1) and run the MMQ contraction with the raw block weights (a3-a6; for MoE the device-side
+expert grouping a7 as well). The weight repack (a2) is one-time and untimed, as on the pages
+(metainfer section 3.2). Inputs are synthetic and seeded (gen.CONFIGS), resident in HBM before
+the timed region starts.
+
+Default workload: q4_0 weights N=4096 x K=4096 from N(0,0.02), activations M=2048 x K=4096
+from N(0,1) with 0.1% outliers x20, f32 output - the q4_0 prefill shape of the MMQ pages'
+7B-class models. `--workload` selects another of gen.CONFIGS for reference measurements (the
+W8A8 workload's activations are int8 already, so its step is the GEMM alone).
 
 Prints ONE JSON line on stdout:
-  value         whole-step throughput, TOPS = 2*M*N*K / step time (inputs resident in HBM)
-  roofline      the MMQ kernel alone: algorithmic ops per launch / its mean launch time
-                (HIP events on the launch stream, over the timed steps) against the int8
-                MFMA dense peak (5.0 POP/s); traffic = HBM bytes per launch from rocprofv3
-                counters when measured for this exact kernel, else null
-  cpu_baseline  the CPU oracle (quantiser + per-block integer GEMM in C, OpenMP) timed on
-                this host's cores on the same workload
+  value         whole-step throughput, TOPS = 2*M*N*K / step time (2*T*top_k*N*K for MoE)
+  roofline      the dominant kernel alone: algorithmic ops (or bytes) per launch / its mean
+                launch time (HIP events on the launch stream, over the timed steps) against the
+                MI355X dense int8 MFMA peak (5.0 POP/s) or HBM peak (8 TB/s); traffic = HBM
+                bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters scaled by the
+                copy-kernel calibration, when measured for this exact kernel, else null
+  cpu_baseline  the CPU oracle (quantiser + per-block integer GEMM in C, OpenMP) timed on this
+                host's cores, repeated over the workload for a bounded ~10 s
 Diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -32,31 +37,87 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+HEADLINE = "cfg2a_q4_0"
+METRIC = "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MFMA peak"
 
-# HBM bytes per MMQ launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the kernel
-# version this file ships with (see profiles/); None until measured.
-MEASURED_TRAFFIC_BYTES = None
+# HBM bytes per launch of the dominant kernel, measured with rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE for the kernel version this file ships with and scaled by the copy-kernel factor
+# (profiles/ holds the summaries); None until measured for the current kernel.
+MEASURED_TRAFFIC_BYTES = {}
+
+RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(raw, x, fmt, M, N, K, runs=3):
-    """The oracle as it stands, timed on the host: q8_1 quantisation + per-block GEMM."""
+def cpu_baseline(fmt, raw, x, M, N, K, budget_s=10.0, min_runs=3, max_runs=50):
+    """The oracle as it stands, timed on the host: q8_1 quantisation + per-block C GEMM over
+    the whole workload, repeated until about `budget_s` seconds of CPU work (median reported)."""
     import oracle
     oracle.build()
     times = []
-    for _ in range(runs):
+    t_start = time.perf_counter()
+    while len(times) < min_runs or (time.perf_counter() - t_start < budget_s and len(times) < max_runs):
         t0 = time.perf_counter()
-        xq, xs, xsum = oracle.quantize_q8_1(x)
-        oracle.gemm_c(fmt, raw, N, K, xq, xs, xsum)
+        if fmt == "i8_row":
+            a, sa, w, sw = x
+            oracle.gemm_w8a8(a, sa, w, sw)
+        else:
+            xq, xs, xsum = oracle.quantize_q8_1(x)
+            oracle.gemm_c(fmt, raw, N, K, xq, xs, xsum)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
+    what = "W8A8 int GEMM + bf16 epilogue" if fmt == "i8_row" else "quantize_q8_1 + per-block C GEMM"
     return {"value": 2.0 * M * N * K / t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"full workload (all {M} rows), median of {runs} runs of quantize_q8_1 + "
-                      f"per-block C GEMM; {t:.2f} s per run"}
+            "sample": f"full workload (M={M}, N={N}, K={K}) repeated {len(times)}x "
+                      f"({sum(times):.1f} s of CPU work), median {t:.3f} s per run of {what}"}
+
+
+def cpu_baseline_moe(raw_e, x, ids, E, N, K, budget_s=10.0):
+    """MoE oracle leg on a bounded sample: the dense per-block C GEMM of the tokens routed to
+    the first experts (in expert order) until ~budget_s seconds, scaled to pair-rows per s."""
+    import oracle
+    oracle.build()
+    xq, xs, xsum = oracle.quantize_q8_1(x)
+    rows_done, t_used, experts = 0, 0.0, 0
+    for e in range(E):
+        tt = np.nonzero((ids == e).any(axis=1))[0]
+        if len(tt) == 0:
+            continue
+        t0 = time.perf_counter()
+        oracle.gemm_c("iq1t", raw_e[e], N, K, xq[tt], xs[tt], xsum[tt])
+        t_used += time.perf_counter() - t0
+        rows_done += len(tt)
+        experts += 1
+        if t_used >= budget_s:
+            break
+    ops = 2.0 * rows_done * N * K
+    return {"value": ops / t_used / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{experts} of {E} experts ({rows_done} routed token rows) through the per-block "
+                      f"C GEMM, {t_used:.1f} s"}
+
+
+def timed(step_fn, steps, warmup, nev):
+    """Wall clock over exactly `steps` steps (synchronised both sides), then the same number of
+    steps again with HIP events around each launch for per-kernel durations."""
+    import torch
+    for _ in range(warmup):
+        step_fn(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step_fn(None)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    for i in range(steps):
+        step_fn(evs[i])
+    torch.cuda.synchronize()
+    spans = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nev - 1)] for e in evs]) * 1e-3
+    return step_s, spans.mean(axis=0), np.median(spans, axis=0)
 
 
 def main():
@@ -64,76 +125,152 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE, help="one of gen.CONFIGS")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy 5x (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path is single-GPU; sharding is design-only)", file=sys.stderr)
+              f"(the path is single-GPU; how it would shard is design-only)", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import block_quantized_int8_amd as mmq
     import gen
 
-    cfg = gen.CONFIGS["cfg2a_q4_0"]
+    name = args.workload
+    cfg = gen.CONFIGS[name]
     fmt, M, N, K = cfg["fmt"], cfg["M"], cfg["N"], cfg["K"]
     dev = torch.device("cuda:0")
-    raw = gen.weights(fmt, N, K, seed=0, cfg=cfg["cfg"])
-    x = gen.act_f32(M, K, seed=0, cfg=cfg["cfg"], outlier_rate=cfg["outlier_rate"])
-    log(f"[bench] workload {fmt} M={M} N={N} K={K}")
-
-    xd = torch.from_numpy(x).to(dev)
-    packed = mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K)   # untimed, one-time
-    act = torch.empty(mmq.act_bytes("q8_1", M, K), dtype=torch.uint8, device=dev)
-    out = torch.empty((M, N), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        mmq.quantize_act(xd, out=act)
-        if ev is not None:
-            ev[1].record()
-        mmq.gemm(fmt, packed, act, M, N, K, "f32", out=out)
-        if ev is not None:
-            ev[2].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: exactly `steps` steps, synchronised on both sides
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_s = (t1 - t0) / args.steps
-
-    # per-kernel durations from HIP events on the launch stream (same steps, recorded apart so
-    # the event records do not perturb the wall-clock figure above)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    g_ms_med = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-
+    log(f"[bench] workload {name}: {fmt} M={M} N={N} K={K}")
     ops = 2.0 * M * N * K
-    tops = ops / step_s / 1e12
-    gemm_tops = ops / (g_ms * 1e-3) / 1e12
-    # algorithmic bytes of one MMQ launch: raw q4_0 weights + q8_1 activations + f32 output
-    alg_bytes = N * K // 32 * 18 + M * K + M * (K // 32) * 4 + M * N * 4
-    log(f"[bench] step {step_s * 1e6:.1f} us ({tops:.1f} TOPS); quantize {q_ms * 1e3:.1f} us; "
-        f"mmq mean {g_ms * 1e3:.1f} us / median {g_ms_med * 1e3:.1f} us ({gemm_tops:.1f} TOPS, "
-        f"{100 * gemm_tops / INT8_PEAK_TOPS:.1f}% int8 peak)")
-    q_bytes = M * K * 4 + mmq.act_bytes("q8_1", M, K)
-    log(f"[bench] quantize {q_bytes / (q_ms * 1e-3) / 1e9:.0f} GB/s "
-        f"({100 * q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS:.1f}% HBM)")
+    extra = {}
 
+    if fmt == "i8_row":
+        a, sa = gen.i8_rows(M, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_ACT)
+        w, sw = gen.i8_rows(N, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_WEIGHT)
+        packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
+                                    row_scale=torch.from_numpy(sw).to(dev))
+        ab = mmq.act_bytes("i8_token", M, K)
+        o0, o1 = mmq.act_region_offsets("i8_token", M, K)[:2]
+        act_h = np.zeros(ab, np.uint8)
+        act_h[o0:o0 + M * K] = a.view(np.uint8).ravel()
+        act_h[o1:o1 + 4 * M] = sa.view(np.uint8)
+        act = torch.from_numpy(act_h).to(dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def step(ev):
+            if ev is not None:
+                ev[0].record()
+            mmq.gemm("i8_row", packed, act, M, N, K, "bf16", out=out)
+            if ev is not None:
+                ev[1].record()
+        nev, kernel_names = 2, ["w8a8_gemm"]
+        dom = 0
+        alg_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
+        bound = "mfma"
+        cpu_args = ("i8_row", None, (a, sa, w, sw), M, N, K)
+    elif "E" in cfg:
+        E, top_k = cfg["E"], cfg["top_k"]
+        T = M
+        raw_e = gen.moe_weights(fmt, E, N, K, seed=0, cfg=cfg["cfg"])
+        x = gen.act_f32(T, K, seed=0, cfg=cfg["cfg"])
+        ids = gen.moe_ids(T, top_k, E, seed=0, cfg=cfg["cfg"])
+        pb = mmq.packed_bytes(fmt, N, K)
+        packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
+        for e in range(E):
+            mmq.repack_weights(fmt, torch.from_numpy(np.ascontiguousarray(raw_e[e])).to(dev), N, K,
+                               out=packed[e * pb:(e + 1) * pb])
+        xd = torch.from_numpy(x).to(dev)
+        ids_d = torch.from_numpy(ids).to(dev)
+        act = torch.empty(mmq.act_bytes("q8_1", T, K), dtype=torch.uint8, device=dev)
+        out = torch.empty((T, top_k, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(mmq.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
+
+        def step(ev):
+            if ev is not None:
+                ev[0].record()
+            mmq.quantize_act(xd, out=act)
+            if ev is not None:
+                ev[1].record()
+            mmq.gemm_id(fmt, packed, E, act, ids_d, T, top_k, N, K, out=out, workspace=ws)
+            if ev is not None:
+                ev[2].record()
+        nev, kernel_names = 3, ["quantize_q8_1", "gemm_id (route + gather MMQ)"]
+        dom = 1
+        ops = 2.0 * T * top_k * N * K
+        used = len(np.unique(ids))
+        alg_bytes = int(used * N * K / 32 * RAW_BYTES_PER_32[fmt]) + T * K + T * (K // 32) * 8 + \
+            T * top_k * N * 4 + T * top_k * 4
+        bound = "hbm"
+        cpu_args = None
+        extra = {"E": E, "top_k": top_k, "experts_used": used}
+    else:
+        raw = gen.weights(fmt, N, K, seed=0, cfg=cfg["cfg"])
+        x = gen.act_f32(M, K, seed=0, cfg=cfg["cfg"], outlier_rate=cfg.get("outlier_rate", 0.0))
+        xd = torch.from_numpy(x).to(dev)
+        packed = mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K)
+        act = torch.empty(mmq.act_bytes("q8_1", M, K), dtype=torch.uint8, device=dev)
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+        def step(ev):
+            if ev is not None:
+                ev[0].record()
+            mmq.quantize_act(xd, out=act)
+            if ev is not None:
+                ev[1].record()
+            mmq.gemm(fmt, packed, act, M, N, K, "f32", out=out)
+            if ev is not None:
+                ev[2].record()
+        nev, kernel_names = 3, ["quantize_q8_1", "mmq_block"]
+        dom = 1
+        # raw weights + q8_1 activations (int8 values, f32 scale, int32 sum) + f32 output
+        alg_bytes = int(N * K / 32 * RAW_BYTES_PER_32[fmt]) + M * K + M * (K // 32) * 8 + M * N * 4
+        bound = "mfma"
+        cpu_args = (fmt, raw, x, M, N, K)
+
+    torch.cuda.synchronize()
+    step_s, mean_s, med_s = timed(step, args.steps, args.warmup, nev)
+    tops = ops / step_s / 1e12
+    for i, kn in enumerate(kernel_names):
+        log(f"[bench] {kn}: mean {mean_s[i] * 1e6:.2f} us, median {med_s[i] * 1e6:.2f} us")
+    k_s = float(mean_s[dom])
+    k_tops = ops / k_s / 1e12
+    k_gbs = alg_bytes / k_s / 1e9
+    log(f"[bench] step {step_s * 1e6:.1f} us ({tops:.1f} TOPS, {100 * tops / INT8_PEAK_TOPS:.1f}% int8 peak); "
+        f"dominant kernel {k_s * 1e6:.1f} us = {k_tops:.1f} TOPS ({100 * k_tops / INT8_PEAK_TOPS:.1f}% int8), "
+        f"{k_gbs:.0f} GB/s algorithmic ({100 * k_gbs / HBM_PEAK_GBS:.1f}% HBM)")
+    if nev == 3 and dom == 1:
+        q_bytes = M * K * 4 + mmq.act_bytes("q8_1", M, K)
+        q_s = float(mean_s[0])
+        log(f"[bench] quantize {q_bytes / q_s / 1e9:.0f} GB/s ({100 * q_bytes / q_s / 1e9 / HBM_PEAK_GBS:.1f}% HBM)")
+        extra["quantize_kernel_us"] = round(q_s * 1e6, 2)
+
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(k_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(k_tops / INT8_PEAK_TOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = MEASURED_TRAFFIC_BYTES.get(name)
+    roof["kernel"] = kernel_names[dom]
+    roof["kernel_us"] = round(k_s * 1e6, 2)
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["algorithmic_ops"] = ops
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 5 x 256 MiB device-to-device")
+
+    desc = {"cfg2a_q4_0": "q4_0 MMQ prefill: raw q4_0 weights N=4096 K=4096, q8_1 activations M=2048 "
+                          "(quantised in-step), f32 out"}
     rec = {
-        "metric": "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MFMA peak",
+        "metric": METRIC if name == HEADLINE else f"MMQ TOPS (2MNK/s) on {name}",
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -145,22 +282,22 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": "q4_0 MMQ prefill: raw q4_0 weights N=4096 K=4096, q8_1 activations "
-                               "M=2048 (quantised in-step), f32 out",
-                   "M": M, "N": N, "K": K, "weights": "q4_0", "activations": "q8_1",
-                   "step": "quantize_act + gemm (repack untimed)"},
+        "config": {"workload": desc.get(name, name), "M": M, "N": N, "K": K, "weights": fmt,
+                   "activations": "i8_token" if fmt == "i8_row" else "q8_1",
+                   "step": "gemm (int8 activations given)" if fmt == "i8_row" else
+                           "quantize_act + gemm" + ("_id" if "E" in cfg else "") + " (repack untimed)",
+                   **extra},
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
-        "mmq_kernel_us": round(g_ms * 1e3, 2),
-        "quantize_kernel_us": round(q_ms * 1e3, 2),
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": MEASURED_TRAFFIC_BYTES,
-                     "algorithmic_bytes": alg_bytes},
+        "roofline": roof,
     }
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle) ...")
-        rec["cpu_baseline"] = cpu_baseline(raw, x, fmt, M, N, K)
-        log(f"[bench] cpu baseline {rec['cpu_baseline']['value']:.4f} TOPS on {rec['cpu_baseline']['cores']} threads")
+        if cpu_args is not None:
+            rec["cpu_baseline"] = cpu_baseline(*cpu_args)
+        else:
+            rec["cpu_baseline"] = cpu_baseline_moe(raw_e, x, ids, E, N, K)
+        log(f"[bench] cpu baseline {rec['cpu_baseline']['value']:.4f} TOPS on "
+            f"{rec['cpu_baseline']['cores']} threads: {rec['cpu_baseline']['sample']}")
     print(json.dumps(rec), flush=True)
 
 

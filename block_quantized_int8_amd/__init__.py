@@ -106,10 +106,10 @@ def act_bytes(atype, M: int, K: int) -> int:
     return int(lib().mmq_act_bytes(_at(atype), M, K))
 
 
-def act_region_offsets(atype, M: int, K: int) -> tuple[int, int, int]:
-    arr = (ctypes.c_size_t * 3)()
+def act_region_offsets(atype, M: int, K: int) -> tuple[int, int, int, int]:
+    arr = (ctypes.c_size_t * 4)()
     _check("mmq_act_region_offsets", lib().mmq_act_region_offsets(_at(atype), M, K, arr))
-    return int(arr[0]), int(arr[1]), int(arr[2])
+    return tuple(int(v) for v in arr)
 
 
 def packed_bytes(wtype, N: int, K: int) -> int:
@@ -187,7 +187,7 @@ def gemm_id(wtype, packed, E: int, act, ids, T: int, top_k: int, N: int, K: int,
 def act_to_host(act_bytes_host: np.ndarray, M: int, K: int):
     """Decode a q8_1 act buffer (copied to host as uint8) into plain row-major
     (xq int8 [M,K], xs f32 [M,K/32], xsum int32 [M,K/32]) following the documented layout."""
-    o0, o1, o2 = act_region_offsets("q8_1", M, K)
+    o0, o1, o2 = act_region_offsets("q8_1", M, K)[:3]
     Mp = (M + 31) // 32 * 32
     KB = K // 32
     KBp = (KB + 7) // 8 * 8
@@ -200,10 +200,32 @@ def act_to_host(act_bytes_host: np.ndarray, M: int, K: int):
     return np.ascontiguousarray(xq), np.ascontiguousarray(xs[:M, :KB]), np.ascontiguousarray(xsum[:M, :KB])
 
 
+def act_xs16_host(act_bytes_host: np.ndarray, M: int, K: int):
+    """Decode region 3 (xs as f16 bits) to f32 [Mp, KBp]; it must equal region 1 exactly,
+    padding included."""
+    o = act_region_offsets("q8_1", M, K)
+    Mp = (M + 31) // 32 * 32
+    KBp = (K // 32 + 7) // 8 * 8
+    MT = Mp // 32
+    buf = np.asarray(act_bytes_host, dtype=np.uint8)
+    xs16 = buf[o[3]:o[3] + MT * KBp * 64].view(np.float16).reshape(MT, KBp, 32).transpose(0, 2, 1)
+    return xs16.reshape(Mp, KBp).astype(np.float32)
+
+
+def act_xs_full_host(act_bytes_host: np.ndarray, M: int, K: int):
+    """Region 1 (xs f32) as [Mp, KBp], padding included."""
+    o = act_region_offsets("q8_1", M, K)
+    Mp = (M + 31) // 32 * 32
+    KBp = (K // 32 + 7) // 8 * 8
+    MT = Mp // 32
+    buf = np.asarray(act_bytes_host, dtype=np.uint8)
+    return buf[o[1]:o[1] + MT * KBp * 128].view(np.float32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
+
+
 def act_padding_host(act_bytes_host: np.ndarray, M: int, K: int):
     """The padded rows (m >= M) and padded blocks (b >= K/32) of a q8_1 act buffer, as three
     flat arrays that must all be zero."""
-    o0, o1, o2 = act_region_offsets("q8_1", M, K)
+    o0, o1, o2 = act_region_offsets("q8_1", M, K)[:3]
     Mp = (M + 31) // 32 * 32
     KB = K // 32
     KBp = (KB + 7) // 8 * 8

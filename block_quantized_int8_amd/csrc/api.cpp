@@ -50,18 +50,19 @@ size_t mmq_act_bytes(mmq_atype a, int64_t M, int64_t K) {
     return (size_t)act_i8_layout(M, K).bytes;
 }
 
-mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[3]) {
+mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[4]) {
     if (!offsets || !valid_atype(a) || !sizes_ok(M, 1, K) || K % QK) return MMQ_EINVAL;
     if (a == MMQ_ACT_Q8_1) {
         const ActQ81Layout L = act_q8_1_layout(M, K);
         offsets[0] = (size_t)L.xq_off;
         offsets[1] = (size_t)L.xs_off;
         offsets[2] = (size_t)L.xsum_off;
+        offsets[3] = (size_t)L.xs16_off;
     } else {
         const ActI8Layout L = act_i8_layout(M, K);
         offsets[0] = (size_t)L.a_off;
         offsets[1] = (size_t)L.sa_off;
-        offsets[2] = 0;
+        offsets[2] = offsets[3] = 0;
     }
     return MMQ_OK;
 }
@@ -103,7 +104,12 @@ mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
         if (o == MMQ_OUT_I32_PARTIALS && M * N * (K / QK) > (int64_t(1) << 31)) return MMQ_EINVAL;
     }
     if (!aligned16(packed) || !aligned16(act) || !aligned16(out)) return MMQ_EALIGN;
-    return from_hip(launch_gemm(t, packed, act, M, N, K, o, out, ldo, as_stream(stream)));
+    if (t == MMQ_I8_ROW) {
+        if (!w8a8_grid_ok(M, N)) return MMQ_EINVAL;
+        return from_hip(launch_w8a8_gemm(packed, act, M, N, K, o, out, ldo, as_stream(stream)));
+    }
+    if (!dense_grid_ok(M, N)) return MMQ_EINVAL;
+    return from_hip(launch_block_gemm(t, packed, act, M, N, K, o, out, ldo, as_stream(stream)));
 }
 
 size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
@@ -123,6 +129,7 @@ mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* a
     if (!aligned16(packed) || !aligned16(act) || !aligned16(ids) || !aligned16(out) ||
         !aligned16(workspace))
         return MMQ_EALIGN;
+    if (!gather_grid_ok(gemm_id_max_units(E, T * top_k), N)) return MMQ_EINVAL;
     return from_hip(launch_gemm_id(t, packed, E, act, ids, T, top_k, N, K, out, workspace, ws_bytes,
                                    as_stream(stream)));
 }

@@ -8,7 +8,9 @@
 // bit-identical to the definition.
 //
 // The q8_1 output is written directly in the matrix-core tile order the GEMM consumes
-// (see mmq.h, region 0), so the GEMM streams whole 1 KB fragments straight into LDS.
+// (see mmq.h, region 0), so the GEMM streams whole fragments straight into LDS; xs is also
+// written as f16 bits (region 3, exact: xs is f16-rounded by definition), the form the GEMM's
+// scale outer product consumes.
 #include "mmq_internal.h"
 
 namespace {
@@ -21,7 +23,8 @@ constexpr int QBLK = 8;       // 32-value blocks per CTA along K (256 values)
 // bytes per row. Block reductions are over the 8 consecutive lanes of a row.
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(
     const float* __restrict__ x, int64_t M, int64_t KB, int64_t ldx, int64_t KBp,
-    int8_t* __restrict__ xq, float* __restrict__ xs, int32_t* __restrict__ xsum) {
+    int8_t* __restrict__ xq, float* __restrict__ xs, int32_t* __restrict__ xsum,
+    uint16_t* __restrict__ xs16) {
     const int t = threadIdx.x;
     const int r = t >> 3;
     const int j = t & 7;
@@ -67,8 +70,10 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(
         uint32_t* dst = reinterpret_cast<uint32_t*>(xq + tile * 1024 + (h * 32 + r) * 16 + 4 * (j & 3));
         *dst = packed;
         if (j == 0) {
-            xs[tile * 32 + r] = (float)(_Float16)d;
+            const _Float16 dh = (_Float16)d;
+            xs[tile * 32 + r] = (float)dh;
             xsum[tile * 32 + r] = s;
+            xs16[tile * 32 + r] = __builtin_bit_cast(uint16_t, dh);
         }
     }
 }
@@ -118,7 +123,8 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ld
     hipLaunchKernelGGL(quantize_q8_1_kernel, grid, dim3(256), 0, s, x, M, L.KB, ldx, L.KBp,
                        reinterpret_cast<int8_t*>(base + L.xq_off),
                        reinterpret_cast<float*>(base + L.xs_off),
-                       reinterpret_cast<int32_t*>(base + L.xsum_off));
+                       reinterpret_cast<int32_t*>(base + L.xsum_off),
+                       reinterpret_cast<uint16_t*>(base + L.xs16_off));
     return hipGetLastError();
 }
 

@@ -1,62 +1,77 @@
 // repack.hip - one-time, untimed repack of raw weight rows into matrix-core panels.
 //
-// The packed buffer keeps weights in their raw precision (nibbles stay nibbles, int8 stays
-// int8) and only reorders them so that one 64-lane load of a (32-row tile, 32-value block)
-// fragment is exactly the A operand of v_mfma_i32_32x32x32_i8 (lane L = h*32 + r holds row
-// r's values 16h..16h+15). Scales are gathered per (tile, block, row). Layout details are in
-// mmq_internal.h. Packing is a pure byte permutation done once, outside the timed region
-// (metainfer "INT8 W8A8 GEMM - Prefill", section 3.2: one-time pack into a graph-stable
-// buffer, validated by exact comparison).
+// The packed buffer keeps weights in their raw precision (nibbles stay nibbles, ternary codes
+// stay 2-bit codes, int8 stays int8) and only reorders them so that one 64-lane load of a
+// (32-row tile, 32-value block) fragment is the A operand of v_mfma_i32_32x32x32_i8, lane
+// L = h*32 + r holding row r's values 16h..16h+15. Scales are gathered per (tile, block, row).
+// Layouts: mmq_internal.h. Packing is a byte permutation (plus exact f32 scale products for
+// Q4_K) done once, outside the timed region (metainfer "INT8 W8A8 GEMM - Prefill",
+// section 3.2: one-time pack into a graph-stable buffer, validated by exact comparison).
 #include "mmq_internal.h"
 
 namespace {
 
-__device__ inline uint16_t ld_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+using namespace mmq;
 
-// One thread per (tile nt, block b, lane L): grid covers NT*KBp*64 threads.
+__device__ inline uint16_t ld_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+__device__ inline float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Every kernel: one thread per (tile nt, block b, lane L), NT*KBp*64 threads in total.
+struct Lane {
+    int64_t tb, nt, b, n;
+    int h, r, L;
+    bool live;                          // a real row and a real block
+};
+
+__device__ inline Lane lane_of(int64_t gid, int64_t KBp, int64_t KB, int64_t N) {
+    Lane x;
+    x.L = (int)(gid & 63);
+    x.tb = gid >> 6;
+    x.nt = x.tb / KBp;
+    x.b = x.tb % KBp;
+    x.h = x.L >> 5;
+    x.r = x.L & 31;
+    x.n = x.nt * 32 + x.r;
+    x.live = x.n < N && x.b < KB;
+    return x;
+}
+
 __global__ __launch_bounds__(256) void repack_q8_0_kernel(
-    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t NT,
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
     uint8_t* __restrict__ frag, uint16_t* __restrict__ scale) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= NT * KBp * 64) return;
-    const int L = (int)(gid & 63);
-    const int64_t tb = gid >> 6;                 // nt*KBp + b
-    const int64_t nt = tb / KBp, b = tb % KBp;
-    const int h = L >> 5, r = L & 31;
-    const int64_t n = nt * 32 + r;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t w[4] = {0, 0, 0, 0};
     uint16_t d = 0;
-    if (n < N && b < KB) {
-        const uint8_t* blk = raw + (n * KB + b) * 34;
+    if (x.live) {
+        const uint8_t* blk = raw + (x.n * KB + x.b) * 34;
         d = ld_u16(blk);
-        const uint8_t* q = blk + 2 + 16 * h;
+        const uint8_t* q = blk + 2 + 16 * x.h;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             w[i] = (uint32_t)q[4 * i] | ((uint32_t)q[4 * i + 1] << 8) | ((uint32_t)q[4 * i + 2] << 16) |
                    ((uint32_t)q[4 * i + 3] << 24);
     }
     *reinterpret_cast<uint4*>(frag + gid * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    if (h == 0) scale[tb * 32 + r] = d;
+    if (x.h == 0) scale[x.tb * 32 + x.r] = d;
 }
 
 __global__ __launch_bounds__(256) void repack_q4_0_kernel(
-    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t NT,
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
     uint8_t* __restrict__ frag, uint16_t* __restrict__ scale) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= NT * KBp * 64) return;
-    const int L = (int)(gid & 63);
-    const int64_t tb = gid >> 6;
-    const int64_t nt = tb / KBp, b = tb % KBp;
-    const int h = L >> 5, r = L & 31;
-    const int64_t n = nt * 32 + r;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t X0 = 0, X1 = 0;
     uint16_t d = 0;
-    if (n < N && b < KB) {
-        const uint8_t* blk = raw + (n * KB + b) * 18;
+    if (x.live) {
+        const uint8_t* blk = raw + (x.n * KB + x.b) * 18;
         d = ld_u16(blk);
-        uint32_t t[16];                          // 4-bit two's complement of nib - 8
+        // value 16h + i: nibble (qs[i] >> 4h) & 15; stored as the 4-bit two's complement of nib-8
+        uint32_t t[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) t[i] = ((blk[2 + i] >> (4 * h)) & 0xFu) ^ 0x8u;
+        for (int i = 0; i < 16; ++i) t[i] = ((blk[2 + i] >> (4 * x.h)) & 0xFu) ^ 0x8u;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
             X0 |= ((t[bb] << 4) | t[4 + bb]) << (8 * bb);
@@ -64,23 +79,87 @@ __global__ __launch_bounds__(256) void repack_q4_0_kernel(
         }
     }
     *reinterpret_cast<uint2*>(frag + gid * 8) = make_uint2(X0, X1);
-    if (h == 0) scale[tb * 32 + r] = d;
+    if (x.h == 0) scale[x.tb * 32 + x.r] = d;
+}
+
+__global__ __launch_bounds__(256) void repack_q4_K_kernel(
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    uint8_t* __restrict__ frag, float* __restrict__ scale) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
+    uint32_t X0 = 0, X1 = 0;
+    float ds = 0.f, dm = 0.f;
+    if (x.live) {
+        const int64_t sb = x.b / 8;
+        const int j = (int)(x.b % 8);
+        const uint8_t* blk = raw + (x.n * (KB / 8) + sb) * 144;
+        const uint8_t* qs = blk + 16 + 16 * j;
+        uint32_t nib[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nib[i] = (qs[i] >> (4 * x.h)) & 0xFu;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            X0 |= (nib[bb] | (nib[4 + bb] << 4)) << (8 * bb);
+            X1 |= (nib[8 + bb] | (nib[12 + bb] << 4)) << (8 * bb);
+        }
+        uint64_t scw = 0, mw = 0;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            scw |= (uint64_t)blk[4 + i] << (8 * i);
+            mw |= (uint64_t)blk[10 + i] << (8 * i);
+        }
+        const int sc = (int)((scw >> (6 * j)) & 63u), mm = (int)((mw >> (6 * j)) & 63u);
+        ds = half_bits_to_float(ld_u16(blk)) * (float)sc;          // exact: f16 x 6-bit integer
+        dm = -(half_bits_to_float(ld_u16(blk + 2)) * (float)mm);
+    }
+    *reinterpret_cast<uint2*>(frag + gid * 8) = make_uint2(X0, X1);
+    if (x.h == 0) *reinterpret_cast<float2*>(scale + (x.tb * 32 + x.r) * 2) = make_float2(ds, dm);
+}
+
+__global__ __launch_bounds__(256) void repack_iq1t_kernel(
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    uint8_t* __restrict__ frag, uint16_t* __restrict__ scale) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
+    uint32_t C = 0, meta = 0;
+    uint16_t d = 0;
+    if (x.live) {
+        const uint8_t* blk = raw + (x.n * (KB / 8) + x.b / 8) * 76;
+        const int e0 = (int)(x.b % 8) * 32 + 16 * x.h;    // first of the lane's 16 values
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = e0 + i;
+            const uint32_t c = (blk[e >> 2] >> (2 * (e & 3))) & 3u;
+            C |= c << (8 * (i & 3) + 2 * (i >> 2));
+        }
+        uint64_t sw = 0;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) sw |= (uint64_t)blk[64 + i] << (8 * i);
+        const uint32_t s = (uint32_t)(sw >> (3 * (e0 >> 4))) & 7u;
+        const int g0 = e0 >> 3, g1 = g0 + 1;               // the lane's two 8-value sign groups
+        const uint32_t sg0 = (blk[70 + (g0 >> 3)] >> (g0 & 7)) & 1u;
+        const uint32_t sg1 = (blk[70 + (g1 >> 3)] >> (g1 & 7)) & 1u;
+        meta = s | (sg0 << 3) | (sg1 << 4);
+        d = ld_u16(blk + 74);
+    }
+    uint8_t* f = frag + x.tb * 320;
+    *reinterpret_cast<uint32_t*>(f + x.L * 4) = C;
+    f[256 + x.L] = (uint8_t)meta;
+    if (x.h == 0) scale[x.tb * 32 + x.r] = d;
 }
 
 __global__ __launch_bounds__(256) void repack_i8_row_kernel(
     const int8_t* __restrict__ raw, const float* __restrict__ row_scale, int64_t N, int64_t K,
-    int64_t KB, int64_t KBp, int64_t NT, uint8_t* __restrict__ frag, float* __restrict__ sw) {
+    int64_t KB, int64_t KBp, int64_t total, uint8_t* __restrict__ frag, float* __restrict__ sw) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= NT * KBp * 64) return;
-    const int L = (int)(gid & 63);
-    const int64_t tb = gid >> 6;
-    const int64_t nt = tb / KBp, b = tb % KBp;
-    const int h = L >> 5, r = L & 31;
-    const int64_t n = nt * 32 + r;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (n < N && b < KB) v = *reinterpret_cast<const uint4*>(raw + n * K + b * 32 + 16 * h);
+    if (x.live) v = *reinterpret_cast<const uint4*>(raw + x.n * K + x.b * 32 + 16 * x.h);
     *reinterpret_cast<uint4*>(frag + gid * 16) = v;
-    if (b == 0 && h == 0) sw[n] = (n < N) ? row_scale[n] : 0.0f;
+    if (x.b == 0 && x.h == 0) sw[x.n] = (x.n < N) ? row_scale[x.n] : 0.0f;
 }
 
 }  // namespace
@@ -91,25 +170,32 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const float* row_scale, i
                          int64_t K, void* packed, hipStream_t s) {
     const PackedLayout L = packed_layout(t, N, K);
     uint8_t* base = static_cast<uint8_t*>(packed);
-    const int64_t threads = L.NT * L.KBp * 64;
-    const dim3 grid((unsigned)ceil_div(threads, 256));
+    uint8_t* frag = base + L.frag_off;
+    uint8_t* scale = base + L.scale_off;
+    const int64_t total = L.NT * L.KBp * 64;
+    const dim3 grid((unsigned)ceil_div(total, 256)), block(256);
     const uint8_t* r8 = static_cast<const uint8_t*>(raw);
     switch (t) {
         case MMQ_Q8_0:
-            hipLaunchKernelGGL(repack_q8_0_kernel, grid, dim3(256), 0, s, r8, N, L.KB, L.KBp, L.NT,
-                               base + L.frag_off, reinterpret_cast<uint16_t*>(base + L.scale_off));
+            hipLaunchKernelGGL(repack_q8_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+                               reinterpret_cast<uint16_t*>(scale));
             break;
         case MMQ_Q4_0:
-            hipLaunchKernelGGL(repack_q4_0_kernel, grid, dim3(256), 0, s, r8, N, L.KB, L.KBp, L.NT,
-                               base + L.frag_off, reinterpret_cast<uint16_t*>(base + L.scale_off));
+            hipLaunchKernelGGL(repack_q4_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+                               reinterpret_cast<uint16_t*>(scale));
+            break;
+        case MMQ_Q4_K:
+            hipLaunchKernelGGL(repack_q4_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+                               reinterpret_cast<float*>(scale));
+            break;
+        case MMQ_IQ1T:
+            hipLaunchKernelGGL(repack_iq1t_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+                               reinterpret_cast<uint16_t*>(scale));
             break;
         case MMQ_I8_ROW:
-            hipLaunchKernelGGL(repack_i8_row_kernel, grid, dim3(256), 0, s,
-                               static_cast<const int8_t*>(raw), row_scale, N, K, L.KB, L.KBp, L.NT,
-                               base + L.frag_off, reinterpret_cast<float*>(base + L.scale_off));
+            hipLaunchKernelGGL(repack_i8_row_kernel, grid, block, 0, s, static_cast<const int8_t*>(raw),
+                               row_scale, N, K, L.KB, L.KBp, total, frag, reinterpret_cast<float*>(scale));
             break;
-        default:
-            return hipErrorNotSupported;
     }
     return hipGetLastError();
 }

@@ -187,6 +187,11 @@ def weights(fmt: str, N: int, K: int, **kw):
     raise ValueError(fmt)
 
 
+def moe_weights(fmt: str, E: int, N: int, K: int, *, seed: int = 0, cfg: int = 5) -> np.ndarray:
+    """E expert matrices of N raw rows each, drawn as one (E*N)-row matrix: [E, N, row bytes]."""
+    return weights(fmt, E * N, K, seed=seed, cfg=cfg).reshape(E, N, -1)
+
+
 def moe_ids(T: int, top_k: int, E: int, *, seed: int = 0, cfg: int = 5) -> np.ndarray:
     """Each token picks top_k distinct experts uniformly at random (without replacement)."""
     u = rng(seed, cfg, T_IDS).random((T, E))

@@ -85,12 +85,13 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
  * Activation buffer ("act"). Opaque to most callers, but its layout is fixed so that other
  * producers can fill it. Let Mp = M rounded up to 32, KB = K/32, KBp = KB rounded up to 8.
  *
- * MMQ_ACT_Q8_1 (three regions, each starting on a 256-byte boundary):
+ * MMQ_ACT_Q8_1 (four regions, each starting on a 256-byte boundary):
  *   region 0  xq   int8, Mp*KBp*32 bytes, tiled for the matrix cores: the 32x32 tile
  *                  (row tile mt = m/32, block b) occupies bytes [(mt*KBp + b)*1024, +1024);
  *                  inside it, row r = m%32 and k' = k%32 sit at ((k'/16)*32 + r)*16 + k'%16.
  *   region 1  xs   f32 [Mp/32][KBp][32]: xs of (row mt*32+r, block b) at (mt*KBp + b)*32 + r.
  *   region 2  xsum int32, same indexing as xs.
+ *   region 3  xs16 xs as f16 bits, same indexing as xs (xs is f16-exact by construction).
  *   Rows m >= M and blocks b >= KB hold zeros.
  * MMQ_ACT_I8_TOKEN (two regions):
  *   region 0  a    int8 [M][K] row-major (row stride K).
@@ -100,9 +101,9 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
 /* Total bytes of an act buffer; 0 if the arguments are invalid. (host only) */
 size_t mmq_act_bytes(mmq_atype a, int64_t M, int64_t K);
 
-/* Byte offsets of the act buffer's regions (offsets[2] = 0 for MMQ_ACT_I8_TOKEN).
- * Returns MMQ_EINVAL for invalid arguments. (host only) */
-mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[3]);
+/* Byte offsets of the act buffer's regions 0..3 (MMQ_ACT_I8_TOKEN: regions 0..1, the rest 0),
+ * written to offsets[0..3] (host). Returns MMQ_EINVAL for invalid arguments. (host only) */
+mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[4]);
 
 /* Quantise f32 activations x [M][ldx] (device, row stride ldx >= K floats) into `act`
  * (device, mmq_act_bytes(a, M, K) bytes). Deterministic and bit-exact with the definition
@@ -145,15 +146,19 @@ size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
 /* MUL_MAT_ID (expert-routed MoE, llama.cpp PR #304: MUL_MAT_ID through MMQ):
  *     out[t][j][:] = act[t] x W_{ids[t][j]}^T      for t < T, j < top_k
  *  packed    (device) E packed matrices back to back, each mmq_packed_bytes(t, N, K) bytes
+ *            (so every matrix starts on a 256-byte boundary)
+ *  E         1..4096 experts; 1 <= top_k <= E
  *  act       (device) MMQ_ACT_Q8_1 act of T rows
- *  ids       (device) int32 [T][top_k], each in [0, E). Pairs with an id outside [0, E) are
- *            skipped (their output rows are left untouched).
+ *  ids       (device) int32 [T][top_k]; pair p = t*top_k + j uses expert ids[p]. Pairs with
+ *            an id outside [0, E) are skipped (their output rows are left untouched).
  *  out       (device) f32 [T][top_k][N]
  *  workspace (device) >= mmq_gemm_id_workspace_bytes(E, T, top_k) bytes of scratch; its
- *            contents need no initialisation and are overwritten.
- * The expert grouping (count, scan, scatter, tile list) runs on the device with no host
- * round trip, so the call is stream-ordered and capturable. Block formats only; o must be
- * MMQ_OUT_F32. */
+ *            contents need no initialisation and are overwritten. Two calls that overlap in
+ *            time must not share one workspace.
+ * The expert grouping (count per expert, scan, scatter of the pairs into expert order) runs
+ * on the device with no host round trip, so the call is stream-ordered and capturable; the
+ * order of pairs inside one expert is unspecified and does not affect any output value.
+ * Block formats only; o must be MMQ_OUT_F32. */
 mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
                        const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
                        mmq_otype o, void* out, void* workspace, size_t ws_bytes, void* stream);

@@ -52,10 +52,11 @@ def test_act_bytes_and_offsets(mmq):
     assert o[0] == 0
     assert o[1] == 3 * 8 * 1024        # xq region: MT * KBp * 1 KB
     assert o[2] == o[1] + 3 * 8 * 128
-    assert mmq.act_bytes("q8_1", M, K) == o[2] + 3 * 8 * 128
+    assert o[3] == o[2] + 3 * 8 * 128
+    assert mmq.act_bytes("q8_1", M, K) == o[3] + 3 * 8 * 64   # xs16: 64 B per tile
     assert all(v % 256 == 0 for v in o)
     oi = mmq.act_region_offsets("i8_token", 3, 64)
-    assert oi == (0, 256, 0)
+    assert oi == (0, 256, 0, 0)
     assert mmq.act_bytes("i8_token", 3, 64) == 512
     assert mmq.act_bytes("q8_1", 4, 33) == 0         # K not a multiple of 32
     assert mmq.act_bytes("q8_1", 0, 64) == 0
@@ -117,7 +118,7 @@ def test_gemm_id_validation(mmq):
 def test_act_to_host_layout_decoder(mmq):
     # build a q8_1 act image by hand from the header's formula and decode it back
     M, K = 40, 96
-    o0, o1, o2 = mmq.act_region_offsets("q8_1", M, K)
+    o0, o1, o2 = mmq.act_region_offsets("q8_1", M, K)[:3]
     Mp, KB, KBp = 64, 3, 8
     buf = np.zeros(mmq.act_bytes("q8_1", M, K), np.uint8)
     r = np.random.default_rng(0)

@@ -69,6 +69,10 @@ def test_block_formats_quantize_partials_output(env, fmt, M, N, K):
     assert np.array_equal(xs.view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(xsum, rsum)
     assert np.all(mmq.act_padding_host(host, M, K) == 0)
+    xs16 = mmq.act_xs16_host(host, M, K)
+    full_s = np.zeros(xs16.shape, np.float32)
+    full_s[:M, :K // 32] = rs
+    assert np.array_equal(xs16, full_s)
     parts = mmq.gemm(fmt, packed, act, M, N, K, "i32_partials")
     torch.cuda.synchronize()
     assert np.array_equal(parts.cpu().numpy(), orc.partials(fmt, raw, N, K, rq))
@@ -178,7 +182,7 @@ def _w8a8_case(env, M, N, K, seed, sample_rows=None):
     w, sw = gen.i8_rows(N, K, seed=seed, cfg=74, tensor=1)
     print(f"[case] w8a8 M={M} N={N} K={K}", flush=True)
     act = torch.empty(mmq.act_bytes("i8_token", M, K), dtype=torch.uint8, device=dev)
-    o0, o1, _ = mmq.act_region_offsets("i8_token", M, K)
+    o0, o1 = mmq.act_region_offsets("i8_token", M, K)[:2]
     act[o0:o0 + M * K].copy_(torch.from_numpy(a.view(np.uint8).ravel()))
     act[o1:o1 + 4 * M].copy_(torch.from_numpy(sa.view(np.uint8)))
     packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K, row_scale=torch.from_numpy(sw).to(dev))
@@ -236,7 +240,7 @@ def test_quantize_i8_token_bit_exact(env, M, K):
     act = mmq.quantize_act(torch.from_numpy(x).to("cuda"), "i8_token")
     torch.cuda.synchronize()
     host = act.cpu().numpy()
-    o0, o1, _ = mmq.act_region_offsets("i8_token", M, K)
+    o0, o1 = mmq.act_region_offsets("i8_token", M, K)[:2]
     a = host[o0:o0 + M * K].view(np.int8).reshape(M, K)
     sa = host[o1:o1 + 4 * M].view(np.float32)
     ra, rsa = orc.quantize_i8_token(x)
