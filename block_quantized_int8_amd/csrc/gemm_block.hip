@@ -10,9 +10,9 @@
 // the same 32x32 lane map forms it exactly, and the correction acc += f32(P) * s is applied in
 // registers - no store -> sync -> reload of the accumulator per block (the pages' "wall",
 // Hanzo paper sections 2-3; the fix is a manual MMA with a known lane map, section 4).
-//   q8_0, q4_0, iq1t: scale operands are f16 (d and xs are f16 values); each LDS scale entry
-//     holds its value in all 8 operand slots, so v_mfma_f32_32x32x16_f16 returns exactly
-//     16*wd*xs (products of two f16 are exact in f32; 16 equal exact terms sum exactly).
+//   q8_0, q4_0, iq1t: scale operands are f16 (d and xs are f16 values); each lane's operand
+//     holds its row's value in slot 0 and zeros elsewhere, so v_mfma_f32_32x32x16_f16 returns
+//     exactly 2*wd*xs (k = 0 and k = 8, one per half-wave; a product of two f16 is exact in f32).
 //   q4_K: d*sc and dmin*m are exact f32 but not f16, so v_mfma_f32_32x32x2_f32 forms
 //     2*(d*sc)*xs, and a second one adds the rank-1 min term 2*(-dmin*m)*(xs*xsum) straight into
 //     the accumulator through its C operand (minfer R1 section 2.2: sum w*q = ds*sum nib*q -
@@ -27,8 +27,15 @@
 // (minfer R1 section 2.3: exposed staging latency was the largest single cost; metainfer
 // section 1: global loads of stage i+1 before the stage-i MMAs, wait, write, barrier).
 //
+// Inside a stage the tiles are software-pipelined: the MFMAs of tile t+1 are issued into a
+// second register set before the VALU correction of tile t, so the matrix core works while
+// the vector unit converts and rescales (per 32x32 tile and block: one int8 MFMA and one
+// scale MFMA against 16 cvt + 16 fma per lane, i.e. the VALU side is the longer one).
+//
 // The same kernel serves MUL_MAT_ID: in gather mode every token slot of a tile reads its own
 // activation row and writes its own output row (see gemm_id.hip).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace mmq {
@@ -45,7 +52,7 @@ template <> struct BT<MMQ_Q8_0> {
     static constexpr int SB = 2;           // packed scale bytes per (tile, block, row)
     static constexpr bool F32S = false;    // f32 (q4_K) or replicated f16 scale operands
     static constexpr int SHIFT = 0;        // the MFMA computes P << SHIFT
-    static constexpr float POST = 1.0f / 16;
+    static constexpr float POST = 1.0f / 2;     // scale operand 2*wd*xs
     __device__ static void operands(const uint8_t* frag, int lane, const uint8_t*, v4i* a) {
         a[0] = *reinterpret_cast<const v4i*>(frag + lane * 16);
     }
@@ -60,7 +67,7 @@ template <> struct BT<MMQ_Q4_0> {
     static constexpr int SB = 2;
     static constexpr bool F32S = false;
     static constexpr int SHIFT = 4;
-    static constexpr float POST = 1.0f / 256;
+    static constexpr float POST = 1.0f / 32;    // 16x block dot, 2*wd*xs
     __device__ static void operands(const uint8_t* frag, int lane, const uint8_t*, v4i* a) {
         const uint2 X = *reinterpret_cast<const uint2*>(frag + lane * 8);
         a[0][0] = (int)(X.x & 0xF0F0F0F0u);
@@ -98,7 +105,7 @@ template <> struct BT<MMQ_IQ1T> {
     static constexpr int SB = 2;
     static constexpr bool F32S = false;
     static constexpr int SHIFT = 0;
-    static constexpr float POST = 1.0f / 128;   // scale d/8, operand 16*d*xs
+    static constexpr float POST = 1.0f / 16;    // scale d/8, operand 2*d*xs
     __device__ static void operands(const uint8_t* frag, int lane, const uint8_t* tab, v4i* a) {
         const uint32_t C = *reinterpret_cast<const uint32_t*>(frag + lane * 4);
         const uint32_t meta = frag[256 + lane];
@@ -138,8 +145,8 @@ struct Cfg {
     static constexpr int TM = WM * CT;                    // token tiles per CTA
     static constexpr int WF = TN * KS * T::FB;            // LDS: weight fragments
     static constexpr int XF = TM * KS * 1024;             // LDS: token fragments
-    // scale operands: replicated f16 entries (16 B per row) or f32 pairs (8 B per row)
-    static constexpr int ROWB = T::F32S ? 8 : 16;
+    // scale operands: one f16 per row (2 B) or an f32 pair (8 B per row)
+    static constexpr int ROWB = T::F32S ? 8 : 2;
     static constexpr int WS = TN * KS * 32 * ROWB;
     static constexpr int XS = TM * KS * 32 * ROWB;
     static constexpr int BUF = WF + XF + WS + XS;
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
             ssrc2[i] = ssrc[i];
             // f16: one 16-byte entry per row; f32: a (64-float) pair of 32-float arrays per
             // (tile, block), value at [r] and partner at [32 + r]
-            sdst[i] = C::WF + C::XF + (T::F32S ? ((tile * KS + q) * 64 + r) * 4 : ((tile * KS + q) * 32 + r) * 16);
+            sdst[i] = C::WF + C::XF + (T::F32S ? ((tile * KS + q) * 64 + r) * 4 : ((tile * KS + q) * 32 + r) * 2);
         } else {
             const int j = tile - C::TN;
             const int t = src_token(j, r);
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
             ssrc[i] = T::F32S ? reinterpret_cast<const uint8_t*>(args.xs + idx)
                               : reinterpret_cast<const uint8_t*>(args.xs16 + idx);
             ssrc2[i] = reinterpret_cast<const uint8_t*>(args.xsum + idx);
-            sdst[i] = C::WF + C::XF + C::WS + (T::F32S ? ((j * KS + q) * 64 + r) * 4 : ((j * KS + q) * 32 + r) * 16);
+            sdst[i] = C::WF + C::XF + C::WS + (T::F32S ? ((j * KS + q) * 64 + r) * 4 : ((j * KS + q) * 32 + r) * 2);
         }
         if (tid + i * C::NTH >= C::SI) sdst[i] = -1;
     }
@@ -331,15 +338,13 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
                     d[0] = a;
                     d[32] = b;
                 } else {
-                    const uint32_t rep = sreg[i] | (sreg[i] << 16);
-                    uint32_t* d = reinterpret_cast<uint32_t*>(buf + sdst[i]);
-                    d[0] = rep; d[1] = rep; d[2] = rep; d[3] = rep;
+                    *reinterpret_cast<uint16_t*>(buf + sdst[i]) = (uint16_t)sreg[i];
                 }
             }
         }
     };
 
-    float acc[RT][CT][16];
+    v16f acc[RT][CT];
 #pragma unroll
     for (int x = 0; x < RT; ++x)
 #pragma unroll
@@ -351,85 +356,125 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     const v16f zf = {0};
     const int nstages = KBp / KS;
 
+    // one block's operands for this wave: weight fragments, token fragments, scale operands
+    struct Ops {
+        v4i a[RT][T::NMF];
+        v4i b[CT];
+        h8 wsv[RT], xsv[CT];            // f16 scale operands (slot 0 live)
+        float wsf[RT], wmf[RT], xsf[CT], sxf[CT];   // Q4_K: d*sc, -dmin*m, xs, xs*xsum
+    };
+    auto load_w = [&](const uint8_t* cur, int kb, int rt, Ops& o) {
+        const int i = wn * RT + rt;
+        T::operands(cur + (i * KS + kb) * T::FB, lane, tab, o.a[rt]);
+        const uint8_t* wsl = cur + C::WF + C::XF;
+        if constexpr (T::F32S) {
+            const float* p = reinterpret_cast<const float*>(wsl) + (i * KS + kb) * 64 + (lane & 31);
+            o.wsf[rt] = p[0];
+            o.wmf[rt] = p[32];
+        } else {
+            const uint16_t v = *reinterpret_cast<const uint16_t*>(wsl + ((i * KS + kb) * 32 + (lane & 31)) * 2);
+            v4i t4 = {(int)v, 0, 0, 0};
+            o.wsv[rt] = __builtin_bit_cast(h8, t4);
+        }
+    };
+    auto load_x = [&](const uint8_t* cur, int kb, int ct, Ops& o) {
+        const int j = wm * CT + ct;
+        o.b[ct] = *reinterpret_cast<const v4i*>(cur + C::WF + (j * KS + kb) * 1024 + lane * 16);
+        const uint8_t* xsl = cur + C::WF + C::XF + C::WS;
+        if constexpr (T::F32S) {
+            const float* p = reinterpret_cast<const float*>(xsl) + (j * KS + kb) * 64 + (lane & 31);
+            o.xsf[ct] = p[0];
+            o.sxf[ct] = p[32];
+        } else {
+            const uint16_t v = *reinterpret_cast<const uint16_t*>(xsl + ((j * KS + kb) * 32 + (lane & 31)) * 2);
+            v4i t4 = {(int)v, 0, 0, 0};
+            o.xsv[ct] = __builtin_bit_cast(h8, t4);
+        }
+    };
+    // matrix-core half of one (tile, block): exact int32 dots D, scale outer product S, and
+    // for Q4_K the rank-1 min term added into the accumulator through the C operand
+    auto issue = [&](const Ops& o, int t, v16i& D, v16f& S) {
+        const int rt = t / CT, ct = t % CT;
+        D = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][0], o.b[ct], zi, 0, 0, 0);
+        if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][1], o.b[ct], D, 0, 0, 0);
+        if constexpr (MODE != DENSE_PARTIALS) {
+            if constexpr (T::F32S) {
+                S = __builtin_amdgcn_mfma_f32_32x32x2f32(o.wsf[rt], o.xsf[ct], zf, 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.wmf[rt], o.sxf[ct], acc[rt][ct], 0, 0, 0);
+            } else {
+                S = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.wsv[rt], o.xsv[ct], zf, 0, 0, 0);
+            }
+        }
+    };
+    // vector half: acc += f32(D) * S (or the partials store)
+    auto finish = [&](int s, int kb, int t, const v16i& D, const v16f& S) {
+        const int rt = t / CT, ct = t % CT;
+        if constexpr (MODE == DENSE_PARTIALS) {
+            const int kbg = s * KS + kb;
+            const int m = (mt_base + wm * CT + ct) * 32 + (lane & 31);
+            if (kbg < args.KB && m < args.M) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = (nt_base + wn * RT + rt) * 32 + acc_row(lane, r);
+                    if (n < args.N) args.partials[((int64_t)m * args.N + n) * args.KB + kbg] = D[r] >> T::SHIFT;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rt][ct][r] = __builtin_fmaf((float)D[r], S[r], acc[rt][ct][r]);
+        }
+    };
+
+    // Tile t of a block is (rt, ct) = (t / CT, t % CT). Step t issues tile t+1 (or tile 0 of
+    // the next block) and then finishes tile t. Right after the issue of the last tile that
+    // reads an operand (a[rt]: tile rt*CT + CT-1; b[ct]: tile (RT-1)*CT + ct), that operand is
+    // reloaded for the next block, so one register set serves and every LDS read has at least
+    // two steps of VALU work to land before its next use.
+    constexpr int NT_ = RT * CT;
+    // One stage: its KS blocks through the tile pipeline. `last` is a compile-time flag so the
+    // steady-state loop body has no branches (a branch lets the compiler sink the VALU half of
+    // the pipeline past it).
+    auto run_stage = [&](int s, auto last_tag) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        const uint8_t* cur = lds[s & 1];
+        if constexpr (!LAST) load_stage();              // in flight during this stage's MFMAs
+        Ops op;
+        v16i D[2];
+        v16f S[2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) load_w(cur, 0, rt, op);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) load_x(cur, 0, ct, op);
+        issue(op, 0, D[0], S[0]);
+#pragma unroll
+        for (int kb = 0; kb < KS; ++kb) {
+#pragma unroll
+            for (int t = 0; t < NT_; ++t) {
+                const int i = kb * NT_ + t;
+                if (t + 1 < NT_ || kb + 1 < KS) issue(op, (t + 1) % NT_, D[(i + 1) & 1], S[(i + 1) & 1]);
+                if (kb + 1 < KS) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        if (t == (rt * CT + CT - 2 > 0 ? rt * CT + CT - 2 : 0)) load_w(cur, kb + 1, rt, op);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        if (t == ((RT - 1) * CT + ct - 1 > 0 ? (RT - 1) * CT + ct - 1 : 0)) load_x(cur, kb + 1, ct, op);
+                }
+                // keep the next tile's MFMAs ahead of this tile's VALU work
+                __builtin_amdgcn_sched_barrier(0);
+                finish(s, kb, t, D[i & 1], S[i & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if constexpr (!LAST) store_stage(lds[(s + 1) & 1]);
+        __syncthreads();
+    };
+
     load_stage();
     store_stage(lds[0]);
     __syncthreads();
-    for (int s = 0; s < nstages; ++s) {
-        const uint8_t* cur = lds[s & 1];
-        if (s + 1 < nstages) load_stage();              // in flight during this stage's MFMAs
-        const uint8_t* wf = cur;
-        const uint8_t* xf = cur + C::WF;
-        const uint8_t* wsl = cur + C::WF + C::XF;
-        const uint8_t* xsl = wsl + C::WS;
-#pragma unroll 1
-        for (int kb = 0; kb < KS; ++kb) {
-            v4i a[RT][T::NMF];
-            h8 wsv[RT];
-            float wsf[RT], wmf[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const int i = wn * RT + rt;
-                T::operands(wf + (i * KS + kb) * T::FB, lane, tab, a[rt]);
-                if constexpr (T::F32S) {
-                    const float* p = reinterpret_cast<const float*>(wsl) + (i * KS + kb) * 64 + (lane & 31);
-                    wsf[rt] = p[0];
-                    wmf[rt] = p[32];
-                } else {
-                    wsv[rt] = *reinterpret_cast<const h8*>(wsl + ((i * KS + kb) * 32 + (lane & 31)) * 16);
-                }
-            }
-            v4i b[CT];
-            h8 xsv[CT];
-            float xsf[CT], sxf[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const int j = wm * CT + ct;
-                b[ct] = *reinterpret_cast<const v4i*>(xf + (j * KS + kb) * 1024 + lane * 16);
-                if constexpr (T::F32S) {
-                    const float* p = reinterpret_cast<const float*>(xsl) + (j * KS + kb) * 64 + (lane & 31);
-                    xsf[ct] = p[0];
-                    sxf[ct] = p[32];
-                } else {
-                    xsv[ct] = *reinterpret_cast<const h8*>(xsl + ((j * KS + kb) * 32 + (lane & 31)) * 16);
-                }
-            }
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rt][0], b[ct], zi, 0, 0, 0);
-                    if constexpr (T::NMF == 2)
-                        D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rt][1], b[ct], D, 0, 0, 0);
-                    if constexpr (MODE == DENSE_PARTIALS) {
-                        const int kbg = s * KS + kb;
-                        const int m = (mt_base + wm * CT + ct) * 32 + (lane & 31);
-                        if (kbg < args.KB && m < args.M) {
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int n = (nt_base + wn * RT + rt) * 32 + acc_row(lane, r);
-                                if (n < args.N)
-                                    args.partials[((int64_t)m * args.N + n) * args.KB + kbg] = D[r] >> T::SHIFT;
-                            }
-                        }
-                    } else if constexpr (T::F32S) {
-                        const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(wsf[rt], xsf[ct], zf, 0, 0, 0);
-                        v16f Tm;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) Tm[r] = acc[rt][ct][r];
-                        Tm = __builtin_amdgcn_mfma_f32_32x32x2f32(wmf[rt], sxf[ct], Tm, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[rt][ct][r] = __builtin_fmaf((float)D[r], S[r], Tm[r]);
-                    } else {
-                        const v16f S = __builtin_amdgcn_mfma_f32_32x32x16_f16(wsv[rt], xsv[ct], zf, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            acc[rt][ct][r] = __builtin_fmaf((float)D[r], S[r], acc[rt][ct][r]);
-                    }
-                }
-        }
-        if (s + 1 < nstages) store_stage(lds[(s + 1) & 1]);
-        __syncthreads();
-    }
+    for (int s = 0; s + 1 < nstages; ++s) run_stage(s, std::false_type{});
+    run_stage(nstages - 1, std::true_type{});
 
     if constexpr (MODE != DENSE_PARTIALS) {
         const int64_t ldo = args.ldo;
