@@ -106,8 +106,8 @@ def act_bytes(atype, M: int, K: int) -> int:
     return int(lib().mmq_act_bytes(_at(atype), M, K))
 
 
-def act_region_offsets(atype, M: int, K: int) -> tuple[int, int, int, int]:
-    arr = (ctypes.c_size_t * 4)()
+def act_region_offsets(atype, M: int, K: int) -> tuple[int, int, int, int, int]:
+    arr = (ctypes.c_size_t * 5)()
     _check("mmq_act_region_offsets", lib().mmq_act_region_offsets(_at(atype), M, K, arr))
     return tuple(int(v) for v in arr)
 
@@ -184,57 +184,59 @@ def gemm_id(wtype, packed, E: int, act, ids, T: int, top_k: int, N: int, K: int,
 
 # -------------------------------------------------------------------------- host helpers
 
+def _act_dims(M: int, K: int):
+    Mp = (M + 31) // 32 * 32
+    KB = K // 32
+    KBp = (KB + 7) // 8 * 8
+    return Mp, KB, KBp, Mp // 32
+
+
+def _act_regions(act_bytes_host: np.ndarray, M: int, K: int):
+    """All five q8_1 regions, padding included: xq int8 [Mp, KBp*32], xs f32 [Mp, KBp],
+    xsum int32 [Mp, KBp], xs2 uint32 [Mp, KBp], xsx f32 [Mp, KBp]."""
+    o = act_region_offsets("q8_1", M, K)
+    Mp, KB, KBp, MT = _act_dims(M, K)
+    buf = np.asarray(act_bytes_host, dtype=np.uint8)
+    t = buf[o[0]:o[0] + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)   # [mt, b, h, r, 16]
+    xq = t.transpose(0, 3, 1, 2, 4).reshape(Mp, KBp * 32)
+    cells = Mp * KBp
+    xs = buf[o[1]:o[1] + 4 * cells].view(np.float32).reshape(Mp, KBp)
+    xsum = buf[o[2]:o[2] + 4 * cells].view(np.int32).reshape(Mp, KBp)
+    xs2 = buf[o[3]:o[3] + 4 * cells].view(np.uint32).reshape(Mp, KBp)
+    xsx = buf[o[4]:o[4] + 4 * cells].view(np.float32).reshape(Mp, KBp)
+    return xq, xs, xsum, xs2, xsx
+
+
 def act_to_host(act_bytes_host: np.ndarray, M: int, K: int):
     """Decode a q8_1 act buffer (copied to host as uint8) into plain row-major
     (xq int8 [M,K], xs f32 [M,K/32], xsum int32 [M,K/32]) following the documented layout."""
-    o0, o1, o2 = act_region_offsets("q8_1", M, K)[:3]
-    Mp = (M + 31) // 32 * 32
+    xq, xs, xsum, _, _ = _act_regions(act_bytes_host, M, K)
     KB = K // 32
-    KBp = (KB + 7) // 8 * 8
-    MT = Mp // 32
-    buf = np.asarray(act_bytes_host, dtype=np.uint8)
-    t = buf[o0:o0 + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)   # [mt, b, h, r, 16]
-    xq = t.transpose(0, 3, 1, 2, 4).reshape(Mp, KBp * 32)[:M, :K]
-    xs = buf[o1:o1 + MT * KBp * 128].view(np.float32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
-    xsum = buf[o2:o2 + MT * KBp * 128].view(np.int32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
-    return np.ascontiguousarray(xq), np.ascontiguousarray(xs[:M, :KB]), np.ascontiguousarray(xsum[:M, :KB])
+    return (np.ascontiguousarray(xq[:M, :K]), np.ascontiguousarray(xs[:M, :KB]),
+            np.ascontiguousarray(xsum[:M, :KB]))
 
 
-def act_xs16_host(act_bytes_host: np.ndarray, M: int, K: int):
-    """Decode region 3 (xs as f16 bits) to f32 [Mp, KBp]; it must equal region 1 exactly,
-    padding included."""
-    o = act_region_offsets("q8_1", M, K)
-    Mp = (M + 31) // 32 * 32
-    KBp = (K // 32 + 7) // 8 * 8
-    MT = Mp // 32
-    buf = np.asarray(act_bytes_host, dtype=np.uint8)
-    xs16 = buf[o[3]:o[3] + MT * KBp * 64].view(np.float16).reshape(MT, KBp, 32).transpose(0, 2, 1)
-    return xs16.reshape(Mp, KBp).astype(np.float32)
+def act_derived_host(act_bytes_host: np.ndarray, M: int, K: int):
+    """Regions 3 and 4 decoded to f32 [Mp, KBp] each (padding included): the low and high f16
+    halves of xs2, and xsx. They must equal xs, xs and xs * xsum exactly."""
+    _, _, _, xs2, xsx = _act_regions(act_bytes_host, M, K)
+    lo = (xs2 & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float32)
+    hi = (xs2 >> 16).astype(np.uint16).view(np.float16).astype(np.float32)
+    return lo, hi, xsx.copy()
 
 
-def act_xs_full_host(act_bytes_host: np.ndarray, M: int, K: int):
-    """Region 1 (xs f32) as [Mp, KBp], padding included."""
-    o = act_region_offsets("q8_1", M, K)
-    Mp = (M + 31) // 32 * 32
-    KBp = (K // 32 + 7) // 8 * 8
-    MT = Mp // 32
-    buf = np.asarray(act_bytes_host, dtype=np.uint8)
-    return buf[o[1]:o[1] + MT * KBp * 128].view(np.float32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
+def act_full_host(act_bytes_host: np.ndarray, M: int, K: int):
+    """Regions 1 and 2 (xs f32, xsum int32) as [Mp, KBp], padding included."""
+    _, xs, xsum, _, _ = _act_regions(act_bytes_host, M, K)
+    return xs.copy(), xsum.copy()
 
 
 def act_padding_host(act_bytes_host: np.ndarray, M: int, K: int):
-    """The padded rows (m >= M) and padded blocks (b >= K/32) of a q8_1 act buffer, as three
-    flat arrays that must all be zero."""
-    o0, o1, o2 = act_region_offsets("q8_1", M, K)[:3]
-    Mp = (M + 31) // 32 * 32
+    """The padded rows (m >= M) and padded blocks (b >= K/32) of every region of a q8_1 act
+    buffer, as one flat array that must be all zero."""
+    xq, xs, xsum, xs2, xsx = _act_regions(act_bytes_host, M, K)
     KB = K // 32
-    KBp = (KB + 7) // 8 * 8
-    MT = Mp // 32
-    buf = np.asarray(act_bytes_host, dtype=np.uint8)
-    t = buf[o0:o0 + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)
-    xq = t.transpose(0, 3, 1, 2, 4).reshape(Mp, KBp * 32)
-    xs = buf[o1:o1 + MT * KBp * 128].view(np.float32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
-    xsum = buf[o2:o2 + MT * KBp * 128].view(np.int32).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
-    pads = [xq[M:].ravel(), xq[:, K:].ravel(), xs[M:].ravel(), xs[:, KB:].ravel(),
-            xsum[M:].ravel(), xsum[:, KB:].ravel()]
-    return np.concatenate([p.astype(np.float64) for p in pads]) if pads else np.zeros(0)
+    pads = [xq[M:].ravel(), xq[:, K:].ravel()]
+    for r in (xs, xsum, xs2, xsx):
+        pads += [r[M:].ravel(), r[:, KB:].ravel()]
+    return np.concatenate([p.astype(np.float64) for p in pads])

@@ -50,19 +50,20 @@ size_t mmq_act_bytes(mmq_atype a, int64_t M, int64_t K) {
     return (size_t)act_i8_layout(M, K).bytes;
 }
 
-mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[4]) {
+mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[5]) {
     if (!offsets || !valid_atype(a) || !sizes_ok(M, 1, K) || K % QK) return MMQ_EINVAL;
     if (a == MMQ_ACT_Q8_1) {
         const ActQ81Layout L = act_q8_1_layout(M, K);
         offsets[0] = (size_t)L.xq_off;
         offsets[1] = (size_t)L.xs_off;
         offsets[2] = (size_t)L.xsum_off;
-        offsets[3] = (size_t)L.xs16_off;
+        offsets[3] = (size_t)L.xs2_off;
+        offsets[4] = (size_t)L.xsx_off;
     } else {
         const ActI8Layout L = act_i8_layout(M, K);
         offsets[0] = (size_t)L.a_off;
         offsets[1] = (size_t)L.sa_off;
-        offsets[2] = offsets[3] = 0;
+        offsets[2] = offsets[3] = offsets[4] = 0;
     }
     return MMQ_OK;
 }

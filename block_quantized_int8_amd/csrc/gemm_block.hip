@@ -4,36 +4,41 @@
 //
 // ("A Negative Result on int8 Tensor-Core MMQ", section 2; minfer "08 . R1", sections 2.1-2.2.)
 //
-// Per 32-value block and 32x32 output tile, v_mfma_i32_32x32x32_i8 computes the exact int32
-// block dots P (K = 32 is exactly one block, so no two scales ever share an accumulator). The
-// block scale is an outer product of a weight-row vector and a token vector; a second MFMA on
-// the same 32x32 lane map forms it exactly, and the correction acc += f32(P) * s is applied in
-// registers - no store -> sync -> reload of the accumulator per block (the pages' "wall",
-// Hanzo paper sections 2-3; the fix is a manual MMA with a known lane map, section 4).
-//   q8_0, q4_0, iq1t: scale operands are f16 (d and xs are f16 values); each lane's operand
-//     holds its row's value in slot 0 and zeros elsewhere, so v_mfma_f32_32x32x16_f16 returns
-//     exactly 2*wd*xs (k = 0 and k = 8, one per half-wave; a product of two f16 is exact in f32).
-//   q4_K: d*sc and dmin*m are exact f32 but not f16, so v_mfma_f32_32x32x2_f32 forms
-//     2*(d*sc)*xs, and a second one adds the rank-1 min term 2*(-dmin*m)*(xs*xsum) straight into
-//     the accumulator through its C operand (minfer R1 section 2.2: sum w*q = ds*sum nib*q -
-//     dmin*sum q, with the activation block sum produced by the quantiser).
+// Per 32-value block and 32x32 output tile (rows = weight rows n, columns = tokens m):
+//  1. v_mfma_i32_32x32x32_i8 forms the exact int32 block dots P. K = 32 is exactly one block, so
+//     no two scales ever share an accumulator. Its C operand holds the bits of c = 1/(2 pi)
+//     (0x3E22F983, mantissa field 0x22F983): adding an integer P to those bits stays inside the
+//     [1/8, 1/4) binade for -2291075 <= P < 6097533, so every result D, read as f32, equals
+//     c + P * 2^-26 exactly (|P| <= 548640 for every format).
+//  2. v_mfma_f32_32x32x8_f16 forms the scale outer product S = wd (x) xs from one f16 per row on
+//     each side (both half-waves contribute, so S = 2 wd xs; a product of two f16 is exact).
+//  3. acc += (D - c) * S: one exact subtraction and one FMA per element on the known 32x32 lane
+//     map, in registers - no store -> sync -> reload of the accumulator per block (the pages'
+//     "wall", Hanzo paper sections 2-3; the fix is a manual MMA with a known lane map, section 4).
+//     The 2^26 goes into the epilogue's power-of-two scale.
+// Measured on gfx950: v_cvt_f32_i32 issues at about half the rate of v_sub_f32, and a
+// matrix-core op that reads a 16-register C operand from VGPRs costs the vector unit about 19
+// cycles, so the conversion is the subtraction above rather than a convert or a third MFMA.
+// The vector unit has no packed-f32 path here: the 32 vector ops per tile and block are the
+// binding cost, and the two MFMAs (64 cycles) hide behind them.
+//
+//   q4_K: S = xs * (d*sc) from the exact f16 split d*sc = hi + lo (slots 0 and 1 against xs in
+//     both), and the rank-1 min term -(dmin*m) * (xs*xsum) (minfer R1 section 2.2: sum w*q =
+//     ds * sum nib*q - dmin * sum q) is added straight into the accumulator by
+//     v_mfma_f32_32x32x2_f32 over two blocks at once (one per half-wave).
 //   iq1t: the IQ1_M fold (llama.cpp PR #304) turns each value into the integer 8g +- 1 with a
 //     per-16 factor (2s+1) and a per-block scale d/8. (2s+1)*v = 2s*v + v with |2s*v| <= 126,
 //     so two chained int8 MFMAs over [2s*v] and [v] (same token operand) give the folded
 //     per-32 integer sum_h (2s_h+1)*P16_h exactly, and only d remains as a scale.
 //
-// Operands stream through LDS with register staging: the next stage's global loads are issued
-// before the current stage's MFMA sequence and written to the other LDS buffer after it
-// (minfer R1 section 2.3: exposed staging latency was the largest single cost; metainfer
-// section 1: global loads of stage i+1 before the stage-i MMAs, wait, write, barrier).
-//
-// Inside a stage the tiles are software-pipelined: the MFMAs of tile t+1 are issued into a
-// second register set before the VALU correction of tile t, so the matrix core works while
-// the vector unit converts and rescales (per 32x32 tile and block: one int8 MFMA and one
-// scale MFMA against 16 cvt + 16 fma per lane, i.e. the VALU side is the longer one).
-//
-// The same kernel serves MUL_MAT_ID: in gather mode every token slot of a tile reads its own
-// activation row and writes its own output row (see gemm_id.hip).
+// Operands reach LDS by direct global->LDS DMA (global_load_lds_dwordx4: each lane names its
+// own 16-byte source, the wave writes 1 KB of LDS), double-buffered per 4-block stage: stage
+// s+1 is in flight while stage s runs its MFMAs (minfer R1 section 2.3: exposed staging
+// latency was the largest single cost; metainfer section 1: global loads of stage i+1 before
+// the stage-i MMACs). Nothing is staged through registers, so the copy costs no vector work.
+// Token rows are fetched per lane, which is also how MUL_MAT_ID gathers its rows: in gather
+// mode every token slot of a tile reads its own activation row and writes its own output row
+// (see gemm_id.hip).
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -41,21 +46,34 @@
 namespace mmq {
 namespace {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+constexpr int MAGIC_I = 0x3E22F983;        // bits of 1/(2 pi)
+constexpr float MAGIC_F = 0.15915494309189535f;     // the same value as f32
+constexpr float UNBIAS = 67108864.0f;      // 2^26: D - c = P * 2^-26
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+constexpr int KS = 4;                      // blocks per stage: one row's scales = 16 bytes
+static_assert(KB_ALIGN % (2 * KS) == 0, "stages come in pairs (two LDS buffers)");
 
 // ------------------------------------------------------------------- weight formats
 template <mmq_wtype FMT> struct BT;
 
+// Each format reads its lane's raw fragment bytes from LDS a block ahead (fetch), may do a
+// second dependent read (mid, the IQ1T table), and turns them into MFMA operands just before use
+// (unpack), so no LDS latency sits in front of an unpack.
 template <> struct BT<MMQ_Q8_0> {
     static constexpr int FB = 1024;        // packed fragment bytes per (tile, block)
     static constexpr int NMF = 1;          // int8 MFMAs per block
-    static constexpr int SB = 2;           // packed scale bytes per (tile, block, row)
-    static constexpr bool F32S = false;    // f32 (q4_K) or replicated f16 scale operands
     static constexpr int SHIFT = 0;        // the MFMA computes P << SHIFT
-    static constexpr float POST = 1.0f / 2;     // scale operand 2*wd*xs
-    __device__ static void operands(const uint8_t* frag, int lane, const uint8_t*, v4i* a) {
-        a[0] = *reinterpret_cast<const v4i*>(frag + lane * 16);
+    static constexpr bool MIN = false;     // q4_K min term
+    static constexpr float POST = UNBIAS / 2;   // S = 2 wd xs
+    struct Raw { v4i x; };
+    __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
+        r.x = *reinterpret_cast<const v4i*>(frag + lane * 16);
     }
+    __device__ static void mid(Raw&, uint32_t, int, const uint8_t*) {}
+    __device__ static void unpack(const Raw& r, v4i* a) { a[0] = r.x; }
+    __device__ static uint32_t scale_op(uint32_t w) { return w; }
 };
 
 // q4_0 lane bytes: high nibbles of X0 are k = 16h+0..3, low nibbles 16h+4..7 (X1: 8..15), each
@@ -64,52 +82,66 @@ template <> struct BT<MMQ_Q8_0> {
 template <> struct BT<MMQ_Q4_0> {
     static constexpr int FB = 512;
     static constexpr int NMF = 1;
-    static constexpr int SB = 2;
-    static constexpr bool F32S = false;
     static constexpr int SHIFT = 4;
-    static constexpr float POST = 1.0f / 32;    // 16x block dot, 2*wd*xs
-    __device__ static void operands(const uint8_t* frag, int lane, const uint8_t*, v4i* a) {
-        const uint2 X = *reinterpret_cast<const uint2*>(frag + lane * 8);
-        a[0][0] = (int)(X.x & 0xF0F0F0F0u);
-        a[0][1] = (int)((X.x << 4) & 0xF0F0F0F0u);
-        a[0][2] = (int)(X.y & 0xF0F0F0F0u);
-        a[0][3] = (int)((X.y << 4) & 0xF0F0F0F0u);
+    static constexpr bool MIN = false;
+    static constexpr float POST = UNBIAS / 32;  // 16x block dot, S = 2 wd xs
+    struct Raw { uint2 x; };
+    __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
+        r.x = *reinterpret_cast<const uint2*>(frag + lane * 8);
     }
+    __device__ static void mid(Raw&, uint32_t, int, const uint8_t*) {}
+    __device__ static void unpack(const Raw& r, v4i* a) {
+        a[0][0] = (int)(r.x.x & 0xF0F0F0F0u);
+        a[0][1] = (int)((r.x.x << 4) & 0xF0F0F0F0u);
+        a[0][2] = (int)(r.x.y & 0xF0F0F0F0u);
+        a[0][3] = (int)((r.x.y << 4) & 0xF0F0F0F0u);
+    }
+    __device__ static uint32_t scale_op(uint32_t w) { return w; }
 };
 
 // q4_K lane bytes: unsigned nibbles, X0 & 0x0F0F0F0F = k 16h+0..3, (X0 >> 4) & .. = 16h+4..7.
 template <> struct BT<MMQ_Q4_K> {
     static constexpr int FB = 512;
     static constexpr int NMF = 1;
-    static constexpr int SB = 8;           // f32 d*sc, f32 -dmin*m
-    static constexpr bool F32S = true;
     static constexpr int SHIFT = 0;
-    static constexpr float POST = 1.0f / 2;
-    __device__ static void operands(const uint8_t* frag, int lane, const uint8_t*, v4i* a) {
-        const uint2 X = *reinterpret_cast<const uint2*>(frag + lane * 8);
-        a[0][0] = (int)(X.x & 0x0F0F0F0Fu);
-        a[0][1] = (int)((X.x >> 4) & 0x0F0F0F0Fu);
-        a[0][2] = (int)(X.y & 0x0F0F0F0Fu);
-        a[0][3] = (int)((X.y >> 4) & 0x0F0F0F0Fu);
+    static constexpr bool MIN = true;
+    static constexpr float POST = UNBIAS / 2;
+    struct Raw { uint2 x; };
+    __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
+        r.x = *reinterpret_cast<const uint2*>(frag + lane * 8);
     }
+    __device__ static void mid(Raw&, uint32_t, int, const uint8_t*) {}
+    __device__ static void unpack(const Raw& r, v4i* a) {
+        a[0][0] = (int)(r.x.x & 0x0F0F0F0Fu);
+        a[0][1] = (int)((r.x.x >> 4) & 0x0F0F0F0Fu);
+        a[0][2] = (int)(r.x.y & 0x0F0F0F0Fu);
+        a[0][3] = (int)((r.x.y >> 4) & 0x0F0F0F0Fu);
+    }
+    __device__ static uint32_t scale_op(uint32_t w) { return w; }     // (hi, lo) of d*sc
 };
 
-// iq1t lane data: one dword of 2-bit codes (value 4q+b at bits 8b+2q) and a meta byte
-// s | sigma0 << 3 | sigma1 << 4 (sigma_i: sign bit of the lane's 8-value group i). The table
-// entry for a meta byte holds four byte-LUTs indexed by the code: v = 8(c-1) + sigma for both
-// sign groups, and 2s*v for both. v_perm picks the bytes: selectors 0..2 address the first
-// group's LUT, 4..6 the second's.
+// iq1t lane data: one dword of 2-bit codes (value 4q+b at bits 8b+2q); the lane's meta byte
+// s | sigma0 << 3 | sigma1 << 4 sits in its row's scale dword (byte 2 + half). The table entry
+// for a meta byte holds four byte-LUTs indexed by the code: v = 8(c-1) + sigma for both sign
+// groups, and 2s*v for both. v_perm picks the bytes: selectors 0..2 address the first group's
+// LUT, 4..6 the second's.
 template <> struct BT<MMQ_IQ1T> {
-    static constexpr int FB = 320;         // 64 lanes x 4 B codes + 64 meta bytes
+    static constexpr int FB = 256;
     static constexpr int NMF = 2;
-    static constexpr int SB = 2;
-    static constexpr bool F32S = false;
     static constexpr int SHIFT = 0;
-    static constexpr float POST = 1.0f / 16;    // scale d/8, operand 2*d*xs
-    __device__ static void operands(const uint8_t* frag, int lane, const uint8_t* tab, v4i* a) {
-        const uint32_t C = *reinterpret_cast<const uint32_t*>(frag + lane * 4);
-        const uint32_t meta = frag[256 + lane];
-        const v4i t = *reinterpret_cast<const v4i*>(tab + meta * 16);   // v0, v1, 2s*v0, 2s*v1
+    static constexpr bool MIN = false;
+    static constexpr float POST = UNBIAS / 16;  // scale d/8, S = 2 d xs
+    struct Raw { uint32_t C; v4i t; };
+    __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
+        r.C = *reinterpret_cast<const uint32_t*>(frag + lane * 4);
+    }
+    __device__ static void mid(Raw& r, uint32_t wsd, int lane, const uint8_t* tab) {
+        const uint32_t meta = (wsd >> (16 + 8 * (lane >> 5))) & 0xFFu;
+        r.t = *reinterpret_cast<const v4i*>(tab + meta * 16);     // v0, v1, 2s*v0, 2s*v1
+    }
+    __device__ static void unpack(const Raw& r, v4i* a) {
+        const uint32_t C = r.C;
+        const v4i t = r.t;
         const uint32_t s0 = C & 0x03030303u;
         const uint32_t s1 = (C >> 2) & 0x03030303u;
         const uint32_t s2 = ((C >> 4) & 0x03030303u) | 0x04040404u;
@@ -123,6 +155,7 @@ template <> struct BT<MMQ_IQ1T> {
         a[1][2] = (int)__builtin_amdgcn_perm((uint32_t)t[1], (uint32_t)t[0], s2);
         a[1][3] = (int)__builtin_amdgcn_perm((uint32_t)t[1], (uint32_t)t[0], s3);
     }
+    __device__ static uint32_t scale_op(uint32_t w) { return w & 0xFFFFu; }   // f16 d only
     // table entry e (meta byte) word w: w=0,1: LUT of v for sign group 0/1; w=2,3: LUT of 2s*v
     __device__ static uint32_t table_word(int e, int w) {
         const int s = e & 7;
@@ -137,36 +170,40 @@ template <> struct BT<MMQ_IQ1T> {
 // ------------------------------------------------------------------- kernel configuration
 enum Mode { DENSE_F32 = 0, DENSE_PARTIALS = 1, GATHER_F32 = 2 };
 
-template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int KS>
+// WN x WM waves, each owning RT weight tiles x CT token tiles of 32 x 32.
+// LDS stage layout (bytes): weight fragments [TN][KS][FB] | token fragments [TM][KS][1024] |
+// weight scale dwords [TN][32][KS] | token scale dwords [TM][32][KS] | (q4_K) weight mins,
+// token xs*xsum [..][32][KS] | padding chunks. Every region is loaded in whole 1 KB chunks (one
+// wave-wide 16-byte DMA each); scale regions hold two tiles per chunk.
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT>
 struct Cfg {
     using T = BT<FMT>;
     static constexpr int NW = WN * WM, NTH = NW * 64;
-    static constexpr int TN = WN * RT;                    // weight tiles per CTA
-    static constexpr int TM = WM * CT;                    // token tiles per CTA
-    static constexpr int WF = TN * KS * T::FB;            // LDS: weight fragments
-    static constexpr int XF = TM * KS * 1024;             // LDS: token fragments
-    // scale operands: one f16 per row (2 B) or an f32 pair (8 B per row)
-    static constexpr int ROWB = T::F32S ? 8 : 2;
-    static constexpr int WS = TN * KS * 32 * ROWB;
-    static constexpr int XS = TM * KS * 32 * ROWB;
-    static constexpr int BUF = WF + XF + WS + XS;
-    static constexpr int UW = WF / 16;                    // 16-byte weight units per stage
-    static constexpr int UX = TM * KS * 64;               // 16-byte token units per stage
-    static constexpr int UPT_W = (UW + NTH - 1) / NTH;
-    static constexpr int UPT_X = (UX + NTH - 1) / NTH;
-    static constexpr int SI = (TN + TM) * KS * 32;        // scale items (rows) per stage
-    static constexpr int SPT = (SI + NTH - 1) / NTH;
-    static_assert(WF % 16 == 0, "fragment stage must be whole 16-byte units");
+    static constexpr int TN = WN * RT, TM = WM * CT;
+    static constexpr int WF = TN * KS * T::FB;
+    static constexpr int XF = TM * KS * 1024;
+    static constexpr int SCW = ((TN + 1) / 2) * 1024;
+    static constexpr int SCX = ((TM + 1) / 2) * 1024;
+    static constexpr int MNW = T::MIN ? SCW : 0;
+    static constexpr int MNX = T::MIN ? SCX : 0;
+    static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + SCW;
+    static constexpr int O_WM = O_XS + SCX, O_XM = O_WM + MNW, O_PAD = O_XM + MNX;
+    static constexpr int C_WF = WF / 1024, C_XF = TM * KS, C_WS = SCW / 1024, C_XS = SCX / 1024;
+    static constexpr int C_WM = MNW / 1024, C_XM = MNX / 1024;
+    static constexpr int C_ALL = C_WF + C_XF + C_WS + C_XS + C_WM + C_XM;
+    static constexpr int CPW = (C_ALL + NW - 1) / NW;          // chunks per wave per stage
+    static constexpr int BUF = O_PAD + (CPW * NW - C_ALL) * 1024;
+    static_assert(WF % 1024 == 0, "weight fragments of a stage must be whole 1 KB chunks");
 };
 
 struct BlockArgs {
     const uint8_t* w;           // packed weights (expert 0 in gather mode)
-    int64_t w_scale_off;        // offset of the scale region inside one packed matrix
+    int64_t w_scale_off;        // offsets of the scale / min regions inside one packed matrix
+    int64_t w_min_off;
     int64_t w_stride;           // bytes between experts' packed matrices (gather mode)
     const uint8_t* xq;          // act region 0 (tiled int8)
-    const float* xs;            // act region 1
-    const int32_t* xsum;        // act region 2
-    const uint16_t* xs16;       // act region 3 (f16 xs)
+    const uint32_t* xs2;        // act region 3 (xs as an f16 pair)
+    const float* xsx;           // act region 4 (xs * xsum)
     int M, N, KB, KBp, NT, MT, tiles_m;
     float* out;
     int64_t ldo;
@@ -178,17 +215,33 @@ struct BlockArgs {
     int E, top_k, ntiles_n;
 };
 
-template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int KS, int MODE>
+typedef __attribute__((address_space(1))) const void gmem_t;
+typedef __attribute__((address_space(3))) void lmem_t;
+
+// One wave-wide 16-byte-per-lane DMA: lane l's 16 source bytes land at lds + 16 l.
+__device__ inline void dma16(const uint8_t* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds((gmem_t*)src, (lmem_t*)lds, 16, 0, 0);
+}
+
+// an f16x4 operand with the dword `lo` in slots 0-1 and zeros in slots 2-3
+__device__ inline h4 as_h4(uint32_t lo) {
+    const v2i t = {(int)lo, 0};
+    return __builtin_bit_cast(h4, t);
+}
+
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int MODE>
 __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs args) {
-    using C = Cfg<FMT, WN, WM, RT, CT, KS>;
+    using C = Cfg<FMT, WN, WM, RT, CT>;
     using T = typename C::T;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][C::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::BUF];
     __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 512 : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WN, wm = wave / WN;
+    const int r32 = lane & 31;
 
     // ---- which tile: dense grids are XCD-swizzled over (n-tile, m-tile); gather grids are
     // (unit, n-tile) with the unit list produced on the device
@@ -216,12 +269,10 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         nt_base = (lid / args.tiles_m) * C::TN;
         mt_base = (lid % args.tiles_m) * C::TM;
     }
-    const uint8_t* wfrag = wbase;
-    const uint8_t* wscale = wbase + args.w_scale_off;
-    const int NT = args.NT, KBp = args.KBp;
+    const int NT = args.NT, KBp = args.KBp, Np = NT * 32;
 
     // token slot (tile j, row r) -> activation row to read
-    auto src_token = [&](int j, int r) -> int {
+    auto src_token = [&](int j, int r) __attribute__((always_inline)) -> int {
         if constexpr (MODE == GATHER_F32) {
             const int s = j * 32 + r;
             return s < unit_count ? args.pairs[unit_first + s] / args.top_k : 0;
@@ -234,113 +285,75 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         if (tid < 128) reinterpret_cast<uint32_t*>(tab)[tid] = T::table_word(tid >> 2, tid & 3);
     }
 
-    // ---- copy plan: per-thread source pointers, advanced by a fixed stride every stage
-    const uint8_t* wsrc[C::UPT_W];
-    int wdst[C::UPT_W];
+    // ---- DMA plan: chunk c of a stage belongs to wave c % NW; per chunk this lane keeps a
+    // 32-bit source offset from the chunk's (wave-uniform) region base, advanced by a fixed
+    // stride per stage, and the chunk's LDS offset.
+    const uint8_t* gbase[C::CPW];
+    uint32_t goff[C::CPW];
+    int gadv[C::CPW], ldso[C::CPW];
+    {
+        const uint8_t* wfrag = wbase;
+        const uint8_t* wsc = wbase + args.w_scale_off;
+        const uint8_t* wmn = wbase + args.w_min_off;
 #pragma unroll
-    for (int i = 0; i < C::UPT_W; ++i) {
-        const int u = min(tid + i * C::NTH, C::UW - 1);
-        constexpr int per = KS * T::FB / 16;               // units per tile per stage
-        const int nt = min(nt_base + u / per, NT - 1);
-        wsrc[i] = wfrag + (int64_t)nt * KBp * T::FB + (u % per) * 16;
-        wdst[i] = (tid + i * C::NTH < C::UW) ? u * 16 : -1;
-    }
-    const uint8_t* xsrc[C::UPT_X];
-    int xdst[C::UPT_X];
-#pragma unroll
-    for (int i = 0; i < C::UPT_X; ++i) {
-        const int u = min(tid + i * C::NTH, C::UX - 1);
-        const int L = u & 63, q = (u >> 6) % KS, j = (u >> 6) / KS;
-        const int t = src_token(j, L & 31);
-        xsrc[i] = args.xq + ((int64_t)(t >> 5) * KBp + q) * 1024 + ((L >> 5) * 32 + (t & 31)) * 16;
-        xdst[i] = (tid + i * C::NTH < C::UX) ? C::WF + (j * KS + q) * 1024 + L * 16 : -1;
-    }
-    // scale items: (side, tile, block-in-stage, row)
-    const uint8_t* ssrc[C::SPT];
-    const uint8_t* ssrc2[C::SPT];
-    int sdst[C::SPT];
-    bool sw_[C::SPT];
-#pragma unroll
-    for (int i = 0; i < C::SPT; ++i) {
-        const int it = min(tid + i * C::NTH, C::SI - 1);
-        const int r = it & 31, q = (it >> 5) % KS, tile = (it >> 5) / KS;
-        const bool wside = tile < C::TN;
-        sw_[i] = wside;
-        if (wside) {
-            const int nt = min(nt_base + tile, NT - 1);
-            ssrc[i] = wscale + (((int64_t)nt * KBp + q) * 32 + r) * T::SB;
-            ssrc2[i] = ssrc[i];
-            // f16: one 16-byte entry per row; f32: a (64-float) pair of 32-float arrays per
-            // (tile, block), value at [r] and partner at [32 + r]
-            sdst[i] = C::WF + C::XF + (T::F32S ? ((tile * KS + q) * 64 + r) * 4 : ((tile * KS + q) * 32 + r) * 2);
-        } else {
-            const int j = tile - C::TN;
-            const int t = src_token(j, r);
-            const int64_t idx = ((int64_t)(t >> 5) * KBp + q) * 32 + (t & 31);
-            ssrc[i] = T::F32S ? reinterpret_cast<const uint8_t*>(args.xs + idx)
-                              : reinterpret_cast<const uint8_t*>(args.xs16 + idx);
-            ssrc2[i] = reinterpret_cast<const uint8_t*>(args.xsum + idx);
-            sdst[i] = C::WF + C::XF + C::WS + (T::F32S ? ((j * KS + q) * 64 + r) * 4 : ((j * KS + q) * 32 + r) * 2);
-        }
-        if (tid + i * C::NTH >= C::SI) sdst[i] = -1;
-    }
-    // per-stage advance of the scale sources (bytes)
-    constexpr int WSTEP = KS * 32 * T::SB;
-    constexpr int XSTEP = KS * 32 * (T::F32S ? 4 : 2);
-
-    v4i wreg[C::UPT_W], xreg[C::UPT_X];
-    uint32_t sreg[C::SPT], sreg2[C::SPT];
-    auto load_stage = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::UPT_W; ++i) {
-            wreg[i] = *reinterpret_cast<const v4i*>(wsrc[i]);
-            wsrc[i] += KS * T::FB;
-        }
-#pragma unroll
-        for (int i = 0; i < C::UPT_X; ++i) {
-            xreg[i] = *reinterpret_cast<const v4i*>(xsrc[i]);
-            xsrc[i] += KS * 1024;
-        }
-#pragma unroll
-        for (int i = 0; i < C::SPT; ++i) {
-            if constexpr (T::F32S) {
-                if (sw_[i]) {
-                    const uint2 v = *reinterpret_cast<const uint2*>(ssrc[i]);
-                    sreg[i] = v.x;
-                    sreg2[i] = v.y;
-                } else {
-                    sreg[i] = *reinterpret_cast<const uint32_t*>(ssrc[i]);
-                    sreg2[i] = *reinterpret_cast<const uint32_t*>(ssrc2[i]);
-                    ssrc2[i] += XSTEP;
-                }
-            } else {
-                sreg[i] = *reinterpret_cast<const uint16_t*>(ssrc[i]);
+        for (int j = 0; j < C::CPW; ++j) {
+            int c = wave + j * C::NW;
+            const int h = lane >> 5;
+            if (c < C::C_WF) {
+                const int byte = c * 1024 + lane * 16;
+                const int tile = byte / (KS * T::FB), off = byte % (KS * T::FB);
+                const int nt = min(nt_base + tile, NT - 1);
+                gbase[j] = wfrag;
+                goff[j] = (uint32_t)(nt * KBp * T::FB + off);
+                gadv[j] = KS * T::FB;
+                ldso[j] = c * 1024;
+            } else if ((c -= C::C_WF) < C::C_XF) {
+                const int jt = c / KS, q = c % KS;
+                const int t = src_token(jt, r32);
+                gbase[j] = args.xq;
+                goff[j] = (uint32_t)((((t >> 5) * KBp + q) * 64 + h * 32 + (t & 31)) * 16);
+                gadv[j] = KS * 1024;
+                ldso[j] = C::O_XF + c * 1024;
+            } else if ((c -= C::C_XF) < C::C_WS) {
+                const int n = min((nt_base + 2 * c + h) * 32 + r32, Np - 1);
+                gbase[j] = wsc;
+                goff[j] = (uint32_t)(n * KBp * 4);
+                gadv[j] = KS * 4;
+                ldso[j] = C::O_WS + c * 1024;
+            } else if ((c -= C::C_WS) < C::C_XS) {
+                const int jt = 2 * c + h;
+                const int t = jt < C::TM ? src_token(jt, r32) : 0;
+                gbase[j] = reinterpret_cast<const uint8_t*>(args.xs2);
+                goff[j] = (uint32_t)(t * KBp * 4);
+                gadv[j] = KS * 4;
+                ldso[j] = C::O_XS + c * 1024;
+            } else if ((c -= C::C_XS) < C::C_WM) {
+                const int n = min((nt_base + 2 * c + h) * 32 + r32, Np - 1);
+                gbase[j] = wmn;
+                goff[j] = (uint32_t)(n * KBp * 4);
+                gadv[j] = KS * 4;
+                ldso[j] = C::O_WM + c * 1024;
+            } else if ((c -= C::C_WM) < C::C_XM) {
+                const int jt = 2 * c + h;
+                const int t = jt < C::TM ? src_token(jt, r32) : 0;
+                gbase[j] = reinterpret_cast<const uint8_t*>(args.xsx);
+                goff[j] = (uint32_t)(t * KBp * 4);
+                gadv[j] = KS * 4;
+                ldso[j] = C::O_XM + c * 1024;
+            } else {                                        // padding chunk: any valid source
+                c -= C::C_XM;
+                gbase[j] = wfrag;
+                goff[j] = (uint32_t)(lane * 16);
+                gadv[j] = 0;
+                ldso[j] = C::O_PAD + c * 1024;
             }
-            ssrc[i] += sw_[i] ? WSTEP : XSTEP;
         }
-    };
-    auto store_stage = [&](uint8_t* buf) {
+    }
+    auto issue_stage = [&](uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::UPT_W; ++i)
-            if (C::UW % C::NTH == 0 || wdst[i] >= 0) *reinterpret_cast<v4i*>(buf + wdst[i]) = wreg[i];
-#pragma unroll
-        for (int i = 0; i < C::UPT_X; ++i)
-            if (C::UX % C::NTH == 0 || xdst[i] >= 0) *reinterpret_cast<v4i*>(buf + xdst[i]) = xreg[i];
-#pragma unroll
-        for (int i = 0; i < C::SPT; ++i) {
-            if (C::SI % C::NTH == 0 || sdst[i] >= 0) {
-                if constexpr (T::F32S) {
-                    // weights: d*sc, -dmin*m; tokens: xs, xs*xsum (exact in f32)
-                    float* d = reinterpret_cast<float*>(buf + sdst[i]);
-                    const float a = __builtin_bit_cast(float, sreg[i]);
-                    const float b = sw_[i] ? __builtin_bit_cast(float, sreg2[i])
-                                           : a * (float)(int32_t)sreg2[i];
-                    d[0] = a;
-                    d[32] = b;
-                } else {
-                    *reinterpret_cast<uint16_t*>(buf + sdst[i]) = (uint16_t)sreg[i];
-                }
-            }
+        for (int j = 0; j < C::CPW; ++j) {
+            dma16(gbase[j] + goff[j], buf + __builtin_amdgcn_readfirstlane(ldso[j]));
+            goff[j] += gadv[j];
         }
     };
 
@@ -352,129 +365,190 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
-    const v16i zi = {0};
     const v16f zf = {0};
-    const int nstages = KBp / KS;
+    v16i magic;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) magic[r] = MAGIC_I;
 
-    // one block's operands for this wave: weight fragments, token fragments, scale operands
+    constexpr int NT_ = RT * CT;
+    // one block's operands for this wave: raw LDS words (fetched a block ahead), then the MFMA
+    // operands unpacked from them one step before the block starts
+    struct Raw {
+        typename T::Raw w[RT];
+        v4i b[CT];
+        uint32_t wsd[RT], xs[CT];
+    };
     struct Ops {
         v4i a[RT][T::NMF];
         v4i b[CT];
-        h8 wsv[RT], xsv[CT];            // f16 scale operands (slot 0 live)
-        float wsf[RT], wmf[RT], xsf[CT], sxf[CT];   // Q4_K: d*sc, -dmin*m, xs, xs*xsum
+        uint32_t ws[RT], xs[CT];
     };
-    auto load_w = [&](const uint8_t* cur, int kb, int rt, Ops& o) {
-        const int i = wn * RT + rt;
-        T::operands(cur + (i * KS + kb) * T::FB, lane, tab, o.a[rt]);
-        const uint8_t* wsl = cur + C::WF + C::XF;
-        if constexpr (T::F32S) {
-            const float* p = reinterpret_cast<const float*>(wsl) + (i * KS + kb) * 64 + (lane & 31);
-            o.wsf[rt] = p[0];
-            o.wmf[rt] = p[32];
-        } else {
-            const uint16_t v = *reinterpret_cast<const uint16_t*>(wsl + ((i * KS + kb) * 32 + (lane & 31)) * 2);
-            v4i t4 = {(int)v, 0, 0, 0};
-            o.wsv[rt] = __builtin_bit_cast(h8, t4);
+    auto fetch = [&](const uint8_t* cur, int kb, Raw& R) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int i = wn * RT + rt;
+            R.wsd[rt] = *reinterpret_cast<const uint32_t*>(cur + C::O_WS + ((i * 32 + r32) * KS + kb) * 4);
+            T::fetch(cur + (i * KS + kb) * T::FB, lane, R.w[rt]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int j = wm * CT + ct;
+            R.b[ct] = *reinterpret_cast<const v4i*>(cur + C::O_XF + (j * KS + kb) * 1024 + lane * 16);
+            R.xs[ct] = *reinterpret_cast<const uint32_t*>(cur + C::O_XS + ((j * 32 + r32) * KS + kb) * 4);
         }
     };
-    auto load_x = [&](const uint8_t* cur, int kb, int ct, Ops& o) {
-        const int j = wm * CT + ct;
-        o.b[ct] = *reinterpret_cast<const v4i*>(cur + C::WF + (j * KS + kb) * 1024 + lane * 16);
-        const uint8_t* xsl = cur + C::WF + C::XF + C::WS;
-        if constexpr (T::F32S) {
-            const float* p = reinterpret_cast<const float*>(xsl) + (j * KS + kb) * 64 + (lane & 31);
-            o.xsf[ct] = p[0];
-            o.sxf[ct] = p[32];
-        } else {
-            const uint16_t v = *reinterpret_cast<const uint16_t*>(xsl + ((j * KS + kb) * 32 + (lane & 31)) * 2);
-            v4i t4 = {(int)v, 0, 0, 0};
-            o.xsv[ct] = __builtin_bit_cast(h8, t4);
+    auto mid = [&](Raw& R) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) T::mid(R.w[rt], R.wsd[rt], lane, tab);
+    };
+    auto unpack = [&](const Raw& R, Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            T::unpack(R.w[rt], o.a[rt]);
+            o.ws[rt] = T::scale_op(R.wsd[rt]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            o.b[ct] = R.b[ct];
+            o.xs[ct] = R.xs[ct];
         }
     };
-    // matrix-core half of one (tile, block): exact int32 dots D, scale outer product S, and
-    // for Q4_K the rank-1 min term added into the accumulator through the C operand
-    auto issue = [&](const Ops& o, int t, v16i& D, v16f& S) {
+    auto load_ops = [&](const uint8_t* cur, int kb, Ops& o) __attribute__((always_inline)) {
+        Raw R;
+        fetch(cur, kb, R);
+        mid(R);
+        unpack(R, o);
+    };
+
+    // matrix-core half of tile t of a block: D (exact int32 dots), S (scale outer product)
+    auto mfma_dots = [&](const Ops& o, int t) __attribute__((always_inline)) -> v16i {
         const int rt = t / CT, ct = t % CT;
-        D = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][0], o.b[ct], zi, 0, 0, 0);
+        v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][0], o.b[ct], magic, 0, 0, 0);
         if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][1], o.b[ct], D, 0, 0, 0);
-        if constexpr (MODE != DENSE_PARTIALS) {
-            if constexpr (T::F32S) {
-                S = __builtin_amdgcn_mfma_f32_32x32x2f32(o.wsf[rt], o.xsf[ct], zf, 0, 0, 0);
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(o.wmf[rt], o.sxf[ct], acc[rt][ct], 0, 0, 0);
-            } else {
-                S = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.wsv[rt], o.xsv[ct], zf, 0, 0, 0);
+        return D;
+    };
+    auto mfma_scale = [&](const Ops& o, int t) __attribute__((always_inline)) -> v16f {
+        const int rt = t / CT, ct = t % CT;
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(as_h4(o.ws[rt]), as_h4(o.xs[ct]), zf, 0, 0, 0);
+    };
+    // The empty asm after a tile's last FMA pins its accumulator: FMAs are pure, and left alone
+    // the compiler sinks a whole stage of them below its matrix-core work, which then has to
+    // hold every X and S at once.
+    // D -> X = D - c, in place: 16 independent subtractions. (The whole vector is
+    // reinterpreted at once: hipcc's __builtin_bit_cast of a single vector element reads element
+    // 0 whatever the index.)
+    auto unbias = [&](const v16i& D) __attribute__((always_inline)) -> v16f {
+        return __builtin_bit_cast(v16f, D) - MAGIC_F;
+    };
+    // acc += X * S: 16 independent FMAs. The empty asm after them pins the accumulator: FMAs are
+    // pure, and left alone the compiler sinks a whole stage of them below its matrix-core work,
+    // which then has to hold every D and S at once.
+    auto fma_tile = [&](int t, const v16f& X, const v16f& S) __attribute__((always_inline)) {
+        const int rt = t / CT, ct = t % CT;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[rt][ct][r] = __builtin_fmaf(X[r], S[r], acc[rt][ct][r]);
+        asm volatile("" : "+v"(acc[rt][ct]));
+    };
+    // partials mode: the exact int32 dots of block kbg go straight to memory
+    auto store_partials = [&](int kbg, int t, const v16i& D) __attribute__((always_inline)) {
+        const int rt = t / CT, ct = t % CT;
+        const int m = (mt_base + wm * CT + ct) * 32 + r32;
+        if (kbg < args.KB && m < args.M) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = (nt_base + wn * RT + rt) * 32 + acc_row(lane, r);
+                if (n < args.N) args.partials[((int64_t)m * args.N + n) * args.KB + kbg] = (D[r] - MAGIC_I) >> T::SHIFT;
             }
         }
     };
-    // vector half: acc += f32(D) * S (or the partials store)
-    auto finish = [&](int s, int kb, int t, const v16i& D, const v16f& S) {
-        const int rt = t / CT, ct = t % CT;
-        if constexpr (MODE == DENSE_PARTIALS) {
-            const int kbg = s * KS + kb;
-            const int m = (mt_base + wm * CT + ct) * 32 + (lane & 31);
-            if (kbg < args.KB && m < args.M) {
+    // q4_K: the min term of blocks (2p, 2p+1) of the stage, one half-wave per block
+    auto min_term = [&](const uint8_t* cur, int p) __attribute__((always_inline)) {
+        if constexpr (T::MIN) {
+            const int kb = 2 * p + (lane >> 5);
+            float wv[RT], xv[CT];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int n = (nt_base + wn * RT + rt) * 32 + acc_row(lane, r);
-                    if (n < args.N) args.partials[((int64_t)m * args.N + n) * args.KB + kbg] = D[r] >> T::SHIFT;
-                }
-            }
-        } else {
+            for (int rt = 0; rt < RT; ++rt)
+                wv[rt] = *reinterpret_cast<const float*>(cur + C::O_WM + (((wn * RT + rt) * 32 + r32) * KS + kb) * 4);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[rt][ct][r] = __builtin_fmaf((float)D[r], S[r], acc[rt][ct][r]);
+            for (int ct = 0; ct < CT; ++ct)      // * 2^-25, like S = 2 wd xs times D - c = P 2^-26
+                xv[ct] = (2.0f / UNBIAS) * *reinterpret_cast<const float*>(cur + C::O_XM + (((wm * CT + ct) * 32 + r32) * KS + kb) * 4);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(wv[rt], xv[ct], acc[rt][ct], 0, 0, 0);
         }
     };
 
-    // Tile t of a block is (rt, ct) = (t / CT, t % CT). Step t issues tile t+1 (or tile 0 of
-    // the next block) and then finishes tile t. Right after the issue of the last tile that
-    // reads an operand (a[rt]: tile rt*CT + CT-1; b[ct]: tile (RT-1)*CT + ct), that operand is
-    // reloaded for the next block, so one register set serves and every LDS read has at least
-    // two steps of VALU work to land before its next use.
-    constexpr int NT_ = RT * CT;
-    // One stage: its KS blocks through the tile pipeline. `last` is a compile-time flag so the
-    // steady-state loop body has no branches (a branch lets the compiler sink the VALU half of
-    // the pipeline past it).
-    auto run_stage = [&](int s, auto last_tag) {
-        constexpr bool LAST = decltype(last_tag)::value;
-        const uint8_t* cur = lds[s & 1];
-        if constexpr (!LAST) load_stage();              // in flight during this stage's MFMAs
-        Ops op;
-        v16i D[2];
-        v16f S[2];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) load_w(cur, 0, rt, op);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) load_x(cur, 0, ct, op);
-        issue(op, 0, D[0], S[0]);
+    // One stage: KS blocks x NT_ tiles as one software pipeline. Step i issues the matrix-core
+    // work of step i+1 (dots, scale, conversion) around the vector FMAs of step i, so the
+    // matrix core and the vector unit stay busy together. The next block's operands are read
+    // from LDS at its first step and unpacked at its last.
+    auto run_stage = [&](const uint8_t* cur, int s) __attribute__((always_inline)) {
+        Ops op[2];
+        Raw raw;
+        load_ops(cur, 0, op[0]);
+        v16i Dc;
+        v16f Sc;
+        Dc = mfma_dots(op[0], 0);
+        if constexpr (MODE == DENSE_PARTIALS) store_partials(s * KS, 0, Dc);
+        else Sc = mfma_scale(op[0], 0);
 #pragma unroll
         for (int kb = 0; kb < KS; ++kb) {
 #pragma unroll
             for (int t = 0; t < NT_; ++t) {
-                const int i = kb * NT_ + t;
-                if (t + 1 < NT_ || kb + 1 < KS) issue(op, (t + 1) % NT_, D[(i + 1) & 1], S[(i + 1) & 1]);
+                const bool more = t + 1 < NT_ || kb + 1 < KS;
+                const int kn = (t + 1 < NT_) ? kb : kb + 1, tn = (t + 1) % NT_;
                 if (kb + 1 < KS) {
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        if (t == (rt * CT + CT - 2 > 0 ? rt * CT + CT - 2 : 0)) load_w(cur, kb + 1, rt, op);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        if (t == ((RT - 1) * CT + ct - 1 > 0 ? (RT - 1) * CT + ct - 1 : 0)) load_x(cur, kb + 1, ct, op);
+                    if (t == 0) fetch(cur, kb + 1, raw);
+                    if (t == (NT_ >= 3 ? NT_ - 2 : 0)) mid(raw);
+                    if (t == NT_ - 1) unpack(raw, op[(kb + 1) & 1]);
                 }
-                // keep the next tile's MFMAs ahead of this tile's VALU work
-                __builtin_amdgcn_sched_barrier(0);
-                finish(s, kb, t, D[i & 1], S[i & 1]);
-                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (MODE == DENSE_PARTIALS) {
+                    if (more) store_partials(s * KS + kn, tn, mfma_dots(op[kn & 1], tn));
+                } else {
+                    v16i Dn;
+                    v16f Sn;
+                    // Two fenced halves per step, each a matrix-core op over a run of independent
+                    // vector ops of the previous tile: the int8 MFMA of the next tile with this
+                    // tile's 16 subtractions, then the scale MFMA with its 16 FMAs. (Unfenced, the
+                    // scheduler threads subtractions and FMAs into one dependent chain through a
+                    // single temporary.)
+                    __builtin_amdgcn_sched_barrier(0);
+                    const v16f X = unbias(Dc);
+                    if (more) {
+                        Dn = mfma_dots(op[kn & 1], tn);
+                        __builtin_amdgcn_sched_group_barrier(0x008, T::NMF, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    fma_tile(t, X, Sc);
+                    if (more) {
+                        Sn = mfma_scale(op[kn & 1], tn);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (T::MIN && t == NT_ - 1 && (kb & 1)) min_term(cur, kb >> 1);
+                    Dc = Dn;
+                    Sc = Sn;
+                }
             }
         }
-        if constexpr (!LAST) store_stage(lds[(s + 1) & 1]);
-        __syncthreads();
     };
 
-    load_stage();
-    store_stage(lds[0]);
-    __syncthreads();
-    for (int s = 0; s + 1 < nstages; ++s) run_stage(s, std::false_type{});
-    run_stage(nstages - 1, std::true_type{});
+    const int nstages = KBp / KS;                // even: KBp is a multiple of 8
+    issue_stage(buf0);
+    for (int s = 0; s < nstages; s += 2) {
+        __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0): this wave's DMA of stage s landed
+        __syncthreads();                          // ... and everyone's; stage s-1 fully consumed
+        issue_stage(buf1);
+        run_stage(buf0, s);
+        __builtin_amdgcn_s_waitcnt(0x3f70);
+        __syncthreads();
+        if (s + 2 < nstages) issue_stage(buf0);
+        run_stage(buf1, s + 1);
+    }
 
     if constexpr (MODE != DENSE_PARTIALS) {
         const int64_t ldo = args.ldo;
@@ -483,10 +557,10 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         for (int ct = 0; ct < CT; ++ct) {
             int row;
             if constexpr (MODE == GATHER_F32) {
-                const int sl = (wm * CT + ct) * 32 + (lane & 31);
+                const int sl = (wm * CT + ct) * 32 + r32;
                 row = sl < unit_count ? args.pairs[unit_first + sl] : -1;
             } else {
-                const int m = (mt_base + wm * CT + ct) * 32 + (lane & 31);
+                const int m = (mt_base + wm * CT + ct) * 32 + r32;
                 row = m < args.M ? m : -1;
             }
             if (row < 0) continue;
@@ -512,8 +586,8 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 }
 
 // Tile configuration: 2 x 2 waves, each owning 2 weight tiles x 2 token tiles -> 128 x 128
-// CTA tiles, 2 blocks per stage.
-constexpr int WN_ = 2, WM_ = 2, RT_ = 2, CT_ = 2, KS_ = 2;
+// CTA tiles.
+constexpr int WN_ = 2, WM_ = 2, RT_ = 2, CT_ = 2;
 
 template <mmq_wtype FMT>
 BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, int64_t K) {
@@ -523,11 +597,11 @@ BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, 
     BlockArgs g{};
     g.w = static_cast<const uint8_t*>(packed) + P.frag_off;
     g.w_scale_off = P.scale_off - P.frag_off;
+    g.w_min_off = P.min_off - P.frag_off;
     g.w_stride = 0;
     g.xq = ab + A.xq_off;
-    g.xs = reinterpret_cast<const float*>(ab + A.xs_off);
-    g.xsum = reinterpret_cast<const int32_t*>(ab + A.xsum_off);
-    g.xs16 = reinterpret_cast<const uint16_t*>(ab + A.xs16_off);
+    g.xs2 = reinterpret_cast<const uint32_t*>(ab + A.xs2_off);
+    g.xsx = reinterpret_cast<const float*>(ab + A.xsx_off);
     g.M = (int)M;
     g.N = (int)N;
     g.KB = (int)A.KB;
@@ -548,10 +622,10 @@ hipError_t launch_dense(const void* packed, const void* act, int64_t M, int64_t 
     const dim3 grid((unsigned)((int64_t)tiles_n * tiles_m)), block(WN_ * WM_ * 64);
     if (o == MMQ_OUT_I32_PARTIALS) {
         g.partials = static_cast<int32_t*>(out);
-        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, KS_, DENSE_PARTIALS>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_PARTIALS>), grid, block, 0, s, g);
     } else {
         g.out = static_cast<float*>(out);
-        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, KS_, DENSE_F32>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_F32>), grid, block, 0, s, g);
     }
     return hipGetLastError();
 }
@@ -572,7 +646,7 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
     g.ldo = N;
     const int64_t nblk = round_up(max_units, 8) * g.ntiles_n;
     const dim3 grid((unsigned)nblk), block(WN_ * WM_ * 64);
-    hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, KS_, GATHER_F32>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, GATHER_F32>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 

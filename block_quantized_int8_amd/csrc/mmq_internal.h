@@ -19,12 +19,18 @@ __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ activation layout
-// MMQ_ACT_Q8_1 (see mmq.h): region 0 xq tiled [Mp/32][KBp][64 lanes][16 B] (lane L = h*32 + r
-// holds row r's values 16h..16h+15 of the block: the B operand of v_mfma_i32_32x32x32_i8);
-// region 1 xs f32, region 2 xsum int32, region 3 xs as f16 bits, each [Mp/32][KBp][32].
+// MMQ_ACT_Q8_1 (see mmq.h):
+//   region 0 xq   int8, tiled [Mp/32][KBp][64 lanes][16 B]: lane L = h*32 + r holds row r's
+//                 values 16h..16h+15 of the block (the B operand of v_mfma_i32_32x32x32_i8)
+//   region 1 xs   f32   [Mp][KBp]   (row-major)
+//   region 2 xsum int32 [Mp][KBp]
+//   region 3 xs2  u32   [Mp][KBp]   xs as f16 bits in both halves (the scale-MFMA operand)
+//   region 4 xsx  f32   [Mp][KBp]   xs * xsum, exact in f32 (the Q4_K min-term operand)
+// Row-major scale regions let one 16-byte load fetch one row's 4 consecutive blocks, which is
+// what a gathered (MUL_MAT_ID) token row needs.
 struct ActQ81Layout {
     int64_t Mp, MT, KB, KBp;
-    int64_t xq_off, xs_off, xsum_off, xs16_off, bytes;
+    int64_t xq_off, xs_off, xsum_off, xs2_off, xsx_off, bytes;
 };
 
 inline ActQ81Layout act_q8_1_layout(int64_t M, int64_t K) {
@@ -33,12 +39,13 @@ inline ActQ81Layout act_q8_1_layout(int64_t M, int64_t K) {
     L.MT = L.Mp / TILE;
     L.KB = K / QK;
     L.KBp = round_up(L.KB, KB_ALIGN);
-    const int64_t tiles = L.MT * L.KBp;
+    const int64_t cells = L.Mp * L.KBp;          // (row, block) entries of a scale region
     L.xq_off = 0;
-    L.xs_off = round_up(tiles * 1024, REGION_ALIGN);
-    L.xsum_off = L.xs_off + round_up(tiles * TILE * 4, REGION_ALIGN);
-    L.xs16_off = L.xsum_off + round_up(tiles * TILE * 4, REGION_ALIGN);
-    L.bytes = L.xs16_off + round_up(tiles * TILE * 2, REGION_ALIGN);
+    L.xs_off = round_up(L.MT * L.KBp * 1024, REGION_ALIGN);
+    L.xsum_off = L.xs_off + round_up(cells * 4, REGION_ALIGN);
+    L.xs2_off = L.xsum_off + round_up(cells * 4, REGION_ALIGN);
+    L.xsx_off = L.xs2_off + round_up(cells * 4, REGION_ALIGN);
+    L.bytes = L.xsx_off + round_up(cells * 4, REGION_ALIGN);
     return L;
 }
 
@@ -66,16 +73,19 @@ inline ActI8Layout act_i8_layout(int64_t M, int64_t K) {
 //         the matrix core computes 16x the block dot, exactly -> 512 B.
 //   Q4_K: 8 B per lane, unsigned nibbles: X0 & 0x0F0F0F0F = k 16h+0..3, (X0 >> 4) & 0x0F0F0F0F
 //         = 16h+4..7, likewise X1 for 8..15 -> 512 B.
-//   IQ1T: per lane a dword of 2-bit codes (value 16h + 4q + b at bits 8b + 2q), then 64 meta
-//         bytes s | sigma0 << 3 | sigma1 << 4 (the lane's 16-value sub-scale and the sign bits of
-//         its two 8-value groups) -> 320 B.
-// Region 1 holds the per-(nt, b, row) scales [NT][KBp][32]: f16 d for Q8_0, Q4_0 and IQ1T (the
-// super-block's d); f32 pairs (d*sc, -dmin*m) for Q4_K. I8_ROW keeps one f32 per row [Np].
+//   IQ1T: 4 B per lane of 2-bit codes (value 16h + 4q + b at bits 8b + 2q) -> 256 B.
+// Region 1 holds one dword per (row n, block b), row-major [Np][KBp]:
+//   Q8_0, Q4_0: f16 d in the low half, 0 in the high half.
+//   IQ1T:       f16 d (the super-block's) | meta0 << 16 | meta1 << 24, meta_h = s | sigma0 << 3 |
+//               sigma1 << 4 for the half h = 0, 1 of the block (its 16-value sub-scale and the
+//               sign bits of its two 8-value groups).
+//   Q4_K:       d*sc split exactly into two f16 (hi | lo << 16), hi + lo = d*sc.
+// Region 2 (Q4_K only): f32 -dmin*m per (row, block), [Np][KBp].
+// I8_ROW keeps one f32 per row [Np] in region 1.
 struct PackedLayout {
     int64_t Np, NT, KB, KBp;
     int64_t frag_bytes;          // bytes per (nt, b) fragment
-    int64_t scale_bytes;         // bytes per (nt, b, row) scale entry
-    int64_t frag_off, scale_off, bytes;
+    int64_t frag_off, scale_off, min_off, bytes;
 };
 
 inline PackedLayout packed_layout(mmq_wtype t, int64_t N, int64_t K) {
@@ -85,16 +95,18 @@ inline PackedLayout packed_layout(mmq_wtype t, int64_t N, int64_t K) {
     L.KB = K / QK;
     L.KBp = round_up(L.KB, KB_ALIGN);
     switch (t) {
-        case MMQ_Q8_0: L.frag_bytes = 1024; L.scale_bytes = 2; break;
-        case MMQ_Q4_0: L.frag_bytes = 512; L.scale_bytes = 2; break;
-        case MMQ_Q4_K: L.frag_bytes = 512; L.scale_bytes = 8; break;
-        case MMQ_IQ1T: L.frag_bytes = 320; L.scale_bytes = 2; break;
-        default: L.frag_bytes = 1024; L.scale_bytes = 0; break;           // I8_ROW
+        case MMQ_Q8_0: L.frag_bytes = 1024; break;
+        case MMQ_Q4_0: L.frag_bytes = 512; break;
+        case MMQ_Q4_K: L.frag_bytes = 512; break;
+        case MMQ_IQ1T: L.frag_bytes = 256; break;
+        default: L.frag_bytes = 1024; break;           // I8_ROW
     }
+    const int64_t cells = L.Np * L.KBp;
     L.frag_off = 0;
     L.scale_off = round_up(L.NT * L.KBp * L.frag_bytes, REGION_ALIGN);
-    const int64_t sb = (t == MMQ_I8_ROW) ? L.Np * 4 : L.NT * L.KBp * TILE * L.scale_bytes;
-    L.bytes = L.scale_off + round_up(sb, REGION_ALIGN);
+    const int64_t sb = (t == MMQ_I8_ROW) ? L.Np * 4 : cells * 4;
+    L.min_off = L.scale_off + round_up(sb, REGION_ALIGN);
+    L.bytes = L.min_off + (t == MMQ_Q4_K ? round_up(cells * 4, REGION_ALIGN) : 0);
     return L;
 }
 

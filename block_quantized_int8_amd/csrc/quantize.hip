@@ -7,74 +7,99 @@
 // -fhip-fp32-correctly-rounded-divide-sqrt) and nothing is contracted, so the result is
 // bit-identical to the definition.
 //
-// The q8_1 output is written directly in the matrix-core tile order the GEMM consumes
-// (see mmq.h, region 0), so the GEMM streams whole fragments straight into LDS; xs is also
-// written as f16 bits (region 3, exact: xs is f16-rounded by definition), the form the GEMM's
-// scale outer product consumes.
+// Work split: one wave per (32-row tile, group of 8 blocks). Lane L = h*32 + r owns row r's
+// values 16h..16h+15 of each block - exactly the 16 bytes it writes to the tiled xq layout, so
+// every block's 1 KB tile is one contiguous wave store. The two lanes of a block (r and r+32)
+// combine their half-block max and sum with one cross-half exchange. Each row's 8 scale entries
+// per region are contiguous (row-major regions): lane h = 0 writes xs and xsum, lane h = 1 the
+// derived xs2 (f16 pair) and xsx = xs * xsum (exact in f32: an 11-bit significand times a
+// |sum| <= 32*128).
 #include "mmq_internal.h"
 
 namespace {
 
-constexpr int QROWS = 32;     // rows per CTA (one row tile)
-constexpr int QBLK = 8;       // 32-value blocks per CTA along K (256 values)
+constexpr int QG = 8;             // blocks per wave (one 32-row tile x 256 values)
+constexpr int QWAVES = 4;         // waves per workgroup
 
-// One CTA = 32 rows x 8 blocks. Thread t: row r = t/8, lane-in-block j = t%8 holds the four
-// values 4j..4j+3 of each of the 8 blocks, so each load instruction reads 128 contiguous
-// bytes per row. Block reductions are over the 8 consecutive lanes of a row.
-__global__ __launch_bounds__(256) void quantize_q8_1_kernel(
-    const float* __restrict__ x, int64_t M, int64_t KB, int64_t ldx, int64_t KBp,
+__device__ inline uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)(d & 0xFF) << 24);
+}
+
+__device__ inline int q_of(float x, float di) {
+    return (int)fminf(fmaxf(__builtin_rintf(x * di), -128.f), 127.f);
+}
+
+__global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
+    const float* __restrict__ x, int64_t M, int64_t KB, int64_t ldx, int64_t KBp, int64_t units,
     int8_t* __restrict__ xq, float* __restrict__ xs, int32_t* __restrict__ xsum,
-    uint16_t* __restrict__ xs16) {
-    const int t = threadIdx.x;
-    const int r = t >> 3;
-    const int j = t & 7;
-    const int64_t mt = blockIdx.y;
-    const int64_t m = mt * QROWS + r;
-    const int64_t kb0 = (int64_t)blockIdx.x * QBLK;
+    uint32_t* __restrict__ xs2, float* __restrict__ xsx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t u = (int64_t)blockIdx.x * QWAVES + (threadIdx.x >> 6);
+    if (u >= units) return;                                 // uniform per wave
+    const int64_t G = KBp / QG;
+    const int64_t mt = u / G, g = u % G;
+    const int r = lane & 31, h = lane >> 5;
+    const int64_t m = mt * 32 + r;
+    const int64_t kb0 = g * QG;
     const bool row_ok = m < M;
 
-    float4 v[QBLK];
+    float4 v[QG][4];
 #pragma unroll
-    for (int i = 0; i < QBLK; ++i) {
-        const int64_t kb = kb0 + i;
-        if (row_ok && kb < KB) {
-            v[i] = *reinterpret_cast<const float4*>(x + m * ldx + kb * 32 + 4 * j);
-        } else {
-            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    for (int i = 0; i < QG; ++i) {
+        const bool ok = row_ok && kb0 + i < KB;
+        const float* p = x + m * ldx + (kb0 + i) * 32 + 16 * h;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            v[i][c] = ok ? *reinterpret_cast<const float4*>(p + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
+    float s_xs[QG];
+    int s_sum[QG];
 #pragma unroll
-    for (int i = 0; i < QBLK; ++i) {
-        const int64_t kb = kb0 + i;
-        if (kb >= KBp) break;   // uniform across the CTA
-        float amax = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        amax = fmaxf(amax, __shfl_xor(amax, 4));
+    for (int i = 0; i < QG; ++i) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i][c].x), fabsf(v[i][c].y)),
+                                     fmaxf(fabsf(v[i][c].z), fabsf(v[i][c].w))));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
         const float d = amax / 127.0f;
         const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
-        float q0 = fminf(fmaxf(__builtin_rintf(v[i].x * di), -128.f), 127.f);
-        float q1 = fminf(fmaxf(__builtin_rintf(v[i].y * di), -128.f), 127.f);
-        float q2 = fminf(fmaxf(__builtin_rintf(v[i].z * di), -128.f), 127.f);
-        float q3 = fminf(fmaxf(__builtin_rintf(v[i].w * di), -128.f), 127.f);
-        const int iq0 = (int)q0, iq1 = (int)q1, iq2 = (int)q2, iq3 = (int)q3;
-        int s = iq0 + iq1 + iq2 + iq3;
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        const uint32_t packed = (uint32_t)(iq0 & 0xFF) | ((uint32_t)(iq1 & 0xFF) << 8) |
-                                ((uint32_t)(iq2 & 0xFF) << 16) | ((uint32_t)(iq3 & 0xFF) << 24);
-        const int64_t tile = mt * KBp + kb;
-        const int h = j >> 2;                       // values 4j..4j+3 sit in half h = j/4
-        uint32_t* dst = reinterpret_cast<uint32_t*>(xq + tile * 1024 + (h * 32 + r) * 16 + 4 * (j & 3));
-        *dst = packed;
-        if (j == 0) {
-            const _Float16 dh = (_Float16)d;
-            xs[tile * 32 + r] = (float)dh;
-            xsum[tile * 32 + r] = s;
-            xs16[tile * 32 + r] = __builtin_bit_cast(uint16_t, dh);
+        uint32_t w[4];
+        int s = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int a = q_of(v[i][c].x, di), b = q_of(v[i][c].y, di);
+            const int e = q_of(v[i][c].z, di), f = q_of(v[i][c].w, di);
+            s += a + b + e + f;
+            w[c] = pack4(a, b, e, f);
         }
+        s += __shfl_xor(s, 32);
+        *reinterpret_cast<uint4*>(xq + ((mt * KBp + kb0 + i) * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        s_xs[i] = (float)(_Float16)d;
+        s_sum[i] = s;
+    }
+
+    const int64_t row = (mt * 32 + r) * KBp + kb0;
+    if (h == 0) {
+        *reinterpret_cast<float4*>(xs + row) = make_float4(s_xs[0], s_xs[1], s_xs[2], s_xs[3]);
+        *reinterpret_cast<float4*>(xs + row + 4) = make_float4(s_xs[4], s_xs[5], s_xs[6], s_xs[7]);
+        *reinterpret_cast<int4*>(xsum + row) = make_int4(s_sum[0], s_sum[1], s_sum[2], s_sum[3]);
+        *reinterpret_cast<int4*>(xsum + row + 4) = make_int4(s_sum[4], s_sum[5], s_sum[6], s_sum[7]);
+    } else {
+        uint32_t p2[QG];
+        float px[QG];
+#pragma unroll
+        for (int i = 0; i < QG; ++i) {
+            const uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)s_xs[i]);
+            p2[i] = b | (b << 16);
+            px[i] = s_xs[i] * (float)s_sum[i];
+        }
+        *reinterpret_cast<uint4*>(xs2 + row) = make_uint4(p2[0], p2[1], p2[2], p2[3]);
+        *reinterpret_cast<uint4*>(xs2 + row + 4) = make_uint4(p2[4], p2[5], p2[6], p2[7]);
+        *reinterpret_cast<float4*>(xsx + row) = make_float4(px[0], px[1], px[2], px[3]);
+        *reinterpret_cast<float4*>(xsx + row + 4) = make_float4(px[4], px[5], px[6], px[7]);
     }
 }
 
@@ -100,13 +125,8 @@ __global__ __launch_bounds__(256) void quantize_i8_token_kernel(
     const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
     for (int64_t k = (int64_t)threadIdx.x * 4; k < K; k += 1024) {
         float4 v = *reinterpret_cast<const float4*>(row + k);
-        int q0 = (int)fminf(fmaxf(__builtin_rintf(v.x * di), -128.f), 127.f);
-        int q1 = (int)fminf(fmaxf(__builtin_rintf(v.y * di), -128.f), 127.f);
-        int q2 = (int)fminf(fmaxf(__builtin_rintf(v.z * di), -128.f), 127.f);
-        int q3 = (int)fminf(fmaxf(__builtin_rintf(v.w * di), -128.f), 127.f);
         *reinterpret_cast<uint32_t*>(a + m * K + k) =
-            (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-            ((uint32_t)(q3 & 0xFF) << 24);
+            pack4(q_of(v.x, di), q_of(v.y, di), q_of(v.z, di), q_of(v.w, di));
     }
     if (threadIdx.x == 0) sa[m] = d;
 }
@@ -117,14 +137,17 @@ namespace mmq {
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ldx, void* act,
                                 hipStream_t s) {
+    static_assert(KB_ALIGN % QG == 0, "block padding must be whole wave groups");
     const ActQ81Layout L = act_q8_1_layout(M, K);
     uint8_t* base = static_cast<uint8_t*>(act);
-    dim3 grid((unsigned)(L.KBp / QBLK), (unsigned)L.MT);
-    hipLaunchKernelGGL(quantize_q8_1_kernel, grid, dim3(256), 0, s, x, M, L.KB, ldx, L.KBp,
-                       reinterpret_cast<int8_t*>(base + L.xq_off),
+    const int64_t units = L.MT * (L.KBp / QG);
+    const dim3 grid((unsigned)ceil_div(units, QWAVES));
+    hipLaunchKernelGGL(quantize_q8_1_kernel, grid, dim3(QWAVES * 64), 0, s, x, M, L.KB, ldx, L.KBp,
+                       units, reinterpret_cast<int8_t*>(base + L.xq_off),
                        reinterpret_cast<float*>(base + L.xs_off),
                        reinterpret_cast<int32_t*>(base + L.xsum_off),
-                       reinterpret_cast<uint16_t*>(base + L.xs16_off));
+                       reinterpret_cast<uint32_t*>(base + L.xs2_off),
+                       reinterpret_cast<float*>(base + L.xsx_off));
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ __device__ inline Lane lane_of(int64_t gid, int64_t KBp, int64_t KB, int64_t N) 
 
 __global__ __launch_bounds__(256) void repack_q8_0_kernel(
     const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
-    uint8_t* __restrict__ frag, uint16_t* __restrict__ scale) {
+    uint8_t* __restrict__ frag, uint32_t* __restrict__ scale) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
@@ -54,12 +54,12 @@ __global__ __launch_bounds__(256) void repack_q8_0_kernel(
                    ((uint32_t)q[4 * i + 3] << 24);
     }
     *reinterpret_cast<uint4*>(frag + gid * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    if (x.h == 0) scale[x.tb * 32 + x.r] = d;
+    if (x.h == 0) scale[x.n * KBp + x.b] = d;            // f16 d | 0 << 16
 }
 
 __global__ __launch_bounds__(256) void repack_q4_0_kernel(
     const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
-    uint8_t* __restrict__ frag, uint16_t* __restrict__ scale) {
+    uint8_t* __restrict__ frag, uint32_t* __restrict__ scale) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
@@ -79,17 +79,18 @@ __global__ __launch_bounds__(256) void repack_q4_0_kernel(
         }
     }
     *reinterpret_cast<uint2*>(frag + gid * 8) = make_uint2(X0, X1);
-    if (x.h == 0) scale[x.tb * 32 + x.r] = d;
+    if (x.h == 0) scale[x.n * KBp + x.b] = d;            // f16 d | 0 << 16
 }
 
 __global__ __launch_bounds__(256) void repack_q4_K_kernel(
     const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
-    uint8_t* __restrict__ frag, float* __restrict__ scale) {
+    uint8_t* __restrict__ frag, uint32_t* __restrict__ scale, float* __restrict__ mins) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t X0 = 0, X1 = 0;
-    float ds = 0.f, dm = 0.f;
+    uint32_t ds2 = 0;
+    float dm = 0.f;
     if (x.live) {
         const int64_t sb = x.b / 8;
         const int j = (int)(x.b % 8);
@@ -110,16 +111,24 @@ __global__ __launch_bounds__(256) void repack_q4_K_kernel(
             mw |= (uint64_t)blk[10 + i] << (8 * i);
         }
         const int sc = (int)((scw >> (6 * j)) & 63u), mm = (int)((mw >> (6 * j)) & 63u);
-        ds = half_bits_to_float(ld_u16(blk)) * (float)sc;          // exact: f16 x 6-bit integer
+        // d*sc is exact in f32 (11-bit significand x 6-bit integer); split it into two f16 with
+        // hi + lo == d*sc exactly (the remainder has at most 6 significant bits)
+        const float ds = half_bits_to_float(ld_u16(blk)) * (float)sc;
+        const _Float16 hi = (_Float16)ds;
+        const _Float16 lo = (_Float16)(ds - (float)hi);
+        ds2 = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
         dm = -(half_bits_to_float(ld_u16(blk + 2)) * (float)mm);
     }
     *reinterpret_cast<uint2*>(frag + gid * 8) = make_uint2(X0, X1);
-    if (x.h == 0) *reinterpret_cast<float2*>(scale + (x.tb * 32 + x.r) * 2) = make_float2(ds, dm);
+    if (x.h == 0) {
+        scale[x.n * KBp + x.b] = ds2;
+        mins[x.n * KBp + x.b] = dm;
+    }
 }
 
 __global__ __launch_bounds__(256) void repack_iq1t_kernel(
     const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
-    uint8_t* __restrict__ frag, uint16_t* __restrict__ scale) {
+    uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
@@ -144,10 +153,15 @@ __global__ __launch_bounds__(256) void repack_iq1t_kernel(
         meta = s | (sg0 << 3) | (sg1 << 4);
         d = ld_u16(blk + 74);
     }
-    uint8_t* f = frag + x.tb * 320;
-    *reinterpret_cast<uint32_t*>(f + x.L * 4) = C;
-    f[256 + x.L] = (uint8_t)meta;
-    if (x.h == 0) scale[x.tb * 32 + x.r] = d;
+    *reinterpret_cast<uint32_t*>(frag + gid * 4) = C;
+    // scale dword of (row, block): f16 d | meta0 << 16 | meta1 << 24 (meta_h from lane half h)
+    uint8_t* e = scale + (x.n * KBp + x.b) * 4;
+    if (x.h == 0) {
+        *reinterpret_cast<uint16_t*>(e) = d;
+        e[2] = (uint8_t)meta;
+    } else {
+        e[3] = (uint8_t)meta;
+    }
 }
 
 __global__ __launch_bounds__(256) void repack_i8_row_kernel(
@@ -178,19 +192,18 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const float* row_scale, i
     switch (t) {
         case MMQ_Q8_0:
             hipLaunchKernelGGL(repack_q8_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
-                               reinterpret_cast<uint16_t*>(scale));
+                               reinterpret_cast<uint32_t*>(scale));
             break;
         case MMQ_Q4_0:
             hipLaunchKernelGGL(repack_q4_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
-                               reinterpret_cast<uint16_t*>(scale));
+                               reinterpret_cast<uint32_t*>(scale));
             break;
         case MMQ_Q4_K:
             hipLaunchKernelGGL(repack_q4_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
-                               reinterpret_cast<float*>(scale));
+                               reinterpret_cast<uint32_t*>(scale), reinterpret_cast<float*>(base + L.min_off));
             break;
         case MMQ_IQ1T:
-            hipLaunchKernelGGL(repack_iq1t_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
-                               reinterpret_cast<uint16_t*>(scale));
+            hipLaunchKernelGGL(repack_iq1t_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag, scale);
             break;
         case MMQ_I8_ROW:
             hipLaunchKernelGGL(repack_i8_row_kernel, grid, block, 0, s, static_cast<const int8_t*>(raw),

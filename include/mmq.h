@@ -85,14 +85,16 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
  * Activation buffer ("act"). Opaque to most callers, but its layout is fixed so that other
  * producers can fill it. Let Mp = M rounded up to 32, KB = K/32, KBp = KB rounded up to 8.
  *
- * MMQ_ACT_Q8_1 (four regions, each starting on a 256-byte boundary):
+ * MMQ_ACT_Q8_1 (five regions, each starting on a 256-byte boundary):
  *   region 0  xq   int8, Mp*KBp*32 bytes, tiled for the matrix cores: the 32x32 tile
  *                  (row tile mt = m/32, block b) occupies bytes [(mt*KBp + b)*1024, +1024);
  *                  inside it, row r = m%32 and k' = k%32 sit at ((k'/16)*32 + r)*16 + k'%16.
- *   region 1  xs   f32 [Mp/32][KBp][32]: xs of (row mt*32+r, block b) at (mt*KBp + b)*32 + r.
- *   region 2  xsum int32, same indexing as xs.
- *   region 3  xs16 xs as f16 bits, same indexing as xs (xs is f16-exact by construction).
- *   Rows m >= M and blocks b >= KB hold zeros.
+ *   region 1  xs   f32 [Mp][KBp], row-major: xs of (row m, block b) at m*KBp + b.
+ *   region 2  xsum int32 [Mp][KBp], same indexing.
+ *   region 3  xs2  uint32 [Mp][KBp]: xs as f16 bits in both 16-bit halves (xs is f16-exact by
+ *                  construction); the operand form of the GEMM's scale outer product.
+ *   region 4  xsx  f32 [Mp][KBp]: xs * xsum (exact in f32), the operand of the q4_K min term.
+ *   Rows m >= M and blocks b >= KB hold zeros in every region.
  * MMQ_ACT_I8_TOKEN (two regions):
  *   region 0  a    int8 [M][K] row-major (row stride K).
  *   region 1  sa   f32 [M], starting at the first 256-byte boundary after region 0.
@@ -101,9 +103,9 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
 /* Total bytes of an act buffer; 0 if the arguments are invalid. (host only) */
 size_t mmq_act_bytes(mmq_atype a, int64_t M, int64_t K);
 
-/* Byte offsets of the act buffer's regions 0..3 (MMQ_ACT_I8_TOKEN: regions 0..1, the rest 0),
- * written to offsets[0..3] (host). Returns MMQ_EINVAL for invalid arguments. (host only) */
-mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[4]);
+/* Byte offsets of the act buffer's regions 0..4 (MMQ_ACT_I8_TOKEN: regions 0..1, the rest 0),
+ * written to offsets[0..4] (host). Returns MMQ_EINVAL for invalid arguments. (host only) */
+mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[5]);
 
 /* Quantise f32 activations x [M][ldx] (device, row stride ldx >= K floats) into `act`
  * (device, mmq_act_bytes(a, M, K) bytes). Deterministic and bit-exact with the definition

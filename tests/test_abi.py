@@ -49,14 +49,16 @@ def test_status_strings(mmq):
 def test_act_bytes_and_offsets(mmq):
     M, K = 70, 96                      # Mp = 96, KB = 3, KBp = 8
     o = mmq.act_region_offsets("q8_1", M, K)
+    cells = 96 * 8                     # (row, block) entries of a row-major scale region
     assert o[0] == 0
     assert o[1] == 3 * 8 * 1024        # xq region: MT * KBp * 1 KB
-    assert o[2] == o[1] + 3 * 8 * 128
-    assert o[3] == o[2] + 3 * 8 * 128
-    assert mmq.act_bytes("q8_1", M, K) == o[3] + 3 * 8 * 64   # xs16: 64 B per tile
+    assert o[2] == o[1] + 4 * cells    # xs f32
+    assert o[3] == o[2] + 4 * cells    # xsum int32
+    assert o[4] == o[3] + 4 * cells    # xs2 f16 pair
+    assert mmq.act_bytes("q8_1", M, K) == o[4] + 4 * cells   # xsx f32
     assert all(v % 256 == 0 for v in o)
     oi = mmq.act_region_offsets("i8_token", 3, 64)
-    assert oi == (0, 256, 0, 0)
+    assert oi == (0, 256, 0, 0, 0)
     assert mmq.act_bytes("i8_token", 3, 64) == 512
     assert mmq.act_bytes("q8_1", 4, 33) == 0         # K not a multiple of 32
     assert mmq.act_bytes("q8_1", 0, 64) == 0
@@ -64,9 +66,12 @@ def test_act_bytes_and_offsets(mmq):
 
 
 def test_packed_bytes(mmq):
-    # q4_0: NT=2, KBp=8 -> 2*8*512 B fragments + 2*8*32*2 B f16 scales
-    assert mmq.packed_bytes("q4_0", 40, 64) == 2 * 8 * 512 + 2 * 8 * 64
-    assert mmq.packed_bytes("q8_0", 32, 256) == 8 * 1024 + 8 * 64
+    # q4_0: NT=2 (Np=64), KBp=8 -> 2*8*512 B fragments + 64*8 scale dwords
+    assert mmq.packed_bytes("q4_0", 40, 64) == 2 * 8 * 512 + 64 * 8 * 4
+    assert mmq.packed_bytes("q8_0", 32, 256) == 8 * 1024 + 32 * 8 * 4
+    # q4_K: + a row-major f32 min region; iq1t: 256 B code fragments
+    assert mmq.packed_bytes("q4_K", 32, 256) == 8 * 512 + 2 * 32 * 8 * 4
+    assert mmq.packed_bytes("iq1t", 32, 256) == 8 * 256 + 32 * 8 * 4
     assert mmq.packed_bytes("i8_row", 33, 32) == 2 * 8 * 1024 + 256
     assert mmq.packed_bytes("q4_K", 32, 128) == 0      # Q4_K needs K % 256 == 0
     assert mmq.packed_bytes("iq1t", 32, 200) == 0
@@ -118,23 +123,29 @@ def test_gemm_id_validation(mmq):
 def test_act_to_host_layout_decoder(mmq):
     # build a q8_1 act image by hand from the header's formula and decode it back
     M, K = 40, 96
-    o0, o1, o2 = mmq.act_region_offsets("q8_1", M, K)[:3]
+    o = mmq.act_region_offsets("q8_1", M, K)
     Mp, KB, KBp = 64, 3, 8
     buf = np.zeros(mmq.act_bytes("q8_1", M, K), np.uint8)
     r = np.random.default_rng(0)
     xq = r.integers(-128, 128, (M, K)).astype(np.int8)
-    xs = r.random((M, KB)).astype(np.float32)
+    xs = r.random((M, KB)).astype(np.float16).astype(np.float32)
     xsum = r.integers(-4000, 4000, (M, KB)).astype(np.int32)
     for m in range(M):
         for k in range(K):
             mt, b, kk = m // 32, k // 32, k % 32
-            buf[o0 + (mt * KBp + b) * 1024 + ((kk // 16) * 32 + m % 32) * 16 + kk % 16] = xq[m, k].view(np.uint8)
+            buf[o[0] + (mt * KBp + b) * 1024 + ((kk // 16) * 32 + m % 32) * 16 + kk % 16] = xq[m, k].view(np.uint8)
         for b in range(KB):
-            idx = ((m // 32) * KBp + b) * 32 + m % 32
-            buf[o1 + 4 * idx:o1 + 4 * idx + 4] = np.frombuffer(xs[m, b].tobytes(), np.uint8)
-            buf[o2 + 4 * idx:o2 + 4 * idx + 4] = np.frombuffer(xsum[m, b].tobytes(), np.uint8)
+            idx = 4 * (m * KBp + b)
+            h = int(np.float16(xs[m, b]).view(np.uint16))
+            buf[o[1] + idx:o[1] + idx + 4] = np.frombuffer(xs[m, b].tobytes(), np.uint8)
+            buf[o[2] + idx:o[2] + idx + 4] = np.frombuffer(xsum[m, b].tobytes(), np.uint8)
+            buf[o[3] + idx:o[3] + idx + 4] = np.frombuffer(np.uint32(h | (h << 16)).tobytes(), np.uint8)
+            buf[o[4] + idx:o[4] + idx + 4] = np.frombuffer(np.float32(xs[m, b] * xsum[m, b]).tobytes(), np.uint8)
     a, s, u = mmq.act_to_host(buf, M, K)
     assert np.array_equal(a, xq) and np.array_equal(s, xs) and np.array_equal(u, xsum)
+    lo, hi, xsx = mmq.act_derived_host(buf, M, K)
+    assert np.array_equal(lo[:M, :KB], xs) and np.array_equal(hi[:M, :KB], xs)
+    assert np.array_equal(xsx[:M, :KB], xs * xsum)
     assert np.all(mmq.act_padding_host(buf, M, K) == 0)
 
 

@@ -69,10 +69,13 @@ def test_block_formats_quantize_partials_output(env, fmt, M, N, K):
     assert np.array_equal(xs.view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(xsum, rsum)
     assert np.all(mmq.act_padding_host(host, M, K) == 0)
-    xs16 = mmq.act_xs16_host(host, M, K)
-    full_s = np.zeros(xs16.shape, np.float32)
+    lo, hi, xsx = mmq.act_derived_host(host, M, K)
+    full_s = np.zeros(lo.shape, np.float32)
     full_s[:M, :K // 32] = rs
-    assert np.array_equal(xs16, full_s)
+    full_x = np.zeros(lo.shape, np.float32)
+    full_x[:M, :K // 32] = rs * rsum.astype(np.float32)
+    assert np.array_equal(lo, full_s) and np.array_equal(hi, full_s)
+    assert np.array_equal(xsx, full_x)
     parts = mmq.gemm(fmt, packed, act, M, N, K, "i32_partials")
     torch.cuda.synchronize()
     assert np.array_equal(parts.cpu().numpy(), orc.partials(fmt, raw, N, K, rq))
