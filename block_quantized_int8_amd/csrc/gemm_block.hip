@@ -172,9 +172,13 @@ enum Mode { DENSE_F32 = 0, DENSE_PARTIALS = 1, GATHER_F32 = 2 };
 
 // WN x WM waves, each owning RT weight tiles x CT token tiles of 32 x 32.
 // LDS stage layout (bytes): weight fragments [TN][KS][FB] | token fragments [TM][KS][1024] |
-// weight scale dwords [TN][32][KS] | token scale dwords [TM][32][KS] | (q4_K) weight mins,
-// token xs*xsum [..][32][KS] | padding chunks. Every region is loaded in whole 1 KB chunks (one
-// wave-wide 16-byte DMA each); scale regions hold two tiles per chunk.
+// weight scale dwords | token scale dwords | (q4_K) weight mins | token xs*xsum | padding.
+// Fragments arrive in 1 KB chunks (one wave-wide 16-byte DMA each). Scale regions arrive as one
+// 4-byte-per-lane DMA per (pair of 32-row tiles, block), so they sit block-major,
+// [tile pair][KS][64 rows] dwords, and the per-block reads of 32 consecutive rows are free of
+// bank conflicts; each lane names its own row, which also gathers MUL_MAT_ID rows.
+// Chunk c goes to wave c % NW; every chunk type's count is a multiple of NW, so the type of a
+// wave's j-th chunk is known at compile time.
 template <mmq_wtype FMT, int WN, int WM, int RT, int CT>
 struct Cfg {
     using T = BT<FMT>;
@@ -182,18 +186,31 @@ struct Cfg {
     static constexpr int TN = WN * RT, TM = WM * CT;
     static constexpr int WF = TN * KS * T::FB;
     static constexpr int XF = TM * KS * 1024;
-    static constexpr int SCW = ((TN + 1) / 2) * 1024;
-    static constexpr int SCX = ((TM + 1) / 2) * 1024;
-    static constexpr int MNW = T::MIN ? SCW : 0;
-    static constexpr int MNX = T::MIN ? SCX : 0;
-    static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + SCW;
-    static constexpr int O_WM = O_XS + SCX, O_XM = O_WM + MNW, O_PAD = O_XM + MNX;
-    static constexpr int C_WF = WF / 1024, C_XF = TM * KS, C_WS = SCW / 1024, C_XS = SCX / 1024;
-    static constexpr int C_WM = MNW / 1024, C_XM = MNX / 1024;
+    static constexpr int C_WF = WF / 1024, C_XF = TM * KS;
+    static constexpr int C_WS = (TN + 1) / 2 * KS, C_XS = (TM + 1) / 2 * KS;
+    static constexpr int C_WM = T::MIN ? C_WS : 0, C_XM = T::MIN ? C_XS : 0;
+    static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + C_WS * 256;
+    static constexpr int O_WM = O_XS + C_XS * 256, O_XM = O_WM + C_WM * 256;
+    static constexpr int BUF = O_XM + C_XM * 256;
     static constexpr int C_ALL = C_WF + C_XF + C_WS + C_XS + C_WM + C_XM;
-    static constexpr int CPW = (C_ALL + NW - 1) / NW;          // chunks per wave per stage
-    static constexpr int BUF = O_PAD + (CPW * NW - C_ALL) * 1024;
+    static constexpr int CPW = C_ALL / NW;                     // chunks per wave per stage
     static_assert(WF % 1024 == 0, "weight fragments of a stage must be whole 1 KB chunks");
+    static_assert(C_WF % NW == 0 && C_XF % NW == 0 && C_WS % NW == 0 && C_XS % NW == 0,
+                  "every chunk type must split evenly over the waves");
+    // chunk types
+    enum { K_WF = 0, K_XF = 1, K_WS = 2, K_XS = 3, K_WM = 4, K_XM = 5 };
+    __host__ __device__ static constexpr int kind(int c) {
+        return c < C_WF ? K_WF : (c -= C_WF) < C_XF ? K_XF : (c -= C_XF) < C_WS ? K_WS
+             : (c -= C_WS) < C_XS ? K_XS : (c -= C_XS) < C_WM ? K_WM : K_XM;
+    }
+    __host__ __device__ static constexpr int first(int k) {
+        return k == K_WF ? 0 : k == K_XF ? C_WF : k == K_WS ? C_WF + C_XF : k == K_XS ? C_WF + C_XF + C_WS
+             : k == K_WM ? C_WF + C_XF + C_WS + C_XS : C_WF + C_XF + C_WS + C_XS + C_WM;
+    }
+    // LDS byte offset of the scale dword of (tile i, row r, block kb) in a region at `base`
+    __host__ __device__ static constexpr int sc(int base, int i, int r, int kb) {
+        return base + (((i >> 1) * KS + kb) * 64 + (i & 1) * 32 + r) * 4;
+    }
 };
 
 struct BlockArgs {
@@ -221,6 +238,10 @@ typedef __attribute__((address_space(3))) void lmem_t;
 // One wave-wide 16-byte-per-lane DMA: lane l's 16 source bytes land at lds + 16 l.
 __device__ inline void dma16(const uint8_t* src, uint8_t* lds) {
     __builtin_amdgcn_global_load_lds((gmem_t*)src, (lmem_t*)lds, 16, 0, 0);
+}
+// The same with 4 bytes per lane: lane l's dword lands at lds + 4 l.
+__device__ inline void dma4(const uint8_t* src, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds((gmem_t*)src, (lmem_t*)lds, 4, 0, 0);
 }
 
 // an f16x4 operand with the dword `lo` in slots 0-1 and zeros in slots 2-3
@@ -285,76 +306,60 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         if (tid < 128) reinterpret_cast<uint32_t*>(tab)[tid] = T::table_word(tid >> 2, tid & 3);
     }
 
-    // ---- DMA plan: chunk c of a stage belongs to wave c % NW; per chunk this lane keeps a
-    // 32-bit source offset from the chunk's (wave-uniform) region base, advanced by a fixed
-    // stride per stage, and the chunk's LDS offset.
-    const uint8_t* gbase[C::CPW];
+    // ---- DMA plan: per chunk this lane keeps a 32-bit source offset from the chunk's region
+    // base, advanced by a fixed stride per stage; the chunk's LDS offset is wave-uniform.
     uint32_t goff[C::CPW];
-    int gadv[C::CPW], ldso[C::CPW];
-    {
-        const uint8_t* wfrag = wbase;
-        const uint8_t* wsc = wbase + args.w_scale_off;
-        const uint8_t* wmn = wbase + args.w_min_off;
+    int ldso[C::CPW];
+    const uint8_t* const wsc = wbase + args.w_scale_off;
+    const uint8_t* const wmn = wbase + args.w_min_off;
+    auto chunk_base = [&](int k) __attribute__((always_inline)) -> const uint8_t* {
+        return k == C::K_WF ? wbase : k == C::K_XF ? args.xq : k == C::K_WS ? wsc
+             : k == C::K_XS ? reinterpret_cast<const uint8_t*>(args.xs2)
+             : k == C::K_WM ? wmn : reinterpret_cast<const uint8_t*>(args.xsx);
+    };
+    auto chunk_adv = [&](int k) __attribute__((always_inline)) -> int {
+        return k == C::K_WF ? KS * T::FB : k == C::K_XF ? KS * 1024 : KS * 4;
+    };
 #pragma unroll
-        for (int j = 0; j < C::CPW; ++j) {
-            int c = wave + j * C::NW;
-            const int h = lane >> 5;
-            if (c < C::C_WF) {
-                const int byte = c * 1024 + lane * 16;
-                const int tile = byte / (KS * T::FB), off = byte % (KS * T::FB);
-                const int nt = min(nt_base + tile, NT - 1);
-                gbase[j] = wfrag;
-                goff[j] = (uint32_t)(nt * KBp * T::FB + off);
-                gadv[j] = KS * T::FB;
-                ldso[j] = c * 1024;
-            } else if ((c -= C::C_WF) < C::C_XF) {
-                const int jt = c / KS, q = c % KS;
-                const int t = src_token(jt, r32);
-                gbase[j] = args.xq;
-                goff[j] = (uint32_t)((((t >> 5) * KBp + q) * 64 + h * 32 + (t & 31)) * 16);
-                gadv[j] = KS * 1024;
-                ldso[j] = C::O_XF + c * 1024;
-            } else if ((c -= C::C_XF) < C::C_WS) {
-                const int n = min((nt_base + 2 * c + h) * 32 + r32, Np - 1);
-                gbase[j] = wsc;
-                goff[j] = (uint32_t)(n * KBp * 4);
-                gadv[j] = KS * 4;
-                ldso[j] = C::O_WS + c * 1024;
-            } else if ((c -= C::C_WS) < C::C_XS) {
-                const int jt = 2 * c + h;
-                const int t = jt < C::TM ? src_token(jt, r32) : 0;
-                gbase[j] = reinterpret_cast<const uint8_t*>(args.xs2);
-                goff[j] = (uint32_t)(t * KBp * 4);
-                gadv[j] = KS * 4;
-                ldso[j] = C::O_XS + c * 1024;
-            } else if ((c -= C::C_XS) < C::C_WM) {
-                const int n = min((nt_base + 2 * c + h) * 32 + r32, Np - 1);
-                gbase[j] = wmn;
-                goff[j] = (uint32_t)(n * KBp * 4);
-                gadv[j] = KS * 4;
-                ldso[j] = C::O_WM + c * 1024;
-            } else if ((c -= C::C_WM) < C::C_XM) {
-                const int jt = 2 * c + h;
-                const int t = jt < C::TM ? src_token(jt, r32) : 0;
-                gbase[j] = reinterpret_cast<const uint8_t*>(args.xsx);
-                goff[j] = (uint32_t)(t * KBp * 4);
-                gadv[j] = KS * 4;
-                ldso[j] = C::O_XM + c * 1024;
-            } else {                                        // padding chunk: any valid source
-                c -= C::C_XM;
-                gbase[j] = wfrag;
-                goff[j] = (uint32_t)(lane * 16);
-                gadv[j] = 0;
-                ldso[j] = C::O_PAD + c * 1024;
+    for (int j = 0; j < C::CPW; ++j) {
+        const int k = C::kind(j * C::NW);                    // compile-time per j
+        const int c = j * C::NW + wave - C::first(k);         // index within its type
+        const int h = lane >> 5;
+        if (k == C::K_WF) {
+            const int byte = c * 1024 + lane * 16;
+            const int tile = byte / (KS * T::FB), off = byte % (KS * T::FB);
+            const int nt = min(nt_base + tile, NT - 1);
+            goff[j] = (uint32_t)(nt * KBp * T::FB + off);
+            ldso[j] = c * 1024;
+        } else if (k == C::K_XF) {
+            const int jt = c / KS, q = c % KS;
+            const int t = src_token(jt, r32);
+            goff[j] = (uint32_t)((((t >> 5) * KBp + q) * 64 + h * 32 + (t & 31)) * 16);
+            ldso[j] = C::O_XF + c * 1024;
+        } else {
+            // scale-type chunk: (tile pair, block) -> 64 rows x one dword
+            const int pr = c / KS, q = c % KS, tile = 2 * pr + h;
+            int row;
+            if (k == C::K_WS || k == C::K_WM) {
+                row = min((nt_base + tile) * 32 + r32, Np - 1);
+            } else {
+                row = tile < C::TM ? src_token(tile, r32) : 0;
             }
+            goff[j] = (uint32_t)((row * KBp + q) * 4);
+            const int base = k == C::K_WS ? C::O_WS : k == C::K_XS ? C::O_XS : k == C::K_WM ? C::O_WM : C::O_XM;
+            ldso[j] = base + c * 256;
         }
     }
+    auto issue_chunk = [&](uint8_t* buf, int j) __attribute__((always_inline)) {
+        const int k = C::kind(j * C::NW);
+        uint8_t* dst = buf + __builtin_amdgcn_readfirstlane(ldso[j]);
+        if (k == C::K_WF || k == C::K_XF) dma16(chunk_base(k) + goff[j], dst);
+        else dma4(chunk_base(k) + goff[j], dst);
+        goff[j] += chunk_adv(k);
+    };
     auto issue_stage = [&](uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < C::CPW; ++j) {
-            dma16(gbase[j] + goff[j], buf + __builtin_amdgcn_readfirstlane(ldso[j]));
-            goff[j] += gadv[j];
-        }
+        for (int j = 0; j < C::CPW; ++j) issue_chunk(buf, j);
     };
 
     v16f acc[RT][CT];
@@ -387,14 +392,14 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int i = wn * RT + rt;
-            R.wsd[rt] = *reinterpret_cast<const uint32_t*>(cur + C::O_WS + ((i * 32 + r32) * KS + kb) * 4);
+            R.wsd[rt] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_WS, i, r32, kb));
             T::fetch(cur + (i * KS + kb) * T::FB, lane, R.w[rt]);
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int j = wm * CT + ct;
             R.b[ct] = *reinterpret_cast<const v4i*>(cur + C::O_XF + (j * KS + kb) * 1024 + lane * 16);
-            R.xs[ct] = *reinterpret_cast<const uint32_t*>(cur + C::O_XS + ((j * 32 + r32) * KS + kb) * 4);
+            R.xs[ct] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_XS, j, r32, kb));
         }
     };
     auto mid = [&](Raw& R) __attribute__((always_inline)) {
@@ -468,10 +473,10 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
             float wv[RT], xv[CT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-                wv[rt] = *reinterpret_cast<const float*>(cur + C::O_WM + (((wn * RT + rt) * 32 + r32) * KS + kb) * 4);
+                wv[rt] = *reinterpret_cast<const float*>(cur + C::sc(C::O_WM, wn * RT + rt, r32, kb));
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)      // * 2^-25, like S = 2 wd xs times D - c = P 2^-26
-                xv[ct] = (2.0f / UNBIAS) * *reinterpret_cast<const float*>(cur + C::O_XM + (((wm * CT + ct) * 32 + r32) * KS + kb) * 4);
+                xv[ct] = (2.0f / UNBIAS) * *reinterpret_cast<const float*>(cur + C::sc(C::O_XM, wm * CT + ct, r32, kb));
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -484,7 +489,9 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     // work of step i+1 (dots, scale, conversion) around the vector FMAs of step i, so the
     // matrix core and the vector unit stay busy together. The next block's operands are read
     // from LDS at its first step and unpacked at its last.
-    auto run_stage = [&](const uint8_t* cur, int s) __attribute__((always_inline)) {
+    // `nxt` (if not null) receives the DMA of the following stage: its chunks are issued one per
+    // step over the first steps, so the vector-memory issue never holds a wave for long.
+    auto run_stage = [&](const uint8_t* cur, int s, uint8_t* nxt) __attribute__((always_inline)) {
         Ops op[2];
         Raw raw;
         load_ops(cur, 0, op[0]);
@@ -499,6 +506,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
             for (int t = 0; t < NT_; ++t) {
                 const bool more = t + 1 < NT_ || kb + 1 < KS;
                 const int kn = (t + 1 < NT_) ? kb : kb + 1, tn = (t + 1) % NT_;
+                if (nxt != nullptr && kb * NT_ + t < C::CPW) issue_chunk(nxt, kb * NT_ + t);
                 if (kb + 1 < KS) {
                     if (t == 0) fetch(cur, kb + 1, raw);
                     if (t == (NT_ >= 3 ? NT_ - 2 : 0)) mid(raw);
@@ -542,12 +550,10 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     for (int s = 0; s < nstages; s += 2) {
         __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0): this wave's DMA of stage s landed
         __syncthreads();                          // ... and everyone's; stage s-1 fully consumed
-        issue_stage(buf1);
-        run_stage(buf0, s);
+        run_stage(buf0, s, buf1);                 // stage s+1 streams into buf1 meanwhile
         __builtin_amdgcn_s_waitcnt(0x3f70);
         __syncthreads();
-        if (s + 2 < nstages) issue_stage(buf0);
-        run_stage(buf1, s + 1);
+        run_stage(buf1, s + 1, s + 2 < nstages ? buf0 : nullptr);
     }
 
     if constexpr (MODE != DENSE_PARTIALS) {
