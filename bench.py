@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9   # non-packed f32 vector lane-ops per second
 HEADLINE = "cfg2a_q4_0"
 METRIC = "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MFMA peak"
 
@@ -253,6 +254,13 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4)}
+    if fmt != "i8_row":
+        # the per-block scale application: >= 2 vector ops (exact conversion + FMA) per
+        # element-block E = rows * N * K/32, against 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+        rows = M * cfg.get("top_k", 1)
+        E = rows * N * (K // 32)
+        roof["valu_ceiling"] = {"ops_per_element_block": 2, "peak_lane_ops": VALU_PEAK_LANE_OPS,
+                                "frac": round(2.0 * E / k_s / VALU_PEAK_LANE_OPS, 4)}
     roof["traffic"] = MEASURED_TRAFFIC_BYTES.get(name)
     roof["kernel"] = kernel_names[dom]
     roof["kernel_us"] = round(k_s * 1e6, 2)
