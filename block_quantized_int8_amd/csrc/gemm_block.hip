@@ -12,15 +12,16 @@
 //     c + P * 2^-26 exactly (|P| <= 548640 for every format).
 //  2. v_mfma_f32_32x32x8_f16 forms the scale outer product S = wd (x) xs from one f16 per row on
 //     each side (both half-waves contribute, so S = 2 wd xs; a product of two f16 is exact).
-//  3. acc += (D - c) * S: one exact subtraction and one FMA per element on the known 32x32 lane
-//     map, in registers - no store -> sync -> reload of the accumulator per block (the pages'
-//     "wall", Hanzo paper sections 2-3; the fix is a manual MMA with a known lane map, section 4).
-//     The 2^26 goes into the epilogue's power-of-two scale.
-// Measured on gfx950: v_cvt_f32_i32 issues at about half the rate of v_sub_f32, and a
-// matrix-core op that reads a 16-register C operand from VGPRs costs the vector unit about 19
-// cycles, so the conversion is the subtraction above rather than a convert or a third MFMA.
-// The vector unit has no packed-f32 path here: the 32 vector ops per tile and block are the
-// binding cost, and the two MFMAs (64 cycles) hide behind them.
+//  3. X = D - c = P * 2^-26 exactly, on the matrix core: v_mfma_f32_32x32x8_f16 with C = D and
+//     A*B = -c (see unbias_m). Then acc += X * S - one FMA per element on the known 32x32 lane
+//     map, in registers: no store -> sync -> reload of the accumulator per block (the pages'
+//     "wall", Hanzo paper sections 2-3; the fix is a manual MMA with a known lane map, section
+//     4). The 2^26 goes into the epilogue's power-of-two scale.
+// Measured on gfx950: a non-packed f32 vector op costs 4 cycles per wave64, v_cvt_f32_i32 about
+// twice that, and a matrix-core op that reads a 16-register C operand from VGPRs costs the vector
+// unit about 19 cycles. Per tile and block the matrix-core conversion (32 MFMA cycles + one such
+// read) beats 16 vector subtractions (64 cycles); packed f32 is not used. The XM switch keeps the
+// vector-subtraction form (X = D - c, 16 v_sub) for comparison.
 //
 //   q4_K: S = xs * (d*sc) from the exact f16 split d*sc = hi + lo (slots 0 and 1 against xs in
 //     both), and the rank-1 min term -(dmin*m) * (xs*xsum) (minfer R1 section 2.2: sum w*q =
@@ -250,7 +251,7 @@ __device__ inline h4 as_h4(uint32_t lo) {
     return __builtin_bit_cast(h4, t);
 }
 
-template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int MODE>
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int MODE, bool XM>
 __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs args) {
     using C = Cfg<FMT, WN, WM, RT, CT>;
     using T = typename C::T;
@@ -439,6 +440,16 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     // The empty asm after a tile's last FMA pins its accumulator: FMAs are pure, and left alone
     // the compiler sinks a whole stage of them below its matrix-core work, which then has to
     // hold every X and S at once.
+    // Conversion on the matrix core (XM): v_mfma_f32_32x32x8_f16 with C = D and A*B = -c, c
+    // written as three exact f16 products (its 24-bit significand 0xA2F983 byte by byte, each
+    // byte * 2^-13 against 8, 2^-5 and 2^-13, low half-wave only): X = D - c exactly, whatever
+    // order the matrix core adds in.
+    const v2i cAi = {lane < 32 ? (int)0xA7C8A510u : 0, lane < 32 ? (int)0x0000A418u : 0};
+    const v2i cBi = {(int)0x28004800u, (int)0x00000800u};
+    auto unbias_m = [&](const v16i& D) __attribute__((always_inline)) -> v16f {
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, cAi), __builtin_bit_cast(h4, cBi),
+                                                    __builtin_bit_cast(v16f, D), 0, 0, 0);
+    };
     // D -> X = D - c, in place: 16 independent subtractions. (The whole vector is
     // reinterpreted at once: hipcc's __builtin_bit_cast of a single vector element reads element
     // 0 whatever the index.)
@@ -448,11 +459,11 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     // acc += X * S: 16 independent FMAs. The empty asm after them pins the accumulator: FMAs are
     // pure, and left alone the compiler sinks a whole stage of them below its matrix-core work,
     // which then has to hold every D and S at once.
-    auto fma_tile = [&](int t, const v16f& X, const v16f& S) __attribute__((always_inline)) {
+    auto fma_tile = [&](int t, const v16f& X, const v16f& S, int r0 = 0, int r1 = 16) __attribute__((always_inline)) {
         const int rt = t / CT, ct = t % CT;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[rt][ct][r] = __builtin_fmaf(X[r], S[r], acc[rt][ct][r]);
-        asm volatile("" : "+v"(acc[rt][ct]));
+        for (int r = r0; r < r1; ++r) acc[rt][ct][r] = __builtin_fmaf(X[r], S[r], acc[rt][ct][r]);
+        if (r1 == 16) asm volatile("" : "+v"(acc[rt][ct]));
     };
     // partials mode: the exact int32 dots of block kbg go straight to memory
     auto store_partials = [&](int kbg, int t, const v16i& D) __attribute__((always_inline)) {
@@ -496,10 +507,11 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         Raw raw;
         load_ops(cur, 0, op[0]);
         v16i Dc;
-        v16f Sc;
+        v16f Sc, Xc;
         Dc = mfma_dots(op[0], 0);
         if constexpr (MODE == DENSE_PARTIALS) store_partials(s * KS, 0, Dc);
         else Sc = mfma_scale(op[0], 0);
+        if constexpr (XM && MODE != DENSE_PARTIALS) Xc = unbias_m(Dc);
 #pragma unroll
         for (int kb = 0; kb < KS; ++kb) {
 #pragma unroll
@@ -517,26 +529,47 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
                 } else {
                     v16i Dn;
                     v16f Sn;
-                    // Two fenced halves per step, each a matrix-core op over a run of independent
-                    // vector ops of the previous tile: the int8 MFMA of the next tile with this
-                    // tile's 16 subtractions, then the scale MFMA with its 16 FMAs. (Unfenced, the
-                    // scheduler threads subtractions and FMAs into one dependent chain through a
-                    // single temporary.)
-                    __builtin_amdgcn_sched_barrier(0);
-                    const v16f X = unbias(Dc);
-                    if (more) {
-                        Dn = mfma_dots(op[kn & 1], tn);
-                        __builtin_amdgcn_sched_group_barrier(0x008, T::NMF, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                    if constexpr (XM) {
+                        // Three fenced thirds per step: each matrix-core op of the next tile (dots,
+                        // scale, conversion) over a run of this tile's FMAs (X came from the matrix
+                        // core one step ago).
+                        v16f Xn;
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (more) {
+                            Dn = mfma_dots(op[kn & 1], tn);
+                            __builtin_amdgcn_sched_group_barrier(0x008, T::NMF, 0);
+                        }
+                        fma_tile(t, Xc, Sc, 0, 6);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (more) Sn = mfma_scale(op[kn & 1], tn);
+                        fma_tile(t, Xc, Sc, 6, 11);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (more) Xn = unbias_m(Dn);
+                        fma_tile(t, Xc, Sc, 11, 16);
+                        __builtin_amdgcn_sched_barrier(0);
+                        Xc = Xn;
+                    } else {
+                        // Two fenced halves per step, each a matrix-core op over a run of
+                        // independent vector ops of the previous tile: the int8 MFMA of the next
+                        // tile with this tile's 16 subtractions, then the scale MFMA with its 16
+                        // FMAs. (Unfenced, the scheduler threads subtractions and FMAs into one
+                        // dependent chain through a single temporary.)
+                        __builtin_amdgcn_sched_barrier(0);
+                        const v16f X = unbias(Dc);
+                        if (more) {
+                            Dn = mfma_dots(op[kn & 1], tn);
+                            __builtin_amdgcn_sched_group_barrier(0x008, T::NMF, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        fma_tile(t, X, Sc);
+                        if (more) {
+                            Sn = mfma_scale(op[kn & 1], tn);
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                    fma_tile(t, X, Sc);
-                    if (more) {
-                        Sn = mfma_scale(op[kn & 1], tn);
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
                     if (T::MIN && t == NT_ - 1 && (kb & 1)) min_term(cur, kb >> 1);
                     Dc = Dn;
                     Sc = Sn;
@@ -594,6 +627,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 // Tile configuration: 2 x 2 waves, each owning 2 weight tiles x 2 token tiles -> 128 x 128
 // CTA tiles.
 constexpr int WN_ = 2, WM_ = 2, RT_ = 2, CT_ = 2;
+constexpr bool XM_ = true;        // conversion on the matrix core (see the kernel notes)
 
 template <mmq_wtype FMT>
 BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, int64_t K) {
@@ -628,10 +662,10 @@ hipError_t launch_dense(const void* packed, const void* act, int64_t M, int64_t 
     const dim3 grid((unsigned)((int64_t)tiles_n * tiles_m)), block(WN_ * WM_ * 64);
     if (o == MMQ_OUT_I32_PARTIALS) {
         g.partials = static_cast<int32_t*>(out);
-        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_PARTIALS>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_PARTIALS, XM_>), grid, block, 0, s, g);
     } else {
         g.out = static_cast<float*>(out);
-        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_F32>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_F32, XM_>), grid, block, 0, s, g);
     }
     return hipGetLastError();
 }
@@ -652,7 +686,7 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
     g.ldo = N;
     const int64_t nblk = round_up(max_units, 8) * g.ntiles_n;
     const dim3 grid((unsigned)nblk), block(WN_ * WM_ * 64);
-    hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, GATHER_F32>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, GATHER_F32, XM_>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 

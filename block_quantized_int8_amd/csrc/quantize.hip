@@ -7,18 +7,19 @@
 // -fhip-fp32-correctly-rounded-divide-sqrt) and nothing is contracted, so the result is
 // bit-identical to the definition.
 //
-// Work split: one wave per (32-row tile, group of 8 blocks). Lane L = h*32 + r owns row r's
-// values 16h..16h+15 of each block - exactly the 16 bytes it writes to the tiled xq layout, so
-// every block's 1 KB tile is one contiguous wave store. The two lanes of a block (r and r+32)
-// combine their half-block max and sum with one cross-half exchange. Each row's 8 scale entries
-// per region are contiguous (row-major regions): lane h = 0 writes xs and xsum, lane h = 1 the
-// derived xs2 (f16 pair) and xsx = xs * xsum (exact in f32: an 11-bit significand times a
-// |sum| <= 32*128).
+// Work split: one wave per (32-row tile, pair of blocks). Lane L = h*32 + r owns row r's values
+// 16h..16h+15 of each block - exactly the 16 bytes it writes to the tiled xq layout, so every
+// block's 1 KB tile is one contiguous wave store. The two lanes of a block (r and r+32) combine
+// their half-block max and sum with one cross-half exchange. Each row's two scale entries per
+// region are one 8-byte store (row-major regions): lane h = 0 writes xs and xsum, lane h = 1
+// the derived xs2 (f16 pair) and xsx = xs * xsum (exact in f32: an 11-bit significand times a
+// |sum| <= 32*128). Small units keep several waves per SIMD in flight, so one wave's loads
+// overlap another's arithmetic.
 #include "mmq_internal.h"
 
 namespace {
 
-constexpr int QG = 8;             // blocks per wave (one 32-row tile x 256 values)
+constexpr int QG = 2;             // blocks per wave (one 32-row tile x 64 values)
 constexpr int QWAVES = 4;         // waves per workgroup
 
 __device__ inline uint32_t pack4(int a, int b, int c, int d) {
@@ -83,10 +84,8 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
 
     const int64_t row = (mt * 32 + r) * KBp + kb0;
     if (h == 0) {
-        *reinterpret_cast<float4*>(xs + row) = make_float4(s_xs[0], s_xs[1], s_xs[2], s_xs[3]);
-        *reinterpret_cast<float4*>(xs + row + 4) = make_float4(s_xs[4], s_xs[5], s_xs[6], s_xs[7]);
-        *reinterpret_cast<int4*>(xsum + row) = make_int4(s_sum[0], s_sum[1], s_sum[2], s_sum[3]);
-        *reinterpret_cast<int4*>(xsum + row + 4) = make_int4(s_sum[4], s_sum[5], s_sum[6], s_sum[7]);
+        *reinterpret_cast<float2*>(xs + row) = make_float2(s_xs[0], s_xs[1]);
+        *reinterpret_cast<int2*>(xsum + row) = make_int2(s_sum[0], s_sum[1]);
     } else {
         uint32_t p2[QG];
         float px[QG];
@@ -96,10 +95,8 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
             p2[i] = b | (b << 16);
             px[i] = s_xs[i] * (float)s_sum[i];
         }
-        *reinterpret_cast<uint4*>(xs2 + row) = make_uint4(p2[0], p2[1], p2[2], p2[3]);
-        *reinterpret_cast<uint4*>(xs2 + row + 4) = make_uint4(p2[4], p2[5], p2[6], p2[7]);
-        *reinterpret_cast<float4*>(xsx + row) = make_float4(px[0], px[1], px[2], px[3]);
-        *reinterpret_cast<float4*>(xsx + row + 4) = make_float4(px[4], px[5], px[6], px[7]);
+        *reinterpret_cast<uint2*>(xs2 + row) = make_uint2(p2[0], p2[1]);
+        *reinterpret_cast<float2*>(xsx + row) = make_float2(px[0], px[1]);
     }
 }
 
