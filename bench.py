@@ -153,12 +153,7 @@ def main():
         w, sw = gen.i8_rows(N, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_WEIGHT)
         packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
                                     row_scale=torch.from_numpy(sw).to(dev))
-        ab = mmq.act_bytes("i8_token", M, K)
-        o0, o1 = mmq.act_region_offsets("i8_token", M, K)[:2]
-        act_h = np.zeros(ab, np.uint8)
-        act_h[o0:o0 + M * K] = a.view(np.uint8).ravel()
-        act_h[o1:o1 + 4 * M] = sa.view(np.uint8)
-        act = torch.from_numpy(act_h).to(dev)
+        act = torch.from_numpy(mmq.act_i8_pack_host(a, sa)).to(dev)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
         def step(ev):

@@ -9,7 +9,9 @@ The functions mirror include/mmq.h one to one (same names without the `mmq_` pre
     act_bytes, act_region_offsets, quantize_act, packed_bytes, repack_weights, gemm,
     gemm_id_workspace_bytes, gemm_id, status_string
 
-plus `act_to_host`, a host-side decoder of the documented q8_1 act layout used by tests.
+plus host-side encoders/decoders of the documented act layouts (`act_to_host` and friends for
+q8_1, `act_i8_pack_host` / `act_i8_to_host` for the per-token int8 form), used by tests and the
+bench to fill or read act buffers.
 """
 from __future__ import annotations
 
@@ -240,3 +242,35 @@ def act_padding_host(act_bytes_host: np.ndarray, M: int, K: int):
     for r in (xs, xsum, xs2, xsx):
         pads += [r[M:].ravel(), r[:, KB:].ravel()]
     return np.concatenate([p.astype(np.float64) for p in pads])
+
+
+def act_i8_pack_host(a: np.ndarray, sa: np.ndarray) -> np.ndarray:
+    """Encode int8 activations a [M, K] and per-token scales sa [M] into the documented
+    MMQ_ACT_I8_TOKEN layout (uint8 buffer of act_bytes("i8_token", M, K) bytes)."""
+    a = np.asarray(a, dtype=np.int8)
+    M, K = a.shape
+    o = act_region_offsets("i8_token", M, K)
+    Mp, KB, KBp, MT = _act_dims(M, K)
+    buf = np.zeros(act_bytes("i8_token", M, K), np.uint8)
+    full = np.zeros((Mp, KBp * 32), np.int8)
+    full[:M, :K] = a
+    t = full.reshape(MT, 32, KBp, 2, 16).transpose(0, 2, 3, 1, 4)          # [mt, b, h, r, 16]
+    buf[o[0]:o[0] + MT * KBp * 1024] = t.reshape(-1).view(np.uint8)
+    sp = np.zeros(Mp, np.float32)
+    sp[:M] = np.asarray(sa, dtype=np.float32)
+    buf[o[1]:o[1] + 4 * Mp] = sp.view(np.uint8)
+    return buf
+
+
+def act_i8_to_host(act_bytes_host: np.ndarray, M: int, K: int, padded: bool = False):
+    """Decode an MMQ_ACT_I8_TOKEN buffer (copied to host as uint8) into (a int8 [M, K],
+    sa f32 [M]), or with padded=True into ([Mp, KBp*32], [Mp]) including the zero padding."""
+    o = act_region_offsets("i8_token", M, K)
+    Mp, KB, KBp, MT = _act_dims(M, K)
+    buf = np.asarray(act_bytes_host, dtype=np.uint8)
+    t = buf[o[0]:o[0] + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)
+    full = t.transpose(0, 3, 1, 2, 4).reshape(Mp, KBp * 32)
+    sa = buf[o[1]:o[1] + 4 * Mp].view(np.float32)
+    if padded:
+        return full.copy(), sa.copy()
+    return np.ascontiguousarray(full[:M, :K]), sa[:M].copy()

@@ -49,16 +49,24 @@ inline ActQ81Layout act_q8_1_layout(int64_t M, int64_t K) {
     return L;
 }
 
-// MMQ_ACT_I8_TOKEN: a int8 [M][K] row-major, sa f32 [M].
+// MMQ_ACT_I8_TOKEN (see mmq.h):
+//   region 0 a    int8, tiled [Mp/32][KBp][64 lanes][16 B] exactly like the q8_1 xq region
+//   region 1 sa   f32 [Mp], the per-token scale
+// The tiled order lets the GEMM stage 1 KB of whole cache lines per (row tile, block).
 struct ActI8Layout {
+    int64_t Mp, MT, KB, KBp;
     int64_t a_off, sa_off, bytes;
 };
 
 inline ActI8Layout act_i8_layout(int64_t M, int64_t K) {
     ActI8Layout L;
+    L.Mp = round_up(M, TILE);
+    L.MT = L.Mp / TILE;
+    L.KB = K / QK;
+    L.KBp = round_up(L.KB, KB_ALIGN);
     L.a_off = 0;
-    L.sa_off = round_up(M * K, REGION_ALIGN);
-    L.bytes = L.sa_off + round_up(M * 4, REGION_ALIGN);
+    L.sa_off = round_up(L.MT * L.KBp * 1024, REGION_ALIGN);
+    L.bytes = L.sa_off + round_up(L.Mp * 4, REGION_ALIGN);
     return L;
 }
 

@@ -15,6 +15,8 @@
 // the derived xs2 (f16 pair) and xsx = xs * xsum (exact in f32: an 11-bit significand times a
 // |sum| <= 32*128). Small units keep several waves per SIMD in flight, so one wave's loads
 // overlap another's arithmetic.
+#include <algorithm>
+
 #include "mmq_internal.h"
 
 namespace {
@@ -100,32 +102,46 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
     }
 }
 
-// Per-token int8: one CTA per row; amax over the whole row, then q = rint(x * (1/d)),
-// scale kept in f32 (metainfer "INT8 W8A8 GEMM - Prefill", section 1 operator contract).
+// Per-token int8: one CTA per row (grid-stride over the Mp rows); amax over the whole row,
+// then q = rint(x * (1/d)), scale kept in f32 (metainfer "INT8 W8A8 GEMM - Prefill", section
+// 1 operator contract). The values go to the tiled layout (4 bytes per thread inside one
+// lane's 16-byte run); rows m >= M and blocks past K/32 are written as zeros.
 __global__ __launch_bounds__(256) void quantize_i8_token_kernel(
-    const float* __restrict__ x, int64_t K, int64_t ldx, int8_t* __restrict__ a,
-    float* __restrict__ sa) {
+    const float* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t KBp,
+    int8_t* __restrict__ a, float* __restrict__ sa) {
     __shared__ float red[4];
-    const int64_t m = blockIdx.x;
-    const float* row = x + m * ldx;
-    float amax = 0.f;
-    for (int64_t k = (int64_t)threadIdx.x * 4; k < K; k += 1024) {
-        float4 v = *reinterpret_cast<const float4*>(row + k);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
+    const int64_t Mp = (M + 31) & ~(int64_t)31;
+    for (int64_t m = blockIdx.x; m < Mp; m += gridDim.x) {
+        const bool live = m < M;
+        const float* row = x + (live ? m : 0) * ldx;
+        float amax = 0.f;
+        if (live) {
+            for (int64_t k = (int64_t)threadIdx.x * 4; k < K; k += 1024) {
+                float4 v = *reinterpret_cast<const float4*>(row + k);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+        }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float d = amax / 127.0f;
-    const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
-    for (int64_t k = (int64_t)threadIdx.x * 4; k < K; k += 1024) {
-        float4 v = *reinterpret_cast<const float4*>(row + k);
-        *reinterpret_cast<uint32_t*>(a + m * K + k) =
-            pack4(q_of(v.x, di), q_of(v.y, di), q_of(v.z, di), q_of(v.w, di));
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        const float d = amax / 127.0f;
+        const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+        uint8_t* tile = reinterpret_cast<uint8_t*>(a) + (m >> 5) * KBp * 1024;
+        const int r = (int)(m & 31);
+        for (int64_t k = (int64_t)threadIdx.x * 4; k < KBp * 32; k += 1024) {
+            uint32_t w = 0;
+            if (live && k < K) {
+                float4 v = *reinterpret_cast<const float4*>(row + k);
+                w = pack4(q_of(v.x, di), q_of(v.y, di), q_of(v.z, di), q_of(v.w, di));
+            }
+            const int kk = (int)(k & 31);
+            *reinterpret_cast<uint32_t*>(tile + (((k >> 5) * 64 + (kk >> 4) * 32 + r) * 16 + (kk & 15))) = w;
+        }
+        if (threadIdx.x == 0) sa[m] = d;
+        __syncthreads();                  // red[] is reused by the next row
     }
-    if (threadIdx.x == 0) sa[m] = d;
 }
 
 }  // namespace
@@ -152,8 +168,9 @@ hipError_t launch_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_
                                     hipStream_t s) {
     const ActI8Layout L = act_i8_layout(M, K);
     uint8_t* base = static_cast<uint8_t*>(act);
-    hipLaunchKernelGGL(quantize_i8_token_kernel, dim3((unsigned)M), dim3(256), 0, s, x, K, ldx,
-                       reinterpret_cast<int8_t*>(base + L.a_off),
+    const unsigned grid = (unsigned)std::min<int64_t>(L.Mp, 65536);
+    hipLaunchKernelGGL(quantize_i8_token_kernel, dim3(grid), dim3(256), 0, s, x, M, K, ldx,
+                       L.KBp, reinterpret_cast<int8_t*>(base + L.a_off),
                        reinterpret_cast<float*>(base + L.sa_off));
     return hipGetLastError();
 }

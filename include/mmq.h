@@ -95,9 +95,12 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
  *                  construction); the operand form of the GEMM's scale outer product.
  *   region 4  xsx  f32 [Mp][KBp]: xs * xsum (exact in f32), the operand of the q4_K min term.
  *   Rows m >= M and blocks b >= KB hold zeros in every region.
- * MMQ_ACT_I8_TOKEN (two regions):
- *   region 0  a    int8 [M][K] row-major (row stride K).
- *   region 1  sa   f32 [M], starting at the first 256-byte boundary after region 0.
+ * MMQ_ACT_I8_TOKEN (two regions, each starting on a 256-byte boundary):
+ *   region 0  a    int8, Mp*KBp*32 bytes, tiled exactly like region 0 of MMQ_ACT_Q8_1 (the
+ *                  value of row m, column k at ((m/32)*KBp + k/32)*1024 +
+ *                  (((k%32)/16)*32 + m%32)*16 + k%16).
+ *   region 1  sa   f32 [Mp]: the per-token scale.
+ *   Rows m >= M and blocks b >= KB hold zeros in both regions.
  * --------------------------------------------------------------------------------------- */
 
 /* Total bytes of an act buffer; 0 if the arguments are invalid. (host only) */

@@ -57,9 +57,10 @@ def test_act_bytes_and_offsets(mmq):
     assert o[4] == o[3] + 4 * cells    # xs2 f16 pair
     assert mmq.act_bytes("q8_1", M, K) == o[4] + 4 * cells   # xsx f32
     assert all(v % 256 == 0 for v in o)
+    # i8_token: Mp=32, KBp=8 -> one 8 KB tile region, then sa f32 [Mp]
     oi = mmq.act_region_offsets("i8_token", 3, 64)
-    assert oi == (0, 256, 0, 0, 0)
-    assert mmq.act_bytes("i8_token", 3, 64) == 512
+    assert oi == (0, 8192, 0, 0, 0)
+    assert mmq.act_bytes("i8_token", 3, 64) == 8192 + 256
     assert mmq.act_bytes("q8_1", 4, 33) == 0         # K not a multiple of 32
     assert mmq.act_bytes("q8_1", 0, 64) == 0
     assert mmq.act_bytes(7, 4, 64) == 0
@@ -163,3 +164,25 @@ def test_product_path_does_not_import_oracle():
         if f.endswith((".py", ".c")):
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "block_quantized_int8_amd" not in text, f
+
+
+def test_act_i8_layout_roundtrip(mmq):
+    """The host encoder of the per-token int8 act layout places value (m, k) where the header
+    says: ((m/32)*KBp + k/32)*1024 + (((k%32)/16)*32 + m%32)*16 + k%16, and the decoder
+    inverts it; padding rows/blocks and scales are zero."""
+    M, K = 37, 96
+    rng = np.random.default_rng(3)
+    a = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    sa = rng.random(M, dtype=np.float32) + 0.5
+    buf = mmq.act_i8_pack_host(a, sa)
+    assert buf.size == mmq.act_bytes("i8_token", M, K)
+    o = mmq.act_region_offsets("i8_token", M, K)
+    KBp = 8
+    for m, k in [(0, 0), (5, 17), (31, 95), (32, 0), (36, 63), (33, 40)]:
+        pos = o[0] + ((m // 32) * KBp + k // 32) * 1024 + (((k % 32) // 16) * 32 + m % 32) * 16 + k % 16
+        assert buf[pos].view(np.int8) == a[m, k]
+    a2, sa2 = mmq.act_i8_to_host(buf, M, K)
+    assert np.array_equal(a2, a) and np.array_equal(sa2, sa)
+    full, sap = mmq.act_i8_to_host(buf, M, K, padded=True)
+    assert full.shape == (64, KBp * 32) and not full[M:].any() and not full[:, K:].any()
+    assert not sap[M:].any()

@@ -184,10 +184,7 @@ def _w8a8_case(env, M, N, K, seed, sample_rows=None):
     a, sa = gen.i8_rows(M, K, seed=seed, cfg=74, tensor=0)
     w, sw = gen.i8_rows(N, K, seed=seed, cfg=74, tensor=1)
     print(f"[case] w8a8 M={M} N={N} K={K}", flush=True)
-    act = torch.empty(mmq.act_bytes("i8_token", M, K), dtype=torch.uint8, device=dev)
-    o0, o1 = mmq.act_region_offsets("i8_token", M, K)[:2]
-    act[o0:o0 + M * K].copy_(torch.from_numpy(a.view(np.uint8).ravel()))
-    act[o1:o1 + 4 * M].copy_(torch.from_numpy(sa.view(np.uint8)))
+    act = torch.from_numpy(mmq.act_i8_pack_host(a, sa)).to(dev)
     packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K, row_scale=torch.from_numpy(sw).to(dev))
     out = mmq.gemm("i8_row", packed, act, M, N, K, "bf16")
     acc = mmq.gemm("i8_row", packed, act, M, N, K, "i32_partials")
@@ -243,9 +240,9 @@ def test_quantize_i8_token_bit_exact(env, M, K):
     act = mmq.quantize_act(torch.from_numpy(x).to("cuda"), "i8_token")
     torch.cuda.synchronize()
     host = act.cpu().numpy()
-    o0, o1 = mmq.act_region_offsets("i8_token", M, K)[:2]
-    a = host[o0:o0 + M * K].view(np.int8).reshape(M, K)
-    sa = host[o1:o1 + 4 * M].view(np.float32)
+    a, sa = mmq.act_i8_to_host(host, M, K)
     ra, rsa = orc.quantize_i8_token(x)
     assert np.array_equal(a, ra)
     assert np.array_equal(sa.view(np.uint32), rsa.view(np.uint32))
+    full, sap = mmq.act_i8_to_host(host, M, K, padded=True)      # padding rows/blocks are zero
+    assert not full[M:].any() and not full[:, K:].any() and not sap[M:].any()
