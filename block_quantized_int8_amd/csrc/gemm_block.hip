@@ -500,8 +500,9 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     // work of step i+1 (dots, scale, conversion) around the vector FMAs of step i, so the
     // matrix core and the vector unit stay busy together. The next block's operands are read
     // from LDS at its first step and unpacked at its last.
-    // `nxt` (if not null) receives the DMA of the following stage: its chunks are issued one per
-    // step over the first steps, so the vector-memory issue never holds a wave for long.
+    // `nxt` (if not null) receives the DMA of the following stage: its chunks are issued a few
+    // per step (one per step when there are enough steps) over the first steps, so the
+    // vector-memory issue never holds a wave for long.
     auto run_stage = [&](const uint8_t* cur, int s, uint8_t* nxt) __attribute__((always_inline)) {
         Ops op[2];
         Raw raw;
@@ -518,7 +519,13 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
             for (int t = 0; t < NT_; ++t) {
                 const bool more = t + 1 < NT_ || kb + 1 < KS;
                 const int kn = (t + 1 < NT_) ? kb : kb + 1, tn = (t + 1) % NT_;
-                if (nxt != nullptr && kb * NT_ + t < C::CPW) issue_chunk(nxt, kb * NT_ + t);
+                if (nxt != nullptr) {
+                    constexpr int PER = (C::CPW + KS * NT_ - 1) / (KS * NT_);   // chunks per step
+                    const int st = kb * NT_ + t;
+#pragma unroll
+                    for (int j = st * PER; j < st * PER + PER; ++j)
+                        if (j < C::CPW) issue_chunk(nxt, j);
+                }
                 if (kb + 1 < KS) {
                     if (t == 0) fetch(cur, kb + 1, raw);
                     if (t == (NT_ >= 3 ? NT_ - 2 : 0)) mid(raw);
@@ -628,6 +635,10 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 // CTA tiles.
 constexpr int WN_ = 2, WM_ = 2, RT_ = 2, CT_ = 2;
 constexpr bool XM_ = true;        // conversion on the matrix core (see the kernel notes)
+// MUL_MAT_ID: 4 x 1 waves, each 1 weight tile x 2 token tiles -> 128 weight rows x 64 token
+// slots. An expert sees about T*top_k/E tokens (64 for 512 tokens, top-8 of 64), so 64-slot
+// units leave fewer empty slots than 128-slot ones, with the same unpack work per tile pair.
+constexpr int GWN_ = 4, GWM_ = 1, GRT_ = 1, GCT_ = 2;
 
 template <mmq_wtype FMT>
 BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, int64_t K) {
@@ -681,19 +692,19 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
     g.pairs = pairs;
     g.E = (int)E;
     g.top_k = (int)top_k;
-    g.ntiles_n = (int)ceil_div(N, WN_ * RT_ * 32);
+    g.ntiles_n = (int)ceil_div(N, GWN_ * GRT_ * 32);
     g.out = static_cast<float*>(out);
     g.ldo = N;
     const int64_t nblk = round_up(max_units, 8) * g.ntiles_n;
-    const dim3 grid((unsigned)nblk), block(WN_ * WM_ * 64);
-    hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, GATHER_F32, XM_>), grid, block, 0, s, g);
+    const dim3 grid((unsigned)nblk), block(GWN_ * GWM_ * 64);
+    hipLaunchKernelGGL((mmq_block_kernel<FMT, GWN_, GWM_, GRT_, GCT_, GATHER_F32, XM_>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Tokens per MUL_MAT_ID unit (one CTA's token extent).
-int gather_unit_tokens() { return WM_ * CT_ * 32; }
+int gather_unit_tokens() { return GWM_ * GCT_ * 32; }
 
 // One-dimensional grids stay below 2^31 workgroups.
 constexpr int64_t MAX_GRID = int64_t(1) << 31;
@@ -703,7 +714,7 @@ bool dense_grid_ok(int64_t M, int64_t N) {
 }
 
 bool gather_grid_ok(int64_t max_units, int64_t N) {
-    return round_up(max_units, 8) * ceil_div(N, WN_ * RT_ * 32) < MAX_GRID;
+    return round_up(max_units, 8) * ceil_div(N, GWN_ * GRT_ * 32) < MAX_GRID;
 }
 
 hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,

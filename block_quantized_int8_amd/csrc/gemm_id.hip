@@ -7,8 +7,9 @@
 //      counts (pair offsets) and of the per-expert unit counts ceil(count / U) (unit offsets),
 //      then scatter the pair ids into expert order.
 //   2. the gather-mode MMQ kernel: one workgroup per (unit, 128-row weight tile); a unit is up
-//      to U = 128 pairs of one expert. It finds its expert by binary search over the unit
-//      offsets, reads its tokens' activation rows and writes each pair's own output row.
+//      to U = 64 pairs of one expert (gather_unit_tokens()). It finds its expert by binary
+//      search over the unit offsets, reads its tokens' activation rows and writes each pair's
+//      own output row.
 // No host round trip: the grid is sized for the worst case (P/U + min(E, P) units) and
 // workgroups past the actual unit count leave at once.
 #include "mmq_internal.h"
