@@ -194,8 +194,9 @@ def _act_dims(M: int, K: int):
 
 
 def _act_regions(act_bytes_host: np.ndarray, M: int, K: int):
-    """All five q8_1 regions, padding included: xq int8 [Mp, KBp*32], xs f32 [Mp, KBp],
-    xsum int32 [Mp, KBp], xs2 uint32 [Mp, KBp], xsx f32 [Mp, KBp]."""
+    """All five q8_1 regions, padding included, as row-major arrays: xq int8 [Mp, KBp*32],
+    xs f32 [Mp, KBp], xsum int32 [Mp, KBp], xs2 uint32 [Mp, KBp], xsx f32 [Mp, KBp] (regions 3
+    and 4 are stored tile-major, [MT][KBp][32], and transposed back here)."""
     o = act_region_offsets("q8_1", M, K)
     Mp, KB, KBp, MT = _act_dims(M, K)
     buf = np.asarray(act_bytes_host, dtype=np.uint8)
@@ -204,8 +205,10 @@ def _act_regions(act_bytes_host: np.ndarray, M: int, K: int):
     cells = Mp * KBp
     xs = buf[o[1]:o[1] + 4 * cells].view(np.float32).reshape(Mp, KBp)
     xsum = buf[o[2]:o[2] + 4 * cells].view(np.int32).reshape(Mp, KBp)
-    xs2 = buf[o[3]:o[3] + 4 * cells].view(np.uint32).reshape(Mp, KBp)
-    xsx = buf[o[4]:o[4] + 4 * cells].view(np.float32).reshape(Mp, KBp)
+    def tile_major(region, dt):
+        return buf[region:region + 4 * cells].view(dt).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
+    xs2 = tile_major(o[3], np.uint32)
+    xsx = tile_major(o[4], np.float32)
     return xq, xs, xsum, xs2, xsx
 
 

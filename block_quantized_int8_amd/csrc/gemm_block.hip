@@ -169,48 +169,57 @@ template <> struct BT<MMQ_IQ1T> {
 };
 
 // ------------------------------------------------------------------- kernel configuration
-enum Mode { DENSE_F32 = 0, DENSE_PARTIALS = 1, GATHER_F32 = 2 };
+// GATHER_F32: MUL_MAT_ID full units (up to unit_rows pairs of one expert); GATHER_TAIL: the
+// tail unit of an expert (the at most unit_rows/2 pairs after its full units).
+enum Mode { DENSE_F32 = 0, DENSE_PARTIALS = 1, GATHER_F32 = 2, GATHER_TAIL = 3 };
+constexpr bool is_gather(int mode) { return mode == GATHER_F32 || mode == GATHER_TAIL; }
 
 // WN x WM waves, each owning RT weight tiles x CT token tiles of 32 x 32.
 // LDS stage layout (bytes): weight fragments [TN][KS][FB] | token fragments [TM][KS][1024] |
-// weight scale dwords | token scale dwords | (q4_K) weight mins | token xs*xsum | padding.
-// Fragments arrive in 1 KB chunks (one wave-wide 16-byte DMA each). Scale regions arrive as one
-// 4-byte-per-lane DMA per (pair of 32-row tiles, block), so they sit block-major,
-// [tile pair][KS][64 rows] dwords, and the per-block reads of 32 consecutive rows are free of
-// bank conflicts; each lane names its own row, which also gathers MUL_MAT_ID rows.
-// Chunk c goes to wave c % NW; every chunk type's count is a multiple of NW, so the type of a
-// wave's j-th chunk is known at compile time.
-template <mmq_wtype FMT, int WN, int WM, int RT, int CT>
+// weight scale dwords | token scale dwords | (q4_K) weight mins | token xs*xsum.
+// Fragments arrive in 1 KB chunks (one wave-wide 16-byte DMA each). The scale regions are
+// tile-major in memory and in LDS, [tile][KS][32 rows] dwords (512 bytes per tile and stage,
+// one cache line per block), so one 16-byte DMA brings a pair of tiles; gathered MUL_MAT_ID
+// token rows come one dword per lane instead, a 4-byte DMA per (tile, pair of blocks). The
+// per-block reads of 32 consecutive rows are free of bank conflicts.
+// Chunk c goes to wave c % NW. Fragment chunk counts are multiples of NW, so the kind of those
+// slots is known at compile time; the scale chunks (padded to a multiple of NW) take the last
+// slots, their kind chosen per wave.
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT, bool GATHER>
 struct Cfg {
     using T = BT<FMT>;
     static constexpr int NW = WN * WM, NTH = NW * 64;
     static constexpr int TN = WN * RT, TM = WM * CT;
     static constexpr int WF = TN * KS * T::FB;
     static constexpr int XF = TM * KS * 1024;
+    static constexpr int SCB = KS * 32 * 4;                 // one tile's scale dwords per stage
     static constexpr int C_WF = WF / 1024, C_XF = TM * KS;
-    static constexpr int C_WS = (TN + 1) / 2 * KS, C_XS = (TM + 1) / 2 * KS;
+    static constexpr int C_WS = (TN + 1) / 2;               // a pair of tiles per chunk
+    static constexpr int C_XS = GATHER ? TM * KS / 2 : (TM + 1) / 2;
     static constexpr int C_WM = T::MIN ? C_WS : 0, C_XM = T::MIN ? C_XS : 0;
-    static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + C_WS * 256;
-    static constexpr int O_WM = O_XS + C_XS * 256, O_XM = O_WM + C_WM * 256;
-    static constexpr int BUF = O_XM + C_XM * 256;
-    static constexpr int C_ALL = C_WF + C_XF + C_WS + C_XS + C_WM + C_XM;
-    static constexpr int CPW = C_ALL / NW;                     // chunks per wave per stage
+    static constexpr int RW = C_WS * 2 * SCB, RX = (TM + 1) / 2 * 2 * SCB;   // region bytes
+    static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + RW;
+    static constexpr int O_WM = O_XS + RX, O_XM = O_WM + (T::MIN ? RW : 0);
+    static constexpr int BUF = O_XM + (T::MIN ? RX : 0);
+    static constexpr int C_FR = C_WF + C_XF;
+    static constexpr int C_SC = C_WS + C_XS + C_WM + C_XM;
+    static constexpr int C_ALL = C_FR + (C_SC + NW - 1) / NW * NW;
+    static constexpr int CPW = C_ALL / NW;                  // chunks per wave per stage
     static_assert(WF % 1024 == 0, "weight fragments of a stage must be whole 1 KB chunks");
-    static_assert(C_WF % NW == 0 && C_XF % NW == 0 && C_WS % NW == 0 && C_XS % NW == 0,
-                  "every chunk type must split evenly over the waves");
-    // chunk types
-    enum { K_WF = 0, K_XF = 1, K_WS = 2, K_XS = 3, K_WM = 4, K_XM = 5 };
-    __host__ __device__ static constexpr int kind(int c) {
-        return c < C_WF ? K_WF : (c -= C_WF) < C_XF ? K_XF : (c -= C_XF) < C_WS ? K_WS
-             : (c -= C_WS) < C_XS ? K_XS : (c -= C_XS) < C_WM ? K_WM : K_XM;
+    static_assert(C_WF % NW == 0 && C_XF % NW == 0, "fragment chunks must split evenly over the waves");
+    static_assert(KS % 2 == 0, "gathered scale chunks cover two blocks");
+    enum { K_WF = 0, K_XF = 1, K_SC = 2 };                      // slot kinds
+    enum { S_WS = 0, S_XS = 1, S_WM = 2, S_XM = 3, S_NONE = 4 };  // scale chunk kinds
+    __host__ __device__ static constexpr int slot_kind(int j) {
+        return j * NW < C_WF ? K_WF : j * NW < C_FR ? K_XF : K_SC;
     }
-    __host__ __device__ static constexpr int first(int k) {
-        return k == K_WF ? 0 : k == K_XF ? C_WF : k == K_WS ? C_WF + C_XF : k == K_XS ? C_WF + C_XF + C_WS
-             : k == K_WM ? C_WF + C_XF + C_WS + C_XS : C_WF + C_XF + C_WS + C_XS + C_WM;
+    __host__ __device__ static constexpr int scale_kind(int ci) {
+        return ci < C_WS ? S_WS : (ci -= C_WS) < C_XS ? S_XS : (ci -= C_XS) < C_WM ? S_WM
+             : (ci -= C_WM) < C_XM ? S_XM : S_NONE;
     }
     // LDS byte offset of the scale dword of (tile i, row r, block kb) in a region at `base`
     __host__ __device__ static constexpr int sc(int base, int i, int r, int kb) {
-        return base + (((i >> 1) * KS + kb) * 64 + (i & 1) * 32 + r) * 4;
+        return base + ((i * KS + kb) * 32 + r) * 4;
     }
 };
 
@@ -229,8 +238,9 @@ struct BlockArgs {
     // gather mode (MUL_MAT_ID)
     const int32_t* offs;        // [E+1] first pair of each expert in `pairs`
     const int32_t* uoff;        // [E+1] first unit of each expert; uoff[E] = live units
+    const int32_t* ufull;       // [E+1] full-unit offsets (tail mode: full units per expert)
     const int32_t* pairs;       // pair ids in expert order (pair = token*top_k + slot)
-    int E, top_k, ntiles_n;
+    int E, top_k, ntiles_n, unit_rows;
 };
 
 typedef __attribute__((address_space(1))) const void gmem_t;
@@ -253,7 +263,7 @@ __device__ inline h4 as_h4(uint32_t lo) {
 
 template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int MODE, bool XM>
 __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs args) {
-    using C = Cfg<FMT, WN, WM, RT, CT>;
+    using C = Cfg<FMT, WN, WM, RT, CT, is_gather(MODE)>;
     using T = typename C::T;
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::BUF];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::BUF];
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     // (unit, n-tile) with the unit list produced on the device
     int nt_base, mt_base = 0, unit_first = 0, unit_count = 0;
     const uint8_t* wbase = args.w;
-    if constexpr (MODE == GATHER_F32) {
+    if constexpr (is_gather(MODE)) {
         // workgroup b runs on XCD b % 8; unit u = 8 * (rest / ntiles_n) + b % 8 keeps all weight
         // tiles of a unit (which share its activation rows) on one XCD and spreads the live
         // units (the lowest ids) evenly over the XCDs
@@ -282,8 +292,13 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
             if (args.uoff[mid] <= u) lo = mid; else hi = mid;
         }
         const int e = lo;
-        unit_first = args.offs[e] + (u - args.uoff[e]) * (C::TM * 32);
-        unit_count = min(C::TM * 32, args.offs[e + 1] - unit_first);
+        if constexpr (MODE == GATHER_TAIL) {
+            unit_first = args.offs[e] + (args.ufull[e + 1] - args.ufull[e]) * args.unit_rows;
+            unit_count = args.offs[e + 1] - unit_first;           // 1 .. unit_rows/2 <= TM*32
+        } else {
+            unit_first = args.offs[e] + (u - args.uoff[e]) * args.unit_rows;
+            unit_count = min(args.unit_rows, args.offs[e + 1] - unit_first);
+        }
         wbase = args.w + (int64_t)e * args.w_stride;
         nt_base = (rest % args.ntiles_n) * C::TN;
     } else {
@@ -291,11 +306,11 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         nt_base = (lid / args.tiles_m) * C::TN;
         mt_base = (lid % args.tiles_m) * C::TM;
     }
-    const int NT = args.NT, KBp = args.KBp, Np = NT * 32;
+    const int NT = args.NT, KBp = args.KBp;
 
     // token slot (tile j, row r) -> activation row to read
     auto src_token = [&](int j, int r) __attribute__((always_inline)) -> int {
-        if constexpr (MODE == GATHER_F32) {
+        if constexpr (is_gather(MODE)) {
             const int s = j * 32 + r;
             return s < unit_count ? args.pairs[unit_first + s] / args.top_k : 0;
         } else {
@@ -311,21 +326,17 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     // base, advanced by a fixed stride per stage; the chunk's LDS offset is wave-uniform.
     uint32_t goff[C::CPW];
     int ldso[C::CPW];
+    int skind[C::CPW];                                       // scale slots: kind, wave-uniform
     const uint8_t* const wsc = wbase + args.w_scale_off;
     const uint8_t* const wmn = wbase + args.w_min_off;
-    auto chunk_base = [&](int k) __attribute__((always_inline)) -> const uint8_t* {
-        return k == C::K_WF ? wbase : k == C::K_XF ? args.xq : k == C::K_WS ? wsc
-             : k == C::K_XS ? reinterpret_cast<const uint8_t*>(args.xs2)
-             : k == C::K_WM ? wmn : reinterpret_cast<const uint8_t*>(args.xsx);
-    };
-    auto chunk_adv = [&](int k) __attribute__((always_inline)) -> int {
-        return k == C::K_WF ? KS * T::FB : k == C::K_XF ? KS * 1024 : KS * 4;
-    };
 #pragma unroll
     for (int j = 0; j < C::CPW; ++j) {
-        const int k = C::kind(j * C::NW);                    // compile-time per j
-        const int c = j * C::NW + wave - C::first(k);         // index within its type
+        const int k = C::slot_kind(j);                       // compile-time per j
+        const int c = j * C::NW + wave;
         const int h = lane >> 5;
+        skind[j] = C::S_NONE;
+        goff[j] = 0;
+        ldso[j] = 0;
         if (k == C::K_WF) {
             const int byte = c * 1024 + lane * 16;
             const int tile = byte / (KS * T::FB), off = byte % (KS * T::FB);
@@ -333,30 +344,57 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
             goff[j] = (uint32_t)(nt * KBp * T::FB + off);
             ldso[j] = c * 1024;
         } else if (k == C::K_XF) {
-            const int jt = c / KS, q = c % KS;
+            const int ci = c - C::C_WF;
+            const int jt = ci / KS, q = ci % KS;
             const int t = src_token(jt, r32);
             goff[j] = (uint32_t)((((t >> 5) * KBp + q) * 64 + h * 32 + (t & 31)) * 16);
-            ldso[j] = C::O_XF + c * 1024;
+            ldso[j] = C::O_XF + ci * 1024;
         } else {
-            // scale-type chunk: (tile pair, block) -> 64 rows x one dword
-            const int pr = c / KS, q = c % KS, tile = 2 * pr + h;
-            int row;
-            if (k == C::K_WS || k == C::K_WM) {
-                row = min((nt_base + tile) * 32 + r32, Np - 1);
-            } else {
-                row = tile < C::TM ? src_token(tile, r32) : 0;
+            const int ci = c - C::C_FR;
+            const int sk = C::scale_kind(ci);
+            skind[j] = sk;
+            if (sk == C::S_WS || sk == C::S_WM) {
+                // a pair of weight tiles: lanes 0-31 tile 2pr, lanes 32-63 tile 2pr+1, 16 bytes
+                // each of the tile's contiguous 512-byte stage
+                const int pr = ci - (sk == C::S_WS ? 0 : C::C_WS + C::C_XS);
+                const int nt = min(nt_base + 2 * pr + h, NT - 1);
+                goff[j] = (uint32_t)(nt * KBp * 128 + r32 * 16);
+                ldso[j] = (sk == C::S_WS ? C::O_WS : C::O_WM) + pr * 1024;
+            } else if (sk == C::S_XS || sk == C::S_XM) {
+                const int x = ci - (sk == C::S_XS ? C::C_WS : C::C_WS + C::C_XS + C::C_WM);
+                const int base = sk == C::S_XS ? C::O_XS : C::O_XM;
+                if constexpr (is_gather(MODE)) {
+                    // (tile i, blocks 2bp and 2bp+1): each lane fetches its own gathered row's dword
+                    const int i = x / (KS / 2), bp = x % (KS / 2);
+                    const int m = src_token(i, r32);
+                    goff[j] = (uint32_t)((((m >> 5) * KBp + 2 * bp + h) * 32 + (m & 31)) * 4);
+                    ldso[j] = base + (i * KS + 2 * bp) * 128;
+                } else {
+                    const int mt = min(mt_base + 2 * x + h, args.MT - 1);
+                    goff[j] = (uint32_t)(mt * KBp * 128 + r32 * 16);
+                    ldso[j] = base + x * 1024;
+                }
             }
-            goff[j] = (uint32_t)((row * KBp + q) * 4);
-            const int base = k == C::K_WS ? C::O_WS : k == C::K_XS ? C::O_XS : k == C::K_WM ? C::O_WM : C::O_XM;
-            ldso[j] = base + c * 256;
         }
     }
     auto issue_chunk = [&](uint8_t* buf, int j) __attribute__((always_inline)) {
-        const int k = C::kind(j * C::NW);
+        const int k = C::slot_kind(j);
         uint8_t* dst = buf + __builtin_amdgcn_readfirstlane(ldso[j]);
-        if (k == C::K_WF || k == C::K_XF) dma16(chunk_base(k) + goff[j], dst);
-        else dma4(chunk_base(k) + goff[j], dst);
-        goff[j] += chunk_adv(k);
+        if (k == C::K_WF) {
+            dma16(wbase + goff[j], dst);
+            goff[j] += KS * T::FB;
+        } else if (k == C::K_XF) {
+            dma16(args.xq + goff[j], dst);
+            goff[j] += KS * 1024;
+        } else {
+            const int sk = skind[j];
+            if (sk == C::S_NONE) return;
+            const uint8_t* base = sk == C::S_WS ? wsc : sk == C::S_XS ? reinterpret_cast<const uint8_t*>(args.xs2)
+                                : sk == C::S_WM ? wmn : reinterpret_cast<const uint8_t*>(args.xsx);
+            if (is_gather(MODE) && (sk == C::S_XS || sk == C::S_XM)) dma4(base + goff[j], dst);
+            else dma16(base + goff[j], dst);
+            goff[j] += C::SCB;
+        }
     };
     auto issue_stage = [&](uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -602,7 +640,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             int row;
-            if constexpr (MODE == GATHER_F32) {
+            if constexpr (is_gather(MODE)) {
                 const int sl = (wm * CT + ct) * 32 + r32;
                 row = sl < unit_count ? args.pairs[unit_first + sl] : -1;
             } else {
@@ -639,6 +677,11 @@ constexpr bool XM_ = true;        // conversion on the matrix core (see the kern
 // slots. An expert sees about T*top_k/E tokens (64 for 512 tokens, top-8 of 64), so 64-slot
 // units leave fewer empty slots than 128-slot ones, with the same unpack work per tile pair.
 constexpr int GWN_ = 4, GWM_ = 1, GRT_ = 1, GCT_ = 2;
+// Tail units (at most 32 pairs): the same with one token tile per wave. With ~64 +- 8 pairs per
+// expert, splitting off tails this way leaves at most 31 empty slots per expert.
+constexpr int TCT_ = 1;
+constexpr int UNIT_ROWS = GWM_ * GCT_ * 32;
+static_assert(UNIT_ROWS / 2 <= GWM_ * TCT_ * 32, "a tail unit fits the tail configuration");
 
 template <mmq_wtype FMT>
 BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, int64_t K) {
@@ -683,28 +726,36 @@ hipError_t launch_dense(const void* packed, const void* act, int64_t M, int64_t 
 
 template <mmq_wtype FMT>
 hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t T, int64_t top_k,
-                         int64_t N, int64_t K, const int32_t* offs, const int32_t* uoff,
-                         const int32_t* pairs, int max_units, void* out, hipStream_t s) {
+                         int64_t N, int64_t K, const int32_t* offs, const int32_t* ufull,
+                         const int32_t* utail, const int32_t* pairs, int max_full, int max_tail,
+                         void* out, hipStream_t s) {
     BlockArgs g = dense_args<FMT>(packed, act, T, N, K);
     g.w_stride = (int64_t)packed_layout(FMT, N, K).bytes;
     g.offs = offs;
-    g.uoff = uoff;
+    g.ufull = ufull;
     g.pairs = pairs;
     g.E = (int)E;
     g.top_k = (int)top_k;
     g.ntiles_n = (int)ceil_div(N, GWN_ * GRT_ * 32);
+    g.unit_rows = UNIT_ROWS;
     g.out = static_cast<float*>(out);
     g.ldo = N;
-    const int64_t nblk = round_up(max_units, 8) * g.ntiles_n;
-    const dim3 grid((unsigned)nblk), block(GWN_ * GWM_ * 64);
-    hipLaunchKernelGGL((mmq_block_kernel<FMT, GWN_, GWM_, GRT_, GCT_, GATHER_F32, XM_>), grid, block, 0, s, g);
+    const dim3 block(GWN_ * GWM_ * 64);
+    g.uoff = ufull;
+    hipLaunchKernelGGL((mmq_block_kernel<FMT, GWN_, GWM_, GRT_, GCT_, GATHER_F32, XM_>),
+                       dim3((unsigned)(round_up(max_full, 8) * g.ntiles_n)), block, 0, s, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g.uoff = utail;
+    hipLaunchKernelGGL((mmq_block_kernel<FMT, GWN_, GWM_, GRT_, TCT_, GATHER_TAIL, XM_>),
+                       dim3((unsigned)(round_up(max_tail, 8) * g.ntiles_n)), block, 0, s, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Tokens per MUL_MAT_ID unit (one CTA's token extent).
-int gather_unit_tokens() { return GWM_ * GCT_ * 32; }
+// Pairs per full MUL_MAT_ID unit (one full-unit workgroup's token extent).
+int gather_unit_tokens() { return UNIT_ROWS; }
 
 // One-dimensional grids stay below 2^31 workgroups.
 constexpr int64_t MAX_GRID = int64_t(1) << 31;
@@ -730,15 +781,17 @@ hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, i
 
 hipError_t launch_block_gather(mmq_wtype t, const void* packed, int64_t E, const void* act, int64_t T,
                                int64_t top_k, int64_t N, int64_t K, const int32_t* offs,
-                               const int32_t* uoff, const int32_t* pairs, int max_units, void* out,
-                               hipStream_t s) {
+                               const int32_t* ufull, const int32_t* utail, const int32_t* pairs,
+                               int max_full, int max_tail, void* out, hipStream_t s) {
+#define MMQ_GATHER(F) launch_gather<F>(packed, E, act, T, top_k, N, K, offs, ufull, utail, pairs, max_full, max_tail, out, s)
     switch (t) {
-        case MMQ_Q8_0: return launch_gather<MMQ_Q8_0>(packed, E, act, T, top_k, N, K, offs, uoff, pairs, max_units, out, s);
-        case MMQ_Q4_0: return launch_gather<MMQ_Q4_0>(packed, E, act, T, top_k, N, K, offs, uoff, pairs, max_units, out, s);
-        case MMQ_Q4_K: return launch_gather<MMQ_Q4_K>(packed, E, act, T, top_k, N, K, offs, uoff, pairs, max_units, out, s);
-        case MMQ_IQ1T: return launch_gather<MMQ_IQ1T>(packed, E, act, T, top_k, N, K, offs, uoff, pairs, max_units, out, s);
+        case MMQ_Q8_0: return MMQ_GATHER(MMQ_Q8_0);
+        case MMQ_Q4_0: return MMQ_GATHER(MMQ_Q4_0);
+        case MMQ_Q4_K: return MMQ_GATHER(MMQ_Q4_K);
+        case MMQ_IQ1T: return MMQ_GATHER(MMQ_IQ1T);
         default: return hipErrorNotSupported;
     }
+#undef MMQ_GATHER
 }
 
 }  // namespace mmq

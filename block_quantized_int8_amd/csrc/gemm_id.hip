@@ -3,15 +3,18 @@
 // out[t][j][:] = act[t] x W_{ids[t][j]}^T. The (token, slot) pairs are grouped by expert on the
 // device (llama.cpp PR #304 routes MUL_MAT_ID through MMQ instead of one small product per
 // expert, which it reports dominates prompt processing otherwise):
-//   1. route_kernel (one workgroup): count pairs per expert in LDS, exclusive scan of the
-//      counts (pair offsets) and of the per-expert unit counts ceil(count / U) (unit offsets),
-//      then scatter the pair ids into expert order.
-//   2. the gather-mode MMQ kernel: one workgroup per (unit, 128-row weight tile); a unit is up
-//      to U = 64 pairs of one expert (gather_unit_tokens()). It finds its expert by binary
-//      search over the unit offsets, reads its tokens' activation rows and writes each pair's
-//      own output row.
-// No host round trip: the grid is sized for the worst case (P/U + min(E, P) units) and
-// workgroups past the actual unit count leave at once.
+//   1. route_kernel (one workgroup): count pairs per expert in LDS; split each expert's c pairs
+//      into full units of U = gather_unit_tokens() pairs plus, when the remainder is at most
+//      U/2, one tail unit (a larger remainder is a last full unit); exclusive scans of the
+//      pair counts (pair offsets), full-unit counts and tail-unit counts (unit offsets); then
+//      scatter the pair ids into expert order.
+//   2. the gather-mode MMQ kernel, one launch for the full units and one for the tails (a
+//      workgroup per (unit, 128-row weight tile); tails use one 32-slot token tile per wave, so
+//      at most 31 slots per expert stay empty). A workgroup finds its expert by binary search
+//      over the unit offsets, reads its tokens' activation rows and writes each pair's own
+//      output row.
+// No host round trip: the grids are sized for the worst case and workgroups past the actual
+// unit counts leave at once.
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -21,25 +24,31 @@ constexpr int ROUTE_THREADS = 1024;
 constexpr int MAX_E = 4096;
 
 struct IdWorkspace {
-    int64_t offs_w, uoff_w, perm_w, words;
+    int64_t offs_w, ufull_w, utail_w, perm_w, words;
 };
 
 IdWorkspace id_workspace(int64_t E, int64_t P) {
     IdWorkspace w;
-    w.offs_w = 0;                        // pair offsets [E+1]
-    w.uoff_w = E + 1;                    // unit offsets [E+1]
-    w.perm_w = round_up(2 * (E + 1), 64);  // pair ids in expert order [P]
+    w.offs_w = 0;                          // pair offsets [E+1]
+    w.ufull_w = E + 1;                     // full-unit offsets [E+1]
+    w.utail_w = 2 * (E + 1);               // tail-unit offsets [E+1]
+    w.perm_w = round_up(3 * (E + 1), 64);  // pair ids in expert order [P]
     w.words = w.perm_w + P;
     return w;
 }
 
+// full units and tail units of an expert with c pairs (unit size U)
+__device__ inline int full_units(int c, int U) { return c / U + (c % U > U / 2 ? 1 : 0); }
+__device__ inline int tail_units(int c, int U) { const int r = c % U; return (r > 0 && r <= U / 2) ? 1 : 0; }
+
 __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                              int U, int32_t* __restrict__ offs,
-                                                             int32_t* __restrict__ uoff,
+                                                             int32_t* __restrict__ ufull,
+                                                             int32_t* __restrict__ utail,
                                                              int32_t* __restrict__ perm) {
     __shared__ int cnt[MAX_E];
     __shared__ int cur[MAX_E];
-    __shared__ int wtot[2][ROUTE_THREADS / 64];
+    __shared__ int wtot[3][ROUTE_THREADS / 64];
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += ROUTE_THREADS) cnt[e] = 0;
     __syncthreads();
@@ -52,43 +61,50 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __r
     // thread t owns experts [t*EPT, t*EPT + EPT)
     const int EPT = (E + ROUTE_THREADS - 1) / ROUTE_THREADS;
     const int e0 = tid * EPT, e1 = min(e0 + EPT, E);
-    int sc = 0, su = 0;
+    int sc = 0, sf = 0, st = 0;
     for (int e = e0; e < e1; ++e) {
         sc += cnt[e];
-        su += (cnt[e] + U - 1) / U;
+        sf += full_units(cnt[e], U);
+        st += tail_units(cnt[e], U);
     }
-    // inclusive scan across the wave, then across the 16 waves
-    int ic = sc, iu = su;
+    // inclusive scans across the wave, then across the 16 waves
+    int ic = sc, jf = sf, jt = st;
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int oc = __shfl_up(ic, d, 64), ou = __shfl_up(iu, d, 64);
+        const int oc = __shfl_up(ic, d, 64), of = __shfl_up(jf, d, 64), ot = __shfl_up(jt, d, 64);
         if (lane >= d) {
             ic += oc;
-            iu += ou;
+            jf += of;
+            jt += ot;
         }
     }
     if (lane == 63) {
         wtot[0][wave] = ic;
-        wtot[1][wave] = iu;
+        wtot[1][wave] = jf;
+        wtot[2][wave] = jt;
     }
     __syncthreads();
-    int bc = 0, bu = 0;
+    int bc = 0, bf = 0, bt = 0;
     for (int w = 0; w < wave; ++w) {
         bc += wtot[0][w];
-        bu += wtot[1][w];
+        bf += wtot[1][w];
+        bt += wtot[2][w];
     }
-    int pc = bc + ic - sc, pu = bu + iu - su;      // exclusive prefixes of this thread's range
+    int pc = bc + ic - sc, pf = bf + jf - sf, pt = bt + jt - st;   // exclusive prefixes
     for (int e = e0; e < e1; ++e) {
         offs[e] = pc;
-        uoff[e] = pu;
+        ufull[e] = pf;
+        utail[e] = pt;
         cur[e] = pc;
         pc += cnt[e];
-        pu += (cnt[e] + U - 1) / U;
+        pf += full_units(cnt[e], U);
+        pt += tail_units(cnt[e], U);
     }
     if (tid == ROUTE_THREADS - 1) {
         offs[E] = pc;
-        uoff[E] = pu;
+        ufull[E] = pf;
+        utail[E] = pt;
     }
     __syncthreads();
     for (int p = tid; p < P; p += ROUTE_THREADS) {
@@ -99,6 +115,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __r
 
 }  // namespace
 
+// Worst-case full units (the tail launch needs at most min(E, P)): sum over experts of
+// floor(c/U) + 1 <= P/U + min(E, P).
 int64_t gemm_id_max_units(int64_t E, int64_t P) {
     const int64_t U = gather_unit_tokens();
     return P / U + (E < P ? E : P);
@@ -117,14 +135,15 @@ hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void
     const IdWorkspace w = id_workspace(E, P);
     int32_t* ws = static_cast<int32_t*>(workspace);
     int32_t* offs = ws + w.offs_w;
-    int32_t* uoff = ws + w.uoff_w;
+    int32_t* ufull = ws + w.ufull_w;
+    int32_t* utail = ws + w.utail_w;
     int32_t* perm = ws + w.perm_w;
     hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, ids, (int)P, (int)E,
-                       gather_unit_tokens(), offs, uoff, perm);
+                       gather_unit_tokens(), offs, ufull, utail, perm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_block_gather(t, packed, E, act, T, top_k, N, K, offs, uoff, perm,
-                               (int)gemm_id_max_units(E, P), out, s);
+    return launch_block_gather(t, packed, E, act, T, top_k, N, K, offs, ufull, utail, perm,
+                               (int)gemm_id_max_units(E, P), (int)(E < P ? E : P), out, s);
 }
 
 }  // namespace mmq

@@ -24,10 +24,13 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 //                 values 16h..16h+15 of the block (the B operand of v_mfma_i32_32x32x32_i8)
 //   region 1 xs   f32   [Mp][KBp]   (row-major)
 //   region 2 xsum int32 [Mp][KBp]
-//   region 3 xs2  u32   [Mp][KBp]   xs as f16 bits in both halves (the scale-MFMA operand)
-//   region 4 xsx  f32   [Mp][KBp]   xs * xsum, exact in f32 (the Q4_K min-term operand)
-// Row-major scale regions let one 16-byte load fetch one row's 4 consecutive blocks, which is
-// what a gathered (MUL_MAT_ID) token row needs.
+//   region 3 xs2  u32   tile-major [MT][KBp][32]: xs as f16 bits in both halves (the
+//                 scale-MFMA operand)
+//   region 4 xsx  f32   tile-major [MT][KBp][32]: xs * xsum, exact in f32 (the Q4_K min-term
+//                 operand)
+// The GEMM's own operands (regions 3 and 4) are tile-major so that a stage of a 32-row tile is
+// one contiguous 512-byte run (the global->LDS DMA's cost is per cache line touched); a
+// gathered (MUL_MAT_ID) token row reads one dword per block.
 struct ActQ81Layout {
     int64_t Mp, MT, KB, KBp;
     int64_t xq_off, xs_off, xsum_off, xs2_off, xsx_off, bytes;
@@ -82,13 +85,14 @@ inline ActI8Layout act_i8_layout(int64_t M, int64_t K) {
 //   Q4_K: 8 B per lane, unsigned nibbles: X0 & 0x0F0F0F0F = k 16h+0..3, (X0 >> 4) & 0x0F0F0F0F
 //         = 16h+4..7, likewise X1 for 8..15 -> 512 B.
 //   IQ1T: 4 B per lane of 2-bit codes (value 16h + 4q + b at bits 8b + 2q) -> 256 B.
-// Region 1 holds one dword per (row n, block b), row-major [Np][KBp]:
+// Region 1 holds one dword per (row n, block b), tile-major [NT][KBp][32] (row n, block b at
+// (n/32 * KBp + b) * 32 + n%32, so a 32-row tile's stage of blocks is one contiguous run):
 //   Q8_0, Q4_0: f16 d in the low half, 0 in the high half.
 //   IQ1T:       f16 d (the super-block's) | meta0 << 16 | meta1 << 24, meta_h = s | sigma0 << 3 |
 //               sigma1 << 4 for the half h = 0, 1 of the block (its 16-value sub-scale and the
 //               sign bits of its two 8-value groups).
 //   Q4_K:       d*sc split exactly into two f16 (hi | lo << 16), hi + lo = d*sc.
-// Region 2 (Q4_K only): f32 -dmin*m per (row, block), [Np][KBp].
+// Region 2 (Q4_K only): f32 -dmin*m per (row, block), tile-major like region 1.
 // I8_ROW keeps one f32 per row [Np] in region 1.
 struct PackedLayout {
     int64_t Np, NT, KB, KBp;
@@ -138,10 +142,13 @@ hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, i
                              hipStream_t s);
 // Dense grids: false if the launch would exceed the grid limit (checked before any launch).
 bool dense_grid_ok(int64_t M, int64_t N);
+// MUL_MAT_ID gather: full units (ufull offsets, up to gather_unit_tokens() pairs) and tail
+// units (utail offsets, at most half that), each a launch of its own.
 hipError_t launch_block_gather(mmq_wtype t, const void* packed, int64_t E, const void* act,
                                int64_t T, int64_t top_k, int64_t N, int64_t K,
-                               const int32_t* offs, const int32_t* uoff, const int32_t* perm,
-                               int max_units, void* out, hipStream_t s);
+                               const int32_t* offs, const int32_t* ufull, const int32_t* utail,
+                               const int32_t* perm, int max_full, int max_tail, void* out,
+                               hipStream_t s);
 int gather_unit_tokens();
 bool gather_grid_ok(int64_t max_units, int64_t N);
 int64_t gemm_id_max_units(int64_t E, int64_t P);

@@ -97,8 +97,13 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
             p2[i] = b | (b << 16);
             px[i] = s_xs[i] * (float)s_sum[i];
         }
-        *reinterpret_cast<uint2*>(xs2 + row) = make_uint2(p2[0], p2[1]);
-        *reinterpret_cast<float2*>(xsx + row) = make_float2(px[0], px[1]);
+        // tile-major [MT][KBp][32]: the 32 rows of a block are one 128-byte line
+#pragma unroll
+        for (int i = 0; i < QG; ++i) {
+            const int64_t tix = (mt * KBp + kb0 + i) * 32 + r;
+            xs2[tix] = p2[i];
+            xsx[tix] = px[i];
+        }
     }
 }
 

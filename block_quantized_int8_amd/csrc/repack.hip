@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void repack_q8_0_kernel(
                    ((uint32_t)q[4 * i + 3] << 24);
     }
     *reinterpret_cast<uint4*>(frag + gid * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    if (x.h == 0) scale[x.n * KBp + x.b] = d;            // f16 d | 0 << 16
+    if (x.h == 0) scale[(x.nt * KBp + x.b) * 32 + x.r] = d;            // f16 d | 0 << 16
 }
 
 __global__ __launch_bounds__(256) void repack_q4_0_kernel(
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void repack_q4_0_kernel(
         }
     }
     *reinterpret_cast<uint2*>(frag + gid * 8) = make_uint2(X0, X1);
-    if (x.h == 0) scale[x.n * KBp + x.b] = d;            // f16 d | 0 << 16
+    if (x.h == 0) scale[(x.nt * KBp + x.b) * 32 + x.r] = d;            // f16 d | 0 << 16
 }
 
 __global__ __launch_bounds__(256) void repack_q4_K_kernel(
@@ -121,8 +121,8 @@ __global__ __launch_bounds__(256) void repack_q4_K_kernel(
     }
     *reinterpret_cast<uint2*>(frag + gid * 8) = make_uint2(X0, X1);
     if (x.h == 0) {
-        scale[x.n * KBp + x.b] = ds2;
-        mins[x.n * KBp + x.b] = dm;
+        scale[(x.nt * KBp + x.b) * 32 + x.r] = ds2;
+        mins[(x.nt * KBp + x.b) * 32 + x.r] = dm;
     }
 }
 
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void repack_iq1t_kernel(
     }
     *reinterpret_cast<uint32_t*>(frag + gid * 4) = C;
     // scale dword of (row, block): f16 d | meta0 << 16 | meta1 << 24 (meta_h from lane half h)
-    uint8_t* e = scale + (x.n * KBp + x.b) * 4;
+    uint8_t* e = scale + ((x.nt * KBp + x.b) * 32 + x.r) * 4;
     if (x.h == 0) {
         *reinterpret_cast<uint16_t*>(e) = d;
         e[2] = (uint8_t)meta;

@@ -91,9 +91,11 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
  *                  inside it, row r = m%32 and k' = k%32 sit at ((k'/16)*32 + r)*16 + k'%16.
  *   region 1  xs   f32 [Mp][KBp], row-major: xs of (row m, block b) at m*KBp + b.
  *   region 2  xsum int32 [Mp][KBp], same indexing.
- *   region 3  xs2  uint32 [Mp][KBp]: xs as f16 bits in both 16-bit halves (xs is f16-exact by
- *                  construction); the operand form of the GEMM's scale outer product.
- *   region 4  xsx  f32 [Mp][KBp]: xs * xsum (exact in f32), the operand of the q4_K min term.
+ *   region 3  xs2  uint32, tile-major: (row m, block b) at ((m/32)*KBp + b)*32 + m%32; xs as
+ *                  f16 bits in both 16-bit halves (xs is f16-exact by construction); the
+ *                  operand form of the GEMM's scale outer product.
+ *   region 4  xsx  f32, tile-major like region 3: xs * xsum (exact in f32), the operand of
+ *                  the q4_K min term.
  *   Rows m >= M and blocks b >= KB hold zeros in every region.
  * MMQ_ACT_I8_TOKEN (two regions, each starting on a 256-byte boundary):
  *   region 0  a    int8, Mp*KBp*32 bytes, tiled exactly like region 0 of MMQ_ACT_Q8_1 (the

@@ -136,12 +136,13 @@ def test_act_to_host_layout_decoder(mmq):
             mt, b, kk = m // 32, k // 32, k % 32
             buf[o[0] + (mt * KBp + b) * 1024 + ((kk // 16) * 32 + m % 32) * 16 + kk % 16] = xq[m, k].view(np.uint8)
         for b in range(KB):
-            idx = 4 * (m * KBp + b)
+            idx = 4 * (m * KBp + b)                                  # regions 1, 2: row-major
+            tdx = 4 * (((m // 32) * KBp + b) * 32 + m % 32)          # regions 3, 4: tile-major
             h = int(np.float16(xs[m, b]).view(np.uint16))
             buf[o[1] + idx:o[1] + idx + 4] = np.frombuffer(xs[m, b].tobytes(), np.uint8)
             buf[o[2] + idx:o[2] + idx + 4] = np.frombuffer(xsum[m, b].tobytes(), np.uint8)
-            buf[o[3] + idx:o[3] + idx + 4] = np.frombuffer(np.uint32(h | (h << 16)).tobytes(), np.uint8)
-            buf[o[4] + idx:o[4] + idx + 4] = np.frombuffer(np.float32(xs[m, b] * xsum[m, b]).tobytes(), np.uint8)
+            buf[o[3] + tdx:o[3] + tdx + 4] = np.frombuffer(np.uint32(h | (h << 16)).tobytes(), np.uint8)
+            buf[o[4] + tdx:o[4] + tdx + 4] = np.frombuffer(np.float32(xs[m, b] * xsum[m, b]).tobytes(), np.uint8)
     a, s, u = mmq.act_to_host(buf, M, K)
     assert np.array_equal(a, xq) and np.array_equal(s, xs) and np.array_equal(u, xsum)
     lo, hi, xsx = mmq.act_derived_host(buf, M, K)

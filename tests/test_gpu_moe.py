@@ -108,6 +108,21 @@ def test_moe_workspace_reuse_and_determinism(env):
     _check_full(env, "iq1t", E, N, K, ids2, raw, rq, rs, b)
 
 
+@pytest.mark.parametrize("fmt", ["q4_0", "iq1t"])
+def test_moe_unit_boundaries(env, fmt):
+    # per-expert pair counts on both sides of the gather unit sizes (64-pair full units, tails
+    # of at most 32): 0, 31, 32, 33, 64, 65, 96, 97 pairs; top_k = 2, pairs in shuffled order
+    counts = [0, 31, 32, 33, 64, 65, 96, 97]
+    E, top_k, N, K = len(counts), 2, 160, 256
+    flat = np.repeat(np.arange(E, dtype=np.int32), counts)
+    assert flat.size % top_k == 0
+    np.random.default_rng(11).shuffle(flat)
+    T = flat.size // top_k
+    ids = flat.reshape(T, top_k)
+    raw, rq, rs, got = _moe(env, fmt, E, T, top_k, N, K, ids, seed=11)
+    _check_full(env, fmt, E, N, K, ids, raw, rq, rs, got)
+
+
 def test_moe_matches_dense_per_expert(env):
     # each pair's row equals the dense MMQ of its token against its expert, bit for bit
     torch, mmq, _ = env
