@@ -7,14 +7,15 @@
 // -fhip-fp32-correctly-rounded-divide-sqrt) and nothing is contracted, so the result is
 // bit-identical to the definition.
 //
-// Work split: one wave per (32-row tile, pair of blocks). Lane L = h*32 + r owns row r's values
-// 16h..16h+15 of each block - exactly the 16 bytes it writes to the tiled xq layout, so every
-// block's 1 KB tile is one contiguous wave store. The two lanes of a block (r and r+32) combine
-// their half-block max and sum with one cross-half exchange. Each row's two scale entries per
-// region are one 8-byte store (row-major regions): lane h = 0 writes xs and xsum, lane h = 1
-// the derived xs2 (f16 pair) and xsx = xs * xsum (exact in f32: an 11-bit significand times a
-// |sum| <= 32*128). Small units keep several waves per SIMD in flight, so one wave's loads
-// overlap another's arithmetic.
+// Work split: a unit is (32-row tile, pair of blocks); each wave walks several units, loading
+// the next one before it quantises and stores the current one, so loads and stores overlap
+// (with one unit per wave the whole grid would load, then store, in lockstep). In a unit, lane
+// L = h*32 + r owns row r's values 16h..16h+15 of each block - exactly the 16 bytes it writes
+// to the tiled xq layout, so every block's 1 KB tile is one contiguous wave store. The two
+// lanes of a block (r and r+32) combine their half-block max and sum with one cross-half
+// exchange. Lane h = 0 writes the row's xs and xsum pairs (row-major: one 8-byte store each),
+// lane h = 1 the derived xs2 (f16 pair) and xsx = xs * xsum (exact in f32: an 11-bit
+// significand times a |sum| <= 32*128; tile-major, the wave's 32 rows one 128-byte line).
 #include <algorithm>
 
 #include "mmq_internal.h"
@@ -23,6 +24,7 @@ namespace {
 
 constexpr int QG = 2;             // blocks per wave (one 32-row tile x 64 values)
 constexpr int QWAVES = 4;         // waves per workgroup
+constexpr int QBLOCKS = 1024;     // workgroups at most (four per CU); waves then loop over units
 
 __device__ inline uint32_t pack4(int a, int b, int c, int d) {
     return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
@@ -38,72 +40,82 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
     int8_t* __restrict__ xq, float* __restrict__ xs, int32_t* __restrict__ xsum,
     uint32_t* __restrict__ xs2, float* __restrict__ xsx) {
     const int lane = threadIdx.x & 63;
-    const int64_t u = (int64_t)blockIdx.x * QWAVES + (threadIdx.x >> 6);
+    const int64_t stride = (int64_t)gridDim.x * QWAVES;
+    int64_t u = (int64_t)blockIdx.x * QWAVES + (threadIdx.x >> 6);
     if (u >= units) return;                                 // uniform per wave
     const int64_t G = KBp / QG;
-    const int64_t mt = u / G, g = u % G;
     const int r = lane & 31, h = lane >> 5;
-    const int64_t m = mt * 32 + r;
-    const int64_t kb0 = g * QG;
-    const bool row_ok = m < M;
 
-    float4 v[QG][4];
-#pragma unroll
-    for (int i = 0; i < QG; ++i) {
-        const bool ok = row_ok && kb0 + i < KB;
-        const float* p = x + m * ldx + (kb0 + i) * 32 + 16 * h;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            v[i][c] = ok ? *reinterpret_cast<const float4*>(p + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    float s_xs[QG];
-    int s_sum[QG];
-#pragma unroll
-    for (int i = 0; i < QG; ++i) {
-        float amax = 0.f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i][c].x), fabsf(v[i][c].y)),
-                                     fmaxf(fabsf(v[i][c].z), fabsf(v[i][c].w))));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float d = amax / 127.0f;
-        const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
-        uint32_t w[4];
-        int s = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int a = q_of(v[i][c].x, di), b = q_of(v[i][c].y, di);
-            const int e = q_of(v[i][c].z, di), f = q_of(v[i][c].w, di);
-            s += a + b + e + f;
-            w[c] = pack4(a, b, e, f);
-        }
-        s += __shfl_xor(s, 32);
-        *reinterpret_cast<uint4*>(xq + ((mt * KBp + kb0 + i) * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-        s_xs[i] = (float)(_Float16)d;
-        s_sum[i] = s;
-    }
-
-    const int64_t row = (mt * 32 + r) * KBp + kb0;
-    if (h == 0) {
-        *reinterpret_cast<float2*>(xs + row) = make_float2(s_xs[0], s_xs[1]);
-        *reinterpret_cast<int2*>(xsum + row) = make_int2(s_sum[0], s_sum[1]);
-    } else {
-        uint32_t p2[QG];
-        float px[QG];
+    auto load = [&](int64_t uu, float4 (&v)[QG][4]) __attribute__((always_inline)) {
+        const int64_t mt = uu / G, kb0 = (uu % G) * QG;
+        const int64_t m = mt * 32 + r;
 #pragma unroll
         for (int i = 0; i < QG; ++i) {
-            const uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)s_xs[i]);
-            p2[i] = b | (b << 16);
-            px[i] = s_xs[i] * (float)s_sum[i];
+            const bool ok = m < M && kb0 + i < KB;
+            const float* p = x + m * ldx + (kb0 + i) * 32 + 16 * h;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                v[i][c] = ok ? *reinterpret_cast<const float4*>(p + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        // tile-major [MT][KBp][32]: the 32 rows of a block are one 128-byte line
+    };
+    auto process = [&](int64_t uu, const float4 (&v)[QG][4]) __attribute__((always_inline)) {
+        const int64_t mt = uu / G, kb0 = (uu % G) * QG;
+        float s_xs[QG];
+        int s_sum[QG];
 #pragma unroll
         for (int i = 0; i < QG; ++i) {
-            const int64_t tix = (mt * KBp + kb0 + i) * 32 + r;
-            xs2[tix] = p2[i];
-            xsx[tix] = px[i];
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i][c].x), fabsf(v[i][c].y)),
+                                         fmaxf(fabsf(v[i][c].z), fabsf(v[i][c].w))));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const float d = amax / 127.0f;
+            const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+            uint32_t w[4];
+            int sum = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int a = q_of(v[i][c].x, di), b = q_of(v[i][c].y, di);
+                const int e = q_of(v[i][c].z, di), f = q_of(v[i][c].w, di);
+                sum += a + b + e + f;
+                w[c] = pack4(a, b, e, f);
+            }
+            sum += __shfl_xor(sum, 32);
+            *reinterpret_cast<uint4*>(xq + ((mt * KBp + kb0 + i) * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            s_xs[i] = (float)(_Float16)d;
+            s_sum[i] = sum;
         }
+        if (h == 0) {
+            const int64_t row = (mt * 32 + r) * KBp + kb0;
+            *reinterpret_cast<float2*>(xs + row) = make_float2(s_xs[0], s_xs[1]);
+            *reinterpret_cast<int2*>(xsum + row) = make_int2(s_sum[0], s_sum[1]);
+        } else {
+            // tile-major [MT][KBp][32]: the 32 rows of a block are one 128-byte line
+#pragma unroll
+            for (int i = 0; i < QG; ++i) {
+                const int64_t tix = (mt * KBp + kb0 + i) * 32 + r;
+                const uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)s_xs[i]);
+                xs2[tix] = b | (b << 16);
+                xsx[tix] = s_xs[i] * (float)s_sum[i];
+            }
+        }
+    };
+
+    // each wave walks its units with the next unit's loads in flight while it quantises and
+    // stores the current one
+    float4 va[QG][4], vb[QG][4];
+    load(u, va);
+    for (;;) {
+        const int64_t u1 = u + stride;
+        if (u1 < units) load(u1, vb);
+        process(u, va);
+        if (u1 >= units) break;
+        const int64_t u2 = u1 + stride;
+        if (u2 < units) load(u2, va);
+        process(u1, vb);
+        if (u2 >= units) break;
+        u = u2;
     }
 }
 
@@ -159,7 +171,7 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ld
     const ActQ81Layout L = act_q8_1_layout(M, K);
     uint8_t* base = static_cast<uint8_t*>(act);
     const int64_t units = L.MT * (L.KBp / QG);
-    const dim3 grid((unsigned)ceil_div(units, QWAVES));
+    const dim3 grid((unsigned)std::min<int64_t>(ceil_div(units, QWAVES), QBLOCKS));
     hipLaunchKernelGGL(quantize_q8_1_kernel, grid, dim3(QWAVES * 64), 0, s, x, M, L.KB, ldx, L.KBp,
                        units, reinterpret_cast<int8_t*>(base + L.xq_off),
                        reinterpret_cast<float*>(base + L.xs_off),
