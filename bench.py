@@ -41,10 +41,16 @@ VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9   # non-packed f32 vector lane-ops per
 HEADLINE = "cfg2a_q4_0"
 METRIC = "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MFMA peak"
 
-# HBM bytes per launch of the dominant kernel, measured with rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE for the kernel version this file ships with and scaled by the copy-kernel factor
-# (profiles/ holds the summaries); None until measured for the current kernel.
-MEASURED_TRAFFIC_BYTES = {}
+# HBM bytes per launch of the dominant kernel (for MUL_MAT_ID: route + both gather launches),
+# measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE for the kernel version this file ships
+# with and scaled by the copy-kernel factor (profiles/ holds the summaries); absent (reported
+# as null) until measured for the current kernel.
+MEASURED_TRAFFIC_BYTES = {
+    "cfg2a_q4_0": 166249957,
+    "cfg3a_q4_K": 98540837,
+    "cfg4_w8a8": 60068437,
+    "cfg5_moe_iq1t": 387446793,
+}
 
 RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8}
 
