@@ -705,23 +705,35 @@ BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, 
     return g;
 }
 
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT>
+hipError_t launch_dense_cfg(BlockArgs g, int64_t M, int64_t N, mmq_otype o, void* out, hipStream_t s) {
+    const int tiles_n = (int)ceil_div(N, WN * RT * 32);
+    const int tiles_m = (int)ceil_div(M, WM * CT * 32);
+    g.tiles_m = tiles_m;
+    const dim3 grid((unsigned)((int64_t)tiles_n * tiles_m)), block(WN * WM * 64);
+    if (o == MMQ_OUT_I32_PARTIALS) {
+        g.partials = static_cast<int32_t*>(out);
+        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN, WM, RT, CT, DENSE_PARTIALS, XM_>), grid, block, 0, s, g);
+    } else {
+        g.out = static_cast<float*>(out);
+        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN, WM, RT, CT, DENSE_F32, XM_>), grid, block, 0, s, g);
+    }
+    return hipGetLastError();
+}
+
+// Dense tile shape: 128 x 128 while that gives the chip about two workgroups per CU; smaller
+// problems (few token or weight tiles, e.g. M = 512 with N = 4096) use 128 weight rows x 32
+// token slots (4 x 1 waves, one tile each) and four times the workgroups.
+constexpr int64_t DENSE_FILL = 448;
+
 template <mmq_wtype FMT>
 hipError_t launch_dense(const void* packed, const void* act, int64_t M, int64_t N, int64_t K,
                         mmq_otype o, void* out, int64_t ldo, hipStream_t s) {
     BlockArgs g = dense_args<FMT>(packed, act, M, N, K);
-    const int tiles_n = (int)ceil_div(N, WN_ * RT_ * 32);
-    const int tiles_m = (int)ceil_div(M, WM_ * CT_ * 32);
-    g.tiles_m = tiles_m;
     g.ldo = ldo;
-    const dim3 grid((unsigned)((int64_t)tiles_n * tiles_m)), block(WN_ * WM_ * 64);
-    if (o == MMQ_OUT_I32_PARTIALS) {
-        g.partials = static_cast<int32_t*>(out);
-        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_PARTIALS, XM_>), grid, block, 0, s, g);
-    } else {
-        g.out = static_cast<float*>(out);
-        hipLaunchKernelGGL((mmq_block_kernel<FMT, WN_, WM_, RT_, CT_, DENSE_F32, XM_>), grid, block, 0, s, g);
-    }
-    return hipGetLastError();
+    if (ceil_div(N, WN_ * RT_ * 32) * ceil_div(M, WM_ * CT_ * 32) >= DENSE_FILL)
+        return launch_dense_cfg<FMT, WN_, WM_, RT_, CT_>(g, M, N, o, out, s);
+    return launch_dense_cfg<FMT, GWN_, GWM_, GRT_, TCT_>(g, M, N, o, out, s);
 }
 
 template <mmq_wtype FMT>
@@ -757,15 +769,15 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
 // Pairs per full MUL_MAT_ID unit (one full-unit workgroup's token extent).
 int gather_unit_tokens() { return UNIT_ROWS; }
 
-// One-dimensional grids stay below 2^31 workgroups.
-constexpr int64_t MAX_GRID = int64_t(1) << 31;
+// A grid stays below 2^32 work-items: 2^24 workgroups of 256 threads.
+constexpr int64_t MAX_GRID = (int64_t(1) << 24) - 1;
 
-bool dense_grid_ok(int64_t M, int64_t N) {
-    return ceil_div(N, WN_ * RT_ * 32) * ceil_div(M, WM_ * CT_ * 32) < MAX_GRID;
+bool dense_grid_ok(int64_t M, int64_t N) {      // the larger of the two dense grids
+    return ceil_div(N, GWN_ * GRT_ * 32) * ceil_div(M, GWM_ * TCT_ * 32) <= MAX_GRID;
 }
 
 bool gather_grid_ok(int64_t max_units, int64_t N) {
-    return round_up(max_units, 8) * ceil_div(N, GWN_ * GRT_ * 32) < MAX_GRID;
+    return round_up(max_units, 8) * ceil_div(N, GWN_ * GRT_ * 32) <= MAX_GRID;
 }
 
 hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
