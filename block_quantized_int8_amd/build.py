@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmmq.so")
-SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "gemm_block.hip", "gemm_w8a8.hip", "gemm_id.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "gemm_block.hip", "gemm_w8a8.hip", "gemm_id.hip",
+           "gemm_mmvq.hip"]
 ARCH = os.environ.get("MMQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

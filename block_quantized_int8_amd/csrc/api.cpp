@@ -105,6 +105,10 @@ mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
         if (o == MMQ_OUT_I32_PARTIALS && M * N * (K / QK) > (int64_t(1) << 31)) return MMQ_EINVAL;
     }
     if (!aligned16(packed) || !aligned16(act) || !aligned16(out)) return MMQ_EALIGN;
+    // decode batches go to the split-K matrix-vector kernel; the debug partials stay on the
+    // prefill kernels
+    if (o != MMQ_OUT_I32_PARTIALS && M <= mmvq_max_tokens())
+        return from_hip(launch_mmvq(t, packed, act, M, N, K, out, ldo, as_stream(stream)));
     if (t == MMQ_I8_ROW) {
         if (!w8a8_grid_ok(M, N)) return MMQ_EINVAL;
         return from_hip(launch_w8a8_gemm(packed, act, M, N, K, o, out, ldo, as_stream(stream)));

@@ -155,6 +155,10 @@ int64_t gemm_id_max_units(int64_t E, int64_t P);
 bool w8a8_grid_ok(int64_t M, int64_t N);
 hipError_t launch_w8a8_gemm(const void* packed, const void* act, int64_t M, int64_t N, int64_t K,
                             mmq_otype o, void* out, int64_t ldo, hipStream_t s);
+// Decode batches (M <= mmvq_max_tokens()): f32 out for the block formats, bf16 for I8_ROW.
+int mmvq_max_tokens();
+hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
+                       int64_t K, void* out, int64_t ldo, hipStream_t s);
 hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
                           const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
                           void* out, void* workspace, size_t ws_bytes, hipStream_t s);

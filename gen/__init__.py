@@ -207,4 +207,14 @@ CONFIGS = {
     "cfg3b_q4_K": dict(cfg=3, fmt="q4_K", M=512, N=4096, K=14336, out="f32"),
     "cfg4_w8a8": dict(cfg=4, fmt="i8_row", M=3072, N=1536, K=4096, out="bf16"),
     "cfg5_moe_iq1t": dict(cfg=5, fmt="iq1t", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
+    # decode batches (a few tokens) on the same weight shapes: the small-M path
+    "dec1_q4_0": dict(cfg=2, fmt="q4_0", M=1, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec8_q4_0": dict(cfg=2, fmt="q4_0", M=8, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec16_q4_0": dict(cfg=2, fmt="q4_0", M=16, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec8_q4_0_ffn": dict(cfg=2, fmt="q4_0", M=8, N=11008, K=4096, out="f32", outlier_rate=1e-3),
+    "dec8_q8_0": dict(cfg=1, fmt="q8_0", M=8, N=4096, K=4096, out="f32"),
+    "dec8_q4_K": dict(cfg=3, fmt="q4_K", M=8, N=14336, K=4096, out="f32"),
+    "dec8_q4_K_down": dict(cfg=3, fmt="q4_K", M=8, N=4096, K=14336, out="f32"),
+    "dec8_iq1t": dict(cfg=5, fmt="iq1t", M=8, N=2048, K=4096, out="f32"),
+    "dec8_w8a8": dict(cfg=4, fmt="i8_row", M=8, N=1536, K=4096, out="bf16"),
 }

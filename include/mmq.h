@@ -143,7 +143,13 @@ mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const float* row_sca
  *         left untouched.
  *  ldo    >= N, in elements.
  * Supported (t, o): block formats with F32 or I32_PARTIALS; I8_ROW with BF16 or
- * I32_PARTIALS. */
+ * I32_PARTIALS.
+ * Dispatch: batches of M <= 16 token rows (F32 / BF16 output) run the small-batch split-K
+ * kernel, larger ones the prefill tiles (a decode batch would leave a prefill tile mostly
+ * empty; llama.cpp PR #304, Summary: small batches stay on a matrix-vector kernel). Both
+ * compute the same per-block integer dots; the small-batch kernel reads the zero padding
+ * rows M..31 of the activation buffer, so that padding must be zero (mmq_quantize_act
+ * writes it so). */
 mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                     int64_t K, mmq_otype o, void* out, int64_t ldo, void* stream);
 

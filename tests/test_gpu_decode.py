@@ -1,0 +1,193 @@
+"""GPU parity of the decode (small-batch) path against the CPU oracle, through the C ABI.
+
+mmq_gemm sends batches of M <= 16 token rows (f32 out for the block formats, bf16 for W8A8)
+to the split-K matrix-vector kernel; M = 17 goes back to the prefill tiles. The bars are the
+prefill ones: f32 outputs within max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition
+(minfer R1 section 4), W8A8 bf16 outputs bit-exact (metainfer section 3.1). Cases cover every
+live-register count (M = 1, 2, 3, 4 and M > 4), the largest batch (16), ragged N (a last
+16-row group that is partly or wholly padding), K whose block count is not a multiple of the
+kernel's 4-block chunk or of the 16 waves' share, ldo > N, and the full decode shapes the
+bench times, on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+import gen
+
+pytestmark = pytest.mark.gpu
+
+GATE = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import block_quantized_int8_amd as mmq
+    import oracle
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mmq.lib()
+    oracle.build()
+    return torch, mmq, oracle
+
+
+def _rel(got, ref):
+    return float(np.max(np.abs(got.astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def _case(env, fmt, M, N, K, seed, ldo=None, cfg=80, outlier=1e-2):
+    torch, mmq, orc = env
+    dev = torch.device("cuda:0")
+    print(f"[case] decode {fmt} M={M} N={N} K={K} ldo={ldo} seed={seed}", flush=True)
+    raw = gen.weights(fmt, N, K, seed=seed, cfg=cfg)
+    x = gen.act_f32(M, K, seed=seed, cfg=cfg, outlier_rate=outlier)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev))
+    packed = mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K)
+    L = ldo or N
+    out = torch.full((M, L), 7.0, dtype=torch.float32, device=dev)
+    mmq.gemm(fmt, packed, act, M, N, K, "f32", out=out, ldo=L)
+    torch.cuda.synchronize()
+    rq, rs, _ = orc.quantize_q8_1(x)
+    return raw, rq, rs, out.cpu().numpy(), (packed, act, out)
+
+
+# (N, K): K = 256 (8 blocks: two chunks, only two waves busy), 416 (13 blocks padded to 16),
+# 768 (24 blocks), 4096 (128 blocks: one 8-block share per wave); N with a ragged last group
+SMALL = [(32, 256), (48, 416), (33, 768), (300, 4096), (129, 1024)]
+SUPER = [(32, 256), (33, 768), (300, 4096), (129, 1024)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 16])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_K", "iq1t"])
+def test_decode_block_formats(env, fmt, M):
+    torch, mmq, orc = env
+    shapes = SMALL if fmt in ("q8_0", "q4_0") else SUPER
+    for i, (N, K) in enumerate(shapes):
+        raw, rq, rs, got, _ = _case(env, fmt, M, N, K, seed=100 * M + i)
+        ref = orc.gemm_f64(fmt, raw, N, K, rq, rs)
+        rel = _rel(got, ref)
+        print(f"  rel err {rel:.3e}", flush=True)
+        assert rel <= GATE, (fmt, M, N, K)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_K"])
+def test_decode_crossover_and_ldo(env, fmt):
+    # M = 16 (the decode kernel's largest batch) and M = 17 (the prefill tiles) on the same
+    # weights agree with the oracle; ldo > N leaves the row padding untouched
+    torch, mmq, orc = env
+    N, K, ldo = 80, 512, 100
+    for M in (16, 17):
+        raw, rq, rs, got, _ = _case(env, fmt, M, N, K, seed=7, ldo=ldo)
+        assert np.all(got[:, N:] == 7.0)
+        assert _rel(got[:, :N], orc.gemm_f64(fmt, raw, N, K, rq, rs)) <= GATE, M
+
+
+def test_decode_zero_and_padded_rows(env):
+    # a zero activation row gives exact zeros; the other rows keep the gate per row
+    torch, mmq, orc = env
+    M, N, K = 6, 64, 1024
+    dev = torch.device("cuda:0")
+    raw = gen.weights("q4_0", N, K, seed=3, cfg=81)
+    x = gen.act_f32(M, K, seed=3, cfg=81)
+    x[2] = 0
+    x[4] *= np.float32(1e-30)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev))
+    packed = mmq.repack_weights("q4_0", torch.from_numpy(raw).to(dev), N, K)
+    out = mmq.gemm("q4_0", packed, act, M, N, K, "f32")
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rq, rs, _ = orc.quantize_q8_1(x)
+    ref = orc.gemm_f64("q4_0", raw, N, K, rq, rs)
+    assert np.all(got[2] == 0)
+    for m in range(M):
+        if m == 2:
+            continue
+        den = max(np.max(np.abs(ref[m])), 1e-300)
+        assert np.max(np.abs(got[m] - ref[m])) / den <= GATE, m
+
+
+def test_decode_deterministic(env):
+    # the 16 waves' partial sums are added in a fixed order: repeated calls are bit-identical
+    torch, mmq, orc = env
+    raw, rq, rs, got, (packed, act, out) = _case(env, "q4_K", 9, 200, 4096, seed=11)
+    for _ in range(3):
+        again = mmq.gemm("q4_K", packed, act, 9, 200, 4096, "f32")
+        torch.cuda.synchronize()
+        assert np.array_equal(again.cpu().numpy(), got)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (3, 33, 96), (8, 97, 256), (16, 130, 544), (5, 64, 4096)])
+def test_decode_w8a8_bit_exact(env, M, N, K):
+    torch, mmq, orc = env
+    dev = torch.device("cuda:0")
+    a, sa = gen.i8_rows(M, K, seed=M + N, cfg=82, tensor=0)
+    w, sw = gen.i8_rows(N, K, seed=M + N, cfg=82, tensor=1)
+    print(f"[case] decode w8a8 M={M} N={N} K={K}", flush=True)
+    act = torch.from_numpy(mmq.act_i8_pack_host(a, sa)).to(dev)
+    packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
+                                row_scale=torch.from_numpy(sw).to(dev))
+    out = mmq.gemm("i8_row", packed, act, M, N, K, "bf16")
+    torch.cuda.synchronize()
+    ref_bf, _ = orc.gemm_w8a8(a, sa, w, sw, rows=(0, M), want_acc=True)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref_bf)
+
+
+@pytest.mark.parametrize("name", ["dec1_q4_0", "dec8_q4_0", "dec16_q4_0", "dec8_q4_0_ffn", "dec8_q8_0",
+                                  "dec8_q4_K", "dec8_q4_K_down", "dec8_iq1t"])
+def test_decode_full_size(env, name):
+    # the decode workloads in the bench's launch configuration: every token row in full
+    # against the f64 definition on 512 sampled weight rows (plus the first and last)
+    torch, mmq, orc = env
+    c = gen.CONFIGS[name]
+    fmt, M, N, K = c["fmt"], c["M"], c["N"], c["K"]
+    dev = torch.device("cuda:0")
+    print(f"[case] {name}: {fmt} M={M} N={N} K={K}", flush=True)
+    raw = gen.weights(fmt, N, K, seed=0, cfg=c["cfg"])
+    x = gen.act_f32(M, K, seed=0, cfg=c["cfg"], outlier_rate=c.get("outlier_rate", 0.0))
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev))
+    packed = mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K)
+    out = mmq.gemm(fmt, packed, act, M, N, K, "f32")
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rq, rs, _ = orc.quantize_q8_1(x)
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N + M).choice(N, 512, replace=False)]))
+    ref = orc.gemm_f64(fmt, raw, N, K, rq, rs, cols=cols)
+    rel = _rel(got[:, cols], ref)
+    print(f"  rel err {rel:.3e}", flush=True)
+    assert rel <= GATE
+
+
+def test_decode_w8a8_full_size(env):
+    torch, mmq, orc = env
+    c = gen.CONFIGS["dec8_w8a8"]
+    M, N, K = c["M"], c["N"], c["K"]
+    dev = torch.device("cuda:0")
+    a, sa = gen.i8_rows(M, K, seed=0, cfg=c["cfg"], tensor=gen.T_ACT)
+    w, sw = gen.i8_rows(N, K, seed=0, cfg=c["cfg"], tensor=gen.T_WEIGHT)
+    print(f"[case] dec8_w8a8 M={M} N={N} K={K}", flush=True)
+    act = torch.from_numpy(mmq.act_i8_pack_host(a, sa)).to(dev)
+    packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
+                                row_scale=torch.from_numpy(sw).to(dev))
+    out = mmq.gemm("i8_row", packed, act, M, N, K, "bf16")
+    torch.cuda.synchronize()
+    ref_bf, _ = orc.gemm_w8a8(a, sa, w, sw, rows=(0, M), want_acc=True)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref_bf)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_K", "iq1t", "q8_0"])
+@pytest.mark.parametrize("M", [1, 7])
+def test_decode_persistent_groups(env, fmt, M):
+    # more 16-row groups than workgroups (N > 16 x compute units): workgroups loop over groups
+    # with loads running ahead across group boundaries; K = 768 leaves most waves without a
+    # chunk (they only reduce), K = 4352 gives waves unequal chunk counts (34 chunks, 16 waves)
+    torch, mmq, orc = env
+    for K in (768, 4352):
+        N = 16 * 256 + 53
+        raw, rq, rs, got, _ = _case(env, fmt, M, N, K, seed=M + K)
+        cols = np.unique(np.concatenate([np.arange(0, 64), np.arange(N - 80, N),
+                                         np.random.default_rng(K).choice(N, 256, replace=False)]))
+        ref = orc.gemm_f64(fmt, raw, N, K, rq, rs, cols=cols)
+        rel = _rel(got[:, cols], ref)
+        print(f"  K={K} rel err {rel:.3e}", flush=True)
+        assert rel <= GATE, K
