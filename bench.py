@@ -1,4 +1,4 @@
-"""Benchmark of the prefill MMQ hot path on one MI355X.
+"""Benchmark of the MMQ hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch: quantise the f32 activations to q8_1
 (a1) and run the MMQ contraction with the raw block weights (a3-a6; for MoE the device-side
@@ -9,17 +9,32 @@ the timed region starts.
 Default workload: q4_0 weights N=4096 x K=4096 from N(0,0.02), activations M=2048 x K=4096
 from N(0,1) with 0.1% outliers x20, f32 output - the q4_0 prefill shape of the MMQ pages'
 7B-class models. `--workload` selects another of gen.CONFIGS for reference measurements (the
-W8A8 workload's activations are int8 already, so its step is the GEMM alone).
+W8A8 workload's activations are int8 already, so its step is the GEMM alone; the dec*
+workloads are decode batches of 1-16 tokens on the same weight shapes).
+
+Timing (the pages' protocol: warm-up, then 30 samples of 100 back-to-back launches (or a
+hipGraph replay) timed with hipEvents, median and min/max spread; P2 section 3.3):
+  step time     one step is captured in a hipGraph and replayed --steps times (with rotating
+                weight copies, all --steps steps are captured in one graph and replayed once)
+                between two synchronisations; value = 2*M*N*K / step time. The graph keeps
+                host launch cost out of the GPU timeline.
+  kernel times  per kernel, a hipGraph of 100 back-to-back launches replayed 30 times, each
+                replay bracketed by HIP events on the launch stream: 30 samples of the average
+                launch duration (mean, median, min, max reported).
+  cold MALL     --rotate R cycles R copies of the packed weights through the launches so every
+                launch reads its weights from HBM rather than the 256 MB last-level cache
+                (default for the decode workloads: enough copies for >= 1 GB).
 
 Prints ONE JSON line on stdout:
   value         whole-step throughput, TOPS = 2*M*N*K / step time (2*T*top_k*N*K for MoE)
   roofline      the dominant kernel alone: algorithmic ops (or bytes) per launch / its mean
-                launch time (HIP events on the launch stream, over the timed steps) against the
-                MI355X dense int8 MFMA peak (5.0 POP/s) or HBM peak (8 TB/s); traffic = HBM
-                bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters scaled by the
-                copy-kernel calibration, when measured for this exact kernel, else null
+                event-timed launch time against the MI355X dense int8 MFMA peak (5.0 POP/s)
+                or the HBM peak (8 TB/s, decode and MoE); traffic = HBM bytes per launch from
+                rocprofv3 FETCH_SIZE + WRITE_SIZE counters scaled by the copy-kernel
+                calibration, when measured for this exact kernel and workload, else null
   cpu_baseline  the CPU oracle (quantiser + per-block integer GEMM in C, OpenMP) timed on this
-                host's cores, repeated over the workload for a bounded ~10 s
+                host's cores, repeated over the workload for a bounded ~10 s, plus one short
+                single-thread pass
 Diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -27,6 +42,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -40,6 +57,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9   # non-packed f32 vector lane-ops per second
 HEADLINE = "cfg2a_q4_0"
 METRIC = "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MFMA peak"
+DECODE_MAX_M = 16                # mmq_gemm runs batches up to this many rows on the decode kernel
+COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at least this much
 
 # HBM bytes per launch of the dominant kernel (for MUL_MAT_ID: route + both gather launches),
 # measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE for the kernel version this file ships
@@ -52,35 +71,64 @@ MEASURED_TRAFFIC_BYTES = {
     "cfg5_moe_iq1t": 387446793,
 }
 
-RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8}
+RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "i8_row": 32}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def sclk_mhz():
+    """Current shader clock from rocm-smi (a child process), or None."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        m = re.findall(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", r.stdout, flags=re.I)
+        return int(m[0]) if m else None
+    except Exception:
+        return None
+
+
+def _oracle_env():
+    return {"os_cpu_count": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(fmt, raw, x, M, N, K, budget_s=10.0, min_runs=3, max_runs=50):
     """The oracle as it stands, timed on the host: q8_1 quantisation + per-block C GEMM over
-    the whole workload, repeated until about `budget_s` seconds of CPU work (median reported)."""
+    the whole workload, repeated until about `budget_s` seconds of CPU work (median reported),
+    then one single-thread pass over the first rows."""
     import oracle
     oracle.build()
+
+    def run(rows):
+        if fmt == "i8_row":
+            a, sa, w, sw = x
+            oracle.gemm_w8a8(a[:rows], sa[:rows], w, sw)
+        else:
+            xq, xs, xsum = oracle.quantize_q8_1(x[:rows])
+            oracle.gemm_c(fmt, raw, N, K, xq, xs, xsum)
+
     times = []
     t_start = time.perf_counter()
     while len(times) < min_runs or (time.perf_counter() - t_start < budget_s and len(times) < max_runs):
         t0 = time.perf_counter()
-        if fmt == "i8_row":
-            a, sa, w, sw = x
-            oracle.gemm_w8a8(a, sa, w, sw)
-        else:
-            xq, xs, xsum = oracle.quantize_q8_1(x)
-            oracle.gemm_c(fmt, raw, N, K, xq, xs, xsum)
+        run(M)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
+    cores = oracle.num_threads()
+    # single-thread pass on a row sample sized to about a second at the multi-thread rate
+    rows1 = int(max(1, min(M, round(M * 1.0 / max(t * cores, 1e-9)))))
+    oracle.set_threads(1)
+    t0 = time.perf_counter()
+    run(rows1)
+    t1 = time.perf_counter() - t0
+    oracle.set_threads(cores)
     what = "W8A8 int GEMM + bf16 epilogue" if fmt == "i8_row" else "quantize_q8_1 + per-block C GEMM"
-    return {"value": 2.0 * M * N * K / t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    return {"value": 2.0 * M * N * K / t / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": f"full workload (M={M}, N={N}, K={K}) repeated {len(times)}x "
-                      f"({sum(times):.1f} s of CPU work), median {t:.3f} s per run of {what}"}
+                      f"({sum(times):.1f} s of CPU work), median {t:.3f} s per run of {what}",
+            "single_thread": {"value": 2.0 * rows1 * N * K / t1 / 1e12, "unit": "TOPS",
+                              "sample": f"first {rows1} rows, one run, {t1:.2f} s"},
+            **_oracle_env()}
 
 
 def cpu_baseline_moe(raw_e, x, ids, E, N, K, budget_s=10.0):
@@ -104,27 +152,65 @@ def cpu_baseline_moe(raw_e, x, ids, E, N, K, budget_s=10.0):
     ops = 2.0 * rows_done * N * K
     return {"value": ops / t_used / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{experts} of {E} experts ({rows_done} routed token rows) through the per-block "
-                      f"C GEMM, {t_used:.1f} s"}
+                      f"C GEMM, {t_used:.1f} s", **_oracle_env()}
 
 
-def timed(step_fn, steps, warmup, nev):
-    """Wall clock over exactly `steps` steps (synchronised both sides), then the same number of
-    steps again with HIP events around each launch for per-kernel durations."""
+def _graph(fns, n):
+    """A hipGraph of n calls cycling through fns (each launches on the current stream)."""
     import torch
-    for _ in range(warmup):
-        step_fn(None)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                         # warm the capture stream outside capture
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fns[i % len(fns)]()
+    return g
+
+
+def timed(kernels, n_rot, steps, warmup, samples=30, per_sample=100):
+    """kernels: [(name, fn(r))] launched in this order make one step on weight copy r.
+    Step time: a hipGraph of one step replayed `steps` times (with rotating copies, one graph of
+    all `steps` steps, replayed once) between two synchronisations. Kernel times: per kernel, a
+    hipGraph of `per_sample` back-to-back launches replayed `samples` times, each replay
+    bracketed by HIP events on the launch stream. Returns (step seconds, {name: samples [s]})."""
+    import torch
+    def step(r):
+        for _, f in kernels:
+            f(r)
+    for i in range(warmup):
+        step(i % n_rot)
+    torch.cuda.synchronize()
+    per_graph = 1 if n_rot == 1 else steps
+    g = _graph([lambda r=r: step(r) for r in range(n_rot)], per_graph)
+    g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step_fn(None)
+    for _ in range(steps // per_graph):
+        g.replay()
     torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
-    for i in range(steps):
-        step_fn(evs[i])
-    torch.cuda.synchronize()
-    spans = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nev - 1)] for e in evs]) * 1e-3
-    return step_s, spans.mean(axis=0), np.median(spans, axis=0)
+    step_s = (time.perf_counter() - t0) / (steps // per_graph * per_graph)
+    del g
+    kt = {}
+    for name, f in kernels:
+        g = _graph([lambda r=r, f=f: f(r) for r in range(n_rot)], per_sample)
+        g.replay()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(samples):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e-3 / per_sample)
+        kt[name] = np.array(res)
+        del g
+    return step_s, kt
 
 
 def main():
@@ -133,6 +219,9 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=HEADLINE, help="one of gen.CONFIGS")
+    ap.add_argument("--rotate", type=int, default=-1,
+                    help="weight copies cycled through the steps (cold MALL); default: 1, or enough "
+                         "for >= 1 GB on the decode workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy 5x (counter calibration)")
@@ -149,105 +238,106 @@ def main():
     name = args.workload
     cfg = gen.CONFIGS[name]
     fmt, M, N, K = cfg["fmt"], cfg["M"], cfg["N"], cfg["K"]
+    moe = "E" in cfg
+    decode = not moe and M <= DECODE_MAX_M
     dev = torch.device("cuda:0")
     log(f"[bench] workload {name}: {fmt} M={M} N={N} K={K}")
     ops = 2.0 * M * N * K
     extra = {}
 
+    def copies_of(t):
+        if args.rotate > 0:
+            n = args.rotate
+        elif args.rotate == 0 or not decode:
+            n = 1
+        else:
+            n = max(3, -(-COLD_BYTES // t.numel()))
+        return [t] + [t.clone() for _ in range(n - 1)]
+
     if fmt == "i8_row":
         a, sa = gen.i8_rows(M, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_ACT)
         w, sw = gen.i8_rows(N, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_WEIGHT)
-        packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
-                                    row_scale=torch.from_numpy(sw).to(dev))
+        packed = copies_of(mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
+                                              row_scale=torch.from_numpy(sw).to(dev)))
         act = torch.from_numpy(mmq.act_i8_pack_host(a, sa)).to(dev)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-        def step(ev):
-            if ev is not None:
-                ev[0].record()
-            mmq.gemm("i8_row", packed, act, M, N, K, "bf16", out=out)
-            if ev is not None:
-                ev[1].record()
-        nev, kernel_names = 2, ["w8a8_gemm"]
+        kernels = [("mmvq (decode)" if decode else "w8a8_gemm",
+                    lambda r: mmq.gemm("i8_row", packed[r], act, M, N, K, "bf16", out=out))]
         dom = 0
         alg_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
-        bound = "mfma"
         cpu_args = ("i8_row", None, (a, sa, w, sw), M, N, K)
-    elif "E" in cfg:
+    elif moe:
         E, top_k = cfg["E"], cfg["top_k"]
         T = M
         raw_e = gen.moe_weights(fmt, E, N, K, seed=0, cfg=cfg["cfg"])
         x = gen.act_f32(T, K, seed=0, cfg=cfg["cfg"])
         ids = gen.moe_ids(T, top_k, E, seed=0, cfg=cfg["cfg"])
         pb = mmq.packed_bytes(fmt, N, K)
-        packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
+        p0 = torch.empty(E * pb, dtype=torch.uint8, device=dev)
         for e in range(E):
             mmq.repack_weights(fmt, torch.from_numpy(np.ascontiguousarray(raw_e[e])).to(dev), N, K,
-                               out=packed[e * pb:(e + 1) * pb])
+                               out=p0[e * pb:(e + 1) * pb])
+        packed = copies_of(p0)
         xd = torch.from_numpy(x).to(dev)
         ids_d = torch.from_numpy(ids).to(dev)
         act = torch.empty(mmq.act_bytes("q8_1", T, K), dtype=torch.uint8, device=dev)
         out = torch.empty((T, top_k, N), dtype=torch.float32, device=dev)
         ws = torch.empty(mmq.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
 
-        def step(ev):
-            if ev is not None:
-                ev[0].record()
-            mmq.quantize_act(xd, out=act)
-            if ev is not None:
-                ev[1].record()
-            mmq.gemm_id(fmt, packed, E, act, ids_d, T, top_k, N, K, out=out, workspace=ws)
-            if ev is not None:
-                ev[2].record()
-        nev, kernel_names = 3, ["quantize_q8_1", "gemm_id (route + gather MMQ)"]
+        kernels = [("quantize_q8_1", lambda r: mmq.quantize_act(xd, out=act)),
+                   ("gemm_id (route + gather MMQ)",
+                    lambda r: mmq.gemm_id(fmt, packed[r], E, act, ids_d, T, top_k, N, K, out=out, workspace=ws))]
         dom = 1
         ops = 2.0 * T * top_k * N * K
         used = len(np.unique(ids))
         alg_bytes = int(used * N * K / 32 * RAW_BYTES_PER_32[fmt]) + T * K + T * (K // 32) * 8 + \
             T * top_k * N * 4 + T * top_k * 4
-        bound = "hbm"
         cpu_args = None
         extra = {"E": E, "top_k": top_k, "experts_used": used}
     else:
         raw = gen.weights(fmt, N, K, seed=0, cfg=cfg["cfg"])
         x = gen.act_f32(M, K, seed=0, cfg=cfg["cfg"], outlier_rate=cfg.get("outlier_rate", 0.0))
         xd = torch.from_numpy(x).to(dev)
-        packed = mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K)
+        packed = copies_of(mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K))
         act = torch.empty(mmq.act_bytes("q8_1", M, K), dtype=torch.uint8, device=dev)
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
 
-        def step(ev):
-            if ev is not None:
-                ev[0].record()
-            mmq.quantize_act(xd, out=act)
-            if ev is not None:
-                ev[1].record()
-            mmq.gemm(fmt, packed, act, M, N, K, "f32", out=out)
-            if ev is not None:
-                ev[2].record()
-        nev, kernel_names = 3, ["quantize_q8_1", "mmq_block"]
+        kernels = [("quantize_q8_1", lambda r: mmq.quantize_act(xd, out=act)),
+                   ("mmvq (decode)" if decode else "mmq_block",
+                    lambda r: mmq.gemm(fmt, packed[r], act, M, N, K, "f32", out=out))]
         dom = 1
         # raw weights + q8_1 activations (int8 values, f32 scale, int32 sum) + f32 output
         alg_bytes = int(N * K / 32 * RAW_BYTES_PER_32[fmt]) + M * K + M * (K // 32) * 8 + M * N * 4
-        bound = "mfma"
         cpu_args = (fmt, raw, x, M, N, K)
+    n_rot = len(packed)
+    bound = "hbm" if (moe or decode) else "mfma"
+    if n_rot > 1:
+        extra["weight_copies_rotated"] = n_rot
+        extra["weight_bytes_rotated"] = int(n_rot * packed[0].numel())
 
     torch.cuda.synchronize()
-    step_s, mean_s, med_s = timed(step, args.steps, args.warmup, nev)
+    step_s, kt = timed(kernels, n_rot, args.steps, args.warmup)
+    sclk = sclk_mhz()
     tops = ops / step_s / 1e12
-    for i, kn in enumerate(kernel_names):
-        log(f"[bench] {kn}: mean {mean_s[i] * 1e6:.2f} us, median {med_s[i] * 1e6:.2f} us")
-    k_s = float(mean_s[dom])
+    kstats = []
+    for kn, _ in kernels:
+        c = kt[kn]
+        kstats.append({"mean": float(c.mean()), "median": float(np.median(c)), "min": float(c.min()),
+                       "max": float(c.max())})
+        log(f"[bench] {kn}: per launch mean {c.mean() * 1e6:.3f} us, median {np.median(c) * 1e6:.3f} us, "
+            f"min {c.min() * 1e6:.3f}, max {c.max() * 1e6:.3f} (30 samples x 100 launches)")
+    k_s = kstats[dom]["mean"]
     k_tops = ops / k_s / 1e12
     k_gbs = alg_bytes / k_s / 1e9
-    log(f"[bench] step {step_s * 1e6:.1f} us ({tops:.1f} TOPS, {100 * tops / INT8_PEAK_TOPS:.1f}% int8 peak); "
-        f"dominant kernel {k_s * 1e6:.1f} us = {k_tops:.1f} TOPS ({100 * k_tops / INT8_PEAK_TOPS:.1f}% int8), "
-        f"{k_gbs:.0f} GB/s algorithmic ({100 * k_gbs / HBM_PEAK_GBS:.1f}% HBM)")
-    if nev == 3 and dom == 1:
+    log(f"[bench] step {step_s * 1e6:.2f} us ({tops:.1f} TOPS, {100 * tops / INT8_PEAK_TOPS:.1f}% int8 peak); "
+        f"dominant kernel {k_s * 1e6:.2f} us = {k_tops:.1f} TOPS ({100 * k_tops / INT8_PEAK_TOPS:.1f}% int8), "
+        f"{k_gbs:.0f} GB/s algorithmic ({100 * k_gbs / HBM_PEAK_GBS:.1f}% HBM); sclk {sclk} MHz")
+    if len(kernels) == 2:
         q_bytes = M * K * 4 + mmq.act_bytes("q8_1", M, K)
-        q_s = float(mean_s[0])
+        q_s = kstats[0]["mean"]
         log(f"[bench] quantize {q_bytes / q_s / 1e9:.0f} GB/s ({100 * q_bytes / q_s / 1e9 / HBM_PEAK_GBS:.1f}% HBM)")
-        extra["quantize_kernel_us"] = round(q_s * 1e6, 2)
+        extra["quantize_kernel_us"] = round(q_s * 1e6, 3)
 
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(k_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
@@ -255,16 +345,16 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4)}
-    if fmt != "i8_row":
+    if fmt != "i8_row" and not decode:
         # the per-block scale application: >= 2 vector ops (exact conversion + FMA) per
         # element-block E = rows * N * K/32, against 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
         rows = M * cfg.get("top_k", 1)
         E = rows * N * (K // 32)
         roof["valu_ceiling"] = {"ops_per_element_block": 2, "peak_lane_ops": VALU_PEAK_LANE_OPS,
                                 "frac": round(2.0 * E / k_s / VALU_PEAK_LANE_OPS, 4)}
-    roof["traffic"] = MEASURED_TRAFFIC_BYTES.get(name)
-    roof["kernel"] = kernel_names[dom]
-    roof["kernel_us"] = round(k_s * 1e6, 2)
+    roof["traffic"] = MEASURED_TRAFFIC_BYTES.get(name) if n_rot == 1 or name.startswith("dec") else None
+    roof["kernel"] = kernels[dom][0]
+    roof["kernel_us"] = {k: round(v * 1e6, 3) for k, v in kstats[dom].items()}
     roof["algorithmic_bytes"] = alg_bytes
     roof["algorithmic_ops"] = ops
 
@@ -280,12 +370,12 @@ def main():
                           "(quantised in-step), f32 out"}
     rec = {
         "metric": METRIC if name == HEADLINE else f"MMQ TOPS (2MNK/s) on {name}",
-        "value": round(tops, 2),
+        "value": round(tops, 3),
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 5),
+        "ms_per_step": round(step_s * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -294,9 +384,11 @@ def main():
         "config": {"workload": desc.get(name, name), "M": M, "N": N, "K": K, "weights": fmt,
                    "activations": "i8_token" if fmt == "i8_row" else "q8_1",
                    "step": "gemm (int8 activations given)" if fmt == "i8_row" else
-                           "quantize_act + gemm" + ("_id" if "E" in cfg else "") + " (repack untimed)",
+                           "quantize_act + gemm" + ("_id" if moe else "") + " (repack untimed)",
+                   "timing": "hipGraph replay of the step; kernels: 30 samples x 100 graph-replayed launches, hipEvents",
                    **extra},
-        "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+        "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 3),
+        "sclk_mhz_after_run": sclk,
         "roofline": roof,
     }
     if not args.no_cpu:

@@ -7,26 +7,31 @@
 // a batch of a few tokens: a decode-shaped problem wastes all but one row of a 16-token
 // matrix fragment (minfer "08 . R1", section 2.1), and llama.cpp keeps such batches (n <= 8)
 // on a separate matrix-vector kernel, MMVQ ("CUDA: add IQ1_M to MMQ", PR #304, Summary). With
-// so few tokens the work is bound by one pass over the weights, and the kernel is built for
-// that:
-//  * a workgroup owns 16 weight rows and its 16 waves split the blocks of K (chunks of 4
-//    blocks dealt round-robin), so N = 4096 already gives 256 workgroups of 16 waves; a wave
-//    keeps one chunk's loads in flight while it computes the previous one;
-//  * every lane loads its operands straight from the packed panels into registers (no LDS
-//    staging): the weight side of v_mfma_i32_16x16x32_i8 is 8 values of one row, which the
-//    packed fragment keeps contiguous;
-//  * tokens are the A side, so accumulator register v of lane l holds token 4*(l/16) + v and
-//    row l%16 (the 16x16 accumulator lane map); with M <= 4 only registers v < M hold tokens
-//    and only those are rescaled;
-//  * per block: the exact int32 dot P (two chained MFMAs for iq1t's folded per-16 factor, as
-//    in the prefill kernel), the scale product S = xs * wd from one f16 MFMA (exact: a product
-//    of two f16; q4_K's d*sc arrives as an exact f16 pair), then acc += f32(P) * S on the live
-//    registers. q4_K adds its rank-1 min term -(dmin*m) * (xs*xsum) four blocks at a time with
-//    one f32 MFMA (minfer R1 section 2.2). W8A8 has no per-block scale: its int32 accumulator
-//    runs through the whole of K and the epilogue applies the two per-row scales (metainfer
-//    "INT8 W8A8 GEMM - Prefill", section 1);
-//  * the 16 waves' partial sums meet in LDS and are added in wave order: deterministic, with
-//    no atomics and no workspace.
+// so few tokens the work is one pass over the weights, and on gfx950 such a pass is bound by
+// the number of vector-memory instructions per byte long before HBM is (a per-lane 4-byte
+// load of scattered fragments moved ~80 useful bytes per instruction; plain streaming reads
+// need ~250). The kernel is built around that:
+//  * one v_mfma_i32_16x16x64_i8 covers a PAIR of blocks: its k-groups 0-1 carry block 2p and
+//    k-groups 2-3 block 2p+1, so every lane loads one whole packed fragment lane (16 int8
+//    values: 16 bytes of q8_0 / activations, 8 of q4_0 / q4_K, 4 of iq1t codes);
+//  * the token side is block-diagonal: output rows 0-7 are tokens 0-7 against the first block
+//    (their A operand is zero in k-groups 2-3), rows 8-15 the same tokens against the second
+//    (zero in k-groups 0-1). So each block's integer dot stays exact and separate - no two
+//    scales share an accumulator - and the zeros come from loads whose offset lies past the
+//    buffer descriptor's range (the hardware returns 0 without a memory access), not from
+//    extra instructions. Rows t and t+8 are added in the final reduction. Batches of 9-16
+//    tokens run a second such operand for tokens 8-15;
+//  * the scale product S = xs * wd comes from one f16 MFMA per pair (exact: a product of two
+//    f16; q4_K's d*sc arrives as an exact f16 pair): the weight scales of four blocks are
+//    loaded at once, block b0+g in k-group g, and the token scale of the pair's first block
+//    feeds rows 0-7 through k-group 2p, the second's rows 8-15 through k-group 2p+1. Then
+//    acc += f32(P) * S on the live registers. q4_K adds its rank-1 min term -(dmin*m) *
+//    (xs*xsum) four blocks at a time with one f32 MFMA (minfer R1 section 2.2). W8A8 has no
+//    per-block scale: its int32 accumulator runs through the whole of K and the epilogue
+//    applies the two per-row scales (metainfer "INT8 W8A8 GEMM - Prefill", section 1);
+//  * persistent workgroups own 16-row weight groups; their 16 waves split the blocks of K
+//    (chunks of 4 blocks dealt round-robin) and keep two chunks' loads in flight, across
+//    group boundaries; the waves' partial sums meet in LDS and are added in a fixed order.
 #include <algorithm>
 
 #include "gemm_common.h"
@@ -39,20 +44,16 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int MV_W = 16;          // waves per workgroup (they split the blocks of K)
-constexpr int MV_CH = 4;          // blocks per chunk: the unit of a wave's loads
-constexpr int MV_ROWS = 16;       // weight rows per workgroup
+constexpr int MV_CH = 4;          // blocks per chunk: two MFMA pairs, one scale load
+constexpr int MV_ROWS = 16;       // weight rows per workgroup group
+constexpr int MV_TOK = 16;        // largest batch
 static_assert(KB_ALIGN % MV_CH == 0, "chunks tile the padded block count");
-static_assert(MV_CH % 4 == 0, "the q4_K min term takes four blocks per MFMA");
-
-__device__ inline long pk2(uint32_t lo, uint32_t hi) {
-    return (long)(((uint64_t)hi << 32) | (uint64_t)lo);
-}
 
 // Buffer loads: a wave-uniform descriptor (base, byte range) in scalar registers plus a 32-bit
-// lane offset; the hardware returns zero past the range, and no vector registers go to 64-bit
-// address arithmetic (which would tie them to loads still in flight).
+// lane offset; the hardware returns zero for an offset past the range, without a memory access.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int RSRC_W3 = 0x00020000;        // descriptor word 3: raw 32-bit data format (gfx9)
+constexpr uint32_t OOR = 0x40000000u;      // a lane offset past every range used here
 __device__ inline rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, RSRC_W3);
 }
@@ -63,6 +64,11 @@ __device__ inline uint2 ld64(rsrc_t r, uint32_t off) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
     return make_uint2(v[0], v[1]);
 }
+__device__ inline v4i ld128(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    const v4i o = {(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+    return o;
+}
 
 // an f16x4 operand with the dword `lo` in slots 0-1 and zeros in slots 2-3
 __device__ inline h4 as_h4(uint32_t lo) {
@@ -70,20 +76,18 @@ __device__ inline h4 as_h4(uint32_t lo) {
     return __builtin_bit_cast(h4, t);
 }
 
-// Per weight format: where lane (row n of the tile, k-group g) finds its 8 values 8g..8g+7 of
-// a block inside the (tile, block) fragment, how they become int8 MFMA operands, and the power
-// of two the integer dot carries (POST undoes it).
+// Per weight format: the bytes of one packed fragment lane (row r, values 16h..16h+15 of a
+// block), how they become the 16-byte int8 operand(s) in value order, and the power of two the
+// integer dot carries (POST undoes it).
 template <mmq_wtype FMT> struct VQ;
 
-// q8_0: lane h*32 + r of the fragment holds row r's int8 values 16h..16h+15.
 template <> struct VQ<MMQ_Q8_0> {
     static constexpr int FB = 1024, NMF = 1;
-    static constexpr bool MIN = false, ROW = false;
+    static constexpr bool MIN = false, ROW = false, META = false;
     static constexpr float POST = 1.0f;
-    typedef uint2 Raw;
-    __device__ static int off(int n, int g) { return ((g >> 1) * 32 + n) * 16 + (g & 1) * 8; }
-    __device__ static Raw load(rsrc_t r, uint32_t off) { return ld64(r, off); }
-    __device__ static void ops(Raw r, uint32_t, int, const uint2*, long* b) { b[0] = pk2(r.x, r.y); }
+    typedef v4i Raw;
+    __device__ static Raw load(rsrc_t r, uint32_t off) { return ld128(r, off); }
+    __device__ static void ops(Raw r, uint32_t, const uint2*, v4i* b) { b[0] = r; }
     __device__ static uint32_t scale_op(uint32_t w) { return w; }
 };
 
@@ -92,59 +96,69 @@ template <> struct VQ<MMQ_I8_ROW> : VQ<MMQ_Q8_0> {
     static constexpr bool ROW = true;
 };
 
-// q4_0: 8 bytes per fragment lane; dword X(g&1) holds the lane's 8 values as the 4-bit two's
-// complement of nib - 8 (values +0..3 in the high nibbles, +4..7 in the low ones), so the
-// masked bytes are int8 16*(nib-8).
+// q4_0: X0 holds values 0-3 in its high nibbles and 4-7 in its low ones (X1: 8-15), each the
+// 4-bit two's complement of nib - 8, so the masked bytes are int8 16*(nib-8).
 template <> struct VQ<MMQ_Q4_0> {
     static constexpr int FB = 512, NMF = 1;
-    static constexpr bool MIN = false, ROW = false;
+    static constexpr bool MIN = false, ROW = false, META = false;
     static constexpr float POST = 1.0f / 16;
-    typedef uint32_t Raw;
-    __device__ static int off(int n, int g) { return ((g >> 1) * 32 + n) * 8 + (g & 1) * 4; }
-    __device__ static Raw load(rsrc_t r, uint32_t off) { return ld32(r, off); }
-    __device__ static void ops(Raw r, uint32_t, int, const uint2*, long* b) {
-        b[0] = pk2(r & 0xF0F0F0F0u, (r << 4) & 0xF0F0F0F0u);
+    typedef uint2 Raw;
+    __device__ static Raw load(rsrc_t r, uint32_t off) { return ld64(r, off); }
+    __device__ static void ops(Raw r, uint32_t, const uint2*, v4i* b) {
+        b[0][0] = (int)(r.x & 0xF0F0F0F0u);
+        b[0][1] = (int)((r.x << 4) & 0xF0F0F0F0u);
+        b[0][2] = (int)(r.y & 0xF0F0F0F0u);
+        b[0][3] = (int)((r.y << 4) & 0xF0F0F0F0u);
     }
     __device__ static uint32_t scale_op(uint32_t w) { return w; }
 };
 
-// q4_K: unsigned nibbles, values +0..3 in the low nibbles of the lane's dword, +4..7 in the
-// high ones; the scale dword is the exact f16 pair (hi, lo) of d*sc, the min region -dmin*m.
+// q4_K: unsigned nibbles, values 0-3 in the low nibbles of X0 and 4-7 in its high ones; the
+// scale dword is the exact f16 pair (hi, lo) of d*sc, the min region -dmin*m.
 template <> struct VQ<MMQ_Q4_K> {
     static constexpr int FB = 512, NMF = 1;
-    static constexpr bool MIN = true, ROW = false;
+    static constexpr bool MIN = true, ROW = false, META = false;
     static constexpr float POST = 1.0f;
-    typedef uint32_t Raw;
-    __device__ static int off(int n, int g) { return ((g >> 1) * 32 + n) * 8 + (g & 1) * 4; }
-    __device__ static Raw load(rsrc_t r, uint32_t off) { return ld32(r, off); }
-    __device__ static void ops(Raw r, uint32_t, int, const uint2*, long* b) {
-        b[0] = pk2(r & 0x0F0F0F0Fu, (r >> 4) & 0x0F0F0F0Fu);
+    typedef uint2 Raw;
+    __device__ static Raw load(rsrc_t r, uint32_t off) { return ld64(r, off); }
+    __device__ static void ops(Raw r, uint32_t, const uint2*, v4i* b) {
+        b[0][0] = (int)(r.x & 0x0F0F0F0Fu);
+        b[0][1] = (int)((r.x >> 4) & 0x0F0F0F0Fu);
+        b[0][2] = (int)(r.y & 0x0F0F0F0Fu);
+        b[0][3] = (int)((r.y >> 4) & 0x0F0F0F0Fu);
     }
     __device__ static uint32_t scale_op(uint32_t w) { return w; }
 };
 
-// iq1t: one dword of 2-bit codes per fragment lane (value 16h + 4q + b at bits 8b + 2q), so
-// the lane's values 8(g&1) + j sit at q = 2(g&1) + j/4, b = j%4. The lane's half h = g/2 has
-// the meta byte s | sigma0 << 3 | sigma1 << 4 in its scale dword (byte 2 + h), and its 8
-// values are sign group g&1 of that half. The IQ1_M fold (llama.cpp PR #304, Design) makes
-// each value the integer v = 8(c-1) + sigma (sigma = +-1) under the per-16 factor (2s+1) and
-// the scale d/8; (2s+1)*v is split as 2s*v + v (|2s*v| <= 126) over two int8 MFMAs.
-// tab[s | sign << 3] = (byte LUT code -> v, byte LUT code -> 2s*v).
+// iq1t: one dword of 2-bit codes per fragment lane (value 4q + b at bits 8b + 2q). The lane's
+// half h has the meta byte s | sigma0 << 3 | sigma1 << 4 in its row's scale dword (byte
+// 2 + h); values 0-7 are sign group 0, 8-15 group 1. The IQ1_M fold (llama.cpp PR #304,
+// Design) makes each value the integer v = 8(c-1) + sigma (sigma = +-1) under the per-16
+// factor (2s+1) and the scale d/8; (2s+1)*v is split as 2s*v + v (|2s*v| <= 126) over two
+// chained int8 MFMAs. tab[s | sign << 3] = (byte LUT code -> v, byte LUT code -> 2s*v).
 template <> struct VQ<MMQ_IQ1T> {
     static constexpr int FB = 256, NMF = 2;
-    static constexpr bool MIN = false, ROW = false;
+    static constexpr bool MIN = false, ROW = false, META = true;
     static constexpr float POST = 1.0f / 8;
     typedef uint32_t Raw;
-    __device__ static int off(int n, int g) { return ((g >> 1) * 32 + n) * 4; }
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld32(r, off); }
-    __device__ static void ops(Raw r, uint32_t wsd, int g, const uint2* tab, long* b) {
-        const uint32_t meta = (wsd >> (16 + 8 * (g >> 1))) & 0xFFu;
-        const uint32_t e = (meta & 7u) | (((meta >> (3 + (g & 1))) & 1u) << 3);
-        const uint2 t = tab[e];
-        const uint32_t sh = 4u * (uint32_t)(g & 1);
-        const uint32_t s0 = (r >> sh) & 0x03030303u, s1 = (r >> (sh + 2)) & 0x03030303u;
-        b[0] = pk2(__builtin_amdgcn_perm(0u, t.y, s0), __builtin_amdgcn_perm(0u, t.y, s1));
-        b[1] = pk2(__builtin_amdgcn_perm(0u, t.x, s0), __builtin_amdgcn_perm(0u, t.x, s1));
+    // meta: the lane's meta byte
+    __device__ static void ops(Raw C, uint32_t meta, const uint2* tab, v4i* b) {
+        const uint32_t s = meta & 7u;
+        const uint2 t0 = tab[s | (((meta >> 3) & 1u) << 3)];
+        const uint2 t1 = tab[s | (((meta >> 4) & 1u) << 3)];
+        const uint32_t q0 = C & 0x03030303u, q1 = (C >> 2) & 0x03030303u;
+        const uint32_t q2 = ((C >> 4) & 0x03030303u) | 0x04040404u;
+        const uint32_t q3 = ((C >> 6) & 0x03030303u) | 0x04040404u;
+        // selectors 0-2 pick group 0's LUT (low word), 4-6 group 1's (high word)
+        b[0][0] = (int)__builtin_amdgcn_perm(t1.y, t0.y, q0);
+        b[0][1] = (int)__builtin_amdgcn_perm(t1.y, t0.y, q1);
+        b[0][2] = (int)__builtin_amdgcn_perm(t1.y, t0.y, q2);
+        b[0][3] = (int)__builtin_amdgcn_perm(t1.y, t0.y, q3);
+        b[1][0] = (int)__builtin_amdgcn_perm(t1.x, t0.x, q0);
+        b[1][1] = (int)__builtin_amdgcn_perm(t1.x, t0.x, q1);
+        b[1][2] = (int)__builtin_amdgcn_perm(t1.x, t0.x, q2);
+        b[1][3] = (int)__builtin_amdgcn_perm(t1.x, t0.x, q3);
     }
     __device__ static uint32_t scale_op(uint32_t w) { return w & 0xFFFFu; }   // f16 d only
     __device__ static uint2 table(int e) {
@@ -167,7 +181,7 @@ struct MvArgs {
     const uint32_t* xs2;        // q8_1 region 3: xs as an f16 pair, tile-major
     const float* xsx;           // q8_1 region 4: xs * xsum, tile-major
     const float* sa;            // i8_token region 1: per-token scale
-    int M, N, KBp, groups;      // groups: 16-row groups of the padded weight rows
+    int M, N, KBp, groups;      // groups: 16-row groups holding at least one real row
     void* out;
     int64_t ldo;
 };
@@ -176,14 +190,14 @@ struct MvArgs {
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Persistent workgroups: workgroup b handles the 16-row groups b, b + gridDim.x, ... (group q
-// = rows 16q..16q+15 = half q&1 of tile q/2), all M <= 16 tokens, all of K. Each wave's work is
-// one stream of items (group, chunk), its chunks being wave, wave + MV_W, ... of every group;
-// loads run two items ahead across group boundaries, so the memory pipe does not drain while
-// a group is reduced. NR = accumulator registers that hold a live token.
-template <mmq_wtype FMT, int NR>
+// = rows 16q..16q+15 = half q&1 of weight tile q/2), all M <= 16 tokens, all of K. Each wave's
+// work is one stream of items (group, chunk), its chunks being wave, wave + MV_W, ... of every
+// group; loads run two items ahead. TG = token groups of 8 (1 or 2); NR = accumulator
+// registers holding a live token (min(M, 4)).
+template <mmq_wtype FMT, int TG, int NR>
 __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     using T = VQ<FMT>;
-    __shared__ float red[2][MV_W][4][64];
+    __shared__ float red[2][MV_W][4 * TG][64];
     __shared__ uint2 tab[16];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -200,31 +214,37 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     const int cw = wave < nch ? (nch - wave + MV_W - 1) / MV_W : 0;      // this wave's chunks per group
     const int total = ng * cw;
 
-    // Each address is a wave-uniform base (scalar registers) plus a loop-invariant 32-bit lane
-    // offset plus a per-block immediate, so no vector registers go to address arithmetic.
-    // Lanes whose token does not exist (c16 >= M), and the k-groups that do not supply xs (the
-    // scale MFMA takes it from k-group 0 only: S = xs * wd once), get an offset past the
-    // descriptor's range: the load returns zero without touching memory, and no branch is needed.
-    constexpr int LB = T::FB / 64;                                  // fragment bytes per lane
-    constexpr uint32_t OOR = 0x40000000u;                           // beyond every range below
-    const bool tl = c16 < a.M;
-    const uint32_t o_w = (uint32_t)T::off(c16, g);                  // rows 0..15 of the half
-    const uint32_t o_s = (uint32_t)c16 * 4;
-    const uint32_t o_mw = (uint32_t)(g * 32 + c16) * 4;             // f32 MFMA k = g: block b0 + g
-    const uint32_t o_mx = tl ? o_mw : OOR;
-    const uint32_t o_x = tl ? (uint32_t)(((g >> 1) * 32 + c16) * 16 + (g & 1) * 8) : OOR;
-    const uint32_t o_xs = (tl && g == 0) ? (uint32_t)c16 * 4 : OOR;
+    // ---- loop-invariant lane offsets (bytes); per-item bases are wave-uniform
+    constexpr int LB = T::FB / 64;                   // packed bytes per fragment lane
+    const int fb = g >> 1, fh = g & 1;               // block of the pair, half of the block
+    // weight operand: fragment lane fh*32 + (row of the 16-row group) of block 2p + fb
+    const uint32_t o_w = (uint32_t)(fb * T::FB + (fh * 32 + c16) * LB);
+    // token operand, block-diagonal: row c16 < 8 takes token c16 against block 2p (k-groups
+    // 0-1), row c16 >= 8 token c16-8 against block 2p+1 (k-groups 2-3); other lanes read zero
+    const bool diag = (c16 >> 3) == fb;
+    const int t0 = c16 & 7, t1 = 8 + (c16 & 7);
+    const uint32_t o_x0 = (diag && t0 < a.M) ? (uint32_t)(fb * 1024 + (fh * 32 + t0) * 16) : OOR;
+    const uint32_t o_x1 = (diag && t1 < a.M) ? (uint32_t)(fb * 1024 + (fh * 32 + t1) * 16) : OOR;
+    // scales of four blocks at once: k-group g holds block b0 + g
+    const uint32_t o_s = (uint32_t)(g * 128 + c16 * 4);                  // weight row c16
+    const uint32_t o_xs0 = t0 < a.M ? (uint32_t)(g * 128 + t0 * 4) : OOR;   // token of row c16
+    const uint32_t o_xs1 = t1 < a.M ? (uint32_t)(g * 128 + t1 * 4) : OOR;
+    // q4_K min term (rows 0-7 only): token c16 (< 8) of block b0 + g against weight row c16
+    const uint32_t o_mx0 = (c16 < 8 && c16 < a.M) ? (uint32_t)(g * 128 + c16 * 4) : OOR;
+    const uint32_t o_mx1 = (c16 < 8 && 8 + c16 < a.M) ? (uint32_t)(g * 128 + (8 + c16) * 4) : OOR;
+    // iq1t: the scale dword of this lane's own (block 2p + fb, row c16), for its meta byte
+    const uint32_t o_wso = (uint32_t)(fb * 128 + c16 * 4);
     const uint8_t* const xsb = reinterpret_cast<const uint8_t*>(a.xs2);
     const uint8_t* const xmb = reinterpret_cast<const uint8_t*>(a.xsx);
     const uint8_t* const wsb = a.w + a.w_scale_off;
     const uint8_t* const wmb = a.w + a.w_min_off;
 
     struct Chunk {
-        typename T::Raw w[MV_CH];
-        uint32_t ws[MV_CH];
-        uint2 x[MV_CH];
-        uint32_t xs[MV_CH];
-        float xm, wm;
+        typename T::Raw w[2];
+        v4i x[TG][2];
+        uint32_t ws, xs[TG];
+        uint32_t wso[2];
+        float xm[TG], wm;
     };
     // item t (clamped to the last one, so that the tail issues harmless repeat loads)
     auto load = [&](int t, Chunk& k) __attribute__((always_inline)) {
@@ -237,79 +257,105 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         const rsrc_t rw = rsrc(a.w + tb * T::FB + half * (MV_ROWS * LB), MV_CH * T::FB);
         const rsrc_t rx = rsrc(a.xq + (int64_t)b0 * 1024, MV_CH * 1024);
 #pragma unroll
-        for (int u = 0; u < MV_CH; ++u) {
-            k.w[u] = T::load(rw, o_w + u * T::FB);
-            k.x[u] = ld64(rx, o_x + u * 1024);
+        for (int p = 0; p < 2; ++p) {
+            k.w[p] = T::load(rw, o_w + p * 2 * T::FB);
+            k.x[0][p] = ld128(rx, o_x0 + p * 2048);
+            if constexpr (TG == 2) k.x[1][p] = ld128(rx, o_x1 + p * 2048);
         }
         if constexpr (!T::ROW) {
             const rsrc_t rs = rsrc(wsb + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128);
             const rsrc_t rxs = rsrc(xsb + (int64_t)b0 * 128, MV_CH * 128);
-#pragma unroll
-            for (int u = 0; u < MV_CH; ++u) {
-                k.ws[u] = ld32(rs, o_s + u * 128);
-                k.xs[u] = ld32(rxs, o_xs + u * 128);
+            k.ws = ld32(rs, o_s);
+            k.xs[0] = ld32(rxs, o_xs0);
+            if constexpr (TG == 2) k.xs[1] = ld32(rxs, o_xs1);
+            if constexpr (T::META) {
+                k.wso[0] = ld32(rs, o_wso);
+                k.wso[1] = ld32(rs, o_wso + 256);
             }
         }
         if constexpr (T::MIN) {
-            k.xm = __builtin_bit_cast(float, ld32(rsrc(xmb + (int64_t)b0 * 128, 4 * 128), o_mx));
-            k.wm = __builtin_bit_cast(float, ld32(rsrc(wmb + (tb * 32 + half * MV_ROWS) * 4, 4 * 128), o_mw));
+            const rsrc_t rxm = rsrc(xmb + (int64_t)b0 * 128, MV_CH * 128);
+            k.xm[0] = __builtin_bit_cast(float, ld32(rxm, o_mx0));
+            if constexpr (TG == 2) k.xm[1] = __builtin_bit_cast(float, ld32(rxm, o_mx1));
+            k.wm = __builtin_bit_cast(float, ld32(rsrc(wmb + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128), o_s));
         }
     };
 
     const v4i zi = {0, 0, 0, 0};
     const v4f zf = {0.f, 0.f, 0.f, 0.f};
-    v4f acc = zf;
-    v4i iacc = zi;
+    v4f acc[TG];
+    v4i iacc[TG];
+#pragma unroll
+    for (int x = 0; x < TG; ++x) {
+        acc[x] = zf;
+        iacc[x] = zi;
+    }
+    // k-group of the token scale feeding this lane's row in pair p: 2p for rows 0-7, 2p+1 for 8-15
+    const bool sel0 = g == (c16 >> 3), sel1 = g == 2 + (c16 >> 3);
     auto compute = [&](const Chunk& k) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < MV_CH; ++u) {
-            long bop[T::NMF];
-            T::ops(k.w[u], T::ROW ? 0u : k.ws[u], g, tab, bop);
-            const long aop = pk2(k.x[u].x, k.x[u].y);
-            if constexpr (T::ROW) {
-                iacc = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop[0], iacc, 0, 0, 0);
-            } else {
-                v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop[0], zi, 0, 0, 0);
-                if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop[1], D, 0, 0, 0);
-                const v4f S = __builtin_amdgcn_mfma_f32_16x16x16f16(as_h4(k.xs[u]), as_h4(T::scale_op(k.ws[u])),
-                                                                    zf, 0, 0, 0);
+        for (int p = 0; p < 2; ++p) {
+            v4i bop[T::NMF];
+            uint32_t meta = 0;
+            if constexpr (T::META) meta = (k.wso[p] >> (16 + 8 * fh)) & 0xFFu;
+            T::ops(k.w[p], meta, tab, bop);
 #pragma unroll
-                for (int v = 0; v < NR; ++v) acc[v] = __builtin_fmaf((float)D[v], S[v], acc[v]);
+            for (int x = 0; x < TG; ++x) {
+                if constexpr (T::ROW) {
+                    iacc[x] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.x[x][p], bop[0], iacc[x], 0, 0, 0);
+                } else {
+                    v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.x[x][p], bop[0], zi, 0, 0, 0);
+                    if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.x[x][p], bop[1], D, 0, 0, 0);
+                    const uint32_t xa = (p == 0 ? sel0 : sel1) ? k.xs[x] : 0u;
+                    const v4f S = __builtin_amdgcn_mfma_f32_16x16x16f16(as_h4(xa), as_h4(T::scale_op(k.ws)), zf, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < NR; ++v) acc[x][v] = __builtin_fmaf((float)D[v], S[v], acc[x][v]);
+                }
             }
         }
-        if constexpr (T::MIN) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.xm, k.wm, acc, 0, 0, 0);
+        if constexpr (T::MIN) {
+#pragma unroll
+            for (int x = 0; x < TG; ++x) acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(k.xm[x], k.wm, acc[x], 0, 0, 0);
+        }
     };
 
-    // group i's reduction: the waves' partial sums meet in LDS buffer i&1 and are added in
-    // wave order. One barrier per group suffices: buffer i&1 is written again only by group
+    // group i's reduction: the waves' partial sums meet in LDS buffer i&1 and are added in a
+    // fixed order. One barrier per group suffices: buffer i&1 is written again only by group
     // i+2, after every thread has passed group i+1's barrier, i.e. finished group i's reads.
     auto finish = [&](int i) __attribute__((always_inline)) {
-        const int p = i & 1;
+        const int pb = i & 1;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            // element to a scalar first: a bit cast of the vector element expression itself
-            // is lowered to element 0
-            const int iv = iacc[v];
-            red[p][wave][v][lane] = T::ROW ? __builtin_bit_cast(float, iv) : acc[v];
+        for (int x = 0; x < TG; ++x) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                // element to a scalar first: a bit cast of the vector element expression itself
+                // is lowered to element 0
+                const int iv = iacc[x][v];
+                red[pb][wave][4 * x + v][lane] = T::ROW ? __builtin_bit_cast(float, iv) : acc[x][v];
+            }
+            acc[x] = zf;
+            iacc[x] = zi;
         }
-        acc = zf;
-        iacc = zi;
         lds_barrier();
-        if (tid < 4 * 64) {
-            const int l = tid & 63, v = tid >> 6;
-            const int m = 4 * (l >> 4) + v;                      // token of register v in lane l
-            const int col = ((int)blockIdx.x + i * (int)gridDim.x) * MV_ROWS + (l & 15);
+        if (tid < MV_TOK * MV_ROWS) {
+            // token m, column n: register (m & 3) of lanes 16*((m & 7) >> 2) + n (rows 0-7,
+            // even blocks) and that + 32 (rows 8-15, odd blocks), token group m >> 3
+            const int m = tid >> 4, n = tid & 15;
+            const int col = ((int)blockIdx.x + i * (int)gridDim.x) * MV_ROWS + n;
             if (m < a.M && col < a.N) {
+                const int r = 4 * (m >> 3) + (m & 3);
+                const int la = 16 * ((m & 7) >> 2) + n, lb = la + 32;
                 if constexpr (T::ROW) {
                     int s = 0;
 #pragma unroll
-                    for (int w = 0; w < MV_W; ++w) s += __builtin_bit_cast(int, red[p][w][v][l]);
+                    for (int w = 0; w < MV_W; ++w)
+                        s += __builtin_bit_cast(int, red[pb][w][r][la]) + __builtin_bit_cast(int, red[pb][w][r][lb]);
                     const float sw = reinterpret_cast<const float*>(wsb)[col];
                     reinterpret_cast<uint16_t*>(a.out)[(int64_t)m * a.ldo + col] = bf16_rne(((float)s * a.sa[m]) * sw);
                 } else {
                     float s = 0.f;
 #pragma unroll
-                    for (int w = 0; w < MV_W; ++w) s += red[p][w][v][l];
+                    for (int w = 0; w < MV_W; ++w) s += red[pb][w][r][la] + red[pb][w][r][lb];
                     reinterpret_cast<float*>(a.out)[(int64_t)m * a.ldo + col] = s * T::POST;
                 }
             }
@@ -320,7 +366,8 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         for (int i = 0; i < ng; ++i) finish(i);
         return;
     }
-    // item t lives in buffer t % 3; step P computes buffer P and refills buffer (P+2) % 3
+    // item t lives in buffer t % 3; each step computes one buffer and refills the one
+    // computed in the step before
     Chunk k0, k1, k2;
     load(0, k0);
     load(1, k1);
@@ -357,21 +404,23 @@ template <mmq_wtype FMT>
 hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
     const dim3 grid((unsigned)std::min(args.groups, cu_count())), block(MV_W * 64);
     switch (args.M) {
-        case 1: hipLaunchKernelGGL((mmvq_kernel<FMT, 1>), grid, block, 0, s, args); break;
-        case 2: hipLaunchKernelGGL((mmvq_kernel<FMT, 2>), grid, block, 0, s, args); break;
-        case 3: hipLaunchKernelGGL((mmvq_kernel<FMT, 3>), grid, block, 0, s, args); break;
-        default: hipLaunchKernelGGL((mmvq_kernel<FMT, 4>), grid, block, 0, s, args); break;
+        case 1: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 1>), grid, block, 0, s, args); break;
+        case 2: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 2>), grid, block, 0, s, args); break;
+        case 3: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 3>), grid, block, 0, s, args); break;
+        case 4: case 5: case 6: case 7: case 8:
+            hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4>), grid, block, 0, s, args); break;
+        default: hipLaunchKernelGGL((mmvq_kernel<FMT, 2, 4>), grid, block, 0, s, args); break;
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-int mmvq_max_tokens() { return MV_ROWS; }
+int mmvq_max_tokens() { return MV_TOK; }
 
 hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                        int64_t K, void* out, int64_t ldo, hipStream_t s) {
-    if (M < 1 || M > MV_ROWS) return hipErrorInvalidValue;
+    if (M < 1 || M > MV_TOK) return hipErrorInvalidValue;
     const PackedLayout P = packed_layout(t, N, K);
     const uint8_t* ab = static_cast<const uint8_t*>(act);
     MvArgs args{};

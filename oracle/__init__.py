@@ -76,6 +76,7 @@ def lib():
         L.orc_gemm_w8a8.argtypes = [P, P, I, P, P, I, I, P, P, I, I]
         L.orc_gemm_w8a8.restype = ctypes.c_int
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -104,6 +105,11 @@ def float_to_bf16_bits(x: float) -> int:
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP thread count of later calls (timing only; results do not depend on it)."""
+    lib().orc_set_threads(int(n))
 
 
 # -------------------------------------------------------------- quantisers

@@ -400,3 +400,13 @@ int orc_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Thread count for the timed baseline only (no effect on any result). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
