@@ -210,7 +210,13 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     }
     const int KBp = a.KBp;
     const int nch = KBp / MV_CH;
-    const int ng = (a.groups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;   // >= 1
+    // Group of round i: off + G*i. Workgroups are dealt to the 8 XCDs round-robin (b -> b % 8),
+    // and the two 16-row halves of a weight tile share their 128-byte scale lines, so with a
+    // grid of whole 16s the halves of a tile go to workgroups b and b + 8 - the same XCD, whose
+    // L2 then fetches each scale line once.
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int off = (G % 16 == 0) ? 2 * (8 * (b >> 4) + (b & 7)) + ((b >> 3) & 1) : b;
+    const int ng = (a.groups - off + G - 1) / G;                         // >= 1
     const int cw = wave < nch ? (nch - wave + MV_W - 1) / MV_W : 0;      // this wave's chunks per group
     const int total = ng * cw;
 
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     auto load = [&](int t, Chunk& k) __attribute__((always_inline)) {
         t = min(t, total - 1);
         const int i = t / cw, j = t - i * cw;
-        const int q = (int)blockIdx.x + i * (int)gridDim.x;             // 16-row group
+        const int q = off + i * G;                                      // 16-row group
         const int half = q & 1;
         const int b0 = (wave + j * MV_W) * MV_CH;
         const int64_t tb = (int64_t)(q >> 1) * KBp + b0;                // (tile, block) index
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             // token m, column n: register (m & 3) of lanes 16*((m & 7) >> 2) + n (rows 0-7,
             // even blocks) and that + 32 (rows 8-15, odd blocks), token group m >> 3
             const int m = tid >> 4, n = tid & 15;
-            const int col = ((int)blockIdx.x + i * (int)gridDim.x) * MV_ROWS + n;
+            const int col = (off + i * G) * MV_ROWS + n;
             if (m < a.M && col < a.N) {
                 const int r = 4 * (m >> 3) + (m & 3);
                 const int la = 16 * ((m & 7) >> 2) + n, lb = la + 32;
