@@ -65,10 +65,12 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # with and scaled by the copy-kernel factor (profiles/ holds the summaries); absent (reported
 # as null) until measured for the current kernel.
 MEASURED_TRAFFIC_BYTES = {
-    "cfg2a_q4_0": 166249957,
-    "cfg3a_q4_K": 98540837,
-    "cfg4_w8a8": 60068437,
-    "cfg5_moe_iq1t": 387446793,
+    "cfg2a_q4_0": 166180201,
+    "cfg3a_q4_K": 98550577,
+    "cfg4_w8a8": 60068906,
+    "cfg5_moe_iq1t": 387556612,
+    "dec8_q4_0": 11114121,
+    "dec8_q4_K": 45142006,
 }
 
 RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "i8_row": 32}
@@ -222,6 +224,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=-1,
                     help="weight copies cycled through the steps (cold MALL); default: 1, or enough "
                          "for >= 1 GB on the decode workloads")
+    ap.add_argument("--samples", type=int, default=30, help="kernel-timing samples")
+    ap.add_argument("--per-sample", type=int, default=100, help="graph-replayed launches per sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy 5x (counter calibration)")
@@ -317,7 +321,7 @@ def main():
         extra["weight_bytes_rotated"] = int(n_rot * packed[0].numel())
 
     torch.cuda.synchronize()
-    step_s, kt = timed(kernels, n_rot, args.steps, args.warmup)
+    step_s, kt = timed(kernels, n_rot, args.steps, args.warmup, args.samples, args.per_sample)
     sclk = sclk_mhz()
     tops = ops / step_s / 1e12
     kstats = []
@@ -326,7 +330,7 @@ def main():
         kstats.append({"mean": float(c.mean()), "median": float(np.median(c)), "min": float(c.min()),
                        "max": float(c.max())})
         log(f"[bench] {kn}: per launch mean {c.mean() * 1e6:.3f} us, median {np.median(c) * 1e6:.3f} us, "
-            f"min {c.min() * 1e6:.3f}, max {c.max() * 1e6:.3f} (30 samples x 100 launches)")
+            f"min {c.min() * 1e6:.3f}, max {c.max() * 1e6:.3f} ({args.samples} samples x {args.per_sample} launches)")
     k_s = kstats[dom]["mean"]
     k_tops = ops / k_s / 1e12
     k_gbs = alg_bytes / k_s / 1e9
@@ -385,7 +389,8 @@ def main():
                    "activations": "i8_token" if fmt == "i8_row" else "q8_1",
                    "step": "gemm (int8 activations given)" if fmt == "i8_row" else
                            "quantize_act + gemm" + ("_id" if moe else "") + " (repack untimed)",
-                   "timing": "hipGraph replay of the step; kernels: 30 samples x 100 graph-replayed launches, hipEvents",
+                   "timing": f"hipGraph replay of the step; kernels: {args.samples} samples x {args.per_sample} "
+                             f"graph-replayed launches, hipEvents",
                    **extra},
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 3),
         "sclk_mhz_after_run": sclk,
