@@ -14,10 +14,9 @@ workloads are decode batches of 1-16 tokens on the same weight shapes).
 
 Timing (the pages' protocol: warm-up, then 30 samples of 100 back-to-back launches (or a
 hipGraph replay) timed with hipEvents, median and min/max spread; P2 section 3.3):
-  step time     one step is captured in a hipGraph and replayed --steps times (with rotating
-                weight copies, all --steps steps are captured in one graph and replayed once)
+  step time     all --steps steps are captured in one hipGraph, replayed once untimed and once
                 between two synchronisations; value = 2*M*N*K / step time. The graph keeps
-                host launch cost out of the GPU timeline.
+                host launch cost (and the ~8 us gap between graph launches) out of the timing.
   kernel times  per kernel, a hipGraph of 100 back-to-back launches replayed 30 times, each
                 replay bracketed by HIP events on the launch stream: 30 samples of the average
                 launch duration (mean, median, min, max reported).
@@ -176,8 +175,8 @@ def _graph(fns, n):
 
 def timed(kernels, n_rot, steps, warmup, samples=30, per_sample=100):
     """kernels: [(name, fn(r))] launched in this order make one step on weight copy r.
-    Step time: a hipGraph of one step replayed `steps` times (with rotating copies, one graph of
-    all `steps` steps, replayed once) between two synchronisations. Kernel times: per kernel, a
+    Step time: one hipGraph of all `steps` steps, replayed once between two synchronisations
+    (after one untimed replay). Kernel times: per kernel, a
     hipGraph of `per_sample` back-to-back launches replayed `samples` times, each replay
     bracketed by HIP events on the launch stream. Returns (step seconds, {name: samples [s]})."""
     import torch
@@ -187,15 +186,15 @@ def timed(kernels, n_rot, steps, warmup, samples=30, per_sample=100):
     for i in range(warmup):
         step(i % n_rot)
     torch.cuda.synchronize()
-    per_graph = 1 if n_rot == 1 else steps
-    g = _graph([lambda r=r: step(r) for r in range(n_rot)], per_graph)
+    # all `steps` steps in one graph: one graph launch per timed region (a replay of a one-step
+    # graph costs ~8 us of launch gap between replays, longer than a decode step)
+    g = _graph([lambda r=r: step(r) for r in range(n_rot)], steps)
     g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps // per_graph):
-        g.replay()
+    g.replay()
     torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / (steps // per_graph * per_graph)
+    step_s = (time.perf_counter() - t0) / steps
     del g
     kt = {}
     for name, f in kernels:
@@ -389,7 +388,7 @@ def main():
                    "activations": "i8_token" if fmt == "i8_row" else "q8_1",
                    "step": "gemm (int8 activations given)" if fmt == "i8_row" else
                            "quantize_act + gemm" + ("_id" if moe else "") + " (repack untimed)",
-                   "timing": f"hipGraph replay of the step; kernels: {args.samples} samples x {args.per_sample} "
+                   "timing": f"one hipGraph of all steps; kernels: {args.samples} samples x {args.per_sample} "
                              f"graph-replayed launches, hipEvents",
                    **extra},
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 3),
