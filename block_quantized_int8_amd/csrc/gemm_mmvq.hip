@@ -47,6 +47,10 @@ constexpr int MV_W = 16;          // waves per workgroup (they split the blocks 
 constexpr int MV_CH = 4;          // blocks per chunk: two MFMA pairs, one scale load
 constexpr int MV_ROWS = 16;       // weight rows per workgroup group
 constexpr int MV_TOK = 16;        // largest batch
+// Activation staging in LDS (token rows 0..8*TG-1 of every block, 16 bytes per (block, half,
+// token)): capacity in blocks per token-group count, within the 160 KB LDS beside the
+// reduction buffers. Longer K runs the register path (each wave loads its own operands).
+template <int TG> struct XCap { static constexpr int KB = TG == 1 ? 448 : 128; };
 static_assert(KB_ALIGN % MV_CH == 0, "chunks tile the padded block count");
 
 // Buffer loads: a wave-uniform descriptor (base, byte range) in scalar registers plus a 32-bit
@@ -194,11 +198,14 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // work is one stream of items (group, chunk), its chunks being wave, wave + MV_W, ... of every
 // group; loads run two items ahead. TG = token groups of 8 (1 or 2); NR = accumulator
 // registers holding a live token (min(M, 4)).
-template <mmq_wtype FMT, int TG, int NR>
+template <mmq_wtype FMT, int TG, int NR, bool XL>
 __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     using T = VQ<FMT>;
+    constexpr int TOK = 8 * TG;                              // staged token rows
+    constexpr int XSLOTS = XL ? XCap<TG>::KB * 2 * TOK : 0;  // 16-byte slots; slot XSLOTS is zero
     __shared__ float red[2][MV_W][4 * TG][64];
     __shared__ uint2 tab[16];
+    __shared__ __attribute__((aligned(16))) uint8_t xl[(XSLOTS + 1) * 16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,7 +254,8 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
 
     struct Chunk {
         typename T::Raw w[2];
-        v4i x[TG][2];
+        v4i x[TG][2];                // register path only
+        int b0;
         uint32_t ws, xs[TG];
         uint32_t wso[2];
         float xm[TG], wm;
@@ -262,11 +270,14 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         const int64_t tb = (int64_t)(q >> 1) * KBp + b0;                // (tile, block) index
         const rsrc_t rw = rsrc(a.w + tb * T::FB + half * (MV_ROWS * LB), MV_CH * T::FB);
         const rsrc_t rx = rsrc(a.xq + (int64_t)b0 * 1024, MV_CH * 1024);
+        k.b0 = b0;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             k.w[p] = T::load(rw, o_w + p * 2 * T::FB);
-            k.x[0][p] = ld128(rx, o_x0 + p * 2048);
-            if constexpr (TG == 2) k.x[1][p] = ld128(rx, o_x1 + p * 2048);
+            if constexpr (!XL) {
+                k.x[0][p] = ld128(rx, o_x0 + p * 2048);
+                if constexpr (TG == 2) k.x[1][p] = ld128(rx, o_x1 + p * 2048);
+            }
         }
         if constexpr (!T::ROW) {
             const rsrc_t rs = rsrc(wsb + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128);
@@ -299,6 +310,19 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     // k-group of the token scale feeding this lane's row in pair p: 2p for rows 0-7, 2p+1 for 8-15
     const bool sel0 = g == (c16 >> 3), sel1 = g == 2 + (c16 >> 3);
     auto compute = [&](const Chunk& k) __attribute__((always_inline)) {
+        // token operands of both pairs (LDS path: the diagonal lanes' slots, else the zero slot)
+        v4i xo[TG][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int x = 0; x < TG; ++x) {
+                if constexpr (XL) {
+                    const int sl = diag ? ((k.b0 + 2 * p + fb) * 2 + fh) * TOK + (x == 0 ? t0 : t1) : XSLOTS;
+                    xo[x][p] = *reinterpret_cast<const v4i*>(xl + sl * 16);
+                } else {
+                    xo[x][p] = k.x[x][p];
+                }
+            }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             v4i bop[T::NMF];
@@ -308,10 +332,10 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
 #pragma unroll
             for (int x = 0; x < TG; ++x) {
                 if constexpr (T::ROW) {
-                    iacc[x] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.x[x][p], bop[0], iacc[x], 0, 0, 0);
+                    iacc[x] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], bop[0], iacc[x], 0, 0, 0);
                 } else {
-                    v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.x[x][p], bop[0], zi, 0, 0, 0);
-                    if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.x[x][p], bop[1], D, 0, 0, 0);
+                    v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], bop[0], zi, 0, 0, 0);
+                    if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], bop[1], D, 0, 0, 0);
                     const uint32_t xa = (p == 0 ? sel0 : sel1) ? k.xs[x] : 0u;
                     const v4f S = __builtin_amdgcn_mfma_f32_16x16x16f16(as_h4(xa), as_h4(T::scale_op(k.ws)), zf, 0, 0, 0);
 #pragma unroll
@@ -368,7 +392,40 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         }
     };
 
+    // LDS path: the token rows 0..TOK-1 of every block go to slot (b*2 + h)*TOK + t (the tiled
+    // xq keeps row t's values 16h..16h+15 of block b at lane h*32 + t; rows >= M are the
+    // buffer's zero padding). The staging loads are issued first, then the first two items'
+    // weight loads, then the LDS writes (which wait only for the staging loads) and a barrier
+    // that leaves the weight loads in flight.
+    constexpr int PER = XL ? (XSLOTS + MV_W * 64 - 1) / (MV_W * 64) : 1;
+    v4i xv[PER];
+    if constexpr (XL) {
+        const int nslot = KBp * 2 * TOK;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int sl = min(tid + u * MV_W * 64, nslot - 1);     // loads unconditional
+            const int t = sl % TOK, h = (sl / TOK) & 1, b = sl / (2 * TOK);
+            xv[u] = *reinterpret_cast<const v4i*>(a.xq + ((int64_t)b * 64 + h * 32 + t) * 16);
+        }
+    }
+    auto stage = [&]() __attribute__((always_inline)) {
+        if constexpr (XL) {
+            const int nslot = KBp * 2 * TOK;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int sl = tid + u * MV_W * 64;
+                if (sl < nslot) *reinterpret_cast<v4i*>(xl + sl * 16) = xv[u];
+            }
+            if (tid == 0) {
+                const v4i z = {0, 0, 0, 0};
+                *reinterpret_cast<v4i*>(xl + XSLOTS * 16) = z;
+            }
+            lds_barrier();
+        }
+    };
+
     if (cw == 0) {                       // fewer chunks than waves: this wave only reduces
+        stage();
         for (int i = 0; i < ng; ++i) finish(i);
         return;
     }
@@ -377,6 +434,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     Chunk k0, k1, k2;
     load(0, k0);
     load(1, k1);
+    stage();
     auto step = [&](int t, const Chunk& cur, Chunk& nxt) __attribute__((always_inline)) {
         load(t + 2, nxt);
         compute(cur);
@@ -406,17 +464,25 @@ int cu_count() {
     return cus[dev];
 }
 
+template <mmq_wtype FMT, bool XL>
+void launch_xl(const MvArgs& args, dim3 grid, hipStream_t s) {
+    const dim3 block(MV_W * 64);
+    switch (args.M) {
+        case 1: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 1, XL>), grid, block, 0, s, args); break;
+        case 2: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 2, XL>), grid, block, 0, s, args); break;
+        case 3: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 3, XL>), grid, block, 0, s, args); break;
+        case 4: case 5: case 6: case 7: case 8:
+            hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4, XL>), grid, block, 0, s, args); break;
+        default: hipLaunchKernelGGL((mmvq_kernel<FMT, 2, 4, XL>), grid, block, 0, s, args); break;
+    }
+}
+
 template <mmq_wtype FMT>
 hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
-    const dim3 grid((unsigned)std::min(args.groups, cu_count())), block(MV_W * 64);
-    switch (args.M) {
-        case 1: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 1>), grid, block, 0, s, args); break;
-        case 2: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 2>), grid, block, 0, s, args); break;
-        case 3: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 3>), grid, block, 0, s, args); break;
-        case 4: case 5: case 6: case 7: case 8:
-            hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4>), grid, block, 0, s, args); break;
-        default: hipLaunchKernelGGL((mmvq_kernel<FMT, 2, 4>), grid, block, 0, s, args); break;
-    }
+    const dim3 grid((unsigned)std::min(args.groups, cu_count()));
+    const int cap = args.M <= 8 ? XCap<1>::KB : XCap<2>::KB;
+    if (args.KBp <= cap) launch_xl<FMT, true>(args, grid, s);
+    else launch_xl<FMT, false>(args, grid, s);
     return hipGetLastError();
 }
 
