@@ -68,8 +68,8 @@ MEASURED_TRAFFIC_BYTES = {
     "cfg3a_q4_K": 98550577,
     "cfg4_w8a8": 60068906,
     "cfg5_moe_iq1t": 387556612,
-    "dec8_q4_0": 11114121,
-    "dec8_q4_K": 45142006,
+    "dec8_q4_0": 11137667,
+    "dec8_q4_K": 45158633,
 }
 
 RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "i8_row": 32}
