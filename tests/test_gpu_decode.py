@@ -191,3 +191,39 @@ def test_decode_persistent_groups(env, fmt, M):
         rel = _rel(got[:, cols], ref)
         print(f"  K={K} rel err {rel:.3e}", flush=True)
         assert rel <= GATE, K
+
+
+@pytest.mark.parametrize("fmt,M", [("q4_0", 3), ("q4_K", 12)])
+def test_decode_graph_capture_replay_with_changed_contents(env, fmt, M):
+    # the decode launch captured with its quantiser in a hipGraph and replayed after the input
+    # changed: every replay equals the eager result and passes the gate
+    torch, mmq, orc = env
+    N, K = 160, 1024
+    dev = torch.device("cuda:0")
+    raw = gen.weights(fmt, N, K, seed=17, cfg=83)
+    packed = mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K)
+    xbuf = torch.zeros((M, K), dtype=torch.float32, device=dev)
+    act = torch.empty(mmq.act_bytes("q8_1", M, K), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mmq.quantize_act(xbuf, out=act)
+        mmq.gemm(fmt, packed, act, M, N, K, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mmq.quantize_act(xbuf, out=act)
+        mmq.gemm(fmt, packed, act, M, N, K, out=out)
+    for rep in range(3):
+        x = gen.act_f32(M, K, seed=200 + rep, cfg=83)
+        xbuf.copy_(torch.from_numpy(x))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = mmq.gemm(fmt, packed, mmq.quantize_act(torch.from_numpy(x).to(dev)), M, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        rq, rs, _ = orc.quantize_q8_1(x)
+        assert _rel(out.cpu().numpy(), orc.gemm_f64(fmt, raw, N, K, rq, rs)) <= GATE
