@@ -14,7 +14,9 @@
 //      over the unit offsets, reads its tokens' activation rows and writes each pair's own
 //      output row.
 // No host round trip: the grids are sized for the worst case and workgroups past the actual
-// unit counts leave at once.
+// unit counts leave at once. With at most 4 tokens (a decode batch, where the gather tiles
+// would be nearly empty) step 2 is the decode kernel instead, over (batch of up to 8 of one
+// expert's pairs, 16-row group) units (gemm_mmvq.hip).
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -142,6 +144,9 @@ hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void
                        gather_unit_tokens(), offs, ufull, utail, perm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // a decode batch of a few tokens: the decode kernel
+    if (mmvq_id_ok(t, T, top_k, K))
+        return launch_mmvq_id(t, packed, E, act, T, top_k, N, K, offs, perm, out, s);
     return launch_block_gather(t, packed, E, act, T, top_k, N, K, offs, ufull, utail, perm,
                                (int)gemm_id_max_units(E, P), (int)(E < P ? E : P), out, s);
 }

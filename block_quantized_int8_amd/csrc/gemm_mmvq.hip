@@ -188,7 +188,18 @@ struct MvArgs {
     int M, N, KBp, groups;      // groups: 16-row groups holding at least one real row
     void* out;
     int64_t ldo;
+    // MUL_MAT_ID with at most 16 tokens: the route kernel's pair offsets and expert order
+    int64_t w_stride;           // bytes between experts' packed matrices
+    const int32_t* offs;        // [E+1] first pair of each expert in `perm`
+    const int32_t* perm;        // pair ids (token * top_k + slot) in expert order
+    int E, top_k, P;
 };
+
+constexpr int MV_IDP = 256;     // MUL_MAT_ID decode: pairs (and so pair batches) at most
+// MUL_MAT_ID decode: tokens at most. Measured on 64 IQ1T experts of 2048 x 4096, top-8: with
+// 1, 2, 4 tokens the decode units take 20, 30, 42 us against the prefill gather's 36, 40, 47;
+// from 6 tokens on the gather's 32-slot tiles are faster.
+constexpr int MV_ID_TOK = 4;
 
 // LDS barrier that leaves global loads in flight (__syncthreads() would also wait for them)
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -198,14 +209,20 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // work is one stream of items (group, chunk), its chunks being wave, wave + MV_W, ... of every
 // group; loads run two items ahead. TG = token groups of 8 (1 or 2); NR = accumulator
 // registers holding a live token (min(M, 4)).
-template <mmq_wtype FMT, int TG, int NR, bool XL>
+template <mmq_wtype FMT, int TG, int NR, bool XL, bool ID>
 __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
+    static_assert(!ID || XL, "MUL_MAT_ID reads its gathered tokens from the staged rows");
     using T = VQ<FMT>;
     constexpr int TOK = 8 * TG;                              // staged token rows
     constexpr int XSLOTS = XL ? XCap<TG>::KB * 2 * TOK : 0;  // 16-byte slots; slot XSLOTS is zero
     __shared__ float red[2][MV_W][4 * TG][64];
     __shared__ uint2 tab[16];
     __shared__ __attribute__((aligned(16))) uint8_t xl[(XSLOTS + 1) * 16];
+    // MUL_MAT_ID: per batch of at most TOK pairs of one expert (expert id, first pair in
+    // expert order, pairs), the pair ids, and the scan's wave totals
+    __shared__ int s_e[ID ? MV_IDP : 1], s_po[ID ? MV_IDP : 1], s_me[ID ? MV_IDP : 1];
+    __shared__ int s_pp[ID ? MV_IDP : 1];
+    __shared__ int s_wt[MV_W + 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -223,7 +240,40 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     // L2 then fetches each scale line once.
     const int G = (int)gridDim.x, b = (int)blockIdx.x;
     const int off = (G % 16 == 0) ? 2 * (8 * (b >> 4) + (b & 7)) + ((b >> 3) & 1) : b;
-    const int ng = (a.groups - off + G - 1) / G;                         // >= 1
+    // work units: 16-row groups, or (pair batch, group) for MUL_MAT_ID, where a batch is up to
+    // TOK pairs of one expert (one batch per used expert when a token's experts are distinct;
+    // more for an expert named by several slots of a token)
+    int units = a.groups;
+    if constexpr (ID) {
+        const int EPT = (a.E + MV_W * 64 - 1) / (MV_W * 64);         // experts per thread
+        const int e0 = min(tid * EPT, a.E), e1 = min(e0 + EPT, a.E);
+        int nb = 0;
+        for (int e = e0; e < e1; ++e) nb += (a.offs[e + 1] - a.offs[e] + TOK - 1) / TOK;
+        int inc = nb;                                                // inclusive scan, wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += o;
+        }
+        if (lane == 63) s_wt[wave] = inc;
+        __syncthreads();
+        int u = inc - nb;
+        for (int w = 0; w < wave; ++w) u += s_wt[w];
+        if (tid == MV_W * 64 - 1) s_wt[MV_W] = u + nb;              // batches in all
+        for (int e = e0; e < e1; ++e) {
+            const int po = a.offs[e], c = a.offs[e + 1] - po;
+            for (int q = 0; q < c; q += TOK, ++u) {
+                s_e[u] = e;
+                s_po[u] = po + q;
+                s_me[u] = min(TOK, c - q);
+            }
+        }
+        for (int q = tid; q < a.P; q += MV_W * 64) s_pp[q] = a.perm[q];
+        __syncthreads();
+        units = s_wt[MV_W] * a.groups;
+    }
+    const int ng = (units - off + G - 1) / G;                            // >= 1 for dense grids
+    if (ng <= 0) return;                                                 // uniform: nothing to do
     const int cw = wave < nch ? (nch - wave + MV_W - 1) / MV_W : 0;      // this wave's chunks per group
     const int total = ng * cw;
 
@@ -238,24 +288,19 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     const int t0 = c16 & 7, t1 = 8 + (c16 & 7);
     const uint32_t o_x0 = (diag && t0 < a.M) ? (uint32_t)(fb * 1024 + (fh * 32 + t0) * 16) : OOR;
     const uint32_t o_x1 = (diag && t1 < a.M) ? (uint32_t)(fb * 1024 + (fh * 32 + t1) * 16) : OOR;
-    // scales of four blocks at once: k-group g holds block b0 + g
-    const uint32_t o_s = (uint32_t)(g * 128 + c16 * 4);                  // weight row c16
-    const uint32_t o_xs0 = t0 < a.M ? (uint32_t)(g * 128 + t0 * 4) : OOR;   // token of row c16
-    const uint32_t o_xs1 = t1 < a.M ? (uint32_t)(g * 128 + t1 * 4) : OOR;
-    // q4_K min term (rows 0-7 only): token c16 (< 8) of block b0 + g against weight row c16
-    const uint32_t o_mx0 = (c16 < 8 && c16 < a.M) ? (uint32_t)(g * 128 + c16 * 4) : OOR;
-    const uint32_t o_mx1 = (c16 < 8 && 8 + c16 < a.M) ? (uint32_t)(g * 128 + (8 + c16) * 4) : OOR;
+    // scales of four blocks at once: k-group g holds block b0 + g (weight row c16; the token
+    // scales of the token of row c16, and q4_K's min term for rows 0-7, per unit in load())
+    const uint32_t o_s = (uint32_t)(g * 128 + c16 * 4);
     // iq1t: the scale dword of this lane's own (block 2p + fb, row c16), for its meta byte
     const uint32_t o_wso = (uint32_t)(fb * 128 + c16 * 4);
     const uint8_t* const xsb = reinterpret_cast<const uint8_t*>(a.xs2);
     const uint8_t* const xmb = reinterpret_cast<const uint8_t*>(a.xsx);
     const uint8_t* const wsb = a.w + a.w_scale_off;
-    const uint8_t* const wmb = a.w + a.w_min_off;
 
     struct Chunk {
         typename T::Raw w[2];
         v4i x[TG][2];                // register path only
-        int b0;
+        int b0, tk[TG];
         uint32_t ws, xs[TG];
         uint32_t wso[2];
         float xm[TG], wm;
@@ -264,11 +309,28 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     auto load = [&](int t, Chunk& k) __attribute__((always_inline)) {
         t = min(t, total - 1);
         const int i = t / cw, j = t - i * cw;
-        const int q = off + i * G;                                      // 16-row group
+        int q = off + i * G;                                            // 16-row group
+        const uint8_t* wx = a.w;                                        // this unit's weights
+        int me = a.M, po = 0;                                           // its tokens
+        if constexpr (ID) {
+            const int ue = q / a.groups;
+            q -= ue * a.groups;
+            wx += (int64_t)s_e[ue] * a.w_stride;
+            me = s_me[ue];
+            po = s_po[ue];
+        }
+        // the token of this lane's rows (t0 / t1 of the unit), -1 past its token count
+#pragma unroll
+        for (int x = 0; x < TG; ++x) {
+            const int ix = (c16 & 7) + 8 * x;
+            int tk = ix < me ? ix : -1;
+            if constexpr (ID) tk = ix < me ? s_pp[po + ix] / a.top_k : -1;
+            k.tk[x] = tk;
+        }
         const int half = q & 1;
         const int b0 = (wave + j * MV_W) * MV_CH;
         const int64_t tb = (int64_t)(q >> 1) * KBp + b0;                // (tile, block) index
-        const rsrc_t rw = rsrc(a.w + tb * T::FB + half * (MV_ROWS * LB), MV_CH * T::FB);
+        const rsrc_t rw = rsrc(wx + tb * T::FB + half * (MV_ROWS * LB), MV_CH * T::FB);
         const rsrc_t rx = rsrc(a.xq + (int64_t)b0 * 1024, MV_CH * 1024);
         k.b0 = b0;
 #pragma unroll
@@ -280,11 +342,12 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             }
         }
         if constexpr (!T::ROW) {
-            const rsrc_t rs = rsrc(wsb + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128);
+            const rsrc_t rs = rsrc(wx + a.w_scale_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128);
             const rsrc_t rxs = rsrc(xsb + (int64_t)b0 * 128, MV_CH * 128);
             k.ws = ld32(rs, o_s);
-            k.xs[0] = ld32(rxs, o_xs0);
-            if constexpr (TG == 2) k.xs[1] = ld32(rxs, o_xs1);
+#pragma unroll
+            for (int x = 0; x < TG; ++x)       // token of row c16, block b0 + g
+                k.xs[x] = ld32(rxs, k.tk[x] >= 0 ? (uint32_t)(g * 128 + k.tk[x] * 4) : OOR);
             if constexpr (T::META) {
                 k.wso[0] = ld32(rs, o_wso);
                 k.wso[1] = ld32(rs, o_wso + 256);
@@ -292,9 +355,10 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         }
         if constexpr (T::MIN) {
             const rsrc_t rxm = rsrc(xmb + (int64_t)b0 * 128, MV_CH * 128);
-            k.xm[0] = __builtin_bit_cast(float, ld32(rxm, o_mx0));
-            if constexpr (TG == 2) k.xm[1] = __builtin_bit_cast(float, ld32(rxm, o_mx1));
-            k.wm = __builtin_bit_cast(float, ld32(rsrc(wmb + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128), o_s));
+#pragma unroll
+            for (int x = 0; x < TG; ++x)       // rows 0-7 only: token of row c16 = k.tk[x]
+                k.xm[x] = __builtin_bit_cast(float, ld32(rxm, (c16 < 8 && k.tk[x] >= 0) ? (uint32_t)(g * 128 + k.tk[x] * 4) : OOR));
+            k.wm = __builtin_bit_cast(float, ld32(rsrc(wx + a.w_min_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128), o_s));
         }
     };
 
@@ -317,7 +381,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
 #pragma unroll
             for (int x = 0; x < TG; ++x) {
                 if constexpr (XL) {
-                    const int sl = diag ? ((k.b0 + 2 * p + fb) * 2 + fh) * TOK + (x == 0 ? t0 : t1) : XSLOTS;
+                    const int sl = (diag && k.tk[x] >= 0) ? ((k.b0 + 2 * p + fb) * 2 + fh) * TOK + k.tk[x] : XSLOTS;
                     xo[x][p] = *reinterpret_cast<const v4i*>(xl + sl * 16);
                 } else {
                     xo[x][p] = k.x[x][p];
@@ -371,8 +435,15 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             // token m, column n: register (m & 3) of lanes 16*((m & 7) >> 2) + n (rows 0-7,
             // even blocks) and that + 32 (rows 8-15, odd blocks), token group m >> 3
             const int m = tid >> 4, n = tid & 15;
-            const int col = (off + i * G) * MV_ROWS + n;
-            if (m < a.M && col < a.N) {
+            int q = off + i * G, me = a.M, row = m;
+            if constexpr (ID) {
+                const int ue = q / a.groups;
+                q -= ue * a.groups;
+                me = s_me[ue];
+                row = m < me ? s_pp[s_po[ue] + m] : 0;     // the pair's own output row
+            }
+            const int col = q * MV_ROWS + n;
+            if (m < me && col < a.N) {
                 const int r = 4 * (m >> 3) + (m & 3);
                 const int la = 16 * ((m & 7) >> 2) + n, lb = la + 32;
                 if constexpr (T::ROW) {
@@ -381,12 +452,12 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
                     for (int w = 0; w < MV_W; ++w)
                         s += __builtin_bit_cast(int, red[pb][w][r][la]) + __builtin_bit_cast(int, red[pb][w][r][lb]);
                     const float sw = reinterpret_cast<const float*>(wsb)[col];
-                    reinterpret_cast<uint16_t*>(a.out)[(int64_t)m * a.ldo + col] = bf16_rne(((float)s * a.sa[m]) * sw);
+                    reinterpret_cast<uint16_t*>(a.out)[(int64_t)row * a.ldo + col] = bf16_rne(((float)s * a.sa[m]) * sw);
                 } else {
                     float s = 0.f;
 #pragma unroll
                     for (int w = 0; w < MV_W; ++w) s += red[pb][w][r][la] + red[pb][w][r][lb];
-                    reinterpret_cast<float*>(a.out)[(int64_t)m * a.ldo + col] = s * T::POST;
+                    reinterpret_cast<float*>(a.out)[(int64_t)row * a.ldo + col] = s * T::POST;
                 }
             }
         }
@@ -464,16 +535,21 @@ int cu_count() {
     return cus[dev];
 }
 
-template <mmq_wtype FMT, bool XL>
+template <mmq_wtype FMT, bool XL, bool ID = false>
 void launch_xl(const MvArgs& args, dim3 grid, hipStream_t s) {
     const dim3 block(MV_W * 64);
+    if constexpr (ID) {
+        // batches of up to 8 pairs whatever the token count: every register is live
+        hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4, XL, ID>), grid, block, 0, s, args);
+        return;
+    }
     switch (args.M) {
-        case 1: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 1, XL>), grid, block, 0, s, args); break;
-        case 2: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 2, XL>), grid, block, 0, s, args); break;
-        case 3: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 3, XL>), grid, block, 0, s, args); break;
+        case 1: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 1, XL, ID>), grid, block, 0, s, args); break;
+        case 2: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 2, XL, ID>), grid, block, 0, s, args); break;
+        case 3: hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 3, XL, ID>), grid, block, 0, s, args); break;
         case 4: case 5: case 6: case 7: case 8:
-            hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4, XL>), grid, block, 0, s, args); break;
-        default: hipLaunchKernelGGL((mmvq_kernel<FMT, 2, 4, XL>), grid, block, 0, s, args); break;
+            hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4, XL, ID>), grid, block, 0, s, args); break;
+        default: hipLaunchKernelGGL((mmvq_kernel<FMT, 2, 4, XL, ID>), grid, block, 0, s, args); break;
     }
 }
 
@@ -489,6 +565,50 @@ hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
 }  // namespace
 
 int mmvq_max_tokens() { return MV_TOK; }
+
+bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K) {
+    if (t == MMQ_I8_ROW || T < 1 || T > MV_ID_TOK || T * top_k > MV_IDP) return false;
+    return round_up(K / QK, KB_ALIGN) <= XCap<1>::KB;          // batches of 8: one token group
+}
+
+hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void* act, int64_t T,
+                          int64_t top_k, int64_t N, int64_t K, const int32_t* offs,
+                          const int32_t* perm, void* out, hipStream_t s) {
+    if (!mmvq_id_ok(t, T, top_k, K)) return hipErrorInvalidValue;
+    const PackedLayout P = packed_layout(t, N, K);
+    const ActQ81Layout L = act_q8_1_layout(T, K);
+    const uint8_t* ab = static_cast<const uint8_t*>(act);
+    MvArgs args{};
+    args.w = static_cast<const uint8_t*>(packed);
+    args.w_scale_off = P.scale_off;
+    args.w_min_off = P.min_off;
+    args.w_stride = P.bytes;
+    args.M = (int)T;
+    args.N = (int)N;
+    args.KBp = (int)P.KBp;
+    args.groups = (int)ceil_div(N, MV_ROWS);
+    args.out = out;
+    args.ldo = N;
+    args.xq = ab + L.xq_off;
+    args.xs2 = reinterpret_cast<const uint32_t*>(ab + L.xs2_off);
+    args.xsx = reinterpret_cast<const float*>(ab + L.xsx_off);
+    args.offs = offs;
+    args.perm = perm;
+    args.E = (int)E;
+    args.top_k = (int)top_k;
+    args.P = (int)(T * top_k);
+    // grid for the most units possible (a batch per pair at most); the rest leave at once
+    const int64_t units = T * top_k * args.groups;
+    const dim3 grid((unsigned)std::min<int64_t>(units, cu_count()));
+    switch (t) {
+        case MMQ_Q8_0: launch_xl<MMQ_Q8_0, true, true>(args, grid, s); break;
+        case MMQ_Q4_0: launch_xl<MMQ_Q4_0, true, true>(args, grid, s); break;
+        case MMQ_Q4_K: launch_xl<MMQ_Q4_K, true, true>(args, grid, s); break;
+        case MMQ_IQ1T: launch_xl<MMQ_IQ1T, true, true>(args, grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                        int64_t K, void* out, int64_t ldo, hipStream_t s) {

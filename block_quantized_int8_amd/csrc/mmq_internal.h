@@ -159,6 +159,13 @@ hipError_t launch_w8a8_gemm(const void* packed, const void* act, int64_t M, int6
 int mmvq_max_tokens();
 hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                        int64_t K, void* out, int64_t ldo, hipStream_t s);
+// MUL_MAT_ID with at most 4 tokens (and 256 pairs, K within the staging capacity): the
+// decode kernel over (batch of up to 8 of one expert's pairs, 16-row group) units, from the
+// route kernel's pair offsets and expert order.
+bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K);
+hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void* act, int64_t T,
+                          int64_t top_k, int64_t N, int64_t K, const int32_t* offs,
+                          const int32_t* perm, void* out, hipStream_t s);
 hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
                           const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
                           void* out, void* workspace, size_t ws_bytes, hipStream_t s);
