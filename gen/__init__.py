@@ -217,4 +217,6 @@ CONFIGS = {
     "dec8_q4_K_down": dict(cfg=3, fmt="q4_K", M=8, N=4096, K=14336, out="f32"),
     "dec8_iq1t": dict(cfg=5, fmt="iq1t", M=8, N=2048, K=4096, out="f32"),
     "dec8_w8a8": dict(cfg=4, fmt="i8_row", M=8, N=1536, K=4096, out="bf16"),
+    "dec1_moe_iq1t": dict(cfg=5, fmt="iq1t", M=1, N=2048, K=4096, out="f32", E=64, top_k=8),
+    "dec4_moe_iq1t": dict(cfg=5, fmt="iq1t", M=4, N=2048, K=4096, out="f32", E=64, top_k=8),
 }
