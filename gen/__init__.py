@@ -24,6 +24,13 @@ K/256 consecutive blocks):
           sub-scales s (one per 16 values, LSB-first bit stream), 4 bytes of
           sign bits (one per 8 values; 0 -> delta=+1/8, 1 -> delta=-1/8),
           then f16 d.                             w = d*(2s+1)*(g+delta)
+* iq1c  - 56 B per 256 values (the IQ1_M codebook form, 1.75 bits per value):
+          32 bytes qs (low 8 bits of each 8-value group's 11-bit grid index),
+          16 bytes qh (byte j: groups 2j and 2j+1 in its low and high nibble;
+          nibble bits 0-2 = index bits 8-10, bit 3 = that group's delta sign),
+          6 bytes of 3-bit sub-scales s (one per 16 values, LSB-first), f16 d.
+          The grid is a table of 2048 uint16 entries, each eight 2-bit codes
+          c = g+1 (value j at bits 2j..2j+1).     w = d*(2s+1)*(g+delta)
 * i8_row - int8 [N][K] plus one f32 scale per row.            w = sw[n]*q
 
 The shapes and value distributions follow the five workloads the MMQ pages
@@ -37,11 +44,13 @@ import numpy as np
 QK = 32          # values per quantisation block
 QK_SUPER = 256   # values per K-quant / iq1t super-block
 
-ROW_BYTES_PER_BLOCK = {"q8_0": 34, "q4_0": 18, "q4_K": 144, "iq1t": 76}
-VALUES_PER_BLOCK = {"q8_0": 32, "q4_0": 32, "q4_K": 256, "iq1t": 256}
+ROW_BYTES_PER_BLOCK = {"q8_0": 34, "q4_0": 18, "q4_K": 144, "iq1t": 76, "iq1c": 56}
+VALUES_PER_BLOCK = {"q8_0": 32, "q4_0": 32, "q4_K": 256, "iq1t": 256, "iq1c": 256}
 
 # tensor ids inside a configuration's seed sequence
-T_ACT, T_WEIGHT, T_IDS, T_OUTLIER = 0, 1, 2, 3
+T_ACT, T_WEIGHT, T_IDS, T_OUTLIER, T_GRID = 0, 1, 2, 3, 4
+GRID_SIZE = 2048        # iq1c codebook entries (11-bit index)
+GRID_CFG = 90           # the codebook's own seed-sequence slot
 
 
 def rng(seed: int, cfg: int, tensor: int) -> np.random.Generator:
@@ -165,6 +174,45 @@ def weights_iq1t(N: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T
     return out.reshape(N, -1)
 
 
+def iq1c_grid(seed: int = 0) -> np.ndarray:
+    """The iq1c codebook: 2048 distinct ternary 8-vectors drawn uniformly without replacement
+    from all 3^8 = 6561, each stored as eight 2-bit codes c = g+1 (value j at bits 2j..2j+1).
+    The pages name an 11-bit grid index per 8 values but do not print the grid, so this one is
+    self-generated; it is an input of the repack and of the oracle alike."""
+    pick = rng(seed, GRID_CFG, T_GRID).choice(3 ** 8, size=GRID_SIZE, replace=False)
+    codes = np.zeros(GRID_SIZE, dtype=np.uint16)
+    v = pick.copy()
+    for j in range(8):
+        codes |= ((v % 3).astype(np.uint16) << np.uint16(2 * j))
+        v //= 3
+    return codes
+
+
+IQ1C_GRID = iq1c_grid()
+
+
+def weights_iq1c(N: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T_WEIGHT,
+                 d_value: float = 0.02 / 4) -> np.ndarray:
+    """IQ1_M codebook rows: per 8 values a grid index uniform in 0..2047 and a delta sign
+    uniform in {0, 1}; s uniform in 0..7 per 16 values; d = f16(d_value) per super-block."""
+    nsb = K // QK_SUPER
+    r = rng(seed, cfg, tensor)
+    out = np.empty((N, nsb, 56), dtype=np.uint8)
+    idx = r.integers(0, GRID_SIZE, size=(N, nsb, 32), dtype=np.uint16)
+    sgn = r.integers(0, 2, size=(N, nsb, 32), dtype=np.uint8)
+    s = r.integers(0, 8, size=(N, nsb, 16), dtype=np.uint64)
+    out[..., 0:32] = (idx & 0xFF).astype(np.uint8)
+    nib = ((idx >> 8) & 7).astype(np.uint8) | (sgn << 3)                  # one nibble per group
+    out[..., 32:48] = nib[..., 0::2] | (nib[..., 1::2] << 4)
+    word = np.zeros((N, nsb), dtype=np.uint64)
+    for h in range(16):
+        word |= s[..., h] << np.uint64(3 * h)
+    for b in range(6):
+        out[..., 48 + b] = ((word >> np.uint64(8 * b)) & np.uint64(0xFF)).astype(np.uint8)
+    out[..., 54:56] = np.full((N, nsb), np.float16(d_value)).view(np.uint8).reshape(N, nsb, 2)
+    return out.reshape(N, -1)
+
+
 def i8_rows(R: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T_WEIGHT):
     """Per-row int8: v ~ N(0,1), scale = max|v|/127 (f32), q = clip(rint(v/scale), -127, 127)."""
     v = rng(seed, cfg, tensor).standard_normal((R, K), dtype=np.float32)
@@ -182,6 +230,8 @@ def weights(fmt: str, N: int, K: int, **kw):
         return weights_q4_K(N, K, **kw)
     if fmt == "iq1t":
         return weights_iq1t(N, K, **kw)
+    if fmt == "iq1c":
+        return weights_iq1c(N, K, **kw)
     if fmt == "i8_row":
         return i8_rows(N, K, **kw)
     raise ValueError(fmt)
@@ -207,6 +257,8 @@ CONFIGS = {
     "cfg3b_q4_K": dict(cfg=3, fmt="q4_K", M=512, N=4096, K=14336, out="f32"),
     "cfg4_w8a8": dict(cfg=4, fmt="i8_row", M=3072, N=1536, K=4096, out="bf16"),
     "cfg5_moe_iq1t": dict(cfg=5, fmt="iq1t", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
+    # the same MoE with the IQ1_M codebook form of the weights (1.75 bits per value)
+    "cfg5c_moe_iq1c": dict(cfg=5, fmt="iq1c", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
     # decode batches (a few tokens) on the same weight shapes: the small-M path
     "dec1_q4_0": dict(cfg=2, fmt="q4_0", M=1, N=4096, K=4096, out="f32", outlier_rate=1e-3),
     "dec8_q4_0": dict(cfg=2, fmt="q4_0", M=8, N=4096, K=4096, out="f32", outlier_rate=1e-3),
@@ -216,6 +268,7 @@ CONFIGS = {
     "dec8_q4_K": dict(cfg=3, fmt="q4_K", M=8, N=14336, K=4096, out="f32"),
     "dec8_q4_K_down": dict(cfg=3, fmt="q4_K", M=8, N=4096, K=14336, out="f32"),
     "dec8_iq1t": dict(cfg=5, fmt="iq1t", M=8, N=2048, K=4096, out="f32"),
+    "dec8_iq1c": dict(cfg=5, fmt="iq1c", M=8, N=2048, K=4096, out="f32"),
     "dec8_w8a8": dict(cfg=4, fmt="i8_row", M=8, N=1536, K=4096, out="bf16"),
     "dec1_moe_iq1t": dict(cfg=5, fmt="iq1t", M=1, N=2048, K=4096, out="f32", E=64, top_k=8),
     "dec4_moe_iq1t": dict(cfg=5, fmt="iq1t", M=4, N=2048, K=4096, out="f32", E=64, top_k=8),

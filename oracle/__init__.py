@@ -36,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mmq_oracle.c")
 _LIB = os.path.join(_HERE, "liborc.so")
 
-FMT_ID = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3}
+FMT_ID = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "iq1c": 4}
 
 
 def build(force: bool = False) -> str:
@@ -67,12 +67,15 @@ def lib():
         L.orc_float_to_bf16.restype = ctypes.c_uint16
         L.orc_quantize_q8_1.argtypes = [P, I, I, I, P, P, P]
         L.orc_quantize_i8_token.argtypes = [P, I, I, I, P, P]
-        L.orc_decode_row.argtypes = [ctypes.c_int, P, I, P, P, P]
-        L.orc_partials.argtypes = [ctypes.c_int, P, I, I, P, I, P]
+        L.orc_decode_row.argtypes = [ctypes.c_int, P, I, P, P, P, P, P]
+        L.orc_decode_row.restype = ctypes.c_int
+        L.orc_partials.argtypes = [ctypes.c_int, P, I, I, P, P, I, P]
         L.orc_partials.restype = ctypes.c_int
         L.orc_partials16_iq1t.argtypes = [P, I, I, P, I, P]
-        L.orc_gemm_rows.argtypes = [ctypes.c_int, P, I, I, P, P, P, I, I, P, I]
-        L.orc_gemm.argtypes = [ctypes.c_int, P, I, I, P, P, P, I, P]
+        L.orc_gemm_rows.argtypes = [ctypes.c_int, P, I, I, P, P, P, P, I, I, P, I]
+        L.orc_gemm_rows.restype = ctypes.c_int
+        L.orc_gemm.argtypes = [ctypes.c_int, P, I, I, P, P, P, P, I, P]
+        L.orc_gemm.restype = ctypes.c_int
         L.orc_gemm_w8a8.argtypes = [P, P, I, P, P, I, I, P, P, I, I]
         L.orc_gemm_w8a8.restype = ctypes.c_int
         L.orc_num_threads.restype = ctypes.c_int
@@ -142,24 +145,44 @@ def quantize_i8_token(x: np.ndarray):
 
 # ------------------------------------------------------------ C decode / partials
 
-def decode_row_c(fmt: str, raw_row: np.ndarray, K: int):
-    """C decoder for one row: (wq int16 [K], wd f32 [K/16], wm f32 [K/32])."""
+def _grid_arg(fmt: str, grid):
+    """The iq1c codebook as a contiguous uint16 [2048] array (required for iq1c only)."""
+    if fmt != "iq1c":
+        return None
+    if grid is None:
+        raise ValueError("iq1c needs its grid (uint16 [2048])")
+    g = _c(grid, np.uint16)
+    if g.shape != (2048,):
+        raise ValueError("the iq1c grid has 2048 entries")
+    return g
+
+
+def decode_row_c(fmt: str, raw_row: np.ndarray, K: int, grid=None):
+    """C decoder for one row: (wq int16 [K], wd f32 [K/16], wm f32 [K/32], mult int16 [K/16])."""
     raw_row = _c(raw_row, np.uint8)
+    g = _grid_arg(fmt, grid)
     wq = np.empty(K, np.int16)
     wd = np.empty(K // 16, np.float32)
     wm = np.empty(K // 32, np.float32)
-    lib().orc_decode_row(FMT_ID[fmt], _p(raw_row), K, _p(wq), _p(wd), _p(wm))
-    return wq, wd, wm
+    mult = np.empty(K // 16, np.int16)
+    rc = lib().orc_decode_row(FMT_ID[fmt], _p(raw_row), K, None if g is None else _p(g), _p(wq), _p(wd),
+                              _p(wm), _p(mult))
+    if rc != 0:
+        raise ValueError("invalid iq1c grid code (3)")
+    return wq, wd, wm, mult
 
 
-def partials(fmt: str, raw: np.ndarray, N: int, K: int, xq: np.ndarray) -> np.ndarray:
-    """Exact int32 block partials P[m,n,b] (iq1t: the folded per-32 integer
+def partials(fmt: str, raw: np.ndarray, N: int, K: int, xq: np.ndarray, grid=None) -> np.ndarray:
+    """Exact int32 block partials P[m,n,b] (iq1t, iq1c: the folded per-32 integer
     sum_h (2s_h+1)*P16_h, PR #304's fold)."""
     raw = _c(raw, np.uint8)
     xq = _c(xq, np.int8)
+    g = _grid_arg(fmt, grid)
     M = xq.shape[0]
     P = np.empty((M, N, K // 32), np.int32)
-    rc = lib().orc_partials(FMT_ID[fmt], _p(raw), N, K, _p(xq), M, _p(P))
+    rc = lib().orc_partials(FMT_ID[fmt], _p(raw), N, K, None if g is None else _p(g), _p(xq), M, _p(P))
+    if rc == -2:
+        raise ValueError("invalid iq1c grid code (3)")
     if rc != 0:
         raise OverflowError("a block partial left int32")
     return P
@@ -174,17 +197,21 @@ def partials16_iq1t(raw: np.ndarray, N: int, K: int, xq: np.ndarray) -> np.ndarr
     return P
 
 
-def gemm_c(fmt: str, raw: np.ndarray, N: int, K: int, xq, xs, xsum, rows=None) -> np.ndarray:
+def gemm_c(fmt: str, raw: np.ndarray, N: int, K: int, xq, xs, xsum, rows=None, grid=None) -> np.ndarray:
     """Per-block C oracle output (double accumulation, one f32 rounding). rows=(m0,m1)
     restricts to a row range."""
     raw = _c(raw, np.uint8)
     xq = _c(xq, np.int8)
     xs = _c(xs, np.float32)
     xsum = _c(xsum, np.int32)
+    g = _grid_arg(fmt, grid)
     M = xq.shape[0]
     m0, m1 = (0, M) if rows is None else rows
     out = np.empty((m1 - m0, N), np.float32)
-    lib().orc_gemm_rows(FMT_ID[fmt], _p(raw), N, K, _p(xq), _p(xs), _p(xsum), m0, m1, _p(out), N)
+    rc = lib().orc_gemm_rows(FMT_ID[fmt], _p(raw), N, K, None if g is None else _p(g), _p(xq), _p(xs),
+                             _p(xsum), m0, m1, _p(out), N)
+    if rc != 0:
+        raise ValueError("invalid iq1c grid code (3)")
     return out
 
 
@@ -213,10 +240,11 @@ def _f16(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
-def dequant_weights(fmt: str, raw: np.ndarray, N: int, K: int) -> np.ndarray:
+def dequant_weights(fmt: str, raw: np.ndarray, N: int, K: int, grid=None) -> np.ndarray:
     """w_hat [N,K] in f64 from each format's defining formula (independent of the C decoder):
     q8_0 d*q; q4_0 d*(nib-8); q4_K d*sc*nib - dmin*m (minfer R1 section 2.2);
-    iq1t d*(2s+1)*(g+delta) (PR #304 description)."""
+    iq1t and iq1c d*(2s+1)*(g+delta) (PR #304 description; iq1c takes the eight g of a group
+    from the grid entry its 11-bit index names)."""
     raw = np.asarray(raw, dtype=np.uint8).reshape(N, -1)
     if fmt == "q8_0":
         b = raw.reshape(N, K // 32, 34)
@@ -253,6 +281,21 @@ def dequant_weights(fmt: str, raw: np.ndarray, N: int, K: int) -> np.ndarray:
         d = _f16(b[..., 74].astype(np.uint16) | (b[..., 75].astype(np.uint16) << 8))
         w = (d[..., None] * np.repeat(2.0 * s + 1.0, 16, axis=-1)) * (g + np.repeat(delta, 8, axis=-1))
         return w.reshape(N, K)
+    if fmt == "iq1c":
+        table = _grid_arg(fmt, grid)
+        gvals = np.stack([(table >> (2 * j)) & 3 for j in range(8)], axis=-1).astype(np.int64)
+        if np.any(gvals == 3):
+            raise ValueError("invalid iq1c grid code (3)")
+        b = raw.reshape(N, K // 256, 56)
+        qh = np.stack([b[..., 32:48] & 0xF, b[..., 32:48] >> 4], axis=-1).reshape(N, K // 256, 32)
+        idx = b[..., 0:32].astype(np.int64) + 256 * (qh & 7).astype(np.int64)
+        g = gvals[idx].astype(np.float64) - 1.0                                # [N, sb, 32, 8]
+        delta = np.where((qh >> 3) == 1, -0.125, 0.125)
+        s_bits = np.unpackbits(b[..., 48:54], axis=-1, bitorder="little")[..., :48].reshape(N, K // 256, 16, 3)
+        s = s_bits @ np.array([1.0, 2.0, 4.0])
+        d = _f16(b[..., 54].astype(np.uint16) | (b[..., 55].astype(np.uint16) << 8))
+        w = (d[..., None] * np.repeat(2.0 * s + 1.0, 16, axis=-1)) * (g + delta[..., None]).reshape(N, K // 256, 256)
+        return w.reshape(N, K)
     raise ValueError(fmt)
 
 
@@ -263,19 +306,19 @@ def dequant_act(xq: np.ndarray, xs: np.ndarray) -> np.ndarray:
 
 
 def gemm_f64(fmt: str, raw: np.ndarray, N: int, K: int, xq: np.ndarray, xs: np.ndarray,
-             rows=None, cols=None) -> np.ndarray:
+             rows=None, cols=None, grid=None) -> np.ndarray:
     """The definition: out[m,n] = sum_k x_hat[m,k] * w_hat[n,k] in f64 (optionally on a
     subset of rows / weight rows, for sampled checks of large shapes)."""
     xh = dequant_act(xq if rows is None else xq[rows], xs if rows is None else xs[rows])
     raw2 = np.asarray(raw, np.uint8).reshape(N, -1)
     if cols is not None:
         raw2 = raw2[cols]
-    wh = dequant_weights(fmt, raw2, raw2.shape[0], K)
+    wh = dequant_weights(fmt, raw2, raw2.shape[0], K, grid=grid)
     return xh @ wh.T
 
 
 def moe_f64(fmt: str, raw_experts: np.ndarray, E: int, N: int, K: int, xq, xs, ids,
-            pairs=None) -> np.ndarray:
+            pairs=None, grid=None) -> np.ndarray:
     """MUL_MAT_ID: out[t, j, :] = dense(W_{ids[t,j]}, x[t]) (PR #304: MUL_MAT_ID routes each
     token's rows through the selected experts). pairs: optional list of (t, j) to evaluate;
     returns [T, top_k, N] (NaN where not evaluated) or [len(pairs), N]."""
@@ -287,12 +330,12 @@ def moe_f64(fmt: str, raw_experts: np.ndarray, E: int, N: int, K: int, xq, xs, i
             tt, jj = np.nonzero(ids == e)
             if len(tt) == 0:
                 continue
-            out[tt, jj] = gemm_f64(fmt, raw_experts[e], N, K, xq[tt], xs[tt])
+            out[tt, jj] = gemm_f64(fmt, raw_experts[e], N, K, xq[tt], xs[tt], grid=grid)
         return out
     res = np.zeros((len(pairs), N), np.float64)
     for i, (t, j) in enumerate(pairs):
         e = int(ids[t, j])
-        res[i] = gemm_f64(fmt, raw_experts[e], N, K, xq[t:t + 1], xs[t:t + 1])[0]
+        res[i] = gemm_f64(fmt, raw_experts[e], N, K, xq[t:t + 1], xs[t:t + 1], grid=grid)[0]
     return res
 
 

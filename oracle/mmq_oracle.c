@@ -18,7 +18,8 @@
  *    contraction out[m,n] = sum over 32-blocks of (xs*wd) * sum(xq*wq).
  *  - llama.cpp PR #304 "CUDA: add IQ1_M to MMQ", description: an IQ1_M value
  *    is d*(2s+1)*(g+delta); 8(g+delta) = 8g +- 1 and the per-16 scale becomes
- *    d(2s+1)/8.
+ *    d(2s+1)/8. In the codebook form the ternary g of 8 values come from one
+ *    grid entry named by an 11-bit index (the grid itself is an input here).
  *  - "INT8 W8A8 GEMM - Prefill" (metainfer), section 1: int8 activations with
  *    a per-token f32 scale, int8 weights with a per-channel f32 scale, int32
  *    accumulation, epilogue fragment -> scale -> bf16, no bias.
@@ -42,6 +43,7 @@
 #define ORC_Q4_0 1
 #define ORC_Q4_K 2
 #define ORC_IQ1T 3
+#define ORC_IQ1C 4
 
 /* ---------------------------------------------------------------- scalars */
 
@@ -163,16 +165,22 @@ void orc_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_t ldx,
 
 /* Decode one weight row into:
  *   wq[K]      - the integer that enters the int8 dot for each value
- *                (q8_0: q; q4_0: nib-8; q4_K: nib (unsigned); iq1t: 8g+sigma)
+ *                (q8_0: q; q4_0: nib-8; q4_K: nib (unsigned); iq1t/iq1c: 8g+sigma)
  *   wd[K/16]   - the f32 scale multiplying each 16-value half of the dot
- *                (q8_0/q4_0: d; q4_K: d*sc; iq1t: d*(2s+1)/8)
+ *                (q8_0/q4_0: d; q4_K: d*sc; iq1t/iq1c: d*(2s+1)/8)
  *   wm[K/32]   - the f32 coefficient of the activation block sum
  *                (q4_K: -dmin*m, others 0)
- * Every scale here is exact in f32 (an f16 times a small integer, or /8).    */
-static void decode_row(int fmt, const uint8_t* row, int64_t K,
-                       int16_t* wq, float* wd, float* wm) {
+ *   mult[K/16] - the integer factor of each half in the folded block partial
+ *                (iq1t/iq1c: 2s+1, others 1)
+ * Every scale here is exact in f32 (an f16 times a small integer, or /8).
+ * grid: the iq1c codebook (2048 entries of eight 2-bit codes), else unused.
+ * Returns 0, or -1 if an iq1c grid entry holds the invalid code 3.          */
+static int decode_row(int fmt, const uint8_t* row, int64_t K, const uint16_t* grid,
+                      int16_t* wq, float* wd, float* wm, int16_t* mult) {
     const int64_t KB = K / 32;
+    int bad = 0;
     for (int64_t b = 0; b < KB; ++b) wm[b] = 0.0f;
+    for (int64_t h = 0; h < K / 16; ++h) mult[h] = 1;
     if (fmt == ORC_Q8_0) {
         for (int64_t b = 0; b < KB; ++b) {
             const uint8_t* blk = row + b * 34;
@@ -216,7 +224,7 @@ static void decode_row(int fmt, const uint8_t* row, int64_t K,
                 wm[b] = -(dmin * (float)mm);
             }
         }
-    } else { /* ORC_IQ1T */
+    } else if (fmt == ORC_IQ1T) {
         for (int64_t sb = 0; sb < K / 256; ++sb) {
             const uint8_t* blk = row + sb * 76;
             float d = orc_half_to_float(rd16(blk + 74));
@@ -231,14 +239,43 @@ static void decode_row(int fmt, const uint8_t* row, int64_t K,
             for (int h = 0; h < 16; ++h) {
                 int s = (int)((sw >> (3 * h)) & 7u);
                 wd[sb * 16 + h] = d * (float)(2 * s + 1) / 8.0f;
+                mult[sb * 16 + h] = (int16_t)(2 * s + 1);
+            }
+        }
+    } else if (fmt == ORC_IQ1C) {
+        /* group q (values 8q..8q+7): index = qs[q] | (index bits 8-10 from the nibble of
+         * qh[q/2] selected by q%2), delta sign = bit 3 of that nibble; the grid entry gives
+         * the eight codes c = g+1. */
+        for (int64_t sb = 0; sb < K / 256; ++sb) {
+            const uint8_t* blk = row + sb * 56;
+            float d = orc_half_to_float(rd16(blk + 54));
+            uint64_t sw = 0;
+            for (int i = 0; i < 6; ++i) sw |= (uint64_t)blk[48 + i] << (8 * i);
+            for (int q = 0; q < 32; ++q) {
+                int nib = (blk[32 + q / 2] >> (4 * (q % 2))) & 15;
+                int idx = blk[q] | ((nib & 7) << 8);
+                int sgn = (nib >> 3) & 1;
+                uint16_t entry = grid[idx];
+                for (int j = 0; j < 8; ++j) {
+                    int c = (entry >> (2 * j)) & 3;
+                    if (c == 3) bad = 1;
+                    wq[sb * 256 + 8 * q + j] = (int16_t)(8 * (c - 1) + (sgn ? -1 : 1));
+                }
+            }
+            for (int h = 0; h < 16; ++h) {
+                int s = (int)((sw >> (3 * h)) & 7u);
+                wd[sb * 16 + h] = d * (float)(2 * s + 1) / 8.0f;
+                mult[sb * 16 + h] = (int16_t)(2 * s + 1);
             }
         }
     }
+    return bad ? -1 : 0;
 }
 
 /* Expose the decoder (one row) for the oracle's own tests. */
-void orc_decode_row(int fmt, const uint8_t* row, int64_t K, int16_t* wq, float* wd, float* wm) {
-    decode_row(fmt, row, K, wq, wd, wm);
+int orc_decode_row(int fmt, const uint8_t* row, int64_t K, const uint16_t* grid,
+                   int16_t* wq, float* wd, float* wm, int16_t* mult) {
+    return decode_row(fmt, row, K, grid, wq, wd, wm, mult);
 }
 
 static int64_t raw_row_bytes(int fmt, int64_t K) {
@@ -246,6 +283,7 @@ static int64_t raw_row_bytes(int fmt, int64_t K) {
         case ORC_Q8_0: return K / 32 * 34;
         case ORC_Q4_0: return K / 32 * 18;
         case ORC_Q4_K: return K / 256 * 144;
+        case ORC_IQ1C: return K / 256 * 56;
         default:       return K / 256 * 76;
     }
 }
@@ -254,12 +292,12 @@ static int64_t raw_row_bytes(int fmt, int64_t K) {
 
 /* P[m][n][b] = the exact integer dot of block b:
  *   q8_0, q4_0: sum xq*wq;  q4_K: sum xq*nib (unsigned nibbles);
- *   iq1t: the folded per-32 form sum_h (2s_h+1) * sum_{16 in half h} xq*(8g+sigma).
- * Returns 0, or -1 if any partial falls outside int32.                        */
-int orc_partials(int fmt, const uint8_t* raw, int64_t N, int64_t K,
+ *   iq1t, iq1c: the folded per-32 form sum_h (2s_h+1) * sum_{16 in half h} xq*(8g+sigma).
+ * Returns 0, -1 if any partial falls outside int32, -2 on an invalid grid code. */
+int orc_partials(int fmt, const uint8_t* raw, int64_t N, int64_t K, const uint16_t* grid,
                  const int8_t* xq, int64_t M, int32_t* P) {
     const int64_t KB = K / 32, rb = raw_row_bytes(fmt, K);
-    int bad = 0;
+    int bad = 0, badgrid = 0;
 #pragma omp parallel
     {
         int16_t* wq = (int16_t*)malloc(sizeof(int16_t) * K);
@@ -268,16 +306,7 @@ int orc_partials(int fmt, const uint8_t* raw, int64_t N, int64_t K,
         int16_t* mult = (int16_t*)malloc(sizeof(int16_t) * (K / 16));
 #pragma omp for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
-            decode_row(fmt, raw + n * rb, K, wq, wd, wm);
-            for (int64_t h = 0; h < K / 16; ++h) mult[h] = 1;
-            if (fmt == ORC_IQ1T) {
-                const uint8_t* row = raw + n * rb;
-                for (int64_t sb = 0; sb < K / 256; ++sb) {
-                    uint64_t sw = 0;
-                    for (int i = 0; i < 6; ++i) sw |= (uint64_t)row[sb * 76 + 64 + i] << (8 * i);
-                    for (int h = 0; h < 16; ++h) mult[sb * 16 + h] = (int16_t)(2 * ((sw >> (3 * h)) & 7u) + 1);
-                }
-            }
+            if (decode_row(fmt, raw + n * rb, K, grid, wq, wd, wm, mult) != 0) badgrid = 1;
             for (int64_t m = 0; m < M; ++m) {
                 for (int64_t b = 0; b < KB; ++b) {
                     int64_t total = 0;
@@ -296,7 +325,7 @@ int orc_partials(int fmt, const uint8_t* raw, int64_t N, int64_t K,
         }
         free(wq); free(wd); free(wm); free(mult);
     }
-    return bad ? -1 : 0;
+    return badgrid ? -2 : bad ? -1 : 0;
 }
 
 /* Per-16 iq1t partials P16[m][n][h] = sum over the 16 values of half-block h of
@@ -309,9 +338,10 @@ void orc_partials16_iq1t(const uint8_t* raw, int64_t N, int64_t K,
         int16_t* wq = (int16_t*)malloc(sizeof(int16_t) * K);
         float* wd = (float*)malloc(sizeof(float) * KH);
         float* wm = (float*)malloc(sizeof(float) * (K / 32));
+        int16_t* mult = (int16_t*)malloc(sizeof(int16_t) * KH);
 #pragma omp for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
-            decode_row(ORC_IQ1T, raw + n * rb, K, wq, wd, wm);
+            decode_row(ORC_IQ1T, raw + n * rb, K, NULL, wq, wd, wm, mult);
             for (int64_t m = 0; m < M; ++m)
                 for (int64_t h = 0; h < KH; ++h) {
                     int32_t s = 0;
@@ -319,7 +349,7 @@ void orc_partials16_iq1t(const uint8_t* raw, int64_t N, int64_t K,
                     P16[(m * N + n) * KH + h] = s;
                 }
         }
-        free(wq); free(wd); free(wm);
+        free(wq); free(wd); free(wm); free(mult);
     }
 }
 
@@ -327,17 +357,22 @@ void orc_partials16_iq1t(const uint8_t* raw, int64_t N, int64_t K,
 
 /* out[m*ldo + n] = sum over blocks b of xs[m,b] * ( sum_half wd*P16 + wm*xsum[m,b] ),
  * accumulated in double and rounded to f32 once. Rows m0 <= m < m1 only (the
- * bench times a bounded sample of rows with this).                           */
-void orc_gemm_rows(int fmt, const uint8_t* raw, int64_t N, int64_t K,
-                   const int8_t* xq, const float* xs, const int32_t* xsum,
-                   int64_t m0, int64_t m1, float* out, int64_t ldo) {
+ * bench times a bounded sample of rows with this). Returns -2 on an invalid
+ * iq1c grid code, else 0.                                                    */
+int orc_gemm_rows(int fmt, const uint8_t* raw, int64_t N, int64_t K, const uint16_t* grid,
+                  const int8_t* xq, const float* xs, const int32_t* xsum,
+                  int64_t m0, int64_t m1, float* out, int64_t ldo) {
     const int64_t KB = K / 32, rb = raw_row_bytes(fmt, K);
+    int badgrid = 0;
     int16_t* wq_all = (int16_t*)malloc(sizeof(int16_t) * (size_t)(N * K));
     float* wd_all = (float*)malloc(sizeof(float) * (size_t)(N * (K / 16)));
     float* wm_all = (float*)malloc(sizeof(float) * (size_t)(N * KB));
+    int16_t* mult_all = (int16_t*)malloc(sizeof(int16_t) * (size_t)(N * (K / 16)));
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n)
-        decode_row(fmt, raw + n * rb, K, wq_all + n * K, wd_all + n * (K / 16), wm_all + n * KB);
+        if (decode_row(fmt, raw + n * rb, K, grid, wq_all + n * K, wd_all + n * (K / 16), wm_all + n * KB,
+                       mult_all + n * (K / 16)) != 0)
+            badgrid = 1;
 #pragma omp parallel for schedule(static)
     for (int64_t m = m0; m < m1; ++m) {
         for (int64_t n = 0; n < N; ++n) {
@@ -361,12 +396,13 @@ void orc_gemm_rows(int fmt, const uint8_t* raw, int64_t N, int64_t K,
             out[(m - m0) * ldo + n] = (float)acc;
         }
     }
-    free(wq_all); free(wd_all); free(wm_all);
+    free(wq_all); free(wd_all); free(wm_all); free(mult_all);
+    return badgrid ? -2 : 0;
 }
 
-void orc_gemm(int fmt, const uint8_t* raw, int64_t N, int64_t K,
-              const int8_t* xq, const float* xs, const int32_t* xsum, int64_t M, float* out) {
-    orc_gemm_rows(fmt, raw, N, K, xq, xs, xsum, 0, M, out, N);
+int orc_gemm(int fmt, const uint8_t* raw, int64_t N, int64_t K, const uint16_t* grid,
+             const int8_t* xq, const float* xs, const int32_t* xsum, int64_t M, float* out) {
+    return orc_gemm_rows(fmt, raw, N, K, grid, xq, xs, xsum, 0, M, out, N);
 }
 
 /* ---------------------------------------------------------------- W8A8 */

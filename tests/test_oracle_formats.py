@@ -36,7 +36,7 @@ def test_golden_block_decodes(orc, fmt):
         assert expect[int(k)] == v, (fmt, k)
     wh = orc.dequant_weights(fmt, raw[None, :], 1, K)[0]
     assert np.array_equal(wh, expect)
-    wq, wd, wm = orc.decode_row_c(fmt, raw, K)
+    wq, wd, wm, _ = orc.decode_row_c(fmt, raw, K)
     wc = np.repeat(wd.astype(np.float64), 16) * wq + np.repeat(wm.astype(np.float64), 32)
     assert np.array_equal(wc, expect)
 
@@ -57,7 +57,7 @@ def test_q4_K_sixbit_fields_round_trip_every_value(orc):
             blk[off:off + 6] = np.frombuffer(word.to_bytes(6, "little"), np.uint8)
         blk[16:] = 0x11                           # nib = 1 everywhere
         rows.append(blk)
-        wq, wd, wm = orc.decode_row_c("q4_K", blk, K)
+        wq, wd, wm, _ = orc.decode_row_c("q4_K", blk, K)
         assert np.array_equal(wd[::2], vals.astype(np.float32))
         assert np.array_equal(wm, -(63 - vals).astype(np.float32))
     wh = orc.dequant_weights("q4_K", np.stack(rows), len(rows), K)
@@ -90,7 +90,7 @@ def test_iq1_c_decoder_uses_fold_and_matches_definition(orc):
     raw = gen.weights_iq1t(N, K, seed=3, cfg=99)
     wh = orc.dequant_weights("iq1t", raw, N, K)
     for n in range(N):
-        wq, wd, wm = orc.decode_row_c("iq1t", raw[n], K)
+        wq, wd, wm, _ = orc.decode_row_c("iq1t", raw[n], K)
         assert set(np.unique(wq)) <= {-9, -7, -1, 1, 7, 9}
         assert np.array_equal(np.repeat(wd.astype(np.float64), 16) * wq, wh[n])
         assert np.all(wm == 0)
