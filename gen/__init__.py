@@ -31,6 +31,11 @@ K/256 consecutive blocks):
           6 bytes of 3-bit sub-scales s (one per 16 values, LSB-first), f16 d.
           The grid is a table of 2048 uint16 entries, each eight 2-bit codes
           c = g+1 (value j at bits 2j..2j+1).     w = d*(2s+1)*(g+delta)
+* q6_K  - 210 B per 256 values: 128 bytes ql, 64 bytes qh, 16 int8 sub-scales
+          sc (one per 16 values), f16 d. In 32-value block j, value 32j+i
+          (i < 16) has its low 4 bits in the low nibble of ql[16j+i] and value
+          32j+16+i in the high nibble; the high 2 bits of value 32j+8t+i
+          (t < 4, i < 8) are bits 2t..2t+1 of qh[8j+i].  w = d*sc_h*(q-32)
 * i8_row - int8 [N][K] plus one f32 scale per row.            w = sw[n]*q
 
 The shapes and value distributions follow the five workloads the MMQ pages
@@ -44,8 +49,8 @@ import numpy as np
 QK = 32          # values per quantisation block
 QK_SUPER = 256   # values per K-quant / iq1t super-block
 
-ROW_BYTES_PER_BLOCK = {"q8_0": 34, "q4_0": 18, "q4_K": 144, "iq1t": 76, "iq1c": 56}
-VALUES_PER_BLOCK = {"q8_0": 32, "q4_0": 32, "q4_K": 256, "iq1t": 256, "iq1c": 256}
+ROW_BYTES_PER_BLOCK = {"q8_0": 34, "q4_0": 18, "q4_K": 144, "iq1t": 76, "iq1c": 56, "q6_K": 210}
+VALUES_PER_BLOCK = {"q8_0": 32, "q4_0": 32, "q4_K": 256, "iq1t": 256, "iq1c": 256, "q6_K": 256}
 
 # tensor ids inside a configuration's seed sequence
 T_ACT, T_WEIGHT, T_IDS, T_OUTLIER, T_GRID = 0, 1, 2, 3, 4
@@ -152,6 +157,40 @@ def weights_q4_K(N: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T
     return out.reshape(N, -1)
 
 
+def pack_q6_K(q: np.ndarray, sc: np.ndarray, d16: np.ndarray) -> np.ndarray:
+    """Lay out 6-bit values q [N, nsb, 256] (0..63), int8 sub-scales sc [N, nsb, 16] and f16 d
+    [N, nsb] in the q6_K byte layout described above."""
+    N, nsb = q.shape[:2]
+    q = q.astype(np.uint8).reshape(N, nsb, 8, 32)
+    out = np.empty((N, nsb, 210), dtype=np.uint8)
+    lo = q & 0xF
+    out[..., 0:128] = (lo[..., :16] | (lo[..., 16:] << 4)).reshape(N, nsb, 128)
+    hi = (q >> 4).reshape(N, nsb, 8, 4, 8)                       # [.., j, t, i]
+    out[..., 128:192] = (hi[..., 0, :] | (hi[..., 1, :] << 2) | (hi[..., 2, :] << 4) |
+                         (hi[..., 3, :] << 6)).reshape(N, nsb, 64)
+    out[..., 192:208] = sc.astype(np.int8).view(np.uint8)
+    out[..., 208:210] = np.asarray(d16, np.float16).view(np.uint8).reshape(N, nsb, 2)
+    return out.reshape(N, -1)
+
+
+def weights_q6_K(N: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T_WEIGHT,
+                 std: float = 0.02) -> np.ndarray:
+    """q6_K-style super-blocks from N(0,std): per 16 values a signed step sf = w_peak / -32
+    (w_peak: the first value of largest magnitude, sign kept); d = f16(max|sf| / 127);
+    sc = clip(rint(sf / d), -127, 127); q = clip(rint(w / (d*sc)) + 32, 0, 63)."""
+    nsb = K // QK_SUPER
+    w = _normal_weights(N, K, seed, cfg, tensor, std).reshape(N, nsb, 16, 16)
+    idx = np.abs(w).argmax(axis=3)
+    peak = np.take_along_axis(w, idx[..., None], axis=3)[..., 0]
+    sf = peak / np.float32(-32)
+    d16 = (np.abs(sf).max(axis=2) / np.float32(127)).astype(np.float16)
+    d = d16.astype(np.float32)[..., None]
+    sc = np.where(d > 0, np.clip(np.rint(sf / np.where(d > 0, d, 1)), -127, 127), 0).astype(np.int8)
+    step = (d * sc.astype(np.float32))[..., None]
+    q = np.where(step != 0, np.clip(np.rint(w / np.where(step != 0, step, 1)) + 32, 0, 63), 32)
+    return pack_q6_K(q.reshape(N, nsb, 256), sc, d16)
+
+
 def weights_iq1t(N: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T_WEIGHT,
                  d_value: float = 0.02 / 4) -> np.ndarray:
     """IQ1_M-style ternary rows: g uniform in {-1,0,1}, s uniform in 0..7 per 16 values,
@@ -232,6 +271,8 @@ def weights(fmt: str, N: int, K: int, **kw):
         return weights_iq1t(N, K, **kw)
     if fmt == "iq1c":
         return weights_iq1c(N, K, **kw)
+    if fmt == "q6_K":
+        return weights_q6_K(N, K, **kw)
     if fmt == "i8_row":
         return i8_rows(N, K, **kw)
     raise ValueError(fmt)
@@ -255,6 +296,8 @@ CONFIGS = {
     "cfg2b_q4_0": dict(cfg=2, fmt="q4_0", M=2048, N=11008, K=4096, out="f32", outlier_rate=1e-3),
     "cfg3a_q4_K": dict(cfg=3, fmt="q4_K", M=512, N=14336, K=4096, out="f32"),
     "cfg3b_q4_K": dict(cfg=3, fmt="q4_K", M=512, N=4096, K=14336, out="f32"),
+    # q6_K carries a 7B model's ffn_down (and lm_head) in q4_k_m files: the down projection
+    "cfg6_q6_K": dict(cfg=6, fmt="q6_K", M=2048, N=4096, K=11008, out="f32", outlier_rate=1e-3),
     "cfg4_w8a8": dict(cfg=4, fmt="i8_row", M=3072, N=1536, K=4096, out="bf16"),
     "cfg5_moe_iq1t": dict(cfg=5, fmt="iq1t", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
     # the same MoE with the IQ1_M codebook form of the weights (1.75 bits per value)
@@ -269,6 +312,7 @@ CONFIGS = {
     "dec8_q4_K_down": dict(cfg=3, fmt="q4_K", M=8, N=4096, K=14336, out="f32"),
     "dec8_iq1t": dict(cfg=5, fmt="iq1t", M=8, N=2048, K=4096, out="f32"),
     "dec8_iq1c": dict(cfg=5, fmt="iq1c", M=8, N=2048, K=4096, out="f32"),
+    "dec8_q6_K": dict(cfg=6, fmt="q6_K", M=8, N=4096, K=11008, out="f32"),
     "dec8_w8a8": dict(cfg=4, fmt="i8_row", M=8, N=1536, K=4096, out="bf16"),
     "dec1_moe_iq1t": dict(cfg=5, fmt="iq1t", M=1, N=2048, K=4096, out="f32", E=64, top_k=8),
     "dec4_moe_iq1t": dict(cfg=5, fmt="iq1t", M=4, N=2048, K=4096, out="f32", E=64, top_k=8),

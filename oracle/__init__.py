@@ -36,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mmq_oracle.c")
 _LIB = os.path.join(_HERE, "liborc.so")
 
-FMT_ID = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "iq1c": 4}
+FMT_ID = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "iq1c": 4, "q6_K": 5}
 
 
 def build(force: bool = False) -> str:
@@ -71,7 +71,7 @@ def lib():
         L.orc_decode_row.restype = ctypes.c_int
         L.orc_partials.argtypes = [ctypes.c_int, P, I, I, P, P, I, P]
         L.orc_partials.restype = ctypes.c_int
-        L.orc_partials16_iq1t.argtypes = [P, I, I, P, I, P]
+        L.orc_partials16.argtypes = [ctypes.c_int, P, I, I, P, P, I, P]
         L.orc_gemm_rows.argtypes = [ctypes.c_int, P, I, I, P, P, P, P, I, I, P, I]
         L.orc_gemm_rows.restype = ctypes.c_int
         L.orc_gemm.argtypes = [ctypes.c_int, P, I, I, P, P, P, P, I, P]
@@ -188,13 +188,21 @@ def partials(fmt: str, raw: np.ndarray, N: int, K: int, xq: np.ndarray, grid=Non
     return P
 
 
-def partials16_iq1t(raw: np.ndarray, N: int, K: int, xq: np.ndarray) -> np.ndarray:
+def partials16(fmt: str, raw: np.ndarray, N: int, K: int, xq: np.ndarray, grid=None) -> np.ndarray:
+    """Exact int32 per-16 partials P16[m,n,h] = sum over half-block h of xq*wq (iq1t/iq1c:
+    before the (2s+1) fold; q6_K: the two separate half-block sums of each 32-value block,
+    minfer R1 sections 2.2 and 3.3)."""
     raw = _c(raw, np.uint8)
     xq = _c(xq, np.int8)
+    g = _grid_arg(fmt, grid)
     M = xq.shape[0]
     P = np.empty((M, N, K // 16), np.int32)
-    lib().orc_partials16_iq1t(_p(raw), N, K, _p(xq), M, _p(P))
+    lib().orc_partials16(FMT_ID[fmt], _p(raw), N, K, None if g is None else _p(g), _p(xq), M, _p(P))
     return P
+
+
+def partials16_iq1t(raw: np.ndarray, N: int, K: int, xq: np.ndarray) -> np.ndarray:
+    return partials16("iq1t", raw, N, K, xq)
 
 
 def gemm_c(fmt: str, raw: np.ndarray, N: int, K: int, xq, xs, xsum, rows=None, grid=None) -> np.ndarray:
@@ -243,6 +251,7 @@ def _f16(bits: np.ndarray) -> np.ndarray:
 def dequant_weights(fmt: str, raw: np.ndarray, N: int, K: int, grid=None) -> np.ndarray:
     """w_hat [N,K] in f64 from each format's defining formula (independent of the C decoder):
     q8_0 d*q; q4_0 d*(nib-8); q4_K d*sc*nib - dmin*m (minfer R1 section 2.2);
+    q6_K d*sc_h*(q-32) with one int8 sc per 16 values (minfer R1 sections 2.2 and 3.3);
     iq1t and iq1c d*(2s+1)*(g+delta) (PR #304 description; iq1c takes the eight g of a group
     from the grid entry its 11-bit index names)."""
     raw = np.asarray(raw, dtype=np.uint8).reshape(N, -1)
@@ -295,6 +304,17 @@ def dequant_weights(fmt: str, raw: np.ndarray, N: int, K: int, grid=None) -> np.
         s = s_bits @ np.array([1.0, 2.0, 4.0])
         d = _f16(b[..., 54].astype(np.uint16) | (b[..., 55].astype(np.uint16) << 8))
         w = (d[..., None] * np.repeat(2.0 * s + 1.0, 16, axis=-1)) * (g + delta[..., None]).reshape(N, K // 256, 256)
+        return w.reshape(N, K)
+    if fmt == "q6_K":
+        b = raw.reshape(N, K // 256, 210)
+        ql = b[..., 0:128].reshape(N, K // 256, 8, 16)
+        lo = np.concatenate([ql & 0xF, ql >> 4], axis=-1)                      # [N, sb, 8, 32]
+        qh = b[..., 128:192].reshape(N, K // 256, 8, 1, 8)
+        hi = ((qh >> (2 * np.arange(4)[:, None])) & 3).reshape(N, K // 256, 8, 32)
+        q = (lo.astype(np.int64) | (hi.astype(np.int64) << 4)).reshape(N, K // 256, 256)
+        sc = b[..., 192:208].view(np.int8).astype(np.float64)
+        d = _f16(b[..., 208].astype(np.uint16) | (b[..., 209].astype(np.uint16) << 8))
+        w = d[..., None] * np.repeat(sc, 16, axis=-1) * (q - 32).astype(np.float64)
         return w.reshape(N, K)
     raise ValueError(fmt)
 

@@ -20,6 +20,10 @@
  *    is d*(2s+1)*(g+delta); 8(g+delta) = 8g +- 1 and the per-16 scale becomes
  *    d(2s+1)/8. In the codebook form the ternary g of 8 values come from one
  *    grid entry named by an 11-bit index (the grid itself is an input here).
+ *  - minfer R1 sections 2.2 and 3.3: q6_K values are a 6-bit grid 0..63 moved
+ *    to the signed domain by -32, with an int8 scale per 16 values; a 32-value
+ *    block is two 16-value halves with separate integer sums, each rescaled by
+ *    its own d*sc.
  *  - "INT8 W8A8 GEMM - Prefill" (metainfer), section 1: int8 activations with
  *    a per-token f32 scale, int8 weights with a per-channel f32 scale, int32
  *    accumulation, epilogue fragment -> scale -> bf16, no bias.
@@ -44,6 +48,7 @@
 #define ORC_Q4_K 2
 #define ORC_IQ1T 3
 #define ORC_IQ1C 4
+#define ORC_Q6_K 5
 
 /* ---------------------------------------------------------------- scalars */
 
@@ -165,9 +170,10 @@ void orc_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_t ldx,
 
 /* Decode one weight row into:
  *   wq[K]      - the integer that enters the int8 dot for each value
- *                (q8_0: q; q4_0: nib-8; q4_K: nib (unsigned); iq1t/iq1c: 8g+sigma)
+ *                (q8_0: q; q4_0: nib-8; q4_K: nib (unsigned); iq1t/iq1c: 8g+sigma;
+ *                q6_K: q-32)
  *   wd[K/16]   - the f32 scale multiplying each 16-value half of the dot
- *                (q8_0/q4_0: d; q4_K: d*sc; iq1t/iq1c: d*(2s+1)/8)
+ *                (q8_0/q4_0: d; q4_K: d*sc; iq1t/iq1c: d*(2s+1)/8; q6_K: d*sc_h)
  *   wm[K/32]   - the f32 coefficient of the activation block sum
  *                (q4_K: -dmin*m, others 0)
  *   mult[K/16] - the integer factor of each half in the folded block partial
@@ -268,6 +274,22 @@ static int decode_row(int fmt, const uint8_t* row, int64_t K, const uint16_t* gr
                 mult[sb * 16 + h] = (int16_t)(2 * s + 1);
             }
         }
+    } else if (fmt == ORC_Q6_K) {
+        /* 32-value block j of a super-block: value 32j+i (i < 16) has its low 4 bits in the
+         * low nibble of ql[16j+i], value 32j+16+i in the high nibble; value 32j+8t+i (t < 4,
+         * i < 8) has its high 2 bits at bits 2t..2t+1 of qh[8j+i]. */
+        for (int64_t sb = 0; sb < K / 256; ++sb) {
+            const uint8_t* blk = row + sb * 210;
+            float d = orc_half_to_float(rd16(blk + 208));
+            for (int j = 0; j < 8; ++j) {
+                for (int u = 0; u < 32; ++u) {
+                    int lo = (blk[16 * j + (u % 16)] >> (4 * (u / 16))) & 15;
+                    int hi = (blk[128 + 8 * j + (u % 8)] >> (2 * (u / 8))) & 3;
+                    wq[sb * 256 + 32 * j + u] = (int16_t)((lo | (hi << 4)) - 32);
+                }
+            }
+            for (int h = 0; h < 16; ++h) wd[sb * 16 + h] = d * (float)(int8_t)blk[192 + h];
+        }
     }
     return bad ? -1 : 0;
 }
@@ -284,6 +306,7 @@ static int64_t raw_row_bytes(int fmt, int64_t K) {
         case ORC_Q4_0: return K / 32 * 18;
         case ORC_Q4_K: return K / 256 * 144;
         case ORC_IQ1C: return K / 256 * 56;
+        case ORC_Q6_K: return K / 256 * 210;
         default:       return K / 256 * 76;
     }
 }
@@ -328,11 +351,12 @@ int orc_partials(int fmt, const uint8_t* raw, int64_t N, int64_t K, const uint16
     return badgrid ? -2 : bad ? -1 : 0;
 }
 
-/* Per-16 iq1t partials P16[m][n][h] = sum over the 16 values of half-block h of
- * xq * (8g+sigma), before the (2s+1) fold.                                    */
-void orc_partials16_iq1t(const uint8_t* raw, int64_t N, int64_t K,
-                         const int8_t* xq, int64_t M, int32_t* P16) {
-    const int64_t KH = K / 16, rb = raw_row_bytes(ORC_IQ1T, K);
+/* Per-16 partials P16[m][n][h] = sum over the 16 values of half-block h of
+ * xq * wq (iq1t/iq1c: wq = 8g+sigma, before the (2s+1) fold; q6_K: wq = q-32,
+ * the two separate half-block sums of each 32-value block).                  */
+void orc_partials16(int fmt, const uint8_t* raw, int64_t N, int64_t K, const uint16_t* grid,
+                    const int8_t* xq, int64_t M, int32_t* P16) {
+    const int64_t KH = K / 16, rb = raw_row_bytes(fmt, K);
 #pragma omp parallel
     {
         int16_t* wq = (int16_t*)malloc(sizeof(int16_t) * K);
@@ -341,7 +365,7 @@ void orc_partials16_iq1t(const uint8_t* raw, int64_t N, int64_t K,
         int16_t* mult = (int16_t*)malloc(sizeof(int16_t) * KH);
 #pragma omp for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
-            decode_row(ORC_IQ1T, raw + n * rb, K, NULL, wq, wd, wm, mult);
+            decode_row(fmt, raw + n * rb, K, grid, wq, wd, wm, mult);
             for (int64_t m = 0; m < M; ++m)
                 for (int64_t h = 0; h < KH; ++h) {
                     int32_t s = 0;

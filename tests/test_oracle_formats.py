@@ -4,7 +4,8 @@
   oracle's decoders (the C one used for integer partials and the NumPy f64 one
   used for the definition) to the value formulas: q8_0 d*q, q4_0 d*(nib-8)
   (minfer R1 section 1), Q4_K d*sc*nib - dmin*m (minfer R1 section 2.2),
-  IQ1_M-style d*(2s+1)*(g+delta) (llama.cpp PR #304 description).
+  IQ1_M-style d*(2s+1)*(g+delta) (llama.cpp PR #304 description), q6_K d*sc_h*(q-32)
+  with an int8 scale per 16 values (minfer R1 sections 2.2 and 3.3).
 * The IQ1_M fold 8(g+delta) = 8g+-1 with per-16 scale d(2s+1)/8 (PR #304) is
   checked exhaustively for exactness in f64 and f32.
 * The seeded generators are checked to encode what they claim (round trip
@@ -26,7 +27,7 @@ def _golden():
         return json.load(f)
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_K", "iq1t"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_K", "q6_K", "iq1t"])
 def test_golden_block_decodes(orc, fmt):
     g = _golden()[fmt]
     raw = np.frombuffer(bytes.fromhex(g["hex"].replace(" ", "")), np.uint8)
@@ -147,6 +148,26 @@ def test_iq1t_generator_distribution(orc):
     assert np.all(np.abs(frac - 1 / 3) < 0.01)
     d = b[..., 74:76].copy().view(np.float16)
     assert np.all(d == np.float16(0.005))
+
+
+def test_q6_K_generator_round_trip(orc):
+    N, K = 7, 512
+    raw = gen.weights_q6_K(N, K, seed=0, cfg=6)
+    w = gen._normal_weights(N, K, 0, 6, gen.T_WEIGHT, 0.02).astype(np.float64).reshape(N, K // 16, 16)
+    wh = orc.dequant_weights("q6_K", raw, N, K).reshape(N, K // 16, 16)
+    b = raw.reshape(N, K // 256, 210)
+    sc = b[..., 192:208].view(np.int8).astype(np.float64).reshape(N, K // 16, 1)
+    d = b[..., 208:210].copy().view(np.float16).astype(np.float64).reshape(N, K // 256, 1, 1)
+    step = np.abs(np.broadcast_to(d, (N, K // 256, 16, 1)).reshape(N, K // 16, 1) * sc)
+    err = np.abs(wh - w)
+    # values inside the grid round to the nearest step (d*sc); only values beyond it clip at
+    # q = 0 or 63 (the step is the rounded w_peak/-32, so the far side can exceed 31 steps)
+    ratio = w / np.where(step != 0, np.sign(sc) * step, 1)
+    inside = (ratio >= -32.5) & (ratio <= 31.5)
+    assert np.all(err[inside] <= 0.5 * np.broadcast_to(step, err.shape)[inside] * (1 + 1e-6) + 1e-12)
+    assert inside.mean() > 0.95
+    assert np.median(err / np.maximum(step, 1e-12)) < 0.3
+    assert np.any(sc < 0) and np.any(sc > 0)      # both signs of sub-scale occur
 
 
 def test_i8_rows_generator(orc):

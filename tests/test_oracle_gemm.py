@@ -99,6 +99,29 @@ def test_partials_iq1t_folded_is_integer_matmul_with_d8(orc):
         assert np.array_equal(P16[..., h], ref)
 
 
+def test_partials16_q6_K_are_half_block_int_matmuls(orc):
+    # minfer R1 sections 2.2 and 3.3: each 32-value q6_K block is two 16-value halves with
+    # separate integer sums of xq*(q-32). With d = 1 and every sc = 1 the dequantised value is
+    # the integer q-32, so each per-16 partial is the 16-column integer matmul.
+    M, N, K = 6, 9, 512
+    raw = gen.weights_q6_K(N, K, seed=3, cfg=55).reshape(N, K // 256, 210)
+    raw[..., 192:208] = 1
+    raw[..., 208:210] = np.array([np.float16(1.0)]).view(np.uint8)
+    raw = raw.reshape(N, -1)
+    v = orc.dequant_weights("q6_K", raw, N, K)
+    assert np.array_equal(v, np.rint(v)) and v.min() >= -32 and v.max() <= 31
+    xq = _xq(M, K, 9)
+    P16 = orc.partials16("q6_K", raw, N, K, xq)
+    for h in range(K // 16):
+        ref = xq[:, 16 * h:16 * h + 16].astype(np.int64) @ v[:, 16 * h:16 * h + 16].astype(np.int64).T
+        assert np.array_equal(P16[..., h], ref)
+    # worst case of one half: all q = 0 (value -32) against xq = -128 -> 16 * 32 * 128
+    raw0 = raw.reshape(N, K // 256, 210).copy()
+    raw0[..., 0:192] = 0
+    P16w = orc.partials16("q6_K", raw0.reshape(N, -1), N, K, np.full((1, K), -128, np.int8))
+    assert np.all(P16w == 16 * 32 * 128)
+
+
 def test_partials_int32_worst_cases(orc):
     # the bounds behind the exact int32 accumulation (minfer R1 section 2.1; PR #304's per-16 bound
     # 16*9*127 = 18288, garbled on the page): worst blocks hit exactly these values.
@@ -125,7 +148,8 @@ def test_partials_int32_worst_cases(orc):
 
 
 @pytest.mark.parametrize("fmt,K", [("q8_0", 32), ("q8_0", 256), ("q4_0", 96), ("q4_K", 256),
-                                   ("q4_K", 512), ("iq1t", 256), ("iq1t", 768)])
+                                   ("q4_K", 512), ("iq1t", 256), ("iq1t", 768), ("q6_K", 256),
+                                   ("q6_K", 768)])
 @pytest.mark.parametrize("M", [1, 5])
 def test_per_block_oracle_matches_f64_definition(orc, fmt, K, M):
     # brute force: the per-block integer oracle (C) against the f64 definition sum_k x_hat*w_hat
