@@ -72,7 +72,7 @@ MEASURED_TRAFFIC_BYTES = {
     "dec8_q4_K": 45158633,
 }
 
-RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "i8_row": 32}
+RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "i8_row": 32}
 
 
 def log(*a):
@@ -93,7 +93,7 @@ def _oracle_env():
     return {"os_cpu_count": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
-def cpu_baseline(fmt, raw, x, M, N, K, budget_s=10.0, min_runs=3, max_runs=50):
+def cpu_baseline(fmt, raw, x, M, N, K, grid=None, budget_s=10.0, min_runs=3, max_runs=50):
     """The oracle as it stands, timed on the host: q8_1 quantisation + per-block C GEMM over
     the whole workload, repeated until about `budget_s` seconds of CPU work (median reported),
     then one single-thread pass over the first rows."""
@@ -106,7 +106,7 @@ def cpu_baseline(fmt, raw, x, M, N, K, budget_s=10.0, min_runs=3, max_runs=50):
             oracle.gemm_w8a8(a[:rows], sa[:rows], w, sw)
         else:
             xq, xs, xsum = oracle.quantize_q8_1(x[:rows])
-            oracle.gemm_c(fmt, raw, N, K, xq, xs, xsum)
+            oracle.gemm_c(fmt, raw, N, K, xq, xs, xsum, grid=grid)
 
     times = []
     t_start = time.perf_counter()
@@ -132,7 +132,7 @@ def cpu_baseline(fmt, raw, x, M, N, K, budget_s=10.0, min_runs=3, max_runs=50):
             **_oracle_env()}
 
 
-def cpu_baseline_moe(raw_e, x, ids, E, N, K, budget_s=10.0):
+def cpu_baseline_moe(fmt, raw_e, x, ids, E, N, K, grid=None, budget_s=10.0):
     """MoE oracle leg on a bounded sample: the dense per-block C GEMM of the tokens routed to
     each expert (in expert order) until ~budget_s seconds, scaled to pair-rows per s; a small
     workload is passed over again (at least 3 times) until the budget is used."""
@@ -140,19 +140,21 @@ def cpu_baseline_moe(raw_e, x, ids, E, N, K, budget_s=10.0):
     oracle.build()
     xq, xs, xsum = oracle.quantize_q8_1(x)
     rows_done, t_used, experts, passes = 0, 0.0, 0, 0
-    while t_used < budget_s and (passes < 3 or t_used < 1.0):
+    wall0 = time.perf_counter()
+    while t_used < budget_s and (passes < 3 or t_used < 1.0) and time.perf_counter() - wall0 < 6 * budget_s:
         for e in range(E):
             tt = np.nonzero((ids == e).any(axis=1))[0]
             if len(tt) == 0:
                 continue
             t0 = time.perf_counter()
-            oracle.gemm_c("iq1t", raw_e[e], N, K, xq[tt], xs[tt], xsum[tt])
+            oracle.gemm_c(fmt, raw_e[e], N, K, xq[tt], xs[tt], xsum[tt], grid=grid)
             t_used += time.perf_counter() - t0
             rows_done += len(tt)
             experts += 1
             if t_used >= budget_s:
                 break
         passes += 1
+        log(f"[bench] cpu baseline pass {passes}: {experts} expert products, {t_used:.1f} s")
     ops = 2.0 * rows_done * N * K
     return {"value": ops / t_used / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{experts} expert products over {passes} pass(es) ({rows_done} routed token rows) "
@@ -250,6 +252,9 @@ def main():
     log(f"[bench] workload {name}: {fmt} M={M} N={N} K={K}")
     ops = 2.0 * M * N * K
     extra = {}
+    # the iq1c codebook: an input of the repack (and of the oracle leg)
+    grid_np = gen.IQ1C_GRID if fmt == "iq1c" else None
+    grid_d = torch.from_numpy(grid_np.view(np.int16)).to(dev) if grid_np is not None else None
 
     def copies_of(t):
         if args.rotate > 0:
@@ -283,7 +288,7 @@ def main():
         p0 = torch.empty(E * pb, dtype=torch.uint8, device=dev)
         for e in range(E):
             mmq.repack_weights(fmt, torch.from_numpy(np.ascontiguousarray(raw_e[e])).to(dev), N, K,
-                               out=p0[e * pb:(e + 1) * pb])
+                               out=p0[e * pb:(e + 1) * pb], grid=grid_d)
         packed = copies_of(p0)
         xd = torch.from_numpy(x).to(dev)
         ids_d = torch.from_numpy(ids).to(dev)
@@ -305,7 +310,7 @@ def main():
         raw = gen.weights(fmt, N, K, seed=0, cfg=cfg["cfg"])
         x = gen.act_f32(M, K, seed=0, cfg=cfg["cfg"], outlier_rate=cfg.get("outlier_rate", 0.0))
         xd = torch.from_numpy(x).to(dev)
-        packed = copies_of(mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K))
+        packed = copies_of(mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K, grid=grid_d))
         act = torch.empty(mmq.act_bytes("q8_1", M, K), dtype=torch.uint8, device=dev)
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
 
@@ -315,7 +320,7 @@ def main():
         dom = 1
         # raw weights + q8_1 activations (int8 values, f32 scale, int32 sum) + f32 output
         alg_bytes = int(N * K / 32 * RAW_BYTES_PER_32[fmt]) + M * K + M * (K // 32) * 8 + M * N * 4
-        cpu_args = (fmt, raw, x, M, N, K)
+        cpu_args = (fmt, raw, x, M, N, K, grid_np)
     n_rot = len(packed)
     bound = "hbm" if (moe or decode) else "mfma"
     if n_rot > 1:
@@ -403,7 +408,7 @@ def main():
         if cpu_args is not None:
             rec["cpu_baseline"] = cpu_baseline(*cpu_args)
         else:
-            rec["cpu_baseline"] = cpu_baseline_moe(raw_e, x, ids, E, N, K)
+            rec["cpu_baseline"] = cpu_baseline_moe(fmt, raw_e, x, ids, E, N, K, grid_np)
         log(f"[bench] cpu baseline {rec['cpu_baseline']['value']:.4f} TOPS on "
             f"{rec['cpu_baseline']['cores']} threads: {rec['cpu_baseline']['sample']}")
     print(json.dumps(rec), flush=True)

@@ -10,11 +10,14 @@ constexpr int64_t MAX_DIM = int64_t(1) << 24;    // keeps every index of the ker
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_wtype(int t) { return t >= MMQ_Q8_0 && t <= MMQ_I8_ROW; }
+bool valid_wtype(int t) { return t >= MMQ_Q8_0 && t <= MMQ_IQ1C; }
 bool valid_atype(int a) { return a == MMQ_ACT_Q8_1 || a == MMQ_ACT_I8_TOKEN; }
 bool valid_otype(int o) { return o >= MMQ_OUT_F32 && o <= MMQ_OUT_I32_PARTIALS; }
 
-int64_t k_multiple(mmq_wtype t) { return (t == MMQ_Q4_K || t == MMQ_IQ1T) ? 256 : 32; }
+int64_t k_multiple(mmq_wtype t) { return (t == MMQ_Q4_K || t == MMQ_IQ1T || t == MMQ_IQ1C) ? 256 : 32; }
+
+// formats whose repack takes an auxiliary input (I8_ROW: row scales; IQ1C: the grid)
+bool needs_aux(mmq_wtype t) { return t == MMQ_I8_ROW || t == MMQ_IQ1C; }
 
 bool sizes_ok(int64_t M, int64_t N, int64_t K) {
     return M >= 1 && N >= 1 && K >= 32 && M <= MAX_DIM && N <= MAX_DIM && K <= MAX_DIM;
@@ -83,13 +86,13 @@ size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K) {
     return (size_t)packed_layout(t, N, K).bytes;
 }
 
-mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const float* row_scale, int64_t N,
+mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux, int64_t N,
                               int64_t K, void* packed, void* stream) {
     if (!valid_wtype(t) || !sizes_ok(1, N, K) || K % k_multiple(t)) return MMQ_EINVAL;
     if (!raw || !packed) return MMQ_EINVAL;
-    if ((t == MMQ_I8_ROW) != (row_scale != nullptr)) return MMQ_EINVAL;
-    if (!aligned16(raw) || !aligned16(packed) || (row_scale && !aligned16(row_scale))) return MMQ_EALIGN;
-    return from_hip(launch_repack(t, raw, row_scale, N, K, packed, as_stream(stream)));
+    if (needs_aux(t) != (aux != nullptr)) return MMQ_EINVAL;
+    if (!aligned16(raw) || !aligned16(packed) || (aux && !aligned16(aux))) return MMQ_EALIGN;
+    return from_hip(launch_repack(t, raw, aux, N, K, packed, as_stream(stream)));
 }
 
 mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
@@ -105,6 +108,7 @@ mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
         if (o == MMQ_OUT_I32_PARTIALS && M * N * (K / QK) > (int64_t(1) << 31)) return MMQ_EINVAL;
     }
     if (!aligned16(packed) || !aligned16(act) || !aligned16(out)) return MMQ_EALIGN;
+    t = kernel_format(t);
     // decode batches go to the split-K matrix-vector kernel; the debug partials stay on the
     // prefill kernels
     if (o != MMQ_OUT_I32_PARTIALS && M <= mmvq_max_tokens())
@@ -135,6 +139,7 @@ mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* a
         !aligned16(workspace))
         return MMQ_EALIGN;
     if (!gather_grid_ok(gemm_id_max_units(E, T * top_k), N)) return MMQ_EINVAL;
+    t = kernel_format(t);
     return from_hip(launch_gemm_id(t, packed, E, act, ids, T, top_k, N, K, out, workspace, ws_bytes,
                                    as_stream(stream)));
 }

@@ -27,6 +27,12 @@
 //     both), and the rank-1 min term -(dmin*m) * (xs*xsum) (minfer R1 section 2.2: sum w*q =
 //     ds * sum nib*q - dmin * sum q) is added straight into the accumulator by
 //     v_mfma_f32_32x32x2_f32 over two blocks at once (one per half-wave).
+//   q6_K: the 6-bit values q-32 are int8 as they are, but the scale d*sc changes every 16 values
+//     (minfer R1 sections 2.2 and 3.3: one 32-k chunk, two half-block integer sums with separate
+//     accumulators, rescaled by d*sc0 and d*sc1). Each block runs as two virtual tiles: the
+//     int8 MFMA over the fragment with the other half's lanes zeroed (lanes 0-31 carry values
+//     0-15, lanes 32-63 values 16-31), its own scale product S_h = 2 (d*sc_h) xs from the exact
+//     f16 split hi + lo = d*sc_h, its own conversion, and both FMA into the same accumulator.
 //   iq1t: the IQ1_M fold (llama.cpp PR #304) turns each value into the integer 8g +- 1 with a
 //     per-16 factor (2s+1) and a per-block scale d/8. (2s+1)*v = 2s*v + v with |2s*v| <= 126,
 //     so two chained int8 MFMAs over [2s*v] and [v] (same token operand) give the folded
@@ -67,13 +73,14 @@ template <> struct BT<MMQ_Q8_0> {
     static constexpr int NMF = 1;          // int8 MFMAs per block
     static constexpr int SHIFT = 0;        // the MFMA computes P << SHIFT
     static constexpr bool MIN = false;     // q4_K min term
+    static constexpr bool DUAL = false;    // q6_K: two half-block dots per block
     static constexpr float POST = UNBIAS / 2;   // S = 2 wd xs
     struct Raw { v4i x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
         r.x = *reinterpret_cast<const v4i*>(frag + lane * 16);
     }
     __device__ static void mid(Raw&, uint32_t, int, const uint8_t*) {}
-    __device__ static void unpack(const Raw& r, v4i* a) { a[0] = r.x; }
+    __device__ static void unpack(const Raw& r, v4i* a, int) { a[0] = r.x; }
     __device__ static uint32_t scale_op(uint32_t w) { return w; }
 };
 
@@ -85,13 +92,14 @@ template <> struct BT<MMQ_Q4_0> {
     static constexpr int NMF = 1;
     static constexpr int SHIFT = 4;
     static constexpr bool MIN = false;
+    static constexpr bool DUAL = false;
     static constexpr float POST = UNBIAS / 32;  // 16x block dot, S = 2 wd xs
     struct Raw { uint2 x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
         r.x = *reinterpret_cast<const uint2*>(frag + lane * 8);
     }
     __device__ static void mid(Raw&, uint32_t, int, const uint8_t*) {}
-    __device__ static void unpack(const Raw& r, v4i* a) {
+    __device__ static void unpack(const Raw& r, v4i* a, int) {
         a[0][0] = (int)(r.x.x & 0xF0F0F0F0u);
         a[0][1] = (int)((r.x.x << 4) & 0xF0F0F0F0u);
         a[0][2] = (int)(r.x.y & 0xF0F0F0F0u);
@@ -106,13 +114,14 @@ template <> struct BT<MMQ_Q4_K> {
     static constexpr int NMF = 1;
     static constexpr int SHIFT = 0;
     static constexpr bool MIN = true;
+    static constexpr bool DUAL = false;
     static constexpr float POST = UNBIAS / 2;
     struct Raw { uint2 x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
         r.x = *reinterpret_cast<const uint2*>(frag + lane * 8);
     }
     __device__ static void mid(Raw&, uint32_t, int, const uint8_t*) {}
-    __device__ static void unpack(const Raw& r, v4i* a) {
+    __device__ static void unpack(const Raw& r, v4i* a, int) {
         a[0][0] = (int)(r.x.x & 0x0F0F0F0Fu);
         a[0][1] = (int)((r.x.x >> 4) & 0x0F0F0F0Fu);
         a[0][2] = (int)(r.x.y & 0x0F0F0F0Fu);
@@ -131,6 +140,7 @@ template <> struct BT<MMQ_IQ1T> {
     static constexpr int NMF = 2;
     static constexpr int SHIFT = 0;
     static constexpr bool MIN = false;
+    static constexpr bool DUAL = false;
     static constexpr float POST = UNBIAS / 16;  // scale d/8, S = 2 d xs
     struct Raw { uint32_t C; v4i t; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -140,7 +150,7 @@ template <> struct BT<MMQ_IQ1T> {
         const uint32_t meta = (wsd >> (16 + 8 * (lane >> 5))) & 0xFFu;
         r.t = *reinterpret_cast<const v4i*>(tab + meta * 16);     // v0, v1, 2s*v0, 2s*v1
     }
-    __device__ static void unpack(const Raw& r, v4i* a) {
+    __device__ static void unpack(const Raw& r, v4i* a, int) {
         const uint32_t C = r.C;
         const v4i t = r.t;
         const uint32_t s0 = C & 0x03030303u;
@@ -166,6 +176,29 @@ template <> struct BT<MMQ_IQ1T> {
         const int b0 = (-8 + d) * mul, b1 = d * mul, b2 = (8 + d) * mul;
         return (uint32_t)(b0 & 0xFF) | ((uint32_t)(b1 & 0xFF) << 8) | ((uint32_t)(b2 & 0xFF) << 16);
     }
+};
+
+// q6_K lane bytes: 16 int8 values q-32 (k = 16h..16h+15), as q8_0. a[0] keeps them on lanes 0-31
+// (values 0-15 of the block, half 0) and a[1] on lanes 32-63 (values 16-31, half 1); the other
+// lanes are zero, so each int8 MFMA yields one half-block dot. The scale dword of half 0 sits in
+// the first scale region, that of half 1 in the second (hi | lo << 16, hi + lo = d*sc_h).
+template <> struct BT<MMQ_Q6_K> {
+    static constexpr int FB = 1024;
+    static constexpr int NMF = 2;
+    static constexpr int SHIFT = 0;
+    static constexpr bool MIN = false;
+    static constexpr bool DUAL = true;
+    static constexpr float POST = UNBIAS / 2;   // S_h = 2 (d*sc_h) xs
+    struct Raw { v4i x; };
+    __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
+        r.x = *reinterpret_cast<const v4i*>(frag + lane * 16);
+    }
+    __device__ static void mid(Raw&, uint32_t, int, const uint8_t*) {}
+    __device__ static void unpack(const Raw& r, v4i* a, int hmask) {
+        a[0] = r.x & hmask;
+        a[1] = r.x & ~hmask;
+    }
+    __device__ static uint32_t scale_op(uint32_t w) { return w; }     // (hi, lo) of d*sc_h
 };
 
 // ------------------------------------------------------------------- kernel configuration
@@ -196,10 +229,12 @@ struct Cfg {
     static constexpr int C_WF = WF / 1024, C_XF = TM * KS;
     static constexpr int C_WS = (TN + 1) / 2;               // a pair of tiles per chunk
     static constexpr int C_XS = GATHER ? TM * KS / 2 : (TM + 1) / 2;
-    static constexpr int C_WM = T::MIN ? C_WS : 0, C_XM = T::MIN ? C_XS : 0;
+    // second weight-side scale region: q4_K's -dmin*m, q6_K's half-1 scale dwords
+    static constexpr bool W2 = T::MIN || T::DUAL;
+    static constexpr int C_WM = W2 ? C_WS : 0, C_XM = T::MIN ? C_XS : 0;
     static constexpr int RW = C_WS * 2 * SCB, RX = (TM + 1) / 2 * 2 * SCB;   // region bytes
     static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + RW;
-    static constexpr int O_WM = O_XS + RX, O_XM = O_WM + (T::MIN ? RW : 0);
+    static constexpr int O_WM = O_XS + RX, O_XM = O_WM + (W2 ? RW : 0);
     static constexpr int BUF = O_XM + (T::MIN ? RX : 0);
     static constexpr int C_FR = C_WF + C_XF;
     static constexpr int C_SC = C_WS + C_XS + C_WM + C_XM;

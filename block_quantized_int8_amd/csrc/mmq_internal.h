@@ -110,7 +110,8 @@ inline PackedLayout packed_layout(mmq_wtype t, int64_t N, int64_t K) {
         case MMQ_Q8_0: L.frag_bytes = 1024; break;
         case MMQ_Q4_0: L.frag_bytes = 512; break;
         case MMQ_Q4_K: L.frag_bytes = 512; break;
-        case MMQ_IQ1T: L.frag_bytes = 256; break;
+        case MMQ_IQ1T:
+        case MMQ_IQ1C: L.frag_bytes = 256; break;      // IQ1C is repacked into the IQ1T form
         default: L.frag_bytes = 1024; break;           // I8_ROW
     }
     const int64_t cells = L.Np * L.KBp;
@@ -131,11 +132,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 // internal launchers (defined in the .hip files, called by api.cpp)
 namespace mmq {
+// The packed form the GEMM kernels read: IQ1C is repacked into the IQ1T panels.
+inline mmq_wtype kernel_format(mmq_wtype t) { return t == MMQ_IQ1C ? MMQ_IQ1T : t; }
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ldx, void* act,
                                 hipStream_t s);
 hipError_t launch_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_t ldx, void* act,
                                     hipStream_t s);
-hipError_t launch_repack(mmq_wtype t, const void* raw, const float* row_scale, int64_t N,
+hipError_t launch_repack(mmq_wtype t, const void* raw, const void* aux, int64_t N,
                          int64_t K, void* packed, hipStream_t s);
 hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
                              int64_t N, int64_t K, mmq_otype o, void* out, int64_t ldo,

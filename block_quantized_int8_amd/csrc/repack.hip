@@ -164,6 +164,51 @@ __global__ __launch_bounds__(256) void repack_iq1t_kernel(
     }
 }
 
+// IQ1C (the IQ1_M codebook form): the lane's 16 values are the 8-value groups q0 = e0/8 and
+// q0 + 1; each group's 11-bit index (qs byte, plus bits 8-10 from its qh nibble) names a grid
+// entry of eight 2-bit codes, which land in the IQ1T lane word; the delta sign is bit 3 of the
+// same nibble. The packed result is exactly the IQ1T panel of the same values.
+__global__ __launch_bounds__(256) void repack_iq1c_kernel(
+    const uint8_t* __restrict__ raw, const uint16_t* __restrict__ grid, int64_t N, int64_t KB,
+    int64_t KBp, int64_t total, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
+    uint32_t C = 0, meta = 0;
+    uint16_t d = 0;
+    if (x.live) {
+        const uint8_t* blk = raw + (x.n * (KB / 8) + x.b / 8) * 56;
+        const int e0 = (int)(x.b % 8) * 32 + 16 * x.h;    // first of the lane's 16 values
+        uint32_t sg[2];
+#pragma unroll
+        for (int gq = 0; gq < 2; ++gq) {
+            const int q = (e0 >> 3) + gq;
+            const uint32_t nib = (blk[32 + (q >> 1)] >> (4 * (q & 1))) & 0xFu;
+            const uint32_t entry = grid[blk[q] | ((nib & 7u) << 8)];
+            sg[gq] = nib >> 3;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = 8 * gq + j;                  // value index inside the lane
+                C |= ((entry >> (2 * j)) & 3u) << (8 * (i & 3) + 2 * (i >> 2));
+            }
+        }
+        uint64_t sw = 0;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) sw |= (uint64_t)blk[48 + i] << (8 * i);
+        const uint32_t s = (uint32_t)(sw >> (3 * (e0 >> 4))) & 7u;
+        meta = s | (sg[0] << 3) | (sg[1] << 4);
+        d = ld_u16(blk + 54);
+    }
+    *reinterpret_cast<uint32_t*>(frag + gid * 4) = C;
+    uint8_t* e = scale + ((x.nt * KBp + x.b) * 32 + x.r) * 4;
+    if (x.h == 0) {
+        *reinterpret_cast<uint16_t*>(e) = d;
+        e[2] = (uint8_t)meta;
+    } else {
+        e[3] = (uint8_t)meta;
+    }
+}
+
 __global__ __launch_bounds__(256) void repack_i8_row_kernel(
     const int8_t* __restrict__ raw, const float* __restrict__ row_scale, int64_t N, int64_t K,
     int64_t KB, int64_t KBp, int64_t total, uint8_t* __restrict__ frag, float* __restrict__ sw) {
@@ -180,7 +225,7 @@ __global__ __launch_bounds__(256) void repack_i8_row_kernel(
 
 namespace mmq {
 
-hipError_t launch_repack(mmq_wtype t, const void* raw, const float* row_scale, int64_t N,
+hipError_t launch_repack(mmq_wtype t, const void* raw, const void* aux, int64_t N,
                          int64_t K, void* packed, hipStream_t s) {
     const PackedLayout L = packed_layout(t, N, K);
     uint8_t* base = static_cast<uint8_t*>(packed);
@@ -205,9 +250,14 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const float* row_scale, i
         case MMQ_IQ1T:
             hipLaunchKernelGGL(repack_iq1t_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag, scale);
             break;
+        case MMQ_IQ1C:
+            hipLaunchKernelGGL(repack_iq1c_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,
+                               L.KB, L.KBp, total, frag, scale);
+            break;
         case MMQ_I8_ROW:
             hipLaunchKernelGGL(repack_i8_row_kernel, grid, block, 0, s, static_cast<const int8_t*>(raw),
-                               row_scale, N, K, L.KB, L.KBp, total, frag, reinterpret_cast<float*>(scale));
+                               static_cast<const float*>(aux), N, K, L.KB, L.KBp, total, frag,
+                               reinterpret_cast<float*>(scale));
             break;
     }
     return hipGetLastError();

@@ -56,9 +56,19 @@ typedef enum {
  *            16 values, LSB-first), 4 B of 32 sign bits (one per 8 values, 0 -> +1/8,
  *            1 -> -1/8), f16 d.                                   w = d*(2s+1)*(g+delta)
  *  MMQ_I8_ROW int8 [N][K] plus one f32 scale per row (per-channel W8A8).  w = sw[n]*q
+ *  MMQ_IQ1C  56 B per 256 values (the IQ1_M codebook form, 1.75 bits per value): u8 qs[32]
+ *            (low 8 bits of each 8-value group's 11-bit grid index), u8 qh[16] (byte j holds
+ *            groups 2j and 2j+1 in its low and high nibble: nibble bits 0-2 = index bits
+ *            8-10, bit 3 = the group's delta sign, 0 -> +1/8, 1 -> -1/8), 6 B of sixteen
+ *            3-bit sub-scales s (LSB-first), f16 d. The grid (passed to the repack) holds
+ *            2048 uint16 entries, each eight 2-bit codes c = g+1 (value j of the group at
+ *            bits 2j..2j+1; code 3 is invalid).                   w = d*(2s+1)*(g+delta)
  * Value formulas: minfer R1 sections 1-2.2 (q8_0, q4_0, Q4_K); llama.cpp PR #304
- * description (IQ1_M); metainfer "INT8 W8A8 GEMM - Prefill" section 1 (per-channel). */
-typedef enum { MMQ_Q8_0 = 0, MMQ_Q4_0 = 1, MMQ_Q4_K = 2, MMQ_IQ1T = 3, MMQ_I8_ROW = 4 } mmq_wtype;
+ * description (IQ1_M, its 11-bit grid index per 8 values and per-16 sub-scales);
+ * metainfer "INT8 W8A8 GEMM - Prefill" section 1 (per-channel). */
+typedef enum {
+    MMQ_Q8_0 = 0, MMQ_Q4_0 = 1, MMQ_Q4_K = 2, MMQ_IQ1T = 3, MMQ_I8_ROW = 4, MMQ_IQ1C = 5
+} mmq_wtype;
 
 /* Activation formats.
  *  MMQ_ACT_Q8_1     per 32-value block: amax = max|x|; d = amax/127 (f32); q = clamp(
@@ -75,7 +85,7 @@ typedef enum { MMQ_ACT_Q8_1 = 0, MMQ_ACT_I8_TOKEN = 1 } mmq_atype;
  *                       with MMQ_ACT_I8_TOKEN only (metainfer section 1: fragment -> scale ->
  *                       bf16, no bias)
  *  MMQ_OUT_I32_PARTIALS debug: block formats: int32 [M][N][K/32] of the exact per-block
- *                       integer dots (Q4_K: sum xq*nib with unsigned nibbles; IQ1T: the folded
+ *                       integer dots (Q4_K: sum xq*nib with unsigned nibbles; IQ1T, IQ1C: the folded
  *                       sum_h (2s_h+1) * sum_16 xq*(8g+-1)); MMQ_I8_ROW: int32 [M][N] of the
  *                       full-K accumulators. ldo must equal N. Same kernels as the scaled
  *                       outputs, the scale step replaced by a store. */
@@ -125,13 +135,17 @@ size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K);
 /* One-time, untimed repack of raw weights into the library's matrix-core panel layout.
  *  raw       (device) raw rows as described at mmq_wtype; for MMQ_I8_ROW the int8 [N][K]
  *            values.
- *  row_scale (device) f32 [N] per-row scales, MMQ_I8_ROW only; must be NULL otherwise.
+ *  aux       (device) MMQ_I8_ROW: f32 [N] per-row scales; MMQ_IQ1C: the grid, uint16
+ *            [2048]; must be NULL for every other format. Read only during the call's
+ *            kernels; not referenced afterwards.
  *  packed    (device) mmq_packed_bytes(t, N, K) bytes; written completely (padding rows
  *            are zero). Immutable afterwards and safe to reuse across graph replays
  *            (metainfer section 3.2: one-time pack outside the timed region).
- * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, IQ1T). An invalid IQ1T
- * code (3) decodes as 0 - the caller must not pass one. */
-mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const float* row_scale,
+ * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, IQ1T, IQ1C). MMQ_IQ1C is
+ * expanded here, once, through the grid into the MMQ_IQ1T panel form (2-bit codes, per-16
+ * sub-scale and per-8 delta sign), so both formats share the GEMM kernels. An invalid code
+ * (3, in IQ1T rows or in an IQ1C grid entry) decodes as 0 - the caller must not pass one. */
+mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux,
                               int64_t N, int64_t K, void* packed, void* stream);
 
 /* The MMQ contraction out = act x packed^T.

@@ -76,6 +76,9 @@ def test_packed_bytes(mmq):
     assert mmq.packed_bytes("i8_row", 33, 32) == 2 * 8 * 1024 + 256
     assert mmq.packed_bytes("q4_K", 32, 128) == 0      # Q4_K needs K % 256 == 0
     assert mmq.packed_bytes("iq1t", 32, 200) == 0
+    # iq1c is repacked into the iq1t panels: same packed size, K % 256 required
+    assert mmq.packed_bytes("iq1c", 40, 512) == mmq.packed_bytes("iq1t", 40, 512)
+    assert mmq.packed_bytes("iq1c", 32, 288) == 0
     assert mmq.packed_bytes(9, 32, 64) == 0
 
 
@@ -103,9 +106,13 @@ def test_validation_rejects_before_any_launch(mmq):
     assert L.mmq_quantize_act(0, GOOD, 4, 64, 66, GOOD, None) == mmq.MMQ_EALIGN     # ldx % 4
     assert L.mmq_gemm(0, GOOD, BAD, 4, 32, 64, 0, GOOD, 32, None) == mmq.MMQ_EALIGN
     assert L.mmq_repack_weights(1, BAD, None, 32, 64, GOOD, None) == mmq.MMQ_EALIGN
-    # row_scale only with i8_row
+    # the auxiliary input: row scales with i8_row, the grid with iq1c, NULL otherwise
     assert L.mmq_repack_weights(1, GOOD, GOOD, 32, 64, GOOD, None) == mmq.MMQ_EINVAL
     assert L.mmq_repack_weights(4, GOOD, None, 32, 64, GOOD, None) == mmq.MMQ_EINVAL
+    assert L.mmq_repack_weights(5, GOOD, None, 32, 256, GOOD, None) == mmq.MMQ_EINVAL
+    assert L.mmq_repack_weights(3, GOOD, GOOD, 32, 256, GOOD, None) == mmq.MMQ_EINVAL
+    assert L.mmq_repack_weights(5, GOOD, GOOD, 32, 128, GOOD, None) == mmq.MMQ_EINVAL   # K % 256
+    assert L.mmq_repack_weights(5, GOOD, BAD, 32, 256, GOOD, None) == mmq.MMQ_EALIGN
 
 
 def test_gemm_id_validation(mmq):

@@ -1,0 +1,164 @@
+"""GPU parity of the IQ1_M codebook form (iq1c) against the CPU oracle, through the C ABI.
+
+iq1c rows carry an 11-bit grid index per 8 values (llama.cpp PR #304 description; the grid is
+the self-generated gen.IQ1C_GRID, an input of the repack). The repack expands each index
+through the grid once into the iq1t panel form, so the checks are:
+
+* the packed buffer equals, byte for byte, the iq1t repack of the same values written in the
+  iq1t layout (the iq1t path has its own parity tests);
+* dense prefill: q8_1 bit-exact, the folded int32 block partials bit-exact, f32 within
+  max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4), on shapes
+  with ragged M and N tails;
+* decode batches (M <= 16, the small-batch kernel) within the same gate;
+* MUL_MAT_ID at small sizes (every output row) and at the 64-expert workload size on sampled
+  pairs and columns in the launch configuration the bench times, plus a decode-size MoE.
+"""
+import numpy as np
+import pytest
+
+import gen
+
+pytestmark = pytest.mark.gpu
+
+GATE = 1e-3
+SENTINEL = np.float32(-12345.0)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import block_quantized_int8_amd as mmq
+    import oracle
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mmq.lib()
+    oracle.build()
+    grid = torch.from_numpy(gen.IQ1C_GRID.view(np.int16)).to("cuda:0")
+    return torch, mmq, oracle, grid
+
+
+def _rel(got, ref):
+    return float(np.max(np.abs(got.astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def _as_iq1t(raw_c, N, K, grid):
+    """The same g, s, delta and d in the iq1t byte layout (a re-layout of fields)."""
+    b = raw_c.reshape(N, K // 256, 56)
+    qh = np.stack([b[..., 32:48] & 0xF, b[..., 32:48] >> 4], axis=-1).reshape(N, K // 256, 32)
+    idx = b[..., 0:32].astype(np.int64) | ((qh & 7).astype(np.int64) << 8)
+    codes = np.stack([(grid[idx] >> (2 * j)) & 3 for j in range(8)], axis=-1).reshape(N, K // 256, 256)
+    c4 = codes.astype(np.uint8).reshape(N, K // 256, 64, 4)
+    t = np.empty((N, K // 256, 76), np.uint8)
+    t[..., 0:64] = c4[..., 0] | (c4[..., 1] << 2) | (c4[..., 2] << 4) | (c4[..., 3] << 6)
+    t[..., 64:70] = b[..., 48:54]
+    t[..., 70:74] = np.packbits((qh >> 3).astype(np.uint8).reshape(N, K // 256, 4, 8), axis=-1,
+                                bitorder="little")[..., 0]
+    t[..., 74:76] = b[..., 54:56]
+    return t.reshape(N, -1)
+
+
+def _pack(env, raw, N, K):
+    torch, mmq, _, grid = env
+    return mmq.repack_weights("iq1c", torch.from_numpy(np.ascontiguousarray(raw)).to("cuda:0"), N, K,
+                              grid=grid)
+
+
+@pytest.mark.parametrize("N,K", [(32, 256), (33, 768), (300, 512), (64, 4096)])
+def test_packed_equals_iq1t_packing_of_same_values(env, N, K):
+    torch, mmq, _, _ = env
+    print(f"[case] iq1c repack N={N} K={K}", flush=True)
+    raw = gen.weights_iq1c(N, K, seed=N + K, cfg=85)
+    assert mmq.packed_bytes("iq1c", N, K) == mmq.packed_bytes("iq1t", N, K)
+    pc = _pack(env, raw, N, K)
+    pt = mmq.repack_weights("iq1t", torch.from_numpy(_as_iq1t(raw, N, K, gen.IQ1C_GRID)).to("cuda:0"), N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(pc.cpu().numpy(), pt.cpu().numpy())
+
+
+SHAPES = [(1, 32, 256), (17, 33, 256), (65, 97, 768), (130, 300, 512), (256, 256, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_dense_prefill(env, M, N, K):
+    torch, mmq, orc, _ = env
+    dev = torch.device("cuda:0")
+    seed = 5 * M + N + K
+    print(f"[case] iq1c M={M} N={N} K={K} seed={seed}", flush=True)
+    raw = gen.weights_iq1c(N, K, seed=seed, cfg=86)
+    x = gen.act_f32(M, K, seed=seed, cfg=86, outlier_rate=1e-2)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
+    packed = _pack(env, raw, N, K)
+    out = mmq.gemm("iq1c", packed, act, M, N, K, "f32")
+    parts = mmq.gemm("iq1c", packed, act, M, N, K, "i32_partials")
+    torch.cuda.synchronize()
+    rq, rs, rsum = orc.quantize_q8_1(x)
+    xq, xs, xsum = mmq.act_to_host(act.cpu().numpy(), M, K)
+    assert np.array_equal(xq, rq) and np.array_equal(xsum, rsum)
+    assert np.array_equal(parts.cpu().numpy(), orc.partials("iq1c", raw, N, K, rq, grid=gen.IQ1C_GRID))
+    rel = _rel(out.cpu().numpy(), orc.gemm_f64("iq1c", raw, N, K, rq, rs, grid=gen.IQ1C_GRID))
+    print(f"  rel err {rel:.3e}")
+    assert rel <= GATE
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
+def test_decode_batches(env, M):
+    torch, mmq, orc, _ = env
+    dev = torch.device("cuda:0")
+    N, K = 300, 4096
+    print(f"[case] iq1c decode M={M} N={N} K={K}", flush=True)
+    raw = gen.weights_iq1c(N, K, seed=M, cfg=87)
+    x = gen.act_f32(M, K, seed=M, cfg=87, outlier_rate=1e-2)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
+    out = mmq.gemm("iq1c", _pack(env, raw, N, K), act, M, N, K, "f32")
+    torch.cuda.synchronize()
+    rq, rs, _ = orc.quantize_q8_1(x)
+    assert _rel(out.cpu().numpy(), orc.gemm_f64("iq1c", raw, N, K, rq, rs, grid=gen.IQ1C_GRID)) <= GATE
+
+
+def _moe(env, E, T, top_k, N, K, ids, seed, cfg=88):
+    torch, mmq, orc, _ = env
+    dev = torch.device("cuda:0")
+    print(f"[case] moe iq1c E={E} T={T} top_k={top_k} N={N} K={K} seed={seed}", flush=True)
+    raw = gen.moe_weights("iq1c", E, N, K, seed=seed, cfg=cfg)
+    x = gen.act_f32(T, K, seed=seed, cfg=cfg, outlier_rate=1e-3)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
+    pb = mmq.packed_bytes("iq1c", N, K)
+    packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        packed[e * pb:(e + 1) * pb] = _pack(env, raw[e], N, K)
+    out = torch.full((T, top_k, N), float(SENTINEL), dtype=torch.float32, device=dev)
+    mmq.gemm_id("iq1c", packed, E, act, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev),
+                T, top_k, N, K, out=out)
+    torch.cuda.synchronize()
+    rq, rs, _ = orc.quantize_q8_1(x)
+    return raw, rq, rs, out.cpu().numpy()
+
+
+@pytest.mark.parametrize("T", [2, 37, 150])
+def test_moe_every_row(env, T):
+    _, _, orc, _ = env
+    E, top_k, N, K = 8, 3, 97, 512
+    ids = gen.moe_ids(T, top_k, E, seed=T, cfg=88)
+    raw, rq, rs, got = _moe(env, E, T, top_k, N, K, ids, seed=T)
+    ref = orc.moe_f64("iq1c", raw.reshape(E * N, -1), E, N, K, rq, rs, ids, grid=gen.IQ1C_GRID)
+    rel = _rel(got, ref)
+    print(f"  rel err {rel:.3e}")
+    assert rel <= GATE
+
+
+def test_moe_full_size_sampled(env):
+    _, _, orc, _ = env
+    c = gen.CONFIGS["cfg5c_moe_iq1c"]
+    E, T, top_k, N, K = c["E"], c["M"], c["top_k"], c["N"], c["K"]
+    ids = gen.moe_ids(T, top_k, E, seed=0, cfg=c["cfg"])
+    raw, rq, rs, got = _moe(env, E, T, top_k, N, K, ids, seed=0, cfg=c["cfg"])
+    assert np.all(np.isfinite(got))
+    r = np.random.default_rng(13)
+    cols = np.sort(np.concatenate([r.choice(N, 192, replace=False), [0, N - 1]]))
+    worst = 0.0
+    for e in r.choice(E, 10, replace=False):
+        tt, jj = np.nonzero(ids == e)
+        ref = orc.gemm_f64("iq1c", raw[e], N, K, rq[tt], rs[tt], cols=cols, grid=gen.IQ1C_GRID)
+        worst = max(worst, _rel(got[tt, jj][:, cols], ref))
+    print(f"  rel err {worst:.3e}")
+    assert worst <= GATE
