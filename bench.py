@@ -72,7 +72,11 @@ MEASURED_TRAFFIC_BYTES = {
     "dec8_q4_K": 45158633,
 }
 
-RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "i8_row": 32}
+RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "q6_K": 210 / 8,
+                    "i8_row": 32}
+# vector ops per element-block of the scale step: exact conversion + FMA, twice for q6_K (one
+# per 16-value half)
+VALU_OPS_PER_EB = {"q6_K": 4}
 
 
 def log(*a):
@@ -161,6 +165,32 @@ def cpu_baseline_moe(fmt, raw_e, x, ids, E, N, K, grid=None, budget_s=10.0):
                       f"through the per-block C GEMM, {t_used:.1f} s", **_oracle_env()}
 
 
+def cpu_leg(name):
+    """The oracle timed on this host's cores over the named workload's own seeded inputs (the
+    same draws the GPU leg uploads)."""
+    import gen
+    cfg = gen.CONFIGS[name]
+    fmt, M, N, K = cfg["fmt"], cfg["M"], cfg["N"], cfg["K"]
+    grid = gen.IQ1C_GRID if fmt == "iq1c" else None
+    log("[bench] cpu baseline (oracle) ...")
+    if fmt == "i8_row":
+        a, sa = gen.i8_rows(M, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_ACT)
+        w, sw = gen.i8_rows(N, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_WEIGHT)
+        r = cpu_baseline("i8_row", None, (a, sa, w, sw), M, N, K)
+    elif "E" in cfg:
+        E, top_k = cfg["E"], cfg["top_k"]
+        raw_e = gen.moe_weights(fmt, E, N, K, seed=0, cfg=cfg["cfg"])
+        x = gen.act_f32(M, K, seed=0, cfg=cfg["cfg"])
+        ids = gen.moe_ids(M, top_k, E, seed=0, cfg=cfg["cfg"])
+        r = cpu_baseline_moe(fmt, raw_e, x, ids, E, N, K, grid)
+    else:
+        raw = gen.weights(fmt, N, K, seed=0, cfg=cfg["cfg"])
+        x = gen.act_f32(M, K, seed=0, cfg=cfg["cfg"], outlier_rate=cfg.get("outlier_rate", 0.0))
+        r = cpu_baseline(fmt, raw, x, M, N, K, grid)
+    log(f"[bench] cpu baseline {r['value']:.4f} TOPS on {r['cores']} threads: {r['sample']}")
+    return r
+
+
 def _graph(fns, n):
     """A hipGraph of n calls cycling through fns (each launches on the current stream)."""
     import torch
@@ -239,9 +269,15 @@ def main():
               f"(the path is single-GPU; how it would shard is design-only)", file=sys.stderr)
         sys.exit(2)
 
+    import gen
+
+    # The CPU-oracle leg runs first, before this process touches the GPU: in a process whose
+    # HIP runtime is live, the MoE leg's several hundred short OpenMP regions stalled for minutes
+    # on the GPU host (the same leg alone there takes ~3 s).
+    cpu_rec = None if args.no_cpu else cpu_leg(args.workload)
+
     import torch
     import block_quantized_int8_amd as mmq
-    import gen
 
     name = args.workload
     cfg = gen.CONFIGS[name]
@@ -277,7 +313,6 @@ def main():
                     lambda r: mmq.gemm("i8_row", packed[r], act, M, N, K, "bf16", out=out))]
         dom = 0
         alg_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
-        cpu_args = ("i8_row", None, (a, sa, w, sw), M, N, K)
     elif moe:
         E, top_k = cfg["E"], cfg["top_k"]
         T = M
@@ -304,7 +339,6 @@ def main():
         used = len(np.unique(ids))
         alg_bytes = int(used * N * K / 32 * RAW_BYTES_PER_32[fmt]) + T * K + T * (K // 32) * 8 + \
             T * top_k * N * 4 + T * top_k * 4
-        cpu_args = None
         extra = {"E": E, "top_k": top_k, "experts_used": used}
     else:
         raw = gen.weights(fmt, N, K, seed=0, cfg=cfg["cfg"])
@@ -315,12 +349,11 @@ def main():
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
 
         kernels = [("quantize_q8_1", lambda r: mmq.quantize_act(xd, out=act)),
-                   ("mmvq (decode)" if decode else "mmq_block",
+                   ("mmvq (decode)" if decode and fmt != "q6_K" else "mmq_block",
                     lambda r: mmq.gemm(fmt, packed[r], act, M, N, K, "f32", out=out))]
         dom = 1
         # raw weights + q8_1 activations (int8 values, f32 scale, int32 sum) + f32 output
         alg_bytes = int(N * K / 32 * RAW_BYTES_PER_32[fmt]) + M * K + M * (K // 32) * 8 + M * N * 4
-        cpu_args = (fmt, raw, x, M, N, K, grid_np)
     n_rot = len(packed)
     bound = "hbm" if (moe or decode) else "mfma"
     if n_rot > 1:
@@ -361,8 +394,9 @@ def main():
         # element-block E = rows * N * K/32, against 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
         rows = M * cfg.get("top_k", 1)
         E = rows * N * (K // 32)
-        roof["valu_ceiling"] = {"ops_per_element_block": 2, "peak_lane_ops": VALU_PEAK_LANE_OPS,
-                                "frac": round(2.0 * E / k_s / VALU_PEAK_LANE_OPS, 4)}
+        nops = VALU_OPS_PER_EB.get(fmt, 2)
+        roof["valu_ceiling"] = {"ops_per_element_block": nops, "peak_lane_ops": VALU_PEAK_LANE_OPS,
+                                "frac": round(nops * E / k_s / VALU_PEAK_LANE_OPS, 4)}
     roof["traffic"] = MEASURED_TRAFFIC_BYTES.get(name) if n_rot == 1 or name.startswith("dec") else None
     roof["kernel"] = kernels[dom][0]
     roof["kernel_us"] = {k: round(v * 1e6, 3) for k, v in kstats[dom].items()}
@@ -403,14 +437,8 @@ def main():
         "sclk_mhz_after_run": sclk,
         "roofline": roof,
     }
-    if not args.no_cpu:
-        log("[bench] cpu baseline (oracle) ...")
-        if cpu_args is not None:
-            rec["cpu_baseline"] = cpu_baseline(*cpu_args)
-        else:
-            rec["cpu_baseline"] = cpu_baseline_moe(fmt, raw_e, x, ids, E, N, K, grid_np)
-        log(f"[bench] cpu baseline {rec['cpu_baseline']['value']:.4f} TOPS on "
-            f"{rec['cpu_baseline']['cores']} threads: {rec['cpu_baseline']['sample']}")
+    if cpu_rec is not None:
+        rec["cpu_baseline"] = cpu_rec
     print(json.dumps(rec), flush=True)
 
 

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libmmq.so")
 
 # enums (include/mmq.h)
 MMQ_OK, MMQ_EINVAL, MMQ_EUNSUPPORTED, MMQ_EALIGN, MMQ_EWORKSPACE, MMQ_EHIP = range(6)
-WTYPE = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "i8_row": 4, "iq1c": 5}
+WTYPE = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "i8_row": 4, "iq1c": 5, "q6_K": 6}
 ATYPE = {"q8_1": 0, "i8_token": 1}
 OTYPE = {"f32": 0, "bf16": 1, "i32_partials": 2}
 
@@ -166,7 +166,8 @@ def gemm(wtype, packed, act, M: int, N: int, K: int, otype="f32", out=None, ldo=
         elif o == OTYPE["bf16"]:
             out = torch.empty((M, N), dtype=torch.bfloat16, device=packed.device)
         else:
-            shape = (M, N) if _wt(wtype) == WTYPE["i8_row"] else (M, N, K // 32)
+            w = _wt(wtype)
+            shape = (M, N) if w == WTYPE["i8_row"] else (M, N, K // 16) if w == WTYPE["q6_K"] else (M, N, K // 32)
             out = torch.empty(shape, dtype=torch.int32, device=packed.device)
     if ldo is None:
         ldo = out.stride(0) if out.dim() == 2 else N

@@ -10,11 +10,17 @@ constexpr int64_t MAX_DIM = int64_t(1) << 24;    // keeps every index of the ker
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_wtype(int t) { return t >= MMQ_Q8_0 && t <= MMQ_IQ1C; }
+bool valid_wtype(int t) { return t >= MMQ_Q8_0 && t <= MMQ_Q6_K; }
 bool valid_atype(int a) { return a == MMQ_ACT_Q8_1 || a == MMQ_ACT_I8_TOKEN; }
 bool valid_otype(int o) { return o >= MMQ_OUT_F32 && o <= MMQ_OUT_I32_PARTIALS; }
 
-int64_t k_multiple(mmq_wtype t) { return (t == MMQ_Q4_K || t == MMQ_IQ1T || t == MMQ_IQ1C) ? 256 : 32; }
+int64_t k_multiple(mmq_wtype t) {
+    return (t == MMQ_Q4_K || t == MMQ_IQ1T || t == MMQ_IQ1C || t == MMQ_Q6_K) ? 256 : 32;
+}
+
+// partial sums per (row, column) in MMQ_OUT_I32_PARTIALS: one per 32-value block, q6_K one per
+// 16-value half
+int64_t partials_per_row(mmq_wtype t, int64_t K) { return t == MMQ_Q6_K ? K / 16 : K / QK; }
 
 // formats whose repack takes an auxiliary input (I8_ROW: row scales; IQ1C: the grid)
 bool needs_aux(mmq_wtype t) { return t == MMQ_I8_ROW || t == MMQ_IQ1C; }
@@ -105,13 +111,13 @@ mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
         if (o == MMQ_OUT_F32) return MMQ_EUNSUPPORTED;
     } else {
         if (o == MMQ_OUT_BF16) return MMQ_EUNSUPPORTED;
-        if (o == MMQ_OUT_I32_PARTIALS && M * N * (K / QK) > (int64_t(1) << 31)) return MMQ_EINVAL;
+        if (o == MMQ_OUT_I32_PARTIALS && M * N * partials_per_row(t, K) > (int64_t(1) << 31)) return MMQ_EINVAL;
     }
     if (!aligned16(packed) || !aligned16(act) || !aligned16(out)) return MMQ_EALIGN;
     t = kernel_format(t);
     // decode batches go to the split-K matrix-vector kernel; the debug partials stay on the
     // prefill kernels
-    if (o != MMQ_OUT_I32_PARTIALS && M <= mmvq_max_tokens())
+    if (o != MMQ_OUT_I32_PARTIALS && M <= mmvq_max_tokens() && t != MMQ_Q6_K)
         return from_hip(launch_mmvq(t, packed, act, M, N, K, out, ldo, as_stream(stream)));
     if (t == MMQ_I8_ROW) {
         if (!w8a8_grid_ok(M, N)) return MMQ_EINVAL;

@@ -449,24 +449,29 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 #pragma unroll
     for (int r = 0; r < 16; ++r) magic[r] = MAGIC_I;
 
-    constexpr int NT_ = RT * CT;
+    // Steps per block: one per tile, two per tile for q6_K (its half-blocks, "virtual tiles"
+    // t = 2 * tile + half that share the tile's accumulator).
+    constexpr int NH = T::DUAL ? 2 : 1;
+    constexpr int NT_ = RT * CT * NH;
+    const int hmask = lane < 32 ? -1 : 0;                 // q6_K: lanes of half-block 0
     // one block's operands for this wave: raw LDS words (fetched a block ahead), then the MFMA
     // operands unpacked from them one step before the block starts
     struct Raw {
         typename T::Raw w[RT];
         v4i b[CT];
-        uint32_t wsd[RT], xs[CT];
+        uint32_t wsd[RT], wsd2[RT], xs[CT];
     };
     struct Ops {
         v4i a[RT][T::NMF];
         v4i b[CT];
-        uint32_t ws[RT], xs[CT];
+        uint32_t ws[RT], ws2[RT], xs[CT];
     };
     auto fetch = [&](const uint8_t* cur, int kb, Raw& R) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int i = wn * RT + rt;
             R.wsd[rt] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_WS, i, r32, kb));
+            if constexpr (T::DUAL) R.wsd2[rt] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_WM, i, r32, kb));
             T::fetch(cur + (i * KS + kb) * T::FB, lane, R.w[rt]);
         }
 #pragma unroll
@@ -483,8 +488,9 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     auto unpack = [&](const Raw& R, Ops& o) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            T::unpack(R.w[rt], o.a[rt]);
+            T::unpack(R.w[rt], o.a[rt], hmask);
             o.ws[rt] = T::scale_op(R.wsd[rt]);
+            if constexpr (T::DUAL) o.ws2[rt] = T::scale_op(R.wsd2[rt]);
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -500,15 +506,17 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     };
 
     // matrix-core half of tile t of a block: D (exact int32 dots), S (scale outer product)
+    // step t -> (weight tile rt, token tile ct, half hf); hf is 0 except for q6_K
     auto mfma_dots = [&](const Ops& o, int t) __attribute__((always_inline)) -> v16i {
-        const int rt = t / CT, ct = t % CT;
+        const int tt = t / NH, hf = t % NH, rt = tt / CT, ct = tt % CT;
+        if constexpr (T::DUAL) return __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][hf], o.b[ct], magic, 0, 0, 0);
         v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][0], o.b[ct], magic, 0, 0, 0);
         if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt][1], o.b[ct], D, 0, 0, 0);
         return D;
     };
     auto mfma_scale = [&](const Ops& o, int t) __attribute__((always_inline)) -> v16f {
-        const int rt = t / CT, ct = t % CT;
-        return __builtin_amdgcn_mfma_f32_32x32x8f16(as_h4(o.ws[rt]), as_h4(o.xs[ct]), zf, 0, 0, 0);
+        const int tt = t / NH, hf = t % NH, rt = tt / CT, ct = tt % CT;
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(as_h4(hf ? o.ws2[rt] : o.ws[rt]), as_h4(o.xs[ct]), zf, 0, 0, 0);
     };
     // The empty asm after a tile's last FMA pins its accumulator: FMAs are pure, and left alone
     // the compiler sinks a whole stage of them below its matrix-core work, which then has to
@@ -533,20 +541,23 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     // pure, and left alone the compiler sinks a whole stage of them below its matrix-core work,
     // which then has to hold every D and S at once.
     auto fma_tile = [&](int t, const v16f& X, const v16f& S, int r0 = 0, int r1 = 16) __attribute__((always_inline)) {
-        const int rt = t / CT, ct = t % CT;
+        const int tt = t / NH, rt = tt / CT, ct = tt % CT;
 #pragma unroll
         for (int r = r0; r < r1; ++r) acc[rt][ct][r] = __builtin_fmaf(X[r], S[r], acc[rt][ct][r]);
         if (r1 == 16) asm volatile("" : "+v"(acc[rt][ct]));
     };
     // partials mode: the exact int32 dots of block kbg go straight to memory
+    // (q6_K: the dot of half hf of block kbg goes to index 2 kbg + hf of 2 KB per (m, n))
     auto store_partials = [&](int kbg, int t, const v16i& D) __attribute__((always_inline)) {
-        const int rt = t / CT, ct = t % CT;
+        const int tt = t / NH, hf = t % NH, rt = tt / CT, ct = tt % CT;
         const int m = (mt_base + wm * CT + ct) * 32 + r32;
         if (kbg < args.KB && m < args.M) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int n = (nt_base + wn * RT + rt) * 32 + acc_row(lane, r);
-                if (n < args.N) args.partials[((int64_t)m * args.N + n) * args.KB + kbg] = (D[r] - MAGIC_I) >> T::SHIFT;
+                if (n < args.N)
+                    args.partials[((int64_t)m * args.N + n) * (NH * args.KB) + NH * kbg + hf] =
+                        (D[r] - MAGIC_I) >> T::SHIFT;
             }
         }
     };
@@ -822,6 +833,7 @@ hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, i
         case MMQ_Q4_0: return launch_dense<MMQ_Q4_0>(packed, act, M, N, K, o, out, ldo, s);
         case MMQ_Q4_K: return launch_dense<MMQ_Q4_K>(packed, act, M, N, K, o, out, ldo, s);
         case MMQ_IQ1T: return launch_dense<MMQ_IQ1T>(packed, act, M, N, K, o, out, ldo, s);
+        case MMQ_Q6_K: return launch_dense<MMQ_Q6_K>(packed, act, M, N, K, o, out, ldo, s);
         default: return hipErrorNotSupported;
     }
 }
@@ -836,6 +848,7 @@ hipError_t launch_block_gather(mmq_wtype t, const void* packed, int64_t E, const
         case MMQ_Q4_0: return MMQ_GATHER(MMQ_Q4_0);
         case MMQ_Q4_K: return MMQ_GATHER(MMQ_Q4_K);
         case MMQ_IQ1T: return MMQ_GATHER(MMQ_IQ1T);
+        case MMQ_Q6_K: return MMQ_GATHER(MMQ_Q6_K);
         default: return hipErrorNotSupported;
     }
 #undef MMQ_GATHER

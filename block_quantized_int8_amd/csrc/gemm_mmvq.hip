@@ -567,7 +567,7 @@ hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
 int mmvq_max_tokens() { return MV_TOK; }
 
 bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K) {
-    if (t == MMQ_I8_ROW || T < 1 || T > MV_ID_TOK || T * top_k > MV_IDP) return false;
+    if (t == MMQ_I8_ROW || t == MMQ_Q6_K || T < 1 || T > MV_ID_TOK || T * top_k > MV_IDP) return false;
     return round_up(K / QK, KB_ALIGN) <= XCap<1>::KB;          // batches of 8: one token group
 }
 

@@ -85,6 +85,7 @@ inline ActI8Layout act_i8_layout(int64_t M, int64_t K) {
 //   Q4_K: 8 B per lane, unsigned nibbles: X0 & 0x0F0F0F0F = k 16h+0..3, (X0 >> 4) & 0x0F0F0F0F
 //         = 16h+4..7, likewise X1 for 8..15 -> 512 B.
 //   IQ1T: 4 B per lane of 2-bit codes (value 16h + 4q + b at bits 8b + 2q) -> 256 B.
+//   Q6_K: 16 B per lane of int8 q-32, as Q8_0 -> 1024 B.
 // Region 1 holds one dword per (row n, block b), tile-major [NT][KBp][32] (row n, block b at
 // (n/32 * KBp + b) * 32 + n%32, so a 32-row tile's stage of blocks is one contiguous run):
 //   Q8_0, Q4_0: f16 d in the low half, 0 in the high half.
@@ -92,7 +93,9 @@ inline ActI8Layout act_i8_layout(int64_t M, int64_t K) {
 //               sigma1 << 4 for the half h = 0, 1 of the block (its 16-value sub-scale and the
 //               sign bits of its two 8-value groups).
 //   Q4_K:       d*sc split exactly into two f16 (hi | lo << 16), hi + lo = d*sc.
-// Region 2 (Q4_K only): f32 -dmin*m per (row, block), tile-major like region 1.
+//   Q6_K:       d*sc_0 of the block's first 16 values, split the same way.
+// Region 2: Q4_K: f32 -dmin*m per (row, block); Q6_K: the d*sc_1 split of the block's last 16
+// values; tile-major like region 1.
 // I8_ROW keeps one f32 per row [Np] in region 1.
 struct PackedLayout {
     int64_t Np, NT, KB, KBp;
@@ -112,6 +115,7 @@ inline PackedLayout packed_layout(mmq_wtype t, int64_t N, int64_t K) {
         case MMQ_Q4_K: L.frag_bytes = 512; break;
         case MMQ_IQ1T:
         case MMQ_IQ1C: L.frag_bytes = 256; break;      // IQ1C is repacked into the IQ1T form
+        case MMQ_Q6_K: L.frag_bytes = 1024; break;     // int8 q-32
         default: L.frag_bytes = 1024; break;           // I8_ROW
     }
     const int64_t cells = L.Np * L.KBp;
@@ -119,7 +123,7 @@ inline PackedLayout packed_layout(mmq_wtype t, int64_t N, int64_t K) {
     L.scale_off = round_up(L.NT * L.KBp * L.frag_bytes, REGION_ALIGN);
     const int64_t sb = (t == MMQ_I8_ROW) ? L.Np * 4 : cells * 4;
     L.min_off = L.scale_off + round_up(sb, REGION_ALIGN);
-    L.bytes = L.min_off + (t == MMQ_Q4_K ? round_up(cells * 4, REGION_ALIGN) : 0);
+    L.bytes = L.min_off + ((t == MMQ_Q4_K || t == MMQ_Q6_K) ? round_up(cells * 4, REGION_ALIGN) : 0);
     return L;
 }
 

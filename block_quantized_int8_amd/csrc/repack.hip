@@ -164,6 +164,40 @@ __global__ __launch_bounds__(256) void repack_iq1t_kernel(
     }
 }
 
+// q6_K: lane half h carries values 16h..16h+15 of the block as int8 q-32 (q = the low nibble
+// from ql, plus the high 2 bits from qh, see mmq.h); the half's scale d*sc_h is exact in f32
+// (f16 d times an int8) and is split exactly into two f16, hi + lo; lanes of half 0 write it to
+// the first scale region, lanes of half 1 to the second.
+__global__ __launch_bounds__(256) void repack_q6_K_kernel(
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    uint8_t* __restrict__ frag, uint32_t* __restrict__ scale, uint32_t* __restrict__ scale2) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
+    uint32_t w[4] = {0, 0, 0, 0};
+    uint32_t ds2 = 0;
+    if (x.live) {
+        const uint8_t* blk = raw + (x.n * (KB / 8) + x.b / 8) * 210;
+        const int j = (int)(x.b % 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int u = 16 * x.h + i;                        // value inside the 32-block
+            const uint32_t lo = (blk[16 * j + i] >> (4 * x.h)) & 0xFu;
+            const uint32_t hi = (blk[128 + 8 * j + (u & 7)] >> (2 * (u >> 3))) & 3u;
+            const uint32_t v = (uint32_t)((int)(lo | (hi << 4)) - 32) & 0xFFu;
+            w[i >> 2] |= v << (8 * (i & 3));
+        }
+        const int8_t sc = (int8_t)blk[192 + 2 * j + x.h];
+        const float ds = half_bits_to_float(ld_u16(blk + 208)) * (float)sc;
+        const _Float16 hi = (_Float16)ds;
+        const _Float16 lo = (_Float16)(ds - (float)hi);
+        ds2 = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+    }
+    *reinterpret_cast<uint4*>(frag + gid * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    uint32_t* dst = x.h == 0 ? scale : scale2;
+    dst[(x.nt * KBp + x.b) * 32 + x.r] = ds2;
+}
+
 // IQ1C (the IQ1_M codebook form): the lane's 16 values are the 8-value groups q0 = e0/8 and
 // q0 + 1; each group's 11-bit index (qs byte, plus bits 8-10 from its qh nibble) names a grid
 // entry of eight 2-bit codes, which land in the IQ1T lane word; the delta sign is bit 3 of the
@@ -249,6 +283,10 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const void* aux, int64_t 
             break;
         case MMQ_IQ1T:
             hipLaunchKernelGGL(repack_iq1t_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag, scale);
+            break;
+        case MMQ_Q6_K:
+            hipLaunchKernelGGL(repack_q6_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+                               reinterpret_cast<uint32_t*>(scale), reinterpret_cast<uint32_t*>(base + L.min_off));
             break;
         case MMQ_IQ1C:
             hipLaunchKernelGGL(repack_iq1c_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,

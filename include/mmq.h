@@ -63,11 +63,19 @@ typedef enum {
  *            3-bit sub-scales s (LSB-first), f16 d. The grid (passed to the repack) holds
  *            2048 uint16 entries, each eight 2-bit codes c = g+1 (value j of the group at
  *            bits 2j..2j+1; code 3 is invalid).                   w = d*(2s+1)*(g+delta)
- * Value formulas: minfer R1 sections 1-2.2 (q8_0, q4_0, Q4_K); llama.cpp PR #304
- * description (IQ1_M, its 11-bit grid index per 8 values and per-16 sub-scales);
- * metainfer "INT8 W8A8 GEMM - Prefill" section 1 (per-channel). */
+ *  MMQ_Q6_K  210 B per 256 values: u8 ql[128], u8 qh[64], int8 sc[16] (one per 16 values),
+ *            f16 d. In 32-value block j, value 32j+i (i < 16) has its low 4 bits in the low
+ *            nibble of ql[16j+i] and value 32j+16+i in the high nibble; the high 2 bits of
+ *            value 32j+8t+i (t < 4, i < 8) are bits 2t..2t+1 of qh[8j+i]; q = low | high << 4
+ *            in 0..63.                                                   w = d*sc_h*(q-32)
+ *            d*|sc| must stay below 65504 (the repack splits d*sc into two f16).
+ * Value formulas: minfer R1 sections 1-2.2 (q8_0, q4_0, Q4_K), 2.2 and 3.3 (q6_K: 6-bit grid
+ * moved to the signed domain by -32, a scale per 16 values); llama.cpp PR #304 description
+ * (IQ1_M, its 11-bit grid index per 8 values and per-16 sub-scales); metainfer "INT8 W8A8
+ * GEMM - Prefill" section 1 (per-channel). */
 typedef enum {
-    MMQ_Q8_0 = 0, MMQ_Q4_0 = 1, MMQ_Q4_K = 2, MMQ_IQ1T = 3, MMQ_I8_ROW = 4, MMQ_IQ1C = 5
+    MMQ_Q8_0 = 0, MMQ_Q4_0 = 1, MMQ_Q4_K = 2, MMQ_IQ1T = 3, MMQ_I8_ROW = 4, MMQ_IQ1C = 5,
+    MMQ_Q6_K = 6
 } mmq_wtype;
 
 /* Activation formats.
@@ -86,9 +94,11 @@ typedef enum { MMQ_ACT_Q8_1 = 0, MMQ_ACT_I8_TOKEN = 1 } mmq_atype;
  *                       bf16, no bias)
  *  MMQ_OUT_I32_PARTIALS debug: block formats: int32 [M][N][K/32] of the exact per-block
  *                       integer dots (Q4_K: sum xq*nib with unsigned nibbles; IQ1T, IQ1C: the folded
- *                       sum_h (2s_h+1) * sum_16 xq*(8g+-1)); MMQ_I8_ROW: int32 [M][N] of the
- *                       full-K accumulators. ldo must equal N. Same kernels as the scaled
- *                       outputs, the scale step replaced by a store. */
+ *                       sum_h (2s_h+1) * sum_16 xq*(8g+-1)); MMQ_Q6_K: int32 [M][N][K/16], the
+ *                       two half-block dots sum_16 xq*(q-32) of every block (half h of block b
+ *                       at index 2b+h); MMQ_I8_ROW: int32 [M][N] of the full-K accumulators.
+ *                       ldo must equal N. Same kernels as the scaled outputs, the scale step
+ *                       replaced by a store. */
 typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq_otype;
 
 /* ---------------------------------------------------------------------------------------
@@ -141,7 +151,7 @@ size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K);
  *  packed    (device) mmq_packed_bytes(t, N, K) bytes; written completely (padding rows
  *            are zero). Immutable afterwards and safe to reuse across graph replays
  *            (metainfer section 3.2: one-time pack outside the timed region).
- * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, IQ1T, IQ1C). MMQ_IQ1C is
+ * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, Q6_K, IQ1T, IQ1C). MMQ_IQ1C is
  * expanded here, once, through the grid into the MMQ_IQ1T panel form (2-bit codes, per-16
  * sub-scale and per-8 delta sign), so both formats share the GEMM kernels. An invalid code
  * (3, in IQ1T rows or in an IQ1C grid entry) decodes as 0 - the caller must not pass one. */
@@ -163,7 +173,7 @@ mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux,
  * empty; llama.cpp PR #304, Summary: small batches stay on a matrix-vector kernel). Both
  * compute the same per-block integer dots; the small-batch kernel reads the zero padding
  * rows M..31 of the activation buffer, so that padding must be zero (mmq_quantize_act
- * writes it so). */
+ * writes it so). MMQ_Q6_K has no small-batch kernel: every M runs the prefill tiles. */
 mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                     int64_t K, mmq_otype o, void* out, int64_t ldo, void* stream);
 
