@@ -42,7 +42,6 @@ import argparse
 import json
 import os
 import re
-import subprocess
 import sys
 import time
 
@@ -70,6 +69,8 @@ MEASURED_TRAFFIC_BYTES = {
     "cfg5_moe_iq1t": 387556612,
     "dec8_q4_0": 11137667,
     "dec8_q4_K": 45158633,
+    "cfg6_q6_K": 475612543,
+    "cfg5c_moe_iq1c": 387268560,
 }
 
 RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "q6_K": 210 / 8,
@@ -84,13 +85,30 @@ def log(*a):
 
 
 def sclk_mhz():
-    """Current shader clock from rocm-smi (a child process), or None."""
+    """Current shader clock of cuda:0 read from sysfs (the DPM level marked '*'), or None. A
+    file read: this process has initialised the GPU, so it starts no other program for it. The
+    card is matched by PCI bus when torch reports one, else the first card with the file."""
+    import glob
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        m = re.findall(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", r.stdout, flags=re.I)
-        return int(m[0]) if m else None
+        import torch
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
     except Exception:
-        return None
+        bus = None
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if bus is not None:
+        tag = f":{int(bus):02x}:"
+        files = [f for f in files if tag in os.path.realpath(os.path.dirname(f))] or files
+    try:
+        for f in files:
+            with open(f) as fh:
+                for line in fh:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*mhz", line, flags=re.I)
+                        if m:
+                            return int(m.group(1))
+    except OSError:
+        pass
+    return None
 
 
 def _oracle_env():
