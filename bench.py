@@ -367,7 +367,7 @@ def main():
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
 
         kernels = [("quantize_q8_1", lambda r: mmq.quantize_act(xd, out=act)),
-                   ("mmvq (decode)" if decode and fmt != "q6_K" else "mmq_block",
+                   ("mmvq (decode)" if decode else "mmq_block",
                     lambda r: mmq.gemm(fmt, packed[r], act, M, N, K, "f32", out=out))]
         dom = 1
         # raw weights + q8_1 activations (int8 values, f32 scale, int32 sum) + f32 output

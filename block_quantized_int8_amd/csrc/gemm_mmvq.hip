@@ -29,6 +29,11 @@
 //    (xs*xsum) four blocks at a time with one f32 MFMA (minfer R1 section 2.2). W8A8 has no
 //    per-block scale: its int32 accumulator runs through the whole of K and the epilogue
 //    applies the two per-row scales (metainfer "INT8 W8A8 GEMM - Prefill", section 1);
+//  * q6_K's scale changes every 16 values (minfer R1 sections 2.2 and 3.3: two half-block sums
+//    per 32 values, each with its own d*sc). A lane's fragment bytes are one half of one block
+//    (k-groups 0 and 2 hold halves 0, k-groups 1 and 3 halves 1), so each pair runs two int8
+//    MFMAs over the weight operand with the other half's lanes zeroed, two scale MFMAs (the
+//    half-0 and half-1 scale regions) and two FMAs into the same accumulator;
 //  * persistent workgroups own 16-row weight groups; their 16 waves split the blocks of K
 //    (chunks of 4 blocks dealt round-robin) and keep two chunks' loads in flight, across
 //    group boundaries; the waves' partial sums meet in LDS and are added in a fixed order.
@@ -87,7 +92,7 @@ template <mmq_wtype FMT> struct VQ;
 
 template <> struct VQ<MMQ_Q8_0> {
     static constexpr int FB = 1024, NMF = 1;
-    static constexpr bool MIN = false, ROW = false, META = false;
+    static constexpr bool MIN = false, ROW = false, META = false, DUAL = false;
     static constexpr float POST = 1.0f;
     typedef v4i Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld128(r, off); }
@@ -100,11 +105,17 @@ template <> struct VQ<MMQ_I8_ROW> : VQ<MMQ_Q8_0> {
     static constexpr bool ROW = true;
 };
 
+// q6_K: int8 q - 32 in the q8_0 fragment layout; scale dwords per 16-value half (half 0 in the
+// scale region, half 1 in the second region), each the exact f16 pair (hi, lo) of d*sc_h
+template <> struct VQ<MMQ_Q6_K> : VQ<MMQ_Q8_0> {
+    static constexpr bool DUAL = true;
+};
+
 // q4_0: X0 holds values 0-3 in its high nibbles and 4-7 in its low ones (X1: 8-15), each the
 // 4-bit two's complement of nib - 8, so the masked bytes are int8 16*(nib-8).
 template <> struct VQ<MMQ_Q4_0> {
     static constexpr int FB = 512, NMF = 1;
-    static constexpr bool MIN = false, ROW = false, META = false;
+    static constexpr bool MIN = false, ROW = false, META = false, DUAL = false;
     static constexpr float POST = 1.0f / 16;
     typedef uint2 Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld64(r, off); }
@@ -121,7 +132,7 @@ template <> struct VQ<MMQ_Q4_0> {
 // scale dword is the exact f16 pair (hi, lo) of d*sc, the min region -dmin*m.
 template <> struct VQ<MMQ_Q4_K> {
     static constexpr int FB = 512, NMF = 1;
-    static constexpr bool MIN = true, ROW = false, META = false;
+    static constexpr bool MIN = true, ROW = false, META = false, DUAL = false;
     static constexpr float POST = 1.0f;
     typedef uint2 Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld64(r, off); }
@@ -142,7 +153,7 @@ template <> struct VQ<MMQ_Q4_K> {
 // chained int8 MFMAs. tab[s | sign << 3] = (byte LUT code -> v, byte LUT code -> 2s*v).
 template <> struct VQ<MMQ_IQ1T> {
     static constexpr int FB = 256, NMF = 2;
-    static constexpr bool MIN = false, ROW = false, META = true;
+    static constexpr bool MIN = false, ROW = false, META = true, DUAL = false;
     static constexpr float POST = 1.0f / 8;
     typedef uint32_t Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld32(r, off); }
@@ -180,7 +191,7 @@ template <> struct VQ<MMQ_IQ1T> {
 struct MvArgs {
     const uint8_t* w;           // packed weights
     int64_t w_scale_off;        // scale region (per-row f32 sw for W8A8)
-    int64_t w_min_off;          // q4_K min region
+    int64_t w_min_off;          // q4_K min region; q6_K half-1 scale region
     const uint8_t* xq;          // act region 0: tiled int8 values (token tile 0)
     const uint32_t* xs2;        // q8_1 region 3: xs as an f16 pair, tile-major
     const float* xsx;           // q8_1 region 4: xs * xsum, tile-major
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         typename T::Raw w[2];
         v4i x[TG][2];                // register path only
         int b0, tk[TG];
-        uint32_t ws, xs[TG];
+        uint32_t ws, ws2, xs[TG];
         uint32_t wso[2];
         float xm[TG], wm;
     };
@@ -345,6 +356,8 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             const rsrc_t rs = rsrc(wx + a.w_scale_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128);
             const rsrc_t rxs = rsrc(xsb + (int64_t)b0 * 128, MV_CH * 128);
             k.ws = ld32(rs, o_s);
+            if constexpr (T::DUAL)
+                k.ws2 = ld32(rsrc(wx + a.w_min_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128), o_s);
 #pragma unroll
             for (int x = 0; x < TG; ++x)       // token of row c16, block b0 + g
                 k.xs[x] = ld32(rxs, k.tk[x] >= 0 ? (uint32_t)(g * 128 + k.tk[x] * 4) : OOR);
@@ -397,6 +410,19 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             for (int x = 0; x < TG; ++x) {
                 if constexpr (T::ROW) {
                     iacc[x] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], bop[0], iacc[x], 0, 0, 0);
+                } else if constexpr (T::DUAL) {
+                    // half h's dot: the weight lanes of the other half read as zero
+                    const v4i w0 = fh == 0 ? bop[0] : zi, w1 = fh == 0 ? zi : bop[0];
+                    const v4i D0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], w0, zi, 0, 0, 0);
+                    const v4i D1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], w1, zi, 0, 0, 0);
+                    const uint32_t xa = (p == 0 ? sel0 : sel1) ? k.xs[x] : 0u;
+                    const v4f S0 = __builtin_amdgcn_mfma_f32_16x16x16f16(as_h4(xa), as_h4(k.ws), zf, 0, 0, 0);
+                    const v4f S1 = __builtin_amdgcn_mfma_f32_16x16x16f16(as_h4(xa), as_h4(k.ws2), zf, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < NR; ++v) {
+                        acc[x][v] = __builtin_fmaf((float)D0[v], S0[v], acc[x][v]);
+                        acc[x][v] = __builtin_fmaf((float)D1[v], S1[v], acc[x][v]);
+                    }
                 } else {
                     v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], bop[0], zi, 0, 0, 0);
                     if constexpr (T::NMF == 2) D = __builtin_amdgcn_mfma_i32_16x16x64_i8(xo[x][p], bop[1], D, 0, 0, 0);
@@ -567,7 +593,7 @@ hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
 int mmvq_max_tokens() { return MV_TOK; }
 
 bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K) {
-    if (t == MMQ_I8_ROW || t == MMQ_Q6_K || T < 1 || T > MV_ID_TOK || T * top_k > MV_IDP) return false;
+    if (t == MMQ_I8_ROW || T < 1 || T > MV_ID_TOK || T * top_k > MV_IDP) return false;
     return round_up(K / QK, KB_ALIGN) <= XCap<1>::KB;          // batches of 8: one token group
 }
 
@@ -605,6 +631,7 @@ hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void
         case MMQ_Q4_0: launch_xl<MMQ_Q4_0, true, true>(args, grid, s); break;
         case MMQ_Q4_K: launch_xl<MMQ_Q4_K, true, true>(args, grid, s); break;
         case MMQ_IQ1T: launch_xl<MMQ_IQ1T, true, true>(args, grid, s); break;
+        case MMQ_Q6_K: launch_xl<MMQ_Q6_K, true, true>(args, grid, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -642,6 +669,8 @@ hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t
         case MMQ_Q4_K: return launch_fmt<MMQ_Q4_K>(args, s);
         case MMQ_IQ1T: return launch_fmt<MMQ_IQ1T>(args, s);
         case MMQ_I8_ROW: return launch_fmt<MMQ_I8_ROW>(args, s);
+        case MMQ_Q6_K: return launch_fmt<MMQ_Q6_K>(args, s);
+        default: break;
     }
     return hipErrorInvalidValue;
 }

@@ -173,7 +173,7 @@ mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux,
  * empty; llama.cpp PR #304, Summary: small batches stay on a matrix-vector kernel). Both
  * compute the same per-block integer dots; the small-batch kernel reads the zero padding
  * rows M..31 of the activation buffer, so that padding must be zero (mmq_quantize_act
- * writes it so). MMQ_Q6_K has no small-batch kernel: every M runs the prefill tiles. */
+ * writes it so). */
 mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                     int64_t K, mmq_otype o, void* out, int64_t ldo, void* stream);
 

@@ -9,7 +9,8 @@ rescaled by its own d*sc (minfer R1 sections 2.2 and 3.3). The checks:
 * prefill: q8_1 bit-exact, the per-16 int32 partials (two per block) bit-exact, f32 within
   max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4), on shapes with
   ragged M and N tails and both signs of sub-scale, plus worst-case blocks;
-* small batches (M <= 16 also run the prefill tiles for this format), MUL_MAT_ID, and the 7B
+* small batches (M <= 16: the decode kernel, two half-block MFMAs per block), MUL_MAT_ID
+  (prefill gather and, for at most 4 tokens, the decode kernel), and the 7B
   ffn_down shape (M = 2048, N = 4096, K = 11008) on sampled rows and columns in the launch
   configuration the bench times.
 """
@@ -113,15 +114,31 @@ def test_extreme_blocks(env):
     assert _rel(out, orc.gemm_f64("q6_K", raw, N, K, rq, rs)) <= GATE
 
 
-@pytest.mark.parametrize("M", [1, 8, 16])
-def test_small_batches(env, M):
+# small batches run the decode kernel: token rows staged in LDS (K up to 448 blocks for M <= 8,
+# 128 for M > 8) or loaded per wave (longer K), every live-register count, ragged N
+@pytest.mark.parametrize("M,K", [(1, 2304), (3, 2304), (8, 2304), (16, 2304), (2, 11008), (8, 11008),
+                                 (13, 11008)])
+def test_small_batches(env, M, K):
     _, _, orc = env
-    N, K = 300, 2304
+    N = 300
+    print(f"[case] q6_K decode M={M} N={N} K={K}", flush=True)
     raw = gen.weights_q6_K(N, K, seed=M, cfg=64)
     x = gen.act_f32(M, K, seed=M, cfg=64)
     _, _, out, _ = _run(env, raw, x, M, N, K, partials=False)
     rq, rs, _ = orc.quantize_q8_1(x)
     assert _rel(out, orc.gemm_f64("q6_K", raw, N, K, rq, rs)) <= GATE
+
+
+def test_small_batch_matches_prefill_tiles(env):
+    # M = 16 (decode kernel) against M = 17 (prefill tiles) on the same first 16 rows: both are
+    # the same per-half contraction, so they agree to f32 rounding order
+    torch, mmq, _ = env
+    N, K = 200, 1024
+    raw = gen.weights_q6_K(N, K, seed=5, cfg=66)
+    x = gen.act_f32(17, K, seed=5, cfg=66)
+    _, _, o17, _ = _run(env, raw, x, 17, N, K, partials=False)
+    _, _, o16, _ = _run(env, raw, x[:16], 16, N, K, partials=False)
+    assert _rel(o16, o17[:16].astype(np.float64)) <= 1e-5
 
 
 def test_moe(env):
@@ -131,6 +148,29 @@ def test_moe(env):
     ids = gen.moe_ids(T, top_k, E, seed=9, cfg=65)
     raw = gen.moe_weights("q6_K", E, N, K, seed=9, cfg=65)
     x = gen.act_f32(T, K, seed=9, cfg=65, outlier_rate=1e-3)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
+    pb = mmq.packed_bytes("q6_K", N, K)
+    packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        mmq.repack_weights("q6_K", torch.from_numpy(np.ascontiguousarray(raw[e])).to(dev), N, K,
+                           out=packed[e * pb:(e + 1) * pb])
+    out = mmq.gemm_id("q6_K", packed, E, act, torch.from_numpy(ids).to(dev), T, top_k, N, K)
+    torch.cuda.synchronize()
+    rq, rs, _ = orc.quantize_q8_1(x)
+    ref = orc.moe_f64("q6_K", raw.reshape(E * N, -1), E, N, K, rq, rs, ids)
+    assert _rel(out.cpu().numpy(), ref) <= GATE
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_moe_decode(env, T):
+    # MUL_MAT_ID with at most 4 tokens runs the decode kernel per expert
+    torch, mmq, orc = env
+    dev = torch.device("cuda:0")
+    E, top_k, N, K = 16, 8, 160, 1024
+    print(f"[case] q6_K moe decode T={T}", flush=True)
+    ids = gen.moe_ids(T, top_k, E, seed=T, cfg=67)
+    raw = gen.moe_weights("q6_K", E, N, K, seed=T, cfg=67)
+    x = gen.act_f32(T, K, seed=T, cfg=67)
     act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
     pb = mmq.packed_bytes("q6_K", N, K)
     packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
