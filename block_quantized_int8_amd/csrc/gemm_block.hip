@@ -203,7 +203,7 @@ template <> struct BT<MMQ_Q6_K> {
 
 // ------------------------------------------------------------------- kernel configuration
 // GATHER_F32: MUL_MAT_ID full units (up to unit_rows pairs of one expert); GATHER_TAIL: the
-// tail unit of an expert (the at most unit_rows/2 pairs after its full units).
+// tail unit of an expert (the at most TAIL_ROWS pairs after its full units).
 enum Mode { DENSE_F32 = 0, DENSE_PARTIALS = 1, GATHER_F32 = 2, GATHER_TAIL = 3 };
 constexpr bool is_gather(int mode) { return mode == GATHER_F32 || mode == GATHER_TAIL; }
 
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         const int e = lo;
         if constexpr (MODE == GATHER_TAIL) {
             unit_first = args.offs[e] + (args.ufull[e + 1] - args.ufull[e]) * args.unit_rows;
-            unit_count = args.offs[e + 1] - unit_first;           // 1 .. unit_rows/2 <= TM*32
+            unit_count = args.offs[e + 1] - unit_first;           // 1 .. TAIL_ROWS = TM*32
         } else {
             unit_first = args.offs[e] + (u - args.uoff[e]) * args.unit_rows;
             unit_count = min(args.unit_rows, args.offs[e + 1] - unit_first);
@@ -720,14 +720,19 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
 constexpr int WN_ = 2, WM_ = 2, RT_ = 2, CT_ = 2;
 constexpr bool XM_ = true;        // conversion on the matrix core (see the kernel notes)
 // MUL_MAT_ID: 4 x 1 waves, each 1 weight tile x 2 token tiles -> 128 weight rows x 64 token
-// slots. An expert sees about T*top_k/E tokens (64 for 512 tokens, top-8 of 64), so 64-slot
-// units leave fewer empty slots than 128-slot ones, with the same unpack work per tile pair.
+// slots per full unit. An expert sees about T*top_k/E pairs (64 +- 8 for 512 tokens, top-8 of
+// 64), so 64-slot units leave fewer empty slots than 128-slot ones, with the same unpack work per
+// tile pair. An expert's remainder of at most 32 pairs is one tail unit (one token tile per
+// wave); a larger remainder is one more full unit. (96-slot full units with 64-slot tails read
+// every expert's weights once on that routing, but need 198 instead of 160 registers for IQ1T,
+// 2 instead of 3 waves per SIMD, and measured 2.5% slower.)
 constexpr int GWN_ = 4, GWM_ = 1, GRT_ = 1, GCT_ = 2;
-// Tail units (at most 32 pairs): the same with one token tile per wave. With ~64 +- 8 pairs per
-// expert, splitting off tails this way leaves at most 31 empty slots per expert.
 constexpr int TCT_ = 1;
 constexpr int UNIT_ROWS = GWM_ * GCT_ * 32;
-static_assert(UNIT_ROWS / 2 <= GWM_ * TCT_ * 32, "a tail unit fits the tail configuration");
+constexpr int TAIL_ROWS = GWM_ * TCT_ * 32;
+static_assert(TAIL_ROWS < UNIT_ROWS, "a tail unit is smaller than a full unit");
+// Small dense problems: 4 x 1 waves of one tile each, 128 weight rows x 32 token rows.
+constexpr int DCT_ = 1;
 
 template <mmq_wtype FMT>
 BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, int64_t K) {
@@ -779,7 +784,7 @@ hipError_t launch_dense(const void* packed, const void* act, int64_t M, int64_t 
     g.ldo = ldo;
     if (ceil_div(N, WN_ * RT_ * 32) * ceil_div(M, WM_ * CT_ * 32) >= DENSE_FILL)
         return launch_dense_cfg<FMT, WN_, WM_, RT_, CT_>(g, M, N, o, out, s);
-    return launch_dense_cfg<FMT, GWN_, GWM_, GRT_, TCT_>(g, M, N, o, out, s);
+    return launch_dense_cfg<FMT, GWN_, GWM_, GRT_, DCT_>(g, M, N, o, out, s);
 }
 
 template <mmq_wtype FMT>
@@ -812,14 +817,16 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
 
 }  // namespace
 
-// Pairs per full MUL_MAT_ID unit (one full-unit workgroup's token extent).
+// Pairs per full MUL_MAT_ID unit (one full-unit workgroup's token extent), and the largest
+// remainder that goes to a tail unit.
 int gather_unit_tokens() { return UNIT_ROWS; }
+int gather_tail_tokens() { return TAIL_ROWS; }
 
 // A grid stays below 2^32 work-items: 2^24 workgroups of 256 threads.
 constexpr int64_t MAX_GRID = (int64_t(1) << 24) - 1;
 
 bool dense_grid_ok(int64_t M, int64_t N) {      // the larger of the two dense grids
-    return ceil_div(N, GWN_ * GRT_ * 32) * ceil_div(M, GWM_ * TCT_ * 32) <= MAX_GRID;
+    return ceil_div(N, GWN_ * GRT_ * 32) * ceil_div(M, GWM_ * DCT_ * 32) <= MAX_GRID;
 }
 
 bool gather_grid_ok(int64_t max_units, int64_t N) {

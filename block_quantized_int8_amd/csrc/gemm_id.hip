@@ -5,12 +5,12 @@
 // expert, which it reports dominates prompt processing otherwise):
 //   1. route_kernel (one workgroup): count pairs per expert in LDS; split each expert's c pairs
 //      into full units of U = gather_unit_tokens() pairs plus, when the remainder is at most
-//      U/2, one tail unit (a larger remainder is a last full unit); exclusive scans of the
-//      pair counts (pair offsets), full-unit counts and tail-unit counts (unit offsets); then
-//      scatter the pair ids into expert order.
-//   2. the gather-mode MMQ kernel, one launch for the full units and one for the tails (a
-//      workgroup per (unit, 128-row weight tile); tails use one 32-slot token tile per wave, so
-//      at most 31 slots per expert stay empty). A workgroup finds its expert by binary search
+//      R = gather_tail_tokens(), one tail unit (a larger remainder is a last full unit);
+//      exclusive scans of the pair counts (pair offsets), full-unit counts and tail-unit counts
+//      (unit offsets); then scatter the pair ids into expert order.
+//   2. the gather-mode MMQ kernel, one launch for the full units (64 token slots) and one for
+//      the tails (32 slots, one token tile per wave); a workgroup per (unit, 128-row weight
+//      tile). A workgroup finds its expert by binary search
 //      over the unit offsets, reads its tokens' activation rows and writes each pair's own
 //      output row.
 // No host round trip: the grids are sized for the worst case and workgroups past the actual
@@ -39,12 +39,12 @@ IdWorkspace id_workspace(int64_t E, int64_t P) {
     return w;
 }
 
-// full units and tail units of an expert with c pairs (unit size U)
-__device__ inline int full_units(int c, int U) { return c / U + (c % U > U / 2 ? 1 : 0); }
-__device__ inline int tail_units(int c, int U) { const int r = c % U; return (r > 0 && r <= U / 2) ? 1 : 0; }
+// full units and tail units of an expert with c pairs (unit size U, tail size at most R < U)
+__device__ inline int full_units(int c, int U, int R) { return c / U + (c % U > R ? 1 : 0); }
+__device__ inline int tail_units(int c, int U, int R) { const int r = c % U; return (r > 0 && r <= R) ? 1 : 0; }
 
 __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                             int U, int32_t* __restrict__ offs,
+                                                             int U, int R, int32_t* __restrict__ offs,
                                                              int32_t* __restrict__ ufull,
                                                              int32_t* __restrict__ utail,
                                                              int32_t* __restrict__ perm) {
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __r
     int sc = 0, sf = 0, st = 0;
     for (int e = e0; e < e1; ++e) {
         sc += cnt[e];
-        sf += full_units(cnt[e], U);
-        st += tail_units(cnt[e], U);
+        sf += full_units(cnt[e], U, R);
+        st += tail_units(cnt[e], U, R);
     }
     // inclusive scans across the wave, then across the 16 waves
     int ic = sc, jf = sf, jt = st;
@@ -100,8 +100,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __r
         utail[e] = pt;
         cur[e] = pc;
         pc += cnt[e];
-        pf += full_units(cnt[e], U);
-        pt += tail_units(cnt[e], U);
+        pf += full_units(cnt[e], U, R);
+        pt += tail_units(cnt[e], U, R);
     }
     if (tid == ROUTE_THREADS - 1) {
         offs[E] = pc;
@@ -141,7 +141,7 @@ hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void
     int32_t* utail = ws + w.utail_w;
     int32_t* perm = ws + w.perm_w;
     hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, ids, (int)P, (int)E,
-                       gather_unit_tokens(), offs, ufull, utail, perm);
+                       gather_unit_tokens(), gather_tail_tokens(), offs, ufull, utail, perm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // a decode batch of a few tokens: the decode kernel

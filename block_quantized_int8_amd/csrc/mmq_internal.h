@@ -150,13 +150,14 @@ hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, i
 // Dense grids: false if the launch would exceed the grid limit (checked before any launch).
 bool dense_grid_ok(int64_t M, int64_t N);
 // MUL_MAT_ID gather: full units (ufull offsets, up to gather_unit_tokens() pairs) and tail
-// units (utail offsets, at most half that), each a launch of its own.
+// units (utail offsets, at most gather_tail_tokens() pairs), each a launch of its own.
 hipError_t launch_block_gather(mmq_wtype t, const void* packed, int64_t E, const void* act,
                                int64_t T, int64_t top_k, int64_t N, int64_t K,
                                const int32_t* offs, const int32_t* ufull, const int32_t* utail,
                                const int32_t* perm, int max_full, int max_tail, void* out,
                                hipStream_t s);
 int gather_unit_tokens();
+int gather_tail_tokens();
 bool gather_grid_ok(int64_t max_units, int64_t N);
 int64_t gemm_id_max_units(int64_t E, int64_t P);
 bool w8a8_grid_ok(int64_t M, int64_t N);

@@ -74,7 +74,7 @@ def test_moe_uniform_routing(env, fmt):
 
 
 def test_moe_hot_expert_empty_experts_and_invalid_ids(env):
-    # 300 tokens: slot 0 always expert 2 (three 128-token units), slot 1 spread over experts
+    # 300 tokens: slot 0 always expert 2 (four 64-pair units and a tail), slot 1 spread over experts
     # 5..7, experts 0, 1, 3, 4 empty; a few ids out of range in both directions
     E, T, top_k, N, K = 8, 300, 2, 160, 256
     r = np.random.default_rng(7)
@@ -111,8 +111,9 @@ def test_moe_workspace_reuse_and_determinism(env):
 @pytest.mark.parametrize("fmt", ["q4_0", "iq1t"])
 def test_moe_unit_boundaries(env, fmt):
     # per-expert pair counts on both sides of the gather unit sizes (64-pair full units, tails
-    # of at most 32): 0, 31, 32, 33, 64, 65, 96, 97 pairs; top_k = 2, pairs in shuffled order
-    counts = [0, 31, 32, 33, 64, 65, 96, 97]
+    # of at most 32): a tail of 1, 31, 32; one full unit of 33, 63, 64; a full unit plus a tail
+    # (65, 96); two full units (97, 128); and an empty expert. top_k = 2, shuffled pairs
+    counts = [0, 1, 31, 32, 33, 63, 64, 65, 96, 97, 128]
     E, top_k, N, K = len(counts), 2, 160, 256
     flat = np.repeat(np.arange(E, dtype=np.int32), counts)
     assert flat.size % top_k == 0
