@@ -31,6 +31,11 @@ K/256 consecutive blocks):
           6 bytes of 3-bit sub-scales s (one per 16 values, LSB-first), f16 d.
           The grid is a table of 2048 uint16 entries, each eight 2-bit codes
           c = g+1 (value j at bits 2j..2j+1).     w = d*(2s+1)*(g+delta)
+* iq1s  - 50 B per 256 values (the IQ1_S codebook form, 1.5625 bits per value):
+          f16 d, 32 bytes qs (low 8 bits of each 8-value group's 11-bit grid index),
+          8 uint16 qh, one per 32 values: bits 3j..3j+2 = index bits 8-10 of the
+          block's group j (j < 4), bits 12-14 = the block's sub-scale s, bit 15 =
+          its delta sign. Same grid as iq1c.        w = d*(2s+1)*(g+delta)
 * q6_K  - 210 B per 256 values: 128 bytes ql, 64 bytes qh, 16 int8 sub-scales
           sc (one per 16 values), f16 d. In 32-value block j, value 32j+i
           (i < 16) has its low 4 bits in the low nibble of ql[16j+i] and value
@@ -49,8 +54,8 @@ import numpy as np
 QK = 32          # values per quantisation block
 QK_SUPER = 256   # values per K-quant / iq1t super-block
 
-ROW_BYTES_PER_BLOCK = {"q8_0": 34, "q4_0": 18, "q4_K": 144, "iq1t": 76, "iq1c": 56, "q6_K": 210}
-VALUES_PER_BLOCK = {"q8_0": 32, "q4_0": 32, "q4_K": 256, "iq1t": 256, "iq1c": 256, "q6_K": 256}
+ROW_BYTES_PER_BLOCK = {"q8_0": 34, "q4_0": 18, "q4_K": 144, "iq1t": 76, "iq1c": 56, "iq1s": 50, "q6_K": 210}
+VALUES_PER_BLOCK = {"q8_0": 32, "q4_0": 32, "q4_K": 256, "iq1t": 256, "iq1c": 256, "iq1s": 256, "q6_K": 256}
 
 # tensor ids inside a configuration's seed sequence
 T_ACT, T_WEIGHT, T_IDS, T_OUTLIER, T_GRID = 0, 1, 2, 3, 4
@@ -252,6 +257,24 @@ def weights_iq1c(N: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T
     return out.reshape(N, -1)
 
 
+def weights_iq1s(N: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T_WEIGHT,
+                  d_value: float = 0.02 / 4) -> np.ndarray:
+    """IQ1_S codebook rows: per 8 values a grid index uniform in 0..2047; per 32 values s
+    uniform in 0..7 and a delta sign uniform in {0, 1}; d = f16(d_value) per super-block."""
+    nsb = K // QK_SUPER
+    r = rng(seed, cfg, tensor)
+    out = np.empty((N, nsb, 50), dtype=np.uint8)
+    idx = r.integers(0, GRID_SIZE, size=(N, nsb, 8, 4), dtype=np.uint16)
+    s = r.integers(0, 8, size=(N, nsb, 8), dtype=np.uint16)
+    sgn = r.integers(0, 2, size=(N, nsb, 8), dtype=np.uint16)
+    out[..., 0:2] = np.full((N, nsb), np.float16(d_value)).view(np.uint8).reshape(N, nsb, 2)
+    out[..., 2:34] = (idx & 0xFF).astype(np.uint8).reshape(N, nsb, 32)
+    hi = (idx >> 8) & 7
+    qh = hi[..., 0] | (hi[..., 1] << 3) | (hi[..., 2] << 6) | (hi[..., 3] << 9) | (s << 12) | (sgn << 15)
+    out[..., 34:50] = qh.astype(np.uint16).view(np.uint8).reshape(N, nsb, 16)
+    return out.reshape(N, -1)
+
+
 def i8_rows(R: int, K: int, *, seed: int = 0, cfg: int = 0, tensor: int = T_WEIGHT):
     """Per-row int8: v ~ N(0,1), scale = max|v|/127 (f32), q = clip(rint(v/scale), -127, 127)."""
     v = rng(seed, cfg, tensor).standard_normal((R, K), dtype=np.float32)
@@ -271,6 +294,8 @@ def weights(fmt: str, N: int, K: int, **kw):
         return weights_iq1t(N, K, **kw)
     if fmt == "iq1c":
         return weights_iq1c(N, K, **kw)
+    if fmt == "iq1s":
+        return weights_iq1s(N, K, **kw)
     if fmt == "q6_K":
         return weights_q6_K(N, K, **kw)
     if fmt == "i8_row":
@@ -302,6 +327,8 @@ CONFIGS = {
     "cfg5_moe_iq1t": dict(cfg=5, fmt="iq1t", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
     # the same MoE with the IQ1_M codebook form of the weights (1.75 bits per value)
     "cfg5c_moe_iq1c": dict(cfg=5, fmt="iq1c", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
+    # and with the IQ1_S codebook form (1.5625 bits per value)
+    "cfg5s_moe_iq1s": dict(cfg=5, fmt="iq1s", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
     # decode batches (a few tokens) on the same weight shapes: the small-M path
     "dec1_q4_0": dict(cfg=2, fmt="q4_0", M=1, N=4096, K=4096, out="f32", outlier_rate=1e-3),
     "dec8_q4_0": dict(cfg=2, fmt="q4_0", M=8, N=4096, K=4096, out="f32", outlier_rate=1e-3),

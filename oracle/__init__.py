@@ -36,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mmq_oracle.c")
 _LIB = os.path.join(_HERE, "liborc.so")
 
-FMT_ID = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "iq1c": 4, "q6_K": 5}
+FMT_ID = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "iq1c": 4, "q6_K": 5, "iq1s": 6}
 
 
 def build(force: bool = False) -> str:
@@ -146,11 +146,11 @@ def quantize_i8_token(x: np.ndarray):
 # ------------------------------------------------------------ C decode / partials
 
 def _grid_arg(fmt: str, grid):
-    """The iq1c codebook as a contiguous uint16 [2048] array (required for iq1c only)."""
-    if fmt != "iq1c":
+    """The codebook as a contiguous uint16 [2048] array (required for iq1c and iq1s only)."""
+    if fmt not in ("iq1c", "iq1s"):
         return None
     if grid is None:
-        raise ValueError("iq1c needs its grid (uint16 [2048])")
+        raise ValueError(f"{fmt} needs its grid (uint16 [2048])")
     g = _c(grid, np.uint16)
     if g.shape != (2048,):
         raise ValueError("the iq1c grid has 2048 entries")
@@ -252,8 +252,8 @@ def dequant_weights(fmt: str, raw: np.ndarray, N: int, K: int, grid=None) -> np.
     """w_hat [N,K] in f64 from each format's defining formula (independent of the C decoder):
     q8_0 d*q; q4_0 d*(nib-8); q4_K d*sc*nib - dmin*m (minfer R1 section 2.2);
     q6_K d*sc_h*(q-32) with one int8 sc per 16 values (minfer R1 sections 2.2 and 3.3);
-    iq1t and iq1c d*(2s+1)*(g+delta) (PR #304 description; iq1c takes the eight g of a group
-    from the grid entry its 11-bit index names)."""
+    iq1t, iq1c and iq1s d*(2s+1)*(g+delta) (PR #304 description; iq1c and iq1s take the eight
+    g of a group from the grid entry its 11-bit index names; iq1s has s and delta per 32)."""
     raw = np.asarray(raw, dtype=np.uint8).reshape(N, -1)
     if fmt == "q8_0":
         b = raw.reshape(N, K // 32, 34)
@@ -304,6 +304,21 @@ def dequant_weights(fmt: str, raw: np.ndarray, N: int, K: int, grid=None) -> np.
         s = s_bits @ np.array([1.0, 2.0, 4.0])
         d = _f16(b[..., 54].astype(np.uint16) | (b[..., 55].astype(np.uint16) << 8))
         w = (d[..., None] * np.repeat(2.0 * s + 1.0, 16, axis=-1)) * (g + delta[..., None]).reshape(N, K // 256, 256)
+        return w.reshape(N, K)
+    if fmt == "iq1s":
+        table = _grid_arg(fmt, grid)
+        gvals = np.stack([(table >> (2 * j)) & 3 for j in range(8)], axis=-1).astype(np.int64)
+        if np.any(gvals == 3):
+            raise ValueError("invalid iq1s grid code (3)")
+        b = raw.reshape(N, K // 256, 50)
+        d = _f16(b[..., 0].astype(np.uint16) | (b[..., 1].astype(np.uint16) << 8))
+        qh = (b[..., 34:50:2].astype(np.int64) | (b[..., 35:50:2].astype(np.int64) << 8))   # [N, sb, 8]
+        hi = np.stack([(qh >> (3 * j)) & 7 for j in range(4)], axis=-1)                    # [N, sb, 8, 4]
+        idx = b[..., 2:34].astype(np.int64).reshape(N, K // 256, 8, 4) + 256 * hi
+        g = gvals[idx].astype(np.float64) - 1.0                                            # [N, sb, 8, 4, 8]
+        s = ((qh >> 12) & 7).astype(np.float64)
+        delta = np.where(((qh >> 15) & 1) == 1, -0.125, 0.125)
+        w = d[..., None, None, None] * (2.0 * s + 1.0)[..., None, None] * (g + delta[..., None, None])
         return w.reshape(N, K)
     if fmt == "q6_K":
         b = raw.reshape(N, K // 256, 210)

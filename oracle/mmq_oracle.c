@@ -18,8 +18,9 @@
  *    contraction out[m,n] = sum over 32-blocks of (xs*wd) * sum(xq*wq).
  *  - llama.cpp PR #304 "CUDA: add IQ1_M to MMQ", description: an IQ1_M value
  *    is d*(2s+1)*(g+delta); 8(g+delta) = 8g +- 1 and the per-16 scale becomes
- *    d(2s+1)/8. In the codebook form the ternary g of 8 values come from one
- *    grid entry named by an 11-bit index (the grid itself is an input here).
+ *    d(2s+1)/8. In the codebook forms the ternary g of 8 values come from one
+ *    grid entry named by an 11-bit index (the grid itself is an input here):
+ *    IQ1_M with s per 16 and delta per 8 values, IQ1_S with both per 32.
  *  - minfer R1 sections 2.2 and 3.3: q6_K values are a 6-bit grid 0..63 moved
  *    to the signed domain by -32, with an int8 scale per 16 values; a 32-value
  *    block is two 16-value halves with separate integer sums, each rescaled by
@@ -49,6 +50,7 @@
 #define ORC_IQ1T 3
 #define ORC_IQ1C 4
 #define ORC_Q6_K 5
+#define ORC_IQ1S 6
 
 /* ---------------------------------------------------------------- scalars */
 
@@ -274,6 +276,32 @@ static int decode_row(int fmt, const uint8_t* row, int64_t K, const uint16_t* gr
                 mult[sb * 16 + h] = (int16_t)(2 * s + 1);
             }
         }
+    } else if (fmt == ORC_IQ1S) {
+        /* block b (values 32b..32b+31) of a super-block: its uint16 qh word holds index bits
+         * 8-10 of group j (values 32b+8j..+7) at bits 3j..3j+2, s at bits 12-14 and the delta
+         * sign at bit 15; the low index bytes are qs[4b+j]. */
+        for (int64_t sb = 0; sb < K / 256; ++sb) {
+            const uint8_t* blk = row + sb * 50;
+            float d = orc_half_to_float(rd16(blk));
+            for (int b = 0; b < 8; ++b) {
+                uint16_t qh = rd16(blk + 34 + 2 * b);
+                int s = (qh >> 12) & 7;
+                int sgn = (qh >> 15) & 1;
+                for (int j = 0; j < 4; ++j) {
+                    int idx = blk[2 + 4 * b + j] | (((qh >> (3 * j)) & 7) << 8);
+                    uint16_t entry = grid[idx];
+                    for (int i = 0; i < 8; ++i) {
+                        int c = (entry >> (2 * i)) & 3;
+                        if (c == 3) bad = 1;
+                        wq[sb * 256 + 32 * b + 8 * j + i] = (int16_t)(8 * (c - 1) + (sgn ? -1 : 1));
+                    }
+                }
+                for (int h = 0; h < 2; ++h) {
+                    wd[sb * 16 + 2 * b + h] = d * (float)(2 * s + 1) / 8.0f;
+                    mult[sb * 16 + 2 * b + h] = (int16_t)(2 * s + 1);
+                }
+            }
+        }
     } else if (fmt == ORC_Q6_K) {
         /* 32-value block j of a super-block: value 32j+i (i < 16) has its low 4 bits in the
          * low nibble of ql[16j+i], value 32j+16+i in the high nibble; value 32j+8t+i (t < 4,
@@ -307,6 +335,7 @@ static int64_t raw_row_bytes(int fmt, int64_t K) {
         case ORC_Q4_K: return K / 256 * 144;
         case ORC_IQ1C: return K / 256 * 56;
         case ORC_Q6_K: return K / 256 * 210;
+        case ORC_IQ1S: return K / 256 * 50;
         default:       return K / 256 * 76;
     }
 }

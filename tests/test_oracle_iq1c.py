@@ -1,4 +1,4 @@
-"""Pins for the oracle's iq1c (IQ1_M codebook form) decoders and partials.
+"""Pins for the oracle's iq1c and iq1s (IQ1_M and IQ1_S codebook forms) decoders and partials.
 
 llama.cpp PR #304 describes an IQ1_M value as d*(2s+1)*(g+delta) where the ternary g of
 eight values come from one grid entry named by an 11-bit index, with a 3-bit sub-scale s
@@ -14,6 +14,9 @@ library's repack.
 * With d = 8 every value is an integer, so the folded per-32 partials are an integer
   matmul per block (library routine: NumPy int64 @).
 * The generated codebook holds 2048 distinct valid entries; an invalid code is rejected.
+* iq1s (IQ1_S: the same 11-bit index per 8 values, but one s and one delta sign per 32
+  values) has its own golden block, and re-laid as iq1t (s and delta repeated over the
+  block's halves and groups) decodes to the same values.
 """
 import json
 import os
@@ -31,21 +34,23 @@ def _golden_grid(closed_form):
                      for e in range(2048)], np.uint16)
 
 
-def test_golden_block_decodes(orc):
+@pytest.mark.parametrize("fmt,nbytes", [("iq1c", 56), ("iq1s", 50)])
+def test_golden_block_decodes(orc, fmt, nbytes):
     with open(os.path.join(GOLD, "weight_blocks.json")) as f:
-        g = json.load(f)["iq1c"]
+        g = json.load(f)[fmt]
     grid = _golden_grid(g["grid_closed_form"])
     raw = np.frombuffer(bytes.fromhex(g["hex"].replace(" ", "")), np.uint8)
-    assert raw.size == 56
+    assert raw.size == nbytes
     expect = np.array([eval(g["closed_form"], {}, {"i": i}) for i in range(256)], np.float64)
     for k, v in g["spot"].items():
         assert expect[int(k)] == v, k
-    wh = orc.dequant_weights("iq1c", raw[None, :], 1, 256, grid=grid)[0]
+    wh = orc.dequant_weights(fmt, raw[None, :], 1, 256, grid=grid)[0]
     assert np.array_equal(wh, expect)
-    wq, wd, wm, mult = orc.decode_row_c("iq1c", raw, 256, grid=grid)
+    wq, wd, wm, mult = orc.decode_row_c(fmt, raw, 256, grid=grid)
     assert np.array_equal(np.repeat(wd.astype(np.float64), 16) * wq, expect)
     assert np.all(wm == 0)
-    assert np.array_equal(mult, 2 * (np.arange(16) % 8) + 1)
+    s_of_half = np.arange(16) % 8 if fmt == "iq1c" else np.arange(16) // 2
+    assert np.array_equal(mult, 2 * s_of_half + 1)
 
 
 def _as_iq1t(raw_c, N, K, grid):
@@ -138,3 +143,43 @@ def test_invalid_grid_code_is_rejected(orc):
         orc.dequant_weights("iq1c", raw, 1, 256, grid=grid)
     with pytest.raises(ValueError):
         orc.partials("iq1c", raw, 1, 256, np.ones((1, 256), np.int8), grid=grid)
+
+
+def _iq1s_as_iq1t(raw_s, N, K, grid):
+    """The same g, s, delta and d in the iq1t byte layout: s and the delta sign of each 32-value
+    block repeated over its two halves and four groups (a re-layout of fields)."""
+    b = raw_s.reshape(N, K // 256, 50)
+    qh = (b[..., 34:50:2].astype(np.int64) | (b[..., 35:50:2].astype(np.int64) << 8))
+    hi = np.stack([(qh >> (3 * j)) & 7 for j in range(4)], axis=-1)
+    idx = b[..., 2:34].astype(np.int64).reshape(N, K // 256, 8, 4) | (hi << 8)
+    codes = np.stack([(grid[idx] >> (2 * j)) & 3 for j in range(8)], axis=-1).reshape(N, K // 256, 256)
+    c4 = codes.astype(np.uint8).reshape(N, K // 256, 64, 4)
+    t = np.empty((N, K // 256, 76), np.uint8)
+    t[..., 0:64] = c4[..., 0] | (c4[..., 1] << 2) | (c4[..., 2] << 4) | (c4[..., 3] << 6)
+    s16 = np.repeat((qh >> 12) & 7, 2, axis=-1).astype(np.uint64)            # [N, sb, 16]
+    word = np.zeros((N, K // 256), np.uint64)
+    for h in range(16):
+        word |= s16[..., h] << np.uint64(3 * h)
+    for k in range(6):
+        t[..., 64 + k] = ((word >> np.uint64(8 * k)) & np.uint64(0xFF)).astype(np.uint8)
+    sg = np.repeat((qh >> 15) & 1, 4, axis=-1).astype(np.uint8).reshape(N, K // 256, 4, 8)
+    t[..., 70:74] = np.packbits(sg, axis=-1, bitorder="little")[..., 0]
+    t[..., 74:76] = b[..., 0:2]
+    return t.reshape(N, -1)
+
+
+def test_iq1s_same_fields_as_iq1t(orc):
+    N, K, M = 7, 768, 3
+    grid = gen.IQ1C_GRID
+    raw = gen.weights_iq1s(N, K, seed=4, cfg=89)
+    raw_t = _iq1s_as_iq1t(raw, N, K, grid)
+    assert np.array_equal(orc.dequant_weights("iq1s", raw, N, K, grid=grid),
+                          orc.dequant_weights("iq1t", raw_t, N, K))
+    xq = np.random.default_rng(5).integers(-128, 128, size=(M, K), dtype=np.int8)
+    assert np.array_equal(orc.partials("iq1s", raw, N, K, xq, grid=grid),
+                          orc.partials("iq1t", raw_t, N, K, xq))
+    x = gen.act_f32(M, K, seed=4, cfg=89)
+    q, xs, xsum = orc.quantize_q8_1(x)
+    ref = orc.gemm_f64("iq1s", raw, N, K, q, xs, grid=grid)
+    assert np.max(np.abs(orc.gemm_c("iq1s", raw, N, K, q, xs, xsum, grid=grid) - ref)) <= 4e-7 * np.abs(ref).max()
+    assert raw.shape[1] * 8 == K * 1.5625                 # 50 B per 256 values
