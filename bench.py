@@ -73,7 +73,8 @@ MEASURED_TRAFFIC_BYTES = {
     "cfg5c_moe_iq1c": 387268560,
 }
 
-RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "q6_K": 210 / 8,
+RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "iq1s": 50 / 8,
+                    "q6_K": 210 / 8,
                     "i8_row": 32}
 # vector ops per element-block of the scale step: exact conversion + FMA, twice for q6_K (one
 # per 16-value half)
@@ -157,13 +158,13 @@ def cpu_baseline(fmt, raw, x, M, N, K, grid=None, budget_s=10.0, min_runs=3, max
 def cpu_baseline_moe(fmt, raw_e, x, ids, E, N, K, grid=None, budget_s=10.0):
     """MoE oracle leg on a bounded sample: the dense per-block C GEMM of the tokens routed to
     each expert (in expert order) until ~budget_s seconds, scaled to pair-rows per s; a small
-    workload is passed over again (at least 3 times) until the budget is used."""
+    workload is passed over again until the budget is used."""
     import oracle
     oracle.build()
     xq, xs, xsum = oracle.quantize_q8_1(x)
     rows_done, t_used, experts, passes = 0, 0.0, 0, 0
     wall0 = time.perf_counter()
-    while t_used < budget_s and (passes < 3 or t_used < 1.0) and time.perf_counter() - wall0 < 6 * budget_s:
+    while t_used < budget_s and time.perf_counter() - wall0 < 6 * budget_s:
         for e in range(E):
             tt = np.nonzero((ids == e).any(axis=1))[0]
             if len(tt) == 0:
@@ -189,7 +190,7 @@ def cpu_leg(name):
     import gen
     cfg = gen.CONFIGS[name]
     fmt, M, N, K = cfg["fmt"], cfg["M"], cfg["N"], cfg["K"]
-    grid = gen.IQ1C_GRID if fmt == "iq1c" else None
+    grid = gen.IQ1C_GRID if fmt in ("iq1c", "iq1s") else None
     log("[bench] cpu baseline (oracle) ...")
     if fmt == "i8_row":
         a, sa = gen.i8_rows(M, K, seed=0, cfg=cfg["cfg"], tensor=gen.T_ACT)
@@ -307,7 +308,7 @@ def main():
     ops = 2.0 * M * N * K
     extra = {}
     # the iq1c codebook: an input of the repack (and of the oracle leg)
-    grid_np = gen.IQ1C_GRID if fmt == "iq1c" else None
+    grid_np = gen.IQ1C_GRID if fmt in ("iq1c", "iq1s") else None
     grid_d = torch.from_numpy(grid_np.view(np.int16)).to(dev) if grid_np is not None else None
 
     def copies_of(t):

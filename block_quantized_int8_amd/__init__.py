@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libmmq.so")
 
 # enums (include/mmq.h)
 MMQ_OK, MMQ_EINVAL, MMQ_EUNSUPPORTED, MMQ_EALIGN, MMQ_EWORKSPACE, MMQ_EHIP = range(6)
-WTYPE = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "i8_row": 4, "iq1c": 5, "q6_K": 6}
+WTYPE = {"q8_0": 0, "q4_0": 1, "q4_K": 2, "iq1t": 3, "i8_row": 4, "iq1c": 5, "q6_K": 6, "iq1s": 7}
 ATYPE = {"q8_1": 0, "i8_token": 1}
 OTYPE = {"f32": 0, "bf16": 1, "i32_partials": 2}
 
@@ -142,13 +142,13 @@ def quantize_act(x, atype="q8_1", out=None, stream=None):
 def repack_weights(wtype, raw, N: int, K: int, row_scale=None, out=None, stream=None, grid=None):
     """raw: CUDA tensor holding the raw rows (uint8 bytes, or int8 [N,K] for i8_row).
     The repack's auxiliary input `aux` is row_scale (CUDA f32 [N]) for i8_row and grid (CUDA
-    uint16/int16 [2048], the codebook) for iq1c."""
+    uint16/int16 [2048], the codebook) for iq1c and iq1s."""
     import torch
     nbytes = packed_bytes(wtype, N, K)
     if nbytes == 0:
         raise MMQError("mmq_packed_bytes", MMQ_EINVAL)
     if row_scale is not None and grid is not None:
-        raise ValueError("pass row_scale (i8_row) or grid (iq1c), not both")
+        raise ValueError("pass row_scale (i8_row) or grid (iq1c, iq1s), not both")
     aux = row_scale if row_scale is not None else grid
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=raw.device)

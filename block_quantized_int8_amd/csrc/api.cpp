@@ -10,20 +10,20 @@ constexpr int64_t MAX_DIM = int64_t(1) << 24;    // keeps every index of the ker
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_wtype(int t) { return t >= MMQ_Q8_0 && t <= MMQ_Q6_K; }
+bool valid_wtype(int t) { return t >= MMQ_Q8_0 && t <= MMQ_IQ1S; }
 bool valid_atype(int a) { return a == MMQ_ACT_Q8_1 || a == MMQ_ACT_I8_TOKEN; }
 bool valid_otype(int o) { return o >= MMQ_OUT_F32 && o <= MMQ_OUT_I32_PARTIALS; }
 
 int64_t k_multiple(mmq_wtype t) {
-    return (t == MMQ_Q4_K || t == MMQ_IQ1T || t == MMQ_IQ1C || t == MMQ_Q6_K) ? 256 : 32;
+    return (t == MMQ_Q4_K || t == MMQ_IQ1T || t == MMQ_IQ1C || t == MMQ_IQ1S || t == MMQ_Q6_K) ? 256 : 32;
 }
 
 // partial sums per (row, column) in MMQ_OUT_I32_PARTIALS: one per 32-value block, q6_K one per
 // 16-value half
 int64_t partials_per_row(mmq_wtype t, int64_t K) { return t == MMQ_Q6_K ? K / 16 : K / QK; }
 
-// formats whose repack takes an auxiliary input (I8_ROW: row scales; IQ1C: the grid)
-bool needs_aux(mmq_wtype t) { return t == MMQ_I8_ROW || t == MMQ_IQ1C; }
+// formats whose repack takes an auxiliary input (I8_ROW: row scales; IQ1C, IQ1S: the grid)
+bool needs_aux(mmq_wtype t) { return t == MMQ_I8_ROW || t == MMQ_IQ1C || t == MMQ_IQ1S; }
 
 bool sizes_ok(int64_t M, int64_t N, int64_t K) {
     return M >= 1 && N >= 1 && K >= 32 && M <= MAX_DIM && N <= MAX_DIM && K <= MAX_DIM;

@@ -114,7 +114,8 @@ inline PackedLayout packed_layout(mmq_wtype t, int64_t N, int64_t K) {
         case MMQ_Q4_0: L.frag_bytes = 512; break;
         case MMQ_Q4_K: L.frag_bytes = 512; break;
         case MMQ_IQ1T:
-        case MMQ_IQ1C: L.frag_bytes = 256; break;      // IQ1C is repacked into the IQ1T form
+        case MMQ_IQ1C:
+        case MMQ_IQ1S: L.frag_bytes = 256; break;      // IQ1C / IQ1S are repacked into the IQ1T form
         case MMQ_Q6_K: L.frag_bytes = 1024; break;     // int8 q-32
         default: L.frag_bytes = 1024; break;           // I8_ROW
     }
@@ -136,8 +137,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 // internal launchers (defined in the .hip files, called by api.cpp)
 namespace mmq {
-// The packed form the GEMM kernels read: IQ1C is repacked into the IQ1T panels.
-inline mmq_wtype kernel_format(mmq_wtype t) { return t == MMQ_IQ1C ? MMQ_IQ1T : t; }
+// The packed form the GEMM kernels read: IQ1C and IQ1S are repacked into the IQ1T panels.
+inline mmq_wtype kernel_format(mmq_wtype t) { return (t == MMQ_IQ1C || t == MMQ_IQ1S) ? MMQ_IQ1T : t; }
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ldx, void* act,
                                 hipStream_t s);
 hipError_t launch_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_t ldx, void* act,

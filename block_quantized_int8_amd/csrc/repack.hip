@@ -243,6 +243,44 @@ __global__ __launch_bounds__(256) void repack_iq1c_kernel(
     }
 }
 
+// IQ1S (the IQ1_S codebook form): as IQ1C, with the block's one s and one delta sign (its
+// uint16 qh word) repeated for both halves and all four groups of the IQ1T panel.
+__global__ __launch_bounds__(256) void repack_iq1s_kernel(
+    const uint8_t* __restrict__ raw, const uint16_t* __restrict__ grid, int64_t N, int64_t KB,
+    int64_t KBp, int64_t total, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const Lane x = lane_of(gid, KBp, KB, N);
+    uint32_t C = 0, meta = 0;
+    uint16_t d = 0;
+    if (x.live) {
+        const uint8_t* blk = raw + (x.n * (KB / 8) + x.b / 8) * 50;
+        const int j = (int)(x.b % 8);                      // the block inside the super-block
+        const uint32_t qh = ld_u16(blk + 34 + 2 * j);
+#pragma unroll
+        for (int gq = 0; gq < 2; ++gq) {
+            const int q = 2 * x.h + gq;                    // the lane's group inside the block
+            const uint32_t entry = grid[blk[2 + 4 * j + q] | (((qh >> (3 * q)) & 7u) << 8)];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int v = 8 * gq + i;                  // value index inside the lane
+                C |= ((entry >> (2 * i)) & 3u) << (8 * (v & 3) + 2 * (v >> 2));
+            }
+        }
+        const uint32_t s = (qh >> 12) & 7u, sg = (qh >> 15) & 1u;
+        meta = s | (sg << 3) | (sg << 4);
+        d = ld_u16(blk);
+    }
+    *reinterpret_cast<uint32_t*>(frag + gid * 4) = C;
+    uint8_t* e = scale + ((x.nt * KBp + x.b) * 32 + x.r) * 4;
+    if (x.h == 0) {
+        *reinterpret_cast<uint16_t*>(e) = d;
+        e[2] = (uint8_t)meta;
+    } else {
+        e[3] = (uint8_t)meta;
+    }
+}
+
 __global__ __launch_bounds__(256) void repack_i8_row_kernel(
     const int8_t* __restrict__ raw, const float* __restrict__ row_scale, int64_t N, int64_t K,
     int64_t KB, int64_t KBp, int64_t total, uint8_t* __restrict__ frag, float* __restrict__ sw) {
@@ -287,6 +325,10 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const void* aux, int64_t 
         case MMQ_Q6_K:
             hipLaunchKernelGGL(repack_q6_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
                                reinterpret_cast<uint32_t*>(scale), reinterpret_cast<uint32_t*>(base + L.min_off));
+            break;
+        case MMQ_IQ1S:
+            hipLaunchKernelGGL(repack_iq1s_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,
+                               L.KB, L.KBp, total, frag, scale);
             break;
         case MMQ_IQ1C:
             hipLaunchKernelGGL(repack_iq1c_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,

@@ -63,6 +63,11 @@ typedef enum {
  *            3-bit sub-scales s (LSB-first), f16 d. The grid (passed to the repack) holds
  *            2048 uint16 entries, each eight 2-bit codes c = g+1 (value j of the group at
  *            bits 2j..2j+1; code 3 is invalid).                   w = d*(2s+1)*(g+delta)
+ *  MMQ_IQ1S  50 B per 256 values (the IQ1_S codebook form, 1.5625 bits per value): f16 d,
+ *            u8 qs[32] (low 8 bits of each 8-value group's 11-bit grid index), uint16 qh[8]
+ *            (one per 32-value block: bits 3j..3j+2 = index bits 8-10 of the block's group j,
+ *            bits 12-14 = the block's sub-scale s, bit 15 = its delta sign, 0 -> +1/8), with
+ *            the same grid as MMQ_IQ1C.                              w = d*(2s+1)*(g+delta)
  *  MMQ_Q6_K  210 B per 256 values: u8 ql[128], u8 qh[64], int8 sc[16] (one per 16 values),
  *            f16 d. In 32-value block j, value 32j+i (i < 16) has its low 4 bits in the low
  *            nibble of ql[16j+i] and value 32j+16+i in the high nibble; the high 2 bits of
@@ -71,11 +76,11 @@ typedef enum {
  *            d*|sc| must stay below 65504 (the repack splits d*sc into two f16).
  * Value formulas: minfer R1 sections 1-2.2 (q8_0, q4_0, Q4_K), 2.2 and 3.3 (q6_K: 6-bit grid
  * moved to the signed domain by -32, a scale per 16 values); llama.cpp PR #304 description
- * (IQ1_M, its 11-bit grid index per 8 values and per-16 sub-scales); metainfer "INT8 W8A8
+ * (IQ1_M and IQ1_S, the 11-bit grid index per 8 values, IQ1_M's per-16 sub-scales); metainfer "INT8 W8A8
  * GEMM - Prefill" section 1 (per-channel). */
 typedef enum {
     MMQ_Q8_0 = 0, MMQ_Q4_0 = 1, MMQ_Q4_K = 2, MMQ_IQ1T = 3, MMQ_I8_ROW = 4, MMQ_IQ1C = 5,
-    MMQ_Q6_K = 6
+    MMQ_Q6_K = 6, MMQ_IQ1S = 7
 } mmq_wtype;
 
 /* Activation formats.
@@ -93,7 +98,7 @@ typedef enum { MMQ_ACT_Q8_1 = 0, MMQ_ACT_I8_TOKEN = 1 } mmq_atype;
  *                       with MMQ_ACT_I8_TOKEN only (metainfer section 1: fragment -> scale ->
  *                       bf16, no bias)
  *  MMQ_OUT_I32_PARTIALS debug: block formats: int32 [M][N][K/32] of the exact per-block
- *                       integer dots (Q4_K: sum xq*nib with unsigned nibbles; IQ1T, IQ1C: the folded
+ *                       integer dots (Q4_K: sum xq*nib with unsigned nibbles; IQ1T, IQ1C, IQ1S: the folded
  *                       sum_h (2s_h+1) * sum_16 xq*(8g+-1)); MMQ_Q6_K: int32 [M][N][K/16], the
  *                       two half-block dots sum_16 xq*(q-32) of every block (half h of block b
  *                       at index 2b+h); MMQ_I8_ROW: int32 [M][N] of the full-K accumulators.
@@ -145,16 +150,17 @@ size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K);
 /* One-time, untimed repack of raw weights into the library's matrix-core panel layout.
  *  raw       (device) raw rows as described at mmq_wtype; for MMQ_I8_ROW the int8 [N][K]
  *            values.
- *  aux       (device) MMQ_I8_ROW: f32 [N] per-row scales; MMQ_IQ1C: the grid, uint16
- *            [2048]; must be NULL for every other format. Read only during the call's
+ *  aux       (device) MMQ_I8_ROW: f32 [N] per-row scales; MMQ_IQ1C, MMQ_IQ1S: the grid,
+ *            uint16 [2048]; must be NULL for every other format. Read only during the call's
  *            kernels; not referenced afterwards.
  *  packed    (device) mmq_packed_bytes(t, N, K) bytes; written completely (padding rows
  *            are zero). Immutable afterwards and safe to reuse across graph replays
  *            (metainfer section 3.2: one-time pack outside the timed region).
- * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, Q6_K, IQ1T, IQ1C). MMQ_IQ1C is
- * expanded here, once, through the grid into the MMQ_IQ1T panel form (2-bit codes, per-16
- * sub-scale and per-8 delta sign), so both formats share the GEMM kernels. An invalid code
- * (3, in IQ1T rows or in an IQ1C grid entry) decodes as 0 - the caller must not pass one. */
+ * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, Q6_K, IQ1T, IQ1C, IQ1S).
+ * MMQ_IQ1C and MMQ_IQ1S are expanded here, once, through the grid into the MMQ_IQ1T panel
+ * form (2-bit codes, per-16 sub-scale and per-8 delta sign; IQ1S repeats its per-32 s and
+ * sign), so the three formats share the GEMM kernels. An invalid code (3, in IQ1T rows or
+ * in a grid entry) decodes as 0 - the caller must not pass one. */
 mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux,
                               int64_t N, int64_t K, void* packed, void* stream);
 

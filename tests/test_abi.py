@@ -79,6 +79,7 @@ def test_packed_bytes(mmq):
     # iq1c is repacked into the iq1t panels: same packed size, K % 256 required
     assert mmq.packed_bytes("iq1c", 40, 512) == mmq.packed_bytes("iq1t", 40, 512)
     assert mmq.packed_bytes("iq1c", 32, 288) == 0
+    assert mmq.packed_bytes("iq1s", 40, 512) == mmq.packed_bytes("iq1t", 40, 512)
     # q6_K: int8 fragments plus two scale-dword regions (one per 16-value half)
     assert mmq.packed_bytes("q6_K", 32, 256) == 8 * 1024 + 2 * 32 * 8 * 4
     assert mmq.packed_bytes("q6_K", 32, 224) == 0
@@ -102,7 +103,7 @@ def test_validation_rejects_before_any_launch(mmq):
     assert L.mmq_gemm(0, GOOD, GOOD, 4, 32, 64, 3, GOOD, 32, None) == mmq.MMQ_EINVAL   # otype
     assert L.mmq_gemm(0, GOOD, GOOD, 4, 32, 64, 2, GOOD, 40, None) == mmq.MMQ_EINVAL   # partials ldo
     assert L.mmq_gemm(6, GOOD, GOOD, 4, 32, 128, 0, GOOD, 32, None) == mmq.MMQ_EINVAL  # q6_K K
-    assert L.mmq_gemm(7, GOOD, GOOD, 4, 32, 256, 0, GOOD, 32, None) == mmq.MMQ_EINVAL  # wtype
+    assert L.mmq_gemm(8, GOOD, GOOD, 4, 32, 256, 0, GOOD, 32, None) == mmq.MMQ_EINVAL  # wtype
     # unsupported combinations
     assert L.mmq_gemm(0, GOOD, GOOD, 4, 32, 64, 1, GOOD, 32, None) == mmq.MMQ_EUNSUPPORTED  # q8_0 bf16
     assert L.mmq_gemm(4, GOOD, GOOD, 4, 32, 64, 0, GOOD, 32, None) == mmq.MMQ_EUNSUPPORTED  # i8 f32
@@ -118,6 +119,7 @@ def test_validation_rejects_before_any_launch(mmq):
     assert L.mmq_repack_weights(3, GOOD, GOOD, 32, 256, GOOD, None) == mmq.MMQ_EINVAL
     assert L.mmq_repack_weights(5, GOOD, GOOD, 32, 128, GOOD, None) == mmq.MMQ_EINVAL   # K % 256
     assert L.mmq_repack_weights(5, GOOD, BAD, 32, 256, GOOD, None) == mmq.MMQ_EALIGN
+    assert L.mmq_repack_weights(7, GOOD, None, 32, 256, GOOD, None) == mmq.MMQ_EINVAL   # iq1s grid
 
 
 def test_gemm_id_validation(mmq):

@@ -1,8 +1,10 @@
-"""GPU parity of the IQ1_M codebook form (iq1c) against the CPU oracle, through the C ABI.
+"""GPU parity of the IQ1_M and IQ1_S codebook forms (iq1c, iq1s) against the CPU oracle,
+through the C ABI.
 
-iq1c rows carry an 11-bit grid index per 8 values (llama.cpp PR #304 description; the grid is
-the self-generated gen.IQ1C_GRID, an input of the repack). The repack expands each index
-through the grid once into the iq1t panel form, so the checks are:
+iq1c and iq1s rows carry an 11-bit grid index per 8 values (llama.cpp PR #304 description;
+the grid is the self-generated gen.IQ1C_GRID, an input of the repack); iq1c has s per 16 and
+the delta sign per 8 values, iq1s both per 32. The repack expands each index through the grid
+once into the iq1t panel form, so the checks are:
 
 * the packed buffer equals, byte for byte, the iq1t repack of the same values written in the
   iq1t layout (the iq1t path has its own parity tests);
@@ -57,20 +59,47 @@ def _as_iq1t(raw_c, N, K, grid):
     return t.reshape(N, -1)
 
 
-def _pack(env, raw, N, K):
+def _iq1s_as_iq1t(raw_s, N, K, grid):
+    """iq1s fields in the iq1t layout: the block's s and delta sign repeated per half / group."""
+    b = raw_s.reshape(N, K // 256, 50)
+    qh = (b[..., 34:50:2].astype(np.int64) | (b[..., 35:50:2].astype(np.int64) << 8))
+    hi = np.stack([(qh >> (3 * j)) & 7 for j in range(4)], axis=-1)
+    idx = b[..., 2:34].astype(np.int64).reshape(N, K // 256, 8, 4) | (hi << 8)
+    codes = np.stack([(grid[idx] >> (2 * j)) & 3 for j in range(8)], axis=-1).reshape(N, K // 256, 256)
+    c4 = codes.astype(np.uint8).reshape(N, K // 256, 64, 4)
+    t = np.empty((N, K // 256, 76), np.uint8)
+    t[..., 0:64] = c4[..., 0] | (c4[..., 1] << 2) | (c4[..., 2] << 4) | (c4[..., 3] << 6)
+    s16 = np.repeat((qh >> 12) & 7, 2, axis=-1).astype(np.uint64)
+    word = np.zeros((N, K // 256), np.uint64)
+    for h in range(16):
+        word |= s16[..., h] << np.uint64(3 * h)
+    for k in range(6):
+        t[..., 64 + k] = ((word >> np.uint64(8 * k)) & np.uint64(0xFF)).astype(np.uint8)
+    sg = np.repeat((qh >> 15) & 1, 4, axis=-1).astype(np.uint8).reshape(N, K // 256, 4, 8)
+    t[..., 70:74] = np.packbits(sg, axis=-1, bitorder="little")[..., 0]
+    t[..., 74:76] = b[..., 0:2]
+    return t.reshape(N, -1)
+
+
+AS_IQ1T = {"iq1c": _as_iq1t, "iq1s": _iq1s_as_iq1t}
+FMTS = ["iq1c", "iq1s"]
+
+
+def _pack(env, raw, N, K, fmt="iq1c"):
     torch, mmq, _, grid = env
-    return mmq.repack_weights("iq1c", torch.from_numpy(np.ascontiguousarray(raw)).to("cuda:0"), N, K,
+    return mmq.repack_weights(fmt, torch.from_numpy(np.ascontiguousarray(raw)).to("cuda:0"), N, K,
                               grid=grid)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(32, 256), (33, 768), (300, 512), (64, 4096)])
-def test_packed_equals_iq1t_packing_of_same_values(env, N, K):
+def test_packed_equals_iq1t_packing_of_same_values(env, fmt, N, K):
     torch, mmq, _, _ = env
-    print(f"[case] iq1c repack N={N} K={K}", flush=True)
-    raw = gen.weights_iq1c(N, K, seed=N + K, cfg=85)
-    assert mmq.packed_bytes("iq1c", N, K) == mmq.packed_bytes("iq1t", N, K)
-    pc = _pack(env, raw, N, K)
-    pt = mmq.repack_weights("iq1t", torch.from_numpy(_as_iq1t(raw, N, K, gen.IQ1C_GRID)).to("cuda:0"), N, K)
+    print(f"[case] {fmt} repack N={N} K={K}", flush=True)
+    raw = gen.weights(fmt, N, K, seed=N + K, cfg=85)
+    assert mmq.packed_bytes(fmt, N, K) == mmq.packed_bytes("iq1t", N, K)
+    pc = _pack(env, raw, N, K, fmt)
+    pt = mmq.repack_weights("iq1t", torch.from_numpy(AS_IQ1T[fmt](raw, N, K, gen.IQ1C_GRID)).to("cuda:0"), N, K)
     torch.cuda.synchronize()
     assert np.array_equal(pc.cpu().numpy(), pt.cpu().numpy())
 
@@ -78,87 +107,91 @@ def test_packed_equals_iq1t_packing_of_same_values(env, N, K):
 SHAPES = [(1, 32, 256), (17, 33, 256), (65, 97, 768), (130, 300, 512), (256, 256, 1024)]
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_dense_prefill(env, M, N, K):
+def test_dense_prefill(env, fmt, M, N, K):
     torch, mmq, orc, _ = env
     dev = torch.device("cuda:0")
     seed = 5 * M + N + K
-    print(f"[case] iq1c M={M} N={N} K={K} seed={seed}", flush=True)
-    raw = gen.weights_iq1c(N, K, seed=seed, cfg=86)
+    print(f"[case] {fmt} M={M} N={N} K={K} seed={seed}", flush=True)
+    raw = gen.weights(fmt, N, K, seed=seed, cfg=86)
     x = gen.act_f32(M, K, seed=seed, cfg=86, outlier_rate=1e-2)
     act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
-    packed = _pack(env, raw, N, K)
-    out = mmq.gemm("iq1c", packed, act, M, N, K, "f32")
-    parts = mmq.gemm("iq1c", packed, act, M, N, K, "i32_partials")
+    packed = _pack(env, raw, N, K, fmt)
+    out = mmq.gemm(fmt, packed, act, M, N, K, "f32")
+    parts = mmq.gemm(fmt, packed, act, M, N, K, "i32_partials")
     torch.cuda.synchronize()
     rq, rs, rsum = orc.quantize_q8_1(x)
     xq, xs, xsum = mmq.act_to_host(act.cpu().numpy(), M, K)
     assert np.array_equal(xq, rq) and np.array_equal(xsum, rsum)
-    assert np.array_equal(parts.cpu().numpy(), orc.partials("iq1c", raw, N, K, rq, grid=gen.IQ1C_GRID))
-    rel = _rel(out.cpu().numpy(), orc.gemm_f64("iq1c", raw, N, K, rq, rs, grid=gen.IQ1C_GRID))
+    assert np.array_equal(parts.cpu().numpy(), orc.partials(fmt, raw, N, K, rq, grid=gen.IQ1C_GRID))
+    rel = _rel(out.cpu().numpy(), orc.gemm_f64(fmt, raw, N, K, rq, rs, grid=gen.IQ1C_GRID))
     print(f"  rel err {rel:.3e}")
     assert rel <= GATE
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 4, 8, 16])
-def test_decode_batches(env, M):
+def test_decode_batches(env, fmt, M):
     torch, mmq, orc, _ = env
     dev = torch.device("cuda:0")
     N, K = 300, 4096
-    print(f"[case] iq1c decode M={M} N={N} K={K}", flush=True)
-    raw = gen.weights_iq1c(N, K, seed=M, cfg=87)
+    print(f"[case] {fmt} decode M={M} N={N} K={K}", flush=True)
+    raw = gen.weights(fmt, N, K, seed=M, cfg=87)
     x = gen.act_f32(M, K, seed=M, cfg=87, outlier_rate=1e-2)
     act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
-    out = mmq.gemm("iq1c", _pack(env, raw, N, K), act, M, N, K, "f32")
+    out = mmq.gemm(fmt, _pack(env, raw, N, K, fmt), act, M, N, K, "f32")
     torch.cuda.synchronize()
     rq, rs, _ = orc.quantize_q8_1(x)
-    assert _rel(out.cpu().numpy(), orc.gemm_f64("iq1c", raw, N, K, rq, rs, grid=gen.IQ1C_GRID)) <= GATE
+    assert _rel(out.cpu().numpy(), orc.gemm_f64(fmt, raw, N, K, rq, rs, grid=gen.IQ1C_GRID)) <= GATE
 
 
-def _moe(env, E, T, top_k, N, K, ids, seed, cfg=88):
+def _moe(env, E, T, top_k, N, K, ids, seed, cfg=88, fmt="iq1c"):
     torch, mmq, orc, _ = env
     dev = torch.device("cuda:0")
-    print(f"[case] moe iq1c E={E} T={T} top_k={top_k} N={N} K={K} seed={seed}", flush=True)
-    raw = gen.moe_weights("iq1c", E, N, K, seed=seed, cfg=cfg)
+    print(f"[case] moe {fmt} E={E} T={T} top_k={top_k} N={N} K={K} seed={seed}", flush=True)
+    raw = gen.moe_weights(fmt, E, N, K, seed=seed, cfg=cfg)
     x = gen.act_f32(T, K, seed=seed, cfg=cfg, outlier_rate=1e-3)
     act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
-    pb = mmq.packed_bytes("iq1c", N, K)
+    pb = mmq.packed_bytes(fmt, N, K)
     packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
     for e in range(E):
-        packed[e * pb:(e + 1) * pb] = _pack(env, raw[e], N, K)
+        packed[e * pb:(e + 1) * pb] = _pack(env, raw[e], N, K, fmt)
     out = torch.full((T, top_k, N), float(SENTINEL), dtype=torch.float32, device=dev)
-    mmq.gemm_id("iq1c", packed, E, act, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev),
+    mmq.gemm_id(fmt, packed, E, act, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev),
                 T, top_k, N, K, out=out)
     torch.cuda.synchronize()
     rq, rs, _ = orc.quantize_q8_1(x)
     return raw, rq, rs, out.cpu().numpy()
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T", [2, 37, 150])
-def test_moe_every_row(env, T):
+def test_moe_every_row(env, fmt, T):
     _, _, orc, _ = env
     E, top_k, N, K = 8, 3, 97, 512
     ids = gen.moe_ids(T, top_k, E, seed=T, cfg=88)
-    raw, rq, rs, got = _moe(env, E, T, top_k, N, K, ids, seed=T)
-    ref = orc.moe_f64("iq1c", raw.reshape(E * N, -1), E, N, K, rq, rs, ids, grid=gen.IQ1C_GRID)
+    raw, rq, rs, got = _moe(env, E, T, top_k, N, K, ids, seed=T, fmt=fmt)
+    ref = orc.moe_f64(fmt, raw.reshape(E * N, -1), E, N, K, rq, rs, ids, grid=gen.IQ1C_GRID)
     rel = _rel(got, ref)
     print(f"  rel err {rel:.3e}")
     assert rel <= GATE
 
 
-def test_moe_full_size_sampled(env):
+@pytest.mark.parametrize("name", ["cfg5c_moe_iq1c", "cfg5s_moe_iq1s"])
+def test_moe_full_size_sampled(env, name):
     _, _, orc, _ = env
-    c = gen.CONFIGS["cfg5c_moe_iq1c"]
+    c = gen.CONFIGS[name]
     E, T, top_k, N, K = c["E"], c["M"], c["top_k"], c["N"], c["K"]
     ids = gen.moe_ids(T, top_k, E, seed=0, cfg=c["cfg"])
-    raw, rq, rs, got = _moe(env, E, T, top_k, N, K, ids, seed=0, cfg=c["cfg"])
+    raw, rq, rs, got = _moe(env, E, T, top_k, N, K, ids, seed=0, cfg=c["cfg"], fmt=c["fmt"])
     assert np.all(np.isfinite(got))
     r = np.random.default_rng(13)
     cols = np.sort(np.concatenate([r.choice(N, 192, replace=False), [0, N - 1]]))
     worst = 0.0
     for e in r.choice(E, 10, replace=False):
         tt, jj = np.nonzero(ids == e)
-        ref = orc.gemm_f64("iq1c", raw[e], N, K, rq[tt], rs[tt], cols=cols, grid=gen.IQ1C_GRID)
+        ref = orc.gemm_f64(c["fmt"], raw[e], N, K, rq[tt], rs[tt], cols=cols, grid=gen.IQ1C_GRID)
         worst = max(worst, _rel(got[tt, jj][:, cols], ref))
     print(f"  rel err {worst:.3e}")
     assert worst <= GATE
