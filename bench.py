@@ -16,7 +16,9 @@ Timing (the pages' protocol: warm-up, then 30 samples of 100 back-to-back launch
 hipGraph replay) timed with hipEvents, median and min/max spread; P2 section 3.3):
   step time     all --steps steps are captured in one hipGraph, replayed once untimed and once
                 between two synchronisations; value = 2*M*N*K / step time. The graph keeps
-                host launch cost (and the ~8 us gap between graph launches) out of the timing.
+                host launch cost (and the ~8 us gap between graph launches) out of the timing;
+                the one launch and the final synchronisation (~0.7 ms together) are spread over
+                the default 2000 steps.
   kernel times  per kernel, a hipGraph of 100 back-to-back launches replayed 30 times, each
                 replay bracketed by HIP events on the launch stream: 30 samples of the average
                 launch duration (mean, median, min, max reported).
@@ -63,7 +65,7 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # with and scaled by the copy-kernel factor (profiles/ holds the summaries); absent (reported
 # as null) until measured for the current kernel.
 MEASURED_TRAFFIC_BYTES = {
-    "cfg2a_q4_0": 166180201,
+    "cfg2a_q4_0": 166275110,
     "cfg3a_q4_K": 98550577,
     "cfg4_w8a8": 60068906,
     "cfg5_moe_iq1t": 387556612,
@@ -271,7 +273,7 @@ def timed(kernels, n_rot, steps, warmup, samples=30, per_sample=100):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=HEADLINE, help="one of gen.CONFIGS")
     ap.add_argument("--rotate", type=int, default=-1,

@@ -201,3 +201,14 @@ def test_act_i8_layout_roundtrip(mmq):
     full, sap = mmq.act_i8_to_host(buf, M, K, padded=True)
     assert full.shape == (64, KBp * 32) and not full[M:].any() and not full[:, K:].any()
     assert not sap[M:].any()
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    # no CPU fallback: with libmmq.so absent every call raises instead of computing elsewhere
+    import block_quantized_int8_amd as mmq
+    monkeypatch.setattr(mmq, "LIB_PATH", "/nonexistent/libmmq.so")
+    monkeypatch.setattr(mmq, "_lib", None)
+    with pytest.raises(RuntimeError):
+        mmq.lib()
+    with pytest.raises(RuntimeError):
+        mmq.packed_bytes("q4_0", 32, 64)
