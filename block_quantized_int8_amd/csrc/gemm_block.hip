@@ -296,13 +296,15 @@ __device__ inline h4 as_h4(uint32_t lo) {
     return __builtin_bit_cast(h4, t);
 }
 
+// The kernel body, on LDS stage buffers buf0 / buf1 (C::BUF bytes each) and the IQ1T table
+// (512 bytes), as workgroup `bid` of `nblk`: a function so that one launch can run two tile
+// configurations (MUL_MAT_ID full and tail units, below).
 template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int MODE, bool XM>
-__global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs args) {
+__device__ __attribute__((always_inline)) inline void block_body(const BlockArgs& args, uint8_t* buf0,
+                                                                 uint8_t* buf1, uint8_t* tab, int bid,
+                                                                 int nblk) {
     using C = Cfg<FMT, WN, WM, RT, CT, is_gather(MODE)>;
     using T = typename C::T;
-    __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::BUF];
-    __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 512 : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         // workgroup b runs on XCD b % 8; unit u = 8 * (rest / ntiles_n) + b % 8 keeps all weight
         // tiles of a unit (which share its activation rows) on one XCD and spreads the live
         // units (the lowest ids) evenly over the XCDs
-        const int b = blockIdx.x, rest = b >> 3;
+        const int b = bid, rest = b >> 3;
         const int u = (rest / args.ntiles_n) * 8 + (b & 7);
         if (u >= args.uoff[args.E]) return;             // uniform: the whole CTA leaves
         int lo = 0, hi = args.E;                        // largest e with uoff[e] <= u
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
         wbase = args.w + (int64_t)e * args.w_stride;
         nt_base = (rest % args.ntiles_n) * C::TN;
     } else {
-        const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
+        const int lid = xcd_swizzle(bid, nblk);
         nt_base = (lid / args.tiles_m) * C::TN;
         mt_base = (lid % args.tiles_m) * C::TM;
     }
@@ -715,6 +717,32 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     }
 }
 
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int MODE, bool XM>
+__global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs args) {
+    using C = Cfg<FMT, WN, WM, RT, CT, is_gather(MODE)>;
+    __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 512 : 16];
+    block_body<FMT, WN, WM, RT, CT, MODE, XM>(args, buf0, buf1, tab, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// MUL_MAT_ID in one launch: workgroups [0, nfull) run the full units (CT tiles of tokens per
+// wave), the rest the tail units (TCT tiles): the tails start as soon as full-unit workgroups
+// leave, instead of after the whole full-unit launch. nfull is a multiple of 8, so both parts
+// keep the workgroup -> XCD assignment of their own grid. LDS holds the larger configuration.
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int TCT, bool XM>
+__global__ __launch_bounds__(WN * WM * 64, 2) void mmq_gather_kernel(BlockArgs full, BlockArgs tail, int nfull) {
+    using CF = Cfg<FMT, WN, WM, RT, CT, true>;
+    using CTl = Cfg<FMT, WN, WM, RT, TCT, true>;
+    constexpr int BUF = CF::BUF > CTl::BUF ? CF::BUF : CTl::BUF;
+    __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 512 : 16];
+    const int b = (int)blockIdx.x;
+    if (b < nfull) block_body<FMT, WN, WM, RT, CT, GATHER_F32, XM>(full, buf0, buf1, tab, b, nfull);
+    else block_body<FMT, WN, WM, RT, TCT, GATHER_TAIL, XM>(tail, buf0, buf1, tab, b - nfull, (int)gridDim.x - nfull);
+}
+
 // Tile configuration: 2 x 2 waves, each owning 2 weight tiles x 2 token tiles -> 128 x 128
 // CTA tiles.
 constexpr int WN_ = 2, WM_ = 2, RT_ = 2, CT_ = 2;
@@ -804,14 +832,13 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
     g.out = static_cast<float*>(out);
     g.ldo = N;
     const dim3 block(GWN_ * GWM_ * 64);
+    BlockArgs t = g;
     g.uoff = ufull;
-    hipLaunchKernelGGL((mmq_block_kernel<FMT, GWN_, GWM_, GRT_, GCT_, GATHER_F32, XM_>),
-                       dim3((unsigned)(round_up(max_full, 8) * g.ntiles_n)), block, 0, s, g);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    g.uoff = utail;
-    hipLaunchKernelGGL((mmq_block_kernel<FMT, GWN_, GWM_, GRT_, TCT_, GATHER_TAIL, XM_>),
-                       dim3((unsigned)(round_up(max_tail, 8) * g.ntiles_n)), block, 0, s, g);
+    t.uoff = utail;
+    const int nfull = (int)(round_up(max_full, 8) * g.ntiles_n);
+    const int ntail = (int)(round_up(max_tail, 8) * g.ntiles_n);
+    hipLaunchKernelGGL((mmq_gather_kernel<FMT, GWN_, GWM_, GRT_, GCT_, TCT_, XM_>), dim3((unsigned)(nfull + ntail)),
+                       block, 0, s, g, t, nfull);
     return hipGetLastError();
 }
 
@@ -829,8 +856,9 @@ bool dense_grid_ok(int64_t M, int64_t N) {      // the larger of the two dense g
     return ceil_div(N, GWN_ * GRT_ * 32) * ceil_div(M, GWM_ * DCT_ * 32) <= MAX_GRID;
 }
 
+// the one MUL_MAT_ID launch holds the full-unit grid and the tail grid (at most as many units)
 bool gather_grid_ok(int64_t max_units, int64_t N) {
-    return round_up(max_units, 8) * ceil_div(N, GWN_ * GRT_ * 32) <= MAX_GRID;
+    return 2 * round_up(max_units, 8) * ceil_div(N, GWN_ * GRT_ * 32) <= MAX_GRID;
 }
 
 hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,

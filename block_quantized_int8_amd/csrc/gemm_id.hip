@@ -8,9 +8,9 @@
 //      R = gather_tail_tokens(), one tail unit (a larger remainder is a last full unit);
 //      exclusive scans of the pair counts (pair offsets), full-unit counts and tail-unit counts
 //      (unit offsets); then scatter the pair ids into expert order.
-//   2. the gather-mode MMQ kernel, one launch for the full units (64 token slots) and one for
-//      the tails (32 slots, one token tile per wave); a workgroup per (unit, 128-row weight
-//      tile). A workgroup finds its expert by binary search
+//   2. the gather-mode MMQ kernel in one launch: a workgroup per (unit, 128-row weight tile),
+//      the full units (64 token slots) first and the tails (32 slots, one token tile per wave)
+//      after them, so tails fill the CUs the last full units leave idle. A workgroup finds its expert by binary search
 //      over the unit offsets, reads its tokens' activation rows and writes each pair's own
 //      output row.
 // No host round trip: the grids are sized for the worst case and workgroups past the actual
