@@ -68,11 +68,11 @@ MEASURED_TRAFFIC_BYTES = {
     "cfg2a_q4_0": 166275110,
     "cfg3a_q4_K": 98550577,
     "cfg4_w8a8": 60068906,
-    "cfg5_moe_iq1t": 387556612,
+    "cfg5_moe_iq1t": 388458673,
     "dec8_q4_0": 11137667,
     "dec8_q4_K": 45158633,
     "cfg6_q6_K": 475612543,
-    "cfg5c_moe_iq1c": 387268560,
+    "cfg5c_moe_iq1c": 388450164,
 }
 
 RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "iq1s": 50 / 8,
