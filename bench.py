@@ -55,7 +55,7 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9   # non-packed f32 vector lane-ops per second
-HEADLINE = "cfg2a_q4_0"
+HEADLINE = "q4_0_m2048_n4096_k4096"
 METRIC = "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MFMA peak"
 DECODE_MAX_M = 16                # mmq_gemm runs batches up to this many rows on the decode kernel
 COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at least this much
@@ -65,14 +65,14 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # with and scaled by the copy-kernel factor (profiles/ holds the summaries); absent (reported
 # as null) until measured for the current kernel.
 MEASURED_TRAFFIC_BYTES = {
-    "cfg2a_q4_0": 166275110,
-    "cfg3a_q4_K": 98802737,
-    "cfg4_w8a8": 60068906,
-    "cfg5_moe_iq1t": 388458673,
-    "dec8_q4_0": 11134760,
-    "dec8_q4_K": 45164207,
-    "cfg6_q6_K": 475612543,
-    "cfg5c_moe_iq1c": 388450164,
+    "q4_0_m2048_n4096_k4096": 166275110,
+    "q4_K_m512_n14336_k4096": 98802737,
+    "w8a8_m3072_n1536_k4096": 60068906,
+    "moe_iq1t_e64_t512_top8_n2048_k4096": 388458673,
+    "dec_q4_0_m8_n4096_k4096": 11134760,
+    "dec_q4_K_m8_n14336_k4096": 45164207,
+    "q6_K_m2048_n4096_k11008": 475612543,
+    "moe_iq1c_e64_t512_top8_n2048_k4096": 388450164,
 }
 
 RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "iq1s": 50 / 8,
@@ -432,7 +432,7 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 5 x 256 MiB device-to-device")
 
-    desc = {"cfg2a_q4_0": "q4_0 MMQ prefill: raw q4_0 weights N=4096 K=4096, q8_1 activations M=2048 "
+    desc = {"q4_0_m2048_n4096_k4096": "q4_0 MMQ prefill: raw q4_0 weights N=4096 K=4096, q8_1 activations M=2048 "
                           "(quantised in-step), f32 out"}
     rec = {
         "metric": METRIC if name == HEADLINE else f"MMQ TOPS (2MNK/s) on {name}",

@@ -316,31 +316,31 @@ def moe_ids(T: int, top_k: int, E: int, *, seed: int = 0, cfg: int = 5) -> np.nd
 
 # The five measured workloads. 'name' is used by tests and the bench.
 CONFIGS = {
-    "cfg1_q8_0": dict(cfg=1, fmt="q8_0", M=64, N=256, K=256, out="f32"),
-    "cfg2a_q4_0": dict(cfg=2, fmt="q4_0", M=2048, N=4096, K=4096, out="f32", outlier_rate=1e-3),
-    "cfg2b_q4_0": dict(cfg=2, fmt="q4_0", M=2048, N=11008, K=4096, out="f32", outlier_rate=1e-3),
-    "cfg3a_q4_K": dict(cfg=3, fmt="q4_K", M=512, N=14336, K=4096, out="f32"),
-    "cfg3b_q4_K": dict(cfg=3, fmt="q4_K", M=512, N=4096, K=14336, out="f32"),
+    "q8_0_m64_n256_k256": dict(cfg=1, fmt="q8_0", M=64, N=256, K=256, out="f32"),
+    "q4_0_m2048_n4096_k4096": dict(cfg=2, fmt="q4_0", M=2048, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "q4_0_m2048_n11008_k4096": dict(cfg=2, fmt="q4_0", M=2048, N=11008, K=4096, out="f32", outlier_rate=1e-3),
+    "q4_K_m512_n14336_k4096": dict(cfg=3, fmt="q4_K", M=512, N=14336, K=4096, out="f32"),
+    "q4_K_m512_n4096_k14336": dict(cfg=3, fmt="q4_K", M=512, N=4096, K=14336, out="f32"),
     # q6_K carries a 7B model's ffn_down (and lm_head) in q4_k_m files: the down projection
-    "cfg6_q6_K": dict(cfg=6, fmt="q6_K", M=2048, N=4096, K=11008, out="f32", outlier_rate=1e-3),
-    "cfg4_w8a8": dict(cfg=4, fmt="i8_row", M=3072, N=1536, K=4096, out="bf16"),
-    "cfg5_moe_iq1t": dict(cfg=5, fmt="iq1t", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
+    "q6_K_m2048_n4096_k11008": dict(cfg=6, fmt="q6_K", M=2048, N=4096, K=11008, out="f32", outlier_rate=1e-3),
+    "w8a8_m3072_n1536_k4096": dict(cfg=4, fmt="i8_row", M=3072, N=1536, K=4096, out="bf16"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": dict(cfg=5, fmt="iq1t", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
     # the same MoE with the IQ1_M codebook form of the weights (1.75 bits per value)
-    "cfg5c_moe_iq1c": dict(cfg=5, fmt="iq1c", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": dict(cfg=5, fmt="iq1c", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
     # and with the IQ1_S codebook form (1.5625 bits per value)
-    "cfg5s_moe_iq1s": dict(cfg=5, fmt="iq1s", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
+    "moe_iq1s_e64_t512_top8_n2048_k4096": dict(cfg=5, fmt="iq1s", M=512, N=2048, K=4096, out="f32", E=64, top_k=8),
     # decode batches (a few tokens) on the same weight shapes: the small-M path
-    "dec1_q4_0": dict(cfg=2, fmt="q4_0", M=1, N=4096, K=4096, out="f32", outlier_rate=1e-3),
-    "dec8_q4_0": dict(cfg=2, fmt="q4_0", M=8, N=4096, K=4096, out="f32", outlier_rate=1e-3),
-    "dec16_q4_0": dict(cfg=2, fmt="q4_0", M=16, N=4096, K=4096, out="f32", outlier_rate=1e-3),
-    "dec8_q4_0_ffn": dict(cfg=2, fmt="q4_0", M=8, N=11008, K=4096, out="f32", outlier_rate=1e-3),
-    "dec8_q8_0": dict(cfg=1, fmt="q8_0", M=8, N=4096, K=4096, out="f32"),
-    "dec8_q4_K": dict(cfg=3, fmt="q4_K", M=8, N=14336, K=4096, out="f32"),
-    "dec8_q4_K_down": dict(cfg=3, fmt="q4_K", M=8, N=4096, K=14336, out="f32"),
-    "dec8_iq1t": dict(cfg=5, fmt="iq1t", M=8, N=2048, K=4096, out="f32"),
-    "dec8_iq1c": dict(cfg=5, fmt="iq1c", M=8, N=2048, K=4096, out="f32"),
-    "dec8_q6_K": dict(cfg=6, fmt="q6_K", M=8, N=4096, K=11008, out="f32"),
-    "dec8_w8a8": dict(cfg=4, fmt="i8_row", M=8, N=1536, K=4096, out="bf16"),
-    "dec1_moe_iq1t": dict(cfg=5, fmt="iq1t", M=1, N=2048, K=4096, out="f32", E=64, top_k=8),
-    "dec4_moe_iq1t": dict(cfg=5, fmt="iq1t", M=4, N=2048, K=4096, out="f32", E=64, top_k=8),
+    "dec_q4_0_m1_n4096_k4096": dict(cfg=2, fmt="q4_0", M=1, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec_q4_0_m8_n4096_k4096": dict(cfg=2, fmt="q4_0", M=8, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec_q4_0_m16_n4096_k4096": dict(cfg=2, fmt="q4_0", M=16, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec_q4_0_m8_n11008_k4096": dict(cfg=2, fmt="q4_0", M=8, N=11008, K=4096, out="f32", outlier_rate=1e-3),
+    "dec_q8_0_m8_n4096_k4096": dict(cfg=1, fmt="q8_0", M=8, N=4096, K=4096, out="f32"),
+    "dec_q4_K_m8_n14336_k4096": dict(cfg=3, fmt="q4_K", M=8, N=14336, K=4096, out="f32"),
+    "dec_q4_K_m8_n4096_k14336": dict(cfg=3, fmt="q4_K", M=8, N=4096, K=14336, out="f32"),
+    "dec_iq1t_m8_n2048_k4096": dict(cfg=5, fmt="iq1t", M=8, N=2048, K=4096, out="f32"),
+    "dec_iq1c_m8_n2048_k4096": dict(cfg=5, fmt="iq1c", M=8, N=2048, K=4096, out="f32"),
+    "dec_q6_K_m8_n4096_k11008": dict(cfg=6, fmt="q6_K", M=8, N=4096, K=11008, out="f32"),
+    "dec_w8a8_m8_n1536_k4096": dict(cfg=4, fmt="i8_row", M=8, N=1536, K=4096, out="bf16"),
+    "dec_moe_iq1t_e64_t1_top8_n2048_k4096": dict(cfg=5, fmt="iq1t", M=1, N=2048, K=4096, out="f32", E=64, top_k=8),
+    "dec_moe_iq1t_e64_t4_top8_n2048_k4096": dict(cfg=5, fmt="iq1t", M=4, N=2048, K=4096, out="f32", E=64, top_k=8),
 }

@@ -133,8 +133,8 @@ def test_decode_w8a8_bit_exact(env, M, N, K):
     assert np.array_equal(got, ref_bf)
 
 
-@pytest.mark.parametrize("name", ["dec1_q4_0", "dec8_q4_0", "dec16_q4_0", "dec8_q4_0_ffn", "dec8_q8_0",
-                                  "dec8_q4_K", "dec8_q4_K_down", "dec8_iq1t"])
+@pytest.mark.parametrize("name", ["dec_q4_0_m1_n4096_k4096", "dec_q4_0_m8_n4096_k4096", "dec_q4_0_m16_n4096_k4096", "dec_q4_0_m8_n11008_k4096", "dec_q8_0_m8_n4096_k4096",
+                                  "dec_q4_K_m8_n14336_k4096", "dec_q4_K_m8_n4096_k14336", "dec_iq1t_m8_n2048_k4096"])
 def test_decode_full_size(env, name):
     # the decode workloads in the bench's launch configuration: every token row in full
     # against the f64 definition on 512 sampled weight rows (plus the first and last)
@@ -160,12 +160,12 @@ def test_decode_full_size(env, name):
 
 def test_decode_w8a8_full_size(env):
     torch, mmq, orc = env
-    c = gen.CONFIGS["dec8_w8a8"]
+    c = gen.CONFIGS["dec_w8a8_m8_n1536_k4096"]
     M, N, K = c["M"], c["N"], c["K"]
     dev = torch.device("cuda:0")
     a, sa = gen.i8_rows(M, K, seed=0, cfg=c["cfg"], tensor=gen.T_ACT)
     w, sw = gen.i8_rows(N, K, seed=0, cfg=c["cfg"], tensor=gen.T_WEIGHT)
-    print(f"[case] dec8_w8a8 M={M} N={N} K={K}", flush=True)
+    print(f"[case] dec_w8a8_m8_n1536_k4096 M={M} N={N} K={K}", flush=True)
     act = torch.from_numpy(mmq.act_i8_pack_host(a, sa)).to(dev)
     packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
                                 row_scale=torch.from_numpy(sw).to(dev))

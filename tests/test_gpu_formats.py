@@ -89,7 +89,7 @@ def test_extreme_weights(env, fmt):
     assert _rel(out.cpu().numpy(), orc.gemm_f64(fmt, raw, N, K, rq, rs)) <= GATE
 
 
-@pytest.mark.parametrize("name", ["cfg3a_q4_K", "cfg3b_q4_K"])
+@pytest.mark.parametrize("name", ["q4_K_m512_n14336_k4096", "q4_K_m512_n4096_k14336"])
 def test_q4_K_full_size_sampled(env, name):
     torch, mmq, orc = env
     c = gen.CONFIGS[name]

@@ -178,7 +178,7 @@ def test_moe_every_row(env, fmt, T):
     assert rel <= GATE
 
 
-@pytest.mark.parametrize("name", ["cfg5c_moe_iq1c", "cfg5s_moe_iq1s"])
+@pytest.mark.parametrize("name", ["moe_iq1c_e64_t512_top8_n2048_k4096", "moe_iq1s_e64_t512_top8_n2048_k4096"])
 def test_moe_full_size_sampled(env, name):
     _, _, orc, _ = env
     c = gen.CONFIGS[name]

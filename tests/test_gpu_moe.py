@@ -142,9 +142,9 @@ def test_moe_matches_dense_per_expert(env):
 
 def test_moe_full_size_sampled(env):
     torch, mmq, orc = env
-    c = gen.CONFIGS["cfg5_moe_iq1t"]
+    c = gen.CONFIGS["moe_iq1t_e64_t512_top8_n2048_k4096"]
     E, T, top_k, N, K = c["E"], c["M"], c["top_k"], c["N"], c["K"]
-    print(f"[case] cfg5_moe_iq1t E={E} T={T} top_k={top_k} N={N} K={K}", flush=True)
+    print(f"[case] moe_iq1t_e64_t512_top8_n2048_k4096 E={E} T={T} top_k={top_k} N={N} K={K}", flush=True)
     dev = torch.device("cuda:0")
     raw = gen.moe_weights("iq1t", E, N, K, seed=0, cfg=c["cfg"])
     x = gen.act_f32(T, K, seed=0, cfg=c["cfg"])

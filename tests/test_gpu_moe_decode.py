@@ -123,7 +123,7 @@ def test_moe_decode_full_shape_sampled(env, T):
     # the MoE workload's expert shape (64 experts x IQ1T 2048 x 4096, top-8) at decode batches;
     # every pair row in full against the f64 definition on 256 sampled columns
     torch, mmq, orc = env
-    c = gen.CONFIGS["cfg5_moe_iq1t"]
+    c = gen.CONFIGS["moe_iq1t_e64_t512_top8_n2048_k4096"]
     E, top_k, N, K = c["E"], c["top_k"], c["N"], c["K"]
     ids = gen.moe_ids(T, top_k, E, seed=T, cfg=c["cfg"])
     raw, rq, rs, _, _, got = _case(env, "iq1t", E, T, top_k, N, K, ids, seed=T, cfg=c["cfg"])

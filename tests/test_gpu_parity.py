@@ -212,7 +212,7 @@ def test_w8a8_full_size_sampled(env):
 @pytest.mark.parametrize("N", [4096, 11008])
 def test_q4_0_full_size_sampled(env, N):
     torch, mmq, orc = env
-    cfg = gen.CONFIGS["cfg2a_q4_0"]
+    cfg = gen.CONFIGS["q4_0_m2048_n4096_k4096"]
     M, K = cfg["M"], cfg["K"]
     raw, x, act, packed, out = _run(env, "q4_0", M, N, K, seed=0, outlier=cfg["outlier_rate"])
     xq, xs, xsum = mmq.act_to_host(act.cpu().numpy(), M, K)

@@ -185,9 +185,9 @@ def test_moe_decode(env, T):
 
 
 def test_ffn_down_full_size_sampled(env):
-    c = gen.CONFIGS["cfg6_q6_K"]
+    c = gen.CONFIGS["q6_K_m2048_n4096_k11008"]
     M, N, K = c["M"], c["N"], c["K"]
-    print(f"[case] cfg6_q6_K M={M} N={N} K={K}", flush=True)
+    print(f"[case] q6_K_m2048_n4096_k11008 M={M} N={N} K={K}", flush=True)
     _, _, orc = env
     raw = gen.weights_q6_K(N, K, seed=0, cfg=c["cfg"])
     x = gen.act_f32(M, K, seed=0, cfg=c["cfg"], outlier_rate=c["outlier_rate"])
