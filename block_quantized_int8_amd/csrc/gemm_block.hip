@@ -463,10 +463,26 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         v4i b[CT];
         uint32_t wsd[RT], wsd2[RT], xs[CT];
     };
+    // The f16 scale MFMA takes (scale, 0) register pairs. In the dense 128 x 128 kernels the
+    // operand buffers live for the whole K loop and only the scale halves are rewritten, so no
+    // step spends a move on the zeros (q4_0 N = 11008: -2%). The other kernels pair each scale
+    // at its MFMA: the gather and q6_K kernels need every register they can keep (the IQ1T
+    // gather kernel holds three waves per SIMD only up to 168), and the one-tile-per-wave
+    // kernels measured slower with carried pairs.
+    constexpr bool CARRY = !T::DUAL && !is_gather(MODE) && RT * CT >= 4;
+    using SOp = std::conditional_t<CARRY, v2i, uint32_t>;
     struct Ops {
         v4i a[RT][T::NMF];
         v4i b[CT];
-        uint32_t ws[RT], ws2[RT], xs[CT];
+        SOp ws[RT], ws2[RT], xs[CT];
+    };
+    auto set_lo = [](SOp& p, uint32_t v) __attribute__((always_inline)) {
+        if constexpr (CARRY) p.x = (int)v;
+        else p = v;
+    };
+    auto pair = [](const SOp& p) __attribute__((always_inline)) -> h4 {
+        if constexpr (CARRY) return __builtin_bit_cast(h4, p);
+        else return as_h4(p);
     };
     auto fetch = [&](const uint8_t* cur, int kb, Raw& R) __attribute__((always_inline)) {
 #pragma unroll
@@ -491,13 +507,13 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             T::unpack(R.w[rt], o.a[rt], hmask);
-            o.ws[rt] = T::scale_op(R.wsd[rt]);
-            if constexpr (T::DUAL) o.ws2[rt] = T::scale_op(R.wsd2[rt]);
+            set_lo(o.ws[rt], T::scale_op(R.wsd[rt]));
+            if constexpr (T::DUAL) set_lo(o.ws2[rt], T::scale_op(R.wsd2[rt]));
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             o.b[ct] = R.b[ct];
-            o.xs[ct] = R.xs[ct];
+            set_lo(o.xs[ct], R.xs[ct]);
         }
     };
     auto load_ops = [&](const uint8_t* cur, int kb, Ops& o) __attribute__((always_inline)) {
@@ -518,7 +534,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     };
     auto mfma_scale = [&](const Ops& o, int t) __attribute__((always_inline)) -> v16f {
         const int tt = t / NH, hf = t % NH, rt = tt / CT, ct = tt % CT;
-        return __builtin_amdgcn_mfma_f32_32x32x8f16(as_h4(hf ? o.ws2[rt] : o.ws[rt]), as_h4(o.xs[ct]), zf, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(pair(hf ? o.ws2[rt] : o.ws[rt]), pair(o.xs[ct]), zf, 0, 0, 0);
     };
     // The empty asm after a tile's last FMA pins its accumulator: FMAs are pure, and left alone
     // the compiler sinks a whole stage of them below its matrix-core work, which then has to
@@ -589,8 +605,21 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     // `nxt` (if not null) receives the DMA of the following stage: its chunks are issued a few
     // per step (one per step when there are enough steps) over the first steps, so the
     // vector-memory issue never holds a wave for long.
+    // operand buffers: for the whole K loop when the scale pairs are carried (their zero halves
+    // set once), else per stage
+    Ops op_keep[2];
+    if constexpr (CARRY) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) op_keep[i].ws[rt] = op_keep[i].ws2[rt] = SOp{};
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) op_keep[i].xs[ct] = SOp{};
+        }
+    }
     auto run_stage = [&](const uint8_t* cur, int s, uint8_t* nxt) __attribute__((always_inline)) {
-        Ops op[2];
+        Ops op_own[2];
+        Ops (&op)[2] = *(CARRY ? &op_keep : &op_own);
         Raw raw;
         load_ops(cur, 0, op[0]);
         v16i Dc;
