@@ -65,8 +65,8 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # with and scaled by the copy-kernel factor (profiles/ holds the summaries); absent (reported
 # as null) until measured for the current kernel.
 MEASURED_TRAFFIC_BYTES = {
-    "q4_0_m2048_n4096_k4096": 166275110,
-    "q4_K_m512_n14336_k4096": 98802737,
+    "q4_0_m2048_n4096_k4096": 170662206,
+    "q4_K_m512_n14336_k4096": 99522320,
     "w8a8_m3072_n1536_k4096": 60068906,
     "moe_iq1t_e64_t512_top8_n2048_k4096": 388458673,
     "dec_q4_0_m8_n4096_k4096": 11134760,
