@@ -74,6 +74,8 @@ def lib():
         L.orc_partials16.argtypes = [ctypes.c_int, P, I, I, P, P, I, P]
         L.orc_gemm_rows.argtypes = [ctypes.c_int, P, I, I, P, P, P, P, I, I, P, I]
         L.orc_gemm_rows.restype = ctypes.c_int
+        L.orc_gemm_abs_rows.argtypes = [ctypes.c_int, P, I, I, P, P, P, P, I, I, P]
+        L.orc_gemm_abs_rows.restype = ctypes.c_int
         L.orc_gemm.argtypes = [ctypes.c_int, P, I, I, P, P, P, P, I, P]
         L.orc_gemm.restype = ctypes.c_int
         L.orc_gemm_w8a8.argtypes = [P, P, I, P, P, I, I, P, P, I, I]
@@ -218,6 +220,25 @@ def gemm_c(fmt: str, raw: np.ndarray, N: int, K: int, xq, xs, xsum, rows=None, g
     out = np.empty((m1 - m0, N), np.float32)
     rc = lib().orc_gemm_rows(FMT_ID[fmt], _p(raw), N, K, None if g is None else _p(g), _p(xq), _p(xs),
                              _p(xsum), m0, m1, _p(out), N)
+    if rc != 0:
+        raise ValueError("invalid iq1c grid code (3)")
+    return out
+
+
+def gemm_abs(fmt: str, raw: np.ndarray, N: int, K: int, xq, xs, xsum, rows=None, grid=None) -> np.ndarray:
+    """f64 [M, N]: the sum of the magnitudes of the per-block (per-half) terms the contraction
+    adds for each output, sum_b sum_h |xs*wd_h*P16_h| + |xs*wm*xsum|: the scale of the rounding
+    error of any evaluation that adds those terms in f32."""
+    raw = _c(raw, np.uint8)
+    xq = _c(xq, np.int8)
+    xs = _c(xs, np.float32)
+    xsum = _c(xsum, np.int32)
+    g = _grid_arg(fmt, grid)
+    M = xq.shape[0]
+    m0, m1 = (0, M) if rows is None else rows
+    out = np.empty((m1 - m0, N), np.float64)
+    rc = lib().orc_gemm_abs_rows(FMT_ID[fmt], _p(raw), N, K, None if g is None else _p(g), _p(xq), _p(xs),
+                                 _p(xsum), m0, m1, _p(out))
     if rc != 0:
         raise ValueError("invalid iq1c grid code (3)")
     return out

@@ -39,6 +39,7 @@
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -110,37 +111,54 @@ static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); 
 
 /* ------------------------------------------------------ activation quantiser */
 
-/* q8_1: for every row m and 32-value block b of x (row stride ldx floats):
- *   amax = max |x|;  d = amax/127 (f32);  di = d != 0 ? 1/d : 0;
- *   q_i = clamp(rint(x_i*di), -128, 127);  xs = f32(f16_rne(d));  xsum = sum q_i.
- * Outputs are row-major: xq [M][K], xs [M][K/32], xsum [M][K/32].            */
+/* q8_1 (the activation format of the contraction).
+ *
+ * Definition (minfer R1 section 3.2 gives it as the parity test's CPU reference; section 2.2
+ * adds the block sum). For a block B of 32 values:
+ *     d(B)   = max_{i in B} |x_i| / 127                       (one f32 division)
+ *     inv(B) = 0 if d(B) = 0, else 1/d(B) in f32, taken as the largest finite f32 when it
+ *              overflows (d(B) below 2^-128): the pages leave that case open, and this keeps
+ *              0 * inv = 0 and |x * inv| <= 127 (1 + 2^-23) for every x of the block
+ *     q_i    = the integer nearest x_i * inv(B) (ties to even), limited to [-128, 127]
+ *     xs(B)  = d(B) rounded to f16 (nearest even), carried as f32;  xsum(B) = sum of the q_i.
+ * Computed below in three passes over each row: the block scales, then every value, then the
+ * per-block sums. Outputs are row-major: xq [M][K], xs [M][K/32], xsum [M][K/32]. */
+static float q8_block_amax(const float* v) {
+    float a = 0.0f;
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+    return a;
+}
+
+static float q8_inverse(float d) {
+    if (d == 0.0f) return 0.0f;
+    const float r = 1.0f / d;
+    return isinf(r) ? FLT_MAX : r;
+}
+
+static int8_t q8_value(float x, float inv) {
+    const float t = nearbyintf(x * inv);            /* default rounding: ties to even */
+    return (int8_t)(t > 127.0f ? 127 : t < -128.0f ? -128 : (int)t);
+}
+
 void orc_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ldx,
                        int8_t* xq, float* xs, int32_t* xsum) {
     const int64_t KB = K / 32;
-#pragma omp parallel for schedule(static)
-    for (int64_t m = 0; m < M; ++m) {
-        for (int64_t b = 0; b < KB; ++b) {
-            const float* blk = x + m * ldx + b * 32;
-            float amax = 0.0f;
-            for (int i = 0; i < 32; ++i) {
-                float a = fabsf(blk[i]);
-                if (a > amax) amax = a;
+#pragma omp parallel
+    {
+        float* dk = (float*)malloc(sizeof(float) * (size_t)(KB > 0 ? KB : 1));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            const float* row = x + m * ldx;
+            for (int64_t b = 0; b < KB; ++b) dk[b] = q8_block_amax(row + 32 * b) / 127.0f;
+            for (int64_t k = 0; k < K; ++k) xq[m * K + k] = q8_value(row[k], q8_inverse(dk[k / 32]));
+            for (int64_t b = 0; b < KB; ++b) {
+                int32_t total = 0;
+                for (int64_t k = 32 * b; k < 32 * b + 32; ++k) total += xq[m * K + k];
+                xsum[m * KB + b] = total;
+                xs[m * KB + b] = orc_half_to_float(orc_float_to_half(dk[b]));
             }
-            float d = amax / 127.0f;
-            float di = (d != 0.0f) ? 1.0f / d : 0.0f;
-            int32_t s = 0;
-            for (int i = 0; i < 32; ++i) {
-                float v = blk[i] * di;
-                float r = rintf(v);
-                if (r < -128.0f) r = -128.0f;
-                if (r > 127.0f) r = 127.0f;
-                int q = (int)r;
-                xq[m * K + b * 32 + i] = (int8_t)q;
-                s += q;
-            }
-            xs[m * KB + b] = orc_half_to_float(orc_float_to_half(d));
-            xsum[m * KB + b] = s;
         }
+        free(dk);
     }
 }
 
@@ -157,13 +175,8 @@ void orc_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_t ldx,
             if (v > amax) amax = v;
         }
         float d = amax / 127.0f;
-        float di = (d != 0.0f) ? 1.0f / d : 0.0f;
-        for (int64_t k = 0; k < K; ++k) {
-            float r = rintf(row[k] * di);
-            if (r < -128.0f) r = -128.0f;
-            if (r > 127.0f) r = 127.0f;
-            a[m * K + k] = (int8_t)(int)r;
-        }
+        float inv = q8_inverse(d);
+        for (int64_t k = 0; k < K; ++k) a[m * K + k] = q8_value(row[k], inv);
         sa[m] = d;
     }
 }
@@ -450,6 +463,44 @@ int orc_gemm_rows(int fmt, const uint8_t* raw, int64_t N, int64_t K, const uint1
         }
     }
     free(wq_all); free(wd_all); free(wm_all); free(mult_all);
+    return badgrid ? -2 : 0;
+}
+
+/* The magnitude of what the contraction adds up, per output: abs[m*N + n] = sum over blocks
+ * b and halves h of |xs[m,b] * wd_h * P16_h| + |xs[m,b] * wm_b * xsum[m,b]| (in double).
+ * A floating-point evaluation that adds the per-block terms one at a time in f32 makes an
+ * error of at most (number of f32 additions) * 2^-24 * abs (each rounding is relative to a
+ * partial sum, and every partial sum is bounded by abs), so this is the yardstick of the
+ * tests' rounding bound for f32 outputs. Rows m0 <= m < m1. Returns -2 on an invalid grid
+ * code, else 0. */
+int orc_gemm_abs_rows(int fmt, const uint8_t* raw, int64_t N, int64_t K, const uint16_t* grid,
+                      const int8_t* xq, const float* xs, const int32_t* xsum,
+                      int64_t m0, int64_t m1, double* absout) {
+    const int64_t KB = K / 32, rb = raw_row_bytes(fmt, K);
+    int badgrid = 0;
+#pragma omp parallel
+    {
+        int16_t* wq = (int16_t*)malloc(sizeof(int16_t) * K);
+        float* wd = (float*)malloc(sizeof(float) * (K / 16));
+        float* wm = (float*)malloc(sizeof(float) * KB);
+        int16_t* mult = (int16_t*)malloc(sizeof(int16_t) * (K / 16));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            if (decode_row(fmt, raw + n * rb, K, grid, wq, wd, wm, mult) != 0) badgrid = 1;
+            for (int64_t m = m0; m < m1; ++m) {
+                double a = 0.0;
+                for (int64_t h = 0; h < K / 16; ++h) {
+                    int32_t s16 = 0;
+                    for (int i = 0; i < 16; ++i) s16 += (int32_t)xq[m * K + h * 16 + i] * (int32_t)wq[h * 16 + i];
+                    a += fabs((double)xs[m * KB + h / 2] * (double)wd[h] * (double)s16);
+                }
+                for (int64_t b = 0; b < KB; ++b)
+                    a += fabs((double)xs[m * KB + b] * (double)wm[b] * (double)xsum[m * KB + b]);
+                absout[(m - m0) * N + n] = a;
+            }
+        }
+        free(wq); free(wd); free(wm); free(mult);
+    }
     return badgrid ? -2 : 0;
 }
 

@@ -170,3 +170,26 @@ def test_i8_token_scale_not_rounded_to_half(orc):
     assert sa[0] != np.float32(np.float16(np.float32(1.0) / np.float32(127)))
     xq, xs, _ = orc.quantize_q8_1(x)
     assert xs[0, 0] == np.float32(np.float16(np.float32(1.0) / np.float32(127)))
+
+
+def test_q8_1_tiny_blocks_closed_forms(orc):
+    """Blocks whose amax is so small that d = amax/127 is subnormal, and 1/d may overflow f32.
+    The pages leave that open; the reading taken (mmq.h) is di = FLT_MAX where 1/d overflows,
+    so zeros stay 0 and no value leaves [-127, 127]. Hand-derived values:
+      amax = 1e-37: d ~ 7.9e-40, 1/d overflows, 1e-37 * 3.4028235e38 = 34.03 -> 34;
+      amax = 1e-36: d ~ 7.9e-39 (subnormal), 1/d ~ 1.27e38 is finite -> the peak maps to 127;
+      amax = 1e-39: 1/d overflows, 1e-39 * 3.4028235e38 = 0.034 -> 0.
+    In every case f16(d) = 0, so the stored scale is 0."""
+    x = np.zeros((1, 128), np.float32)
+    x[0, 0], x[0, 5] = 1e-37, -1e-37
+    x[0, 32 + 9] = 1e-36
+    x[0, 64 + 31] = -1e-39
+    x[0, 96 + 3], x[0, 96 + 4] = 1e-37, 5e-38          # 5e-38 * FLT_MAX = 17.01 -> 17
+    xq, xs, xsum = orc.quantize_q8_1(x)
+    expect = np.zeros(128, np.int8)
+    expect[0], expect[5] = 34, -34
+    expect[32 + 9] = 127
+    expect[96 + 3], expect[96 + 4] = 34, 17
+    assert np.array_equal(xq[0], expect)
+    assert np.all(xs == 0)
+    assert xsum[0].tolist() == [0, 127, 0, 51]
