@@ -6,7 +6,18 @@ using namespace mmq;
 
 namespace {
 
-constexpr int64_t MAX_DIM = int64_t(1) << 24;    // keeps every index of the kernels in int32
+// Size limits of the ABI (mmq.h states them next to each call):
+//  - M, N (and T * top_k) at most 2^24 and K at most 2^23: row, column and block counts stay
+//    in int32 inside the kernels, and a 128-row tile's fragments of all K blocks stay below
+//    2 GiB, so the dense launches can always be split into pieces whose regions the kernels'
+//    32-bit byte offsets address;
+//  - MMQ_I8_ROW: K < 2^17, so the int32 accumulator over all of K cannot overflow
+//    (|a * w| <= 2^14 per term);
+//  - the debug partials output holds at most 2^31 int32 values.
+constexpr int64_t MAX_DIM = int64_t(1) << 24;
+constexpr int64_t MAX_K = int64_t(1) << 23;
+constexpr int64_t MAX_K_I8_ROW = int64_t(1) << 17;
+constexpr int64_t MAX_PARTIALS = int64_t(1) << 31;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -26,7 +37,14 @@ int64_t partials_per_row(mmq_wtype t, int64_t K) { return t == MMQ_Q6_K ? K / 16
 bool needs_aux(mmq_wtype t) { return t == MMQ_I8_ROW || t == MMQ_IQ1C || t == MMQ_IQ1S; }
 
 bool sizes_ok(int64_t M, int64_t N, int64_t K) {
-    return M >= 1 && N >= 1 && K >= 32 && M <= MAX_DIM && N <= MAX_DIM && K <= MAX_DIM;
+    return M >= 1 && N >= 1 && K >= 32 && M <= MAX_DIM && N <= MAX_DIM && K <= MAX_K;
+}
+
+// a * b * c <= lim for non-negative operands, without overflowing int64
+bool product_le(int64_t a, int64_t b, int64_t c, int64_t lim) {
+    if (a == 0 || b == 0 || c == 0) return true;
+    if (a > lim / b) return false;
+    return a * b <= lim / c;
 }
 
 mmq_status from_hip(hipError_t e) {
@@ -109,21 +127,21 @@ mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
     if (o == MMQ_OUT_I32_PARTIALS && ldo != N) return MMQ_EINVAL;
     if (t == MMQ_I8_ROW) {
         if (o == MMQ_OUT_F32) return MMQ_EUNSUPPORTED;
+        if (K >= MAX_K_I8_ROW) return MMQ_EINVAL;
     } else {
         if (o == MMQ_OUT_BF16) return MMQ_EUNSUPPORTED;
-        if (o == MMQ_OUT_I32_PARTIALS && M * N * partials_per_row(t, K) > (int64_t(1) << 31)) return MMQ_EINVAL;
     }
+    if (o == MMQ_OUT_I32_PARTIALS &&
+        !product_le(M, N, t == MMQ_I8_ROW ? 1 : partials_per_row(t, K), MAX_PARTIALS))
+        return MMQ_EINVAL;
     if (!aligned16(packed) || !aligned16(act) || !aligned16(out)) return MMQ_EALIGN;
     t = kernel_format(t);
     // decode batches go to the split-K matrix-vector kernel; the debug partials stay on the
     // prefill kernels
     if (o != MMQ_OUT_I32_PARTIALS && M <= mmvq_max_tokens())
         return from_hip(launch_mmvq(t, packed, act, M, N, K, out, ldo, as_stream(stream)));
-    if (t == MMQ_I8_ROW) {
-        if (!w8a8_grid_ok(M, N)) return MMQ_EINVAL;
+    if (t == MMQ_I8_ROW)
         return from_hip(launch_w8a8_gemm(packed, act, M, N, K, o, out, ldo, as_stream(stream)));
-    }
-    if (!dense_grid_ok(M, N)) return MMQ_EINVAL;
     return from_hip(launch_block_gemm(t, packed, act, M, N, K, o, out, ldo, as_stream(stream)));
 }
 
@@ -144,8 +162,11 @@ mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* a
     if (!aligned16(packed) || !aligned16(act) || !aligned16(ids) || !aligned16(out) ||
         !aligned16(workspace))
         return MMQ_EALIGN;
-    if (!gather_grid_ok(gemm_id_max_units(E, T * top_k), N)) return MMQ_EINVAL;
     t = kernel_format(t);
+    if (!mmvq_id_ok(t, T, top_k, K)) {          // the prefill gather path (decode batches: the
+        if (!gather_grid_ok(gemm_id_max_units(E, T * top_k), N) || !gather_regions_ok(t, T, N, K))
+            return MMQ_EINVAL;                  // small-batch kernel, 64-bit addressing)
+    }
     return from_hip(launch_gemm_id(t, packed, E, act, ids, T, top_k, N, K, out, workspace, ws_bytes,
                                    as_stream(stream)));
 }

@@ -46,6 +46,7 @@
 // Token rows are fetched per lane, which is also how MUL_MAT_ID gathers its rows: in gather
 // mode every token slot of a tile reads its own activation row and writes its own output row
 // (see gemm_id.hip).
+#include <algorithm>
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -270,6 +271,7 @@ struct BlockArgs {
     float* out;
     int64_t ldo;
     int32_t* partials;
+    int64_t pld;                // partials: elements between consecutive rows m (the full N)
     // gather mode (MUL_MAT_ID)
     const int32_t* offs;        // [E+1] first pair of each expert in `pairs`
     const int32_t* uoff;        // [E+1] first unit of each expert; uoff[E] = live units
@@ -574,7 +576,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
             for (int r = 0; r < 16; ++r) {
                 const int n = (nt_base + wn * RT + rt) * 32 + acc_row(lane, r);
                 if (n < args.N)
-                    args.partials[((int64_t)m * args.N + n) * (NH * args.KB) + NH * kbg + hf] =
+                    args.partials[((int64_t)m * args.pld + n) * (NH * args.KB) + NH * kbg + hf] =
                         (D[r] - MAGIC_I) >> T::SHIFT;
             }
         }
@@ -834,14 +836,67 @@ hipError_t launch_dense_cfg(BlockArgs g, int64_t M, int64_t N, mmq_otype o, void
 // token slots (4 x 1 waves, one tile each) and four times the workgroups.
 constexpr int64_t DENSE_FILL = 448;
 
+// The kernel keeps 32-bit byte offsets from each operand region's base (the DMA plan) and its
+// grid stays below MAX_GRID workgroups, so a problem whose weight or activation regions reach
+// 2 GiB (e.g. a 262144 x 8192 q8_0 vocabulary matrix) runs as several launches over ranges of
+// weight tiles and token tiles: each launch sees its own slice of the tile-major regions.
+constexpr int64_t MAX_REGION = int64_t(1) << 31;
+constexpr int64_t MAX_GRID_ = (int64_t(1) << 24) - 1;
+
+template <mmq_wtype FMT, int WN, int WM, int RT, int CT>
+hipError_t launch_dense_split(const BlockArgs& g0, int64_t M, int64_t N, mmq_otype o, void* out,
+                              int64_t ldo, int64_t scale_off, int64_t min_off, hipStream_t s) {
+    constexpr int TN = WN * RT, TM = WM * CT;                // 32-row tiles per workgroup
+    // the largest per-tile region: a tile's fragments of every block (q8_0, q6_K and the
+    // activations: 1 KB per block)
+    const int64_t tile_bytes = (int64_t)g0.KBp * 1024;
+    const int64_t ntile_cap = std::max<int64_t>(TN, (MAX_REGION - 1) / tile_bytes / TN * TN);
+    const int64_t mtile_cap = std::max<int64_t>(TM, (MAX_REGION - 1) / tile_bytes / TM * TM);
+    const int64_t NT = g0.NT, MT = g0.MT;
+    const int64_t nstep = std::min(ntile_cap, NT);
+    const int64_t mstep = std::min(mtile_cap, std::max<int64_t>(TM, MAX_GRID_ / ceil_div(nstep, TN) / TM * TM));
+    const int64_t FB = BT<FMT>::FB;
+    for (int64_t mt0 = 0; mt0 < MT; mt0 += mstep) {
+        for (int64_t nt0 = 0; nt0 < NT; nt0 += nstep) {
+            BlockArgs g = g0;
+            const int64_t NTc = std::min(nstep, NT - nt0), MTc = std::min(mstep, MT - mt0);
+            const int64_t Nc = std::min(NTc * 32, N - nt0 * 32), Mc = std::min(MTc * 32, M - mt0 * 32);
+            const int64_t wshift = nt0 * g0.KBp * FB;             // fragments of the skipped tiles
+            const int64_t sshift = nt0 * g0.KBp * 128;            // their scale dwords
+            g.w = g0.w + wshift;
+            g.w_scale_off = scale_off + sshift - wshift;
+            g.w_min_off = min_off + sshift - wshift;
+            g.xq = g0.xq + mt0 * g0.KBp * 1024;
+            g.xs2 = g0.xs2 + mt0 * g0.KBp * 32;
+            g.xsx = g0.xsx + mt0 * g0.KBp * 32;
+            g.M = (int)Mc;
+            g.N = (int)Nc;
+            g.NT = (int)NTc;
+            g.MT = (int)MTc;
+            g.pld = N;
+            void* o_sub;
+            if (o == MMQ_OUT_I32_PARTIALS) {
+                const int64_t per = (FMT == MMQ_Q6_K ? 2 : 1) * (int64_t)g0.KB;
+                o_sub = static_cast<int32_t*>(out) + (mt0 * 32 * N + nt0 * 32) * per;
+            } else {
+                o_sub = static_cast<float*>(out) + mt0 * 32 * ldo + nt0 * 32;
+            }
+            const hipError_t e = launch_dense_cfg<FMT, WN, WM, RT, CT>(g, Mc, Nc, o, o_sub, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
 template <mmq_wtype FMT>
 hipError_t launch_dense(const void* packed, const void* act, int64_t M, int64_t N, int64_t K,
                         mmq_otype o, void* out, int64_t ldo, hipStream_t s) {
     BlockArgs g = dense_args<FMT>(packed, act, M, N, K);
     g.ldo = ldo;
+    const int64_t scale_off = g.w_scale_off, min_off = g.w_min_off;
     if (ceil_div(N, WN_ * RT_ * 32) * ceil_div(M, WM_ * CT_ * 32) >= DENSE_FILL)
-        return launch_dense_cfg<FMT, WN_, WM_, RT_, CT_>(g, M, N, o, out, s);
-    return launch_dense_cfg<FMT, GWN_, GWM_, GRT_, DCT_>(g, M, N, o, out, s);
+        return launch_dense_split<FMT, WN_, WM_, RT_, CT_>(g, M, N, o, out, ldo, scale_off, min_off, s);
+    return launch_dense_split<FMT, GWN_, GWM_, GRT_, DCT_>(g, M, N, o, out, ldo, scale_off, min_off, s);
 }
 
 template <mmq_wtype FMT>
@@ -881,13 +936,19 @@ int gather_tail_tokens() { return TAIL_ROWS; }
 // A grid stays below 2^32 work-items: 2^24 workgroups of 256 threads.
 constexpr int64_t MAX_GRID = (int64_t(1) << 24) - 1;
 
-bool dense_grid_ok(int64_t M, int64_t N) {      // the larger of the two dense grids
-    return ceil_div(N, GWN_ * GRT_ * 32) * ceil_div(M, GWM_ * DCT_ * 32) <= MAX_GRID;
-}
-
 // the one MUL_MAT_ID launch holds the full-unit grid and the tail grid (at most as many units)
 bool gather_grid_ok(int64_t max_units, int64_t N) {
     return 2 * round_up(max_units, 8) * ceil_div(N, GWN_ * GRT_ * 32) <= MAX_GRID;
+}
+
+// The gather kernel addresses one expert's packed matrix and the T token rows with 32-bit
+// offsets from each region's base (it is not split into several launches: the unit list lives
+// on the device), so every such region must stay below 2 GiB.
+bool gather_regions_ok(mmq_wtype t, int64_t T, int64_t N, int64_t K) {
+    const PackedLayout P = packed_layout(t, N, K);
+    const ActQ81Layout A = act_q8_1_layout(T, K);
+    return P.NT * P.KBp * P.frag_bytes < MAX_REGION && P.Np * P.KBp * 4 < MAX_REGION &&
+           A.MT * A.KBp * 1024 < MAX_REGION && A.Mp * A.KBp * 4 < MAX_REGION;
 }
 
 hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,

@@ -383,9 +383,6 @@ hipError_t launch_w8a8(const void* packed, const void* act, int64_t M, int64_t N
 
 }  // namespace
 
-// Every size the API accepts fits: launches are split (see launch_w8a8).
-bool w8a8_grid_ok(int64_t, int64_t) { return true; }
-
 hipError_t launch_w8a8_gemm(const void* packed, const void* act, int64_t M, int64_t N, int64_t K,
                             mmq_otype o, void* out, int64_t ldo, hipStream_t s) {
     return o == MMQ_OUT_I32_PARTIALS ? launch_w8a8<true>(packed, act, M, N, K, out, ldo, s)

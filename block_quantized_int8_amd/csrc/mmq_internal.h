@@ -148,8 +148,6 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const void* aux, int64_t 
 hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
                              int64_t N, int64_t K, mmq_otype o, void* out, int64_t ldo,
                              hipStream_t s);
-// Dense grids: false if the launch would exceed the grid limit (checked before any launch).
-bool dense_grid_ok(int64_t M, int64_t N);
 // MUL_MAT_ID gather: full units (ufull offsets, up to gather_unit_tokens() pairs) and tail
 // units (utail offsets, at most gather_tail_tokens() pairs), each a launch of its own.
 hipError_t launch_block_gather(mmq_wtype t, const void* packed, int64_t E, const void* act,
@@ -160,8 +158,10 @@ hipError_t launch_block_gather(mmq_wtype t, const void* packed, int64_t E, const
 int gather_unit_tokens();
 int gather_tail_tokens();
 bool gather_grid_ok(int64_t max_units, int64_t N);
+// false if one expert's packed regions or the T token rows' act regions reach 2 GiB (the
+// gather kernel's 32-bit DMA offsets); dense GEMMs split such problems into several launches
+bool gather_regions_ok(mmq_wtype t, int64_t T, int64_t N, int64_t K);
 int64_t gemm_id_max_units(int64_t E, int64_t P);
-bool w8a8_grid_ok(int64_t M, int64_t N);
 hipError_t launch_w8a8_gemm(const void* packed, const void* act, int64_t M, int64_t N, int64_t K,
                             mmq_otype o, void* out, int64_t ldo, hipStream_t s);
 // Decode batches (M <= mmvq_max_tokens()): f32 out for the block formats, bf16 for I8_ROW.

@@ -1,7 +1,8 @@
 // quantize.hip - f32 activations -> q8_1 (per 32-value block) and per-token int8.
 //
 // q8_1 per block (minfer "08 . R1 - int8 MMQ prefill GEMM", section 3.2 CPU reference and
-// section 2.2): amax = max|x|; d = amax/127 in f32; di = 1/d (0 when d = 0);
+// section 2.2): amax = max|x|; d = amax/127 in f32; di = 1/d (0 when d = 0, the largest finite
+// f32 when 1/d overflows);
 // q = clamp(round-half-even(x*di), -128, 127); stored scale = d rounded to f16; the block's
 // integer sum is written alongside. Division is IEEE-correct (built with
 // -fhip-fp32-correctly-rounded-divide-sqrt) and nothing is contracted, so the result is
@@ -29,6 +30,12 @@ constexpr int QBLOCKS = 1024;     // workgroups at most (four per CU); waves the
 __device__ inline uint32_t pack4(int a, int b, int c, int d) {
     return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
            ((uint32_t)(d & 0xFF) << 24);
+}
+
+// 1/d, 0 for d = 0, and the largest finite f32 where 1/d overflows (d below 2^-128: a block
+// whose amax is under ~3.7e-37), so that 0 * di stays 0 and |x * di| stays within 127(1 + 2^-23)
+__device__ inline float inverse_scale(float d) {
+    return d != 0.0f ? fminf(1.0f / d, 3.40282347e38f) : 0.0f;
 }
 
 __device__ inline int q_of(float x, float di) {
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
                                          fmaxf(fabsf(v[i][c].z), fabsf(v[i][c].w))));
             amax = fmaxf(amax, __shfl_xor(amax, 32));
             const float d = amax / 127.0f;
-            const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+            const float di = inverse_scale(d);
             uint32_t w[4];
             int sum = 0;
 #pragma unroll
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(256) void quantize_i8_token_kernel(
         __syncthreads();
         amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
         const float d = amax / 127.0f;
-        const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+        const float di = inverse_scale(d);
         uint8_t* tile = reinterpret_cast<uint8_t*>(a) + (m >> 5) * KBp * 1024;
         const int r = (int)(m & 31);
         for (int64_t k = (int64_t)threadIdx.x * 4; k < KBp * 32; k += 1024) {

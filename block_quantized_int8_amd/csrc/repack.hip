@@ -7,6 +7,8 @@
 // Layouts: mmq_internal.h. Packing is a byte permutation (plus exact f32 scale products for
 // Q4_K) done once, outside the timed region (metainfer "INT8 W8A8 GEMM - Prefill",
 // section 3.2: one-time pack into a graph-stable buffer, validated by exact comparison).
+#include <algorithm>
+
 #include "mmq_internal.h"
 
 namespace {
@@ -37,9 +39,9 @@ __device__ inline Lane lane_of(int64_t gid, int64_t KBp, int64_t KB, int64_t N) 
 }
 
 __global__ __launch_bounds__(256) void repack_q8_0_kernel(
-    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total, int64_t gid0,
     uint8_t* __restrict__ frag, uint32_t* __restrict__ scale) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t w[4] = {0, 0, 0, 0};
@@ -58,9 +60,9 @@ __global__ __launch_bounds__(256) void repack_q8_0_kernel(
 }
 
 __global__ __launch_bounds__(256) void repack_q4_0_kernel(
-    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total, int64_t gid0,
     uint8_t* __restrict__ frag, uint32_t* __restrict__ scale) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t X0 = 0, X1 = 0;
@@ -83,9 +85,9 @@ __global__ __launch_bounds__(256) void repack_q4_0_kernel(
 }
 
 __global__ __launch_bounds__(256) void repack_q4_K_kernel(
-    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total, int64_t gid0,
     uint8_t* __restrict__ frag, uint32_t* __restrict__ scale, float* __restrict__ mins) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t X0 = 0, X1 = 0;
@@ -127,9 +129,9 @@ __global__ __launch_bounds__(256) void repack_q4_K_kernel(
 }
 
 __global__ __launch_bounds__(256) void repack_iq1t_kernel(
-    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total, int64_t gid0,
     uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t C = 0, meta = 0;
@@ -169,9 +171,9 @@ __global__ __launch_bounds__(256) void repack_iq1t_kernel(
 // (f16 d times an int8) and is split exactly into two f16, hi + lo; lanes of half 0 write it to
 // the first scale region, lanes of half 1 to the second.
 __global__ __launch_bounds__(256) void repack_q6_K_kernel(
-    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total,
+    const uint8_t* __restrict__ raw, int64_t N, int64_t KB, int64_t KBp, int64_t total, int64_t gid0,
     uint8_t* __restrict__ frag, uint32_t* __restrict__ scale, uint32_t* __restrict__ scale2) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t w[4] = {0, 0, 0, 0};
@@ -204,8 +206,8 @@ __global__ __launch_bounds__(256) void repack_q6_K_kernel(
 // same nibble. The packed result is exactly the IQ1T panel of the same values.
 __global__ __launch_bounds__(256) void repack_iq1c_kernel(
     const uint8_t* __restrict__ raw, const uint16_t* __restrict__ grid, int64_t N, int64_t KB,
-    int64_t KBp, int64_t total, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t KBp, int64_t total, int64_t gid0, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t C = 0, meta = 0;
@@ -247,8 +249,8 @@ __global__ __launch_bounds__(256) void repack_iq1c_kernel(
 // uint16 qh word) repeated for both halves and all four groups of the IQ1T panel.
 __global__ __launch_bounds__(256) void repack_iq1s_kernel(
     const uint8_t* __restrict__ raw, const uint16_t* __restrict__ grid, int64_t N, int64_t KB,
-    int64_t KBp, int64_t total, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t KBp, int64_t total, int64_t gid0, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint32_t C = 0, meta = 0;
@@ -283,8 +285,8 @@ __global__ __launch_bounds__(256) void repack_iq1s_kernel(
 
 __global__ __launch_bounds__(256) void repack_i8_row_kernel(
     const int8_t* __restrict__ raw, const float* __restrict__ row_scale, int64_t N, int64_t K,
-    int64_t KB, int64_t KBp, int64_t total, uint8_t* __restrict__ frag, float* __restrict__ sw) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t KB, int64_t KBp, int64_t total, int64_t gid0, uint8_t* __restrict__ frag, float* __restrict__ sw) {
+    const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const Lane x = lane_of(gid, KBp, KB, N);
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -303,44 +305,53 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const void* aux, int64_t 
     uint8_t* base = static_cast<uint8_t*>(packed);
     uint8_t* frag = base + L.frag_off;
     uint8_t* scale = base + L.scale_off;
+    // one thread per (tile, block, lane); launched in pieces of at most 2^30 threads so every
+    // grid stays within the launch limits whatever the matrix size
     const int64_t total = L.NT * L.KBp * 64;
-    const dim3 grid((unsigned)ceil_div(total, 256)), block(256);
+    constexpr int64_t PIECE = int64_t(1) << 30;
     const uint8_t* r8 = static_cast<const uint8_t*>(raw);
+    for (int64_t g0 = 0; g0 < total; g0 += PIECE) {
+    const dim3 grid((unsigned)ceil_div(std::min(PIECE, total - g0), 256)), block(256);
     switch (t) {
         case MMQ_Q8_0:
-            hipLaunchKernelGGL(repack_q8_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+            hipLaunchKernelGGL(repack_q8_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, g0, frag,
                                reinterpret_cast<uint32_t*>(scale));
             break;
         case MMQ_Q4_0:
-            hipLaunchKernelGGL(repack_q4_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+            hipLaunchKernelGGL(repack_q4_0_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, g0, frag,
                                reinterpret_cast<uint32_t*>(scale));
             break;
         case MMQ_Q4_K:
-            hipLaunchKernelGGL(repack_q4_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+            hipLaunchKernelGGL(repack_q4_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, g0, frag,
                                reinterpret_cast<uint32_t*>(scale), reinterpret_cast<float*>(base + L.min_off));
             break;
         case MMQ_IQ1T:
-            hipLaunchKernelGGL(repack_iq1t_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag, scale);
+            hipLaunchKernelGGL(repack_iq1t_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, g0, frag, scale);
             break;
         case MMQ_Q6_K:
-            hipLaunchKernelGGL(repack_q6_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, frag,
+            hipLaunchKernelGGL(repack_q6_K_kernel, grid, block, 0, s, r8, N, L.KB, L.KBp, total, g0, frag,
                                reinterpret_cast<uint32_t*>(scale), reinterpret_cast<uint32_t*>(base + L.min_off));
             break;
         case MMQ_IQ1S:
             hipLaunchKernelGGL(repack_iq1s_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,
-                               L.KB, L.KBp, total, frag, scale);
+                               L.KB, L.KBp, total, g0, frag, scale);
             break;
         case MMQ_IQ1C:
             hipLaunchKernelGGL(repack_iq1c_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,
-                               L.KB, L.KBp, total, frag, scale);
+                               L.KB, L.KBp, total, g0, frag, scale);
             break;
         case MMQ_I8_ROW:
             hipLaunchKernelGGL(repack_i8_row_kernel, grid, block, 0, s, static_cast<const int8_t*>(raw),
-                               static_cast<const float*>(aux), N, K, L.KB, L.KBp, total, frag,
+                               static_cast<const float*>(aux), N, K, L.KB, L.KBp, total, g0, frag,
                                reinterpret_cast<float*>(scale));
             break;
+        default:
+            return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace mmq

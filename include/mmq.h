@@ -21,7 +21,8 @@
  *    call returns a non-zero status and enqueues nothing. A failed kernel launch returns
  *    MMQ_EHIP. Faults inside kernels surface at the caller's next stream synchronisation.
  *  - Every device pointer must be 16-byte aligned (MMQ_EALIGN otherwise).
- *  - Sizes are int64_t; M, N >= 1; K >= 32.
+ *  - Sizes are int64_t: 1 <= M, N <= 2^24 and 32 <= K <= 2^23 for every call (MMQ_EINVAL
+ *    otherwise); further limits are stated at the calls they constrain.
  */
 #ifndef MMQ_H
 #define MMQ_H
@@ -51,6 +52,9 @@ typedef enum {
  *            sc (LSB-first), 6 B of eight 6-bit mins m, u8 qs[128]; sub-block j uses
  *            qs[16j..16j+15], low nibble = value 32j+i, high = value 32j+16+i.
  *                                                             w = d*sc_j*nib - dmin*m_j
+ *            d*sc_j must stay below 65504 and dmin*m_j must be finite in f32 (the repack
+ *            splits d*sc_j exactly into two f16; a larger product is not representable there
+ *            and the call's output is then undefined - the caller must not pass one).
  *  MMQ_IQ1T  76 B per 256 values (IQ1_M-style ternary): u8 codes[64] (2-bit c = g+1, four
  *            per byte LSB-first, c = 3 invalid), 6 B of sixteen 3-bit sub-scales s (one per
  *            16 values, LSB-first), 4 B of 32 sign bits (one per 8 values, 0 -> +1/8,
@@ -73,7 +77,8 @@ typedef enum {
  *            nibble of ql[16j+i] and value 32j+16+i in the high nibble; the high 2 bits of
  *            value 32j+8t+i (t < 4, i < 8) are bits 2t..2t+1 of qh[8j+i]; q = low | high << 4
  *            in 0..63.                                                   w = d*sc_h*(q-32)
- *            d*|sc| must stay below 65504 (the repack splits d*sc into two f16).
+ *            d*|sc| must stay below 65504 (the repack splits d*sc into two f16; a larger
+ *            product makes the output undefined - the caller must not pass one).
  * Value formulas: minfer R1 sections 1-2.2 (q8_0, q4_0, Q4_K), 2.2 and 3.3 (q6_K: 6-bit grid
  * moved to the signed domain by -32, a scale per 16 values); llama.cpp PR #304 description
  * (IQ1_M and IQ1_S, the 11-bit grid index per 8 values, IQ1_M's per-16 sub-scales); metainfer "INT8 W8A8
@@ -84,12 +89,14 @@ typedef enum {
 } mmq_wtype;
 
 /* Activation formats.
- *  MMQ_ACT_Q8_1     per 32-value block: amax = max|x|; d = amax/127 (f32); q = clamp(
- *                   round-half-even(x * (1/d)), -128, 127) (q = 0 if d = 0); the stored scale
- *                   xs = d rounded to f16 (kept as f32); xsum = sum of the 32 q
- *                   (minfer R1 section 3.2 CPU reference; section 2.2 block sum).
- *  MMQ_ACT_I8_TOKEN one block per row (the whole of K), scale kept in f32 (metainfer W8A8
- *                   section 1: int8 activations with a per-token f32 scale). */
+ *  MMQ_ACT_Q8_1     per 32-value block: amax = max|x|; d = amax/127 (f32); di = 1/d in f32,
+ *                   except di = 0 if d = 0 and di = FLT_MAX (the largest finite f32) where 1/d
+ *                   overflows (amax below ~3.7e-37); q = clamp(round-half-even(x * di), -128,
+ *                   127); the stored scale xs = d rounded to f16 (kept as f32); xsum = sum of
+ *                   the 32 q (minfer R1 section 3.2 CPU reference; section 2.2 block sum).
+ *                   The inputs must be finite.
+ *  MMQ_ACT_I8_TOKEN one block per row (the whole of K), the same di rule, scale kept in f32
+ *                   (metainfer W8A8 section 1: int8 activations with a per-token f32 scale). */
 typedef enum { MMQ_ACT_Q8_1 = 0, MMQ_ACT_I8_TOKEN = 1 } mmq_atype;
 
 /* Output types.
@@ -153,8 +160,9 @@ size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K);
  *  aux       (device) MMQ_I8_ROW: f32 [N] per-row scales; MMQ_IQ1C, MMQ_IQ1S: the grid,
  *            uint16 [2048]; must be NULL for every other format. Read only during the call's
  *            kernels; not referenced afterwards.
- *  packed    (device) mmq_packed_bytes(t, N, K) bytes; written completely (padding rows
- *            are zero). Immutable afterwards and safe to reuse across graph replays
+ *  packed    (device) mmq_packed_bytes(t, N, K) bytes; every region is written completely
+ *            (padding rows and blocks are zero), the alignment gaps between regions are not
+ *            written. Immutable afterwards and safe to reuse across graph replays
  *            (metainfer section 3.2: one-time pack outside the timed region).
  * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, Q6_K, IQ1T, IQ1C, IQ1S).
  * MMQ_IQ1C and MMQ_IQ1S are expanded here, once, through the grid into the MMQ_IQ1T panel
@@ -174,6 +182,11 @@ mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux,
  *  ldo    >= N, in elements.
  * Supported (t, o): block formats with F32 or I32_PARTIALS; I8_ROW with BF16 or
  * I32_PARTIALS.
+ * Limits (MMQ_EINVAL before any launch): MMQ_I8_ROW needs K < 131072, so that its int32
+ * accumulator over all of K cannot overflow (|q_a * q_w| <= 2^14 per term); the
+ * I32_PARTIALS output holds at most 2^31 values. Problems whose packed weights or act
+ * buffer reach 2 GiB (e.g. a 262144 x 8192 q8_0 matrix) are run as several launches over
+ * ranges of weight and token tiles, with the same results.
  * Dispatch: batches of M <= 16 token rows (F32 / BF16 output) run the small-batch split-K
  * kernel, larger ones the prefill tiles (a decode batch would leave a prefill tile mostly
  * empty; llama.cpp PR #304, Summary: small batches stay on a matrix-vector kernel). Both
@@ -204,7 +217,11 @@ size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
  * Decode batches (T <= 4, T*top_k <= 256) run the small-batch kernel per expert instead of
  * the prefill tiles (llama.cpp PR #304, Summary: small batches stay on a matrix-vector
  * kernel); the result is the same per-block contraction.
- * Block formats only; o must be MMQ_OUT_F32. */
+ * Block formats only; o must be MMQ_OUT_F32.
+ * Limits (MMQ_EINVAL before any launch): T * top_k <= 2^24; outside the decode-batch case,
+ * one expert's packed matrix must keep its fragment and scale regions below 2 GiB each
+ * (e.g. N * K < 2^31 values of q8_0) and the act buffer's value region below 2 GiB
+ * (T * K < 2^31), because the grouped launch addresses them with 32-bit offsets. */
 mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
                        const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
                        mmq_otype o, void* out, void* workspace, size_t ws_bytes, void* stream);

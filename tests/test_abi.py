@@ -212,3 +212,35 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
         mmq.lib()
     with pytest.raises(RuntimeError):
         mmq.packed_bytes("q4_0", 32, 64)
+
+
+def test_size_limits_rejected_before_any_launch(mmq):
+    """Every size the kernels cannot address is refused on the host with MMQ_EINVAL (the pointers
+    here are never dereferenced: validation returns first)."""
+    L = mmq.lib()
+    G = ctypes.c_void_p(0x10000)
+    EINVAL = mmq.MMQ_EINVAL
+    # K above 2^23 (any format, any call)
+    assert L.mmq_gemm(0, G, G, 4, 32, (1 << 23) + 32, 0, G, 32, None) == EINVAL
+    assert L.mmq_quantize_act(0, G, 4, (1 << 23) + 32, (1 << 23) + 32, G, None) == EINVAL
+    assert mmq.act_bytes("q8_1", 4, (1 << 23) + 32) == 0
+    assert mmq.packed_bytes("q4_0", 32, (1 << 23) + 32) == 0
+    # M, N above 2^24
+    assert L.mmq_gemm(1, G, G, (1 << 24) + 1, 32, 64, 0, G, 32, None) == EINVAL
+    assert L.mmq_gemm(1, G, G, 4, (1 << 24) + 1, 64, 0, G, (1 << 24) + 1, None) == EINVAL
+    # W8A8: the int32 accumulator over all of K needs K < 2^17 (prefill and decode sizes)
+    assert L.mmq_gemm(4, G, G, 64, 32, 1 << 17, 1, G, 32, None) == EINVAL
+    assert L.mmq_gemm(4, G, G, 4, 32, 1 << 17, 1, G, 32, None) == EINVAL
+    assert L.mmq_gemm(4, G, G, 64, 32, 1 << 17, 2, G, 32, None) == EINVAL
+    # debug partials: at most 2^31 values; the largest sizes must not overflow the check
+    assert L.mmq_gemm(1, G, G, 1 << 12, 1 << 12, 1 << 17, 2, G, 1 << 12, None) == EINVAL
+    assert L.mmq_gemm(1, G, G, 1 << 24, 1 << 24, 1 << 23, 2, G, 1 << 24, None) == EINVAL
+    assert L.mmq_gemm(4, G, G, 1 << 16, 1 << 16, 64, 2, G, 1 << 16, None) == EINVAL
+    # MUL_MAT_ID gather path: one expert's fragments (q8_0 N*K = 2^31 values), or the act
+    # values of all T tokens (T*K = 2^31), at 2 GiB or more
+    big = ctypes.c_size_t(1 << 40)
+    assert L.mmq_gemm_id(0, G, 1, G, G, 8, 1, 1 << 17, 1 << 14, 0, G, G, big, None) == EINVAL
+    assert L.mmq_gemm_id(0, G, 1, G, G, 1 << 17, 1, 32, 1 << 14, 0, G, G, big, None) == EINVAL
+    # T * top_k above 2^24
+    assert L.mmq_gemm_id(0, G, 8, G, G, 1 << 22, 8, 32, 64, 0, G, G, big, None) == EINVAL
+    assert mmq.gemm_id_workspace_bytes(8, 1 << 22, 8) == 0
