@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import gen
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -70,8 +71,8 @@ def test_prefill_graph_replay_with_changed_inputs(env, fmt, M, N, K):
         eager = mmq.gemm(fmt, packed, mmq.quantize_act(torch.from_numpy(x).to(dev)), M, N, K)
         torch.cuda.synchronize()
         assert torch.equal(out, eager), rep
-        rq, rs, _ = orc.quantize_q8_1(x)
-        assert _rel(out.cpu().numpy(), orc.gemm_f64(fmt, raw, N, K, rq, rs)) <= GATE
+        rq, rs, rsum = orc.quantize_q8_1(x)
+        parity.check_f32(orc, out.cpu().numpy(), fmt, raw, N, K, rq, rs, rsum, what=(fmt, rep))
 
 
 def test_w8a8_graph_replay_with_changed_inputs(env):
@@ -133,6 +134,7 @@ def test_moe_graph_replay_with_changed_routing(env):
                             torch.from_numpy(ids).to(dev), T, top_k, N, K)
         torch.cuda.synchronize()
         assert torch.equal(out, eager), rep
-        rq, rs, _ = orc.quantize_q8_1(x)
+        rq, rs, rsum = orc.quantize_q8_1(x)
         ref = orc.moe_f64("iq1t", raw.reshape(E * N, -1), E, N, K, rq, rs, ids)
         assert _rel(out.cpu().numpy(), ref) <= GATE
+        parity.check_moe(orc, out.cpu().numpy(), "iq1t", raw.reshape(E, N, -1), N, K, rq, rs, rsum, ids, what=rep)

@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 
 import gen
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -125,9 +126,9 @@ def test_dense_prefill(env, fmt, M, N, K):
     xq, xs, xsum = mmq.act_to_host(act.cpu().numpy(), M, K)
     assert np.array_equal(xq, rq) and np.array_equal(xsum, rsum)
     assert np.array_equal(parts.cpu().numpy(), orc.partials(fmt, raw, N, K, rq, grid=gen.IQ1C_GRID))
-    rel = _rel(out.cpu().numpy(), orc.gemm_f64(fmt, raw, N, K, rq, rs, grid=gen.IQ1C_GRID))
-    print(f"  rel err {rel:.3e}")
-    assert rel <= GATE
+    r1, r2 = parity.check_f32(orc, out.cpu().numpy(), fmt, raw, N, K, rq, rs, rsum, grid=gen.IQ1C_GRID,
+                              what=(fmt, M, N, K))
+    print(f"  rel err {r1:.3e} (definition), {r2:.3e} (C oracle)")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -142,8 +143,8 @@ def test_decode_batches(env, fmt, M):
     act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
     out = mmq.gemm(fmt, _pack(env, raw, N, K, fmt), act, M, N, K, "f32")
     torch.cuda.synchronize()
-    rq, rs, _ = orc.quantize_q8_1(x)
-    assert _rel(out.cpu().numpy(), orc.gemm_f64(fmt, raw, N, K, rq, rs, grid=gen.IQ1C_GRID)) <= GATE
+    rq, rs, rsum = orc.quantize_q8_1(x)
+    parity.check_f32(orc, out.cpu().numpy(), fmt, raw, N, K, rq, rs, rsum, grid=gen.IQ1C_GRID, what=(fmt, M))
 
 
 def _moe(env, E, T, top_k, N, K, ids, seed, cfg=88, fmt="iq1c"):
@@ -174,7 +175,8 @@ def test_moe_every_row(env, fmt, T):
     raw, rq, rs, got = _moe(env, E, T, top_k, N, K, ids, seed=T, fmt=fmt)
     ref = orc.moe_f64(fmt, raw.reshape(E * N, -1), E, N, K, rq, rs, ids, grid=gen.IQ1C_GRID)
     rel = _rel(got, ref)
-    print(f"  rel err {rel:.3e}")
+    r2 = parity.check_moe(orc, got, fmt, raw, N, K, rq, rs, parity.block_sums(rq), ids, grid=gen.IQ1C_GRID)
+    print(f"  rel err {rel:.3e} (definition), {r2:.3e} (C oracle)")
     assert rel <= GATE
 
 
@@ -189,9 +191,12 @@ def test_moe_full_size_sampled(env, name):
     r = np.random.default_rng(13)
     cols = np.sort(np.concatenate([r.choice(N, 192, replace=False), [0, N - 1]]))
     worst = 0.0
-    for e in r.choice(E, 10, replace=False):
+    experts = r.choice(E, 10, replace=False)
+    for e in experts:
         tt, jj = np.nonzero(ids == e)
         ref = orc.gemm_f64(c["fmt"], raw[e], N, K, rq[tt], rs[tt], cols=cols, grid=gen.IQ1C_GRID)
         worst = max(worst, _rel(got[tt, jj][:, cols], ref))
-    print(f"  rel err {worst:.3e}")
+    r2 = parity.check_moe(orc, got[:, :, cols], c["fmt"], raw, N, K, rq, rs, parity.block_sums(rq), ids,
+                          grid=gen.IQ1C_GRID, experts=experts, cols=cols)
+    print(f"  rel err {worst:.3e} (definition), {r2:.3e} (C oracle)")
     assert worst <= GATE

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import gen
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -62,11 +63,9 @@ def test_dense_128x128_ragged_output(env, fmt):
     got = out.cpu().numpy()
     r = np.random.default_rng(5)
     rows = np.sort(np.concatenate([[0, 127, 128, M - 33, M - 1], r.choice(M, 11, replace=False)]))
-    rq, rs, _ = orc.quantize_q8_1(x)
-    ref = orc.gemm_f64(fmt, raw, N, K, rq, rs, rows=rows)
-    rel = _rel(got[rows], ref)
-    print(f"  rel err {rel:.3e} on {len(rows)} full rows", flush=True)
-    assert rel <= GATE
+    rq, rs, rsum = orc.quantize_q8_1(x)
+    r1, r2 = parity.check_f32(orc, got[rows], fmt, raw, N, K, rq, rs, rsum, rows=rows, what=fmt)
+    print(f"  rel err {r1:.3e} (definition), {r2:.3e} (C oracle) on {len(rows)} full rows", flush=True)
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q4_K"])

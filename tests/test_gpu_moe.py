@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import gen
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +62,8 @@ def _check_full(env, fmt, E, N, K, ids, raw, rq, rs, got):
     assert np.all(got[~valid] == SENTINEL)
     if valid.any():
         rel = _rel(got[valid], ref[valid])
-        print(f"  rel err {rel:.3e}")
+        r2 = parity.check_moe(orc, got, fmt, raw, N, K, rq, rs, parity.block_sums(rq), np.where(valid, ids, -1))
+        print(f"  rel err {rel:.3e} (definition), {r2:.3e} (C oracle)")
         assert rel <= GATE
 
 
@@ -163,9 +165,12 @@ def test_moe_full_size_sampled(env):
     r = np.random.default_rng(12)
     cols = np.sort(np.concatenate([r.choice(N, 192, replace=False), [0, N - 1]]))
     worst = 0.0
-    for e in r.choice(E, 12, replace=False):
+    experts = r.choice(E, 12, replace=False)
+    for e in experts:
         tt, jj = np.nonzero(ids == e)
         ref = orc.gemm_f64("iq1t", raw[e], N, K, rq[tt], rs[tt], cols=cols)
         worst = max(worst, _rel(got[tt, jj][:, cols], ref))
-    print(f"  rel err {worst:.3e}")
+    r2 = parity.check_moe(orc, got[:, :, cols], "iq1t", raw, N, K, rq, rs, parity.block_sums(rq), ids,
+                          experts=experts, cols=cols)
+    print(f"  rel err {worst:.3e} (definition), {r2:.3e} (C oracle)")
     assert worst <= GATE

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import gen
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,8 @@ def _check(env, fmt, E, N, K, ids, raw, rq, rs, got):
     assert np.all(got[~valid] == SENTINEL)
     if valid.any():
         rel = _rel(got[valid], ref[valid])
-        print(f"  rel err {rel:.3e}", flush=True)
+        r2 = parity.check_moe(orc, got, fmt, raw, N, K, rq, rs, parity.block_sums(rq), np.where(valid, ids, -1))
+        print(f"  rel err {rel:.3e} (definition), {r2:.3e} (C oracle)", flush=True)
         assert rel <= GATE
 
 
@@ -133,6 +135,7 @@ def test_moe_decode_full_shape_sampled(env, T):
             e = ids[t, j]
             ref = orc.gemm_f64("iq1t", raw[e], N, K, rq[t:t + 1], rs[t:t + 1], cols=cols)
             assert _rel(got[t, j][cols][None, :], ref) <= GATE, (t, j)
+    parity.check_moe(orc, got[:, :, cols], "iq1t", raw, N, K, rq, rs, parity.block_sums(rq), ids, cols=cols)
 
 
 def test_moe_decode_repeated_expert_in_a_token(env):

@@ -7,7 +7,8 @@ rescaled by its own d*sc (minfer R1 sections 2.2 and 3.3). The checks:
 * the repack's scale split: the two f16 halves of every packed scale dword add up to d*sc_h
   exactly (read back at the documented packed offsets);
 * prefill: q8_1 bit-exact, the per-16 int32 partials (two per block) bit-exact, f32 within
-  max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4), on shapes with
+  max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4) and within the
+  rounding bound of tests/parity.py of the per-block C oracle, on shapes with
   ragged M and N tails and both signs of sub-scale, plus worst-case blocks;
 * small batches (M <= 16: the decode kernel, two half-block MFMAs per block), MUL_MAT_ID
   (prefill gather and, for at most 4 tokens, the decode kernel), and the 7B
@@ -18,6 +19,7 @@ import numpy as np
 import pytest
 
 import gen
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -89,9 +91,8 @@ def test_prefill(env, M, N, K):
     xq, xs, xsum = mmq.act_to_host(act.cpu().numpy(), M, K)
     assert np.array_equal(xq, rq) and np.array_equal(xsum, rsum)
     assert np.array_equal(parts, orc.partials16("q6_K", raw, N, K, rq))
-    rel = _rel(out, orc.gemm_f64("q6_K", raw, N, K, rq, rs))
-    print(f"  rel err {rel:.3e}")
-    assert rel <= GATE
+    r1, r2 = parity.check_f32(orc, out, "q6_K", raw, N, K, rq, rs, rsum, what=(M, N, K))
+    print(f"  rel err {r1:.3e} (definition), {r2:.3e} (C oracle)")
 
 
 def test_extreme_blocks(env):
@@ -107,11 +108,11 @@ def test_extreme_blocks(env):
     x[1::2] *= -1
     _, mmq, orc = env
     _, _, out, parts = _run(env, raw, x, M, N, K)
-    rq, rs, _ = orc.quantize_q8_1(x)
+    rq, rs, rsum = orc.quantize_q8_1(x)
     P16 = orc.partials16("q6_K", raw, N, K, rq)
     assert np.abs(P16).max() == 16 * 32 * 127
     assert np.array_equal(parts, P16)
-    assert _rel(out, orc.gemm_f64("q6_K", raw, N, K, rq, rs)) <= GATE
+    parity.check_f32(orc, out, "q6_K", raw, N, K, rq, rs, rsum)
 
 
 # small batches run the decode kernel: token rows staged in LDS (K up to 448 blocks for M <= 8,
@@ -125,8 +126,8 @@ def test_small_batches(env, M, K):
     raw = gen.weights_q6_K(N, K, seed=M, cfg=64)
     x = gen.act_f32(M, K, seed=M, cfg=64)
     _, _, out, _ = _run(env, raw, x, M, N, K, partials=False)
-    rq, rs, _ = orc.quantize_q8_1(x)
-    assert _rel(out, orc.gemm_f64("q6_K", raw, N, K, rq, rs)) <= GATE
+    rq, rs, rsum = orc.quantize_q8_1(x)
+    parity.check_f32(orc, out, "q6_K", raw, N, K, rq, rs, rsum, what=(M, K))
 
 
 def test_small_batch_matches_prefill_tiles(env):
@@ -156,9 +157,10 @@ def test_moe(env):
                            out=packed[e * pb:(e + 1) * pb])
     out = mmq.gemm_id("q6_K", packed, E, act, torch.from_numpy(ids).to(dev), T, top_k, N, K)
     torch.cuda.synchronize()
-    rq, rs, _ = orc.quantize_q8_1(x)
+    rq, rs, rsum = orc.quantize_q8_1(x)
     ref = orc.moe_f64("q6_K", raw.reshape(E * N, -1), E, N, K, rq, rs, ids)
     assert _rel(out.cpu().numpy(), ref) <= GATE
+    parity.check_moe(orc, out.cpu().numpy(), "q6_K", raw, N, K, rq, rs, rsum, ids)
 
 
 @pytest.mark.parametrize("T", [1, 4])
@@ -179,9 +181,10 @@ def test_moe_decode(env, T):
                            out=packed[e * pb:(e + 1) * pb])
     out = mmq.gemm_id("q6_K", packed, E, act, torch.from_numpy(ids).to(dev), T, top_k, N, K)
     torch.cuda.synchronize()
-    rq, rs, _ = orc.quantize_q8_1(x)
+    rq, rs, rsum = orc.quantize_q8_1(x)
     ref = orc.moe_f64("q6_K", raw.reshape(E * N, -1), E, N, K, rq, rs, ids)
     assert _rel(out.cpu().numpy(), ref) <= GATE
+    parity.check_moe(orc, out.cpu().numpy(), "q6_K", raw, N, K, rq, rs, rsum, ids, what=T)
 
 
 def test_ffn_down_full_size_sampled(env):
@@ -195,7 +198,6 @@ def test_ffn_down_full_size_sampled(env):
     r = np.random.default_rng(14)
     rows = np.sort(np.concatenate([r.choice(M, 16, replace=False), [0, M - 1]]))
     cols = np.sort(np.concatenate([r.choice(N, 256, replace=False), [0, N - 1]]))
-    rq, rs, _ = orc.quantize_q8_1(x[rows])
-    rel = _rel(out[np.ix_(rows, cols)], orc.gemm_f64("q6_K", raw, N, K, rq, rs, cols=cols))
-    print(f"  rel err {rel:.3e}")
-    assert rel <= GATE
+    rq, rs, rsum = orc.quantize_q8_1(x[rows])
+    r1, r2 = parity.check_f32(orc, out[np.ix_(rows, cols)], "q6_K", raw, N, K, rq, rs, rsum, cols=cols)
+    print(f"  rel err {r1:.3e} (definition), {r2:.3e} (C oracle)")
