@@ -14,14 +14,16 @@ workloads are decode batches of 1-16 tokens on the same weight shapes).
 
 Timing (the pages' protocol: warm-up, then 30 samples of 100 back-to-back launches (or a
 hipGraph replay) timed with hipEvents, median and min/max spread; P2 section 3.3):
-  step time     all --steps steps are captured in one hipGraph, replayed once untimed and once
-                between two synchronisations; value = 2*M*N*K / step time. The graph keeps
-                host launch cost (and the ~8 us gap between graph launches) out of the timing;
-                the one launch and the final synchronisation (~0.7 ms together) are spread over
-                the default 2000 steps.
-  kernel times  per kernel, a hipGraph of 100 back-to-back launches replayed 30 times, each
-                replay bracketed by HIP events on the launch stream: 30 samples of the average
-                launch duration (mean, median, min, max reported).
+  step time     all --steps steps are captured in one hipGraph; each timed replay is bracketed
+                by HIP events recorded on the launch stream, so the per-step figure does not
+                depend on --steps (no host launch or synchronisation cost inside it); value =
+                2*M*N*K / median step time over --rounds replays.
+  kernel times  per kernel, a hipGraph of 100 back-to-back launches, each replay bracketed by
+                HIP events on the launch stream: 30 samples of the average launch duration
+                (mean, median, min, max reported).
+  interleaving  the step replays and the kernel samples alternate in --rounds rounds (minfer R1
+                section 4: alternate A and B so that a change of machine load shows up as spread,
+                not as a difference); the per-round step times are reported.
   cold MALL     --rotate R cycles R copies of the packed weights through the launches so every
                 launch reads its weights from HBM rather than the 256 MB last-level cache
                 (default for the decode workloads: enough copies for >= 1 GB).
@@ -60,20 +62,36 @@ METRIC = "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MF
 DECODE_MAX_M = 16                # mmq_gemm runs batches up to this many rows on the decode kernel
 COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at least this much
 
-# HBM bytes per launch of the dominant kernel (for MUL_MAT_ID: route + both gather launches),
-# measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE for the kernel version this file ships
-# with and scaled by the copy-kernel factor (profiles/ holds the summaries); absent (reported
-# as null) until measured for the current kernel.
-MEASURED_TRAFFIC_BYTES = {
-    "q4_0_m2048_n4096_k4096": 170662206,
-    "q4_K_m512_n14336_k4096": 99522320,
-    "w8a8_m3072_n1536_k4096": 60068906,
-    "moe_iq1t_e64_t512_top8_n2048_k4096": 388458673,
-    "dec_q4_0_m8_n4096_k4096": 11134760,
-    "dec_q4_K_m8_n14336_k4096": 45164207,
-    "q6_K_m2048_n4096_k11008": 475612543,
-    "moe_iq1c_e64_t512_top8_n2048_k4096": 388450164,
+# HBM bytes per launch of the dominant kernel (for MUL_MAT_ID: route + gather launch), measured
+# with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE and scaled by the copy-kernel factors
+# (profiles/ holds the summaries), with the hash of the kernel sources they were measured on:
+# reported only while the sources still hash the same, else null.
+MEASURED_TRAFFIC = {
 }
+KERNEL_SOURCES = {
+    "block": ["gemm_block.hip", "gemm_common.h"],
+    "gather": ["gemm_block.hip", "gemm_id.hip", "gemm_common.h"],
+    "w8a8": ["gemm_w8a8.hip", "gemm_common.h"],
+    "mmvq": ["gemm_mmvq.hip", "gemm_id.hip", "gemm_common.h"],
+}
+
+
+def kernel_source_hash(kind):
+    """First 16 hex digits of the SHA-256 of the kernel's source files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "block_quantized_int8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, kind):
+    rec = MEASURED_TRAFFIC.get(name)
+    if rec is None or rec[1] != kernel_source_hash(kind):
+        return None
+    return rec[0]
+
 
 RAW_BYTES_PER_32 = {"q8_0": 34, "q4_0": 18, "q4_K": 144 / 8, "iq1t": 76 / 8, "iq1c": 56 / 8, "iq1s": 50 / 8,
                     "q6_K": 210 / 8,
@@ -229,45 +247,53 @@ def _graph(fns, n):
     return g
 
 
-def timed(kernels, n_rot, steps, warmup, samples=30, per_sample=100):
+def timed(kernels, n_rot, steps, warmup, samples=30, per_sample=100, rounds=5):
     """kernels: [(name, fn(r))] launched in this order make one step on weight copy r.
-    Step time: one hipGraph of all `steps` steps, replayed once between two synchronisations
-    (after one untimed replay). Kernel times: per kernel, a
-    hipGraph of `per_sample` back-to-back launches replayed `samples` times, each replay
-    bracketed by HIP events on the launch stream. Returns (step seconds, {name: samples [s]})."""
+
+    Step time: all `steps` steps captured in one hipGraph; each timed replay is bracketed by
+    HIP events recorded on the launch stream (so host launch and synchronisation costs stay out
+    of the figure, whatever `steps` is), with a synchronisation on both sides.
+    Kernel times: per kernel, a hipGraph of `per_sample` back-to-back launches, each replay
+    bracketed by HIP events: one sample of the average launch duration.
+    The phases are interleaved (minfer R1 section 4: alternate the variants so that a change of
+    load on the machine shows up as spread, not as a difference): `rounds` rounds, each one
+    step replay and samples/rounds samples of every kernel. Returns (step seconds per round,
+    {name: kernel samples [s]})."""
     import torch
+    stream = torch.cuda.current_stream()
     def step(r):
         for _, f in kernels:
             f(r)
     for i in range(warmup):
         step(i % n_rot)
     torch.cuda.synchronize()
-    # all `steps` steps in one graph: one graph launch per timed region (a replay of a one-step
-    # graph costs ~8 us of launch gap between replays, longer than a decode step)
-    g = _graph([lambda r=r: step(r) for r in range(n_rot)], steps)
-    g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / steps
-    del g
-    kt = {}
-    for name, f in kernels:
-        g = _graph([lambda r=r, f=f: f(r) for r in range(n_rot)], per_sample)
+    g_step = _graph([lambda r=r: step(r) for r in range(n_rot)], steps)
+    g_k = {name: _graph([lambda r=r, f=f: f(r) for r in range(n_rot)], per_sample) for name, f in kernels}
+    g_step.replay()
+    for g in g_k.values():
         g.replay()
+    torch.cuda.synchronize()
+
+    def event_time(g):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    per_round = max(1, samples // rounds)
+    step_s = []
+    kt = {name: [] for name, _ in kernels}
+    for _ in range(rounds):
         torch.cuda.synchronize()
-        res = []
-        for _ in range(samples):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            e1.synchronize()
-            res.append(e0.elapsed_time(e1) * 1e-3 / per_sample)
-        kt[name] = np.array(res)
-        del g
-    return step_s, kt
+        step_s.append(event_time(g_step) / steps)
+        torch.cuda.synchronize()
+        for name, _ in kernels:
+            for _ in range(per_round):
+                kt[name].append(event_time(g_k[name]) / per_sample)
+    del g_step, g_k
+    return np.array(step_s), {k: np.array(v) for k, v in kt.items()}
 
 
 def main():
@@ -280,6 +306,8 @@ def main():
                     help="weight copies cycled through the steps (cold MALL); default: 1, or enough "
                          "for >= 1 GB on the decode workloads")
     ap.add_argument("--samples", type=int, default=30, help="kernel-timing samples")
+    ap.add_argument("--rounds", type=int, default=5,
+                    help="interleaved rounds of (one timed step replay, samples/rounds kernel samples)")
     ap.add_argument("--per-sample", type=int, default=100, help="graph-replayed launches per sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--calib-copy", action="store_true",
@@ -382,9 +410,11 @@ def main():
         extra["weight_bytes_rotated"] = int(n_rot * packed[0].numel())
 
     torch.cuda.synchronize()
-    step_s, kt = timed(kernels, n_rot, args.steps, args.warmup, args.samples, args.per_sample)
+    step_rounds, kt = timed(kernels, n_rot, args.steps, args.warmup, args.samples, args.per_sample, args.rounds)
+    step_s = float(np.median(step_rounds))
     sclk = sclk_mhz()
     tops = ops / step_s / 1e12
+    log(f"[bench] step per round (us): " + ", ".join(f"{v * 1e6:.2f}" for v in step_rounds))
     kstats = []
     for kn, _ in kernels:
         c = kt[kn]
@@ -418,7 +448,9 @@ def main():
         nops = VALU_OPS_PER_EB.get(fmt, 2)
         roof["valu_ceiling"] = {"ops_per_element_block": nops, "peak_lane_ops": VALU_PEAK_LANE_OPS,
                                 "frac": round(nops * E / k_s / VALU_PEAK_LANE_OPS, 4)}
-    roof["traffic"] = MEASURED_TRAFFIC_BYTES.get(name) if n_rot == 1 or name.startswith("dec") else None
+    kind = "w8a8" if fmt == "i8_row" and not decode else "mmvq" if decode else "gather" if moe else "block"
+    roof["traffic"] = measured_traffic(name, kind) if n_rot == 1 or name.startswith("dec") else None
+    roof["kernel_source_hash"] = kernel_source_hash(kind)
     roof["kernel"] = kernels[dom][0]
     roof["kernel_us"] = {k: round(v * 1e6, 3) for k, v in kstats[dom].items()}
     roof["algorithmic_bytes"] = alg_bytes
@@ -451,8 +483,10 @@ def main():
                    "activations": "i8_token" if fmt == "i8_row" else "q8_1",
                    "step": "gemm (int8 activations given)" if fmt == "i8_row" else
                            "quantize_act + gemm" + ("_id" if moe else "") + " (repack untimed)",
-                   "timing": f"one hipGraph of all steps; kernels: {args.samples} samples x {args.per_sample} "
-                             f"graph-replayed launches, hipEvents",
+                   "timing": f"one hipGraph of all {args.steps} steps, HIP events on the launch stream, median "
+                             f"of {args.rounds} replays interleaved with the kernel samples "
+                             f"({args.samples} samples x {args.per_sample} graph-replayed launches per kernel)",
+                   "step_us_rounds": [round(v * 1e6, 3) for v in step_rounds],
                    **extra},
         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 3),
         "sclk_mhz_after_run": sclk,
