@@ -299,7 +299,7 @@ def timed(kernels, n_rot, steps, warmup, samples=30, per_sample=100, rounds=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=HEADLINE, help="one of gen.CONFIGS")
     ap.add_argument("--rotate", type=int, default=-1,

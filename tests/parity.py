@@ -19,7 +19,9 @@ Two bars for every f32 output of the block-scaled contraction:
    times xs), u * |ref| for the oracle's own final rounding, and the last term for
    accumulators that fall into the f32 subnormal range (2^-150 per rounding, times the
    largest power-of-two scale, 2^26, the kernels apply in the epilogue). On top, the
-   normwise error must stay within 1e-5 (the kernels reach ~1e-7): a defect of the scale
+   normwise error must stay within max(1e-5, 2 u sqrt(K/32)) (the kernels reach ~1e-7 at
+   K of a few thousand; rounding errors of a sequential f32 sum of K/32 terms drift like
+   u sqrt(K/32) relative to its result, 1.3e-5 measured at K = 2^23): a defect of the scale
    path well below the pages' 1e-3 - for instance dropping the low half of q4_K's exact
    f16 split of d*sc, an error of up to 2^-12 per term - fails one of the two.
 """
@@ -34,6 +36,10 @@ def rel(got, ref):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def normwise_gate(K):
+    return max(NORMWISE_GATE, 2 * U * np.sqrt(K // 32))
 
 
 def rounding_bound(ref_c, absum, K):
@@ -53,10 +59,10 @@ def check_tight(got, ref_c, absum, K, what="", per_row=False):
     if per_row:
         for i in range(got.shape[0]):
             r = rel(got[i], ref[i]) if np.any(ref[i]) else float(np.max(err[i]))
-            assert r <= NORMWISE_GATE, (what, i, r)
+            assert r <= normwise_gate(K), (what, i, r)
         return
     r = rel(got, ref)
-    assert r <= NORMWISE_GATE, (what, r)
+    assert r <= normwise_gate(K), (what, r)
     return r
 
 
@@ -106,7 +112,7 @@ def check_moe(orc, got, fmt, raw_e, N, K, xq, xs, xsum, ids, grid=None, experts=
         g_all.append(g)
         r_all.append(ref_c)
     r = rel(np.concatenate(g_all), np.concatenate(r_all))
-    assert r <= NORMWISE_GATE, (what, r)
+    assert r <= normwise_gate(K), (what, r)
     return r
 
 
