@@ -7,7 +7,8 @@ memory and the stream. There is no CPU fallback: if the library is missing, ever
 The functions mirror include/mmq.h one to one (same names without the `mmq_` prefix):
 
     act_bytes, act_region_offsets, quantize_act, packed_bytes, repack_weights, gemm,
-    gemm_id_workspace_bytes, gemm_id, status_string
+    gemm_id_workspace_bytes, gemm_id, gemm_id_noalloc, gemm_id_noalloc_max_workspace_bytes,
+    status_string
 
 plus host-side encoders/decoders of the documented act layouts (`act_to_host` and friends for
 q8_1, `act_i8_pack_host` / `act_i8_to_host` for the per-token int8 form), used by tests and the
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
     L.mmq_gemm_id_workspace_bytes.restype = S
     L.mmq_gemm_id.argtypes = [e, P, I, P, P, I, I, I, I, e, P, P, S, P]
     L.mmq_gemm_id.restype = e
+    L.mmq_gemm_id_noalloc.argtypes = [e, P, I, P, P, I, I, I, I, e, P, P]
+    L.mmq_gemm_id_noalloc.restype = e
+    L.mmq_gemm_id_noalloc_max_workspace_bytes.argtypes = []
+    L.mmq_gemm_id_noalloc_max_workspace_bytes.restype = S
     _lib = L
     return L
 
@@ -187,6 +192,18 @@ def gemm_id(wtype, packed, E: int, act, ids, T: int, top_k: int, N: int, K: int,
     _check("mmq_gemm_id", lib().mmq_gemm_id(_wt(wtype), _ptr(packed), E, _ptr(act), _ptr(ids), T, top_k, N, K,
                                              OTYPE["f32"], _ptr(out), _ptr(workspace), workspace.numel(),
                                              _stream(stream)))
+    return out
+
+
+def gemm_id_noalloc_max_workspace_bytes() -> int:
+    return int(lib().mmq_gemm_id_noalloc_max_workspace_bytes())
+
+
+def gemm_id_noalloc(wtype, packed, E: int, act, ids, T: int, top_k: int, N: int, K: int, out, stream=None):
+    """mmq_gemm_id without a workspace argument: the library's static per-GPU scratch is used.
+    `out` must be given (the call allocates nothing)."""
+    _check("mmq_gemm_id_noalloc", lib().mmq_gemm_id_noalloc(_wt(wtype), _ptr(packed), E, _ptr(act), _ptr(ids), T,
+                                                             top_k, N, K, OTYPE["f32"], _ptr(out), _stream(stream)))
     return out
 
 

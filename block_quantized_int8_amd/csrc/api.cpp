@@ -150,25 +150,51 @@ size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
     return gemm_id_workspace_bytes(E, T, top_k);
 }
 
-mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
-                       const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
-                       mmq_otype o, void* out, void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+// The checks of mmq_gemm_id that do not concern the workspace (MMQ_OK if all pass).
+mmq_status gemm_id_args(mmq_wtype t, const void* packed, int64_t E, const void* act,
+                        const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
+                        mmq_otype o, void* out) {
     if (!valid_wtype(t) || !valid_otype(o) || !sizes_ok(T, N, K) || K % k_multiple(t)) return MMQ_EINVAL;
     if (E < 1 || top_k < 1 || top_k > E || E > 4096 || T * top_k > MAX_DIM) return MMQ_EINVAL;
     if (!packed || !act || !ids || !out) return MMQ_EINVAL;
     if (t == MMQ_I8_ROW || o != MMQ_OUT_F32) return MMQ_EUNSUPPORTED;
-    const size_t need = gemm_id_workspace_bytes(E, T, top_k);
-    if (!workspace || ws_bytes < need) return MMQ_EWORKSPACE;
-    if (!aligned16(packed) || !aligned16(act) || !aligned16(ids) || !aligned16(out) ||
-        !aligned16(workspace))
-        return MMQ_EALIGN;
-    t = kernel_format(t);
-    if (!mmvq_id_ok(t, T, top_k, K)) {          // the prefill gather path (decode batches: the
-        if (!gather_grid_ok(gemm_id_max_units(E, T * top_k), N) || !gather_regions_ok(t, T, N, K))
+    if (!aligned16(packed) || !aligned16(act) || !aligned16(ids) || !aligned16(out)) return MMQ_EALIGN;
+    const mmq_wtype kt = kernel_format(t);
+    if (!mmvq_id_ok(kt, T, top_k, K)) {         // the prefill gather path (decode batches: the
+        if (!gather_grid_ok(gemm_id_max_units(E, T * top_k), N) || !gather_regions_ok(kt, T, N, K))
             return MMQ_EINVAL;                  // small-batch kernel, 64-bit addressing)
     }
-    return from_hip(launch_gemm_id(t, packed, E, act, ids, T, top_k, N, K, out, workspace, ws_bytes,
-                                   as_stream(stream)));
+    return MMQ_OK;
+}
+}  // namespace
+
+mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
+                       const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
+                       mmq_otype o, void* out, void* workspace, size_t ws_bytes, void* stream) {
+    const mmq_status st = gemm_id_args(t, packed, E, act, ids, T, top_k, N, K, o, out);
+    if (st != MMQ_OK) return st;
+    const size_t need = gemm_id_workspace_bytes(E, T, top_k);
+    if (!workspace || ws_bytes < need) return MMQ_EWORKSPACE;
+    if (!aligned16(workspace)) return MMQ_EALIGN;
+    return from_hip(launch_gemm_id(kernel_format(t), packed, E, act, ids, T, top_k, N, K, out, workspace,
+                                   ws_bytes, as_stream(stream)));
+}
+
+size_t mmq_gemm_id_noalloc_max_workspace_bytes(void) { return ID_SCRATCH_BYTES; }
+
+mmq_status mmq_gemm_id_noalloc(mmq_wtype t, const void* packed, int64_t E, const void* act,
+                               const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
+                               mmq_otype o, void* out, void* stream) {
+    const mmq_status st = gemm_id_args(t, packed, E, act, ids, T, top_k, N, K, o, out);
+    if (st != MMQ_OK) return st;
+    const size_t need = gemm_id_workspace_bytes(E, T, top_k);
+    if (need > ID_SCRATCH_BYTES) return MMQ_EWORKSPACE;
+    void* ws = nullptr;
+    const hipError_t e = id_scratch(&ws);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(launch_gemm_id(kernel_format(t), packed, E, act, ids, T, top_k, N, K, out, ws,
+                                   ID_SCRATCH_BYTES, as_stream(stream)));
 }
 
 }  // extern "C"

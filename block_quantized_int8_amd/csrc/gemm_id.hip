@@ -17,10 +17,18 @@
 // unit counts leave at once. With at most 4 tokens (a decode batch, where the gather tiles
 // would be nearly empty) step 2 is the decode kernel instead, over (batch of up to 8 of one
 // expert's pairs, 16-row group) units (gemm_mmvq.hip).
+#include <mutex>
+
 #include "mmq_internal.h"
 
 namespace mmq {
 namespace {
+
+// The allocation-free entry point's workspace: a file-scope device array (one copy per GPU,
+// held until the process ends). Host code never passes `scratch` itself to a kernel (in host
+// code the name is only a stand-in for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[ID_SCRATCH_BYTES];
 
 constexpr int ROUTE_THREADS = 1024;
 constexpr int MAX_E = 4096;
@@ -122,6 +130,26 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __r
 int64_t gemm_id_max_units(int64_t E, int64_t P) {
     const int64_t U = gather_unit_tokens();
     return P / U + (E < P ? E : P);
+}
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+hipError_t id_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* per_device[64] = {nullptr};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (per_device[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 size_t gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {

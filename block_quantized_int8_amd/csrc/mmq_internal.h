@@ -179,4 +179,8 @@ hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void
                           const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
                           void* out, void* workspace, size_t ws_bytes, hipStream_t s);
 size_t gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
+// The allocation-free MUL_MAT_ID's workspace: a static device array of ID_SCRATCH_BYTES per GPU;
+// id_scratch() gives its device address on the current device.
+constexpr size_t ID_SCRATCH_BYTES = size_t(1) << 20;
+hipError_t id_scratch(void** ptr);
 }  // namespace mmq

@@ -226,6 +226,25 @@ mmq_status mmq_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* a
                        const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
                        mmq_otype o, void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* MUL_MAT_ID for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. The same operation, arguments, limits
+ * and kernels as mmq_gemm_id, without the workspace argument: the call allocates nothing and
+ * takes its workspace from a static device array of the library, one per GPU (held until the
+ * process ends), of mmq_gemm_id_noalloc_max_workspace_bytes() bytes (1 MiB).
+ *  - If mmq_gemm_id_workspace_bytes(E, T, top_k) exceeds that size the call returns
+ *    MMQ_EWORKSPACE and enqueues nothing (1 MiB covers e.g. E = 4096 experts with up to
+ *    249,000 (token, slot) pairs).
+ *  - Every call on one GPU shares that GPU's array and leaves its contents behind (the next
+ *    call needs no clearing: every call writes all of the workspace it reads). Calls that
+ *    overlap in time on one GPU (different streams, or different host threads without stream
+ *    ordering between them) race on the array and must not be made. */
+mmq_status mmq_gemm_id_noalloc(mmq_wtype t, const void* packed, int64_t E, const void* act,
+                               const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
+                               mmq_otype o, void* out, void* stream);
+
+/* Size of mmq_gemm_id_noalloc's static workspace, in bytes (host). */
+size_t mmq_gemm_id_noalloc_max_workspace_bytes(void);
+
 /* Static, human-readable name of a status code (host). */
 const char* mmq_status_string(mmq_status s);
 

@@ -244,3 +244,16 @@ def test_size_limits_rejected_before_any_launch(mmq):
     # T * top_k above 2^24
     assert L.mmq_gemm_id(0, G, 8, G, G, 1 << 22, 8, 32, 64, 0, G, G, big, None) == EINVAL
     assert mmq.gemm_id_workspace_bytes(8, 1 << 22, 8) == 0
+
+
+def test_noalloc_gemm_id_refuses_problems_beyond_its_scratch(mmq):
+    """mmq_gemm_id_noalloc takes its workspace from a 1 MiB static array: a problem that needs
+    more is refused with MMQ_EWORKSPACE before anything is enqueued (no device is touched)."""
+    L = mmq.lib()
+    G = ctypes.c_void_p(0x10000)
+    assert mmq.gemm_id_noalloc_max_workspace_bytes() == 1 << 20
+    assert mmq.gemm_id_workspace_bytes(64, 40000, 8) > 1 << 20
+    assert L.mmq_gemm_id_noalloc(3, G, 64, G, G, 40000, 8, 256, 512, 0, G, None) == mmq.MMQ_EWORKSPACE
+    # argument errors come first, as in mmq_gemm_id
+    assert L.mmq_gemm_id_noalloc(3, None, 64, G, G, 512, 8, 256, 512, 0, G, None) == mmq.MMQ_EINVAL
+    assert L.mmq_gemm_id_noalloc(4, G, 64, G, G, 512, 8, 256, 512, 0, G, None) == mmq.MMQ_EUNSUPPORTED
