@@ -10,9 +10,9 @@ The functions mirror include/mmq.h one to one (same names without the `mmq_` pre
     gemm_id_workspace_bytes, gemm_id, gemm_id_noalloc, gemm_id_noalloc_max_workspace_bytes,
     status_string
 
-plus host-side encoders/decoders of the documented act layouts (`act_to_host` and friends for
-q8_1, `act_i8_pack_host` / `act_i8_to_host` for the per-token int8 form), used by tests and the
-bench to fill or read act buffers.
+plus host-side encoders/decoders of the documented act layouts (`act_to_host`,
+`act_q8_1_pack_host` and friends for q8_1, `act_i8_pack_host` / `act_i8_to_host` for the
+per-token int8 form), used by tests and the bench to fill or read act buffers.
 """
 from __future__ import annotations
 
@@ -217,57 +217,89 @@ def _act_dims(M: int, K: int):
 
 
 def _act_regions(act_bytes_host: np.ndarray, M: int, K: int):
-    """All five q8_1 regions, padding included, as row-major arrays: xq int8 [Mp, KBp*32],
-    xs f32 [Mp, KBp], xsum int32 [Mp, KBp], xs2 uint32 [Mp, KBp], xsx f32 [Mp, KBp] (regions 3
-    and 4 are stored tile-major, [MT][KBp][32], and transposed back here)."""
+    """All four q8_1 regions, padding included, as row-major arrays: xq int8 [Mp, KBp*32],
+    xs2 uint32 [Mp, KBp], xsx f32 [Mp, KBp], xg uint32 [Mp, KBp, 2] (the dword of half h of each
+    block; all stored tiled, transposed back here)."""
     o = act_region_offsets("q8_1", M, K)
     Mp, KB, KBp, MT = _act_dims(M, K)
     buf = np.asarray(act_bytes_host, dtype=np.uint8)
     t = buf[o[0]:o[0] + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)   # [mt, b, h, r, 16]
     xq = t.transpose(0, 3, 1, 2, 4).reshape(Mp, KBp * 32)
     cells = Mp * KBp
-    xs = buf[o[1]:o[1] + 4 * cells].view(np.float32).reshape(Mp, KBp)
-    xsum = buf[o[2]:o[2] + 4 * cells].view(np.int32).reshape(Mp, KBp)
     def tile_major(region, dt):
         return buf[region:region + 4 * cells].view(dt).reshape(MT, KBp, 32).transpose(0, 2, 1).reshape(Mp, KBp)
-    xs2 = tile_major(o[3], np.uint32)
-    xsx = tile_major(o[4], np.float32)
-    return xq, xs, xsum, xs2, xsx
+    xs2 = tile_major(o[1], np.uint32)
+    xsx = tile_major(o[2], np.float32)
+    xg = buf[o[3]:o[3] + 8 * cells].view(np.uint32).reshape(MT, KBp, 2, 32).transpose(0, 3, 1, 2).reshape(Mp, KBp, 2)
+    return xq, xs2, xsx, xg
+
+
+def _half_bits(v):
+    return np.asarray(v, np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+
+
+def act_groups_host(act_bytes_host: np.ndarray, M: int, K: int):
+    """Region 3 decoded: the integer 8-value group sums G as int32 [Mp, KBp, 4], padding
+    included (G_j * 2^-13 is stored as f16, so G_j = f16 value * 2^13 exactly)."""
+    _, _, _, xg = _act_regions(act_bytes_host, M, K)
+    g = np.stack([_half_bits(xg & 0xFFFF), _half_bits(xg >> 16)], axis=-1).reshape(xg.shape[0], xg.shape[1], 4)
+    return (g.astype(np.float64) * 8192.0).astype(np.int32)
 
 
 def act_to_host(act_bytes_host: np.ndarray, M: int, K: int):
     """Decode a q8_1 act buffer (copied to host as uint8) into plain row-major
-    (xq int8 [M,K], xs f32 [M,K/32], xsum int32 [M,K/32]) following the documented layout."""
-    xq, xs, xsum, _, _ = _act_regions(act_bytes_host, M, K)
+    (xq int8 [M,K], xs f32 [M,K/32], xsum int32 [M,K/32]) following the documented layout:
+    xs is the low f16 half of region 1, xsum the sum of the four group sums of region 3."""
+    xq, xs2, _, _ = _act_regions(act_bytes_host, M, K)
     KB = K // 32
+    xs = _half_bits(xs2 & 0xFFFF)
+    xsum = act_groups_host(act_bytes_host, M, K).sum(axis=2).astype(np.int32)
     return (np.ascontiguousarray(xq[:M, :K]), np.ascontiguousarray(xs[:M, :KB]),
             np.ascontiguousarray(xsum[:M, :KB]))
 
 
 def act_derived_host(act_bytes_host: np.ndarray, M: int, K: int):
-    """Regions 3 and 4 decoded to f32 [Mp, KBp] each (padding included): the low and high f16
+    """Regions 1 and 2 decoded to f32 [Mp, KBp] each (padding included): the low and high f16
     halves of xs2, and xsx. They must equal xs, xs and xs * xsum exactly."""
-    _, _, _, xs2, xsx = _act_regions(act_bytes_host, M, K)
-    lo = (xs2 & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float32)
-    hi = (xs2 >> 16).astype(np.uint16).view(np.float16).astype(np.float32)
-    return lo, hi, xsx.copy()
-
-
-def act_full_host(act_bytes_host: np.ndarray, M: int, K: int):
-    """Regions 1 and 2 (xs f32, xsum int32) as [Mp, KBp], padding included."""
-    _, xs, xsum, _, _ = _act_regions(act_bytes_host, M, K)
-    return xs.copy(), xsum.copy()
+    _, xs2, xsx, _ = _act_regions(act_bytes_host, M, K)
+    return _half_bits(xs2 & 0xFFFF), _half_bits(xs2 >> 16), xsx.copy()
 
 
 def act_padding_host(act_bytes_host: np.ndarray, M: int, K: int):
     """The padded rows (m >= M) and padded blocks (b >= K/32) of every region of a q8_1 act
     buffer, as one flat array that must be all zero."""
-    xq, xs, xsum, xs2, xsx = _act_regions(act_bytes_host, M, K)
+    xq, xs2, xsx, xg = _act_regions(act_bytes_host, M, K)
     KB = K // 32
     pads = [xq[M:].ravel(), xq[:, K:].ravel()]
-    for r in (xs, xsum, xs2, xsx):
+    for r in (xs2, xsx, xg):
         pads += [r[M:].ravel(), r[:, KB:].ravel()]
     return np.concatenate([p.astype(np.float64) for p in pads])
+
+
+def act_q8_1_pack_host(xq: np.ndarray, xs: np.ndarray) -> np.ndarray:
+    """Encode q8_1 activations (xq int8 [M, K], xs f32 [M, K/32], the f16-exact block scales)
+    into the documented MMQ_ACT_Q8_1 layout (uint8 buffer of act_bytes("q8_1", M, K) bytes);
+    xsum and the group sums are taken from xq."""
+    xq = np.asarray(xq, dtype=np.int8)
+    M, K = xq.shape
+    o = act_region_offsets("q8_1", M, K)
+    Mp, KB, KBp, MT = _act_dims(M, K)
+    buf = np.zeros(act_bytes("q8_1", M, K), np.uint8)
+    full = np.zeros((Mp, KBp * 32), np.int8)
+    full[:M, :K] = xq
+    buf[o[0]:o[0] + MT * KBp * 1024] = full.reshape(MT, 32, KBp, 2, 16).transpose(0, 2, 3, 1, 4).reshape(-1).view(np.uint8)
+    g = full.reshape(Mp, KBp, 4, 8).astype(np.int64).sum(axis=3)                      # [Mp, KBp, 4]
+    s = np.zeros((Mp, KBp), np.float32)
+    s[:M, :KB] = xs
+    h = s.astype(np.float16).view(np.uint16).astype(np.uint32)
+    def tm(a):
+        return a.reshape(MT, 32, KBp).transpose(0, 2, 1).reshape(-1)
+    buf[o[1]:o[1] + 4 * Mp * KBp] = tm(h | (h << 16)).view(np.uint8)
+    buf[o[2]:o[2] + 4 * Mp * KBp] = tm((s * g.sum(axis=2).astype(np.float32)).astype(np.float32)).view(np.uint8)
+    gh = (g.astype(np.float32) * np.float32(2.0 ** -13)).astype(np.float16).view(np.uint16).astype(np.uint32)
+    pair = gh[..., 0::2] | (gh[..., 1::2] << 16)                                      # [Mp, KBp, 2 halves]
+    buf[o[3]:o[3] + 8 * Mp * KBp] = pair.reshape(MT, 32, KBp, 2).transpose(0, 2, 3, 1).reshape(-1).view(np.uint8)
+    return buf
 
 
 def act_i8_pack_host(a: np.ndarray, sa: np.ndarray) -> np.ndarray:

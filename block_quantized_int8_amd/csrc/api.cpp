@@ -82,10 +82,10 @@ mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offs
     if (a == MMQ_ACT_Q8_1) {
         const ActQ81Layout L = act_q8_1_layout(M, K);
         offsets[0] = (size_t)L.xq_off;
-        offsets[1] = (size_t)L.xs_off;
-        offsets[2] = (size_t)L.xsum_off;
-        offsets[3] = (size_t)L.xs2_off;
-        offsets[4] = (size_t)L.xsx_off;
+        offsets[1] = (size_t)L.xs2_off;
+        offsets[2] = (size_t)L.xsx_off;
+        offsets[3] = (size_t)L.xg_off;
+        offsets[4] = 0;
     } else {
         const ActI8Layout L = act_i8_layout(M, K);
         offsets[0] = (size_t)L.a_off;

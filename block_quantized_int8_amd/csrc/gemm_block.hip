@@ -33,10 +33,16 @@
 //     int8 MFMA over the fragment with the other half's lanes zeroed (lanes 0-31 carry values
 //     0-15, lanes 32-63 values 16-31), its own scale product S_h = 2 (d*sc_h) xs from the exact
 //     f16 split hi + lo = d*sc_h, its own conversion, and both FMA into the same accumulator.
-//   iq1t: the IQ1_M fold (llama.cpp PR #304) turns each value into the integer 8g +- 1 with a
-//     per-16 factor (2s+1) and a per-block scale d/8. (2s+1)*v = 2s*v + v with |2s*v| <= 126,
-//     so two chained int8 MFMAs over [2s*v] and [v] (same token operand) give the folded
-//     per-32 integer sum_h (2s_h+1)*P16_h exactly, and only d remains as a scale.
+//   iq1t: the IQ1_M fold (llama.cpp PR #304) turns each value into the integer
+//     (2s+1)(8g + sigma) with a per-block scale d/8 (s per 16 values, sigma = +-1 per 8). Split
+//     it as 8(2s+1)g + (2s+1)sigma: the first part (|.| <= 120) is the int8 operand of the one
+//     int8 MFMA; the second is constant over each 8-value group j, so its dot with the tokens
+//     is sum_j c_j G_j with c_j = (2s+1)sigma_j and G_j the tokens' integer group sums (act
+//     region 3). That rank-4 term rides in the conversion MFMA's spare k-slots: -c is written
+//     there as two exact f16 products (1303 * 2^-13 + 21 * 311 * 2^-26) and the four products
+//     c_j 2^-13 * G_j 2^-13 fill the others, so X = (P + sum_j c_j G_j) 2^-26 exactly - the
+//     folded per-32 integer sum_h (2s_h+1) P16_h - from three matrix-core ops per tile and
+//     block (int8 dot, scale, conversion), and only d remains as a scale.
 //
 // Operands reach LDS by direct global->LDS DMA (global_load_lds_dwordx4: each lane names its
 // own 16-byte source, the wave writes 1 KB of LDS), double-buffered per 4-block stage: stage
@@ -75,6 +81,7 @@ template <> struct BT<MMQ_Q8_0> {
     static constexpr int SHIFT = 0;        // the MFMA computes P << SHIFT
     static constexpr bool MIN = false;     // q4_K min term
     static constexpr bool DUAL = false;    // q6_K: two half-block dots per block
+    static constexpr bool GSUM = false;    // iq1t: group-sum term in the conversion MFMA
     static constexpr float POST = UNBIAS / 2;   // S = 2 wd xs
     struct Raw { v4i x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -94,6 +101,7 @@ template <> struct BT<MMQ_Q4_0> {
     static constexpr int SHIFT = 4;
     static constexpr bool MIN = false;
     static constexpr bool DUAL = false;
+    static constexpr bool GSUM = false;
     static constexpr float POST = UNBIAS / 32;  // 16x block dot, S = 2 wd xs
     struct Raw { uint2 x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -116,6 +124,7 @@ template <> struct BT<MMQ_Q4_K> {
     static constexpr int SHIFT = 0;
     static constexpr bool MIN = true;
     static constexpr bool DUAL = false;
+    static constexpr bool GSUM = false;
     static constexpr float POST = UNBIAS / 2;
     struct Raw { uint2 x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -132,50 +141,43 @@ template <> struct BT<MMQ_Q4_K> {
 };
 
 // iq1t lane data: one dword of 2-bit codes (value 4q+b at bits 8b+2q); the lane's meta byte
-// s | sigma0 << 3 | sigma1 << 4 sits in its row's scale dword (byte 2 + half). The table entry
-// for a meta byte holds four byte-LUTs indexed by the code: v = 8(c-1) + sigma for both sign
-// groups, and 2s*v for both. v_perm picks the bytes: selectors 0..2 address the first group's
-// LUT, 4..6 the second's.
+// m = s | sigma_a << 3 | sigma_b << 4 (its 16-value half: the sub-scale and the signs of its two
+// 8-value groups) sits in its row's scale dword (byte 2 + half). Table entry m (8 bytes):
+//   word 0: the int8 values 8(2s+1)(c-1) for the codes c = 0, 1, 2 (bytes 0-2), which v_perm
+//           picks by code (selectors 0..2);
+//   word 1: the f16 pair (c_a 2^-13, c_b 2^-13), c = (2s+1)(sigma ? -1 : 1): the lane's two
+//           conversion-MFMA k-slots of the group-sum term.
 template <> struct BT<MMQ_IQ1T> {
     static constexpr int FB = 256;
-    static constexpr int NMF = 2;
+    static constexpr int NMF = 1;
     static constexpr int SHIFT = 0;
     static constexpr bool MIN = false;
     static constexpr bool DUAL = false;
+    static constexpr bool GSUM = true;
     static constexpr float POST = UNBIAS / 16;  // scale d/8, S = 2 d xs
-    struct Raw { uint32_t C; v4i t; };
+    static constexpr int TAB_WORDS = 64;        // 32 entries x 2 words
+    struct Raw { uint32_t C; uint2 t; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
         r.C = *reinterpret_cast<const uint32_t*>(frag + lane * 4);
     }
     __device__ static void mid(Raw& r, uint32_t wsd, int lane, const uint8_t* tab) {
-        const uint32_t meta = (wsd >> (16 + 8 * (lane >> 5))) & 0xFFu;
-        r.t = *reinterpret_cast<const v4i*>(tab + meta * 16);     // v0, v1, 2s*v0, 2s*v1
+        const uint32_t meta = (wsd >> (16 + 8 * (lane >> 5))) & 0x1Fu;
+        r.t = *reinterpret_cast<const uint2*>(tab + meta * 8);
     }
     __device__ static void unpack(const Raw& r, v4i* a, int) {
-        const uint32_t C = r.C;
-        const v4i t = r.t;
-        const uint32_t s0 = C & 0x03030303u;
-        const uint32_t s1 = (C >> 2) & 0x03030303u;
-        const uint32_t s2 = ((C >> 4) & 0x03030303u) | 0x04040404u;
-        const uint32_t s3 = ((C >> 6) & 0x03030303u) | 0x04040404u;
-        a[0][0] = (int)__builtin_amdgcn_perm((uint32_t)t[3], (uint32_t)t[2], s0);
-        a[0][1] = (int)__builtin_amdgcn_perm((uint32_t)t[3], (uint32_t)t[2], s1);
-        a[0][2] = (int)__builtin_amdgcn_perm((uint32_t)t[3], (uint32_t)t[2], s2);
-        a[0][3] = (int)__builtin_amdgcn_perm((uint32_t)t[3], (uint32_t)t[2], s3);
-        a[1][0] = (int)__builtin_amdgcn_perm((uint32_t)t[1], (uint32_t)t[0], s0);
-        a[1][1] = (int)__builtin_amdgcn_perm((uint32_t)t[1], (uint32_t)t[0], s1);
-        a[1][2] = (int)__builtin_amdgcn_perm((uint32_t)t[1], (uint32_t)t[0], s2);
-        a[1][3] = (int)__builtin_amdgcn_perm((uint32_t)t[1], (uint32_t)t[0], s3);
+        const uint32_t C = r.C, lut = r.t.x;
+        a[0][0] = (int)__builtin_amdgcn_perm(lut, lut, C & 0x03030303u);
+        a[0][1] = (int)__builtin_amdgcn_perm(lut, lut, (C >> 2) & 0x03030303u);
+        a[0][2] = (int)__builtin_amdgcn_perm(lut, lut, (C >> 4) & 0x03030303u);
+        a[0][3] = (int)__builtin_amdgcn_perm(lut, lut, (C >> 6) & 0x03030303u);
     }
     __device__ static uint32_t scale_op(uint32_t w) { return w & 0xFFFFu; }   // f16 d only
-    // table entry e (meta byte) word w: w=0,1: LUT of v for sign group 0/1; w=2,3: LUT of 2s*v
     __device__ static uint32_t table_word(int e, int w) {
-        const int s = e & 7;
-        const int sig = ((w & 1) ? (e >> 4) : (e >> 3)) & 1;
-        const int d = sig ? -1 : 1;
-        const int mul = (w >= 2) ? 2 * s : 1;
-        const int b0 = (-8 + d) * mul, b1 = d * mul, b2 = (8 + d) * mul;
-        return (uint32_t)(b0 & 0xFF) | ((uint32_t)(b1 & 0xFF) << 8) | ((uint32_t)(b2 & 0xFF) << 16);
+        const int s = e & 7, k = 2 * s + 1;
+        if (w == 0) return (uint32_t)((-8 * k) & 0xFF) | ((uint32_t)(8 * k) << 16);
+        const uint32_t mag = __builtin_bit_cast(uint16_t, (_Float16)((float)k * 0.0001220703125f));
+        const uint32_t ca = mag | (((e >> 3) & 1) ? 0x8000u : 0u), cb = mag | (((e >> 4) & 1) ? 0x8000u : 0u);
+        return ca | (cb << 16);
     }
 };
 
@@ -189,6 +191,7 @@ template <> struct BT<MMQ_Q6_K> {
     static constexpr int SHIFT = 0;
     static constexpr bool MIN = false;
     static constexpr bool DUAL = true;
+    static constexpr bool GSUM = false;
     static constexpr float POST = UNBIAS / 2;   // S_h = 2 (d*sc_h) xs
     struct Raw { v4i x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -233,25 +236,30 @@ struct Cfg {
     // second weight-side scale region: q4_K's -dmin*m, q6_K's half-1 scale dwords
     static constexpr bool W2 = T::MIN || T::DUAL;
     static constexpr int C_WM = W2 ? C_WS : 0, C_XM = T::MIN ? C_XS : 0;
+    // iq1t: the tokens' group-sum dwords, [TM][KS][64 lanes] (256 bytes per tile and block): a
+    // 1 KB chunk per token tile and stage, or (gathered rows) a 4-byte-per-lane chunk per tile
+    // and block
+    static constexpr int C_XG = T::GSUM ? (GATHER ? TM * KS : TM) : 0;
     static constexpr int RW = C_WS * 2 * SCB, RX = (TM + 1) / 2 * 2 * SCB;   // region bytes
     static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + RW;
     static constexpr int O_WM = O_XS + RX, O_XM = O_WM + (W2 ? RW : 0);
-    static constexpr int BUF = O_XM + (T::MIN ? RX : 0);
+    static constexpr int O_XG = O_XM + (T::MIN ? RX : 0);
+    static constexpr int BUF = O_XG + (T::GSUM ? TM * KS * 256 : 0);
     static constexpr int C_FR = C_WF + C_XF;
-    static constexpr int C_SC = C_WS + C_XS + C_WM + C_XM;
+    static constexpr int C_SC = C_WS + C_XS + C_WM + C_XM + C_XG;
     static constexpr int C_ALL = C_FR + (C_SC + NW - 1) / NW * NW;
     static constexpr int CPW = C_ALL / NW;                  // chunks per wave per stage
     static_assert(WF % 1024 == 0, "weight fragments of a stage must be whole 1 KB chunks");
     static_assert(C_WF % NW == 0 && C_XF % NW == 0, "fragment chunks must split evenly over the waves");
     static_assert(KS % 2 == 0, "gathered scale chunks cover two blocks");
     enum { K_WF = 0, K_XF = 1, K_SC = 2 };                      // slot kinds
-    enum { S_WS = 0, S_XS = 1, S_WM = 2, S_XM = 3, S_NONE = 4 };  // scale chunk kinds
+    enum { S_WS = 0, S_XS = 1, S_WM = 2, S_XM = 3, S_XG = 4, S_NONE = 5 };  // scale chunk kinds
     __host__ __device__ static constexpr int slot_kind(int j) {
         return j * NW < C_WF ? K_WF : j * NW < C_FR ? K_XF : K_SC;
     }
     __host__ __device__ static constexpr int scale_kind(int ci) {
         return ci < C_WS ? S_WS : (ci -= C_WS) < C_XS ? S_XS : (ci -= C_XS) < C_WM ? S_WM
-             : (ci -= C_WM) < C_XM ? S_XM : S_NONE;
+             : (ci -= C_WM) < C_XM ? S_XM : (ci -= C_XM) < C_XG ? S_XG : S_NONE;
     }
     // LDS byte offset of the scale dword of (tile i, row r, block kb) in a region at `base`
     __host__ __device__ static constexpr int sc(int base, int i, int r, int kb) {
@@ -265,8 +273,9 @@ struct BlockArgs {
     int64_t w_min_off;
     int64_t w_stride;           // bytes between experts' packed matrices (gather mode)
     const uint8_t* xq;          // act region 0 (tiled int8)
-    const uint32_t* xs2;        // act region 3 (xs as an f16 pair)
-    const float* xsx;           // act region 4 (xs * xsum)
+    const uint32_t* xs2;        // act region 1 (xs as an f16 pair)
+    const float* xsx;           // act region 2 (xs * xsum)
+    const uint32_t* xg;         // act region 3 (group sums as f16 pairs)
     int M, N, KB, KBp, NT, MT, tiles_m;
     float* out;
     int64_t ldo;
@@ -358,7 +367,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     };
 
     if constexpr (FMT == MMQ_IQ1T) {
-        if (tid < 128) reinterpret_cast<uint32_t*>(tab)[tid] = T::table_word(tid >> 2, tid & 3);
+        if (tid < T::TAB_WORDS) reinterpret_cast<uint32_t*>(tab)[tid] = T::table_word(tid >> 1, tid & 1);
     }
 
     // ---- DMA plan: per chunk this lane keeps a 32-bit source offset from the chunk's region
@@ -399,6 +408,19 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
                 const int nt = min(nt_base + 2 * pr + h, NT - 1);
                 goff[j] = (uint32_t)(nt * KBp * 128 + r32 * 16);
                 ldso[j] = (sk == C::S_WS ? C::O_WS : C::O_WM) + pr * 1024;
+            } else if (sk == C::S_XG) {
+                const int x = ci - (C::C_WS + C::C_XS + C::C_WM + C::C_XM);
+                if constexpr (is_gather(MODE)) {
+                    // (tile i, block kb): lane (h, r) fetches the dword of half h of its row
+                    const int i = x / KS, kb = x % KS;
+                    const int m = src_token(i, r32);
+                    goff[j] = (uint32_t)((((m >> 5) * KBp + kb) * 64 + h * 32 + (m & 31)) * 4);
+                    ldso[j] = C::O_XG + (i * KS + kb) * 256;
+                } else {
+                    const int mt = min(mt_base + x, args.MT - 1);
+                    goff[j] = (uint32_t)(mt * KBp * 256 + lane * 16);
+                    ldso[j] = C::O_XG + x * 1024;
+                }
             } else if (sk == C::S_XS || sk == C::S_XM) {
                 const int x = ci - (sk == C::S_XS ? C::C_WS : C::C_WS + C::C_XS + C::C_WM);
                 const int base = sk == C::S_XS ? C::O_XS : C::O_XM;
@@ -429,10 +451,11 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
             const int sk = skind[j];
             if (sk == C::S_NONE) return;
             const uint8_t* base = sk == C::S_WS ? wsc : sk == C::S_XS ? reinterpret_cast<const uint8_t*>(args.xs2)
-                                : sk == C::S_WM ? wmn : reinterpret_cast<const uint8_t*>(args.xsx);
-            if (is_gather(MODE) && (sk == C::S_XS || sk == C::S_XM)) dma4(base + goff[j], dst);
+                                : sk == C::S_WM ? wmn : sk == C::S_XM ? reinterpret_cast<const uint8_t*>(args.xsx)
+                                : reinterpret_cast<const uint8_t*>(args.xg);
+            if (is_gather(MODE) && (sk == C::S_XS || sk == C::S_XM || sk == C::S_XG)) dma4(base + goff[j], dst);
             else dma16(base + goff[j], dst);
-            goff[j] += C::SCB;
+            goff[j] += sk == C::S_XG ? KS * 256 : C::SCB;
         }
     };
     auto issue_stage = [&](uint8_t* buf) __attribute__((always_inline)) {
@@ -463,7 +486,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     struct Raw {
         typename T::Raw w[RT];
         v4i b[CT];
-        uint32_t wsd[RT], wsd2[RT], xs[CT];
+        uint32_t wsd[RT], wsd2[RT], xs[CT], gx[CT];
     };
     // The f16 scale MFMA takes (scale, 0) register pairs. In the dense 128 x 128 kernels the
     // operand buffers live for the whole K loop and only the scale halves are rewritten, so no
@@ -477,6 +500,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         v4i a[RT][T::NMF];
         v4i b[CT];
         SOp ws[RT], ws2[RT], xs[CT];
+        uint32_t cw[RT], gx[CT];               // iq1t: conversion k-slot pairs (weights, tokens)
     };
     auto set_lo = [](SOp& p, uint32_t v) __attribute__((always_inline)) {
         if constexpr (CARRY) p.x = (int)v;
@@ -499,6 +523,8 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
             const int j = wm * CT + ct;
             R.b[ct] = *reinterpret_cast<const v4i*>(cur + C::O_XF + (j * KS + kb) * 1024 + lane * 16);
             R.xs[ct] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_XS, j, r32, kb));
+            if constexpr (T::GSUM)
+                R.gx[ct] = *reinterpret_cast<const uint32_t*>(cur + C::O_XG + ((j * KS + kb) * 64 + lane) * 4);
         }
     };
     auto mid = [&](Raw& R) __attribute__((always_inline)) {
@@ -509,6 +535,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             T::unpack(R.w[rt], o.a[rt], hmask);
+            if constexpr (T::GSUM) o.cw[rt] = R.w[rt].t.y;
             set_lo(o.ws[rt], T::scale_op(R.wsd[rt]));
             if constexpr (T::DUAL) set_lo(o.ws2[rt], T::scale_op(R.wsd2[rt]));
         }
@@ -516,6 +543,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         for (int ct = 0; ct < CT; ++ct) {
             o.b[ct] = R.b[ct];
             set_lo(o.xs[ct], R.xs[ct]);
+            if constexpr (T::GSUM) o.gx[ct] = R.gx[ct];
         }
     };
     auto load_ops = [&](const uint8_t* cur, int kb, Ops& o) __attribute__((always_inline)) {
@@ -547,9 +575,20 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     // order the matrix core adds in.
     const v2i cAi = {lane < 32 ? (int)0xA7C8A510u : 0, lane < 32 ? (int)0x0000A418u : 0};
     const v2i cBi = {(int)0x28004800u, (int)0x00000800u};
-    auto unbias_m = [&](const v16i& D) __attribute__((always_inline)) -> v16f {
-        return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, cAi), __builtin_bit_cast(h4, cBi),
-                                                    __builtin_bit_cast(v16f, D), 0, 0, 0);
+    // iq1t: k-slots 0-1 (low half-wave) and 4-5 (high half-wave) carry the lane's group-sum
+    // pairs c_j 2^-13 x G_j 2^-13; slots 2-3 of the low half carry -c = -(1303 * 2^-10) * 2^-3
+    // - (21 * 2^-13) * (311 * 2^-13) (f16 0xBD17 x 0x3000, 0x9940 x 0x28DC); 6-7 are zero.
+    const uint32_t gA1 = lane < 32 ? 0x9940BD17u : 0u, gB1 = lane < 32 ? 0x28DC3000u : 0u;
+    auto unbias_m = [&](const v16i& D, const Ops& o, int t) __attribute__((always_inline)) -> v16f {
+        if constexpr (T::GSUM) {
+            const int tt = t / NH, rt = tt / CT, ct = tt % CT;
+            const v2i ga = {(int)o.cw[rt], (int)gA1}, gb = {(int)o.gx[ct], (int)gB1};
+            return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, ga), __builtin_bit_cast(h4, gb),
+                                                        __builtin_bit_cast(v16f, D), 0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, cAi), __builtin_bit_cast(h4, cBi),
+                                                        __builtin_bit_cast(v16f, D), 0, 0, 0);
+        }
     };
     // D -> X = D - c, in place: 16 independent subtractions. (The whole vector is
     // reinterpreted at once: hipcc's __builtin_bit_cast of a single vector element reads element
@@ -568,16 +607,26 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     };
     // partials mode: the exact int32 dots of block kbg go straight to memory
     // (q6_K: the dot of half hf of block kbg goes to index 2 kbg + hf of 2 KB per (m, n))
-    auto store_partials = [&](int kbg, int t, const v16i& D) __attribute__((always_inline)) {
+    // (iq1t: the dot of the int8 MFMA lacks the group-sum term, so the folded integer is taken
+    // from the conversion's exact X = I * 2^-26 instead)
+    auto store_partials = [&](int kbg, int t, const v16i& D, const Ops& o) __attribute__((always_inline)) {
         const int tt = t / NH, hf = t % NH, rt = tt / CT, ct = tt % CT;
         const int m = (mt_base + wm * CT + ct) * 32 + r32;
+        v16i I;
+        if constexpr (T::GSUM) {
+            const v16f X = unbias_m(D, o, t);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) I[r] = (int)(X[r] * UNBIAS);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) I[r] = (D[r] - MAGIC_I) >> T::SHIFT;
+        }
         if (kbg < args.KB && m < args.M) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int n = (nt_base + wn * RT + rt) * 32 + acc_row(lane, r);
                 if (n < args.N)
-                    args.partials[((int64_t)m * args.pld + n) * (NH * args.KB) + NH * kbg + hf] =
-                        (D[r] - MAGIC_I) >> T::SHIFT;
+                    args.partials[((int64_t)m * args.pld + n) * (NH * args.KB) + NH * kbg + hf] = I[r];
             }
         }
     };
@@ -627,9 +676,9 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         v16i Dc;
         v16f Sc, Xc;
         Dc = mfma_dots(op[0], 0);
-        if constexpr (MODE == DENSE_PARTIALS) store_partials(s * KS, 0, Dc);
+        if constexpr (MODE == DENSE_PARTIALS) store_partials(s * KS, 0, Dc, op[0]);
         else Sc = mfma_scale(op[0], 0);
-        if constexpr (XM && MODE != DENSE_PARTIALS) Xc = unbias_m(Dc);
+        if constexpr (XM && MODE != DENSE_PARTIALS) Xc = unbias_m(Dc, op[0], 0);
 #pragma unroll
         for (int kb = 0; kb < KS; ++kb) {
 #pragma unroll
@@ -649,7 +698,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
                     if (t == NT_ - 1) unpack(raw, op[(kb + 1) & 1]);
                 }
                 if constexpr (MODE == DENSE_PARTIALS) {
-                    if (more) store_partials(s * KS + kn, tn, mfma_dots(op[kn & 1], tn));
+                    if (more) store_partials(s * KS + kn, tn, mfma_dots(op[kn & 1], tn), op[kn & 1]);
                 } else {
                     v16i Dn;
                     v16f Sn;
@@ -668,7 +717,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
                         if (more) Sn = mfma_scale(op[kn & 1], tn);
                         fma_tile(t, Xc, Sc, 6, 11);
                         __builtin_amdgcn_sched_barrier(0);
-                        if (more) Xn = unbias_m(Dn);
+                        if (more) Xn = unbias_m(Dn, op[kn & 1], tn);
                         fma_tile(t, Xc, Sc, 11, 16);
                         __builtin_amdgcn_sched_barrier(0);
                         Xc = Xn;
@@ -753,7 +802,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     using C = Cfg<FMT, WN, WM, RT, CT, is_gather(MODE)>;
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::BUF];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 512 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 256 : 16];
     block_body<FMT, WN, WM, RT, CT, MODE, XM>(args, buf0, buf1, tab, (int)blockIdx.x, (int)gridDim.x);
 }
 
@@ -768,7 +817,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_gather_kernel(BlockArgs f
     constexpr int BUF = CF::BUF > CTl::BUF ? CF::BUF : CTl::BUF;
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 512 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 256 : 16];
     const int b = (int)blockIdx.x;
     if (b < nfull) block_body<FMT, WN, WM, RT, CT, GATHER_F32, XM>(full, buf0, buf1, tab, b, nfull);
     else block_body<FMT, WN, WM, RT, TCT, GATHER_TAIL, XM>(tail, buf0, buf1, tab, b - nfull, (int)gridDim.x - nfull);
@@ -806,6 +855,7 @@ BlockArgs dense_args(const void* packed, const void* act, int64_t M, int64_t N, 
     g.xq = ab + A.xq_off;
     g.xs2 = reinterpret_cast<const uint32_t*>(ab + A.xs2_off);
     g.xsx = reinterpret_cast<const float*>(ab + A.xsx_off);
+    g.xg = reinterpret_cast<const uint32_t*>(ab + A.xg_off);
     g.M = (int)M;
     g.N = (int)N;
     g.KB = (int)A.KB;
@@ -869,6 +919,7 @@ hipError_t launch_dense_split(const BlockArgs& g0, int64_t M, int64_t N, mmq_oty
             g.xq = g0.xq + mt0 * g0.KBp * 1024;
             g.xs2 = g0.xs2 + mt0 * g0.KBp * 32;
             g.xsx = g0.xsx + mt0 * g0.KBp * 32;
+            g.xg = g0.xg + mt0 * g0.KBp * 64;
             g.M = (int)Mc;
             g.N = (int)Nc;
             g.NT = (int)NTc;

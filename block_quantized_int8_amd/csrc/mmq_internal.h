@@ -22,18 +22,19 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 // MMQ_ACT_Q8_1 (see mmq.h):
 //   region 0 xq   int8, tiled [Mp/32][KBp][64 lanes][16 B]: lane L = h*32 + r holds row r's
 //                 values 16h..16h+15 of the block (the B operand of v_mfma_i32_32x32x32_i8)
-//   region 1 xs   f32   [Mp][KBp]   (row-major)
-//   region 2 xsum int32 [Mp][KBp]
-//   region 3 xs2  u32   tile-major [MT][KBp][32]: xs as f16 bits in both halves (the
-//                 scale-MFMA operand)
-//   region 4 xsx  f32   tile-major [MT][KBp][32]: xs * xsum, exact in f32 (the Q4_K min-term
+//   region 1 xs2  u32   tile-major [MT][KBp][32]: xs as f16 bits in both halves (the scale-MFMA
 //                 operand)
-// The GEMM's own operands (regions 3 and 4) are tile-major so that a stage of a 32-row tile is
-// one contiguous 512-byte run (the global->LDS DMA's cost is per cache line touched); a
-// gathered (MUL_MAT_ID) token row reads one dword per block.
+//   region 2 xsx  f32   tile-major [MT][KBp][32]: xs * xsum, exact in f32 (the Q4_K min-term
+//                 operand)
+//   region 3 xg   u32   tiled [MT][KBp][64 lanes]: lane L = h*32 + r holds the f16 pair
+//                 (G_2h * 2^-13, G_2h+1 * 2^-13), G_j the integer sum of row r's 8-value group
+//                 j of the block (the IQ1 formats' sign term; xsum = G_0 + G_1 + G_2 + G_3)
+// Every region is tile-major so that a stage of a 32-row tile is one contiguous run (the
+// global->LDS DMA's cost is per cache line touched) and every quantiser store is a whole line;
+// a gathered (MUL_MAT_ID) token row reads one dword per block and region.
 struct ActQ81Layout {
     int64_t Mp, MT, KB, KBp;
-    int64_t xq_off, xs_off, xsum_off, xs2_off, xsx_off, bytes;
+    int64_t xq_off, xs2_off, xsx_off, xg_off, bytes;
 };
 
 inline ActQ81Layout act_q8_1_layout(int64_t M, int64_t K) {
@@ -44,11 +45,10 @@ inline ActQ81Layout act_q8_1_layout(int64_t M, int64_t K) {
     L.KBp = round_up(L.KB, KB_ALIGN);
     const int64_t cells = L.Mp * L.KBp;          // (row, block) entries of a scale region
     L.xq_off = 0;
-    L.xs_off = round_up(L.MT * L.KBp * 1024, REGION_ALIGN);
-    L.xsum_off = L.xs_off + round_up(cells * 4, REGION_ALIGN);
-    L.xs2_off = L.xsum_off + round_up(cells * 4, REGION_ALIGN);
+    L.xs2_off = round_up(L.MT * L.KBp * 1024, REGION_ALIGN);
     L.xsx_off = L.xs2_off + round_up(cells * 4, REGION_ALIGN);
-    L.bytes = L.xsx_off + round_up(cells * 4, REGION_ALIGN);
+    L.xg_off = L.xsx_off + round_up(cells * 4, REGION_ALIGN);
+    L.bytes = L.xg_off + round_up(cells * 8, REGION_ALIGN);
     return L;
 }
 

@@ -12,11 +12,11 @@
 // the next one before it quantises and stores the current one, so loads and stores overlap
 // (with one unit per wave the whole grid would load, then store, in lockstep). In a unit, lane
 // L = h*32 + r owns row r's values 16h..16h+15 of each block - exactly the 16 bytes it writes
-// to the tiled xq layout, so every block's 1 KB tile is one contiguous wave store. The two
-// lanes of a block (r and r+32) combine their half-block max and sum with one cross-half
-// exchange. Lane h = 0 writes the row's xs and xsum pairs (row-major: one 8-byte store each),
-// lane h = 1 the derived xs2 (f16 pair) and xsx = xs * xsum (exact in f32: an 11-bit
-// significand times a |sum| <= 32*128; tile-major, the wave's 32 rows one 128-byte line).
+// to the tiled xq layout and the two 8-value groups whose sums it writes to xg, so every
+// block's 1 KB of xq and 256 B of xg are contiguous wave stores. The two lanes of a block (r
+// and r+32) combine their half-block max and sum with one cross-half exchange. Lanes h = 0
+// write the block's xs2 (f16 pair), lanes h = 1 its xsx = xs * xsum (exact in f32: an 11-bit
+// significand times a |sum| <= 32*128), each a tile-major 128-byte line per block.
 #include <algorithm>
 
 #include "mmq_internal.h"
@@ -42,10 +42,15 @@ __device__ inline int q_of(float x, float di) {
     return (int)fminf(fmaxf(__builtin_rintf(x * di), -128.f), 127.f);
 }
 
+// an integer group sum |g| <= 1024 as the f16 bits of g * 2^-13 (exact: normal, 11 bits)
+__device__ inline uint32_t group_half(int g) {
+    return __builtin_bit_cast(uint16_t, (_Float16)((float)g * 0.0001220703125f));
+}
+
 __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
     const float* __restrict__ x, int64_t M, int64_t KB, int64_t ldx, int64_t KBp, int64_t units,
-    int8_t* __restrict__ xq, float* __restrict__ xs, int32_t* __restrict__ xsum,
-    uint32_t* __restrict__ xs2, float* __restrict__ xsx) {
+    int8_t* __restrict__ xq, uint32_t* __restrict__ xs2, float* __restrict__ xsx,
+    uint32_t* __restrict__ xg) {
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * QWAVES;
     int64_t u = (int64_t)blockIdx.x * QWAVES + (threadIdx.x >> 6);
@@ -80,30 +85,30 @@ __global__ __launch_bounds__(QWAVES * 64) void quantize_q8_1_kernel(
             const float d = amax / 127.0f;
             const float di = inverse_scale(d);
             uint32_t w[4];
-            int sum = 0;
+            int gs[2] = {0, 0};                  // the lane's two 8-value groups
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int a = q_of(v[i][c].x, di), b = q_of(v[i][c].y, di);
                 const int e = q_of(v[i][c].z, di), f = q_of(v[i][c].w, di);
-                sum += a + b + e + f;
+                gs[c >> 1] += a + b + e + f;
                 w[c] = pack4(a, b, e, f);
             }
+            int sum = gs[0] + gs[1];
             sum += __shfl_xor(sum, 32);
-            *reinterpret_cast<uint4*>(xq + ((mt * KBp + kb0 + i) * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            const int64_t blk = (mt * KBp + kb0 + i) * 64 + lane;
+            *reinterpret_cast<uint4*>(xq + blk * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            xg[blk] = group_half(gs[0]) | (group_half(gs[1]) << 16);
             s_xs[i] = (float)(_Float16)d;
             s_sum[i] = sum;
         }
-        if (h == 0) {
-            const int64_t row = (mt * 32 + r) * KBp + kb0;
-            *reinterpret_cast<float2*>(xs + row) = make_float2(s_xs[0], s_xs[1]);
-            *reinterpret_cast<int2*>(xsum + row) = make_int2(s_sum[0], s_sum[1]);
-        } else {
-            // tile-major [MT][KBp][32]: the 32 rows of a block are one 128-byte line
+        // tile-major [MT][KBp][32]: the 32 rows of a block are one 128-byte line
 #pragma unroll
-            for (int i = 0; i < QG; ++i) {
-                const int64_t tix = (mt * KBp + kb0 + i) * 32 + r;
+        for (int i = 0; i < QG; ++i) {
+            const int64_t tix = (mt * KBp + kb0 + i) * 32 + r;
+            if (h == 0) {
                 const uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)s_xs[i]);
                 xs2[tix] = b | (b << 16);
+            } else {
                 xsx[tix] = s_xs[i] * (float)s_sum[i];
             }
         }
@@ -181,10 +186,9 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ld
     const dim3 grid((unsigned)std::min<int64_t>(ceil_div(units, QWAVES), QBLOCKS));
     hipLaunchKernelGGL(quantize_q8_1_kernel, grid, dim3(QWAVES * 64), 0, s, x, M, L.KB, ldx, L.KBp,
                        units, reinterpret_cast<int8_t*>(base + L.xq_off),
-                       reinterpret_cast<float*>(base + L.xs_off),
-                       reinterpret_cast<int32_t*>(base + L.xsum_off),
                        reinterpret_cast<uint32_t*>(base + L.xs2_off),
-                       reinterpret_cast<float*>(base + L.xsx_off));
+                       reinterpret_cast<float*>(base + L.xsx_off),
+                       reinterpret_cast<uint32_t*>(base + L.xg_off));
     return hipGetLastError();
 }
 

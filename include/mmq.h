@@ -117,17 +117,18 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
  * Activation buffer ("act"). Opaque to most callers, but its layout is fixed so that other
  * producers can fill it. Let Mp = M rounded up to 32, KB = K/32, KBp = KB rounded up to 8.
  *
- * MMQ_ACT_Q8_1 (five regions, each starting on a 256-byte boundary):
+ * MMQ_ACT_Q8_1 (four regions, each starting on a 256-byte boundary):
  *   region 0  xq   int8, Mp*KBp*32 bytes, tiled for the matrix cores: the 32x32 tile
  *                  (row tile mt = m/32, block b) occupies bytes [(mt*KBp + b)*1024, +1024);
  *                  inside it, row r = m%32 and k' = k%32 sit at ((k'/16)*32 + r)*16 + k'%16.
- *   region 1  xs   f32 [Mp][KBp], row-major: xs of (row m, block b) at m*KBp + b.
- *   region 2  xsum int32 [Mp][KBp], same indexing.
- *   region 3  xs2  uint32, tile-major: (row m, block b) at ((m/32)*KBp + b)*32 + m%32; xs as
- *                  f16 bits in both 16-bit halves (xs is f16-exact by construction); the
- *                  operand form of the GEMM's scale outer product.
- *   region 4  xsx  f32, tile-major like region 3: xs * xsum (exact in f32), the operand of
- *                  the q4_K min term.
+ *   region 1  xs2  uint32, tile-major: (row m, block b) at ((m/32)*KBp + b)*32 + m%32; the
+ *                  scale xs as f16 bits in both 16-bit halves (xs is f16-exact by construction).
+ *   region 2  xsx  f32, tile-major like region 1: xs * xsum (exact in f32), xsum the block's
+ *                  integer sum of q.
+ *   region 3  xg   uint32, (row m, block b, half h) at ((m/32)*KBp + b)*64 + h*32 + m%32: the
+ *                  f16 pair (G_2h * 2^-13, G_2h+1 * 2^-13) in its low and high halves, G_j the
+ *                  integer sum of the 8 values q of group j (values 8j..8j+7) of the block
+ *                  (exact in f16; xsum = G_0 + G_1 + G_2 + G_3).
  *   Rows m >= M and blocks b >= KB hold zeros in every region.
  * MMQ_ACT_I8_TOKEN (two regions, each starting on a 256-byte boundary):
  *   region 0  a    int8, Mp*KBp*32 bytes, tiled exactly like region 0 of MMQ_ACT_Q8_1 (the
@@ -140,8 +141,9 @@ typedef enum { MMQ_OUT_F32 = 0, MMQ_OUT_BF16 = 1, MMQ_OUT_I32_PARTIALS = 2 } mmq
 /* Total bytes of an act buffer; 0 if the arguments are invalid. (host only) */
 size_t mmq_act_bytes(mmq_atype a, int64_t M, int64_t K);
 
-/* Byte offsets of the act buffer's regions 0..4 (MMQ_ACT_I8_TOKEN: regions 0..1, the rest 0),
- * written to offsets[0..4] (host). Returns MMQ_EINVAL for invalid arguments. (host only) */
+/* Byte offsets of the act buffer's regions (MMQ_ACT_Q8_1: regions 0..3; MMQ_ACT_I8_TOKEN:
+ * regions 0..1), written to offsets[0..4], unused entries 0 (host). Returns MMQ_EINVAL for
+ * invalid arguments. (host only) */
 mmq_status mmq_act_region_offsets(mmq_atype a, int64_t M, int64_t K, size_t offsets[5]);
 
 /* Quantise f32 activations x [M][ldx] (device, row stride ldx >= K floats) into `act`

@@ -49,13 +49,13 @@ def test_status_strings(mmq):
 def test_act_bytes_and_offsets(mmq):
     M, K = 70, 96                      # Mp = 96, KB = 3, KBp = 8
     o = mmq.act_region_offsets("q8_1", M, K)
-    cells = 96 * 8                     # (row, block) entries of a row-major scale region
+    cells = 96 * 8                     # (row, block) entries of a scale region
     assert o[0] == 0
     assert o[1] == 3 * 8 * 1024        # xq region: MT * KBp * 1 KB
-    assert o[2] == o[1] + 4 * cells    # xs f32
-    assert o[3] == o[2] + 4 * cells    # xsum int32
-    assert o[4] == o[3] + 4 * cells    # xs2 f16 pair
-    assert mmq.act_bytes("q8_1", M, K) == o[4] + 4 * cells   # xsx f32
+    assert o[2] == o[1] + 4 * cells    # xs2 f16 pair
+    assert o[3] == o[2] + 4 * cells    # xsx f32
+    assert o[4] == 0
+    assert mmq.act_bytes("q8_1", M, K) == o[3] + 8 * cells   # xg: two f16 pairs per (row, block)
     assert all(v % 256 == 0 for v in o)
     # i8_token: Mp=32, KBp=8 -> one 8 KB tile region, then sa f32 [Mp]
     oi = mmq.act_region_offsets("i8_token", 3, 64)
@@ -135,30 +135,36 @@ def test_gemm_id_validation(mmq):
     assert L.mmq_gemm_id(3, GOOD, 64, GOOD, GOOD, 512, 8, 2048, 4096, 1, GOOD, GOOD, ws, None) == mmq.MMQ_EUNSUPPORTED
 
 
-def test_act_to_host_layout_decoder(mmq):
-    # build a q8_1 act image by hand from the header's formula and decode it back
+def test_act_q8_1_layout_codec(mmq):
+    """Build a q8_1 act image byte by byte from the header's formulas, check that the host
+    encoder produces the same bytes and that the decoders give the values back."""
     M, K = 40, 96
     o = mmq.act_region_offsets("q8_1", M, K)
-    Mp, KB, KBp = 64, 3, 8
+    KB, KBp = 3, 8
     buf = np.zeros(mmq.act_bytes("q8_1", M, K), np.uint8)
     r = np.random.default_rng(0)
     xq = r.integers(-128, 128, (M, K)).astype(np.int8)
     xs = r.random((M, KB)).astype(np.float16).astype(np.float32)
-    xsum = r.integers(-4000, 4000, (M, KB)).astype(np.int32)
+    xsum = xq.reshape(M, KB, 32).astype(np.int64).sum(axis=2).astype(np.int32)
     for m in range(M):
         for k in range(K):
             mt, b, kk = m // 32, k // 32, k % 32
             buf[o[0] + (mt * KBp + b) * 1024 + ((kk // 16) * 32 + m % 32) * 16 + kk % 16] = xq[m, k].view(np.uint8)
         for b in range(KB):
-            idx = 4 * (m * KBp + b)                                  # regions 1, 2: row-major
-            tdx = 4 * (((m // 32) * KBp + b) * 32 + m % 32)          # regions 3, 4: tile-major
+            tdx = 4 * (((m // 32) * KBp + b) * 32 + m % 32)          # regions 1, 2: tile-major
             h = int(np.float16(xs[m, b]).view(np.uint16))
-            buf[o[1] + idx:o[1] + idx + 4] = np.frombuffer(xs[m, b].tobytes(), np.uint8)
-            buf[o[2] + idx:o[2] + idx + 4] = np.frombuffer(xsum[m, b].tobytes(), np.uint8)
-            buf[o[3] + tdx:o[3] + tdx + 4] = np.frombuffer(np.uint32(h | (h << 16)).tobytes(), np.uint8)
-            buf[o[4] + tdx:o[4] + tdx + 4] = np.frombuffer(np.float32(xs[m, b] * xsum[m, b]).tobytes(), np.uint8)
+            buf[o[1] + tdx:o[1] + tdx + 4] = np.frombuffer(np.uint32(h | (h << 16)).tobytes(), np.uint8)
+            buf[o[2] + tdx:o[2] + tdx + 4] = np.frombuffer(np.float32(xs[m, b] * xsum[m, b]).tobytes(), np.uint8)
+            for hh in range(2):                                      # region 3: one dword per half
+                g = [int(xq[m, 32 * b + 8 * j:32 * b + 8 * j + 8].astype(np.int64).sum()) for j in (2 * hh, 2 * hh + 1)]
+                f = [int(np.float16(np.float32(v) * np.float32(2.0 ** -13)).view(np.uint16)) for v in g]
+                gdx = 4 * (((m // 32) * KBp + b) * 64 + hh * 32 + m % 32)
+                buf[o[3] + gdx:o[3] + gdx + 4] = np.frombuffer(np.uint32(f[0] | (f[1] << 16)).tobytes(), np.uint8)
+    assert np.array_equal(mmq.act_q8_1_pack_host(xq, xs), buf)
     a, s, u = mmq.act_to_host(buf, M, K)
     assert np.array_equal(a, xq) and np.array_equal(s, xs) and np.array_equal(u, xsum)
+    G = mmq.act_groups_host(buf, M, K)
+    assert np.array_equal(G[:M, :KB], xq.reshape(M, KB, 4, 8).astype(np.int64).sum(axis=3))
     lo, hi, xsx = mmq.act_derived_host(buf, M, K)
     assert np.array_equal(lo[:M, :KB], xs) and np.array_equal(hi[:M, :KB], xs)
     assert np.array_equal(xsx[:M, :KB], xs * xsum)

@@ -63,6 +63,9 @@ def test_block_formats_quantize_partials_output(env, fmt, M, N, K):
     assert np.array_equal(xq, rq)
     assert np.array_equal(xs.view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(xsum, rsum)
+    # the 8-value group sums (region 3) are the integer sums of the oracle's q
+    G = mmq.act_groups_host(host, M, K)[:M, :K // 32]
+    assert np.array_equal(G, rq.reshape(M, K // 32, 4, 8).astype(np.int64).sum(axis=3))
     assert np.all(mmq.act_padding_host(host, M, K) == 0)
     lo, hi, xsx = mmq.act_derived_host(host, M, K)
     full_s = np.zeros(lo.shape, np.float32)

@@ -20,35 +20,6 @@ pytestmark = pytest.mark.gpu
 M, N, K = 256, 160, 1 << 23
 
 
-def _q8_1_act_host(mmq, xq, xs, xsum):
-    """Encode (xq [M,K], xs [M,K/32], xsum [M,K/32]) into the documented MMQ_ACT_Q8_1 layout."""
-    Mr, Kr = xq.shape
-    o = mmq.act_region_offsets("q8_1", Mr, Kr)
-    Mp, KB = (Mr + 31) // 32 * 32, Kr // 32
-    KBp, MT = (KB + 7) // 8 * 8, Mp // 32
-    buf = np.zeros(mmq.act_bytes("q8_1", Mr, Kr), np.uint8)
-    tiles = buf[o[0]:o[0] + MT * KBp * 1024].view(np.int8).reshape(MT, KBp, 2, 32, 16)
-    for mt in range(MT):                                  # [mt, b, h, r, 16] <- rows of tile mt
-        rows = xq[32 * mt:32 * mt + 32]
-        blk = np.zeros((32, KBp * 32), np.int8)
-        blk[:rows.shape[0], :Kr] = rows
-        tiles[mt] = blk.reshape(32, KBp, 2, 16).transpose(1, 2, 0, 3)
-    cells = Mp * KBp
-    def region(i, dt):
-        return buf[o[i]:o[i] + 4 * cells].view(dt).reshape(Mp, KBp)
-    region(1, np.float32)[:Mr, :KB] = xs
-    region(2, np.int32)[:Mr, :KB] = xsum
-    h = xs.astype(np.float16).view(np.uint16).astype(np.uint32)
-    tm = lambda i, dt: buf[o[i]:o[i] + 4 * cells].view(dt).reshape(MT, KBp, 32)
-    x2 = np.zeros((Mp, KBp), np.uint32)
-    x2[:Mr, :KB] = h | (h << 16)
-    tm(3, np.uint32)[:] = x2.reshape(MT, 32, KBp).transpose(0, 2, 1)
-    xx = np.zeros((Mp, KBp), np.float32)
-    xx[:Mr, :KB] = xs * xsum.astype(np.float32)
-    tm(4, np.float32)[:] = xx.reshape(MT, 32, KBp).transpose(0, 2, 1)
-    return buf
-
-
 def test_dense_gemm_past_the_2gib_split():
     import torch
     import block_quantized_int8_amd as mmq
@@ -66,7 +37,7 @@ def test_dense_gemm_past_the_2gib_split():
         xq[32 * i:32 * i + 32], xs[32 * i:32 * i + 32], xsum[32 * i:32 * i + 32] = q
     print("  inputs ready", flush=True)
     dev = torch.device("cuda:0")
-    act = torch.from_numpy(_q8_1_act_host(mmq, xq, xs, xsum)).to(dev)
+    act = torch.from_numpy(mmq.act_q8_1_pack_host(xq, xs)).to(dev)
     packed = mmq.repack_weights("q4_0", torch.from_numpy(raw).to(dev), N, K)
     out = mmq.gemm("q4_0", packed, act, M, N, K, "f32")
     torch.cuda.synchronize()
