@@ -82,6 +82,7 @@ template <> struct BT<MMQ_Q8_0> {
     static constexpr bool MIN = false;     // q4_K min term
     static constexpr bool DUAL = false;    // q6_K: two half-block dots per block
     static constexpr bool GSUM = false;    // iq1t: group-sum term in the conversion MFMA
+    static constexpr bool GRID = false;    // iq1c: grid indices, d per 4-block group
     static constexpr float POST = UNBIAS / 2;   // S = 2 wd xs
     struct Raw { v4i x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -102,6 +103,7 @@ template <> struct BT<MMQ_Q4_0> {
     static constexpr bool MIN = false;
     static constexpr bool DUAL = false;
     static constexpr bool GSUM = false;
+    static constexpr bool GRID = false;
     static constexpr float POST = UNBIAS / 32;  // 16x block dot, S = 2 wd xs
     struct Raw { uint2 x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -125,6 +127,7 @@ template <> struct BT<MMQ_Q4_K> {
     static constexpr bool MIN = true;
     static constexpr bool DUAL = false;
     static constexpr bool GSUM = false;
+    static constexpr bool GRID = false;
     static constexpr float POST = UNBIAS / 2;
     struct Raw { uint2 x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -154,6 +157,7 @@ template <> struct BT<MMQ_IQ1T> {
     static constexpr bool MIN = false;
     static constexpr bool DUAL = false;
     static constexpr bool GSUM = true;
+    static constexpr bool GRID = false;
     static constexpr float POST = UNBIAS / 16;  // scale d/8, S = 2 d xs
     static constexpr int TAB_WORDS = 64;        // 32 entries x 2 words
     struct Raw { uint32_t C; uint2 t; };
@@ -181,6 +185,33 @@ template <> struct BT<MMQ_IQ1T> {
     }
 };
 
+// iq1c / iq1s grid-index panels: one dword W = ia << 2 | meta << 13 | ib << 20 per lane, ia and
+// ib the 11-bit grid indices of its two 8-value groups, meta as for iq1t. The grid sits in LDS
+// after the iq1t meta table, spread into the iq1t code order (value j of an entry at bits
+// 8(j%4) + 2(j/4)), so the lane's code dword is entry(ia) | entry(ib) << 4 and everything after
+// the lookups is the iq1t step. The scale d comes per (row, 4-block stage) from its own region.
+template <> struct BT<MMQ_IQ1C> : BT<MMQ_IQ1T> {
+    static constexpr bool GRID = true;
+    static constexpr int TAB_BYTES = TAB_WORDS * 4 + 2048 * 4;
+    struct Raw { uint32_t W, ga, gb; uint2 t; };
+    __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
+        r.W = *reinterpret_cast<const uint32_t*>(frag + lane * 4);
+    }
+    __device__ static void mid(Raw& r, uint32_t, int, const uint8_t* tab) {
+        const uint8_t* g = tab + TAB_WORDS * 4;
+        r.ga = *reinterpret_cast<const uint32_t*>(g + (r.W & 0x1FFCu));     // ia * 4
+        r.gb = *reinterpret_cast<const uint32_t*>(g + (r.W >> 18));         // ib * 4
+        r.t = *reinterpret_cast<const uint2*>(tab + ((r.W >> 10) & 0xF8u));  // meta * 8
+    }
+    __device__ static void unpack(const Raw& r, v4i* a, int) {
+        BT<MMQ_IQ1T>::Raw q;
+        q.C = r.ga | (r.gb << 4);
+        q.t = r.t;
+        BT<MMQ_IQ1T>::unpack(q, a, 0);
+    }
+    __device__ static uint32_t scale_op(uint32_t w) { return w; }            // f16 d
+};
+
 // q6_K lane bytes: 16 int8 values q-32 (k = 16h..16h+15), as q8_0. a[0] keeps them on lanes 0-31
 // (values 0-15 of the block, half 0) and a[1] on lanes 32-63 (values 16-31, half 1); the other
 // lanes are zero, so each int8 MFMA yields one half-block dot. The scale dword of half 0 sits in
@@ -192,6 +223,7 @@ template <> struct BT<MMQ_Q6_K> {
     static constexpr bool MIN = false;
     static constexpr bool DUAL = true;
     static constexpr bool GSUM = false;
+    static constexpr bool GRID = false;
     static constexpr float POST = UNBIAS / 2;   // S_h = 2 (d*sc_h) xs
     struct Raw { v4i x; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
@@ -231,7 +263,10 @@ struct Cfg {
     static constexpr int XF = TM * KS * 1024;
     static constexpr int SCB = KS * 32 * 4;                 // one tile's scale dwords per stage
     static constexpr int C_WF = WF / 1024, C_XF = TM * KS;
-    static constexpr int C_WS = (TN + 1) / 2;               // a pair of tiles per chunk
+    // weight scales: a pair of tiles per 1 KB chunk; iq1c: the f16 d of 4 tiles x 32 rows per
+    // stage, one 4-byte-per-lane chunk
+    static constexpr int C_WS = T::GRID ? 1 : (TN + 1) / 2;
+    static_assert(!T::GRID || TN == 4, "one d chunk covers four weight tiles");
     static constexpr int C_XS = GATHER ? TM * KS / 2 : (TM + 1) / 2;
     // second weight-side scale region: q4_K's -dmin*m, q6_K's half-1 scale dwords
     static constexpr bool W2 = T::MIN || T::DUAL;
@@ -240,7 +275,7 @@ struct Cfg {
     // 1 KB chunk per token tile and stage, or (gathered rows) a 4-byte-per-lane chunk per tile
     // and block
     static constexpr int C_XG = T::GSUM ? (GATHER ? TM * KS : TM) : 0;
-    static constexpr int RW = C_WS * 2 * SCB, RX = (TM + 1) / 2 * 2 * SCB;   // region bytes
+    static constexpr int RW = T::GRID ? 256 : C_WS * 2 * SCB, RX = (TM + 1) / 2 * 2 * SCB;   // region bytes
     static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + RW;
     static constexpr int O_WM = O_XS + RX, O_XM = O_WM + (W2 ? RW : 0);
     static constexpr int O_XG = O_XM + (T::MIN ? RX : 0);
@@ -366,8 +401,13 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         }
     };
 
-    if constexpr (FMT == MMQ_IQ1T) {
+    if constexpr (FMT == MMQ_IQ1T || FMT == MMQ_IQ1C) {
         if (tid < T::TAB_WORDS) reinterpret_cast<uint32_t*>(tab)[tid] = T::table_word(tid >> 1, tid & 1);
+    }
+    if constexpr (T::GRID) {          // the packed matrix's grid (its last region) into LDS
+        const uint32_t* g = reinterpret_cast<const uint32_t*>(wbase + args.w_min_off);
+        uint32_t* lg = reinterpret_cast<uint32_t*>(tab) + T::TAB_WORDS;
+        for (int i = tid; i < 2048; i += C::NTH) lg[i] = g[i];
     }
 
     // ---- DMA plan: per chunk this lane keeps a 32-bit source offset from the chunk's region
@@ -401,7 +441,13 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
             const int ci = c - C::C_FR;
             const int sk = C::scale_kind(ci);
             skind[j] = sk;
-            if (sk == C::S_WS || sk == C::S_WM) {
+            if (T::GRID && sk == C::S_WS) {
+                // iq1c: lane l carries rows 2(l%16), 2(l%16)+1 of tile l/16 (their f16 d of the
+                // stage's 4-block group: 64 bytes per tile and stage)
+                const int nt = min(nt_base + (lane >> 4), NT - 1);
+                goff[j] = (uint32_t)((nt * (KBp / 4) * 32 + 2 * (lane & 15)) * 2);
+                ldso[j] = C::O_WS;
+            } else if (sk == C::S_WS || sk == C::S_WM) {
                 // a pair of weight tiles: lanes 0-31 tile 2pr, lanes 32-63 tile 2pr+1, 16 bytes
                 // each of the tile's contiguous 512-byte stage
                 const int pr = ci - (sk == C::S_WS ? 0 : C::C_WS + C::C_XS);
@@ -453,9 +499,11 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
             const uint8_t* base = sk == C::S_WS ? wsc : sk == C::S_XS ? reinterpret_cast<const uint8_t*>(args.xs2)
                                 : sk == C::S_WM ? wmn : sk == C::S_XM ? reinterpret_cast<const uint8_t*>(args.xsx)
                                 : reinterpret_cast<const uint8_t*>(args.xg);
-            if (is_gather(MODE) && (sk == C::S_XS || sk == C::S_XM || sk == C::S_XG)) dma4(base + goff[j], dst);
-            else dma16(base + goff[j], dst);
-            goff[j] += sk == C::S_XG ? KS * 256 : C::SCB;
+            if ((is_gather(MODE) && (sk == C::S_XS || sk == C::S_XM || sk == C::S_XG)) || (T::GRID && sk == C::S_WS))
+                dma4(base + goff[j], dst);
+            else
+                dma16(base + goff[j], dst);
+            goff[j] += sk == C::S_XG ? KS * 256 : (T::GRID && sk == C::S_WS) ? 64 : C::SCB;
         }
     };
     auto issue_stage = [&](uint8_t* buf) __attribute__((always_inline)) {
@@ -514,7 +562,10 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int i = wn * RT + rt;
-            R.wsd[rt] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_WS, i, r32, kb));
+            if constexpr (T::GRID)
+                R.wsd[rt] = *reinterpret_cast<const uint16_t*>(cur + C::O_WS + (i * 32 + r32) * 2);
+            else
+                R.wsd[rt] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_WS, i, r32, kb));
             if constexpr (T::DUAL) R.wsd2[rt] = *reinterpret_cast<const uint32_t*>(cur + C::sc(C::O_WM, i, r32, kb));
             T::fetch(cur + (i * KS + kb) * T::FB, lane, R.w[rt]);
         }
@@ -802,7 +853,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     using C = Cfg<FMT, WN, WM, RT, CT, is_gather(MODE)>;
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::BUF];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 256 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1C ? BT<MMQ_IQ1C>::TAB_BYTES : FMT == MMQ_IQ1T ? 256 : 16];
     block_body<FMT, WN, WM, RT, CT, MODE, XM>(args, buf0, buf1, tab, (int)blockIdx.x, (int)gridDim.x);
 }
 
@@ -817,7 +868,7 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_gather_kernel(BlockArgs f
     constexpr int BUF = CF::BUF > CTl::BUF ? CF::BUF : CTl::BUF;
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[BUF];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1T ? 256 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1C ? BT<MMQ_IQ1C>::TAB_BYTES : FMT == MMQ_IQ1T ? 256 : 16];
     const int b = (int)blockIdx.x;
     if (b < nfull) block_body<FMT, WN, WM, RT, CT, GATHER_F32, XM>(full, buf0, buf1, tab, b, nfull);
     else block_body<FMT, WN, WM, RT, TCT, GATHER_TAIL, XM>(tail, buf0, buf1, tab, b - nfull, (int)gridDim.x - nfull);
@@ -912,10 +963,11 @@ hipError_t launch_dense_split(const BlockArgs& g0, int64_t M, int64_t N, mmq_oty
             const int64_t NTc = std::min(nstep, NT - nt0), MTc = std::min(mstep, MT - mt0);
             const int64_t Nc = std::min(NTc * 32, N - nt0 * 32), Mc = std::min(MTc * 32, M - mt0 * 32);
             const int64_t wshift = nt0 * g0.KBp * FB;             // fragments of the skipped tiles
-            const int64_t sshift = nt0 * g0.KBp * 128;            // their scale dwords
+            // their scale dwords (iq1c: their d per 4-block group; its grid region is shared)
+            const int64_t sshift = BT<FMT>::GRID ? nt0 * (g0.KBp / 4) * 64 : nt0 * g0.KBp * 128;
             g.w = g0.w + wshift;
             g.w_scale_off = scale_off + sshift - wshift;
-            g.w_min_off = min_off + sshift - wshift;
+            g.w_min_off = min_off + (BT<FMT>::GRID ? 0 : sshift) - wshift;
             g.xq = g0.xq + mt0 * g0.KBp * 1024;
             g.xs2 = g0.xs2 + mt0 * g0.KBp * 32;
             g.xsx = g0.xsx + mt0 * g0.KBp * 32;
@@ -1009,6 +1061,7 @@ hipError_t launch_block_gemm(mmq_wtype t, const void* packed, const void* act, i
         case MMQ_Q4_0: return launch_dense<MMQ_Q4_0>(packed, act, M, N, K, o, out, ldo, s);
         case MMQ_Q4_K: return launch_dense<MMQ_Q4_K>(packed, act, M, N, K, o, out, ldo, s);
         case MMQ_IQ1T: return launch_dense<MMQ_IQ1T>(packed, act, M, N, K, o, out, ldo, s);
+        case MMQ_IQ1C: return launch_dense<MMQ_IQ1C>(packed, act, M, N, K, o, out, ldo, s);
         case MMQ_Q6_K: return launch_dense<MMQ_Q6_K>(packed, act, M, N, K, o, out, ldo, s);
         default: return hipErrorNotSupported;
     }
@@ -1024,6 +1077,7 @@ hipError_t launch_block_gather(mmq_wtype t, const void* packed, int64_t E, const
         case MMQ_Q4_0: return MMQ_GATHER(MMQ_Q4_0);
         case MMQ_Q4_K: return MMQ_GATHER(MMQ_Q4_K);
         case MMQ_IQ1T: return MMQ_GATHER(MMQ_IQ1T);
+        case MMQ_IQ1C: return MMQ_GATHER(MMQ_IQ1C);
         case MMQ_Q6_K: return MMQ_GATHER(MMQ_Q6_K);
         default: return hipErrorNotSupported;
     }

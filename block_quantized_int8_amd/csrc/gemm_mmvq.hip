@@ -92,11 +92,11 @@ template <mmq_wtype FMT> struct VQ;
 
 template <> struct VQ<MMQ_Q8_0> {
     static constexpr int FB = 1024, NMF = 1;
-    static constexpr bool MIN = false, ROW = false, META = false, DUAL = false;
+    static constexpr bool MIN = false, ROW = false, META = false, DUAL = false, GRID = false;
     static constexpr float POST = 1.0f;
     typedef v4i Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld128(r, off); }
-    __device__ static void ops(Raw r, uint32_t, const uint2*, v4i* b) { b[0] = r; }
+    __device__ static void ops(Raw r, uint32_t, const uint2*, const uint32_t*, v4i* b) { b[0] = r; }
     __device__ static uint32_t scale_op(uint32_t w) { return w; }
 };
 
@@ -115,11 +115,11 @@ template <> struct VQ<MMQ_Q6_K> : VQ<MMQ_Q8_0> {
 // 4-bit two's complement of nib - 8, so the masked bytes are int8 16*(nib-8).
 template <> struct VQ<MMQ_Q4_0> {
     static constexpr int FB = 512, NMF = 1;
-    static constexpr bool MIN = false, ROW = false, META = false, DUAL = false;
+    static constexpr bool MIN = false, ROW = false, META = false, DUAL = false, GRID = false;
     static constexpr float POST = 1.0f / 16;
     typedef uint2 Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld64(r, off); }
-    __device__ static void ops(Raw r, uint32_t, const uint2*, v4i* b) {
+    __device__ static void ops(Raw r, uint32_t, const uint2*, const uint32_t*, v4i* b) {
         b[0][0] = (int)(r.x & 0xF0F0F0F0u);
         b[0][1] = (int)((r.x << 4) & 0xF0F0F0F0u);
         b[0][2] = (int)(r.y & 0xF0F0F0F0u);
@@ -132,11 +132,11 @@ template <> struct VQ<MMQ_Q4_0> {
 // scale dword is the exact f16 pair (hi, lo) of d*sc, the min region -dmin*m.
 template <> struct VQ<MMQ_Q4_K> {
     static constexpr int FB = 512, NMF = 1;
-    static constexpr bool MIN = true, ROW = false, META = false, DUAL = false;
+    static constexpr bool MIN = true, ROW = false, META = false, DUAL = false, GRID = false;
     static constexpr float POST = 1.0f;
     typedef uint2 Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld64(r, off); }
-    __device__ static void ops(Raw r, uint32_t, const uint2*, v4i* b) {
+    __device__ static void ops(Raw r, uint32_t, const uint2*, const uint32_t*, v4i* b) {
         b[0][0] = (int)(r.x & 0x0F0F0F0Fu);
         b[0][1] = (int)((r.x >> 4) & 0x0F0F0F0Fu);
         b[0][2] = (int)(r.y & 0x0F0F0F0Fu);
@@ -153,12 +153,12 @@ template <> struct VQ<MMQ_Q4_K> {
 // chained int8 MFMAs. tab[s | sign << 3] = (byte LUT code -> v, byte LUT code -> 2s*v).
 template <> struct VQ<MMQ_IQ1T> {
     static constexpr int FB = 256, NMF = 2;
-    static constexpr bool MIN = false, ROW = false, META = true, DUAL = false;
+    static constexpr bool MIN = false, ROW = false, META = true, DUAL = false, GRID = false;
     static constexpr float POST = 1.0f / 8;
     typedef uint32_t Raw;
     __device__ static Raw load(rsrc_t r, uint32_t off) { return ld32(r, off); }
     // meta: the lane's meta byte
-    __device__ static void ops(Raw C, uint32_t meta, const uint2* tab, v4i* b) {
+    __device__ static void ops(Raw C, uint32_t meta, const uint2* tab, const uint32_t*, v4i* b) {
         const uint32_t s = meta & 7u;
         const uint2 t0 = tab[s | (((meta >> 3) & 1u) << 3)];
         const uint2 t1 = tab[s | (((meta >> 4) & 1u) << 3)];
@@ -186,6 +186,19 @@ template <> struct VQ<MMQ_IQ1T> {
         }
         return make_uint2(v, v2);
     }
+};
+
+// iq1c / iq1s grid-index panels: one dword W = ia << 2 | meta << 13 | ib << 20 per fragment lane;
+// the two 11-bit indices name grid entries (kept in LDS, spread into the iq1t code order), so the
+// lane's code dword is entry(ia) | entry(ib) << 4 and meta sits in W itself; then the iq1t fold.
+// The scale d comes per (row, 4-block group) from its own region (16 bits per row).
+template <> struct VQ<MMQ_IQ1C> : VQ<MMQ_IQ1T> {
+    static constexpr bool META = false, GRID = true;
+    __device__ static void ops(Raw W, uint32_t, const uint2* tab, const uint32_t* gtab, v4i* b) {
+        const uint32_t C = gtab[(W >> 2) & 0x7FFu] | (gtab[W >> 20] << 4);
+        VQ<MMQ_IQ1T>::ops(C, (W >> 13) & 0x1Fu, tab, gtab, b);
+    }
+    __device__ static uint32_t scale_op(uint32_t w) { return w; }             // f16 d
 };
 
 struct MvArgs {
@@ -228,6 +241,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     constexpr int XSLOTS = XL ? XCap<TG>::KB * 2 * TOK : 0;  // 16-byte slots; slot XSLOTS is zero
     __shared__ float red[2][MV_W][4 * TG][64];
     __shared__ uint2 tab[16];
+    __shared__ uint32_t gtab[T::GRID ? 2048 : 1];
     __shared__ __attribute__((aligned(16))) uint8_t xl[(XSLOTS + 1) * 16];
     // MUL_MAT_ID: per batch of at most TOK pairs of one expert (expert id, first pair in
     // expert order, pairs), the pair ids, and the scan's wave totals
@@ -239,8 +253,12 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
 
-    if constexpr (FMT == MMQ_IQ1T) {
+    if constexpr (FMT == MMQ_IQ1T || FMT == MMQ_IQ1C) {
         if (tid < 16) tab[tid] = T::table(tid);
+        if constexpr (T::GRID) {          // the grid (the packed matrix's last region; MUL_MAT_ID:
+            const uint32_t* gsrc = reinterpret_cast<const uint32_t*>(a.w + a.w_min_off);   // expert 0's)
+            for (int i = tid; i < 2048; i += MV_W * 64) gtab[i] = gsrc[i];
+        }
         __syncthreads();
     }
     const int KBp = a.KBp;
@@ -355,7 +373,13 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         if constexpr (!T::ROW) {
             const rsrc_t rs = rsrc(wx + a.w_scale_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128);
             const rsrc_t rxs = rsrc(xsb + (int64_t)b0 * 128, MV_CH * 128);
-            k.ws = ld32(rs, o_s);
+            if constexpr (T::GRID) {       // the row's d of this 4-block group (MV_CH = 4 blocks)
+                const int64_t gq = (int64_t)(q >> 1) * (KBp / 4) + b0 / 4;
+                k.ws = __builtin_amdgcn_raw_buffer_load_b16(
+                    rsrc(wx + a.w_scale_off + (gq * 32 + half * MV_ROWS) * 2, MV_ROWS * 2), (int)(c16 * 2), 0, 0);
+            } else {
+                k.ws = ld32(rs, o_s);
+            }
             if constexpr (T::DUAL)
                 k.ws2 = ld32(rsrc(wx + a.w_min_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128), o_s);
 #pragma unroll
@@ -405,7 +429,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             v4i bop[T::NMF];
             uint32_t meta = 0;
             if constexpr (T::META) meta = (k.wso[p] >> (16 + 8 * fh)) & 0xFFu;
-            T::ops(k.w[p], meta, tab, bop);
+            T::ops(k.w[p], meta, tab, gtab, bop);
 #pragma unroll
             for (int x = 0; x < TG; ++x) {
                 if constexpr (T::ROW) {
@@ -631,6 +655,7 @@ hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void
         case MMQ_Q4_0: launch_xl<MMQ_Q4_0, true, true>(args, grid, s); break;
         case MMQ_Q4_K: launch_xl<MMQ_Q4_K, true, true>(args, grid, s); break;
         case MMQ_IQ1T: launch_xl<MMQ_IQ1T, true, true>(args, grid, s); break;
+        case MMQ_IQ1C: launch_xl<MMQ_IQ1C, true, true>(args, grid, s); break;
         case MMQ_Q6_K: launch_xl<MMQ_Q6_K, true, true>(args, grid, s); break;
         default: return hipErrorInvalidValue;
     }
@@ -668,6 +693,7 @@ hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t
         case MMQ_Q4_0: return launch_fmt<MMQ_Q4_0>(args, s);
         case MMQ_Q4_K: return launch_fmt<MMQ_Q4_K>(args, s);
         case MMQ_IQ1T: return launch_fmt<MMQ_IQ1T>(args, s);
+        case MMQ_IQ1C: return launch_fmt<MMQ_IQ1C>(args, s);
         case MMQ_I8_ROW: return launch_fmt<MMQ_I8_ROW>(args, s);
         case MMQ_Q6_K: return launch_fmt<MMQ_Q6_K>(args, s);
         default: break;

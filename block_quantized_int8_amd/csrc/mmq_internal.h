@@ -14,6 +14,7 @@ constexpr int QK = 32;          // values per quantisation block (one int8 MFMA 
 constexpr int KB_ALIGN = 8;     // activation / packed-weight block counts are padded to this
 constexpr int TILE = 32;        // rows per matrix-core tile (v_mfma_*_32x32x*)
 constexpr int64_t REGION_ALIGN = 256;
+constexpr int64_t GRID_ENTRIES = 2048;   // IQ1C / IQ1S codebook: one 11-bit index per 8 values
 
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -85,6 +86,9 @@ inline ActI8Layout act_i8_layout(int64_t M, int64_t K) {
 //   Q4_K: 8 B per lane, unsigned nibbles: X0 & 0x0F0F0F0F = k 16h+0..3, (X0 >> 4) & 0x0F0F0F0F
 //         = 16h+4..7, likewise X1 for 8..15 -> 512 B.
 //   IQ1T: 4 B per lane of 2-bit codes (value 16h + 4q + b at bits 8b + 2q) -> 256 B.
+//   IQ1C, IQ1S (grid-index panels): 4 B per lane, W = ia << 2 | meta << 13 | ib << 20, with ia, ib
+//         the 11-bit grid indices of the lane's 8-value groups 2h and 2h+1 and meta = s |
+//         sigma_a << 3 | sigma_b << 4 (the half's sub-scale and the groups' sign bits) -> 256 B.
 //   Q6_K: 16 B per lane of int8 q-32, as Q8_0 -> 1024 B.
 // Region 1 holds one dword per (row n, block b), tile-major [NT][KBp][32] (row n, block b at
 // (n/32 * KBp + b) * 32 + n%32, so a 32-row tile's stage of blocks is one contiguous run):
@@ -94,8 +98,12 @@ inline ActI8Layout act_i8_layout(int64_t M, int64_t K) {
 //               sign bits of its two 8-value groups).
 //   Q4_K:       d*sc split exactly into two f16 (hi | lo << 16), hi + lo = d*sc.
 //   Q6_K:       d*sc_0 of the block's first 16 values, split the same way.
+//   IQ1C, IQ1S: instead the f16 d of the row's super-block per (row, 4-block group g = b/4),
+//               tile-major [NT][KBp/4][32] (a 4-block stage of a 32-row tile is 64 bytes).
 // Region 2: Q4_K: f32 -dmin*m per (row, block); Q6_K: the d*sc_1 split of the block's last 16
-// values; tile-major like region 1.
+// values; tile-major like region 1. IQ1C, IQ1S: the grid, 2048 dwords, entry i holding the 8
+// codes c = g+1 of index i with value j at bits 8(j%4) + 2(j/4) (so a lane's code dword, in the
+// IQ1T order, is entry(ia) | entry(ib) << 4).
 // I8_ROW keeps one f32 per row [Np] in region 1.
 struct PackedLayout {
     int64_t Np, NT, KB, KBp;
@@ -115,16 +123,18 @@ inline PackedLayout packed_layout(mmq_wtype t, int64_t N, int64_t K) {
         case MMQ_Q4_K: L.frag_bytes = 512; break;
         case MMQ_IQ1T:
         case MMQ_IQ1C:
-        case MMQ_IQ1S: L.frag_bytes = 256; break;      // IQ1C / IQ1S are repacked into the IQ1T form
+        case MMQ_IQ1S: L.frag_bytes = 256; break;
         case MMQ_Q6_K: L.frag_bytes = 1024; break;     // int8 q-32
         default: L.frag_bytes = 1024; break;           // I8_ROW
     }
     const int64_t cells = L.Np * L.KBp;
     L.frag_off = 0;
     L.scale_off = round_up(L.NT * L.KBp * L.frag_bytes, REGION_ALIGN);
-    const int64_t sb = (t == MMQ_I8_ROW) ? L.Np * 4 : cells * 4;
+    const bool grid = (t == MMQ_IQ1C || t == MMQ_IQ1S);
+    const int64_t sb = (t == MMQ_I8_ROW) ? L.Np * 4 : grid ? L.Np * (L.KBp / 4) * 2 : cells * 4;
     L.min_off = L.scale_off + round_up(sb, REGION_ALIGN);
-    L.bytes = L.min_off + ((t == MMQ_Q4_K || t == MMQ_Q6_K) ? round_up(cells * 4, REGION_ALIGN) : 0);
+    L.bytes = L.min_off + ((t == MMQ_Q4_K || t == MMQ_Q6_K) ? round_up(cells * 4, REGION_ALIGN)
+                           : grid ? GRID_ENTRIES * 4 : 0);
     return L;
 }
 
@@ -137,8 +147,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 // internal launchers (defined in the .hip files, called by api.cpp)
 namespace mmq {
-// The packed form the GEMM kernels read: IQ1C and IQ1S are repacked into the IQ1T panels.
-inline mmq_wtype kernel_format(mmq_wtype t) { return (t == MMQ_IQ1C || t == MMQ_IQ1S) ? MMQ_IQ1T : t; }
+// The packed form the GEMM kernels read: IQ1S is repacked into the IQ1C grid-index panels.
+inline mmq_wtype kernel_format(mmq_wtype t) { return t == MMQ_IQ1S ? MMQ_IQ1C : t; }
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, int64_t ldx, void* act,
                                 hipStream_t s);
 hipError_t launch_quantize_i8_token(const float* x, int64_t M, int64_t K, int64_t ldx, void* act,

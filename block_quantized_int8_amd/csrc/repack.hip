@@ -200,87 +200,91 @@ __global__ __launch_bounds__(256) void repack_q6_K_kernel(
     dst[(x.nt * KBp + x.b) * 32 + x.r] = ds2;
 }
 
+// The codebook formats keep their 11-bit grid indices in the packed form (grid-index panels):
+// the GEMMs look every index up in the grid themselves, so the weights stream at the raw
+// format's size (plus the per-lane meta bits) instead of as expanded 2-bit codes. Every launch
+// piece writes, besides its lanes: the first threads, the grid spread into the IQ1T code order
+// (value j of an entry at bits 8(j%4) + 2(j/4)); lanes h = 0 of every fourth block, the row's
+// f16 d (one copy per 4-block group, the GEMMs' stage).
+__device__ inline uint32_t spread_entry(uint32_t e) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= ((e >> (2 * j)) & 3u) << (8 * (j & 3) + 2 * (j >> 2));
+    return w;
+}
+
+__device__ inline void write_grid(const uint16_t* __restrict__ grid, uint32_t* __restrict__ gtab, int64_t gid,
+                                  int64_t total) {
+    for (int64_t i = gid; i < GRID_ENTRIES; i += total) gtab[i] = spread_entry(grid[i]);
+}
+
+__device__ inline uint32_t grid_word(uint32_t ia, uint32_t ib, uint32_t meta) {
+    return (ia << 2) | (meta << 13) | (ib << 20);
+}
+
 // IQ1C (the IQ1_M codebook form): the lane's 16 values are the 8-value groups q0 = e0/8 and
-// q0 + 1; each group's 11-bit index (qs byte, plus bits 8-10 from its qh nibble) names a grid
-// entry of eight 2-bit codes, which land in the IQ1T lane word; the delta sign is bit 3 of the
-// same nibble. The packed result is exactly the IQ1T panel of the same values.
+// q0 + 1; each group's 11-bit index is its qs byte plus bits 8-10 from its qh nibble, whose bit 3
+// is the group's delta sign; s is the half's 3-bit sub-scale.
 __global__ __launch_bounds__(256) void repack_iq1c_kernel(
     const uint8_t* __restrict__ raw, const uint16_t* __restrict__ grid, int64_t N, int64_t KB,
-    int64_t KBp, int64_t total, int64_t gid0, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
+    int64_t KBp, int64_t total, int64_t gid0, uint8_t* __restrict__ frag, uint16_t* __restrict__ dreg,
+    uint32_t* __restrict__ gtab) {
     const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
+    write_grid(grid, gtab, gid, total);
     const Lane x = lane_of(gid, KBp, KB, N);
-    uint32_t C = 0, meta = 0;
+    uint32_t W = 0;
     uint16_t d = 0;
     if (x.live) {
         const uint8_t* blk = raw + (x.n * (KB / 8) + x.b / 8) * 56;
         const int e0 = (int)(x.b % 8) * 32 + 16 * x.h;    // first of the lane's 16 values
-        uint32_t sg[2];
+        uint32_t idx[2], sg[2];
 #pragma unroll
         for (int gq = 0; gq < 2; ++gq) {
             const int q = (e0 >> 3) + gq;
             const uint32_t nib = (blk[32 + (q >> 1)] >> (4 * (q & 1))) & 0xFu;
-            const uint32_t entry = grid[blk[q] | ((nib & 7u) << 8)];
+            idx[gq] = blk[q] | ((nib & 7u) << 8);
             sg[gq] = nib >> 3;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int i = 8 * gq + j;                  // value index inside the lane
-                C |= ((entry >> (2 * j)) & 3u) << (8 * (i & 3) + 2 * (i >> 2));
-            }
         }
         uint64_t sw = 0;
 #pragma unroll
         for (int i = 0; i < 6; ++i) sw |= (uint64_t)blk[48 + i] << (8 * i);
         const uint32_t s = (uint32_t)(sw >> (3 * (e0 >> 4))) & 7u;
-        meta = s | (sg[0] << 3) | (sg[1] << 4);
+        W = grid_word(idx[0], idx[1], s | (sg[0] << 3) | (sg[1] << 4));
         d = ld_u16(blk + 54);
     }
-    *reinterpret_cast<uint32_t*>(frag + gid * 4) = C;
-    uint8_t* e = scale + ((x.nt * KBp + x.b) * 32 + x.r) * 4;
-    if (x.h == 0) {
-        *reinterpret_cast<uint16_t*>(e) = d;
-        e[2] = (uint8_t)meta;
-    } else {
-        e[3] = (uint8_t)meta;
-    }
+    *reinterpret_cast<uint32_t*>(frag + gid * 4) = W;
+    if (x.h == 0 && x.b % 4 == 0) dreg[(x.nt * (KBp / 4) + x.b / 4) * 32 + x.r] = d;
 }
 
 // IQ1S (the IQ1_S codebook form): as IQ1C, with the block's one s and one delta sign (its
-// uint16 qh word) repeated for both halves and all four groups of the IQ1T panel.
+// uint16 qh word) for both halves and all four groups.
 __global__ __launch_bounds__(256) void repack_iq1s_kernel(
     const uint8_t* __restrict__ raw, const uint16_t* __restrict__ grid, int64_t N, int64_t KB,
-    int64_t KBp, int64_t total, int64_t gid0, uint8_t* __restrict__ frag, uint8_t* __restrict__ scale) {
+    int64_t KBp, int64_t total, int64_t gid0, uint8_t* __restrict__ frag, uint16_t* __restrict__ dreg,
+    uint32_t* __restrict__ gtab) {
     const int64_t gid = gid0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
+    write_grid(grid, gtab, gid, total);
     const Lane x = lane_of(gid, KBp, KB, N);
-    uint32_t C = 0, meta = 0;
+    uint32_t W = 0;
     uint16_t d = 0;
     if (x.live) {
         const uint8_t* blk = raw + (x.n * (KB / 8) + x.b / 8) * 50;
         const int j = (int)(x.b % 8);                      // the block inside the super-block
         const uint32_t qh = ld_u16(blk + 34 + 2 * j);
+        uint32_t idx[2];
 #pragma unroll
         for (int gq = 0; gq < 2; ++gq) {
             const int q = 2 * x.h + gq;                    // the lane's group inside the block
-            const uint32_t entry = grid[blk[2 + 4 * j + q] | (((qh >> (3 * q)) & 7u) << 8)];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int v = 8 * gq + i;                  // value index inside the lane
-                C |= ((entry >> (2 * i)) & 3u) << (8 * (v & 3) + 2 * (v >> 2));
-            }
+            idx[gq] = blk[2 + 4 * j + q] | (((qh >> (3 * q)) & 7u) << 8);
         }
         const uint32_t s = (qh >> 12) & 7u, sg = (qh >> 15) & 1u;
-        meta = s | (sg << 3) | (sg << 4);
+        W = grid_word(idx[0], idx[1], s | (sg << 3) | (sg << 4));
         d = ld_u16(blk);
     }
-    *reinterpret_cast<uint32_t*>(frag + gid * 4) = C;
-    uint8_t* e = scale + ((x.nt * KBp + x.b) * 32 + x.r) * 4;
-    if (x.h == 0) {
-        *reinterpret_cast<uint16_t*>(e) = d;
-        e[2] = (uint8_t)meta;
-    } else {
-        e[3] = (uint8_t)meta;
-    }
+    *reinterpret_cast<uint32_t*>(frag + gid * 4) = W;
+    if (x.h == 0 && x.b % 4 == 0) dreg[(x.nt * (KBp / 4) + x.b / 4) * 32 + x.r] = d;
 }
 
 __global__ __launch_bounds__(256) void repack_i8_row_kernel(
@@ -334,11 +338,13 @@ hipError_t launch_repack(mmq_wtype t, const void* raw, const void* aux, int64_t 
             break;
         case MMQ_IQ1S:
             hipLaunchKernelGGL(repack_iq1s_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,
-                               L.KB, L.KBp, total, g0, frag, scale);
+                               L.KB, L.KBp, total, g0, frag, reinterpret_cast<uint16_t*>(scale),
+                               reinterpret_cast<uint32_t*>(base + L.min_off));
             break;
         case MMQ_IQ1C:
             hipLaunchKernelGGL(repack_iq1c_kernel, grid, block, 0, s, r8, static_cast<const uint16_t*>(aux), N,
-                               L.KB, L.KBp, total, g0, frag, scale);
+                               L.KB, L.KBp, total, g0, frag, reinterpret_cast<uint16_t*>(scale),
+                               reinterpret_cast<uint32_t*>(base + L.min_off));
             break;
         case MMQ_I8_ROW:
             hipLaunchKernelGGL(repack_i8_row_kernel, grid, block, 0, s, static_cast<const int8_t*>(raw),

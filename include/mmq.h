@@ -167,10 +167,12 @@ size_t mmq_packed_bytes(mmq_wtype t, int64_t N, int64_t K);
  *            written. Immutable afterwards and safe to reuse across graph replays
  *            (metainfer section 3.2: one-time pack outside the timed region).
  * K must be a multiple of 32 (Q8_0, Q4_0, I8_ROW) or 256 (Q4_K, Q6_K, IQ1T, IQ1C, IQ1S).
- * MMQ_IQ1C and MMQ_IQ1S are expanded here, once, through the grid into the MMQ_IQ1T panel
- * form (2-bit codes, per-16 sub-scale and per-8 delta sign; IQ1S repeats its per-32 s and
- * sign), so the three formats share the GEMM kernels. An invalid code (3, in IQ1T rows or
- * in a grid entry) decodes as 0 - the caller must not pass one. */
+ * MMQ_IQ1C and MMQ_IQ1S keep their grid indices: per 16 values one dword with the two
+ * 11-bit indices and that half-block's s and delta signs (IQ1S repeats its per-32 s and
+ * sign), d per 4-block group, and a copy of the grid (2048 entries, 8 KiB) at the end of the
+ * packed buffer, which the GEMMs look up on chip (about 2.1 bits per value instead of the
+ * 3 of the expanded MMQ_IQ1T form). The two formats share one kernel form. An invalid code
+ * (3, in IQ1T rows or in a grid entry) decodes as 0 - the caller must not pass one. */
 mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux,
                               int64_t N, int64_t K, void* packed, void* stream);
 
@@ -219,7 +221,8 @@ size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
  * Decode batches (T <= 4, T*top_k <= 256) run the small-batch kernel per expert instead of
  * the prefill tiles (llama.cpp PR #304, Summary: small batches stay on a matrix-vector
  * kernel); the result is the same per-block contraction.
- * Block formats only; o must be MMQ_OUT_F32.
+ * Block formats only; o must be MMQ_OUT_F32. MMQ_IQ1C / MMQ_IQ1S: every expert must have
+ * been packed with the same grid (the decode-batch kernel reads the first matrix's copy).
  * Limits (MMQ_EINVAL before any launch): T * top_k <= 2^24; outside the decode-batch case,
  * one expert's packed matrix must keep its fragment and scale regions below 2 GiB each
  * (e.g. N * K < 2^31 values of q8_0) and the act buffer's value region below 2 GiB

@@ -17,6 +17,9 @@ Layout, with Np = N rounded up to 32, NT = Np/32, KB = K/32, KBp = KB rounded up
                             (byte i of X0: low nibble 16h+i, high 16h+4+i)
         iq1t                FB = 256: one dword, value i of the lane at bits 8(i%4) + 2(i/4),
                             the 2-bit code c = g+1
+        iq1c, iq1s          FB = 256: one dword W = ia << 2 | meta << 13 | ib << 20, ia and ib the
+                            11-bit grid indices of the lane's 8-value groups 2h and 2h+1, meta =
+                            s | sigma_a << 3 | sigma_b << 4 (iq1s: its per-32 s and sign twice)
   region 1 (256-aligned, after region 0): one dword per (row n, block b) at
       ((nt*KBp + b)*32 + r)*4; i8_row instead: f32 sw[n] for n < Np
         q8_0, q4_0   f16 d | 0
@@ -25,14 +28,20 @@ Layout, with Np = N rounded up to 32, NT = Np/32, KB = K/32, KBp = KB rounded up
         iq1t         f16 d | meta0 << 16 | meta1 << 24, meta_h = s_h | sigma_a << 3 | sigma_b << 4
                      for the block's 16-value half h (its sub-scale and its two 8-value groups'
                      sign bits)
+        iq1c, iq1s   instead f16 d of the row's super-block per (row n, 4-block group g = b/4)
+                     at ((nt*(KBp/4) + g)*32 + r)*2
   region 2 (q4_K, q6_K; 256-aligned, after region 1), indexed like region 1:
         q4_K         f32 -dmin*m
         q6_K         the hi | lo split of d*sc for the block's last 16 values
+        iq1c, iq1s   the grid: 2048 dwords, entry i = the 8 codes of index i with code j at bits
+                     8(j%4) + 2(j/4)
   Every byte of a padding row (n >= N) or padding block (b >= KB) is zero.
 """
 import numpy as np
 
-FB = {"q8_0": 1024, "q4_0": 512, "q4_K": 512, "iq1t": 256, "q6_K": 1024, "i8_row": 1024}
+FB = {"q8_0": 1024, "q4_0": 512, "q4_K": 512, "iq1t": 256, "q6_K": 1024, "i8_row": 1024, "iq1c": 256,
+      "iq1s": 256}
+GRIDDED = ("iq1c", "iq1s")
 
 
 def _ru(a, b):
@@ -48,10 +57,44 @@ def dims(N, K):
 def offsets(fmt, N, K):
     Np, NT, KB, KBp = dims(N, K)
     scale = _ru(NT * KBp * FB[fmt], 256)
-    sb = Np * 4 if fmt == "i8_row" else Np * KBp * 4
+    sb = Np * 4 if fmt == "i8_row" else Np * (KBp // 4) * 2 if fmt in GRIDDED else Np * KBp * 4
     mn = scale + _ru(sb, 256)
-    total = mn + (_ru(Np * KBp * 4, 256) if fmt in ("q4_K", "q6_K") else 0)
+    total = mn + (_ru(Np * KBp * 4, 256) if fmt in ("q4_K", "q6_K") else 2048 * 4 if fmt in GRIDDED else 0)
     return scale, mn, total
+
+
+def spread(entry):
+    """A grid entry's 8 codes (value j at bits 2j) moved to bits 8(j%4) + 2(j/4)."""
+    e = np.asarray(entry, np.uint32)
+    w = np.zeros(e.shape, np.uint32)
+    for j in range(8):
+        w |= ((e >> np.uint32(2 * j)) & np.uint32(3)) << np.uint32(8 * (j & 3) + 2 * (j >> 2))
+    return w
+
+
+def _gridded(fmt, raw, N, K):
+    """Per (n, block, half): W; per (n, super-block): d bits."""
+    raw = np.asarray(raw, np.uint8).reshape(N, -1)
+    SB = K // 256
+    if fmt == "iq1c":
+        b = raw.reshape(N, SB, 56)
+        qh = np.stack([b[..., 32:48] & 0xF, b[..., 32:48] >> 4], axis=-1).reshape(N, SB, 32).astype(np.uint32)
+        idx = b[..., 0:32].astype(np.uint32) | ((qh & 7) << 8)                            # [N, SB, 32 groups]
+        sg = qh >> 3
+        sbits = np.unpackbits(b[..., 48:54], axis=-1, bitorder="little")[..., :48].reshape(N, SB, 16, 3)
+        s16 = (sbits.astype(np.uint32) * np.array([1, 2, 4], np.uint32)).sum(-1)         # [N, SB, 16 halves]
+        d = (b[..., 54].astype(np.uint32) | (b[..., 55].astype(np.uint32) << 8))
+    else:
+        b = raw.reshape(N, SB, 50)
+        qh = (b[..., 34:50:2].astype(np.uint32) | (b[..., 35:50:2].astype(np.uint32) << 8))   # [N, SB, 8]
+        hi = np.stack([(qh >> (3 * j)) & 7 for j in range(4)], axis=-1)                      # [N, SB, 8, 4]
+        idx = (b[..., 2:34].astype(np.uint32).reshape(N, SB, 8, 4) | (hi << 8)).reshape(N, SB, 32)
+        sg = np.repeat((qh >> 15) & 1, 4, axis=-1)
+        s16 = np.repeat((qh >> 12) & 7, 2, axis=-1)
+        d = (b[..., 0].astype(np.uint32) | (b[..., 1].astype(np.uint32) << 8))
+    meta = s16 | (sg[..., 0::2] << 3) | (sg[..., 1::2] << 4)                              # per half
+    W = (idx[..., 0::2] << 2) | (meta << 13) | (idx[..., 1::2] << 20)                     # [N, SB, 16 halves]
+    return W.reshape(N, K // 32, 2), d
 
 
 def _f16_bits(v):
@@ -148,11 +191,22 @@ def _lane_bytes(fmt, lanes):
 
 
 def pack(fmt, raw, N, K, row_scale=None, fill=0):
-    """The packed buffer (uint8) the layout above prescribes for raw weight rows. The
-    alignment gaps between regions (not written by the repack) hold `fill`."""
+    """The packed buffer (uint8) the layout above prescribes for raw weight rows (row_scale:
+    the f32 row scales of i8_row, the grid of iq1c / iq1s). The alignment gaps between regions
+    (not written by the repack) hold `fill`."""
     Np, NT, KB, KBp = dims(N, K)
     scale_off, min_off, total = offsets(fmt, N, K)
     buf = np.full(total, fill, np.uint8)
+    if fmt in GRIDDED:
+        W, d = _gridded(fmt, raw, N, K)
+        full = np.zeros((Np, KBp, 2), np.uint32)
+        full[:N, :KB] = W
+        buf[:NT * KBp * 256] = full.reshape(NT, 32, KBp, 2).transpose(0, 2, 3, 1).reshape(-1).view(np.uint8)
+        dd = np.zeros((Np, KBp // 4), np.uint16)
+        dd[:N, :KB // 4] = np.repeat(d, 2, axis=1)
+        buf[scale_off:scale_off + Np * (KBp // 4) * 2] = dd.reshape(NT, 32, KBp // 4).transpose(0, 2, 1).reshape(-1).view(np.uint8)
+        buf[min_off:min_off + 8192] = spread(row_scale).view(np.uint8)         # row_scale: the grid
+        return buf
     if fmt == "i8_row":
         v = np.asarray(raw, np.int8).reshape(N, K).astype(np.int64)
         sc1 = sc2 = None
@@ -214,3 +268,16 @@ def scale_dwords(fmt, buf, N, K, region=1):
     off = scale_off if region == 1 else min_off
     a = np.asarray(buf, np.uint8)[off:off + Np * KBp * 4].copy().view(np.uint32)
     return a.reshape(NT, KBp, 32).transpose(0, 2, 1).reshape(Np, KBp)[:N, :KB]
+
+
+def gridded_words(fmt, buf, N, K):
+    """iq1c / iq1s: the lane dwords W as uint32 [N, K/32, 2] and the d bits [N, K/256] (the
+    copies of each super-block's d in its two 4-block groups must agree)."""
+    Np, NT, KB, KBp = dims(N, K)
+    scale_off, _, _ = offsets(fmt, N, K)
+    b = np.asarray(buf, np.uint8)
+    W = b[:NT * KBp * 256].copy().view(np.uint32).reshape(NT, KBp, 2, 32).transpose(0, 3, 1, 2).reshape(Np, KBp, 2)
+    d = b[scale_off:scale_off + Np * (KBp // 4) * 2].copy().view(np.uint16).reshape(NT, KBp // 4, 32)
+    d = d.transpose(0, 2, 1).reshape(Np, KBp // 4)[:N, :KB // 4]
+    assert np.array_equal(d[:, 0::2], d[:, 1::2])            # both 4-block groups of a super-block
+    return W[:N, :KB], d[:, 0::2]

@@ -76,10 +76,11 @@ def test_packed_bytes(mmq):
     assert mmq.packed_bytes("i8_row", 33, 32) == 2 * 8 * 1024 + 256
     assert mmq.packed_bytes("q4_K", 32, 128) == 0      # Q4_K needs K % 256 == 0
     assert mmq.packed_bytes("iq1t", 32, 200) == 0
-    # iq1c is repacked into the iq1t panels: same packed size, K % 256 required
-    assert mmq.packed_bytes("iq1c", 40, 512) == mmq.packed_bytes("iq1t", 40, 512)
+    # iq1c / iq1s grid-index panels (K % 256 required): 256 B index fragments per (tile,
+    # block), f16 d per (row, 4-block group), then the 8 KiB grid; iq1s the same layout
+    assert mmq.packed_bytes("iq1c", 40, 512) == 2 * 16 * 256 + 64 * 4 * 2 + 8192   # Np = 64, KBp = 16
     assert mmq.packed_bytes("iq1c", 32, 288) == 0
-    assert mmq.packed_bytes("iq1s", 40, 512) == mmq.packed_bytes("iq1t", 40, 512)
+    assert mmq.packed_bytes("iq1s", 40, 512) == mmq.packed_bytes("iq1c", 40, 512)
     # q6_K: int8 fragments plus two scale-dword regions (one per 16-value half)
     assert mmq.packed_bytes("q6_K", 32, 256) == 8 * 1024 + 2 * 32 * 8 * 4
     assert mmq.packed_bytes("q6_K", 32, 224) == 0

@@ -3,11 +3,13 @@ through the C ABI.
 
 iq1c and iq1s rows carry an 11-bit grid index per 8 values (llama.cpp PR #304 description;
 the grid is the self-generated gen.IQ1C_GRID, an input of the repack); iq1c has s per 16 and
-the delta sign per 8 values, iq1s both per 32. The repack expands each index through the grid
-once into the iq1t panel form, so the checks are:
+the delta sign per 8 values, iq1s both per 32. The repack keeps the indices: one dword per
+fragment lane (two indices and the lane's s and signs), d per (row, 4-block group) and the grid
+itself, which the GEMMs look up in LDS. The checks are:
 
-* the packed buffer equals, byte for byte, the iq1t repack of the same values written in the
-  iq1t layout (the iq1t path has its own parity tests);
+* the packed buffer equals, byte for byte, tests/packmodel.py's model of that layout;
+* the same values written in the iq1t layout give bit-identical f32 outputs (both forms feed
+  the same matrix-core fold), dense and decode;
 * dense prefill: q8_1 bit-exact, the folded int32 block partials bit-exact, f32 within
   max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4), on shapes
   with ragged M and N tails;
@@ -19,6 +21,7 @@ import numpy as np
 import pytest
 
 import gen
+import packmodel
 import parity
 
 pytestmark = pytest.mark.gpu
@@ -94,15 +97,34 @@ def _pack(env, raw, N, K, fmt="iq1c"):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(32, 256), (33, 768), (300, 512), (64, 4096)])
-def test_packed_equals_iq1t_packing_of_same_values(env, fmt, N, K):
-    torch, mmq, _, _ = env
+def test_packed_matches_the_layout_model(env, fmt, N, K):
+    torch, mmq, _, grid = env
     print(f"[case] {fmt} repack N={N} K={K}", flush=True)
     raw = gen.weights(fmt, N, K, seed=N + K, cfg=85)
-    assert mmq.packed_bytes(fmt, N, K) == mmq.packed_bytes("iq1t", N, K)
-    pc = _pack(env, raw, N, K, fmt)
-    pt = mmq.repack_weights("iq1t", torch.from_numpy(AS_IQ1T[fmt](raw, N, K, gen.IQ1C_GRID)).to("cuda:0"), N, K)
+    out = torch.full((mmq.packed_bytes(fmt, N, K),), 0xA5, dtype=torch.uint8, device="cuda:0")
+    mmq.repack_weights(fmt, torch.from_numpy(np.ascontiguousarray(raw)).to("cuda:0"), N, K, grid=grid, out=out)
     torch.cuda.synchronize()
-    assert np.array_equal(pc.cpu().numpy(), pt.cpu().numpy())
+    got = out.cpu().numpy()
+    want = packmodel.pack(fmt, raw, N, K, row_scale=gen.IQ1C_GRID, fill=0xA5)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (fmt, N, K, int(bad.size), int(bad[0]) if bad.size else None)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", [(130, 300, 512), (4, 97, 4096), (1, 33, 768)])
+def test_same_values_as_iq1t_same_outputs(env, fmt, M, N, K):
+    torch, mmq, _, _ = env
+    dev = torch.device("cuda:0")
+    print(f"[case] {fmt} vs iq1t M={M} N={N} K={K}", flush=True)
+    raw = gen.weights(fmt, N, K, seed=M + N + K, cfg=89)
+    x = gen.act_f32(M, K, seed=M + N, cfg=89, outlier_rate=1e-2)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
+    pc = _pack(env, raw, N, K, fmt)
+    pt = mmq.repack_weights("iq1t", torch.from_numpy(AS_IQ1T[fmt](raw, N, K, gen.IQ1C_GRID)).to(dev), N, K)
+    oc = mmq.gemm(fmt, pc, act, M, N, K, "f32")
+    ot = mmq.gemm("iq1t", pt, act, M, N, K, "f32")
+    torch.cuda.synchronize()
+    assert np.array_equal(oc.cpu().numpy().view(np.uint32), ot.cpu().numpy().view(np.uint32))
 
 
 SHAPES = [(1, 32, 256), (17, 33, 256), (65, 97, 768), (130, 300, 512), (256, 256, 1024)]

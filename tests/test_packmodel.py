@@ -62,3 +62,28 @@ def test_model_size_is_the_library_size(fmt):
     import block_quantized_int8_amd as mmq
     for N, K in [(32, 256), (45, 768), (300, 4096)]:
         assert packmodel.offsets(fmt, N, K)[2] == mmq.packed_bytes(fmt, N, K), (N, K)
+
+
+@pytest.mark.parametrize("fmt", ["iq1c", "iq1s"])
+@pytest.mark.parametrize("N,K", [(32, 256), (45, 768), (70, 512)])
+def test_model_grid_index_panels_decode_to_the_oracle(orc, fmt, N, K):
+    """The grid-index panels: each lane dword names the grid entries of its two 8-value groups
+    and carries the half's s and signs; with the spread grid of region 2 and d of region 1
+    they give the oracle's values 8g +- 1, per-16 factors (2s+1) and scales d(2s+1)/8."""
+    raw = gen.weights(fmt, N, K, seed=N + K, cfg=127)
+    buf = packmodel.pack(fmt, raw, N, K, row_scale=gen.IQ1C_GRID)
+    W, dbits = packmodel.gridded_words(fmt, buf, N, K)
+    mo = packmodel.offsets(fmt, N, K)[1]
+    gtab = np.asarray(buf[mo:mo + 8192]).copy().view(np.uint32)
+    assert np.array_equal(gtab, packmodel.spread(gen.IQ1C_GRID))
+    for n in range(N):
+        wq, wd, wm, mult = orc.decode_row_c(fmt, raw[n], K, grid=gen.IQ1C_GRID)
+        w = W[n].reshape(-1)                                   # per 16-value half
+        ia, ib, meta = (w >> 2) & 0x7FF, (w >> 20) & 0x7FF, (w >> 13) & 0x1F
+        assert np.all((w & 3) == 0) and np.all((w >> 18) & 3 == 0) and np.all(w >> 31 == 0)
+        codes = np.stack([(gen.IQ1C_GRID[ia] >> (2 * j)) & 3 for j in range(8)] +
+                         [(gen.IQ1C_GRID[ib] >> (2 * j)) & 3 for j in range(8)], axis=1).reshape(-1)
+        sig = np.stack([(meta >> 3) & 1, (meta >> 4) & 1], axis=1).reshape(-1)
+        assert np.array_equal(8 * (codes.astype(np.int64) - 1) + np.where(np.repeat(sig, 8) == 1, -1, 1), wq), n
+        d = np.repeat(dbits[n].view(np.float16).astype(np.float64), 16)
+        assert np.array_equal(d * (2 * (meta & 7) + 1) / 8, wd), n
