@@ -44,7 +44,7 @@
 //     folded per-32 integer sum_h (2s_h+1) P16_h - from three matrix-core ops per tile and
 //     block (int8 dot, scale, conversion), and only d remains as a scale.
 //
-// Operands reach LDS by direct global->LDS DMA (global_load_lds_dwordx4: each lane names its
+// Operands reach LDS by direct buffer->LDS DMA (buffer_load_dwordx4 ... lds: each lane names its
 // own 16-byte source, the wave writes 1 KB of LDS), double-buffered per 4-block stage: stage
 // s+1 is in flight while stage s runs its MFMAs (minfer R1 section 2.3: exposed staging
 // latency was the largest single cost; metainfer section 1: global loads of stage i+1 before
@@ -187,27 +187,32 @@ template <> struct BT<MMQ_IQ1T> {
 
 // iq1c / iq1s grid-index panels: one dword W = ia << 2 | meta << 13 | ib << 20 per lane, ia and
 // ib the 11-bit grid indices of its two 8-value groups, meta as for iq1t. The grid sits in LDS
-// after the iq1t meta table, spread into the iq1t code order (value j of an entry at bits
-// 8(j%4) + 2(j/4)), so the lane's code dword is entry(ia) | entry(ib) << 4 and everything after
-// the lookups is the iq1t step. The scale d comes per (row, 4-block stage) from its own region.
+// after the iq1t meta table as two tables of 2048 dwords: entry e's v_perm selectors of its
+// values 0-3 (byte b = code of value b) and of its values 4-7. The lane's four selector dwords
+// are then lo(ia), hi(ia), lo(ib), hi(ib), read with the two index fields of W as byte offsets
+// (ia * 4 and ib * 4), and everything after the lookups is the iq1t step. The scale d comes per
+// (row, 4-block stage) from its own region.
 template <> struct BT<MMQ_IQ1C> : BT<MMQ_IQ1T> {
     static constexpr bool GRID = true;
-    static constexpr int TAB_BYTES = TAB_WORDS * 4 + 2048 * 4;
-    struct Raw { uint32_t W, ga, gb; uint2 t; };
+    static constexpr int GRID_HI = 2048 * 4;                       // offset of the hi table
+    static constexpr int TAB_BYTES = TAB_WORDS * 4 + 2 * GRID_HI;
+    struct Raw { uint32_t W; uint2 ga, gb, t; };
     __device__ static void fetch(const uint8_t* frag, int lane, Raw& r) {
         r.W = *reinterpret_cast<const uint32_t*>(frag + lane * 4);
     }
     __device__ static void mid(Raw& r, uint32_t, int, const uint8_t* tab) {
         const uint8_t* g = tab + TAB_WORDS * 4;
-        r.ga = *reinterpret_cast<const uint32_t*>(g + (r.W & 0x1FFCu));     // ia * 4
-        r.gb = *reinterpret_cast<const uint32_t*>(g + (r.W >> 18));         // ib * 4
+        const uint32_t oa = r.W & 0x1FFCu, ob = r.W >> 18;            // ia * 4, ib * 4
+        r.ga = make_uint2(*reinterpret_cast<const uint32_t*>(g + oa), *reinterpret_cast<const uint32_t*>(g + GRID_HI + oa));
+        r.gb = make_uint2(*reinterpret_cast<const uint32_t*>(g + ob), *reinterpret_cast<const uint32_t*>(g + GRID_HI + ob));
         r.t = *reinterpret_cast<const uint2*>(tab + ((r.W >> 10) & 0xF8u));  // meta * 8
     }
     __device__ static void unpack(const Raw& r, v4i* a, int) {
-        BT<MMQ_IQ1T>::Raw q;
-        q.C = r.ga | (r.gb << 4);
-        q.t = r.t;
-        BT<MMQ_IQ1T>::unpack(q, a, 0);
+        const uint32_t lut = r.t.x;
+        a[0][0] = (int)__builtin_amdgcn_perm(lut, lut, r.ga.x);
+        a[0][1] = (int)__builtin_amdgcn_perm(lut, lut, r.ga.y);
+        a[0][2] = (int)__builtin_amdgcn_perm(lut, lut, r.gb.x);
+        a[0][3] = (int)__builtin_amdgcn_perm(lut, lut, r.gb.y);
     }
     __device__ static uint32_t scale_op(uint32_t w) { return w; }            // f16 d
 };
@@ -324,16 +329,21 @@ struct BlockArgs {
     int E, top_k, ntiles_n, unit_rows;
 };
 
-typedef __attribute__((address_space(1))) const void gmem_t;
-typedef __attribute__((address_space(3))) void lmem_t;
-
-// One wave-wide 16-byte-per-lane DMA: lane l's 16 source bytes land at lds + 16 l.
-__device__ inline void dma16(const uint8_t* src, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds((gmem_t*)src, (lmem_t*)lds, 16, 0, 0);
+// A buffer descriptor over one operand region (base in scalar registers, no range clamp: every
+// offset used stays inside the region by construction).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t region_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
 }
-// The same with 4 bytes per lane: lane l's dword lands at lds + 4 l.
-__device__ inline void dma4(const uint8_t* src, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds((gmem_t*)src, (lmem_t*)lds, 4, 0, 0);
+typedef __attribute__((address_space(3))) void lmem_t;
+// One wave-wide buffer->LDS DMA of 16 (4) bytes per lane: lane l's bytes at region offset
+// voff + soff land at lds + 16 l (4 l). voff is the lane's fixed offset, soff the wave-uniform
+// offset of the stage (a scalar register, so advancing a stage costs no vector instruction).
+__device__ inline void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lmem_t*)lds, 16, (int)voff, soff, 0, 0);
+}
+__device__ inline void dma4(rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lmem_t*)lds, 4, (int)voff, soff, 0, 0);
 }
 
 // an f16x4 operand with the dword `lo` in slots 0-1 and zeros in slots 2-3
@@ -404,14 +414,19 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     if constexpr (FMT == MMQ_IQ1T || FMT == MMQ_IQ1C) {
         if (tid < T::TAB_WORDS) reinterpret_cast<uint32_t*>(tab)[tid] = T::table_word(tid >> 1, tid & 1);
     }
-    if constexpr (T::GRID) {          // the packed matrix's grid (its last region) into LDS
+    if constexpr (T::GRID) {          // the packed matrix's grid (its last region) as selector tables
         const uint32_t* g = reinterpret_cast<const uint32_t*>(wbase + args.w_min_off);
         uint32_t* lg = reinterpret_cast<uint32_t*>(tab) + T::TAB_WORDS;
-        for (int i = tid; i < 2048; i += C::NTH) lg[i] = g[i];
+        for (int i = tid; i < 2048; i += C::NTH) {
+            const uint32_t w = g[i];
+            lg[i] = w & 0x03030303u;
+            lg[2048 + i] = (w >> 2) & 0x03030303u;
+        }
     }
 
-    // ---- DMA plan: per chunk this lane keeps a 32-bit source offset from the chunk's region
-    // base, advanced by a fixed stride per stage; the chunk's LDS offset is wave-uniform.
+    // ---- DMA plan: per chunk this lane keeps its 32-bit source offset in stage 0 from the
+    // chunk's region base; stage st adds st times the region's stage stride as a wave-uniform
+    // offset. The chunk's LDS offset is wave-uniform.
     uint32_t goff[C::CPW];
     int ldso[C::CPW];
     int skind[C::CPW];                                       // scale slots: kind, wave-uniform
@@ -484,31 +499,32 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
             }
         }
     }
-    auto issue_chunk = [&](uint8_t* buf, int j) __attribute__((always_inline)) {
+    const rsrc_t rs_w = region_rsrc(wbase), rs_x = region_rsrc(args.xq), rs_ws = region_rsrc(wsc);
+    const rsrc_t rs_wm = region_rsrc(wmn), rs_xs = region_rsrc(args.xs2), rs_xm = region_rsrc(args.xsx);
+    const rsrc_t rs_xg = region_rsrc(args.xg);
+    // chunk j of stage st into stage buffer buf
+    auto issue_chunk = [&](uint8_t* buf, int j, int st) __attribute__((always_inline)) {
         const int k = C::slot_kind(j);
         uint8_t* dst = buf + __builtin_amdgcn_readfirstlane(ldso[j]);
         if (k == C::K_WF) {
-            dma16(wbase + goff[j], dst);
-            goff[j] += KS * T::FB;
+            dma16(rs_w, dst, goff[j], st * (KS * T::FB));
         } else if (k == C::K_XF) {
-            dma16(args.xq + goff[j], dst);
-            goff[j] += KS * 1024;
+            dma16(rs_x, dst, goff[j], st * (KS * 1024));
         } else {
             const int sk = skind[j];
             if (sk == C::S_NONE) return;
-            const uint8_t* base = sk == C::S_WS ? wsc : sk == C::S_XS ? reinterpret_cast<const uint8_t*>(args.xs2)
-                                : sk == C::S_WM ? wmn : sk == C::S_XM ? reinterpret_cast<const uint8_t*>(args.xsx)
-                                : reinterpret_cast<const uint8_t*>(args.xg);
+            const rsrc_t r = sk == C::S_WS ? rs_ws : sk == C::S_XS ? rs_xs : sk == C::S_WM ? rs_wm
+                           : sk == C::S_XM ? rs_xm : rs_xg;
+            const int stride = sk == C::S_XG ? KS * 256 : (T::GRID && sk == C::S_WS) ? 64 : C::SCB;
             if ((is_gather(MODE) && (sk == C::S_XS || sk == C::S_XM || sk == C::S_XG)) || (T::GRID && sk == C::S_WS))
-                dma4(base + goff[j], dst);
+                dma4(r, dst, goff[j], st * stride);
             else
-                dma16(base + goff[j], dst);
-            goff[j] += sk == C::S_XG ? KS * 256 : (T::GRID && sk == C::S_WS) ? 64 : C::SCB;
+                dma16(r, dst, goff[j], st * stride);
         }
     };
-    auto issue_stage = [&](uint8_t* buf) __attribute__((always_inline)) {
+    auto issue_stage = [&](uint8_t* buf, int st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < C::CPW; ++j) issue_chunk(buf, j);
+        for (int j = 0; j < C::CPW; ++j) issue_chunk(buf, j, st);
     };
 
     v16f acc[RT][CT];
@@ -741,7 +757,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
                     const int st = kb * NT_ + t;
 #pragma unroll
                     for (int j = st * PER; j < st * PER + PER; ++j)
-                        if (j < C::CPW) issue_chunk(nxt, j);
+                        if (j < C::CPW) issue_chunk(nxt, j, s + 1);
                 }
                 if (kb + 1 < KS) {
                     if (t == 0) fetch(cur, kb + 1, raw);
@@ -803,7 +819,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     };
 
     const int nstages = KBp / KS;                // even: KBp is a multiple of 8
-    issue_stage(buf0);
+    issue_stage(buf0, 0);
     for (int s = 0; s < nstages; s += 2) {
         __builtin_amdgcn_s_waitcnt(0x3f70);      // vmcnt(0): this wave's DMA of stage s landed
         __syncthreads();                          // ... and everyone's; stage s-1 fully consumed

@@ -24,8 +24,8 @@
 namespace {
 
 constexpr int QG = 2;             // blocks per wave (one 32-row tile x 64 values)
-constexpr int QWAVES = 4;         // waves per workgroup
-constexpr int QBLOCKS = 1024;     // workgroups at most (four per CU); waves then loop over units
+constexpr int QWAVES = 16;        // waves per workgroup
+constexpr int QBLOCKS = 256;      // workgroups at most (one per CU); waves then loop over units
 
 __device__ inline uint32_t pack4(int a, int b, int c, int d) {
     return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
