@@ -37,7 +37,6 @@
 namespace mmq {
 namespace {
 
-typedef __attribute__((address_space(1))) const void gmem_t;
 typedef __attribute__((address_space(3))) void lmem_t;
 
 // Workgroup barrier for the staging pipeline: LDS is the only memory shared through it, so it
@@ -47,6 +46,14 @@ __device__ inline void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts
 
 // s_waitcnt immediate: wait until at most n vector-memory operations are outstanding
 constexpr int vm_wait(int n) { return 0x3f70 | (n & 15) | ((n >> 4) << 14); }
+
+// One wave-wide buffer->LDS DMA of 16 bytes per lane: lane l's bytes at base + voff + soff land
+// at lds + 16 l; voff is the lane's fixed offset, soff the wave-uniform stage offset (a scalar
+// register, so advancing a stage costs no vector instruction).
+__device__ inline void buf_dma16(const uint8_t* base, uint8_t* lds, uint32_t voff, int soff) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lmem_t*)lds, 16, (int)voff, soff, 0, 0);
+}
 
 constexpr int KS = 2;                  // blocks per stage: a token chunk row is 2 x 32 bytes
 constexpr int NBUF = 4;                // LDS stage buffers
@@ -131,9 +138,9 @@ __global__ __launch_bounds__(WM * KSP * 64, 1) void w8a8_kernel(W8Args g) {
     // line) into buffers nobody reads any more.
     auto issue_chunk = [&](int j, int t) __attribute__((always_inline)) {
         const uint8_t* base = j * C::NW < C::CW_ALL ? g.wf : g.a;
-        const uint32_t off = t < nst ? goff[j] + (uint32_t)t * (KS * 1024) : 0u;
+        const int soff = __builtin_amdgcn_readfirstlane(t < nst ? t * (KS * 1024) : 0);
         uint8_t* dst = smem + (t & (NBUF - 1)) * C::BUF + __builtin_amdgcn_readfirstlane(ldso[j]);
-        __builtin_amdgcn_global_load_lds((gmem_t*)(base + off), (lmem_t*)dst, 16, 0, 0);
+        buf_dma16(base, dst, goff[j], soff);
     };
 
     // fragment read offsets inside a stage buffer (lane * 16 inside each 1 KB fragment)
