@@ -8,17 +8,19 @@
 //
 // The int8 MFMA needs no vector work per block, so the kernel is bound by how fast operands
 // reach the matrix core. Measured on gfx950: one v_mfma_i32_32x32x32_i8 issues every 32 cycles
-// per wave; global->LDS DMA moves about 64 bytes per clock per CU (bound by the texture
-// addresser, also for L2 hits); a CU reads up to ~240 B/clk of LDS. A 7B tensor-parallel share
-// (M = 3072, N = 1536) holds only 18 32x32 output tiles per CU, so each workgroup is one CU's
-// share, 96 weight rows x 192 token rows, whose four waves split it as 2 token halves x 2
-// halves of K (one wave per SIMD, 3 x 3 tiles each); the two K halves are added in LDS before
-// the epilogue. A CU then needs 2 x (96 + 192) x 32 bytes = 18 KB of operands per 288
-// matrix-core cycles (9 MFMAs per SIMD), about what the DMA delivers, so the kernel's job is
-// to keep both busy at once:
+// per wave; global->LDS DMA moves at most about 64 bytes per clock per CU (bound by the texture
+// addresser, also for L2 hits), and about half that inside this kernel, where every CU of an
+// XCD streams its panels through the shared L2 at once; a CU reads up to ~240 B/clk of LDS. A
+// 7B tensor-parallel share (M = 3072, N = 1536) holds only 18 32x32 output tiles per CU, so
+// each workgroup is one CU's share, 96 weight rows x 192 token rows. Its twelve waves split it
+// as 6 token tiles x 2 halves of K (three waves per SIMD, each 3 weight tiles x 1 token tile);
+// the two K halves are added in LDS before the epilogue. A CU then needs 2 x (96 + 192) x 32
+// bytes = 18 KB of operands per 288 matrix-core cycles (9 MFMAs per SIMD), more than the DMA
+// delivers, so the kernel's job is to keep the DMA busy and the matrix core fed:
 //  - the DMA of each 2-block stage is spread evenly between the MFMAs (a vector-memory
 //    instruction the texture unit cannot take yet stalls the wave's in-order issue, so a burst
-//    of them would hold the matrix core idle);
+//    of them would hold the matrix core idle), and three waves per SIMD cover each other's
+//    stalls (12 waves measured 2.3% faster than 4 waves of 3 x 3 tiles);
 //  - four LDS stage buffers: stage t's DMA is issued over the blocks of stages t-4 and t-3 and
 //    waited for in the middle of stage t-1, about 2.5 stages later; the wait and the barrier
 //    sit in the middle of a stage, so the next stage's first fragments are read before it
@@ -179,9 +181,9 @@ __global__ __launch_bounds__(WM * KSP * 64, 1) void w8a8_kernel(W8Args g) {
         for (int ct = 0; ct < CT; ++ct)
             o.b[ct] = *reinterpret_cast<const v4i*>(buf + xoff + (ct * KS + kb) * 1024);
     };
-    // one block: the wave's RT x CT MFMAs, each followed by one of the next block's fragment
-    // reads (block nkb of `nbuf`) and one DMA chunk of stage t (chunks j0..j1-1), each step
-    // fenced so the scheduler keeps that order
+    // one block: the wave's RT x CT MFMAs, each followed by its share of the next block's
+    // fragment reads (block nkb of `nbuf`) and of the DMA chunks of stage t (chunks j0..j1-1),
+    // each step fenced so the scheduler keeps that order
     auto block = [&](const Ops& o, Ops& on, const uint8_t* nbuf, int nkb, int j0, int j1, int t)
         __attribute__((always_inline)) {
 #pragma unroll
@@ -190,10 +192,15 @@ __global__ __launch_bounds__(WM * KSP * 64, 1) void w8a8_kernel(W8Args g) {
             const int rt = i / CT, ct = i % CT;
             acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[rt], o.b[ct], acc[rt][ct], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (i < RT)
-                on.a[i] = *reinterpret_cast<const v4i*>(nbuf + woff + (i * KS + nkb) * 1024);
-            else if (i < RT + CT)
-                on.b[i - RT] = *reinterpret_cast<const v4i*>(nbuf + xoff + ((i - RT) * KS + nkb) * 1024);
+            // the RT + CT fragment reads spread evenly over the NT_ steps
+            constexpr int F = RT + CT;
+#pragma unroll
+            for (int f = (i * F) / C::NT_; f < ((i + 1) * F) / C::NT_; ++f) {
+                if (f < RT)
+                    on.a[f] = *reinterpret_cast<const v4i*>(nbuf + woff + (f * KS + nkb) * 1024);
+                else
+                    on.b[f - RT] = *reinterpret_cast<const v4i*>(nbuf + xoff + ((f - RT) * KS + nkb) * 1024);
+            }
             const int nd = j1 - j0;                          // DMAs spread evenly: one at the
             if ((i * nd) / C::NT_ != ((i + 1) * nd) / C::NT_)  // steps where i*nd/NT_ steps up
                 issue_chunk(j0 + (i * nd) / C::NT_, t);
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(WM * KSP * 64, 1) void w8a8_kernel(W8Args g) {
 }
 
 // 96 weight rows x 192 token rows per workgroup (see the notes at the top).
-constexpr int RT = 3, CT = 3, WM = 2, KSP = 2;
+constexpr int RT = 3, CT = 1, WM = 6, KSP = 2;
 using Cfg = W8Cfg<RT, CT, WM, KSP>;
 
 // Byte offsets inside one launch stay below 2^31 (they are 32-bit lane offsets) and a grid
