@@ -67,6 +67,10 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # (profiles/ holds the summaries), with the hash of the kernel sources they were measured on:
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
+    "q4_0_m2048_n4096_k4096": (168_367_369, "3b7050e972d25bd1"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (289_122_629 + 40_674, "0a04d98b318ab119"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (380_313_441 + 40_675, "0a04d98b318ab119"),
+    "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],
