@@ -71,6 +71,10 @@ MEASURED_TRAFFIC = {
     "moe_iq1c_e64_t512_top8_n2048_k4096": (289_122_629 + 40_674, "0a04d98b318ab119"),
     "moe_iq1t_e64_t512_top8_n2048_k4096": (380_313_441 + 40_675, "0a04d98b318ab119"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
+    "q4_K_m512_n14336_k4096": (98_670_108, "3b7050e972d25bd1"),
+    "q6_K_m2048_n4096_k11008": (470_992_203, "3b7050e972d25bd1"),
+    "dec_q4_0_m8_n4096_k4096": (11_125_303, "c663d0b66107f67e"),
+    "dec_q4_K_m8_n14336_k4096": (45_160_311, "c663d0b66107f67e"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],
