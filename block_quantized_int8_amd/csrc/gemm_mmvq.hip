@@ -253,13 +253,16 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
 
+    // the grid (the packed matrix's last region; MUL_MAT_ID: expert 0's); on the LDS path its
+    // loads go out with the token staging loads and share their barrier (stage() below)
+    const uint32_t* const gsrc = reinterpret_cast<const uint32_t*>(a.w + a.w_min_off);
     if constexpr (FMT == MMQ_IQ1T || FMT == MMQ_IQ1C) {
         if (tid < 16) tab[tid] = T::table(tid);
-        if constexpr (T::GRID) {          // the grid (the packed matrix's last region; MUL_MAT_ID:
-            const uint32_t* gsrc = reinterpret_cast<const uint32_t*>(a.w + a.w_min_off);   // expert 0's)
-            for (int i = tid; i < 2048; i += MV_W * 64) gtab[i] = gsrc[i];
+        if constexpr (!(XL && T::GRID)) {
+            if constexpr (T::GRID)
+                for (int i = tid; i < 2048; i += MV_W * 64) gtab[i] = gsrc[i];
+            __syncthreads();
         }
-        __syncthreads();
     }
     const int KBp = a.KBp;
     const int nch = KBp / MV_CH;
@@ -515,11 +518,17 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
 
     // LDS path: the token rows 0..TOK-1 of every block go to slot (b*2 + h)*TOK + t (the tiled
     // xq keeps row t's values 16h..16h+15 of block b at lane h*32 + t; rows >= M are the
-    // buffer's zero padding). The staging loads are issued first, then the first two items'
-    // weight loads, then the LDS writes (which wait only for the staging loads) and a barrier
-    // that leaves the weight loads in flight.
+    // buffer's zero padding). The staging loads (and iq1c's grid) are issued first, then the
+    // first two items' weight loads, then the LDS writes (which wait only for the staging
+    // loads) and a barrier that leaves the weight loads in flight.
     constexpr int PER = XL ? (XSLOTS + MV_W * 64 - 1) / (MV_W * 64) : 1;
+    constexpr int GPER = (XL && T::GRID) ? 2048 / (MV_W * 64) : 1;
     v4i xv[PER];
+    uint32_t gv[GPER];
+    if constexpr (XL && T::GRID) {
+#pragma unroll
+        for (int u = 0; u < GPER; ++u) gv[u] = gsrc[tid + u * MV_W * 64];
+    }
     if constexpr (XL) {
         const int nslot = KBp * 2 * TOK;
 #pragma unroll
@@ -540,6 +549,10 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             if (tid == 0) {
                 const v4i z = {0, 0, 0, 0};
                 *reinterpret_cast<v4i*>(xl + XSLOTS * 16) = z;
+            }
+            if constexpr (T::GRID) {
+#pragma unroll
+                for (int u = 0; u < GPER; ++u) gtab[tid + u * MV_W * 64] = gv[u];
             }
             lds_barrier();
         }
