@@ -15,8 +15,9 @@
 //      output row.
 // No host round trip: the grids are sized for the worst case and workgroups past the actual
 // unit counts leave at once. With at most 4 tokens (a decode batch, where the gather tiles
-// would be nearly empty) step 2 is the decode kernel instead, over (batch of up to 8 of one
-// expert's pairs, 16-row group) units (gemm_mmvq.hip).
+// would be nearly empty) both steps are the decode kernel instead: each of its workgroups
+// groups the at most 256 pairs by expert itself (a rank sort in LDS) and runs (batch of up to 8
+// of one expert's pairs, 16-row group) units (gemm_mmvq.hip).
 #include <mutex>
 
 #include "mmq_internal.h"
@@ -161,6 +162,8 @@ hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void
                           void* out, void* workspace, size_t, hipStream_t s) {
     if (E > MAX_E) return hipErrorInvalidValue;
     const int64_t P = T * top_k;
+    // a decode batch of a few tokens: the decode kernel, which groups its <= 256 pairs itself
+    if (mmvq_id_ok(t, T, top_k, K)) return launch_mmvq_id(t, packed, E, act, T, top_k, N, K, ids, out, s);
     if (!gather_grid_ok(gemm_id_max_units(E, P), N)) return hipErrorInvalidValue;
     const IdWorkspace w = id_workspace(E, P);
     int32_t* ws = static_cast<int32_t*>(workspace);
@@ -172,9 +175,6 @@ hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void
                        gather_unit_tokens(), gather_tail_tokens(), offs, ufull, utail, perm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // a decode batch of a few tokens: the decode kernel
-    if (mmvq_id_ok(t, T, top_k, K))
-        return launch_mmvq_id(t, packed, E, act, T, top_k, N, K, offs, perm, out, s);
     return launch_block_gather(t, packed, E, act, T, top_k, N, K, offs, ufull, utail, perm,
                                (int)gemm_id_max_units(E, P), (int)(E < P ? E : P), out, s);
 }

@@ -212,10 +212,10 @@ struct MvArgs {
     int M, N, KBp, groups;      // groups: 16-row groups holding at least one real row
     void* out;
     int64_t ldo;
-    // MUL_MAT_ID with at most 16 tokens: the route kernel's pair offsets and expert order
+    // MUL_MAT_ID with at most 4 tokens: the routing ids themselves (each workgroup groups the
+    // at most 256 pairs by expert on its own, so no routing launch precedes this one)
     int64_t w_stride;           // bytes between experts' packed matrices
-    const int32_t* offs;        // [E+1] first pair of each expert in `perm`
-    const int32_t* perm;        // pair ids (token * top_k + slot) in expert order
+    const int32_t* ids;         // [P] expert of pair p = token * top_k + slot
     int E, top_k, P;
 };
 
@@ -277,30 +277,57 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     // more for an expert named by several slots of a token)
     int units = a.groups;
     if constexpr (ID) {
-        const int EPT = (a.E + MV_W * 64 - 1) / (MV_W * 64);         // experts per thread
-        const int e0 = min(tid * EPT, a.E), e1 = min(e0 + EPT, a.E);
-        int nb = 0;
-        for (int e = e0; e < e1; ++e) nb += (a.offs[e + 1] - a.offs[e] + TOK - 1) / TOK;
-        int inc = nb;                                                // inclusive scan, wave
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(inc, d, 64);
-            if (lane >= d) inc += o;
+        // Group the P <= 256 pairs by expert: key = expert << 8 | pair (ids outside [0, E) sort
+        // last as expert E), rank each key by counting the smaller ones, so s_pp lists the pairs
+        // in expert order; then a batch starts at every TOK-th position of an expert's run.
+        const int P = a.P;
+        int key = 0, e = a.E;
+        if (tid < P) {
+            const int id = a.ids[tid];
+            e = (id >= 0 && id < a.E) ? id : a.E;
+            key = (e << 8) | tid;
+            s_e[tid] = key;                                          // keys, for the ranking
         }
-        if (lane == 63) s_wt[wave] = inc;
         __syncthreads();
-        int u = inc - nb;
-        for (int w = 0; w < wave; ++w) u += s_wt[w];
-        if (tid == MV_W * 64 - 1) s_wt[MV_W] = u + nb;              // batches in all
-        for (int e = e0; e < e1; ++e) {
-            const int po = a.offs[e], c = a.offs[e + 1] - po;
-            for (int q = 0; q < c; q += TOK, ++u) {
-                s_e[u] = e;
-                s_po[u] = po + q;
-                s_me[u] = min(TOK, c - q);
+        int rank = 0, first = 0;                                     // first: the run's start
+        if (tid < P) {
+            for (int j = 0; j < P; ++j) {
+                const int kj = s_e[j];
+                rank += kj < key;
+                first += (kj >> 8) < e;
             }
         }
-        for (int q = tid; q < a.P; q += MV_W * 64) s_pp[q] = a.perm[q];
+        __syncthreads();
+        const bool start = tid < P && e < a.E && (rank - first) % TOK == 0;
+        if (tid < P) {
+            s_pp[rank] = tid;                                        // pairs in expert order
+            s_po[rank] = start ? 1 : 0;                              // batch-start flags
+            s_me[rank] = e;
+        }
+        __syncthreads();
+        // batch u: the u-th start flag in expert order (an exclusive scan over <= 256 flags)
+        int st = 0, cnt = 0, ex = 0, len = 0;
+        if (tid < P) {
+            st = s_po[tid];
+            ex = s_me[tid];
+            for (int j = 0; j < tid; ++j) cnt += s_po[j];
+            if (st) {
+                int l = 1;
+                while (l < TOK && tid + l < P && s_me[tid + l] == ex) ++l;
+                len = l;
+            }
+        }
+        if (tid == 0) {
+            int nb = 0;
+            for (int j = 0; j < P; ++j) nb += s_po[j];
+            s_wt[MV_W] = nb;                                         // batches in all
+        }
+        __syncthreads();
+        if (st) {
+            s_e[cnt] = ex;
+            s_po[cnt] = tid;                                         // first pair in expert order
+            s_me[cnt] = len;
+        }
         __syncthreads();
         units = s_wt[MV_W] * a.groups;
     }
@@ -635,8 +662,8 @@ bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K) {
 }
 
 hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void* act, int64_t T,
-                          int64_t top_k, int64_t N, int64_t K, const int32_t* offs,
-                          const int32_t* perm, void* out, hipStream_t s) {
+                          int64_t top_k, int64_t N, int64_t K, const int32_t* ids, void* out,
+                          hipStream_t s) {
     if (!mmvq_id_ok(t, T, top_k, K)) return hipErrorInvalidValue;
     const PackedLayout P = packed_layout(t, N, K);
     const ActQ81Layout L = act_q8_1_layout(T, K);
@@ -655,8 +682,7 @@ hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void
     args.xq = ab + L.xq_off;
     args.xs2 = reinterpret_cast<const uint32_t*>(ab + L.xs2_off);
     args.xsx = reinterpret_cast<const float*>(ab + L.xsx_off);
-    args.offs = offs;
-    args.perm = perm;
+    args.ids = ids;
     args.E = (int)E;
     args.top_k = (int)top_k;
     args.P = (int)(T * top_k);

@@ -183,8 +183,8 @@ hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t
 // route kernel's pair offsets and expert order.
 bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K);
 hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void* act, int64_t T,
-                          int64_t top_k, int64_t N, int64_t K, const int32_t* offs,
-                          const int32_t* perm, void* out, hipStream_t s);
+                          int64_t top_k, int64_t N, int64_t K, const int32_t* ids, void* out,
+                          hipStream_t s);
 hipError_t launch_gemm_id(mmq_wtype t, const void* packed, int64_t E, const void* act,
                           const int32_t* ids, int64_t T, int64_t top_k, int64_t N, int64_t K,
                           void* out, void* workspace, size_t ws_bytes, hipStream_t s);
