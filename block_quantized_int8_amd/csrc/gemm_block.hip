@@ -511,15 +511,25 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         } else if (k == C::K_XF) {
             dma16(rs_x, dst, goff[j], st * (KS * 1024));
         } else {
-            const int sk = skind[j];
-            if (sk == C::S_NONE) return;
-            const rsrc_t r = sk == C::S_WS ? rs_ws : sk == C::S_XS ? rs_xs : sk == C::S_WM ? rs_wm
-                           : sk == C::S_XM ? rs_xm : rs_xg;
-            const int stride = sk == C::S_XG ? KS * 256 : (T::GRID && sk == C::S_WS) ? 64 : C::SCB;
-            if ((is_gather(MODE) && (sk == C::S_XS || sk == C::S_XM || sk == C::S_XG)) || (T::GRID && sk == C::S_WS))
-                dma4(r, dst, goff[j], st * stride);
-            else
-                dma16(r, dst, goff[j], st * stride);
+            // one wave-uniform branch per kind, each with its own descriptor (a descriptor picked
+            // by a runtime kind made the compiler build a descriptor table in scratch memory)
+            const int sk = __builtin_amdgcn_readfirstlane(skind[j]);
+            const uint32_t v = goff[j];
+            if (sk == C::S_WS) {
+                if constexpr (T::GRID) dma4(rs_ws, dst, v, st * 64);
+                else dma16(rs_ws, dst, v, st * C::SCB);
+            } else if (sk == C::S_XS) {
+                if constexpr (is_gather(MODE)) dma4(rs_xs, dst, v, st * C::SCB);
+                else dma16(rs_xs, dst, v, st * C::SCB);
+            } else if (C::C_WM > 0 && sk == C::S_WM) {
+                dma16(rs_wm, dst, v, st * C::SCB);
+            } else if (C::C_XM > 0 && sk == C::S_XM) {
+                if constexpr (is_gather(MODE)) dma4(rs_xm, dst, v, st * C::SCB);
+                else dma16(rs_xm, dst, v, st * C::SCB);
+            } else if (C::C_XG > 0 && sk == C::S_XG) {
+                if constexpr (is_gather(MODE)) dma4(rs_xg, dst, v, st * (KS * 256));
+                else dma16(rs_xg, dst, v, st * (KS * 256));
+            }
         }
     };
     auto issue_stage = [&](uint8_t* buf, int st) __attribute__((always_inline)) {
