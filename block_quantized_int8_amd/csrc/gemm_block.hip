@@ -368,8 +368,11 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     const int wn = wave % WN, wm = wave / WN;
     const int r32 = lane & 31;
 
-    // ---- which tile: dense grids are XCD-swizzled over (n-tile, m-tile); gather grids are
-    // (unit, n-tile) with the unit list produced on the device
+    // ---- which tile: dense grids are XCD-swizzled over (n-tile, m-tile) in groups of GM
+    // m-tiles, so that an XCD's consecutive logical tiles form a GM x (64 / GM) block whose
+    // operand panels its L2 shares (8 x 8 at M = 2048, N = 4096: 8 weight and 8 token panels per
+    // XCD instead of 4 and all 16; q4_0 2048 x 4096 x 4096 -1.2 to -2.8%, q6_K -0.9%); gather
+    // grids are (unit, n-tile) with the unit list produced on the device
     int nt_base, mt_base = 0, unit_first = 0, unit_count = 0;
     const uint8_t* wbase = args.w;
     if constexpr (is_gather(MODE)) {
@@ -396,8 +399,12 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         nt_base = (rest % args.ntiles_n) * C::TN;
     } else {
         const int lid = xcd_swizzle(bid, nblk);
-        nt_base = (lid / args.tiles_m) * C::TN;
-        mt_base = (lid % args.tiles_m) * C::TM;
+        constexpr int GM = 8;
+        const int tiles_n = nblk / args.tiles_m;
+        const int grp = lid / (GM * tiles_n), first_m = grp * GM;
+        const int gm = min(GM, args.tiles_m - first_m), in = lid - grp * GM * tiles_n;
+        nt_base = (in / gm) * C::TN;
+        mt_base = (first_m + in % gm) * C::TM;
     }
     const int NT = args.NT, KBp = args.KBp;
 
