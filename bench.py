@@ -67,14 +67,14 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # (profiles/ holds the summaries), with the hash of the kernel sources they were measured on:
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
-    "q4_0_m2048_n4096_k4096": (168_367_369, "3b7050e972d25bd1"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (289_122_629 + 40_674, "0a04d98b318ab119"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (380_313_441 + 40_675, "0a04d98b318ab119"),
+    "q4_0_m2048_n4096_k4096": (109_173_579, "e5a1ef918a15b4c4"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (287_240_734 + 40_678, "4f50497c4fbfd8d7"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (380_821_185 + 40_675, "4f50497c4fbfd8d7"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
-    "q4_K_m512_n14336_k4096": (98_670_108, "3b7050e972d25bd1"),
-    "q6_K_m2048_n4096_k11008": (470_992_203, "3b7050e972d25bd1"),
-    "dec_q4_0_m8_n4096_k4096": (11_125_303, "c663d0b66107f67e"),
-    "dec_q4_K_m8_n14336_k4096": (45_160_311, "c663d0b66107f67e"),
+    "q4_K_m512_n14336_k4096": (98_794_478, "e5a1ef918a15b4c4"),
+    "q6_K_m2048_n4096_k11008": (330_896_062, "e5a1ef918a15b4c4"),
+    "dec_q4_0_m8_n4096_k4096": (11_132_423, "f52bec4d8c9bf865"),
+    "dec_q4_K_m8_n14336_k4096": (45_159_420, "f52bec4d8c9bf865"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],
