@@ -890,10 +890,16 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_block_kernel(BlockArgs ar
     block_body<FMT, WN, WM, RT, CT, MODE, XM>(args, buf0, buf1, tab, (int)blockIdx.x, (int)gridDim.x);
 }
 
-// MUL_MAT_ID in one launch: workgroups [0, nfull) run the full units (CT tiles of tokens per
-// wave), the rest the tail units (TCT tiles): the tails start as soon as full-unit workgroups
-// leave, instead of after the whole full-unit launch. nfull is a multiple of 8, so both parts
-// keep the workgroup -> XCD assignment of their own grid. LDS holds the larger configuration.
+// MUL_MAT_ID in one launch: the first workgroups run the full units (CT tiles of tokens per
+// wave), the next ones the tail units (TCT tiles), so the tails start as soon as full-unit
+// workgroups leave, instead of after the whole full-unit launch. The grid is sized for the
+// worst case (nfull full-unit and the rest tail-unit workgroups); the split point is the live
+// full-unit count the routing wrote (rounded up to 8 units), so the workgroups of units that do
+// not exist all come last instead of between the full and the tail units, where the dispatcher
+// spent ~5 us retiring 1024 of them on the 64-expert workload before any tail started (about
+// 1 us of the whole machine's time: MoE IQ1C 136.3 -> 135.7 us). Both
+// split points are multiples of 8, so both parts keep the workgroup -> XCD assignment of their
+// own grid. LDS holds the larger configuration.
 template <mmq_wtype FMT, int WN, int WM, int RT, int CT, int TCT, bool XM>
 __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_gather_kernel(BlockArgs full, BlockArgs tail, int nfull) {
     using CF = Cfg<FMT, WN, WM, RT, CT, true>;
@@ -903,8 +909,10 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_gather_kernel(BlockArgs f
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[BUF];
     __shared__ __attribute__((aligned(16))) uint8_t tab[FMT == MMQ_IQ1C ? BT<MMQ_IQ1C>::TAB_BYTES : FMT == MMQ_IQ1T ? 256 : 16];
     const int b = (int)blockIdx.x;
-    if (b < nfull) block_body<FMT, WN, WM, RT, CT, GATHER_F32, XM>(full, buf0, buf1, tab, b, nfull);
-    else block_body<FMT, WN, WM, RT, TCT, GATHER_TAIL, XM>(tail, buf0, buf1, tab, b - nfull, (int)gridDim.x - nfull);
+    const int live_full = ((full.uoff[full.E] + 7) & ~7) * full.ntiles_n;   // <= nfull
+    if (b < live_full) block_body<FMT, WN, WM, RT, CT, GATHER_F32, XM>(full, buf0, buf1, tab, b, nfull);
+    else if (b - live_full < (int)gridDim.x - nfull)
+        block_body<FMT, WN, WM, RT, TCT, GATHER_TAIL, XM>(tail, buf0, buf1, tab, b - live_full, (int)gridDim.x - nfull);
 }
 
 // Tile configuration: 2 x 2 waves, each owning 2 weight tiles x 2 token tiles -> 128 x 128
