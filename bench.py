@@ -68,8 +68,8 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
     "q4_0_m2048_n4096_k4096": (109_173_579, "e5a1ef918a15b4c4"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (287_240_734 + 40_678, "4f50497c4fbfd8d7"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (380_821_185 + 40_675, "4f50497c4fbfd8d7"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (288_478_431 + 40_675, "b603ff26be0e208c"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (380_982_492 + 40_672, "b603ff26be0e208c"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
     "q4_K_m512_n14336_k4096": (98_794_478, "e5a1ef918a15b4c4"),
     "q6_K_m2048_n4096_k11008": (330_896_062, "e5a1ef918a15b4c4"),
