@@ -67,12 +67,12 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # (profiles/ holds the summaries), with the hash of the kernel sources they were measured on:
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
-    "q4_0_m2048_n4096_k4096": (109_173_579, "e5a1ef918a15b4c4"),
+    "q4_0_m2048_n4096_k4096": (109_362_673, "e5807bab1767c6cc"),
     "moe_iq1c_e64_t512_top8_n2048_k4096": (288_478_431 + 40_675, "b603ff26be0e208c"),
     "moe_iq1t_e64_t512_top8_n2048_k4096": (380_982_492 + 40_672, "b603ff26be0e208c"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
-    "q4_K_m512_n14336_k4096": (98_794_478, "e5a1ef918a15b4c4"),
-    "q6_K_m2048_n4096_k11008": (330_896_062, "e5a1ef918a15b4c4"),
+    "q4_K_m512_n14336_k4096": (98_683_621, "e5807bab1767c6cc"),
+    "q6_K_m2048_n4096_k11008": (330_910_411, "e5807bab1767c6cc"),
     "dec_q4_0_m8_n4096_k4096": (11_132_423, "f52bec4d8c9bf865"),
     "dec_q4_K_m8_n14336_k4096": (45_159_420, "f52bec4d8c9bf865"),
 }
