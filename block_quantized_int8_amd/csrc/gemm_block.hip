@@ -269,9 +269,9 @@ struct Cfg {
     static constexpr int SCB = KS * 32 * 4;                 // one tile's scale dwords per stage
     static constexpr int C_WF = WF / 1024, C_XF = TM * KS;
     // weight scales: a pair of tiles per 1 KB chunk; iq1c: the f16 d of 4 tiles x 32 rows per
-    // stage, one 4-byte-per-lane chunk
-    static constexpr int C_WS = T::GRID ? 1 : (TN + 1) / 2;
-    static_assert(!T::GRID || TN == 4, "one d chunk covers four weight tiles");
+    // stage, one 4-byte-per-lane chunk per four tiles
+    static constexpr int C_WS = T::GRID ? TN / 4 : (TN + 1) / 2;
+    static_assert(!T::GRID || TN % 4 == 0, "one d chunk covers four weight tiles");
     static constexpr int C_XS = GATHER ? TM * KS / 2 : (TM + 1) / 2;
     // second weight-side scale region: q4_K's -dmin*m, q6_K's half-1 scale dwords
     static constexpr bool W2 = T::MIN || T::DUAL;
@@ -280,7 +280,7 @@ struct Cfg {
     // 1 KB chunk per token tile and stage, or (gathered rows) a 4-byte-per-lane chunk per tile
     // and block
     static constexpr int C_XG = T::GSUM ? (GATHER ? TM * KS : TM) : 0;
-    static constexpr int RW = T::GRID ? 256 : C_WS * 2 * SCB, RX = (TM + 1) / 2 * 2 * SCB;   // region bytes
+    static constexpr int RW = T::GRID ? C_WS * 256 : C_WS * 2 * SCB, RX = (TM + 1) / 2 * 2 * SCB;   // region bytes
     static constexpr int O_XF = WF, O_WS = O_XF + XF, O_XS = O_WS + RW;
     static constexpr int O_WM = O_XS + RX, O_XM = O_WM + (W2 ? RW : 0);
     static constexpr int O_XG = O_XM + (T::MIN ? RX : 0);
@@ -464,11 +464,11 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
             const int sk = C::scale_kind(ci);
             skind[j] = sk;
             if (T::GRID && sk == C::S_WS) {
-                // iq1c: lane l carries rows 2(l%16), 2(l%16)+1 of tile l/16 (their f16 d of the
-                // stage's 4-block group: 64 bytes per tile and stage)
-                const int nt = min(nt_base + (lane >> 4), NT - 1);
+                // iq1c, chunk ci: lane l carries rows 2(l%16), 2(l%16)+1 of tile 4 ci + l/16
+                // (their f16 d of the stage's 4-block group: 64 bytes per tile and stage)
+                const int nt = min(nt_base + 4 * ci + (lane >> 4), NT - 1);
                 goff[j] = (uint32_t)((nt * (KBp / 4) * 32 + 2 * (lane & 15)) * 2);
-                ldso[j] = C::O_WS;
+                ldso[j] = C::O_WS + ci * 256;
             } else if (sk == C::S_WS || sk == C::S_WM) {
                 // a pair of weight tiles: lanes 0-31 tile 2pr, lanes 32-63 tile 2pr+1, 16 bytes
                 // each of the tile's contiguous 512-byte stage
@@ -919,15 +919,33 @@ __global__ __launch_bounds__(WN * WM * 64, 2) void mmq_gather_kernel(BlockArgs f
 // CTA tiles.
 constexpr int WN_ = 2, WM_ = 2, RT_ = 2, CT_ = 2;
 constexpr bool XM_ = true;        // conversion on the matrix core (see the kernel notes)
-// MUL_MAT_ID: 4 x 1 waves, each 1 weight tile x 2 token tiles -> 128 weight rows x 64 token
-// slots per full unit. An expert sees about T*top_k/E pairs (64 +- 8 for 512 tokens, top-8 of
-// 64), so 64-slot units leave fewer empty slots than 128-slot ones, with the same unpack work per
-// tile pair. An expert's remainder of at most 32 pairs is one tail unit (one token tile per
-// wave); a larger remainder is one more full unit. (96-slot full units with 64-slot tails read
-// every expert's weights once on that routing, but need 198 instead of 160 registers for IQ1T,
-// 2 instead of 3 waves per SIMD, and measured 2.5% slower.)
+// MUL_MAT_ID: 4 x 1 waves, each gather_rt<FMT>() weight tiles x 2 token tiles -> 256 (or 128)
+// weight rows x 64 token slots per full unit. An expert sees about T*top_k/E pairs (64 +- 8 for
+// 512 tokens, top-8 of 64), so 64-slot units leave fewer empty slots than 128-slot ones. An
+// expert's remainder of at most 32 pairs is one tail unit (one token tile per wave); a larger
+// remainder is one more full unit. Two weight tiles per wave read and unpack one weight
+// fragment and one token fragment per tile-step, like the dense 2 x 2 tiles, instead of 1.5;
+// they need ~230 registers (two waves per SIMD instead of three) and twice the weight staging,
+// so a format takes them where two workgroups still fit in a CU's LDS (q4_0, Q4_K, IQ1T, IQ1C;
+// not q8_0 and q6_K, whose 1 KB fragments would leave one). A/B on the 64-expert, 512-token
+// workload against one tile per wave: IQ1T 140.8 -> 131.1 us, q4_0 weights 150.2 -> 129.8, Q4_K
+// 177.3 -> 165.4; 2048 tokens (IQ1T) 490 -> 432. (96-slot full units with 64-slot tails read
+// every expert's weights once on that routing, but at one weight tile per wave needed 198
+// instead of 160 registers for IQ1T and measured 2.5% slower.)
 constexpr int GWN_ = 4, GWM_ = 1, GRT_ = 1, GCT_ = 2;
 constexpr int TCT_ = 1;
+// LDS of a gather workgroup with RT weight tiles per wave: two stage buffers of the larger of the
+// full-unit and tail configurations, plus the format's table
+template <mmq_wtype FMT, int RT>
+constexpr int gather_lds_bytes() {
+    using CF = Cfg<FMT, GWN_, GWM_, RT, GCT_, true>;
+    using CT = Cfg<FMT, GWN_, GWM_, RT, TCT_, true>;
+    return 2 * (CF::BUF > CT::BUF ? CF::BUF : CT::BUF) +
+           (FMT == MMQ_IQ1C ? BT<MMQ_IQ1C>::TAB_BYTES : FMT == MMQ_IQ1T ? 256 : 16);
+}
+constexpr int LDS_PER_CU = 160 * 1024;
+template <mmq_wtype FMT>
+constexpr int gather_rt() { return 2 * gather_lds_bytes<FMT, 2>() + 2048 <= LDS_PER_CU ? 2 : 1; }
 constexpr int UNIT_ROWS = GWM_ * GCT_ * 32;
 constexpr int TAIL_ROWS = GWM_ * TCT_ * 32;
 static_assert(TAIL_ROWS < UNIT_ROWS, "a tail unit is smaller than a full unit");
@@ -1055,7 +1073,8 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
     g.pairs = pairs;
     g.E = (int)E;
     g.top_k = (int)top_k;
-    g.ntiles_n = (int)ceil_div(N, GWN_ * GRT_ * 32);
+    constexpr int GRT = gather_rt<FMT>();
+    g.ntiles_n = (int)ceil_div(N, GWN_ * GRT * 32);
     g.unit_rows = UNIT_ROWS;
     g.out = static_cast<float*>(out);
     g.ldo = N;
@@ -1065,7 +1084,7 @@ hipError_t launch_gather(const void* packed, int64_t E, const void* act, int64_t
     t.uoff = utail;
     const int nfull = (int)(round_up(max_full, 8) * g.ntiles_n);
     const int ntail = (int)(round_up(max_tail, 8) * g.ntiles_n);
-    hipLaunchKernelGGL((mmq_gather_kernel<FMT, GWN_, GWM_, GRT_, GCT_, TCT_, XM_>), dim3((unsigned)(nfull + ntail)),
+    hipLaunchKernelGGL((mmq_gather_kernel<FMT, GWN_, GWM_, GRT, GCT_, TCT_, XM_>), dim3((unsigned)(nfull + ntail)),
                        block, 0, s, g, t, nfull);
     return hipGetLastError();
 }
@@ -1080,7 +1099,8 @@ int gather_tail_tokens() { return TAIL_ROWS; }
 // A grid stays below 2^32 work-items: 2^24 workgroups of 256 threads.
 constexpr int64_t MAX_GRID = (int64_t(1) << 24) - 1;
 
-// the one MUL_MAT_ID launch holds the full-unit grid and the tail grid (at most as many units)
+// the one MUL_MAT_ID launch holds the full-unit grid and the tail grid (at most as many units);
+// counted at 128 weight rows per unit, an upper bound of every format's grid
 bool gather_grid_ok(int64_t max_units, int64_t N) {
     return 2 * round_up(max_units, 8) * ceil_div(N, GWN_ * GRT_ * 32) <= MAX_GRID;
 }

@@ -8,7 +8,8 @@
 //      R = gather_tail_tokens(), one tail unit (a larger remainder is a last full unit);
 //      exclusive scans of the pair counts (pair offsets), full-unit counts and tail-unit counts
 //      (unit offsets); then scatter the pair ids into expert order.
-//   2. the gather-mode MMQ kernel in one launch: a workgroup per (unit, 128-row weight tile),
+//   2. the gather-mode MMQ kernel in one launch: a workgroup per (unit, 256-row weight tile;
+//      128 rows for q8_0 and q6_K),
 //      the full units (64 token slots) first and the tails (32 slots, one token tile per wave)
 //      after them, so tails fill the CUs the last full units leave idle. A workgroup finds its expert by binary search
 //      over the unit offsets, reads its tokens' activation rows and writes each pair's own
