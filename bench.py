@@ -68,8 +68,8 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
     "q4_0_m2048_n4096_k4096": (109_362_673, "e5807bab1767c6cc"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (288_478_431 + 40_675, "b603ff26be0e208c"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (380_982_492 + 40_672, "b603ff26be0e208c"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_460_629 + 40_674, "81128639543942f1"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_521_703 + 40_671, "81128639543942f1"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
     "q4_K_m512_n14336_k4096": (98_683_621, "e5807bab1767c6cc"),
     "q6_K_m2048_n4096_k11008": (330_910_411, "e5807bab1767c6cc"),
