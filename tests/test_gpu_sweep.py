@@ -101,3 +101,36 @@ def test_moe_128_experts(env, fmt, T):
     r2 = parity.check_moe(orc, got, fmt, raw, N, K, rq, rs, parity.block_sums(rq), ids, grid=_grid(fmt))
     print(f"  rel err {rel:.3e} (definition), {r2:.3e} (C oracle)")
     assert rel <= parity.PAGES_GATE
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_K", "q6_K", "iq1t", "iq1c"])
+def test_moe_ragged_weight_units(env, fmt):
+    """N = 300 spans two 256-row MUL_MAT_ID units (q8_0 and q6_K: three 128-row units) whose last
+    one is mostly past the matrix: its clamped weight tiles, and for IQ1C the second d chunk of
+    an eight-tile unit, must not leak into the stored rows. 300 tokens at top-2 of 8 experts
+    give ~75 pairs per expert, so units of both kinds (64-pair full units and tails) occur."""
+    torch, mmq, orc, _ = env
+    dev = torch.device("cuda:0")
+    E, T, top_k, N, K = 8, 300, 2, 300, 512
+    seed = 7 + FMTS.index(fmt)
+    print(f"[case] moe ragged {fmt} E={E} T={T} top_k={top_k} N={N} K={K} seed={seed}", flush=True)
+    raw = gen.moe_weights(fmt, E, N, K, seed=seed, cfg=142)
+    x = gen.act_f32(T, K, seed=seed, cfg=142, outlier_rate=1e-3)
+    ids = gen.moe_ids(T, top_k, E, seed=seed, cfg=142)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
+    pb = mmq.packed_bytes(fmt, N, K)
+    packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        _pack(env, fmt, raw[e], N, K, out=packed[e * pb:(e + 1) * pb])
+    out = torch.full((T, top_k, N), float(SENTINEL), dtype=torch.float32, device=dev)
+    mmq.gemm_id(fmt, packed, E, act, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev),
+                T, top_k, N, K, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert not np.any(got == SENTINEL)
+    rq, rs, _ = orc.quantize_q8_1(x)
+    ref = orc.moe_f64(fmt, raw.reshape(E * N, -1), E, N, K, rq, rs, ids, grid=_grid(fmt))
+    rel = parity.rel(got, ref)
+    r2 = parity.check_moe(orc, got, fmt, raw, N, K, rq, rs, parity.block_sums(rq), ids, grid=_grid(fmt))
+    print(f"  rel err {rel:.3e} (definition), {r2:.3e} (C oracle)")
+    assert rel <= parity.PAGES_GATE
