@@ -569,13 +569,14 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         v4i b[CT];
         uint32_t wsd[RT], wsd2[RT], xs[CT], gx[CT];
     };
-    // The f16 scale MFMA takes (scale, 0) register pairs. In the dense 128 x 128 kernels the
-    // operand buffers live for the whole K loop and only the scale halves are rewritten, so no
-    // step spends a move on the zeros (q4_0 N = 11008: -2%). The other kernels pair each scale
-    // at its MFMA: the gather and q6_K kernels need every register they can keep (the IQ1T
-    // gather kernel holds three waves per SIMD only up to 168), and the one-tile-per-wave
-    // kernels measured slower with carried pairs.
-    constexpr bool CARRY = !T::DUAL && !is_gather(MODE) && RT * CT >= 4;
+    // The f16 scale MFMA takes (scale, 0) register pairs. In the kernels of 2 x 2 tiles per wave
+    // (dense 128 x 128, MUL_MAT_ID full units of 256 rows) the operand buffers live for the whole
+    // K loop and only the scale halves are rewritten, so no step spends a move on the zeros
+    // (q4_0 N = 11008: -2%; MoE 0 to -1.4%). The other kernels pair each scale at its MFMA: q6_K
+    // needs every register it can keep, the gather kernels of one weight tile per wave hold
+    // three waves per SIMD only up to 168, and the one-tile-per-wave kernels measured slower
+    // with carried pairs.
+    constexpr bool CARRY = !T::DUAL && RT * CT >= 4;
     using SOp = std::conditional_t<CARRY, v2i, uint32_t>;
     struct Ops {
         v4i a[RT][T::NMF];
