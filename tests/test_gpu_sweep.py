@@ -134,3 +134,36 @@ def test_moe_ragged_weight_units(env, fmt):
     r2 = parity.check_moe(orc, got, fmt, raw, N, K, rq, rs, parity.block_sums(rq), ids, grid=_grid(fmt))
     print(f"  rel err {rel:.3e} (definition), {r2:.3e} (C oracle)")
     assert rel <= parity.PAGES_GATE
+
+
+@pytest.mark.parametrize("fmt,E,T", [("q8_0", 3000, 200), ("iq1c", 3000, 200), ("iq1c", 4096, 3)])
+def test_moe_thousands_of_experts(env, fmt, E, T):
+    """More experts than the routing workgroup has threads (3000: three experts per thread, the
+    last thread's range ragged; most experts empty or with one pair, so nearly every unit is a
+    tail), and the most experts the call accepts (4096) at a decode batch, where each decode
+    workgroup ranks the pairs by expert itself (keys up to 4096 << 8)."""
+    torch, mmq, orc, _ = env
+    dev = torch.device("cuda:0")
+    top_k, N, K = 8, 64, 256
+    seed = 40 + FMTS.index(fmt)
+    print(f"[case] moe many experts {fmt} E={E} T={T} top_k={top_k} N={N} K={K} seed={seed}", flush=True)
+    raw = gen.moe_weights(fmt, E, N, K, seed=seed, cfg=143)
+    x = gen.act_f32(T, K, seed=seed, cfg=143)
+    ids = gen.moe_ids(T, top_k, E, seed=seed, cfg=143)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev), "q8_1")
+    pb = mmq.packed_bytes(fmt, N, K)
+    packed = torch.empty(E * pb, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        _pack(env, fmt, raw[e], N, K, out=packed[e * pb:(e + 1) * pb])
+    out = torch.full((T, top_k, N), float(SENTINEL), dtype=torch.float32, device=dev)
+    mmq.gemm_id(fmt, packed, E, act, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev),
+                T, top_k, N, K, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert not np.any(got == SENTINEL)
+    rq, rs, _ = orc.quantize_q8_1(x)
+    ref = orc.moe_f64(fmt, raw.reshape(E * N, -1), E, N, K, rq, rs, ids, grid=_grid(fmt))
+    rel = parity.rel(got, ref)
+    r2 = parity.check_moe(orc, got, fmt, raw, N, K, rq, rs, parity.block_sums(rq), ids, grid=_grid(fmt))
+    print(f"  rel err {rel:.3e} (definition), {r2:.3e} (C oracle)")
+    assert rel <= parity.PAGES_GATE
