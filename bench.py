@@ -67,12 +67,12 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # (profiles/ holds the summaries), with the hash of the kernel sources they were measured on:
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
-    "q4_0_m2048_n4096_k4096": (109_181_803, "dead1ff78e2e0c6a"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_461_946 + 40_683, "6b9f543caee085e1"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_180_114 + 40_672, "6b9f543caee085e1"),
+    "q4_0_m2048_n4096_k4096": (94_362_335, "e2f1080f60c862eb"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_390_409 + 40_686, "4071a1e60dd14519"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_302_008 + 40_678, "4071a1e60dd14519"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
-    "q4_K_m512_n14336_k4096": (98_794_522, "dead1ff78e2e0c6a"),
-    "q6_K_m2048_n4096_k11008": (330_871_529, "dead1ff78e2e0c6a"),
+    "q4_K_m512_n14336_k4096": (94_757_800, "e2f1080f60c862eb"),
+    "q6_K_m2048_n4096_k11008": (305_320_196, "e2f1080f60c862eb"),
     "dec_q4_0_m8_n4096_k4096": (11_132_495, "480b00d65ffed919"),
     "dec_q4_K_m8_n14336_k4096": (45_159_352, "480b00d65ffed919"),
 }
