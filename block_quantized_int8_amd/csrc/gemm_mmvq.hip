@@ -596,8 +596,12 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     load(0, k0);
     load(1, k1);
     stage();
+    // the wave's priority is raised while it issues the next item's loads, so that they leave
+    // before the other waves' compute (Q4_K 14336 x 4096 -1.8%, the 4-token MoE -3.5%)
     auto step = [&](int t, const Chunk& cur, Chunk& nxt) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
         load(t + 2, nxt);
+        __builtin_amdgcn_s_setprio(0);
         compute(cur);
         const int i = t / cw;
         if (t - i * cw == cw - 1) finish(i);
