@@ -67,14 +67,14 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # (profiles/ holds the summaries), with the hash of the kernel sources they were measured on:
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
-    "q4_0_m2048_n4096_k4096": (94_362_335, "e2f1080f60c862eb"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_390_409 + 40_686, "4071a1e60dd14519"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_302_008 + 40_678, "4071a1e60dd14519"),
+    "q4_0_m2048_n4096_k4096": (94_479_302, "81685dcca9c32630"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_098_621 + 40_678, "7823a2b4b23d2986"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_172_499 + 40_675, "7823a2b4b23d2986"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
-    "q4_K_m512_n14336_k4096": (94_757_800, "e2f1080f60c862eb"),
-    "q6_K_m2048_n4096_k11008": (305_320_196, "e2f1080f60c862eb"),
-    "dec_q4_0_m8_n4096_k4096": (11_132_495, "480b00d65ffed919"),
-    "dec_q4_K_m8_n14336_k4096": (45_159_352, "480b00d65ffed919"),
+    "q4_K_m512_n14336_k4096": (94_717_011, "81685dcca9c32630"),
+    "q6_K_m2048_n4096_k11008": (305_931_997, "81685dcca9c32630"),
+    "dec_q4_0_m8_n4096_k4096": (11_135_486, "95e4d01a930df165"),
+    "dec_q4_K_m8_n14336_k4096": (45_156_471, "95e4d01a930df165"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],
