@@ -247,6 +247,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     // expert order, pairs), the pair ids, and the scan's wave totals
     __shared__ int s_e[ID ? MV_IDP : 1], s_po[ID ? MV_IDP : 1], s_me[ID ? MV_IDP : 1];
     __shared__ int s_pp[ID ? MV_IDP : 1];
+    __shared__ int s_tk[ID ? MV_IDP : 1];                            // s_pp's pair's token
     __shared__ int s_wt[MV_W + 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -301,6 +302,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         const bool start = tid < P && e < a.E && (rank - first) % TOK == 0;
         if (tid < P) {
             s_pp[rank] = tid;                                        // pairs in expert order
+            s_tk[rank] = tid / a.top_k;
             s_po[rank] = start ? 1 : 0;                              // batch-start flags
             s_me[rank] = e;
         }
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             s_me[cnt] = len;
         }
         __syncthreads();
-        units = s_wt[MV_W] * a.groups;
+        units = __builtin_amdgcn_readfirstlane(s_wt[MV_W]) * a.groups;
     }
     const int ng = (units - off + G - 1) / G;                            // >= 1 for dense grids
     if (ng <= 0) return;                                                 // uniform: nothing to do
@@ -374,16 +376,21 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         if constexpr (ID) {
             const int ue = q / a.groups;
             q -= ue * a.groups;
-            wx += (int64_t)s_e[ue] * a.w_stride;
-            me = s_me[ue];
-            po = s_po[ue];
+            wx += (int64_t)__builtin_amdgcn_readfirstlane(s_e[ue]) * a.w_stride;
+            me = __builtin_amdgcn_readfirstlane(s_me[ue]);
+            po = __builtin_amdgcn_readfirstlane(s_po[ue]);
         }
-        // the token of this lane's rows (t0 / t1 of the unit), -1 past its token count
+        // the token of this lane's rows (t0 / t1 of the unit), -1 past its token count; the
+        // batch values are wave-uniform and the token read takes no branch (a branch here made the
+        // compiler treat the item loop as divergent and wait on the in-flight loads at its head)
 #pragma unroll
         for (int x = 0; x < TG; ++x) {
             const int ix = (c16 & 7) + 8 * x;
             int tk = ix < me ? ix : -1;
-            if constexpr (ID) tk = ix < me ? s_pp[po + ix] / a.top_k : -1;
+            if constexpr (ID) {
+                const int tv = s_tk[min(po + ix, MV_IDP - 1)];
+                tk = ix < me ? tv : -1;
+            }
             k.tk[x] = tk;
         }
         const int half = q & 1;
@@ -606,13 +613,18 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         const int i = t / cw;
         if (t - i * cw == cw - 1) finish(i);
     };
-    for (int t = 0;; t += 3) {
+    // whole triples in a loop without exits, then the last 0-2 items: with exits inside the loop
+    // the compiler's wait-count pass assumed the loads just issued could still be in flight at
+    // the loop head and waited for them there (the 1-token MoE -13%, Q4_K 14336 x 4096 -7%)
+    int t = 0;
+    for (; t + 3 <= total; t += 3) {
         step(t, k0, k2);
-        if (t + 1 >= total) break;
         step(t + 1, k1, k0);
-        if (t + 2 >= total) break;
         step(t + 2, k2, k1);
-        if (t + 3 >= total) break;
+    }
+    if (t < total) {
+        step(t, k0, k2);
+        if (t + 1 < total) step(t + 1, k1, k0);
     }
 }
 
