@@ -73,8 +73,8 @@ MEASURED_TRAFFIC = {
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
     "q4_K_m512_n14336_k4096": (94_717_011, "81685dcca9c32630"),
     "q6_K_m2048_n4096_k11008": (305_931_997, "81685dcca9c32630"),
-    "dec_q4_0_m8_n4096_k4096": (11_126_255, "1bac913cdf3db877"),
-    "dec_q4_K_m8_n14336_k4096": (45_192_227, "1bac913cdf3db877"),
+    "dec_q4_0_m8_n4096_k4096": (11_121_190, "471e78db32e65972"),
+    "dec_q4_K_m8_n14336_k4096": (45_188_577, "471e78db32e65972"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],

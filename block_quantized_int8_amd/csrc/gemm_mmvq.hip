@@ -565,11 +565,14 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     }
     if constexpr (XL) {
         const int nslot = KBp * 2 * TOK;
+        const rsrc_t rq = rsrc(a.xq, (uint32_t)KBp * 1024);
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int sl = min(tid + u * MV_W * 64, nslot - 1);     // loads unconditional
+            // every thread issues PER loads (sized for the longest K); slots past this K's end
+            // take an offset outside the descriptor, which returns zero without a memory request
+            const int sl = tid + u * MV_W * 64;
             const int t = sl % TOK, h = (sl / TOK) & 1, b = sl / (2 * TOK);
-            xv[u] = *reinterpret_cast<const v4i*>(a.xq + ((int64_t)b * 64 + h * 32 + t) * 16);
+            xv[u] = ld128(rq, sl < nslot ? (uint32_t)((b * 64 + h * 32 + t) * 16) : OOR);
         }
     }
     auto stage = [&]() __attribute__((always_inline)) {
