@@ -167,7 +167,9 @@ def test_decode_w8a8_full_size(env):
 def test_decode_persistent_groups(env, fmt, M):
     # more 16-row groups than workgroups (N > 16 x compute units): workgroups loop over groups
     # with loads running ahead across group boundaries; K = 768 leaves most waves without a
-    # chunk (they only reduce), K = 4352 gives waves unequal chunk counts (34 chunks, 16 waves)
+    # chunk (they only reduce), K = 4352 gives waves unequal chunk counts (34 chunks, 16 waves).
+    # A wave's item count (groups x chunks) is then 1, 2, 3, 4 or 6: the item loop runs zero to
+    # two whole triples and leaves zero, one or two items after them
     torch, mmq, orc = env
     for K in (768, 4352):
         N = 16 * 256 + 53
