@@ -67,12 +67,12 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # (profiles/ holds the summaries), with the hash of the kernel sources they were measured on:
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
-    "q4_0_m2048_n4096_k4096": (94_479_302, "81685dcca9c32630"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_098_621 + 40_678, "7823a2b4b23d2986"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_172_499 + 40_675, "7823a2b4b23d2986"),
+    "q4_0_m2048_n4096_k4096": (94_416_986, "abb5fdd9cfc5cfd2"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_187_096 + 40_679, "9f7101c77e1a2a5a"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (370_883_829 + 40_674, "9f7101c77e1a2a5a"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
-    "q4_K_m512_n14336_k4096": (94_717_011, "81685dcca9c32630"),
-    "q6_K_m2048_n4096_k11008": (305_931_997, "81685dcca9c32630"),
+    "q4_K_m512_n14336_k4096": (94_717_268, "abb5fdd9cfc5cfd2"),
+    "q6_K_m2048_n4096_k11008": (306_039_285, "abb5fdd9cfc5cfd2"),
     "dec_q4_0_m8_n4096_k4096": (11_121_190, "471e78db32e65972"),
     "dec_q4_K_m8_n14336_k4096": (45_188_577, "471e78db32e65972"),
 }

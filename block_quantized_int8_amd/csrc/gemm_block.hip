@@ -381,13 +381,23 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         // units (the lowest ids) evenly over the XCDs
         const int b = bid, rest = b >> 3;
         const int u = (rest / args.ntiles_n) * 8 + (b & 7);
-        if (u >= args.uoff[args.E]) return;             // uniform: the whole CTA leaves
-        int lo = 0, hi = args.E;                        // largest e with uoff[e] <= u
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (args.uoff[mid] <= u) lo = mid; else hi = mid;
+        // the unit's expert: the largest e < E with uoff[e] <= u (uoff rises from uoff[0] = 0
+        // to the unit total uoff[E]). Each lane tests one offset and the wave counts the lanes
+        // that pass: one round of loads for E <= 64 (issued with the total's), else a first
+        // round over every st-th offset picks the segment of st that holds e.
+        const int E = args.E;
+        const int total = args.uoff[E];
+        int base = 0, span = E;
+        if (E > 64) {
+            const int st = (E + 63) >> 6;
+            const int i = lane * st;
+            const bool pass = i < E && args.uoff[i] <= u;
+            base = (__popcll(__ballot(pass)) - 1) * st;
+            span = min(st, E - base);
         }
-        const int e = lo;
+        if (u >= total) return;                         // uniform: the whole CTA leaves
+        const bool pass = lane < span && args.uoff[base + lane] <= u;
+        const int e = base + __popcll(__ballot(pass)) - 1;
         if constexpr (MODE == GATHER_TAIL) {
             unit_first = args.offs[e] + (args.ufull[e + 1] - args.ufull[e]) * args.unit_rows;
             unit_count = args.offs[e + 1] - unit_first;           // 1 .. TAIL_ROWS = TM*32
@@ -408,28 +418,53 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
     }
     const int NT = args.NT, KBp = args.KBp;
 
-    // token slot (tile j, row r) -> activation row to read
-    auto src_token = [&](int j, int r) __attribute__((always_inline)) -> int {
-        if constexpr (is_gather(MODE)) {
-            const int s = j * 32 + r;
-            return s < unit_count ? args.pairs[unit_first + s] / args.top_k : 0;
-        } else {
-            return min((mt_base + j) * 32 + r, args.MT * 32 - 1);
-        }
-    };
-
+    // Gather: this lane's pair of each token tile (at most two), loaded once for every chunk
+    // that needs its token. The pair ids come through a descriptor whose range ends at the
+    // unit's last pair (a slot past it reads 0, token 0), so the loads carry no branch; they go
+    // out with the grid's loads, ahead of the table writes, whose branch would otherwise put a
+    // round trip between them (as per-chunk lookups behind the wave-dependent chunk-kind
+    // branches put one behind each). Two scalars, not an array: a selected array element became
+    // a dynamic index, and the array was moved to LDS.
+    static_assert(!is_gather(MODE) || C::TM <= 2, "gather tiles hold at most two token tiles");
+    int tok0 = 0, tok1 = 0;
+    if constexpr (is_gather(MODE)) {
+        const rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(args.pairs + unit_first), (short)0,
+                                                            unit_count * 4, 0x00020000);
+        tok0 = __builtin_amdgcn_raw_buffer_load_b32(rp, r32 * 4, 0, 0);
+        if constexpr (C::TM > 1) tok1 = __builtin_amdgcn_raw_buffer_load_b32(rp, (32 + r32) * 4, 0, 0);
+    }
+    // the packed matrix's grid (its last region) as selector tables
+    constexpr int GW = T::GRID ? 2048 / C::NTH : 1;
+    static_assert(!T::GRID || 2048 % C::NTH == 0, "the grid copy assumes whole rounds of the workgroup");
+    uint32_t gw[GW];
+    if constexpr (T::GRID) {
+        const uint32_t* g = reinterpret_cast<const uint32_t*>(wbase + args.w_min_off);
+#pragma unroll
+        for (int k = 0; k < GW; ++k) gw[k] = g[tid + k * C::NTH];
+    }
     if constexpr (FMT == MMQ_IQ1T || FMT == MMQ_IQ1C) {
         if (tid < T::TAB_WORDS) reinterpret_cast<uint32_t*>(tab)[tid] = T::table_word(tid >> 1, tid & 1);
     }
-    if constexpr (T::GRID) {          // the packed matrix's grid (its last region) as selector tables
-        const uint32_t* g = reinterpret_cast<const uint32_t*>(wbase + args.w_min_off);
+    if constexpr (T::GRID) {
         uint32_t* lg = reinterpret_cast<uint32_t*>(tab) + T::TAB_WORDS;
-        for (int i = tid; i < 2048; i += C::NTH) {
-            const uint32_t w = g[i];
-            lg[i] = w & 0x03030303u;
-            lg[2048 + i] = (w >> 2) & 0x03030303u;
+#pragma unroll
+        for (int k = 0; k < GW; ++k) {
+            lg[tid + k * C::NTH] = gw[k] & 0x03030303u;
+            lg[2048 + tid + k * C::NTH] = (gw[k] >> 2) & 0x03030303u;
         }
     }
+    if constexpr (is_gather(MODE)) {
+        tok0 /= args.top_k;
+        if constexpr (C::TM > 1) tok1 /= args.top_k;
+    }
+    // token slot (tile i, row r32) -> activation row to read
+    auto row_token = [&](int i) __attribute__((always_inline)) -> int {
+        if constexpr (is_gather(MODE)) {
+            return (C::TM > 1 && i == 1) ? tok1 : tok0;
+        } else {
+            return min((mt_base + i) * 32 + r32, args.MT * 32 - 1);
+        }
+    };
 
     // ---- DMA plan: per chunk this lane keeps its 32-bit source offset in stage 0 from the
     // chunk's region base; stage st adds st times the region's stage stride as a wave-uniform
@@ -456,7 +491,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
         } else if (k == C::K_XF) {
             const int ci = c - C::C_WF;
             const int jt = ci / KS, q = ci % KS;
-            const int t = src_token(jt, r32);
+            const int t = row_token(jt);
             goff[j] = (uint32_t)((((t >> 5) * KBp + q) * 64 + h * 32 + (t & 31)) * 16);
             ldso[j] = C::O_XF + ci * 1024;
         } else {
@@ -481,7 +516,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
                 if constexpr (is_gather(MODE)) {
                     // (tile i, block kb): lane (h, r) fetches the dword of half h of its row
                     const int i = x / KS, kb = x % KS;
-                    const int m = src_token(i, r32);
+                    const int m = row_token(i);
                     goff[j] = (uint32_t)((((m >> 5) * KBp + kb) * 64 + h * 32 + (m & 31)) * 4);
                     ldso[j] = C::O_XG + (i * KS + kb) * 256;
                 } else {
@@ -495,7 +530,7 @@ __device__ __attribute__((always_inline)) inline void block_body(const BlockArgs
                 if constexpr (is_gather(MODE)) {
                     // (tile i, blocks 2bp and 2bp+1): each lane fetches its own gathered row's dword
                     const int i = x / (KS / 2), bp = x % (KS / 2);
-                    const int m = src_token(i, r32);
+                    const int m = row_token(i);
                     goff[j] = (uint32_t)((((m >> 5) * KBp + 2 * bp + h) * 32 + (m & 31)) * 4);
                     ldso[j] = base + (i * KS + 2 * bp) * 128;
                 } else {
