@@ -68,13 +68,13 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
     "q4_0_m2048_n4096_k4096": (94_416_986, "abb5fdd9cfc5cfd2"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_187_096 + 40_679, "9f7101c77e1a2a5a"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (370_883_829 + 40_674, "9f7101c77e1a2a5a"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_289_935 + 40_678, "eab2d5b74adc5527"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_323_864 + 40_674, "eab2d5b74adc5527"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
     "q4_K_m512_n14336_k4096": (94_717_268, "abb5fdd9cfc5cfd2"),
     "q6_K_m2048_n4096_k11008": (306_039_285, "abb5fdd9cfc5cfd2"),
-    "dec_q4_0_m8_n4096_k4096": (11_121_190, "471e78db32e65972"),
-    "dec_q4_K_m8_n14336_k4096": (45_188_577, "471e78db32e65972"),
+    "dec_q4_0_m8_n4096_k4096": (11_121_196, "b46f11929480f304"),
+    "dec_q4_K_m8_n14336_k4096": (45_185_553, "b46f11929480f304"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],
@@ -389,7 +389,8 @@ def main():
         ws = torch.empty(mmq.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
 
         kernels = [("quantize_q8_1", lambda r: mmq.quantize_act(xd, out=act)),
-                   ("gemm_id (route + decode kernel)" if T <= 4 else "gemm_id (route + gather MMQ)",
+                   ("gemm_id (decode kernel, in-kernel grouping)" if T <= 8 and T * top_k <= 256
+                    else "gemm_id (route + gather MMQ)",
                     lambda r: mmq.gemm_id(fmt, packed[r], E, act, ids_d, T, top_k, N, K, out=out, workspace=ws))]
         dom = 1
         ops = 2.0 * T * top_k * N * K

@@ -212,7 +212,7 @@ struct MvArgs {
     int M, N, KBp, groups;      // groups: 16-row groups holding at least one real row
     void* out;
     int64_t ldo;
-    // MUL_MAT_ID with at most 4 tokens: the routing ids themselves (each workgroup groups the
+    // MUL_MAT_ID with at most 8 tokens: the routing ids themselves (each workgroup groups the
     // at most 256 pairs by expert on its own, so no routing launch precedes this one)
     int64_t w_stride;           // bytes between experts' packed matrices
     const int32_t* ids;         // [P] expert of pair p = token * top_k + slot
@@ -220,10 +220,12 @@ struct MvArgs {
 };
 
 constexpr int MV_IDP = 256;     // MUL_MAT_ID decode: pairs (and so pair batches) at most
-// MUL_MAT_ID decode: tokens at most. Measured on 64 IQ1T experts of 2048 x 4096, top-8: with
-// 1, 2, 4 tokens the decode units take 20, 30, 42 us against the prefill gather's 36, 40, 47;
-// from 6 tokens on the gather's 32-slot tiles are faster.
-constexpr int MV_ID_TOK = 4;
+// MUL_MAT_ID decode: tokens at most, the token rows one workgroup stages (its batches of up to
+// 8 pairs read them by token id). Measured on 64 experts of 2048 x 4096, top-8, against the
+// prefill gather: IQ1T 13.7 / 32.5 / 40.6 / 50.0 us at 1 / 4 / 6 / 8 tokens against 36 / 47 /
+// 45.4 / 55.9; at 6 tokens Q4_K 38.9 against 50.4, IQ1C 42.9 against 43.3; q4_0 at 8 tokens 44.0
+// against 48.1.
+constexpr int MV_ID_TOK = 8;
 
 // LDS barrier that leaves global loads in flight (__syncthreads() would also wait for them)
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -1,8 +1,8 @@
 """GPU parity of MUL_MAT_ID at decode batch sizes, through the C ABI.
 
-With at most 4 tokens (and at most 256 (token, slot) pairs) mmq_gemm_id runs its expert
+With at most 8 tokens (and at most 256 (token, slot) pairs) mmq_gemm_id runs its expert
 grouping and then the decode kernel over (batch of up to 8 of one expert's pairs, 16-row group)
-units instead of the prefill gather tiles; 5 tokens or 257 pairs go back to the gather (both
+units instead of the prefill gather tiles; 9 tokens or 257 pairs go back to the gather (both
 sides of each crossover are checked). Bars: each pair's f32 row
 within max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4), rows of
 invalid ids untouched, and each pair's row bit-identical to the dense decode product of its token
@@ -75,7 +75,7 @@ def _check(env, fmt, E, N, K, ids, raw, rq, rs, got):
         assert rel <= GATE
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 5])
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 8, 9])
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_K", "iq1t"])
 def test_moe_decode_formats(env, fmt, T):
     E, top_k, N, K = 32, 4, 160, 512
@@ -120,7 +120,7 @@ def test_moe_decode_pair_limit_crossover(env, top_k):
     _check(env, "q4_0", E, N, K, ids, raw, rq, rs, got)
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 8])
 def test_moe_decode_full_shape_sampled(env, T):
     # the MoE workload's expert shape (64 experts x IQ1T 2048 x 4096, top-8) at decode batches;
     # every pair row in full against the f64 definition on 256 sampled columns
