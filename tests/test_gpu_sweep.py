@@ -136,12 +136,16 @@ def test_moe_ragged_weight_units(env, fmt):
     assert rel <= parity.PAGES_GATE
 
 
-@pytest.mark.parametrize("fmt,E,T", [("q8_0", 3000, 200), ("iq1c", 3000, 200), ("iq1c", 4096, 3)])
+@pytest.mark.parametrize("fmt,E,T", [("q8_0", 3000, 200), ("iq1c", 3000, 200), ("iq1c", 4096, 3),
+                                     ("q4_0", 65, 40), ("iq1t", 4096, 16)])
 def test_moe_thousands_of_experts(env, fmt, E, T):
     """More experts than the routing workgroup has threads (3000: three experts per thread, the
     last thread's range ragged; most experts empty or with one pair, so nearly every unit is a
     tail), and the most experts the call accepts (4096) at a decode batch, where each decode
-    workgroup ranks the pairs by expert itself (keys up to 4096 << 8)."""
+    workgroup ranks the pairs by expert itself (keys up to 4096 << 8). Past 64 experts a gather
+    workgroup finds its unit's expert in two ballot rounds over the unit offsets (every st-th
+    offset, then st of them): 65 experts is the smallest such case (st = 2), 4096 at 16 tokens
+    the largest (st = 64) on the gather path."""
     torch, mmq, orc, _ = env
     dev = torch.device("cuda:0")
     top_k, N, K = 8, 64, 256
