@@ -189,8 +189,10 @@ def _moe(env, E, T, top_k, N, K, ids, seed, cfg=88, fmt="iq1c"):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("T", [2, 37, 150])
+@pytest.mark.parametrize("T", [2, 8, 9, 37, 150])
 def test_moe_every_row(env, fmt, T):
+    # up to 8 tokens the decode kernel (each workgroup groups the pairs itself), from 9 the
+    # routing launch and the prefill gather
     _, _, orc, _ = env
     E, top_k, N, K = 8, 3, 97, 512
     ids = gen.moe_ids(T, top_k, E, seed=T, cfg=88)
