@@ -73,8 +73,8 @@ MEASURED_TRAFFIC = {
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
     "q4_K_m512_n14336_k4096": (94_717_268, "abb5fdd9cfc5cfd2"),
     "q6_K_m2048_n4096_k11008": (306_039_285, "abb5fdd9cfc5cfd2"),
-    "dec_q4_0_m8_n4096_k4096": (11_121_196, "b46f11929480f304"),
-    "dec_q4_K_m8_n14336_k4096": (45_185_553, "b46f11929480f304"),
+    "dec_q4_0_m8_n4096_k4096": (11_103_725, "16a51ac58bdb9f40"),
+    "dec_q4_K_m8_n14336_k4096": (45_187_771, "16a51ac58bdb9f40"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],

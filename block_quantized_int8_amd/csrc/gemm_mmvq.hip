@@ -667,8 +667,12 @@ void launch_xl(const MvArgs& args, dim3 grid, hipStream_t s) {
 template <mmq_wtype FMT>
 hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
     const dim3 grid((unsigned)std::min(args.groups, cu_count()));
+    // Token rows staged in LDS only when workgroups loop over several groups: the staging and
+    // its barrier are a fixed cost per workgroup that one group does not pay back (q4_0 4096 x
+    // 4096, 8 tokens: 4.51 -> 3.71 us without; Q4_K 14336 x 4096, 1 token, 3.5 groups per
+    // workgroup: 9.82 -> 10.16 us without)
     const int cap = args.M <= 8 ? XCap<1>::KB : XCap<2>::KB;
-    if (args.KBp <= cap) launch_xl<FMT, true>(args, grid, s);
+    if (args.KBp <= cap && args.groups > cu_count()) launch_xl<FMT, true>(args, grid, s);
     else launch_xl<FMT, false>(args, grid, s);
     return hipGetLastError();
 }
