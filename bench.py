@@ -59,7 +59,17 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9   # non-packed f32 vector lane-ops per second
 HEADLINE = "q4_0_m2048_n4096_k4096"
 METRIC = "MMQ prefill GEMM TOPS (2MNK/s) at M=2048,K=4096,N=4096 q4_0; % int8 MFMA peak"
-DECODE_MAX_M = 16                # mmq_gemm runs batches up to this many rows on the decode kernel
+DECODE_BATCH = 16                # the decode kernel's token batch
+DECODE_MAX_BATCHES = 8           # mmq_gemm: up to this many batches ...
+DECODE_MAX_ROUNDS = 8            # ... while batches x 16-row groups <= this many rounds of the CUs
+
+
+def decode_path(M, N, cus):
+    """Whether mmq_gemm runs an M x N product on the decode kernel (the library's own rule)."""
+    if M <= DECODE_BATCH:
+        return True
+    nb = -(-M // DECODE_BATCH)
+    return nb <= DECODE_MAX_BATCHES and nb * -(-N // 16) <= DECODE_MAX_ROUNDS * cus
 COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at least this much
 
 # HBM bytes per launch of the dominant kernel (for MUL_MAT_ID: route + gather launch), measured
@@ -73,8 +83,8 @@ MEASURED_TRAFFIC = {
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
     "q4_K_m512_n14336_k4096": (94_717_268, "abb5fdd9cfc5cfd2"),
     "q6_K_m2048_n4096_k11008": (306_039_285, "abb5fdd9cfc5cfd2"),
-    "dec_q4_0_m8_n4096_k4096": (11_103_725, "16a51ac58bdb9f40"),
-    "dec_q4_K_m8_n14336_k4096": (45_187_771, "16a51ac58bdb9f40"),
+    "dec_q4_0_m8_n4096_k4096": (11_088_360, "8ab505a6a6688df5"),
+    "dec_q4_K_m8_n14336_k4096": (45_184_656, "8ab505a6a6688df5"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],
@@ -340,7 +350,8 @@ def main():
     cfg = gen.CONFIGS[name]
     fmt, M, N, K = cfg["fmt"], cfg["M"], cfg["N"], cfg["K"]
     moe = "E" in cfg
-    decode = M <= DECODE_MAX_M             # decode batch: dense M <= 16 / MoE T <= 16 tokens
+    # decode kernel: dense batches as mmq_gemm dispatches them; MoE decode batches (T <= 8)
+    decode = decode_path(M, N, torch.cuda.get_device_properties(0).multi_processor_count)
     dev = torch.device("cuda:0")
     log(f"[bench] workload {name}: {fmt} M={M} N={N} K={K}")
     ops = 2.0 * M * N * K

@@ -138,7 +138,7 @@ mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M,
     t = kernel_format(t);
     // decode batches go to the split-K matrix-vector kernel; the debug partials stay on the
     // prefill kernels
-    if (o != MMQ_OUT_I32_PARTIALS && M <= mmvq_max_tokens())
+    if (o != MMQ_OUT_I32_PARTIALS && mmvq_dense_ok(M, N))
         return from_hip(launch_mmvq(t, packed, act, M, N, K, out, ldo, as_stream(stream)));
     if (t == MMQ_I8_ROW)
         return from_hip(launch_w8a8_gemm(packed, act, M, N, K, o, out, ldo, as_stream(stream)));

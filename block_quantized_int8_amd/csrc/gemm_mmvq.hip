@@ -210,6 +210,7 @@ struct MvArgs {
     const float* xsx;           // q8_1 region 4: xs * xsum, tile-major
     const float* sa;            // i8_token region 1: per-token scale
     int M, N, KBp, groups;      // groups: 16-row groups holding at least one real row
+    int nb;                     // dense: token batches of MV_TOK (units = nb x groups)
     void* out;
     int64_t ldo;
     // MUL_MAT_ID with at most 8 tokens: the routing ids themselves (each workgroup groups the
@@ -234,10 +235,13 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // = rows 16q..16q+15 = half q&1 of weight tile q/2), all M <= 16 tokens, all of K. Each wave's
 // work is one stream of items (group, chunk), its chunks being wave, wave + MV_W, ... of every
 // group; loads run two items ahead. TG = token groups of 8 (1 or 2); NR = accumulator
-// registers holding a live token (min(M, 4)).
-template <mmq_wtype FMT, int TG, int NR, bool XL, bool ID>
+// registers holding a live token (min(M, 4)). BT: dense token batches of MV_TOK rows (more
+// than MV_TOK tokens), a unit being (batch, group); a separate instance, so that one batch pays
+// no per-item batch arithmetic.
+template <mmq_wtype FMT, int TG, int NR, bool XL, bool ID, bool BT = false>
 __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     static_assert(!ID || XL, "MUL_MAT_ID reads its gathered tokens from the staged rows");
+    static_assert(!BT || (!ID && !XL && TG == 2), "token batches: dense, per-item token loads");
     using T = VQ<FMT>;
     constexpr int TOK = 8 * TG;                              // staged token rows
     constexpr int XSLOTS = XL ? XCap<TG>::KB * 2 * TOK : 0;  // 16-byte slots; slot XSLOTS is zero
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     // work units: 16-row groups, or (pair batch, group) for MUL_MAT_ID, where a batch is up to
     // TOK pairs of one expert (one batch per used expert when a token's experts are distinct;
     // more for an expert named by several slots of a token)
-    int units = a.groups;
+    int units = BT ? a.groups * a.nb : a.groups;
     if constexpr (ID) {
         // Group the P <= 256 pairs by expert: key = expert << 8 | pair (ids outside [0, E) sort
         // last as expert E), rank each key by counting the smaller ones, so s_pp lists the pairs
@@ -375,6 +379,13 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         int q = off + i * G;                                            // 16-row group
         const uint8_t* wx = a.w;                                        // this unit's weights
         int me = a.M, po = 0;                                           // its tokens
+        int ro = 0;                                                     // its first token row
+        if constexpr (BT) {             // dense: token batch bt holds rows 16 bt .. 16 bt + 15
+            const int bt = q / a.groups;
+            q -= bt * a.groups;
+            ro = bt * MV_TOK;
+            me = min(a.M - ro, MV_TOK);
+        }
         if constexpr (ID) {
             const int ue = q / a.groups;
             q -= ue * a.groups;
@@ -399,19 +410,27 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         const int b0 = (wave + j * MV_W) * MV_CH;
         const int64_t tb = (int64_t)(q >> 1) * KBp + b0;                // (tile, block) index
         const rsrc_t rw = rsrc(wx + tb * T::FB + half * (MV_ROWS * LB), MV_CH * T::FB);
-        const rsrc_t rx = rsrc(a.xq + (int64_t)b0 * 1024, MV_CH * 1024);
+        // the batch's token tile and its row offset in it (0 or 16)
+        const int64_t tt = ro >> 5;
+        const int rr = ro & 31;
+        const rsrc_t rx = rsrc(a.xq + (tt * KBp + b0) * 1024, MV_CH * 1024);
         k.b0 = b0;
+        uint32_t ox0 = o_x0, ox1 = o_x1;
+        if constexpr (BT) {
+            ox0 = (diag && t0 < me) ? (uint32_t)(fb * 1024 + (fh * 32 + rr + t0) * 16) : OOR;
+            ox1 = (diag && t1 < me) ? (uint32_t)(fb * 1024 + (fh * 32 + rr + t1) * 16) : OOR;
+        }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             k.w[p] = T::load(rw, o_w + p * 2 * T::FB);
             if constexpr (!XL) {
-                k.x[0][p] = ld128(rx, o_x0 + p * 2048);
-                if constexpr (TG == 2) k.x[1][p] = ld128(rx, o_x1 + p * 2048);
+                k.x[0][p] = ld128(rx, ox0 + p * 2048);
+                if constexpr (TG == 2) k.x[1][p] = ld128(rx, ox1 + p * 2048);
             }
         }
         if constexpr (!T::ROW) {
             const rsrc_t rs = rsrc(wx + a.w_scale_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128);
-            const rsrc_t rxs = rsrc(xsb + (int64_t)b0 * 128, MV_CH * 128);
+            const rsrc_t rxs = rsrc(xsb + (tt * KBp + b0) * 128, MV_CH * 128);
             if constexpr (T::GRID) {       // the row's d of this 4-block group (MV_CH = 4 blocks)
                 const int64_t gq = (int64_t)(q >> 1) * (KBp / 4) + b0 / 4;
                 k.ws = __builtin_amdgcn_raw_buffer_load_b16(
@@ -423,17 +442,17 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
                 k.ws2 = ld32(rsrc(wx + a.w_min_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128), o_s);
 #pragma unroll
             for (int x = 0; x < TG; ++x)       // token of row c16, block b0 + g
-                k.xs[x] = ld32(rxs, k.tk[x] >= 0 ? (uint32_t)(g * 128 + k.tk[x] * 4) : OOR);
+                k.xs[x] = ld32(rxs, k.tk[x] >= 0 ? (uint32_t)(g * 128 + (rr + k.tk[x]) * 4) : OOR);
             if constexpr (T::META) {
                 k.wso[0] = ld32(rs, o_wso);
                 k.wso[1] = ld32(rs, o_wso + 256);
             }
         }
         if constexpr (T::MIN) {
-            const rsrc_t rxm = rsrc(xmb + (int64_t)b0 * 128, MV_CH * 128);
+            const rsrc_t rxm = rsrc(xmb + (tt * KBp + b0) * 128, MV_CH * 128);
 #pragma unroll
             for (int x = 0; x < TG; ++x)       // rows 0-7 only: token of row c16 = k.tk[x]
-                k.xm[x] = __builtin_bit_cast(float, ld32(rxm, (c16 < 8 && k.tk[x] >= 0) ? (uint32_t)(g * 128 + k.tk[x] * 4) : OOR));
+                k.xm[x] = __builtin_bit_cast(float, ld32(rxm, (c16 < 8 && k.tk[x] >= 0) ? (uint32_t)(g * 128 + (rr + k.tk[x]) * 4) : OOR));
             k.wm = __builtin_bit_cast(float, ld32(rsrc(wx + a.w_min_off + (tb * 32 + half * MV_ROWS) * 4, MV_CH * 128), o_s));
         }
     };
@@ -525,6 +544,12 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
             // even blocks) and that + 32 (rows 8-15, odd blocks), token group m >> 3
             const int m = tid >> 4, n = tid & 15;
             int q = off + i * G, me = a.M, row = m;
+            if constexpr (BT) {
+                const int bt = q / a.groups;
+                q -= bt * a.groups;
+                me = min(a.M - bt * MV_TOK, MV_TOK);
+                row = bt * MV_TOK + m;
+            }
             if constexpr (ID) {
                 const int ue = q / a.groups;
                 q -= ue * a.groups;
@@ -541,7 +566,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
                     for (int w = 0; w < MV_W; ++w)
                         s += __builtin_bit_cast(int, red[pb][w][r][la]) + __builtin_bit_cast(int, red[pb][w][r][lb]);
                     const float sw = reinterpret_cast<const float*>(wsb)[col];
-                    reinterpret_cast<uint16_t*>(a.out)[(int64_t)row * a.ldo + col] = bf16_rne(((float)s * a.sa[m]) * sw);
+                    reinterpret_cast<uint16_t*>(a.out)[(int64_t)row * a.ldo + col] = bf16_rne(((float)s * a.sa[row]) * sw);
                 } else {
                     float s = 0.f;
 #pragma unroll
@@ -666,13 +691,15 @@ void launch_xl(const MvArgs& args, dim3 grid, hipStream_t s) {
 
 template <mmq_wtype FMT>
 hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
-    const dim3 grid((unsigned)std::min(args.groups, cu_count()));
+    const dim3 grid((unsigned)std::min(args.groups * args.nb, cu_count()));
     // Token rows staged in LDS only when workgroups loop over several groups: the staging and
     // its barrier are a fixed cost per workgroup that one group does not pay back (q4_0 4096 x
     // 4096, 8 tokens: 4.51 -> 3.71 us without; Q4_K 14336 x 4096, 1 token, 3.5 groups per
     // workgroup: 9.82 -> 10.16 us without)
     const int cap = args.M <= 8 ? XCap<1>::KB : XCap<2>::KB;
-    if (args.KBp <= cap && args.groups > cu_count()) launch_xl<FMT, true>(args, grid, s);
+    if (args.nb > 1)
+        hipLaunchKernelGGL((mmvq_kernel<FMT, 2, 4, false, false, true>), grid, dim3(MV_W * 64), 0, s, args);
+    else if (args.KBp <= cap && args.groups > cu_count()) launch_xl<FMT, true>(args, grid, s);
     else launch_xl<FMT, false>(args, grid, s);
     return hipGetLastError();
 }
@@ -680,6 +707,18 @@ hipError_t launch_fmt(const MvArgs& args, hipStream_t s) {
 }  // namespace
 
 int mmvq_max_tokens() { return MV_TOK; }
+
+// more than 16 tokens: batches of 16 as extra units while they take at most MV_MAX_ROUNDS rounds
+// of the grid (a prefill grid of that size leaves most CUs idle: q4_0 4096 x 4096 takes ~23 us
+// at 17 to 128 tokens there)
+constexpr int MV_MAX_ROUNDS = 8;
+constexpr int MV_MAX_BATCHES = 8;
+bool mmvq_dense_ok(int64_t M, int64_t N) {
+    if (M < 1) return false;
+    if (M <= MV_TOK) return true;
+    const int64_t nb = ceil_div(M, MV_TOK);
+    return nb <= MV_MAX_BATCHES && nb * ceil_div(N, MV_ROWS) <= (int64_t)MV_MAX_ROUNDS * cu_count();
+}
 
 bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K) {
     if (t == MMQ_I8_ROW || T < 1 || T > MV_ID_TOK || T * top_k > MV_IDP) return false;
@@ -702,6 +741,7 @@ hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void
     args.N = (int)N;
     args.KBp = (int)P.KBp;
     args.groups = (int)ceil_div(N, MV_ROWS);
+    args.nb = 1;
     args.out = out;
     args.ldo = N;
     args.xq = ab + L.xq_off;
@@ -728,7 +768,7 @@ hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void
 
 hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                        int64_t K, void* out, int64_t ldo, hipStream_t s) {
-    if (M < 1 || M > MV_TOK) return hipErrorInvalidValue;
+    if (!mmvq_dense_ok(M, N)) return hipErrorInvalidValue;
     const PackedLayout P = packed_layout(t, N, K);
     const uint8_t* ab = static_cast<const uint8_t*>(act);
     MvArgs args{};
@@ -740,6 +780,7 @@ hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t
     args.KBp = (int)P.KBp;
     // groups past N (the second half of a last tile with N % 32 <= 16) hold only padding
     args.groups = (int)ceil_div(N, MV_ROWS);
+    args.nb = (int)ceil_div(M, MV_TOK);
     args.out = out;
     args.ldo = ldo;
     if (t == MMQ_I8_ROW) {

@@ -176,6 +176,8 @@ hipError_t launch_w8a8_gemm(const void* packed, const void* act, int64_t M, int6
                             mmq_otype o, void* out, int64_t ldo, hipStream_t s);
 // Decode batches (M <= mmvq_max_tokens()): f32 out for the block formats, bf16 for I8_ROW.
 int mmvq_max_tokens();
+// the decode kernel takes this product (M <= mmvq_max_tokens(), or a few batches of that size)
+bool mmvq_dense_ok(int64_t M, int64_t N);
 hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                        int64_t K, void* out, int64_t ldo, hipStream_t s);
 // MUL_MAT_ID with at most 8 tokens (and 256 pairs, K within the staging capacity): the

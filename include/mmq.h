@@ -192,11 +192,13 @@ mmq_status mmq_repack_weights(mmq_wtype t, const void* raw, const void* aux,
  * buffer reach 2 GiB (e.g. a 262144 x 8192 q8_0 matrix) are run as several launches over
  * ranges of weight and token tiles, with the same results.
  * Dispatch: batches of M <= 16 token rows (F32 / BF16 output) run the small-batch split-K
- * kernel, larger ones the prefill tiles (a decode batch would leave a prefill tile mostly
- * empty; llama.cpp PR #304, Summary: small batches stay on a matrix-vector kernel). Both
- * compute the same per-block integer dots; the small-batch kernel reads the zero padding
- * rows M..31 of the activation buffer, so that padding must be zero (mmq_quantize_act
- * writes it so). */
+ * kernel, and so do up to 128 rows as batches of 16 while the batches times the 16-row weight
+ * groups, ceil(M/16) * ceil(N/16), stay within 8 times the compute-unit count (such products
+ * would leave a prefill grid mostly idle); larger ones run the prefill tiles (a decode batch
+ * would leave a prefill tile mostly empty; llama.cpp PR #304, Summary: small batches stay on a
+ * matrix-vector kernel). Both compute the same per-block integer dots, with their own f32
+ * summation orders; the small-batch kernel may read the zero padding rows M..31 of the
+ * activation buffer, so that padding must be zero (mmq_quantize_act writes it so). */
 mmq_status mmq_gemm(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                     int64_t K, mmq_otype o, void* out, int64_t ldo, void* stream);
 

@@ -1,7 +1,8 @@
 """GPU parity of the decode (small-batch) path against the CPU oracle, through the C ABI.
 
 mmq_gemm sends batches of M <= 16 token rows (f32 out for the block formats, bf16 for W8A8)
-to the split-K matrix-vector kernel; M = 17 goes back to the prefill tiles. The bars are the
+to the split-K matrix-vector kernel, and up to 128 rows as batches of 16 while ceil(M/16) x
+ceil(N/16) stays within 8 rounds of the compute units; more go to the prefill tiles. The bars are the
 prefill ones: f32 outputs within max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition
 (minfer R1 section 4) and within the rounding bound of tests/parity.py of the per-block C
 oracle, W8A8 bf16 outputs bit-exact (metainfer section 3.1). Cases cover every
@@ -66,11 +67,12 @@ def test_decode_block_formats(env, fmt, M):
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q4_K"])
 def test_decode_crossover_and_ldo(env, fmt):
-    # M = 16 (the decode kernel's largest batch) and M = 17 (the prefill tiles) on the same
-    # weights agree with the oracle; ldo > N leaves the row padding untouched
+    # M = 16 (one decode batch), 17 (two, the second with one token), 128 (eight, the most)
+    # and 129 (the prefill tiles) on the same weights agree with the oracle; ldo > N leaves the
+    # row padding untouched
     torch, mmq, orc = env
     N, K, ldo = 80, 512, 100
-    for M in (16, 17):
+    for M in (16, 17, 128, 129):
         raw, q, got, _ = _case(env, fmt, M, N, K, seed=7, ldo=ldo)
         assert np.all(got[:, N:] == 7.0)
         parity.check_f32(orc, got[:, :N], fmt, raw, N, K, *q, what=M)
@@ -160,6 +162,53 @@ def test_decode_w8a8_full_size(env):
     torch.cuda.synchronize()
     ref_bf, _ = orc.gemm_w8a8(a, sa, w, sw, rows=(0, M), want_acc=True)
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref_bf)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 17, 4096, 4096), ("q4_K", 64, 4096, 4096),
+                                        ("iq1t", 128, 2048, 4096), ("q8_0", 40, 300, 1024),
+                                        ("q6_K", 33, 4096, 11008), ("iq1c", 97, 2048, 4096)])
+def test_decode_batches_of_16(env, fmt, M, N, K):
+    # 17..128 token rows as batches of 16 on the decode kernel (units = batches x 16-row groups;
+    # each batch reads its own token tile and row offset): the last batch ragged (17, 33, 97),
+    # whole (64, 128: the most batches) and a ragged N; every row in full against the f64
+    # definition on sampled weight rows
+    torch, mmq, orc = env
+    dev = torch.device("cuda:0")
+    seed = M + N
+    print(f"[case] decode batches {fmt} M={M} N={N} K={K} seed={seed}", flush=True)
+    gridded = fmt in ("iq1c", "iq1s")
+    grid_np = gen.IQ1C_GRID if gridded else None
+    raw = gen.weights(fmt, N, K, seed=seed, cfg=81)
+    x = gen.act_f32(M, K, seed=seed, cfg=81, outlier_rate=1e-2)
+    act = mmq.quantize_act(torch.from_numpy(x).to(dev))
+    packed = mmq.repack_weights(fmt, torch.from_numpy(raw).to(dev), N, K,
+                                grid=torch.from_numpy(grid_np.view(np.int16)).to(dev) if gridded else None)
+    out = mmq.gemm(fmt, packed, act, M, N, K, "f32")
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rq, rs, rsum = orc.quantize_q8_1(x)
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(seed).choice(N, min(N, 256), replace=False)]))
+    r1, r2 = parity.check_f32(orc, got[:, cols], fmt, raw, N, K, rq, rs, rsum, cols=cols, grid=grid_np,
+                              what=(fmt, M, N, K))
+    print(f"  rel err {r1:.3e} (definition), {r2:.3e} (C oracle)", flush=True)
+
+
+def test_decode_w8a8_batches_of_16(env):
+    # W8A8 at 64 and 45 tokens on the decode kernel: bf16 outputs bit-exact
+    torch, mmq, orc = env
+    N, K = 1536, 4096
+    dev = torch.device("cuda:0")
+    for M in (64, 45):
+        print(f"[case] w8a8 batches M={M} N={N} K={K}", flush=True)
+        a, sa = gen.i8_rows(M, K, seed=M, cfg=82, tensor=gen.T_ACT)
+        w, sw = gen.i8_rows(N, K, seed=M, cfg=82, tensor=gen.T_WEIGHT)
+        act = torch.from_numpy(mmq.act_i8_pack_host(a, sa)).to(dev)
+        packed = mmq.repack_weights("i8_row", torch.from_numpy(w).to(dev), N, K,
+                                    row_scale=torch.from_numpy(sw).to(dev))
+        out = mmq.gemm("i8_row", packed, act, M, N, K, "bf16")
+        torch.cuda.synchronize()
+        ref_bf, _ = orc.gemm_w8a8(a, sa, w, sw, rows=(0, M), want_acc=True)
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref_bf)
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q4_K", "iq1t", "q8_0"])

@@ -13,7 +13,7 @@ itself, which the GEMMs look up in LDS. The checks are:
 * dense prefill: q8_1 bit-exact, the folded int32 block partials bit-exact, f32 within
   max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4), on shapes
   with ragged M and N tails;
-* decode batches (M <= 16, the small-batch kernel) within the same gate;
+* decode batches (M <= 16, the small-batch kernel, and up to 128 rows as batches of 16) within the same gate;
 * MUL_MAT_ID at small sizes (every output row) and at the 64-expert workload size on sampled
   pairs and columns in the launch configuration the bench times, plus a decode-size MoE.
 """

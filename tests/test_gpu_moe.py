@@ -127,9 +127,11 @@ def test_moe_unit_boundaries(env, fmt):
 
 
 def test_moe_matches_dense_per_expert(env):
-    # each pair's row equals the dense MMQ of its token against its expert, bit for bit
+    # each pair's row equals the dense MMQ of its token against its expert, bit for bit; 150
+    # tokens keep the dense call on the tile kernel (up to 128 it takes the decode kernel, whose
+    # split-K sums in another order)
     torch, mmq, _ = env
-    E, T, top_k, N, K = 4, 70, 2, 96, 512
+    E, T, top_k, N, K = 4, 150, 2, 96, 512
     ids = gen.moe_ids(T, top_k, E, seed=6, cfg=74)
     raw, _, _, got = _moe(env, "q4_K", E, T, top_k, N, K, ids, seed=6)
     dev = torch.device("cuda:0")

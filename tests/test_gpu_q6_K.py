@@ -10,7 +10,8 @@ rescaled by its own d*sc (minfer R1 sections 2.2 and 3.3). The checks:
   max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4) and within the
   rounding bound of tests/parity.py of the per-block C oracle, on shapes with
   ragged M and N tails and both signs of sub-scale, plus worst-case blocks;
-* small batches (M <= 16: the decode kernel, two half-block MFMAs per block), MUL_MAT_ID
+* small batches (M <= 16, and batches of 16 up to 128 rows: the decode kernel, two half-block
+  MFMAs per block), MUL_MAT_ID
   (prefill gather and, for at most 8 tokens, the decode kernel), and the 7B
   ffn_down shape (M = 2048, N = 4096, K = 11008) on sampled rows and columns in the launch
   configuration the bench times.
@@ -131,15 +132,16 @@ def test_small_batches(env, M, K):
 
 
 def test_small_batch_matches_prefill_tiles(env):
-    # M = 16 (decode kernel) against M = 17 (prefill tiles) on the same first 16 rows: both are
-    # the same per-half contraction, so they agree to f32 rounding order
+    # M = 16 (decode kernel) against M = 129 (prefill tiles; from 129 rows mmq_gemm leaves the
+    # decode kernel's batches) on the same first 16 rows: both are the same per-half
+    # contraction, so they agree to f32 rounding order
     torch, mmq, _ = env
     N, K = 200, 1024
     raw = gen.weights_q6_K(N, K, seed=5, cfg=66)
-    x = gen.act_f32(17, K, seed=5, cfg=66)
-    _, _, o17, _ = _run(env, raw, x, 17, N, K, partials=False)
+    x = gen.act_f32(129, K, seed=5, cfg=66)
+    _, _, o129, _ = _run(env, raw, x, 129, N, K, partials=False)
     _, _, o16, _ = _run(env, raw, x[:16], 16, N, K, partials=False)
-    assert _rel(o16, o17[:16].astype(np.float64)) <= 1e-5
+    assert _rel(o16, o129[:16].astype(np.float64)) <= 1e-5
 
 
 def test_moe(env):
