@@ -193,6 +193,19 @@ def test_decode_batches_of_16(env, fmt, M, N, K):
     print(f"  rel err {r1:.3e} (definition), {r2:.3e} (C oracle)", flush=True)
 
 
+def test_decode_batches_admission_boundary(env):
+    # 128 tokens are 8 batches: N = 16 x the CU count is the widest matrix the decode kernel
+    # takes (8 units per CU); one more row sends the call to the prefill tiles. Both agree with
+    # the oracle, every output checked
+    torch, mmq, orc = env
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    K = 512
+    for N in (16 * cus, 16 * cus + 1):
+        raw, q, got, _ = _case(env, "q4_0", 128, N, K, seed=N)
+        r1, r2 = parity.check_f32(orc, got, "q4_0", raw, N, K, *q, what=N)
+        print(f"  N={N}: rel err {r1:.3e} (definition), {r2:.3e} (C oracle)", flush=True)
+
+
 def test_decode_w8a8_batches_of_16(env):
     # W8A8 at 64 and 45 tokens on the decode kernel: bf16 outputs bit-exact
     torch, mmq, orc = env
