@@ -78,13 +78,13 @@ COLD_BYTES = 1 << 30             # rotated weight copies for a cold-MALL run: at
 # reported only while the sources still hash the same, else null.
 MEASURED_TRAFFIC = {
     "q4_0_m2048_n4096_k4096": (94_416_986, "abb5fdd9cfc5cfd2"),
-    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_289_935 + 40_678, "eab2d5b74adc5527"),
-    "moe_iq1t_e64_t512_top8_n2048_k4096": (371_323_864 + 40_674, "eab2d5b74adc5527"),
+    "moe_iq1c_e64_t512_top8_n2048_k4096": (284_343_218 + 40_680, "99acccf9ff652c0d"),
+    "moe_iq1t_e64_t512_top8_n2048_k4096": (370_881_786 + 40_679, "99acccf9ff652c0d"),
     "w8a8_m3072_n1536_k4096": (61_465_709, "b2f75c48e899bf66"),
     "q4_K_m512_n14336_k4096": (94_717_268, "abb5fdd9cfc5cfd2"),
     "q6_K_m2048_n4096_k11008": (306_039_285, "abb5fdd9cfc5cfd2"),
-    "dec_q4_0_m8_n4096_k4096": (11_088_360, "8ab505a6a6688df5"),
-    "dec_q4_K_m8_n14336_k4096": (45_184_656, "8ab505a6a6688df5"),
+    "dec_q4_0_m8_n4096_k4096": (11_100_648, "e982aaa89fc10ad1"),
+    "dec_q4_K_m8_n14336_k4096": (45_176_926, "e982aaa89fc10ad1"),
 }
 KERNEL_SOURCES = {
     "block": ["gemm_block.hip", "gemm_common.h"],
@@ -350,7 +350,7 @@ def main():
     cfg = gen.CONFIGS[name]
     fmt, M, N, K = cfg["fmt"], cfg["M"], cfg["N"], cfg["K"]
     moe = "E" in cfg
-    # decode kernel: dense batches as mmq_gemm dispatches them; MoE decode batches (T <= 8)
+    # decode kernel: dense batches as mmq_gemm dispatches them; MoE decode batches (T <= 10)
     decode = decode_path(M, N, torch.cuda.get_device_properties(0).multi_processor_count)
     dev = torch.device("cuda:0")
     log(f"[bench] workload {name}: {fmt} M={M} N={N} K={K}")
@@ -400,7 +400,7 @@ def main():
         ws = torch.empty(mmq.gemm_id_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
 
         kernels = [("quantize_q8_1", lambda r: mmq.quantize_act(xd, out=act)),
-                   ("gemm_id (decode kernel, in-kernel grouping)" if T <= 8 and T * top_k <= 256
+                   ("gemm_id (decode kernel, in-kernel grouping)" if T <= 10 and T * top_k <= 256
                     else "gemm_id (route + gather MMQ)",
                     lambda r: mmq.gemm_id(fmt, packed[r], E, act, ids_d, T, top_k, N, K, out=out, workspace=ws))]
         dom = 1

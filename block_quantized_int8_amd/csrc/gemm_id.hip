@@ -15,7 +15,7 @@
 //      over the unit offsets, reads its tokens' activation rows and writes each pair's own
 //      output row.
 // No host round trip: the grids are sized for the worst case and workgroups past the actual
-// unit counts leave at once. With at most 8 tokens (a decode batch, where the gather tiles
+// unit counts leave at once. With at most 10 tokens (a decode batch, where the gather tiles
 // would be nearly empty) both steps are the decode kernel instead: each of its workgroups
 // groups the at most 256 pairs by expert itself (a rank sort in LDS) and runs (batch of up to 8
 // of one expert's pairs, 16-row group) units (gemm_mmvq.hip).

@@ -221,12 +221,15 @@ struct MvArgs {
 };
 
 constexpr int MV_IDP = 256;     // MUL_MAT_ID decode: pairs (and so pair batches) at most
-// MUL_MAT_ID decode: tokens at most, the token rows one workgroup stages (its batches of up to
-// 8 pairs read them by token id). Measured on 64 experts of 2048 x 4096, top-8, against the
-// prefill gather: IQ1T 13.7 / 32.5 / 40.6 / 50.0 us at 1 / 4 / 6 / 8 tokens against 36 / 47 /
-// 45.4 / 55.9; at 6 tokens Q4_K 38.9 against 50.4, IQ1C 42.9 against 43.3; q4_0 at 8 tokens 44.0
-// against 48.1.
-constexpr int MV_ID_TOK = 8;
+// MUL_MAT_ID decode: tokens at most. A workgroup stages the token rows (8, or 16 past 8 tokens)
+// and its batches of up to 8 pairs read them by token id. Measured on 64 experts of 2048 x 4096,
+// top-8, against the prefill gather: IQ1T 13.7 / 32.5 / 40.6 / 50.0 us at 1 / 4 / 6 / 8 tokens
+// against 36 / 47 / 45.4 / 55.9; at 6 tokens Q4_K 38.9 against 50.4, IQ1C 42.9 against 43.3;
+// q4_0 at 8 tokens 44.0 against 48.1. With 16 rows staged: IQ1T 52.5 / 53.9 / 54.4 / 59.4 us at
+// 9 / 10 / 11 / 12 tokens against 57.8 / 56.9 / 57.3 / 58.0, IQ1C 55.3 / 57.1 / 62.6 at 9 / 10 /
+// 12 against 57.9 / 57.7 / 58.1, q4_0 46.2 / 47.3 at 9 / 10 against 48.9 / 49.3, Q4_K 54.8 at
+// 10 against 65.2.
+constexpr int MV_ID_TOK = 10;
 
 // LDS barrier that leaves global loads in flight (__syncthreads() would also wait for them)
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -238,13 +241,15 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // registers holding a live token (min(M, 4)). BT: dense token batches of MV_TOK rows (more
 // than MV_TOK tokens), a unit being (batch, group); a separate instance, so that one batch pays
 // no per-item batch arithmetic.
-template <mmq_wtype FMT, int TG, int NR, bool XL, bool ID, bool BT = false>
+template <mmq_wtype FMT, int TG, int NR, bool XL, bool ID, bool BT = false, bool W16 = false>
 __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
     static_assert(!ID || XL, "MUL_MAT_ID reads its gathered tokens from the staged rows");
     static_assert(!BT || (!ID && !XL && TG == 2), "token batches: dense, per-item token loads");
     using T = VQ<FMT>;
-    constexpr int TOK = 8 * TG;                              // staged token rows
-    constexpr int XSLOTS = XL ? XCap<TG>::KB * 2 * TOK : 0;  // 16-byte slots; slot XSLOTS is zero
+    static_assert(!W16 || (ID && TG == 1), "16 staged rows: MUL_MAT_ID batches of 8 pairs");
+    constexpr int TOK = 8 * TG;                              // token rows (pairs) per item
+    constexpr int SR = W16 ? 16 : TOK;                       // staged token rows
+    constexpr int XSLOTS = XL ? XCap<SR / 8>::KB * 2 * SR : 0;  // 16-byte slots; slot XSLOTS is zero
     __shared__ float red[2][MV_W][4 * TG][64];
     __shared__ uint2 tab[16];
     __shared__ uint32_t gtab[T::GRID ? 2048 : 1];
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
 #pragma unroll
             for (int x = 0; x < TG; ++x) {
                 if constexpr (XL) {
-                    const int sl = (diag && k.tk[x] >= 0) ? ((k.b0 + 2 * p + fb) * 2 + fh) * TOK + k.tk[x] : XSLOTS;
+                    const int sl = (diag && k.tk[x] >= 0) ? ((k.b0 + 2 * p + fb) * 2 + fh) * SR + k.tk[x] : XSLOTS;
                     xo[x][p] = *reinterpret_cast<const v4i*>(xl + sl * 16);
                 } else {
                     xo[x][p] = k.x[x][p];
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         }
     };
 
-    // LDS path: the token rows 0..TOK-1 of every block go to slot (b*2 + h)*TOK + t (the tiled
+    // LDS path: the token rows 0..SR-1 of every block go to slot (b*2 + h)*SR + t (the tiled
     // xq keeps row t's values 16h..16h+15 of block b at lane h*32 + t; rows >= M are the
     // buffer's zero padding). The staging loads (and iq1c's grid) are issued first, then the
     // first two items' weight loads, then the LDS writes (which wait only for the staging
@@ -591,20 +596,20 @@ __global__ __launch_bounds__(MV_W * 64) void mmvq_kernel(MvArgs a) {
         for (int u = 0; u < GPER; ++u) gv[u] = gsrc[tid + u * MV_W * 64];
     }
     if constexpr (XL) {
-        const int nslot = KBp * 2 * TOK;
+        const int nslot = KBp * 2 * SR;
         const rsrc_t rq = rsrc(a.xq, (uint32_t)KBp * 1024);
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             // every thread issues PER loads (sized for the longest K); slots past this K's end
             // take an offset outside the descriptor, which returns zero without a memory request
             const int sl = tid + u * MV_W * 64;
-            const int t = sl % TOK, h = (sl / TOK) & 1, b = sl / (2 * TOK);
+            const int t = sl % SR, h = (sl / SR) & 1, b = sl / (2 * SR);
             xv[u] = ld128(rq, sl < nslot ? (uint32_t)((b * 64 + h * 32 + t) * 16) : OOR);
         }
     }
     auto stage = [&]() __attribute__((always_inline)) {
         if constexpr (XL) {
-            const int nslot = KBp * 2 * TOK;
+            const int nslot = KBp * 2 * SR;
 #pragma unroll
             for (int u = 0; u < PER; ++u) {
                 const int sl = tid + u * MV_W * 64;
@@ -675,8 +680,10 @@ template <mmq_wtype FMT, bool XL, bool ID = false>
 void launch_xl(const MvArgs& args, dim3 grid, hipStream_t s) {
     const dim3 block(MV_W * 64);
     if constexpr (ID) {
-        // batches of up to 8 pairs whatever the token count: every register is live
-        hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4, XL, ID>), grid, block, 0, s, args);
+        // batches of up to 8 pairs whatever the token count: every register is live; more than
+        // 8 tokens stage 16 rows
+        if (args.M > 8) hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4, XL, ID, false, true>), grid, block, 0, s, args);
+        else hipLaunchKernelGGL((mmvq_kernel<FMT, 1, 4, XL, ID>), grid, block, 0, s, args);
         return;
     }
     switch (args.M) {
@@ -722,7 +729,7 @@ bool mmvq_dense_ok(int64_t M, int64_t N) {
 
 bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K) {
     if (t == MMQ_I8_ROW || T < 1 || T > MV_ID_TOK || T * top_k > MV_IDP) return false;
-    return round_up(K / QK, KB_ALIGN) <= XCap<1>::KB;          // batches of 8: one token group
+    return round_up(K / QK, KB_ALIGN) <= (T > 8 ? XCap<2>::KB : XCap<1>::KB);   // staged rows
 }
 
 hipError_t launch_mmvq_id(mmq_wtype t, const void* packed, int64_t E, const void* act, int64_t T,

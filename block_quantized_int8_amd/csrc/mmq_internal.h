@@ -180,7 +180,7 @@ int mmvq_max_tokens();
 bool mmvq_dense_ok(int64_t M, int64_t N);
 hipError_t launch_mmvq(mmq_wtype t, const void* packed, const void* act, int64_t M, int64_t N,
                        int64_t K, void* out, int64_t ldo, hipStream_t s);
-// MUL_MAT_ID with at most 8 tokens (and 256 pairs, K within the staging capacity): the
+// MUL_MAT_ID with at most 10 tokens (and 256 pairs, K within the staging capacity): the
 // decode kernel over (batch of up to 8 of one expert's pairs, 16-row group) units, from the
 // route kernel's pair offsets and expert order.
 bool mmvq_id_ok(mmq_wtype t, int64_t T, int64_t top_k, int64_t K);

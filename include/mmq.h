@@ -220,7 +220,8 @@ size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
  * The expert grouping (count per expert, scan, scatter of the pairs into expert order) runs
  * on the device with no host round trip, so the call is stream-ordered and capturable; the
  * order of pairs inside one expert is unspecified and does not affect any output value.
- * Decode batches (T <= 8, T*top_k <= 256) run the small-batch kernel per expert instead of
+ * Decode batches (T <= 10, T*top_k <= 256; past 8 tokens K <= 4096) run the small-batch kernel
+ * per expert instead of
  * the prefill tiles (llama.cpp PR #304, Summary: small batches stay on a matrix-vector
  * kernel); the result is the same per-block contraction.
  * Block formats only; o must be MMQ_OUT_F32. MMQ_IQ1C / MMQ_IQ1S: every expert must have

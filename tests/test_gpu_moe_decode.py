@@ -1,8 +1,9 @@
 """GPU parity of MUL_MAT_ID at decode batch sizes, through the C ABI.
 
-With at most 8 tokens (and at most 256 (token, slot) pairs) mmq_gemm_id runs its expert
+With at most 10 tokens (and at most 256 (token, slot) pairs) mmq_gemm_id runs its expert
 grouping and then the decode kernel over (batch of up to 8 of one expert's pairs, 16-row group)
-units instead of the prefill gather tiles; 9 tokens or 257 pairs go back to the gather (both
+units instead of the prefill gather tiles; past 8 tokens a workgroup stages 16 token rows, so K
+is then at most 4096. 11 tokens, 257 pairs or 9 tokens at K > 4096 go back to the gather (both
 sides of each crossover are checked). Bars: each pair's f32 row
 within max|gpu - ref| / max|ref| <= 1e-3 of the f64 definition (minfer R1 section 4), rows of
 invalid ids untouched, and each pair's row bit-identical to the dense decode product of its token
@@ -75,7 +76,7 @@ def _check(env, fmt, E, N, K, ids, raw, rq, rs, got):
         assert rel <= GATE
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 5, 8, 9])
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 8, 9, 10, 11])
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_K", "iq1t"])
 def test_moe_decode_formats(env, fmt, T):
     E, top_k, N, K = 32, 4, 160, 512
@@ -84,10 +85,12 @@ def test_moe_decode_formats(env, fmt, T):
     _check(env, fmt, E, N, K, ids, raw, rq, rs, got)
 
 
-def test_moe_decode_matches_dense_decode_per_expert(env):
-    # each pair's row equals the dense decode product of its token against its expert, bit for bit
+@pytest.mark.parametrize("T", [4, 10])
+def test_moe_decode_matches_dense_decode_per_expert(env, T):
+    # each pair's row equals the dense decode product of its token against its expert, bit for
+    # bit (10 tokens: 16 staged token rows, tokens 8 and 9 read from the second group of 8)
     torch, mmq, _ = env
-    E, T, top_k, N, K = 6, 4, 3, 96, 1024
+    E, top_k, N, K = 6, 3, 96, 1024
     ids = gen.moe_ids(T, top_k, E, seed=21, cfg=84)
     raw, _, _, act, packed, got = _case(env, "q4_K", E, T, top_k, N, K, ids, seed=21)
     dev = torch.device("cuda:0")
@@ -96,6 +99,16 @@ def test_moe_decode_matches_dense_decode_per_expert(env):
         dense = mmq.gemm("q4_K", pe, act, T, N, K, "f32").cpu().numpy()
         tt, jj = np.nonzero(ids == e)
         assert np.array_equal(got[tt, jj].view(np.uint32), dense[tt].view(np.uint32)), e
+
+
+@pytest.mark.parametrize("K", [4096, 4128])
+def test_moe_decode_16_rows_k_limit(env, K):
+    # past 8 tokens the decode kernel stages 16 token rows, which fit up to K = 4096 (128 blocks);
+    # one more block sends the call to the gather tiles. Both agree with the oracle
+    E, T, top_k, N = 16, 9, 4, 96
+    ids = gen.moe_ids(T, top_k, E, seed=K, cfg=84)
+    raw, rq, rs, _, _, got = _case(env, "q4_0", E, T, top_k, N, K, ids, seed=K)
+    _check(env, "q4_0", E, N, K, ids, raw, rq, rs, got)
 
 
 def test_moe_decode_invalid_ids_and_shared_expert(env):

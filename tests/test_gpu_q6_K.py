@@ -12,7 +12,7 @@ rescaled by its own d*sc (minfer R1 sections 2.2 and 3.3). The checks:
   ragged M and N tails and both signs of sub-scale, plus worst-case blocks;
 * small batches (M <= 16, and batches of 16 up to 128 rows: the decode kernel, two half-block
   MFMAs per block), MUL_MAT_ID
-  (prefill gather and, for at most 8 tokens, the decode kernel), and the 7B
+  (prefill gather and, for at most 10 tokens, the decode kernel), and the 7B
   ffn_down shape (M = 2048, N = 4096, K = 11008) on sampled rows and columns in the launch
   configuration the bench times.
 """
@@ -165,9 +165,9 @@ def test_moe(env):
     parity.check_moe(orc, out.cpu().numpy(), "q6_K", raw, N, K, rq, rs, rsum, ids)
 
 
-@pytest.mark.parametrize("T", [1, 4, 8])
+@pytest.mark.parametrize("T", [1, 4, 8, 10])
 def test_moe_decode(env, T):
-    # MUL_MAT_ID with at most 8 tokens runs the decode kernel per expert
+    # MUL_MAT_ID with at most 10 tokens runs the decode kernel per expert
     torch, mmq, orc = env
     dev = torch.device("cuda:0")
     E, top_k, N, K = 16, 8, 160, 1024
