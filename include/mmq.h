@@ -221,9 +221,8 @@ size_t mmq_gemm_id_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
  * on the device with no host round trip, so the call is stream-ordered and capturable; the
  * order of pairs inside one expert is unspecified and does not affect any output value.
  * Decode batches (T <= 10, T*top_k <= 256; past 8 tokens K <= 4096) run the small-batch kernel
- * per expert instead of
- * the prefill tiles (llama.cpp PR #304, Summary: small batches stay on a matrix-vector
- * kernel); the result is the same per-block contraction.
+ * per expert instead of the prefill tiles (llama.cpp PR #304, Summary: small batches stay on a
+ * matrix-vector kernel); the result is the same per-block contraction.
  * Block formats only; o must be MMQ_OUT_F32. MMQ_IQ1C / MMQ_IQ1S: every expert must have
  * been packed with the same grid (the decode-batch kernel reads the first matrix's copy).
  * Limits (MMQ_EINVAL before any launch): T * top_k <= 2^24; outside the decode-batch case,
