@@ -334,6 +334,9 @@ CONFIGS = {
     "dec_q4_0_m8_n4096_k4096": dict(cfg=2, fmt="q4_0", M=8, N=4096, K=4096, out="f32", outlier_rate=1e-3),
     "dec_q4_0_m16_n4096_k4096": dict(cfg=2, fmt="q4_0", M=16, N=4096, K=4096, out="f32", outlier_rate=1e-3),
     "dec_q4_0_m8_n11008_k4096": dict(cfg=2, fmt="q4_0", M=8, N=11008, K=4096, out="f32", outlier_rate=1e-3),
+    "dec_q4_0_m32_n4096_k4096": dict(cfg=2, fmt="q4_0", M=32, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec_q4_0_m64_n4096_k4096": dict(cfg=2, fmt="q4_0", M=64, N=4096, K=4096, out="f32", outlier_rate=1e-3),
+    "dec_q4_K_m64_n4096_k4096": dict(cfg=3, fmt="q4_K", M=64, N=4096, K=4096, out="f32"),
     "dec_q8_0_m8_n4096_k4096": dict(cfg=1, fmt="q8_0", M=8, N=4096, K=4096, out="f32"),
     "dec_q4_K_m8_n14336_k4096": dict(cfg=3, fmt="q4_K", M=8, N=14336, K=4096, out="f32"),
     "dec_q4_K_m8_n4096_k14336": dict(cfg=3, fmt="q4_K", M=8, N=4096, K=14336, out="f32"),
@@ -343,4 +346,5 @@ CONFIGS = {
     "dec_w8a8_m8_n1536_k4096": dict(cfg=4, fmt="i8_row", M=8, N=1536, K=4096, out="bf16"),
     "dec_moe_iq1t_e64_t1_top8_n2048_k4096": dict(cfg=5, fmt="iq1t", M=1, N=2048, K=4096, out="f32", E=64, top_k=8),
     "dec_moe_iq1t_e64_t4_top8_n2048_k4096": dict(cfg=5, fmt="iq1t", M=4, N=2048, K=4096, out="f32", E=64, top_k=8),
+    "dec_moe_iq1t_e64_t10_top8_n2048_k4096": dict(cfg=5, fmt="iq1t", M=10, N=2048, K=4096, out="f32", E=64, top_k=8),
 }
