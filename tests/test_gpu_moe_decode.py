@@ -133,10 +133,11 @@ def test_moe_decode_pair_limit_crossover(env, top_k):
     _check(env, "q4_0", E, N, K, ids, raw, rq, rs, got)
 
 
-@pytest.mark.parametrize("T", [1, 4, 8])
+@pytest.mark.parametrize("T", [1, 4, 8, 10])
 def test_moe_decode_full_shape_sampled(env, T):
-    # the MoE workload's expert shape (64 experts x IQ1T 2048 x 4096, top-8) at decode batches;
-    # every pair row in full against the f64 definition on 256 sampled columns
+    # the MoE workload's expert shape (64 experts x IQ1T 2048 x 4096, top-8) at decode batches
+    # (10 tokens: 16 staged token rows); every pair row in full against the f64 definition on
+    # 256 sampled columns
     torch, mmq, orc = env
     c = gen.CONFIGS["moe_iq1t_e64_t512_top8_n2048_k4096"]
     E, top_k, N, K = c["E"], c["top_k"], c["N"], c["K"]
